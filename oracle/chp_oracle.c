@@ -1,0 +1,615 @@
+/*
+ * CPU ORACLE -- test infrastructure only.
+ *
+ * A plain, slow, single-threaded statement of what one constrained coarsening
+ * level and the partition evaluation compute, written from the definitions in
+ *   [P1] Ronzani & Silvano, "Hypergraph Partitioning on GPU with Distinct
+ *        Incident Hyperedges and Size Constraints" (TPDS submission), and
+ *   [P2] Ronzani & Silvano, "Incidence Constraints in Hypergraph Partitioning
+ *        on GPU" (AsHES 2026 prototype).
+ * Only the tests, the smoke check and the CPU-baseline leg of the benchmark
+ * may load this file.  It shares no code with the GPU library.
+ *
+ * Every array is a plain CSR.  Ids are uint32 (0xFFFFFFFF = none), offsets
+ * int64, weights and sizes uint32, fixed-point scores uint64.  Every set is
+ * stored sorted ascending (the canonical form both sides compare bit-exactly).
+ *
+ * Readings of the pages that the text leaves open are applied here exactly as
+ * stated next to each function; the same readings are listed in the design
+ * notes of the repository.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_OK 0
+#define OR_EINVAL (-1)
+#define OR_ENOMEM (-2)
+#define OR_EOVERFLOW (-3)
+#define OR_EINFEASIBLE (-4)
+#define OR_ECYCLE (-5)
+#define OR_EINTERNAL (-7)
+
+#define NONE 0xFFFFFFFFu
+#define FX_SHIFT 40 /* fixed-point scale of the rating: 2^40 */
+
+typedef struct {
+  uint32_t n_nodes, n_edges;
+  const int64_t *e_off;   /* [E+1] */
+  const uint32_t *e_nsrc; /* [E]   sources are stored first in a segment */
+  const uint32_t *e_pins; /* [P]   */
+  const uint32_t *e_w;    /* [E]   */
+  const uint32_t *n_size; /* [N]   */
+} or_edges;
+
+void or_free(void *p) { free(p); }
+
+static int cmp_u32(const void *a, const void *b) {
+  uint32_t x = *(const uint32_t *)a, y = *(const uint32_t *)b;
+  return (x > y) - (x < y);
+}
+
+/* membership in a sorted array, by plain binary search */
+static int sorted_has(const uint32_t *a, int64_t n, uint32_t v) {
+  int64_t lo = 0, hi = n;
+  while (lo < hi) {
+    int64_t mid = lo + (hi - lo) / 2;
+    if (a[mid] < v) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo < n && a[lo] == v;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O1: canonical form and validation.                                       */
+/* [P1] Sec. II-A: an h-edge is a set of pins split into src(e) and dst(e)   */
+/* with src(e) and dst(e) disjoint; omega maps h-edges to weights.           */
+/* [P1] Sec. II-B: |p| <= Omega and at most Delta distinct inbound h-edges   */
+/* per partition, and a valid solution is assumed to exist -- so a node that */
+/* alone breaks a limit is reported as infeasible.                           */
+/* Precedence of errors: EINVAL, then EOVERFLOW, then EINFEASIBLE.           */
+/* Writes every edge's src and dst sub-lists sorted into pins_out.           */
+/* ------------------------------------------------------------------------ */
+int or_canonicalize(const or_edges *g, uint64_t omega, uint32_t delta, uint32_t *pins_out) {
+  uint32_t N = g->n_nodes, E = g->n_edges;
+  if (N == 0xFFFFFFFFu || E == 0xFFFFFFFFu) return OR_EOVERFLOW;
+  if (g->e_off[0] != 0) return OR_EINVAL;
+  for (uint32_t e = 0; e < E; ++e) {
+    int64_t a = g->e_off[e], b = g->e_off[e + 1];
+    if (b <= a) return OR_EINVAL; /* an h-edge holds at least one pin */
+    if ((int64_t)g->e_nsrc[e] > b - a) return OR_EINVAL;
+    if (g->e_w[e] == 0) return OR_EINVAL;
+  }
+  for (uint32_t n = 0; n < N; ++n)
+    if (g->n_size[n] == 0) return OR_EINVAL;
+  int64_t P = g->e_off[E];
+  memcpy(pins_out, g->e_pins, sizeof(uint32_t) * (size_t)P);
+  for (int64_t i = 0; i < P; ++i)
+    if (pins_out[i] >= N) return OR_EINVAL;
+  for (uint32_t e = 0; e < E; ++e) {
+    int64_t a = g->e_off[e], b = g->e_off[e + 1];
+    uint32_t ns = g->e_nsrc[e];
+    uint32_t *src = pins_out + a, *dst = pins_out + a + ns;
+    int64_t nd = b - a - ns;
+    qsort(src, ns, sizeof(uint32_t), cmp_u32);
+    qsort(dst, (size_t)nd, sizeof(uint32_t), cmp_u32);
+    for (uint32_t i = 1; i < ns; ++i)
+      if (src[i] == src[i - 1]) return OR_EINVAL; /* duplicate pin */
+    for (int64_t i = 1; i < nd; ++i)
+      if (dst[i] == dst[i - 1]) return OR_EINVAL;
+    for (uint32_t i = 0; i < ns; ++i)
+      if (sorted_has(dst, nd, src[i])) return OR_EINVAL; /* src and dst overlap */
+  }
+  for (uint32_t e = 0; e < E; ++e)
+    if (g->e_w[e] >= (1u << 24)) return OR_EOVERFLOW; /* omega * 2^40 must fit 64 bits */
+  /* feasibility of single nodes */
+  uint32_t *indeg = (uint32_t *)calloc(N ? N : 1, sizeof(uint32_t));
+  if (!indeg) return OR_ENOMEM;
+  for (uint32_t e = 0; e < E; ++e)
+    for (int64_t i = g->e_off[e] + g->e_nsrc[e]; i < g->e_off[e + 1]; ++i) indeg[pins_out[i]]++;
+  int rc = OR_OK;
+  for (uint32_t n = 0; n < N; ++n)
+    if ((uint64_t)g->n_size[n] > omega || indeg[n] > delta) rc = OR_EINFEASIBLE;
+  free(indeg);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O2: incidence sets.  [P1] Sec. II-A: in(n) = {e : n in dst(e)},          */
+/* out(n) = {e : n in src(e)}, I(n) = in(n) u out(n).  [P1] Sec. IV-B,      */
+/* Fig. 2: one segment per node, inbound ids stored first, |in(n)| kept in   */
+/* a second array.  Edges are visited in ascending id, so each list is       */
+/* produced sorted.                                                          */
+/* ------------------------------------------------------------------------ */
+int or_incidence(const or_edges *g, int64_t *n_off, uint32_t *n_nin, uint32_t *n_inc) {
+  uint32_t N = g->n_nodes, E = g->n_edges;
+  uint32_t *nout = (uint32_t *)calloc(N ? N : 1, sizeof(uint32_t));
+  int64_t *fin = (int64_t *)malloc(sizeof(int64_t) * (N ? N : 1));
+  int64_t *fout = (int64_t *)malloc(sizeof(int64_t) * (N ? N : 1));
+  if (!nout || !fin || !fout) {
+    free(nout), free(fin), free(fout);
+    return OR_ENOMEM;
+  }
+  memset(n_nin, 0, sizeof(uint32_t) * N);
+  for (uint32_t e = 0; e < E; ++e)
+    for (int64_t i = g->e_off[e]; i < g->e_off[e + 1]; ++i) {
+      uint32_t n = g->e_pins[i];
+      if (i < g->e_off[e] + g->e_nsrc[e]) nout[n]++;
+      else n_nin[n]++;
+    }
+  n_off[0] = 0;
+  for (uint32_t n = 0; n < N; ++n) n_off[n + 1] = n_off[n] + n_nin[n] + nout[n];
+  for (uint32_t n = 0; n < N; ++n) {
+    fin[n] = n_off[n];
+    fout[n] = n_off[n] + n_nin[n];
+  }
+  for (uint32_t e = 0; e < E; ++e)
+    for (int64_t i = g->e_off[e]; i < g->e_off[e + 1]; ++i) {
+      uint32_t n = g->e_pins[i];
+      if (i < g->e_off[e] + g->e_nsrc[e]) n_inc[fout[n]++] = e;
+      else n_inc[fin[n]++] = e;
+    }
+  free(nout), free(fin), free(fout);
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O3: unique neighbourhoods.  [P1] Sec. II-A: N(n) = {m in e : e in I(n)}  */
+/* minus {n}.  [P1] Sec. V-B materialises N(.) as one more CSR.  Output is  */
+/* sorted ascending.  *nb_out is malloc'd (free with or_free).               */
+/* ------------------------------------------------------------------------ */
+int or_neighbors(const or_edges *g, const int64_t *n_off, const uint32_t *n_inc,
+                 int64_t *nb_off, uint32_t **nb_out, uint64_t *nb_total) {
+  uint32_t N = g->n_nodes;
+  uint32_t *seen = (uint32_t *)malloc(sizeof(uint32_t) * (N ? N : 1));
+  uint32_t *list = (uint32_t *)malloc(sizeof(uint32_t) * (N ? N : 1));
+  if (!seen || !list) {
+    free(seen), free(list);
+    return OR_ENOMEM;
+  }
+  for (uint32_t n = 0; n < N; ++n) seen[n] = NONE;
+  /* pass 1: sizes */
+  nb_off[0] = 0;
+  for (uint32_t n = 0; n < N; ++n) {
+    uint32_t cnt = 0;
+    for (int64_t j = n_off[n]; j < n_off[n + 1]; ++j) {
+      uint32_t e = n_inc[j];
+      for (int64_t i = g->e_off[e]; i < g->e_off[e + 1]; ++i) {
+        uint32_t m = g->e_pins[i];
+        if (m != n && seen[m] != n) {
+          seen[m] = n;
+          cnt++;
+        }
+      }
+    }
+    nb_off[n + 1] = nb_off[n] + cnt;
+  }
+  uint64_t total = (uint64_t)nb_off[N];
+  uint32_t *nb = (uint32_t *)malloc(sizeof(uint32_t) * (total ? total : 1));
+  if (!nb) {
+    free(seen), free(list);
+    return OR_ENOMEM;
+  }
+  for (uint32_t n = 0; n < N; ++n) seen[n] = NONE;
+  /* pass 2: contents */
+  for (uint32_t n = 0; n < N; ++n) {
+    uint32_t cnt = 0;
+    for (int64_t j = n_off[n]; j < n_off[n + 1]; ++j) {
+      uint32_t e = n_inc[j];
+      for (int64_t i = g->e_off[e]; i < g->e_off[e + 1]; ++i) {
+        uint32_t m = g->e_pins[i];
+        if (m != n && seen[m] != n) {
+          seen[m] = n;
+          list[cnt++] = m;
+        }
+      }
+    }
+    qsort(list, cnt, sizeof(uint32_t), cmp_u32);
+    memcpy(nb + nb_off[n], list, sizeof(uint32_t) * cnt);
+  }
+  free(seen), free(list);
+  *nb_out = nb;
+  *nb_total = total;
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O4: per-edge rating term and noise cap.                                   */
+/* [P1] Eq. 5 adds omega(e)/|e| for every shared h-edge.  Reading: the term  */
+/* is held in fixed point, t(e) = floor(omega(e) * 2^40 / |e|), so sums are  */
+/* exact and eta(n,m) = eta(m,n) holds bit for bit.  |e| is the pin count of */
+/* the current level.                                                        */
+/* [P1] Sec. V-C caps the symmetric noise at 10% of the mean h-edge weight.  */
+/* Reading: the mean of the normalised weight omega/|e| over all h-edges, so */
+/* cap = floor(sum_e t(e) / (10 |E|)) (exact integer division).              */
+/* ------------------------------------------------------------------------ */
+int or_terms(const or_edges *g, uint64_t *t, uint64_t *cap) {
+  unsigned __int128 sum = 0;
+  for (uint32_t e = 0; e < g->n_edges; ++e) {
+    uint64_t sz = (uint64_t)(g->e_off[e + 1] - g->e_off[e]);
+    t[e] = ((uint64_t)g->e_w[e] << FX_SHIFT) / sz;
+    sum += t[e];
+  }
+  *cap = g->n_edges ? (uint64_t)(sum / ((unsigned __int128)10 * g->n_edges)) : 0;
+  return OR_OK;
+}
+
+/* The noise generator.  [P1] Sec. V-C: rng(min(n,m), max(n,m)).  Reading:   */
+/* one output of Vigna's splitmix64 generator whose state is                 */
+/* seed XOR (min * 2^32 + max), reduced modulo cap + 1.                      */
+static uint64_t splitmix64_once(uint64_t state) {
+  uint64_t z = state + 0x9e3779b97f4a7c15ULL;
+  z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ULL;
+  z = (z ^ (z >> 27)) * 0x94d049bb133111ebULL;
+  return z ^ (z >> 31);
+}
+
+uint64_t or_noise(uint64_t seed, uint64_t cap, uint32_t n, uint32_t m) {
+  uint32_t a = n < m ? n : m, b = n < m ? m : n;
+  uint64_t r = splitmix64_once(seed ^ (((uint64_t)a << 32) | b));
+  return r % (cap + 1);
+}
+
+/* |A u B| for two sorted sets, by a plain merge */
+static uint64_t union_size(const uint32_t *a, int64_t na, const uint32_t *b, int64_t nb) {
+  int64_t i = 0, j = 0;
+  uint64_t u = 0;
+  while (i < na && j < nb) {
+    if (a[i] < b[j]) i++;
+    else if (b[j] < a[i]) j++;
+    else i++, j++;
+    u++;
+  }
+  return u + (uint64_t)(na - i) + (uint64_t)(nb - j);
+}
+
+typedef struct {
+  uint64_t eta;
+  uint32_t id;
+} cand;
+
+static int cmp_cand(const void *x, const void *y) { /* eta descending, id ascending */
+  const cand *a = (const cand *)x, *b = (const cand *)y;
+  if (a->eta != b->eta) return a->eta > b->eta ? -1 : 1;
+  return (a->id > b->id) - (a->id < b->id);
+}
+
+/* ------------------------------------------------------------------------ */
+/* O5: candidate proposal for nodes lo..hi-1.                                */
+/* [P1] Eq. 5: eta(n,m) = sum over e in I(n) with m in e of omega(e)/|e|     */
+/*   (fixed point, see O4), plus the symmetric noise of Sec. V-C once per m. */
+/* [P1] Eq. 6: target(n) is the best valid m, ties to the smallest id        */
+/*   (Sec. V-C: equal scores go to the lowest-id neighbour);                 */
+/*   valid(n,m) <=> size(n)+size(m) <= Omega and |in(n) u in(m)| <= Delta.   */
+/* The union is counted by a sorted merge of the two inbound sets ([P2]      */
+/* Sec. III-B2 keeps in(.) sorted for this) and cross-checked against the    */
+/* identity |in(n)| + |in(m)| - inter(n,m) of [P1] Sec. V-C.                 */
+/* A node with no valid neighbour gets target NONE and score 0.              */
+/* EOVERFLOW if some node's sum of terms plus cap reaches 2^63.              */
+/* ------------------------------------------------------------------------ */
+int or_rate(const or_edges *g, const int64_t *n_off, const uint32_t *n_nin, const uint32_t *n_inc,
+            const uint64_t *t, uint64_t cap, uint64_t omega, uint32_t delta, int noise_on,
+            uint64_t seed, uint32_t lo, uint32_t hi, uint32_t *target, uint64_t *score) {
+  uint32_t N = g->n_nodes;
+  if (hi > N || lo > hi) return OR_EINVAL;
+  uint64_t *eta = (uint64_t *)calloc(N ? N : 1, sizeof(uint64_t));
+  uint32_t *inter = (uint32_t *)calloc(N ? N : 1, sizeof(uint32_t));
+  uint32_t *seen = (uint32_t *)malloc(sizeof(uint32_t) * (N ? N : 1));
+  cand *cl = (cand *)malloc(sizeof(cand) * (N ? N : 1));
+  if (!eta || !inter || !seen || !cl) {
+    free(eta), free(inter), free(seen), free(cl);
+    return OR_ENOMEM;
+  }
+  for (uint32_t i = 0; i < N; ++i) seen[i] = NONE;
+  int rc = OR_OK;
+  for (uint32_t n = lo; n < hi && rc == OR_OK; ++n) {
+    /* overflow guard */
+    unsigned __int128 bound = cap;
+    for (int64_t j = n_off[n]; j < n_off[n + 1]; ++j) {
+      uint32_t e = n_inc[j];
+      if (g->e_off[e + 1] - g->e_off[e] >= 2) bound += t[e];
+    }
+    if (bound >= ((unsigned __int128)1 << 63)) {
+      rc = OR_EOVERFLOW;
+      break;
+    }
+    uint32_t cnt = 0;
+    int64_t nin = n_nin[n];
+    for (int64_t j = n_off[n]; j < n_off[n + 1]; ++j) {
+      uint32_t e = n_inc[j];
+      int e_is_in = (j - n_off[n]) < nin; /* e in in(n) */
+      int64_t a = g->e_off[e], b = g->e_off[e + 1], d0 = a + g->e_nsrc[e];
+      for (int64_t i = a; i < b; ++i) {
+        uint32_t m = g->e_pins[i];
+        if (m == n) continue;
+        if (seen[m] != n) {
+          seen[m] = n;
+          eta[m] = 0;
+          inter[m] = 0;
+          cl[cnt++].id = m;
+        }
+        eta[m] += t[e];
+        if (e_is_in && i >= d0) inter[m]++; /* e in in(n) and m in dst(e) */
+      }
+    }
+    for (uint32_t c = 0; c < cnt; ++c) {
+      uint32_t m = cl[c].id;
+      if (noise_on) eta[m] += or_noise(seed, cap, n, m);
+      cl[c].eta = eta[m];
+    }
+    qsort(cl, cnt, sizeof(cand), cmp_cand);
+    target[n] = NONE;
+    score[n] = 0;
+    const uint32_t *in_n = n_inc + n_off[n];
+    for (uint32_t c = 0; c < cnt; ++c) {
+      uint32_t m = cl[c].id;
+      if ((uint64_t)g->n_size[n] + g->n_size[m] > omega) continue;
+      uint64_t u = union_size(in_n, nin, n_inc + n_off[m], n_nin[m]);
+      if (u != (uint64_t)n_nin[n] + n_nin[m] - inter[m]) {
+        rc = OR_EINTERNAL;
+        break;
+      }
+      if (u > delta) continue;
+      target[n] = m;
+      score[n] = cl[c].eta;
+      break;
+    }
+  }
+  free(eta), free(inter), free(seen), free(cl);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O6: deterministic handshake matching ([P2] Sec. III-A and III-B3).       */
+/*  R = {n : target(target(n)) = n}: two-cycles, matched by default.         */
+/*  Each other node places its score on its candidate; the best proposer of  */
+/*  t, bc(t), has the highest score, ties to the smallest id.                */
+/*  Walking down from the roots, n takes its candidate iff the candidate is  */
+/*  still free and n is its best proposer:                                   */
+/*    taken(n) = n in R  or  (target(n) != NONE and bc(target(n)) = n and    */
+/*               not taken(target(n))).                                      */
+/*  match(n) = target(n) if taken(n); otherwise bc(n) if n has a proposer    */
+/*  (that proposer is then taken by n); otherwise n itself.                  */
+/* Reading for nodes with no candidate (left open by [P2]): they are tops of */
+/* their trees, never taken, and may accept their best proposer.             */
+/* ECYCLE if the proposal graph has a cycle longer than two ([P1] Sec. V-A   */
+/* proves there is none).                                                    */
+/* ------------------------------------------------------------------------ */
+int or_match(uint32_t N, const uint32_t *target, const uint64_t *score, uint32_t *match,
+             uint64_t *n_pairs) {
+  for (uint32_t n = 0; n < N; ++n)
+    if (target[n] != NONE && (target[n] >= N || target[n] == n)) return OR_EINVAL;
+  /* cycle check on the functional graph n -> target(n) */
+  uint8_t *col = (uint8_t *)calloc(N ? N : 1, 1);
+  uint32_t *path = (uint32_t *)malloc(sizeof(uint32_t) * (N ? N : 1));
+  uint32_t *bc = (uint32_t *)malloc(sizeof(uint32_t) * (N ? N : 1));
+  int8_t *tk = (int8_t *)malloc(N ? N : 1);
+  if (!col || !path || !bc || !tk) {
+    free(col), free(path), free(bc), free(tk);
+    return OR_ENOMEM;
+  }
+  int rc = OR_OK;
+  for (uint32_t s = 0; s < N && rc == OR_OK; ++s) {
+    if (col[s]) continue;
+    uint32_t len = 0, v = s;
+    while (v != NONE && col[v] == 0) {
+      col[v] = 1; /* on the current path */
+      path[len++] = v;
+      v = target[v];
+    }
+    if (v != NONE && col[v] == 1) { /* closed a cycle on this path */
+      uint32_t cyc = 0;
+      for (uint32_t i = len; i > 0; --i) {
+        cyc++;
+        if (path[i - 1] == v) break;
+      }
+      if (cyc != 2) rc = OR_ECYCLE;
+    }
+    for (uint32_t i = 0; i < len; ++i) col[path[i]] = 2;
+  }
+  if (rc != OR_OK) {
+    free(col), free(path), free(bc), free(tk);
+    return rc;
+  }
+  /* best proposer of every node, over proposers outside R */
+  for (uint32_t n = 0; n < N; ++n) bc[n] = NONE;
+  for (uint32_t c = 0; c < N; ++c) {
+    uint32_t tg = target[c];
+    if (tg == NONE || target[tg] == c) continue; /* no candidate, or c in R */
+    uint32_t b = bc[tg];
+    if (b == NONE || score[c] > score[b] || (score[c] == score[b] && c < b)) bc[tg] = c;
+  }
+  /* taken(.), resolved top-down with an explicit path */
+  for (uint32_t n = 0; n < N; ++n) tk[n] = -1;
+  for (uint32_t s = 0; s < N; ++s) {
+    uint32_t len = 0, v = s;
+    int val = 0;
+    for (;;) {
+      if (tk[v] >= 0) {
+        val = tk[v];
+        break;
+      }
+      uint32_t tg = target[v];
+      if (tg != NONE && target[tg] == v) { /* v in R */
+        tk[v] = 1;
+        val = 1;
+        break;
+      }
+      if (tg == NONE || bc[tg] != v) { /* top of a chain: not taken */
+        tk[v] = 0;
+        val = 0;
+        break;
+      }
+      path[len++] = v; /* taken(v) = not taken(target(v)) */
+      v = tg;
+    }
+    for (uint32_t i = len; i > 0; --i) {
+      val = !val;
+      tk[path[i - 1]] = (int8_t)val;
+    }
+  }
+  uint64_t moved = 0;
+  for (uint32_t n = 0; n < N; ++n) {
+    if (tk[n]) match[n] = target[n];
+    else if (bc[n] != NONE) match[n] = bc[n];
+    else match[n] = n;
+    moved += match[n] != n;
+  }
+  for (uint32_t n = 0; n < N; ++n)
+    if (match[match[n]] != n) rc = OR_EINTERNAL;
+  *n_pairs = moved / 2;
+  free(col), free(path), free(bc), free(tk);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O7: contraction.  [P1] Sec. III and V-E, [P2] Sec. III-B4.                */
+/*  gamma(n) = {n, match(n)}; reading: coarse ids are the ranks of the       */
+/*  smallest member ids.  size'(c) = sum of member sizes.                    */
+/*  E' = {gamma(e)}, omega' = omega, one coarse edge per fine edge, same id  */
+/*  (edges are not merged; single-pin edges are kept).  dst' = gamma(dst),   */
+/*  src' = gamma(src) minus dst' (duplicates between src and dst are dropped  */
+/*  from src, [P1] Sec. V-E).  All lists sorted.                             */
+/*  Outputs are malloc'd (free with or_free).                                */
+/* ------------------------------------------------------------------------ */
+int or_contract(const or_edges *g, const uint32_t *match, uint32_t *gamma, uint32_t *n_coarse,
+                uint32_t **size_out, int64_t **e_off_out, uint32_t **nsrc_out,
+                uint32_t **pins_out) {
+  uint32_t N = g->n_nodes, E = g->n_edges;
+  for (uint32_t n = 0; n < N; ++n)
+    if (match[n] >= N || match[match[n]] != n) return OR_EINVAL;
+  uint32_t *rank = (uint32_t *)malloc(sizeof(uint32_t) * (N ? N : 1));
+  if (!rank) return OR_ENOMEM;
+  uint32_t nc = 0;
+  for (uint32_t n = 0; n < N; ++n) {
+    uint32_t rep = n < match[n] ? n : match[n];
+    if (rep == n) rank[n] = nc++;
+  }
+  for (uint32_t n = 0; n < N; ++n) {
+    uint32_t rep = n < match[n] ? n : match[n];
+    gamma[n] = rank[rep];
+  }
+  free(rank);
+  uint32_t *sz = (uint32_t *)calloc(nc ? nc : 1, sizeof(uint32_t));
+  int64_t *off = (int64_t *)malloc(sizeof(int64_t) * ((size_t)E + 1));
+  uint32_t *ns = (uint32_t *)malloc(sizeof(uint32_t) * (E ? E : 1));
+  uint32_t *pins = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(g->e_off[E] ? g->e_off[E] : 1));
+  uint32_t *tmp = (uint32_t *)malloc(sizeof(uint32_t) * (N ? N : 1));
+  if (!sz || !off || !ns || !pins || !tmp) {
+    free(sz), free(off), free(ns), free(pins), free(tmp);
+    return OR_ENOMEM;
+  }
+  for (uint32_t n = 0; n < N; ++n) sz[gamma[n]] += g->n_size[n];
+  off[0] = 0;
+  for (uint32_t e = 0; e < E; ++e) {
+    int64_t a = g->e_off[e], b = g->e_off[e + 1], d0 = a + g->e_nsrc[e];
+    /* dst' */
+    uint32_t nd = 0;
+    for (int64_t i = d0; i < b; ++i) tmp[nd++] = gamma[g->e_pins[i]];
+    qsort(tmp, nd, sizeof(uint32_t), cmp_u32);
+    uint32_t ud = 0;
+    for (uint32_t i = 0; i < nd; ++i)
+      if (i == 0 || tmp[i] != tmp[i - 1]) tmp[ud++] = tmp[i];
+    /* src' */
+    uint32_t *sl = (uint32_t *)malloc(sizeof(uint32_t) * (g->e_nsrc[e] ? g->e_nsrc[e] : 1));
+    if (!sl) {
+      free(sz), free(off), free(ns), free(pins), free(tmp);
+      return OR_ENOMEM;
+    }
+    uint32_t nsrc = 0;
+    for (int64_t i = a; i < d0; ++i) sl[nsrc++] = gamma[g->e_pins[i]];
+    qsort(sl, nsrc, sizeof(uint32_t), cmp_u32);
+    uint32_t us = 0;
+    for (uint32_t i = 0; i < nsrc; ++i) {
+      if (i > 0 && sl[i] == sl[i - 1]) continue;
+      if (sorted_has(tmp, ud, sl[i])) continue;
+      sl[us++] = sl[i];
+    }
+    int64_t o = off[e];
+    memcpy(pins + o, sl, sizeof(uint32_t) * us);
+    memcpy(pins + o + us, tmp, sizeof(uint32_t) * ud);
+    ns[e] = us;
+    off[e + 1] = o + us + ud;
+    free(sl);
+  }
+  free(tmp);
+  *n_coarse = nc;
+  *size_out = sz;
+  *e_off_out = off;
+  *nsrc_out = ns;
+  *pins_out = pins;
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O8: partition evaluation.                                                 */
+/*  [P1] Eq. 1: Conn = sum_e omega(e) (lambda(e) - 1), lambda(e) = number    */
+/*  of distinct partitions among e's pins.  [P1] Eq. 16 (k-way section):     */
+/*  cut-net = sum_e omega(e) [lambda(e) > 1].                                */
+/*  [P1] Sec. II-B: size(p) = sum of node sizes in p; inbound(p) =           */
+/*  |{e : pins_in(p,e) > 0}| = number of h-edges with a destination in p.    */
+/*  summary = {conn, cutnet, #parts over Omega, #parts over Delta,           */
+/*             #empty parts, max part size, max part inbound, sum lambda}.   */
+/*  Empty parts are counted, not rejected.                                    */
+/* ------------------------------------------------------------------------ */
+int or_evaluate(const or_edges *g, const uint32_t *rho, uint32_t k, uint64_t omega, uint32_t delta,
+                uint64_t *part_size, uint32_t *part_inb, uint64_t *summary) {
+  uint32_t N = g->n_nodes, E = g->n_edges;
+  if (k == 0 && N > 0) return OR_EINVAL;
+  for (uint32_t n = 0; n < N; ++n)
+    if (rho[n] >= k) return OR_EINVAL;
+  uint32_t *cnt = (uint32_t *)calloc(k ? k : 1, sizeof(uint32_t));
+  uint32_t *mark = (uint32_t *)malloc(sizeof(uint32_t) * (k ? k : 1));
+  uint32_t *dmark = (uint32_t *)malloc(sizeof(uint32_t) * (k ? k : 1));
+  if (!cnt || !mark || !dmark) {
+    free(cnt), free(mark), free(dmark);
+    return OR_ENOMEM;
+  }
+  for (uint32_t p = 0; p < k; ++p) {
+    part_size[p] = 0;
+    part_inb[p] = 0;
+    mark[p] = NONE;
+    dmark[p] = NONE;
+  }
+  for (uint32_t n = 0; n < N; ++n) {
+    part_size[rho[n]] += g->n_size[n];
+    cnt[rho[n]]++;
+  }
+  uint64_t conn = 0, cut = 0, sum_lambda = 0;
+  for (uint32_t e = 0; e < E; ++e) {
+    uint64_t lambda = 0;
+    int64_t a = g->e_off[e], b = g->e_off[e + 1], d0 = a + g->e_nsrc[e];
+    for (int64_t i = a; i < b; ++i) {
+      uint32_t p = rho[g->e_pins[i]];
+      if (mark[p] != e) {
+        mark[p] = e;
+        lambda++;
+      }
+      if (i >= d0 && dmark[p] != e) {
+        dmark[p] = e;
+        part_inb[p]++;
+      }
+    }
+    conn += (uint64_t)g->e_w[e] * (lambda - 1);
+    cut += lambda > 1 ? g->e_w[e] : 0;
+    sum_lambda += lambda;
+  }
+  uint64_t over_o = 0, over_d = 0, empty = 0, max_s = 0, max_i = 0;
+  for (uint32_t p = 0; p < k; ++p) {
+    over_o += part_size[p] > omega;
+    over_d += part_inb[p] > delta;
+    empty += cnt[p] == 0;
+    if (part_size[p] > max_s) max_s = part_size[p];
+    if (part_inb[p] > max_i) max_i = part_inb[p];
+  }
+  summary[0] = conn;
+  summary[1] = cut;
+  summary[2] = over_o;
+  summary[3] = over_d;
+  summary[4] = empty;
+  summary[5] = max_s;
+  summary[6] = max_i;
+  summary[7] = sum_lambda;
+  free(cnt), free(mark), free(dmark);
+  return OR_OK;
+}

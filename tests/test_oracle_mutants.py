@@ -1,0 +1,104 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake in a private copy of ``oracle/chp_oracle.c``
+(on the CPU), builds it, and checks that the hand-worked example, the
+brute-force comparisons or the closed forms reject it.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+MUTANTS = {
+    "bc_tie_largest_id": ("(score[c] == score[b] && c < b)", "(score[c] == score[b] && c > b)"),
+    "target_tie_largest_id": ("return (a->id > b->id) - (a->id < b->id);",
+                              "return (a->id < b->id) - (a->id > b->id);"),
+    "inter_counts_out_edges": ("if (e_is_in && i >= d0) inter[m]++;", "if (i >= d0) inter[m]++;"),
+    "delta_off_by_one": ("if (u > delta) continue;", "if (u > (uint64_t)delta + 1) continue;"),
+    "omega_ignored": ("if ((uint64_t)g->n_size[n] + g->n_size[m] > omega) continue;",
+                      "if ((uint64_t)g->n_size[n] > omega) continue;"),
+    "term_wrong_size": ("t[e] = ((uint64_t)g->e_w[e] << FX_SHIFT) / sz;",
+                        "t[e] = ((uint64_t)g->e_w[e] << FX_SHIFT) / (sz > 1 ? sz - 1 : 1);"),
+    "noise_asymmetric": ("uint32_t a = n < m ? n : m, b = n < m ? m : n;",
+                         "uint32_t a = n, b = m;"),
+    "noise_twice": ("if (noise_on) eta[m] += or_noise(seed, cap, n, m);",
+                    "if (noise_on) eta[m] += 2 * or_noise(seed, cap, n, m);"),
+    "src_keeps_dst_dups": ("if (sorted_has(tmp, ud, sl[i])) continue;", ";"),
+    "gamma_rank_by_max": ("uint32_t rep = n < match[n] ? n : match[n];\n    if (rep == n)",
+                          "uint32_t rep = n > match[n] ? n : match[n];\n    if (rep == n)"),
+    "conn_counts_lambda": ("conn += (uint64_t)g->e_w[e] * (lambda - 1);",
+                           "conn += (uint64_t)g->e_w[e] * lambda;"),
+    "in_out_swapped": ("if (i < g->e_off[e] + g->e_nsrc[e]) n_inc[fout[n]++] = e;\n      else n_inc[fin[n]++] = e;",
+                       "if (i < g->e_off[e] + g->e_nsrc[e]) n_inc[fin[n]++] = e;\n      else n_inc[fout[n]++] = e;"),
+    "neighbors_keep_self": ("if (m != n && seen[m] != n) {\n          seen[m] = n;\n          list[cnt++] = m;",
+                            "if (seen[m] != n) {\n          seen[m] = n;\n          list[cnt++] = m;"),
+    "taken_no_alternation": ("val = !val;", "val = val;"),
+    "roots_not_matched_by_default": ("if (tg != NONE && target[tg] == v) { /* v in R */",
+                                     "if (0) {"),
+    "inbound_counts_sources": ("if (i >= d0 && dmark[p] != e) {", "if (dmark[p] != e) {"),
+}
+
+
+def _checks():
+    """A fast subset of the pins."""
+    pins.test_hand_incidence_and_neighbors()
+    pins.test_hand_rate_unconstrained()
+    pins.test_hand_rate_delta_two()
+    pins.test_hand_contract_and_evaluate()
+    for kw in pins.tiny_cases()[:24:2]:
+        pins.test_structures_vs_brute(kw)
+        pins.test_rate_match_vs_brute(kw, False)
+        pins.test_rate_match_vs_brute(kw, True)
+        pins.test_contract_evaluate_vs_brute(kw)
+    pins.test_evaluate_closed_forms(1)
+
+
+def _build_mutant(name, tmpdir):
+    old, new = MUTANTS[name]
+    src = open(oracle._SRC).read()
+    assert src.count(old) == 1, "mutation anchor not found: %s" % name
+    path = os.path.join(tmpdir, name + ".c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib = os.path.join(tmpdir, name + ".so")
+    subprocess.check_call(["gcc", "-O1", "-shared", "-fPIC", "-std=gnu11", "-o", lib, path])
+    return lib
+
+
+def test_unmutated_passes():
+    _checks()
+
+
+RUNNER = """
+import sys
+sys.path[:0] = [%r, %r]
+import oracle
+oracle._LIB = oracle._SRC = %r
+oracle._lib = None
+import test_oracle_mutants as tm
+try:
+    tm._checks()
+except (AssertionError, oracle.OracleError) as ex:
+    print("caught:", type(ex).__name__)
+    sys.exit(3)
+print("not caught")
+sys.exit(0)
+"""
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    """A planted mistake fails a pin, or makes the mutant crash (both count);
+    each mutant runs in a child process so a crash cannot take the suite down."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(here)
+    with tempfile.TemporaryDirectory() as d:
+        lib = _build_mutant(name, d)
+        r = subprocess.run([sys.executable, "-c", RUNNER % (root, here, lib)],
+                           capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, "planted mistake %s was not detected" % name

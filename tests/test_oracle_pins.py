@@ -1,0 +1,380 @@
+"""Pins of the CPU oracle against things other than itself.
+
+* a hand-worked six-node example, every value derived on paper from the
+  definitions (Eqs. 1, 2, 5, 6 of Ronzani & Silvano's TPDS paper and the
+  handshake of their prototype paper, Sec. III-B3);
+* the published splitmix64 output sequence (noise generator);
+* brute force in pure Python (``tests/brute.py``: sets, exact rationals, full
+  sorts, a literal sequential simulation of the handshake) on many tiny
+  random hypergraphs;
+* closed forms and invariants (symmetry, proposal-graph structure, Eq. 1 /
+  Eq. 2 duality, projection invariance across levels).
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import brute
+import oracle
+import synth
+
+NONE = oracle.NONE
+BIG = 1 << 30
+
+
+def load(h, omega=BIG, delta=BIG, neighbors=True):
+    return oracle.build_incidence(h.e_off, h.e_nsrc, h.e_pins, h.e_w, h.n_size, omega, delta,
+                                  neighbors)
+
+
+# ---------------------------------------------------------------- hand-worked
+# Six unit-size nodes, five h-edges (src | dst, weight):
+#   e0: 0 | 1 2   w3     e1: 1 | 2 3   w2     e2: 3 | 4   w4
+#   e3: 4 | 5 0   w1     e4: 2 | 1     w1
+# Eq. 5 terms w/|e|: e0 1, e1 2/3, e2 2, e3 1/3, e4 1/2.
+HAND_EDGES = [([0], [1, 2]), ([1], [2, 3]), ([3], [4]), ([4], [5, 0]), ([2], [1])]
+HAND_W = [3, 2, 4, 1, 1]
+
+
+def hand():
+    return synth.from_lists(6, HAND_EDGES, HAND_W)
+
+
+def test_hand_incidence_and_neighbors():
+    g = load(hand())
+    # in(n) = {e : n in dst(e)}, out(n) = {e : n in src(e)}; in-edges first
+    want_in = [[3], [0, 4], [0, 1], [1], [2], [3]]
+    want_out = [[0], [1], [4], [2], [3], []]
+    for n in range(6):
+        seg = g.n_inc[g.n_off[n]:g.n_off[n + 1]].tolist()
+        k = int(g.n_nin[n])
+        assert seg[:k] == want_in[n] and seg[k:] == want_out[n]
+    want_nb = [[1, 2, 4, 5], [0, 2, 3], [0, 1, 3], [1, 2, 4], [0, 3, 5], [0, 4]]
+    for n in range(6):
+        assert g.nb[g.nb_off[n]:g.nb_off[n + 1]].tolist() == want_nb[n]
+    # the src sub-list of e3 is {4}, dst sorted {0, 5}
+    assert g.e_pins[g.e_off[3]:g.e_off[4]].tolist() == [4, 0, 5]
+
+
+def fx(fr):
+    return fr * (1 << 40)
+
+
+def test_hand_rate_unconstrained():
+    g = load(hand())
+    t, cap = oracle.terms(g)
+    assert t.tolist() == [(3 << 40) // 3, (2 << 40) // 3, (4 << 40) // 2, (1 << 40) // 3,
+                          (1 << 40) // 2]
+    target, score = oracle.rate(g, BIG, BIG, noise_on=False)
+    # n0: eta(0,1) = eta(0,2) = 1 -> lowest id 1.  n1 <-> n2 at 1 + 1/2 + 2/3.
+    # n3 <-> n4 at 2.  n5: eta(5,0) = eta(5,4) = 1/3 -> 0.
+    assert target.tolist() == [1, 2, 1, 4, 3, 0]
+    assert int(score[1]) == int(t[0] + t[4] + t[1]) == int(score[2])
+    assert abs(Fraction(int(score[1]), 1 << 40) - Fraction(13, 6)) <= Fraction(3, 1 << 40)
+    m, npairs = oracle.match(target, score)
+    # roots {1,2}, {3,4}; 0 proposes to root 1 (never taken), 5 is 0's only
+    # proposer and 0 is free, so 5 takes 0.
+    assert m.tolist() == [5, 2, 1, 4, 3, 0] and npairs == 3
+
+
+def test_hand_rate_delta_two():
+    g = load(hand(), delta=2)
+    target, score = oracle.rate(g, BIG, 2, noise_on=False)
+    # |in(1) u in(2)| = |{e0,e4,e1}| = 3 > 2, |in(1) u in(0)| = 3, |in(1) u in(3)| = 3:
+    # node 1 has no valid neighbour.  n2 -> 3 (|{e0,e1}| = 2).  n0: 1 and 2 invalid,
+    # 4 and 5 tie at 1/3 -> 4.  n5 -> 0 (|{e3}| = 1).
+    assert target.tolist() == [4, NONE, 3, 4, 3, 0]
+    assert int(score[1]) == 0
+    m, npairs = oracle.match(target, score)
+    assert m.tolist() == [5, 1, 2, 4, 3, 0] and npairs == 2
+
+
+def test_hand_contract_and_evaluate():
+    g = load(hand())
+    match = np.array([5, 2, 1, 4, 3, 0], np.uint32)
+    gamma, cg = oracle.contract(g, match)
+    assert gamma.tolist() == [0, 1, 1, 2, 2, 0]
+    assert cg.n_size.tolist() == [2, 2, 2]
+    lists = [cg.e_pins[cg.e_off[e]:cg.e_off[e + 1]].tolist() for e in range(5)]
+    nsrc = cg.e_nsrc.tolist()
+    # e0 {0}|{1}; e1 {}|{1,2} (src 1 is also a dst); e2 {}|{2}; e3 {2}|{0}; e4 {}|{1}
+    assert lists == [[0, 1], [1, 2], [2], [2, 0], [1]]
+    assert nsrc == [1, 0, 0, 1, 0]
+    # Eq. 2: Score = sum w (|e| - |e'|) = 3 + 2 + 4 + 1 + 1 = 11;
+    # Eq. 1 on gamma: 17 - 11 = 6; inbound per part: {e3}, {e0,e1,e4}, {e1,e2}
+    ps, pi, summ = oracle.evaluate(g, gamma, 3, BIG, BIG)
+    assert int(summ[0]) == 6 and int(summ[1]) == 6
+    assert ps.tolist() == [2, 2, 2] and pi.tolist() == [1, 3, 2]
+    ps2, pi2, summ2 = oracle.evaluate(cg, np.arange(3, dtype=np.uint32), 3, BIG, BIG)
+    assert ps2.tolist() == ps.tolist() and pi2.tolist() == pi.tolist()
+    assert int(summ2[0]) == 6
+
+
+# ---------------------------------------------------------------- noise source
+def test_splitmix64_published_sequence():
+    # Vigna's splitmix64 from state 0: the first three outputs
+    want = [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+    gam = 0x9E3779B97F4A7C15
+    for k, w in enumerate(want):
+        state = (k * gam) & ((1 << 64) - 1)
+        assert brute.splitmix64_once(state) == w
+    # the oracle's noise is that output of state seed ^ (min << 32 | max), mod cap+1
+    cap = (1 << 64) - 2
+    assert oracle.noise(0, cap, 0, 0) == want[0] % (cap + 1)
+    for seed, a, b in [(0, 1, 2), (7, 5, 3), (123456789, 10, 99999), (2 ** 63, 0, 4000000)]:
+        for c in [0, 1, 17, 2 ** 34 + 5]:
+            assert oracle.noise(seed, c, a, b) == brute.noise_fx(seed, c, a, b)
+            assert oracle.noise(seed, c, a, b) == oracle.noise(seed, c, b, a)
+
+
+# ---------------------------------------------------------------- brute force
+def tiny_cases():
+    cases = []
+    for seed in range(60):
+        n = 3 + seed % 17
+        e = 1 + (seed * 7) % 23
+        cases.append(dict(seed=seed, n_nodes=n, n_edges=e, max_src=seed % 3,
+                          max_dst=1 + seed % 6, max_w=1 + seed % 9, max_size=1 + seed % 3))
+    return cases
+
+
+@pytest.mark.parametrize("kw", tiny_cases(), ids=lambda k: "s%d" % k["seed"])
+def test_structures_vs_brute(kw):
+    h = synth.tiny(**kw)
+    g = load(h)
+    edges = brute.edges_of(h.e_off, h.e_nsrc, h.e_pins)
+    ins, outs = brute.incidence_sets(h.n_nodes, edges)
+    nbs = brute.neighbor_sets(h.n_nodes, edges)
+    for n in range(h.n_nodes):
+        seg = g.n_inc[g.n_off[n]:g.n_off[n + 1]].tolist()
+        k = int(g.n_nin[n])
+        assert seg[:k] == sorted(ins[n]) and seg[k:] == sorted(outs[n])
+        nb = g.nb[g.nb_off[n]:g.nb_off[n + 1]].tolist()
+        assert nb == sorted(nbs[n])
+        # |N(n)| <= sum over incident edges of (|e| - 1)
+        assert len(nb) <= sum(len(edges[e][0] | edges[e][1]) - 1 for e in ins[n] | outs[n])
+    for e in range(h.n_edges):
+        a, b, s = int(g.e_off[e]), int(g.e_off[e + 1]), int(g.e_nsrc[e])
+        assert g.e_pins[a:a + s].tolist() == sorted(edges[e][0])
+        assert g.e_pins[a + s:b].tolist() == sorted(edges[e][1])
+
+
+def constraint_grid(h):
+    tot_in = max(1, int(np.bincount(h.e_pins[np.concatenate(
+        [np.arange(h.e_off[e] + h.e_nsrc[e], h.e_off[e + 1]) for e in range(h.n_edges)])
+        .astype(np.int64)], minlength=h.n_nodes).max()) if h.n_pins else 1)
+    smax = int(h.n_size.max())
+    return [(BIG, BIG), (2 * smax, BIG), (BIG, tot_in + 1), (smax + 1, tot_in)]
+
+
+@pytest.mark.parametrize("kw", tiny_cases()[::2], ids=lambda k: "s%d" % k["seed"])
+@pytest.mark.parametrize("noise_on", [False, True])
+def test_rate_match_vs_brute(kw, noise_on):
+    h = synth.tiny(**kw)
+    edges = brute.edges_of(h.e_off, h.e_nsrc, h.e_pins)
+    for omega, delta in constraint_grid(h):
+        g = load(h, omega, delta)
+        target, score = oracle.rate(g, omega, delta, noise_on=noise_on, seed=kw["seed"])
+        bt, bs = brute.rate(h.n_nodes, edges, h.e_w, h.n_size, omega, delta, noise_on,
+                            kw["seed"])
+        assert target.tolist() == bt
+        assert [int(x) for x in score] == bs
+        m, npairs = oracle.match(target, score)
+        assert m.tolist() == brute.handshake(bt, bs)
+        assert npairs == sum(1 for n in range(h.n_nodes) if m[n] != n) // 2
+
+
+@pytest.mark.parametrize("kw", tiny_cases()[1::3], ids=lambda k: "s%d" % k["seed"])
+def test_fixed_point_vs_exact_eta(kw):
+    """|eta_fx * 2^-40 - eta| <= (#shared edges) * 2^-40, and eta_fx symmetric."""
+    h = synth.tiny(**kw)
+    edges = brute.edges_of(h.e_off, h.e_nsrc, h.e_pins)
+    exact = brute.eta_exact(h.n_nodes, edges, h.e_w)
+    efx = brute.eta_fx(h.n_nodes, edges, h.e_w)
+    for (n, m), v in exact.items():
+        shared = sum(1 for (s, d) in edges if n in (s | d) and m in (s | d))
+        assert abs(Fraction(efx[(n, m)], 1 << 40) - v) <= Fraction(shared, 1 << 40)
+        assert efx[(n, m)] == efx[(m, n)]
+        if v:
+            assert abs(float(Fraction(efx[(n, m)], 1 << 40) / v) - 1.0) < 1e-6
+    # the oracle's best score equals the brute-force fixed-point maximum
+    g = load(h)
+    target, score = oracle.rate(g, BIG, BIG, noise_on=False)
+    for n in range(h.n_nodes):
+        cands = [efx[(n, m)] for m in range(h.n_nodes) if (n, m) in efx]
+        assert int(score[n]) == (max(cands) if cands else 0)
+
+
+@pytest.mark.parametrize("kw", tiny_cases()[::3], ids=lambda k: "s%d" % k["seed"])
+def test_contract_evaluate_vs_brute(kw):
+    h = synth.tiny(**kw)
+    edges = brute.edges_of(h.e_off, h.e_nsrc, h.e_pins)
+    g = load(h)
+    target, score = oracle.rate(g, BIG, BIG, noise_on=True, seed=3)
+    m, _ = oracle.match(target, score)
+    gamma, cg = oracle.contract(g, m)
+    bg, bsize, bedges, bw = brute.contract(h.n_nodes, edges, h.e_w, h.n_size, m)
+    assert gamma.tolist() == bg
+    assert cg.n_size.tolist() == bsize
+    for e, (s, d) in enumerate(bedges):
+        a, b, ns = int(cg.e_off[e]), int(cg.e_off[e + 1]), int(cg.e_nsrc[e])
+        assert cg.e_pins[a:a + ns].tolist() == sorted(s)
+        assert cg.e_pins[a + ns:b].tolist() == sorted(d)
+    # rebuilt incidence / neighbours of G' equal the definitions on G'
+    ins, outs = brute.incidence_sets(cg.n_nodes, bedges)
+    nbs = brute.neighbor_sets(cg.n_nodes, bedges)
+    for c in range(cg.n_nodes):
+        seg = cg.n_inc[cg.n_off[c]:cg.n_off[c + 1]].tolist()
+        k = int(cg.n_nin[c])
+        assert seg[:k] == sorted(ins[c]) and seg[k:] == sorted(outs[c])
+        assert cg.nb[cg.nb_off[c]:cg.nb_off[c + 1]].tolist() == sorted(nbs[c])
+    for k in [1, 2, 5, h.n_nodes]:
+        rho = synth.uniform_u32(kw["seed"], 99, h.n_nodes, k)
+        ps, pi, summ = oracle.evaluate(g, rho, k, BIG, BIG)
+        conn, cut, bps, bpi, empty = brute.evaluate(h.n_nodes, edges, h.e_w, h.n_size, rho, k)
+        assert (int(summ[0]), int(summ[1]), int(summ[4])) == (conn, cut, empty)
+        assert ps.tolist() == bps and pi.tolist() == bpi
+
+
+# ---------------------------------------------------------------- closed forms
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_evaluate_closed_forms(cfg):
+    h = synth.generate(synth.config(cfg, n_nodes=3000))
+    g = load(h, neighbors=False)
+    sizes = np.diff(g.e_off).astype(np.uint64)
+    w = g.e_w.astype(np.uint64)
+    n_dst = sizes - g.e_nsrc
+    # k = 1: no cut; every edge with a destination is inbound to the only part
+    ps, pi, summ = oracle.evaluate(g, np.zeros(g.n_nodes, np.uint32), 1, BIG, BIG)
+    assert int(summ[0]) == 0 and int(summ[1]) == 0
+    assert int(pi[0]) == int((n_dst > 0).sum()) and int(ps[0]) == int(g.n_size.sum())
+    # identity partition: conn = sum w(|e|-1), inbound({n}) = |in(n)|
+    ident = np.arange(g.n_nodes, dtype=np.uint32)
+    ps, pi, summ = oracle.evaluate(g, ident, g.n_nodes, BIG, BIG)
+    assert int(summ[0]) == int((w * (sizes - 1)).sum())
+    assert int(summ[1]) == int(w[sizes > 1].sum())
+    assert pi.tolist() == g.n_nin.tolist()
+    assert int(summ[7]) == int(sizes.sum())
+
+
+def proposal_invariants(target, score):
+    N = target.shape[0]
+    for n in range(N):
+        t = int(target[n])
+        if t == NONE:
+            assert score[n] == 0
+            continue
+        # Sec. V-A: target(m) = n  =>  score(n) >= score(m)
+        assert score[t] >= score[n]
+        # only two-cycles
+        tt = int(target[t])
+        if tt != NONE and tt != n:
+            assert int(target[tt]) != n
+
+
+def match_invariants(target, score, m, g, omega, delta):
+    N = target.shape[0]
+    ins = [set(g.n_inc[g.n_off[n]:g.n_off[n] + g.n_nin[n]].tolist()) for n in range(N)]
+    for n in range(N):
+        p = int(m[n])
+        assert int(m[p]) == n
+        if p != n:
+            # every pair is a proposal edge and a valid cluster
+            assert int(target[n]) == p or int(target[p]) == n
+            assert int(g.n_size[n]) + int(g.n_size[p]) <= omega
+            assert len(ins[n] | ins[p]) <= delta
+        t = int(target[n])
+        if t != NONE:
+            if int(target[t]) == n:
+                assert p == t  # roots always match
+            # every proposal edge has a matched endpoint
+            assert p != n or int(m[t]) != t
+
+
+@pytest.mark.parametrize("cfg,nn", [(1, None), (2, 20000), (3, 20000), (4, 20000), (5, 8192)])
+def test_level_invariants_and_duality(cfg, nn):
+    spec = synth.config(cfg, n_nodes=nn)
+    h = synth.generate(spec)
+    g = load(h, spec.omega, spec.delta)
+    lv = oracle.level(g, spec.omega, spec.delta, noise_on=True, seed=spec.seed)
+    proposal_invariants(lv.target, lv.score)
+    match_invariants(lv.target, lv.score, lv.match, g, spec.omega, spec.delta)
+    assert lv.n_pairs > 0
+    cg = lv.coarse
+    # sizes add up, limits hold, no duplicate pins, src' and dst' disjoint
+    assert int(cg.n_size.astype(np.uint64).sum()) == int(h.n_size.astype(np.uint64).sum())
+    assert int(cg.n_size.max()) <= spec.omega and int(cg.n_nin.max()) <= spec.delta
+    assert cg.n_nodes == g.n_nodes - lv.n_pairs
+    for e in range(0, cg.n_edges, max(1, cg.n_edges // 2000)):
+        a, b, s = int(cg.e_off[e]), int(cg.e_off[e + 1]), int(cg.e_nsrc[e])
+        src, dst = cg.e_pins[a:a + s], cg.e_pins[a + s:b]
+        assert np.all(np.diff(src.astype(np.int64)) > 0) and np.all(np.diff(dst.astype(np.int64)) > 0)
+        assert not set(src.tolist()) & set(dst.tolist())
+    # Eq. 2 duality: Score(gamma) = sum w (|e| - |e'|) and
+    # Conn_G(gamma) = Conn_G'(identity) = sum w (|e| - 1) - Score(gamma)
+    w = g.e_w.astype(np.int64)
+    sz = np.diff(g.e_off)
+    csz = np.diff(cg.e_off)
+    score_g = int((w * (sz - csz)).sum())
+    _, _, s0 = oracle.evaluate(g, lv.gamma, cg.n_nodes, spec.omega, spec.delta)
+    _, _, s1 = oracle.evaluate(cg, np.arange(cg.n_nodes, dtype=np.uint32), cg.n_nodes,
+                               spec.omega, spec.delta)
+    assert int(s0[0]) == int(s1[0]) == int((w * (sz - 1)).sum()) - score_g
+    assert int(s0[2]) == 0 and int(s0[3]) == 0  # the clusters respect Omega and Delta
+
+
+def test_multilevel_projection_invariance():
+    """Coarsen a VLSI-style graph several levels; at every level the projected
+    partition on G0 evaluates exactly like the identity on G_l."""
+    spec = synth.config(4, n_nodes=6000)
+    h = synth.generate(spec)
+    g0 = load(h, spec.omega, spec.delta)
+    cur = g0
+    rho = np.arange(g0.n_nodes, dtype=np.uint32)
+    for lvl in range(6):
+        lv = oracle.level(cur, spec.omega, spec.delta, noise_on=True, seed=spec.seed)
+        if lv.n_pairs == 0:
+            break
+        rho = lv.gamma[rho]
+        cur = lv.coarse
+        k = cur.n_nodes
+        p0, i0, s0 = oracle.evaluate(g0, rho, k, spec.omega, spec.delta)
+        p1, i1, s1 = oracle.evaluate(cur, np.arange(k, dtype=np.uint32), k, spec.omega,
+                                     spec.delta)
+        assert np.array_equal(p0, p1) and np.array_equal(i0, i1)
+        assert np.array_equal(s0, s1)
+        assert int(s0[2]) == 0 and int(s0[3]) == 0 and int(s0[4]) == 0
+    assert lvl >= 3
+
+
+def test_determinism():
+    spec = synth.config(2, n_nodes=5000)
+    h = synth.generate(spec)
+    a = oracle.level(load(h, spec.omega, spec.delta), spec.omega, spec.delta)
+    b = oracle.level(load(h, spec.omega, spec.delta), spec.omega, spec.delta)
+    assert np.array_equal(a.target, b.target) and np.array_equal(a.score, b.score)
+    assert np.array_equal(a.match, b.match) and np.array_equal(a.coarse.e_pins, b.coarse.e_pins)
+
+
+# ---------------------------------------------------------------- error paths
+def err_code(edges, n, w=None, sizes=None, omega=BIG, delta=BIG):
+    h = synth.from_lists(n, edges, w, sizes)
+    try:
+        oracle.canonicalize(h.e_off, h.e_nsrc, h.e_pins, h.e_w, h.n_size, omega, delta)
+        return 0
+    except oracle.OracleError as ex:
+        return ex.code
+
+
+def test_validation_errors():
+    assert err_code([([0], [1, 2])], 3) == 0
+    assert err_code([([0], [1, 3])], 3) == oracle.EINVAL          # id out of range
+    assert err_code([([0], [1, 1])], 3) == oracle.EINVAL          # duplicate pin
+    assert err_code([([0], [0, 1])], 3) == oracle.EINVAL          # src and dst overlap
+    assert err_code([([], [])], 3) == oracle.EINVAL               # empty h-edge
+    assert err_code([([0], [1])], 3, w=[0]) == oracle.EINVAL      # zero weight
+    assert err_code([([0], [1])], 3, w=[1 << 24]) == oracle.EOVERFLOW
+    assert err_code([([0], [1])], 3, sizes=[1, 5, 1], omega=4) == oracle.EINFEASIBLE
+    assert err_code([([0], [1]), ([2], [1])], 3, delta=1) == oracle.EINFEASIBLE
+    assert err_code([([0], [1, 2])], 3, delta=1) == 0
