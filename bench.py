@@ -1,0 +1,197 @@
+"""Benchmark: constrained coarsening of a synthetic SNN-style hypergraph on
+one MI355X.
+
+One step = the whole hot path on the 100,000-node locality-biased ring
+workload (Poisson(32) fan-out clipped to [2,256], 80% of destinations within
++-512 ring positions, weights 1..8, Omega 64, Delta 1024): build the canonical
+CSR, incidence and neighbourhoods; coarsen level by level (rate, handshake
+match, contract) until fewer than 10,000 nodes remain or no pair forms; then
+evaluate the projected partition on the input graph.  The input edge CSR is
+resident in HBM before timing starts.
+
+value = pins processed by the coarsening levels (sum over levels of the
+level's pin count) per second of whole-step time (build and evaluation
+included).  Per-kernel durations come from HIP events the library records
+on its stream during the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", type=int, default=2, help="workload index 1..5")
+    p.add_argument("--nodes", type=int, default=None, help="shrink the workload (testing)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-nodes", type=int, default=None)
+    return p.parse_args()
+
+
+def run_step(chp, ctx, dev_edges, spec, rho_buf):
+    """One pass of the hot path; returns per-level pin counts and the summary."""
+    import torch
+    g0 = ctx.build_incidence(*dev_edges, spec.omega, spec.delta, True)
+    total_size = int(spec_total_size(dev_edges))
+    floor_nodes = -(-total_size // spec.omega)
+    levels = []
+    g = g0
+    rho = None
+    for lvl in range(spec.levels):
+        if spec.target_nodes and g.n_nodes < spec.target_nodes:
+            break
+        if g.n_nodes <= floor_nodes:
+            break
+        _, _, match, npairs = ctx.rate_and_match(g, spec.omega, spec.delta, True, spec.seed)
+        levels.append((g.n_nodes, g.n_pins, npairs, g.nb_total))
+        if npairs == 0:
+            break
+        gamma, cg = ctx.contract(g, match, True)
+        rho = gamma.long() if rho is None else gamma.long()[rho]
+        if g is not g0:
+            g.free()
+        g = cg
+    k = g.n_nodes
+    if rho is None:
+        rho = torch.arange(g0.n_nodes, device=ctx.device)
+    rho_buf.copy_(rho.to(torch.int32))
+    _, _, summ = ctx.evaluate_partition(g0, rho_buf, k, spec.omega, spec.delta)
+    if g is not g0:
+        g.free()
+    g0.free()
+    return levels, summ
+
+
+_size_cache = {}
+
+
+def spec_total_size(dev_edges):
+    key = dev_edges[4].data_ptr()
+    if key not in _size_cache:
+        _size_cache[key] = int(dev_edges[4].long().sum().item())
+    return _size_cache[key]
+
+
+def cpu_baseline(h, spec, workload, sample_nodes):
+    """The CPU oracle, single-threaded, on level 0 of the same workload (or a
+    smaller instance of it): build + rate + match + contract."""
+    import oracle
+    import synth
+    if sample_nodes and sample_nodes < h.n_nodes:
+        h = synth.generate(synth.config(workload, n_nodes=sample_nodes))
+    t0 = time.perf_counter()
+    g = oracle.build_incidence(h.e_off, h.e_nsrc, h.e_pins, h.e_w, h.n_size, spec.omega,
+                               spec.delta)
+    lv = oracle.level(g, spec.omega, spec.delta, True, spec.seed)
+    dt = time.perf_counter() - t0
+    return {"value": h.n_pins / dt, "unit": "pins/s", "cores": 1, "kind": "oracle",
+            "sample": "level 0 (build incidence+neighbours, rate, match, contract) of %s: "
+                      "%d nodes, %d pins, %.1f s single-threaded"
+                      % (h.spec.name, h.n_nodes, h.n_pins, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import constrained_hypergraph_partitioning_amd as chp
+    import synth
+
+    spec = synth.config(args.workload, n_nodes=args.nodes)
+    h = synth.generate(spec)
+    ctx = chp.Context(0)
+    dev_edges = chp.upload_edges(h)
+    rho_buf = torch.empty(h.n_nodes, dtype=torch.int32, device=ctx.device)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        run_step(chp, ctx, dev_edges, spec, rho_buf)
+    torch.cuda.synchronize()
+    ctx.reset_timings()
+    ctx.set_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    pins = 0
+    levels = None
+    for _ in range(args.steps):
+        levels, summ = run_step(chp, ctx, dev_edges, spec, rho_buf)
+        pins += sum(lv[1] for lv in levels)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    timings = ctx.timings()
+    ctx.set_timing(False)
+
+    # dominant kernel and its algorithmic bytes (rating pass byte model:
+    # each array the launches read counted once per level)
+    rate_names = [k for k in timings if k.startswith("rate_") and k != "rate_classify"]
+    dom = max(timings.items(), key=lambda kv: kv[1][1])
+    rate_ms = sum(timings[k][1] for k in rate_names)
+    rate_launches = sum(timings[k][0] for k in rate_names)
+    level_bytes = rate_level_bytes(levels, h, spec)
+    rate_bytes_per_step = sum(level_bytes)
+    achieved = rate_bytes_per_step * args.steps / (rate_ms / 1e3) / 1e9 if rate_ms else 0.0
+    kern_ms = {k: round(v[1] / args.steps, 4) for k, v in
+               sorted(timings.items(), key=lambda kv: -kv[1][1])[:12]}
+    level_ms = sum(v[1] for k, v in timings.items()) / args.steps
+
+    out = {
+        "metric": "pins/s per constrained coarsening level (rate+match+contract); "
+                  "HBM GB/s vs peak",
+        "value": pins / dt,
+        "unit": "pins/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dt * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32/u64 (integer ids, 40-bit fixed-point ratings)",
+        "data": "synthetic (seeded generator shaped like the pages' SNN workloads)",
+        "config": {"workload": spec.name, "nodes": h.n_nodes, "hyperedges": h.n_edges,
+                   "pins": h.n_pins, "omega": spec.omega, "delta": spec.delta,
+                   "levels": len(levels), "final_nodes": levels[-1][0] - levels[-1][2]
+                   if levels else h.n_nodes, "connectivity": int(summ[0])},
+        "roofline": {"bound": "hbm", "kernel": "rate (rate_small + rate_large)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "avg_launch_ms": rate_ms / max(rate_launches, 1),
+                     "alg_bytes_per_step": rate_bytes_per_step, "traffic": None},
+        "kernel_ms_per_step": kern_ms,
+        "kernel_sum_ms_per_step": level_ms,
+        "dominant_kernel": dom[0],
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(h, spec, args.workload, args.cpu_sample_nodes)
+    print(json.dumps(out))
+
+
+def rate_level_bytes(levels, h, spec):
+    """Algorithmic bytes of the rating pass per level, each array read or
+    written once: pins and incidence (4 B each per pin), neighbour lists
+    (4 B per entry), per-hyperedge offsets, source counts and terms (20 B),
+    per-node offsets, counts, sizes and outputs (40 B)."""
+    return [8 * n_pins + 4 * nb_total + 20 * h.n_edges + 40 * n_nodes
+            for n_nodes, n_pins, _, nb_total in levels]
+
+
+if __name__ == "__main__":
+    main()

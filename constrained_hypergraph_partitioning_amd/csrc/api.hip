@@ -1,0 +1,673 @@
+// C ABI: context, allocation, timing, and the host-side sequencing of the
+// kernels of each entry point.  Every kernel runs on the context stream; the
+// host synchronises only where a count must size an allocation or a value
+// is returned to the caller.
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+
+// ---------------------------------------------------------------------------
+// allocation and error plumbing
+
+void *ctx_alloc(chp_ctx *c, size_t bytes) {
+  if (bytes == 0) bytes = 256;
+  void *p = nullptr;
+  if (c->alloc) {
+    p = c->alloc(bytes, c->user);
+  } else if (hipMalloc(&p, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    p = nullptr;
+  }
+  return p;
+}
+
+void ctx_free(chp_ctx *c, void *p) {
+  if (!p) return;
+  if (c->free_fn) c->free_fn(p, c->user);
+  else (void)hipFree(p);
+}
+
+namespace {
+
+struct Fail {
+  int code;
+};
+
+void set_err(chp_ctx *c, const char *fmt, const char *a = "", long long b = 0) {
+  char buf[512];
+  snprintf(buf, sizeof buf, fmt, a, b);
+  c->err = buf;
+}
+
+void hip_check(chp_ctx *c, hipError_t e, const char *what) {
+  if (e != hipSuccess) {
+    set_err(c, "%s: HIP error %lld", what, (long long)e);
+    c->err += std::string(" (") + hipGetErrorString(e) + ")";
+    throw Fail{CHP_EDEVICE};
+  }
+}
+
+void launch_check(chp_ctx *c, const char *what) { hip_check(c, hipPeekAtLastError(), what); }
+
+// Scratch buffers freed when the call returns (stream order keeps later
+// reuse of the memory behind the kernels that used it).
+struct Scratch {
+  chp_ctx *c;
+  std::vector<void *> v;
+  explicit Scratch(chp_ctx *cc) : c(cc) {}
+  ~Scratch() {
+    for (void *p : v) ctx_free(c, p);
+  }
+  template <typename T>
+  T *get(u64 n) {
+    void *p = ctx_alloc(c, (size_t)(n ? n : 1) * sizeof(T));
+    if (!p) {
+      set_err(c, "device allocation of %s%lld bytes failed", "", (long long)(n * sizeof(T)));
+      throw Fail{CHP_ENOMEM};
+    }
+    v.push_back(p);
+    return (T *)p;
+  }
+  void release(void *p) {
+    auto it = std::find(v.begin(), v.end(), p);
+    if (it != v.end()) {
+      ctx_free(c, p);
+      v.erase(it);
+    }
+  }
+};
+
+// Arrays that become part of a published chp_hgraph: freed on failure only.
+struct Owned {
+  chp_ctx *c;
+  std::vector<void *> v;
+  bool keep = false;
+  explicit Owned(chp_ctx *cc) : c(cc) {}
+  ~Owned() {
+    if (!keep)
+      for (void *p : v) ctx_free(c, p);
+  }
+  template <typename T>
+  T *get(u64 n) {
+    void *p = ctx_alloc(c, (size_t)(n ? n : 1) * sizeof(T));
+    if (!p) {
+      set_err(c, "device allocation of %s%lld bytes failed", "", (long long)(n * sizeof(T)));
+      throw Fail{CHP_ENOMEM};
+    }
+    v.push_back(p);
+    return (T *)p;
+  }
+};
+
+__global__ void k_fill_u32(u32 *p, u64 n, u32 v) {
+  for (u64 i = (u64)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (u64)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+__global__ void k_fill_u64(u64 *p, u64 n, u64 v) {
+  for (u64 i = (u64)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (u64)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// copy n bytes device->host and wait for the stream
+void read_back(chp_ctx *c, void *host, const void *dev, size_t n) {
+  hip_check(c, hipMemcpyAsync(c->pinned, dev, n, hipMemcpyDeviceToHost, c->stream), "readback");
+  hip_check(c, hipStreamSynchronize(c->stream), "stream synchronize");
+  memcpy(host, c->pinned, n);
+}
+
+void d2d(chp_ctx *c, void *dst, const void *src, size_t n) {
+  if (n) hip_check(c, hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, c->stream), "copy");
+}
+
+u32 read_flags(chp_ctx *c) {
+  u32 f;
+  read_back(c, &f, c->flags, sizeof f);
+  return f;
+}
+
+int flags_code(u32 f) {
+  if (f & FLAG_EINVAL) return CHP_EINVAL;
+  if (f & FLAG_EOVERFLOW) return CHP_EOVERFLOW;
+  if (f & FLAG_EINFEASIBLE) return CHP_EINFEASIBLE;
+  if (f & FLAG_ECYCLE) return CHP_ECYCLE;
+  return CHP_OK;
+}
+
+void fail_flags(chp_ctx *c, u32 f, const char *what) {
+  int code = flags_code(f);
+  if (code == CHP_OK) return;
+  const char *kind = code == CHP_EINVAL      ? "invalid input"
+                     : code == CHP_EOVERFLOW ? "value out of the supported range"
+                     : code == CHP_EINFEASIBLE
+                         ? "a single node exceeds omega or delta"
+                         : "proposal graph has a cycle longer than two";
+  set_err(c, "%s", what);
+  c->err += std::string(": ") + kind;
+  throw Fail{code};
+}
+
+void clear_flags(chp_ctx *c) { launch_fill_u32(c, c->flags, 64, 0); }
+
+u32 grid_big_for(u32 count) { return count < 256 ? (count ? count : 1) : 256; }
+
+// ---------------------------------------------------------------------------
+// shared steps
+
+// Sort every run listed in rl (counts already on the device).
+void sort_listed_runs(chp_ctx *c, Scratch &s, u32 *data, RunLists rl) {
+  u32 hc[8];
+  read_back(c, hc, rl.cnt, sizeof hc);
+  u32 *scr = nullptr;
+  u64 per_wg = 0;
+  u32 gb = grid_big_for(hc[2]);
+  if (hc[2]) {
+    per_wg = (u64)hc[3];
+    scr = s.get<u32>(per_wg * gb);
+  }
+  launch_sort_runs(c, data, rl, hc, scr, per_wg, gb);
+  launch_check(c, "sort runs");
+}
+
+RunLists make_runlists(Scratch &s, u64 cap) {
+  RunLists rl;
+  for (int k = 0; k < 3; ++k) {
+    rl.start[k] = s.get<i64>(cap);
+    rl.len[k] = s.get<u32>(cap);
+  }
+  rl.cnt = s.get<u32>(8);
+  return rl;
+}
+
+// incidence CSR of a canonical, validated hyperedge CSR (g->e_* set);
+// allocates g->n_off, n_nin, n_inc into `own`.
+void build_incidence_core(chp_ctx *c, Scratch &s, Owned &own, chp_hgraph *g, u64 omega,
+                          u32 delta) {
+  const u32 N = g->n_nodes, E = g->n_edges;
+  const u64 P = g->n_pins;
+  g->n_off = own.get<i64>((u64)N + 1);
+  g->n_nin = own.get<u32>(N);
+  g->n_inc = own.get<u32>(P);
+  u32 *indeg = s.get<u32>(N), *outdeg = s.get<u32>(N), *deg = s.get<u32>(N);
+  launch_fill_u32(c, indeg, N, 0);
+  launch_fill_u32(c, outdeg, N, 0);
+  launch_degrees(c, E, g->e_off, g->e_nsrc, g->e_pins, indeg, outdeg);
+  launch_node_feas(c, N, indeg, outdeg, g->n_size, omega, delta, deg, g->n_nin);
+  i64 *tmp = s.get<i64>(scan_tmp_words(N));
+  scan_u32_to_i64(c, deg, g->n_off, N, tmp);
+  launch_fill_u32(c, indeg, N, 0);
+  launch_fill_u32(c, outdeg, N, 0);
+  launch_scatter(c, E, g->e_off, g->e_nsrc, g->e_pins, g->n_off, g->n_nin, indeg, outdeg,
+                 g->n_inc);
+  launch_check(c, "incidence");
+  s.release(deg);
+  s.release(tmp);
+  RunLists rl = make_runlists(s, 2ull * N);
+  launch_fill_u32(c, rl.cnt, 8, 0);
+  launch_node_runs(c, N, g->n_off, g->n_nin, rl);
+  sort_listed_runs(c, s, g->n_inc, rl);
+}
+
+// neighbourhood CSR of g (incidence already built)
+void build_neighbors_core(chp_ctx *c, Scratch &s, Owned &own, chp_hgraph *g) {
+  const u32 N = g->n_nodes;
+  g->nb_off = own.get<i64>((u64)N + 1);
+  u32 *bound = s.get<u32>(N);
+  NbLists nl;
+  for (int k = 0; k < 3; ++k) nl.list[k] = s.get<u32>(N);
+  nl.cnt = s.get<u32>(8);
+  launch_fill_u32(c, nl.cnt, 8, 0);
+  launch_nb_classify(c, N, g->e_off, g->n_off, g->n_inc, bound, nl);
+  i64 *ooff = s.get<i64>((u64)N + 1);
+  i64 *tmp = s.get<i64>(scan_tmp_words(N));
+  scan_u32_to_i64(c, bound, ooff, N, tmp);
+  launch_check(c, "neighbour classes");
+  i64 obuf_total;
+  u32 hc[8];
+  read_back(c, &obuf_total, ooff + N, sizeof obuf_total);
+  read_back(c, hc, nl.cnt, sizeof hc);
+  if (hc[7]) {
+    set_err(c, "%sa node's incident pins exceed 2^32");
+    throw Fail{CHP_EOVERFLOW};
+  }
+  u32 *obuf = s.get<u32>((u64)obuf_total);
+  u32 *count = s.get<u32>(N);
+  launch_fill_u32(c, count, N, 0);
+  u32 *scr = nullptr;
+  u64 per_wg = 0;
+  u32 gb = grid_big_for(hc[2]);
+  if (hc[2]) {
+    per_wg = 2ull * hc[3];
+    scr = s.get<u32>(per_wg * gb);
+  }
+  launch_nb_build(c, N, g->e_off, g->e_pins, g->n_off, g->n_inc, ooff, obuf, count, nl, hc, scr,
+                  per_wg, gb);
+  scan_u32_to_i64(c, count, g->nb_off, N, tmp);
+  launch_check(c, "neighbours");
+  i64 total;
+  read_back(c, &total, g->nb_off + N, sizeof total);
+  g->nb = own.get<u32>((u64)total);
+  g->nb_total = (u64)total;
+  launch_nb_compact(c, N, ooff, obuf, g->nb_off, g->nb);
+  launch_check(c, "neighbour compaction");
+}
+
+EdgeLists make_edge_lists(chp_ctx *c, Scratch &s, u32 E, const i64 *e_off, u32 hc[8]) {
+  EdgeLists el;
+  for (int k = 0; k < 3; ++k) el.list[k] = s.get<u32>(E);
+  el.cnt = s.get<u32>(8);
+  launch_fill_u32(c, el.cnt, 8, 0);
+  launch_edge_classify(c, E, e_off, el);
+  launch_check(c, "edge classes");
+  read_back(c, hc, el.cnt, 8 * sizeof(u32));
+  return el;
+}
+
+template <typename F>
+int guarded(chp_ctx *c, F &&f) {
+  if (!c) return CHP_EINVAL;
+  c->err.clear();
+  try {
+    int dev;
+    hip_check(c, hipGetDevice(&dev), "hipGetDevice");
+    if (dev != c->device) hip_check(c, hipSetDevice(c->device), "hipSetDevice");
+    f();
+    return CHP_OK;
+  } catch (const Fail &x) {
+    return x.code;
+  }
+}
+
+}  // namespace
+
+void launch_fill_u32(chp_ctx *c, u32 *p, u64 n, u32 v) {
+  if (!n) return;
+  u32 g = grid_for(n, 256);
+  if (g > 4096) g = 4096;
+  CHP_LAUNCH(c, "fill", k_fill_u32, g, 256, 0, p, n, v);
+}
+
+void launch_fill_u64(chp_ctx *c, u64 *p, u64 n, u64 v) {
+  if (!n) return;
+  u32 g = grid_for(n, 256);
+  if (g > 4096) g = 4096;
+  CHP_LAUNCH(c, "fill", k_fill_u64, g, 256, 0, p, n, v);
+}
+
+// ---------------------------------------------------------------------------
+// timing
+
+void timing_begin(chp_ctx *c, const char *name, hipEvent_t *a, hipEvent_t *b) {
+  (void)name;
+  for (hipEvent_t *e : {a, b}) {
+    if (!c->free_events.empty()) {
+      *e = c->free_events.back();
+      c->free_events.pop_back();
+    } else if (hipEventCreate(e) != hipSuccess) {
+      *e = nullptr;
+    }
+  }
+  if (*a) (void)hipEventRecord(*a, c->stream);
+}
+
+static void resolve_timings(chp_ctx *c) {
+  if (c->pending.empty()) return;
+  (void)hipStreamSynchronize(c->stream);
+  for (auto &r : c->pending) {
+    float ms = 0.f;
+    if (r.a && r.b) (void)hipEventElapsedTime(&ms, r.a, r.b);
+    TimingSum *hit = nullptr;
+    for (auto &s : c->sums)
+      if (s.name == r.name || strcmp(s.name, r.name) == 0) {
+        hit = &s;
+        break;
+      }
+    if (!hit) {
+      c->sums.push_back(TimingSum{r.name, 0, 0.0});
+      hit = &c->sums.back();
+    }
+    hit->launches += 1;
+    hit->total_ms += ms;
+    if (r.a) c->free_events.push_back(r.a);
+    if (r.b) c->free_events.push_back(r.b);
+  }
+  c->pending.clear();
+}
+
+void timing_end(chp_ctx *c, const char *name, hipEvent_t a, hipEvent_t b) {
+  if (b) (void)hipEventRecord(b, c->stream);
+  c->pending.push_back(TimingRec{name, a, b});
+  if (c->pending.size() >= 4096) resolve_timings(c);
+}
+
+// ---------------------------------------------------------------------------
+// C ABI
+
+extern "C" {
+
+int chp_create(chp_ctx **out, void *hip_stream, chp_alloc_fn alloc, chp_free_fn free_fn,
+               void *user) {
+  if (!out) return CHP_EINVAL;
+  *out = nullptr;
+  if ((alloc == nullptr) != (free_fn == nullptr)) return CHP_EINVAL;
+  chp_ctx *c = new chp_ctx();
+  c->stream = (hipStream_t)hip_stream;
+  c->alloc = alloc;
+  c->free_fn = free_fn;
+  c->user = user;
+  if (hipGetDevice(&c->device) != hipSuccess ||
+      hipHostMalloc((void **)&c->pinned, 64 * sizeof(u64), hipHostMallocDefault) != hipSuccess) {
+    (void)hipGetLastError();
+    delete c;
+    return CHP_EDEVICE;
+  }
+  c->flags = (u32 *)ctx_alloc(c, 64 * sizeof(u32));
+  if (!c->flags) {
+    (void)hipHostFree(c->pinned);
+    delete c;
+    return CHP_ENOMEM;
+  }
+  *out = c;
+  return CHP_OK;
+}
+
+void chp_destroy(chp_ctx *c) {
+  if (!c) return;
+  (void)hipStreamSynchronize(c->stream);
+  resolve_timings(c);
+  for (hipEvent_t e : c->free_events) (void)hipEventDestroy(e);
+  ctx_free(c, c->flags);
+  (void)hipHostFree(c->pinned);
+  delete c;
+}
+
+const char *chp_last_error(const chp_ctx *c) { return c ? c->err.c_str() : "null context"; }
+
+int chp_set_timing(chp_ctx *c, int on) {
+  if (!c) return CHP_EINVAL;
+  c->timing = on ? 1 : 0;
+  return CHP_OK;
+}
+
+int chp_get_timings(chp_ctx *c, chp_timing *out, int max) {
+  if (!c) return CHP_EINVAL;
+  resolve_timings(c);
+  int n = (int)c->sums.size();
+  for (int i = 0; i < n && i < max && out; ++i)
+    out[i] = chp_timing{c->sums[i].name, c->sums[i].launches, c->sums[i].total_ms};
+  return n;
+}
+
+void chp_reset_timings(chp_ctx *c) {
+  if (!c) return;
+  resolve_timings(c);
+  c->sums.clear();
+}
+
+void chp_hgraph_free(chp_ctx *c, chp_hgraph *g) {
+  if (!c || !g) return;
+  void *ps[] = {g->e_off, g->e_nsrc, g->e_pins, g->e_w, g->n_size,
+                g->n_off, g->n_nin,  g->n_inc,  g->nb_off, g->nb};
+  for (void *p : ps) ctx_free(c, p);
+  memset(g, 0, sizeof *g);
+}
+
+int chp_build_incidence(chp_ctx *c, const chp_edges *in, const chp_params *prm,
+                        int build_neighbors, chp_hgraph *out) {
+  return guarded(c, [&] {
+    if (!in || !prm || !out) {
+      set_err(c, "%snull argument");
+      throw Fail{CHP_EINVAL};
+    }
+    const u32 N = in->n_nodes, E = in->n_edges;
+    const u64 P = in->n_pins;
+    if (!in->e_off || (E && (!in->e_nsrc || !in->e_w)) || (P && !in->e_pins) ||
+        (N && !in->n_size)) {
+      set_err(c, "%snull array in chp_edges");
+      throw Fail{CHP_EINVAL};
+    }
+    if (N == NONE32 || E == NONE32) {
+      set_err(c, "%sids must stay below 2^32-1");
+      throw Fail{CHP_EOVERFLOW};
+    }
+    Scratch s(c);
+    Owned own(c);
+    clear_flags(c);
+    launch_check_edges(c, N, E, P, in->e_off, in->e_nsrc, in->e_w, in->n_size);
+    launch_check(c, "check edges");
+    u32 f = read_flags(c);
+    if (f & FLAG_EINVAL) fail_flags(c, FLAG_EINVAL, "offsets, weights or sizes");
+    chp_hgraph g;
+    memset(&g, 0, sizeof g);
+    g.n_nodes = N;
+    g.n_edges = E;
+    g.n_pins = P;
+    g.e_off = own.get<i64>((u64)E + 1);
+    g.e_nsrc = own.get<u32>(E);
+    g.e_pins = own.get<u32>(P);
+    g.e_w = own.get<u32>(E);
+    g.n_size = own.get<u32>(N);
+    d2d(c, g.e_off, in->e_off, sizeof(i64) * ((size_t)E + 1));
+    d2d(c, g.e_nsrc, in->e_nsrc, sizeof(u32) * (size_t)E);
+    d2d(c, g.e_w, in->e_w, sizeof(u32) * (size_t)E);
+    d2d(c, g.n_size, in->n_size, sizeof(u32) * (size_t)N);
+    // canonical pins: copy, range check, queue unsorted runs
+    RunLists rl = make_runlists(s, 2ull * E + 2);
+    u32 *bad = s.get<u32>(E);
+    launch_fill_u32(c, rl.cnt, 8, 0);
+    launch_edges_canon(c, N, E, in->e_off, in->e_nsrc, in->e_pins, g.e_pins, bad, rl);
+    launch_check(c, "canonical edges");
+    u32 hc[8];
+    read_back(c, hc, rl.cnt, sizeof hc);
+    f = read_flags(c);
+    if (f & FLAG_EINVAL) fail_flags(c, FLAG_EINVAL, "pins");
+    if (hc[4]) {
+      sort_listed_runs(c, s, g.e_pins, rl);
+      launch_edges_check(c, g.e_off, g.e_nsrc, g.e_pins, bad, hc[4]);
+      launch_check(c, "edge check");
+      f = read_flags(c);
+      if (f & FLAG_EINVAL) fail_flags(c, FLAG_EINVAL, "pins");
+    }
+    if (f & FLAG_EOVERFLOW) fail_flags(c, FLAG_EOVERFLOW, "hyperedge weight");
+    s.release(bad);
+    build_incidence_core(c, s, own, &g, prm->omega, prm->delta);
+    f = read_flags(c);
+    if (f) fail_flags(c, f, "node limits");
+    if (build_neighbors) build_neighbors_core(c, s, own, &g);
+    hip_check(c, hipStreamSynchronize(c->stream), "build_incidence");
+    own.keep = true;
+    *out = g;
+  });
+}
+
+int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u32 *target,
+                       u64 *score_fx, u32 *match, u32 *n_pairs_host) {
+  return guarded(c, [&] {
+    if (!g || !prm || !n_pairs_host || (g->n_nodes && (!target || !score_fx || !match))) {
+      set_err(c, "%snull argument");
+      throw Fail{CHP_EINVAL};
+    }
+    const u32 N = g->n_nodes, E = g->n_edges;
+    if (N && (!g->nb_off || !g->nb)) {
+      set_err(c, "%sthe graph has no neighbourhoods (build them first)");
+      throw Fail{CHP_EINVAL};
+    }
+    *n_pairs_host = 0;
+    if (N == 0) return;
+    Scratch s(c);
+    clear_flags(c);
+    u64 *t = s.get<u64>(E);
+    const u32 np = terms_partials(E);
+    u64 *partials = s.get<u64>(2ull * np);
+    u64 *capinfo = s.get<u64>(4);
+    launch_terms(c, E, g->e_off, g->e_w, t, partials, np, capinfo);
+    NbLists nl;
+    nl.list[0] = s.get<u32>(N);
+    nl.list[1] = s.get<u32>(N);
+    nl.list[2] = nullptr;
+    nl.cnt = s.get<u32>(8);
+    launch_fill_u32(c, nl.cnt, 8, 0);
+    launch_rate_classify(c, N, g->nb_off, nl, target, score_fx);
+    launch_check(c, "rate classes");
+    u32 hc[8];
+    read_back(c, hc, nl.cnt, sizeof hc);
+    RateArgs a;
+    a.N = N;
+    a.e_off = g->e_off;
+    a.e_nsrc = g->e_nsrc;
+    a.e_pins = g->e_pins;
+    a.t = t;
+    a.n_off = g->n_off;
+    a.n_nin = g->n_nin;
+    a.n_inc = g->n_inc;
+    a.n_size = g->n_size;
+    a.nb_off = g->nb_off;
+    a.nb = g->nb;
+    a.capinfo = capinfo;
+    a.omega = prm->omega;
+    a.delta = prm->delta;
+    a.noise_on = prm->noise_on ? 1u : 0u;
+    a.seed = prm->noise_seed;
+    a.target = target;
+    a.score = score_fx;
+    a.flags = c->flags;
+    launch_rate(c, a, nl, hc);
+    launch_check(c, "rate");
+    MatchScratch ms;
+    ms.bscore = s.get<u64>(N);
+    ms.bid = s.get<u32>(N);
+    ms.tk = s.get<uint8_t>(N);
+    ms.p0 = ms.p1 = nullptr;
+    ms.x0 = ms.x1 = nullptr;
+    launch_fill_u64(c, ms.bscore, N, 0);
+    launch_fill_u32(c, ms.bid, N, NONE32);
+    u32 *npairs = s.get<u32>(1);
+    launch_fill_u32(c, npairs, 1, 0);
+    launch_match(c, N, target, score_fx, ms, match, npairs);
+    launch_match_write(c, N, target, ms, match, npairs);
+    launch_check(c, "match");
+    u32 f = read_flags(c);
+    if (f & (FLAG_EINVAL | FLAG_EOVERFLOW)) fail_flags(c, f, "rating");
+    if (f & FLAG_LONGCHAIN) {
+      ms.p0 = s.get<u32>(N);
+      ms.p1 = s.get<u32>(N);
+      ms.x0 = s.get<uint8_t>(N);
+      ms.x1 = s.get<uint8_t>(N);
+      launch_match_jump(c, N, target, ms);
+      launch_fill_u32(c, npairs, 1, 0);
+      launch_match_write(c, N, target, ms, match, npairs);
+      launch_check(c, "match (long chains)");
+      f = read_flags(c);
+      if (f & FLAG_ECYCLE) fail_flags(c, FLAG_ECYCLE, "matching");
+    }
+    read_back(c, n_pairs_host, npairs, sizeof(u32));
+  });
+}
+
+int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
+                 int build_neighbors, chp_hgraph *coarse) {
+  return guarded(c, [&] {
+    if (!g || !coarse || (g->n_nodes && (!match || !gamma))) {
+      set_err(c, "%snull argument");
+      throw Fail{CHP_EINVAL};
+    }
+    const u32 N = g->n_nodes, E = g->n_edges;
+    const u64 P = g->n_pins;
+    Scratch s(c);
+    Owned own(c);
+    clear_flags(c);
+    u32 *is_rep = s.get<u32>(N);
+    i64 *rank = s.get<i64>((u64)N + 1);
+    i64 *tmp = s.get<i64>(scan_tmp_words(N > E ? N : E));
+    launch_rep(c, N, match, is_rep);
+    scan_u32_to_i64(c, is_rep, rank, N, tmp);
+    launch_check(c, "representatives");
+    i64 nc;
+    read_back(c, &nc, rank + N, sizeof nc);
+    u32 f = read_flags(c);
+    if (f & FLAG_EINVAL) fail_flags(c, FLAG_EINVAL, "match is not a symmetric pairing");
+    chp_hgraph cg;
+    memset(&cg, 0, sizeof cg);
+    cg.n_nodes = (u32)nc;
+    cg.n_edges = E;
+    cg.n_size = own.get<u32>((u64)nc);
+    cg.e_w = own.get<u32>(E);
+    cg.e_off = own.get<i64>((u64)E + 1);
+    cg.e_nsrc = own.get<u32>(E);
+    d2d(c, cg.e_w, g->e_w, sizeof(u32) * (size_t)E);
+    launch_gamma(c, N, match, rank, g->n_size, gamma, cg.n_size);
+    u32 hc[8];
+    EdgeLists el = make_edge_lists(c, s, E, g->e_off, hc);
+    u64 *scr = nullptr;
+    u64 per_wg = 0;
+    u32 gb = grid_big_for(hc[2]);
+    if (hc[2]) {
+      per_wg = 2ull * hc[3];
+      scr = s.get<u64>(per_wg * gb);
+    }
+    u32 *opins = s.get<u32>(P);
+    u32 *olen = s.get<u32>(E);
+    launch_edge_contract(c, g->e_off, g->e_nsrc, g->e_pins, gamma, opins, olen, cg.e_nsrc, el, hc,
+                         scr, per_wg, gb);
+    scan_u32_to_i64(c, olen, cg.e_off, E, tmp);
+    launch_check(c, "coarse hyperedges");
+    i64 pc;
+    read_back(c, &pc, cg.e_off + E, sizeof pc);
+    cg.n_pins = (u64)pc;
+    cg.e_pins = own.get<u32>((u64)pc);
+    launch_pins_compact(c, E, g->e_off, opins, cg.e_off, cg.e_pins);
+    launch_check(c, "coarse pins");
+    s.release(opins);
+    build_incidence_core(c, s, own, &cg, ~0ull, NONE32);
+    if (build_neighbors) build_neighbors_core(c, s, own, &cg);
+    hip_check(c, hipStreamSynchronize(c->stream), "contract");
+    own.keep = true;
+    *coarse = cg;
+  });
+}
+
+int chp_evaluate_partition(chp_ctx *c, const chp_hgraph *g, const u32 *rho, u32 k,
+                           const chp_params *prm, u64 *part_size, u32 *part_inb,
+                           u64 summary_host[8]) {
+  return guarded(c, [&] {
+    if (!g || !prm || !summary_host || (g->n_nodes && !rho) || (k && (!part_size || !part_inb))) {
+      set_err(c, "%snull argument");
+      throw Fail{CHP_EINVAL};
+    }
+    const u32 N = g->n_nodes, E = g->n_edges;
+    if (N && k == 0) {
+      set_err(c, "%sk must be positive");
+      throw Fail{CHP_EINVAL};
+    }
+    Scratch s(c);
+    clear_flags(c);
+    u64 *summary = s.get<u64>(8);
+    u32 *part_cnt = s.get<u32>(k);
+    launch_fill_u64(c, summary, 8, 0);
+    launch_fill_u64(c, part_size, k, 0);
+    launch_fill_u32(c, part_inb, k, 0);
+    launch_fill_u32(c, part_cnt, k, 0);
+    launch_eval_nodes(c, N, rho, k, g->n_size, part_size, part_cnt);
+    u32 hc[8];
+    EdgeLists el = make_edge_lists(c, s, E, g->e_off, hc);
+    u64 *scr = nullptr;
+    u64 per_wg = 0;
+    u32 gb = grid_big_for(hc[2]);
+    if (hc[2]) {
+      per_wg = 2ull * hc[3];
+      scr = s.get<u64>(per_wg * gb);
+    }
+    launch_eval_edges(c, g->e_off, g->e_nsrc, g->e_pins, g->e_w, rho, k, part_inb, summary, el,
+                      hc, scr, per_wg, gb);
+    launch_eval_parts(c, k, part_size, part_inb, part_cnt, prm->omega, prm->delta, summary);
+    launch_check(c, "evaluate");
+    u64 sum[8];
+    read_back(c, sum, summary, sizeof sum);
+    u32 f = read_flags(c);
+    if (f & FLAG_EINVAL) fail_flags(c, FLAG_EINVAL, "rho has an entry >= k");
+    memcpy(summary_host, sum, sizeof sum);
+  });
+}
+
+}  // extern "C"

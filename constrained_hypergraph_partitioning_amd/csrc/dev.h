@@ -1,0 +1,265 @@
+// Device-side building blocks for wave64 / workgroup cooperation on gfx950:
+// scans and reductions built from cross-lane shuffles, LDS bitonic sorting,
+// a merge-path merge of sorted runs in global memory, and the rating noise.
+#pragma once
+#include "common.h"
+
+#define WAVE 64
+
+__device__ __forceinline__ u32 lane_id() { return __lane_id(); }
+__device__ __forceinline__ u32 wave_id() { return threadIdx.x / WAVE; }
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v) {
+  const u32 l = lane_id();
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    T o = __shfl_up(v, d, WAVE);
+    if (l >= (u32)d) v += o;
+  }
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int d = WAVE / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, WAVE);
+  return v;
+}
+
+// Exclusive scan across a workgroup of BLOCK threads.  `lds` holds at least
+// BLOCK/64 + 1 elements.  Returns this thread's exclusive prefix; *total gets
+// the workgroup total.  Contains barriers: call from every thread.
+template <int BLOCK, typename T>
+__device__ __forceinline__ T wg_excl_scan(T v, T *lds, T *total) {
+  constexpr int NW = BLOCK / WAVE;
+  T inc = wave_incl_scan(v);
+  if (NW == 1) {
+    T tot = __shfl(inc, WAVE - 1, WAVE);
+    *total = tot;
+    return inc - v;
+  }
+  if (lane_id() == WAVE - 1) lds[wave_id()] = inc;
+  __syncthreads();
+  T off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    T s = lds[w];
+    if (w < (int)wave_id()) off += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + inc - v;
+}
+
+template <int BLOCK, typename T>
+__device__ __forceinline__ T wg_sum(T v, T *lds) {
+  constexpr int NW = BLOCK / WAVE;
+  v = wave_sum(v);
+  if (NW == 1) return v;
+  if (lane_id() == 0) lds[wave_id()] = v;
+  __syncthreads();
+  T tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) tot += lds[w];
+  __syncthreads();
+  return tot;
+}
+
+__device__ __forceinline__ u64 sat_add(u64 a, u64 b) {
+  u64 s = a + b;
+  return s < a ? ~0ull : s;
+}
+
+// (eta desc, id asc): is (e1,i1) strictly better than (e2,i2)?
+__device__ __forceinline__ bool better(u64 e1, u32 i1, u64 e2, u32 i2) {
+  return e1 > e2 || (e1 == e2 && i1 < i2);
+}
+
+// Workgroup argmax of (eta, id) under `better`; result broadcast to all.
+template <int BLOCK>
+__device__ __forceinline__ void wg_best(u64 &eta, u32 &id, u64 *lds_e, u32 *lds_i) {
+  constexpr int NW = BLOCK / WAVE;
+#pragma unroll
+  for (int d = WAVE / 2; d > 0; d >>= 1) {
+    u64 oe = __shfl_xor(eta, d, WAVE);
+    u32 oi = __shfl_xor(id, d, WAVE);
+    if (better(oe, oi, eta, id)) eta = oe, id = oi;
+  }
+  if (NW == 1) return;
+  if (lane_id() == 0) lds_e[wave_id()] = eta, lds_i[wave_id()] = id;
+  __syncthreads();
+  eta = lds_e[0];
+  id = lds_i[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w)
+    if (better(lds_e[w], lds_i[w], eta, id)) eta = lds_e[w], id = lds_i[w];
+  __syncthreads();
+}
+
+// ---- binary searches -----------------------------------------------------
+// first index in a[lo,hi) with a[i] >= v
+template <typename P>
+__device__ __forceinline__ i64 lower_bound_i(const P *a, i64 lo, i64 hi, u32 v) {
+  while (lo < hi) {
+    i64 mid = lo + ((hi - lo) >> 1);
+    if (a[mid] < v) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+// first index in a[lo,hi) with a[i] > v
+template <typename P>
+__device__ __forceinline__ i64 upper_bound_i(const P *a, i64 lo, i64 hi, u32 v) {
+  while (lo < hi) {
+    i64 mid = lo + ((hi - lo) >> 1);
+    if (a[mid] <= v) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+// index of the last entry of the non-decreasing u32 array pre[0..n] that is <= v
+// (pre[0] == 0 <= v is assumed); this is the run holding flat index v.
+__device__ __forceinline__ u32 run_of(const u32 *pre, u32 n, u32 v) {
+  u32 lo = 0, hi = n;  // answer in [0, n-1]
+  while (hi - lo > 1) {
+    u32 mid = (lo + hi) >> 1;
+    if (pre[mid] <= v) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ u32 next_pow2(u32 x) {
+  u32 p = 2;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// ---- LDS bitonic sort ----------------------------------------------------
+// Sorts s[0..m) ascending, m a power of two >= 2, all BLOCK threads taking
+// part.  Entries beyond the data must already be padded with the max key.
+template <int BLOCK, typename K>
+__device__ void lds_bitonic(K *s, u32 m) {
+  for (u32 k = 2; k <= m; k <<= 1) {
+    for (u32 j = k >> 1; j > 0; j >>= 1) {
+      for (u32 i = threadIdx.x; i < (m >> 1); i += BLOCK) {
+        u32 lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+        u32 hi = lo + j;
+        K a = s[lo], b = s[hi];
+        bool up = (lo & k) == 0;
+        if ((a > b) == up) {
+          s[lo] = b;
+          s[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+template <typename K>
+__device__ __forceinline__ K key_max();
+template <>
+__device__ __forceinline__ u32 key_max<u32>() { return 0xFFFFFFFFu; }
+template <>
+__device__ __forceinline__ u64 key_max<u64>() { return ~0ull; }
+
+// Merge sorted A[0,na) and B[0,nb) into C (merge path; ties take A first).
+template <int BLOCK, typename K>
+__device__ void wg_merge(const K *A, u64 na, const K *B, u64 nb, K *C) {
+  constexpr int ITEMS = 8;
+  const u64 total = na + nb;
+  for (u64 base = 0; base < total; base += (u64)BLOCK * ITEMS) {
+    u64 d = base + (u64)threadIdx.x * ITEMS;
+    if (d >= total) continue;
+    u64 lo = d > nb ? d - nb : 0, hi = d < na ? d : na;
+    while (lo < hi) {
+      u64 mid = (lo + hi) >> 1;
+      if (A[mid] <= B[d - 1 - mid]) lo = mid + 1;
+      else hi = mid;
+    }
+    u64 i = lo, j = d - lo;
+    for (int k = 0; k < ITEMS && d + k < total; ++k) {
+      bool takeA = j >= nb || (i < na && A[i] <= B[j]);
+      C[d + k] = takeA ? A[i++] : B[j++];
+    }
+  }
+}
+
+// Sort a[0,n) (global memory) with b[0,n) as scratch.  Chunks of CAP keys
+// are sorted in LDS (lds holds CAP keys), then merged pairwise.  Returns the
+// array holding the sorted result (a or b).  All threads must call.
+template <int BLOCK, int CAP, typename K>
+__device__ K *wg_sort_global(K *a, K *b, u64 n, K *lds) {
+  for (u64 c0 = 0; c0 < n; c0 += CAP) {
+    u32 cnt = (u32)((n - c0) < CAP ? (n - c0) : CAP);
+    for (u32 i = threadIdx.x; i < CAP; i += BLOCK) lds[i] = i < cnt ? a[c0 + i] : key_max<K>();
+    __syncthreads();
+    lds_bitonic<BLOCK>(lds, (u32)CAP);
+    for (u32 i = threadIdx.x; i < cnt; i += BLOCK) a[c0 + i] = lds[i];
+    __syncthreads();
+  }
+  K *src = a, *dst = b;
+  for (u64 w = CAP; w < n; w <<= 1) {
+    for (u64 s = 0; s < n; s += 2 * w) {
+      u64 na = (n - s) < w ? (n - s) : w;
+      u64 rest = n - s - na;
+      u64 nb = rest < w ? rest : w;
+      wg_merge<BLOCK>(src + s, na, src + s + na, nb, dst + s);
+    }
+    __syncthreads();
+    K *t = src;
+    src = dst;
+    dst = t;
+  }
+  __syncthreads();
+  return src;
+}
+
+// Bitonic sort of one key per lane across a wave (ascending by lane).
+template <typename K>
+__device__ __forceinline__ K wave_sort64(K v) {
+  const u32 l = lane_id();
+#pragma unroll
+  for (u32 k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (u32 j = k >> 1; j > 0; j >>= 1) {
+      K w = __shfl_xor(v, j, WAVE);
+      bool up = (l & k) == 0;
+      bool lower = (l & j) == 0;
+      v = (lower == up) ? (v < w ? v : w) : (v < w ? w : v);
+    }
+  }
+  return v;
+}
+
+// ---- rating noise ---------------------------------------------------------
+// One output of splitmix64 (Steele, Lea & Flood, OOPSLA 2014) from `state`.
+__device__ __forceinline__ u64 splitmix64_out(u64 state) {
+  u64 z = state + 0x9e3779b97f4a7c15ull;
+  z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+  z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+  return z ^ (z >> 31);
+}
+
+// x mod d for d >= 2 given magic = floor((2^64-1)/d): the quotient estimate
+// mulhi(x, magic) is at most 2 below floor(x/d) (division by invariant
+// integers, Granlund & Montgomery, PLDI 1994), fixed by two subtractions.
+__device__ __forceinline__ u64 mod_magic(u64 x, u64 d, u64 magic) {
+  u64 q = __umul64hi(x, magic);
+  u64 r = x - q * d;
+  if (r >= d) r -= d;
+  if (r >= d) r -= d;
+  return r;
+}
+
+// Symmetric noise of the pair {n, m} in [0, cap]; d = cap + 1.
+__device__ __forceinline__ u64 pair_noise(u64 seed, u32 n, u32 m, u64 d, u64 magic) {
+  if (d <= 1) return 0;
+  u32 a = n < m ? n : m, b = n < m ? m : n;
+  u64 x = splitmix64_out(seed ^ (((u64)a << 32) | b));
+  return mod_magic(x, d, magic);
+}

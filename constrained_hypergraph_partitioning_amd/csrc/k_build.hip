@@ -1,0 +1,482 @@
+// Canonical hyperedge CSR, incidence CSR and unique neighbourhoods.
+//
+// Data layout follows the compressed-sparse h-graph of "Hypergraph
+// Partitioning on GPU with Distinct Incident Hyperedges and Size Constraints"
+// (Sec. IV-B, Fig. 2): one segment per hyperedge with sources first, one
+// segment per node with inbound hyperedges first.  Neighbourhoods N(n)
+// (Sec. II-A, materialised as in Sec. V-B) are the sorted union of the pins of
+// n's incident hyperedges without n.
+#include "dev.h"
+#include "kernels.h"
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// validation of offsets, weights and sizes (before any pin is read)
+__global__ void k_check_edges(u32 N, u32 E, u64 P, const i64 *e_off, const u32 *e_nsrc,
+                              const u32 *e_w, const u32 *n_size, u32 *flags) {
+  u64 i = (u64)blockIdx.x * blockDim.x + threadIdx.x;
+  u32 f = 0;
+  if (i < E) {
+    i64 a = e_off[i], b = e_off[i + 1];
+    if (i == 0 && a != 0) f |= FLAG_EINVAL;
+    if (b <= a || a < 0 || (u64)b > P) f |= FLAG_EINVAL;
+    if (i + 1 == E && (u64)b != P) f |= FLAG_EINVAL;
+    if (b > a && (i64)e_nsrc[i] > b - a) f |= FLAG_EINVAL;
+    u32 w = e_w[i];
+    if (w == 0) f |= FLAG_EINVAL;
+    if (w >= (1u << 24)) f |= FLAG_EOVERFLOW;
+  }
+  if (E == 0 && i == 0 && (e_off[0] != 0 || P != 0)) f |= FLAG_EINVAL;
+  if (i < N && n_size[i] == 0) f |= FLAG_EINVAL;
+  if (f) atomicOr(flags, f);
+}
+
+__device__ __forceinline__ void push_run(RunLists rl, i64 start, u32 len) {
+  if (len < 2) return;
+  int c = len <= 64 ? 0 : (len <= LDS_CAP_U32 ? 1 : 2);
+  u32 slot = atomicAdd(&rl.cnt[c], 1u);
+  rl.start[c][slot] = start;
+  rl.len[c][slot] = len;
+  if (c == 2) atomicMax(&rl.cnt[3], len);
+}
+
+// One wave per hyperedge: copy pins, range check, detect unsorted runs.  A
+// hyperedge whose runs are strictly ascending is also checked for src/dst
+// overlap here; the others are queued for sorting and checked afterwards.
+__global__ __launch_bounds__(256) void k_edges_canon(u32 N, u32 E, const i64 *e_off,
+                                                     const u32 *e_nsrc, const u32 *pins_in,
+                                                     u32 *pins_out, u32 *bad_edges, RunLists rl,
+                                                     u32 *flags) {
+  const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
+  const u32 l = lane_id();
+  for (u32 e = blockIdx.x * (blockDim.x / WAVE) + wave_id(); e < E; e += nwaves) {
+    i64 a = e_off[e], b = e_off[e + 1];
+    u32 ns = e_nsrc[e];
+    u32 len = (u32)(b - a);
+    bool unsorted = false, badpin = false;
+    for (u32 i = l; i < len; i += WAVE) {
+      u32 v = pins_in[a + i];
+      pins_out[a + i] = v;
+      if (v >= N) badpin = true;
+      if (i != 0 && i != ns && pins_in[a + i - 1] >= v) unsorted = true;
+    }
+    badpin = __any(badpin);
+    unsorted = __any(unsorted);
+    if (badpin) {
+      if (l == 0) atomicOr(flags, FLAG_EINVAL);
+      continue;
+    }
+    if (unsorted) {
+      if (l == 0) {
+        u32 slot = atomicAdd(&rl.cnt[4], 1u);
+        bad_edges[slot] = e;
+        push_run(rl, a, ns);
+        push_run(rl, a + ns, len - ns);
+      }
+      continue;
+    }
+    bool overlap = false;
+    for (u32 i = l; i < ns; i += WAVE) {
+      u32 v = pins_in[a + i];
+      i64 p = lower_bound_i(pins_in, a + ns, b, v);
+      if (p < b && pins_in[p] == v) overlap = true;
+    }
+    if (__any(overlap) && l == 0) atomicOr(flags, FLAG_EINVAL);
+  }
+}
+
+// Re-check queued hyperedges after sorting: duplicates and src/dst overlap.
+__global__ __launch_bounds__(256) void k_edges_check(const i64 *e_off, const u32 *e_nsrc,
+                                                     const u32 *pins, const u32 *list, u32 count,
+                                                     u32 *flags) {
+  const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
+  const u32 l = lane_id();
+  for (u32 w = blockIdx.x * (blockDim.x / WAVE) + wave_id(); w < count; w += nwaves) {
+    u32 e = list[w];
+    i64 a = e_off[e], b = e_off[e + 1];
+    u32 ns = e_nsrc[e];
+    u32 len = (u32)(b - a);
+    bool bad = false;
+    for (u32 i = l; i < len; i += WAVE) {
+      u32 v = pins[a + i];
+      if (i != 0 && i != ns && pins[a + i - 1] == v) bad = true;
+      if (i < ns) {
+        i64 p = lower_bound_i(pins, a + ns, b, v);
+        if (p < b && pins[p] == v) bad = true;
+      }
+    }
+    if (__any(bad) && l == 0) atomicOr(flags, FLAG_EINVAL);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// in-place run sorting, three length classes
+
+__global__ __launch_bounds__(256) void k_runs_wave(u32 *data, const i64 *start, const u32 *len,
+                                                   const u32 *cnt) {
+  const u32 n = *cnt;
+  const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
+  const u32 l = lane_id();
+  for (u32 r = blockIdx.x * (blockDim.x / WAVE) + wave_id(); r < n; r += nwaves) {
+    i64 s = start[r];
+    u32 m = len[r];
+    u32 v = l < m ? data[s + l] : NONE32;
+    v = wave_sort64(v);
+    if (l < m) data[s + l] = v;
+  }
+}
+
+template <int BLOCK, int CAP>
+__global__ __launch_bounds__(BLOCK) void k_runs_lds(u32 *data, const i64 *start, const u32 *len,
+                                                    const u32 *cnt) {
+  __shared__ u32 s[CAP];
+  const u32 n = *cnt;
+  for (u32 r = blockIdx.x; r < n; r += gridDim.x) {
+    i64 st = start[r];
+    u32 m = len[r];
+    u32 p = next_pow2(m);
+    for (u32 i = threadIdx.x; i < p; i += BLOCK) s[i] = i < m ? data[st + i] : NONE32;
+    __syncthreads();
+    lds_bitonic<BLOCK>(s, p);
+    for (u32 i = threadIdx.x; i < m; i += BLOCK) data[st + i] = s[i];
+    __syncthreads();
+  }
+}
+
+template <int BLOCK, int CAP>
+__global__ __launch_bounds__(BLOCK) void k_runs_global(u32 *data, const i64 *start,
+                                                       const u32 *len, const u32 *cnt,
+                                                       u32 *scratch, u64 per_wg) {
+  __shared__ u32 s[CAP];
+  const u32 n = *cnt;
+  u32 *tmp = scratch + (u64)blockIdx.x * per_wg;
+  for (u32 r = blockIdx.x; r < n; r += gridDim.x) {
+    i64 st = start[r];
+    u32 m = len[r];
+    u32 *res = wg_sort_global<BLOCK, CAP>(data + st, tmp, (u64)m, s);
+    if (res != data + st)
+      for (u32 i = threadIdx.x; i < m; i += BLOCK) data[st + i] = res[i];
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// incidence: degrees, feasibility, scatter, per-node runs
+__global__ __launch_bounds__(256) void k_degrees(u32 E, const i64 *e_off, const u32 *e_nsrc,
+                                                 const u32 *pins, u32 *indeg, u32 *outdeg) {
+  const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
+  const u32 l = lane_id();
+  for (u32 e = blockIdx.x * (blockDim.x / WAVE) + wave_id(); e < E; e += nwaves) {
+    i64 a = e_off[e], b = e_off[e + 1];
+    u32 ns = e_nsrc[e];
+    for (u32 i = l; i < (u32)(b - a); i += WAVE) {
+      u32 v = pins[a + i];
+      atomicAdd(i < ns ? &outdeg[v] : &indeg[v], 1u);
+    }
+  }
+}
+
+__global__ void k_node_feas(u32 N, const u32 *indeg, const u32 *outdeg, const u32 *n_size,
+                            u64 omega, u32 delta, u32 *deg, u32 *n_nin, u32 *flags) {
+  u32 n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  u32 di = indeg[n], dout = outdeg[n];
+  deg[n] = di + dout;
+  n_nin[n] = di;
+  if ((u64)n_size[n] > omega || di > delta) atomicOr(flags, FLAG_EINFEASIBLE);
+}
+
+__global__ __launch_bounds__(256) void k_scatter(u32 E, const i64 *e_off, const u32 *e_nsrc,
+                                                 const u32 *pins, const i64 *n_off,
+                                                 const u32 *n_nin, u32 *cur_in, u32 *cur_out,
+                                                 u32 *n_inc) {
+  const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
+  const u32 l = lane_id();
+  for (u32 e = blockIdx.x * (blockDim.x / WAVE) + wave_id(); e < E; e += nwaves) {
+    i64 a = e_off[e], b = e_off[e + 1];
+    u32 ns = e_nsrc[e];
+    for (u32 i = l; i < (u32)(b - a); i += WAVE) {
+      u32 v = pins[a + i];
+      i64 pos;
+      if (i < ns) pos = n_off[v] + n_nin[v] + atomicAdd(&cur_out[v], 1u);
+      else pos = n_off[v] + atomicAdd(&cur_in[v], 1u);
+      n_inc[pos] = e;
+    }
+  }
+}
+
+__global__ void k_node_runs(u32 N, const i64 *n_off, const u32 *n_nin, RunLists rl) {
+  u32 n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  i64 a = n_off[n], b = n_off[n + 1];
+  u32 ni = n_nin[n];
+  push_run(rl, a, ni);
+  push_run(rl, a + ni, (u32)(b - a - ni));
+}
+
+// ---------------------------------------------------------------------------
+// neighbourhoods: W_n = sum_{e in I(n)} |e| decides the class; the oversize
+// bound of |N(n)| is W_n - |I(n)| (n is a pin of each of its hyperedges).
+__global__ void k_nb_classify(u32 N, const i64 *e_off, const i64 *n_off, const u32 *n_inc,
+                              u32 *bound, NbLists nl) {
+  u32 n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  i64 a = n_off[n], b = n_off[n + 1];
+  u64 w = 0;
+  for (i64 j = a; j < b; ++j) {
+    u32 e = n_inc[j];
+    w += (u64)(e_off[e + 1] - e_off[e]);
+  }
+  u64 bnd = w - (u64)(b - a);
+  if (w > 0xFFFFFFFFull) {  // per-node work must fit 32 bits
+    atomicOr(nl.cnt + 7, 1u);
+    bnd = 0;
+  }
+  bound[n] = (u32)bnd;
+  if (bnd == 0) return;  // isolated node: empty N(n)
+  int c = w <= 64 ? 0 : (w <= LDS_CAP_U32 ? 1 : 2);
+  u32 slot = atomicAdd(&nl.cnt[c], 1u);
+  nl.list[c][slot] = n;
+  if (c == 2) atomicMax(&nl.cnt[3], (u32)w);
+}
+
+// wave per node, W_n <= 64: gather into lanes, sort, unique, drop n
+__global__ __launch_bounds__(256) void k_nb_wave(const i64 *e_off, const u32 *pins,
+                                                 const i64 *n_off, const u32 *n_inc,
+                                                 const i64 *ooff, u32 *obuf, u32 *count,
+                                                 const u32 *list, const u32 *cnt) {
+  const u32 total = *cnt;
+  const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
+  const u32 l = lane_id();
+  for (u32 w = blockIdx.x * (blockDim.x / WAVE) + wave_id(); w < total; w += nwaves) {
+    u32 n = list[w];
+    i64 a = n_off[n], b = n_off[n + 1];
+    u32 deg = (u32)(b - a);
+    // lane j < deg holds hyperedge j's segment
+    i64 es = 0;
+    u32 elen = 0;
+    if (l < deg) {
+      u32 e = n_inc[a + l];
+      es = e_off[e];
+      elen = (u32)(e_off[e + 1] - es);
+    }
+    u32 pre = wave_incl_scan(elen) - elen;
+    u32 v = NONE32;
+    for (u32 j = 0; j < deg; ++j) {
+      u32 pj = __shfl(pre, j, WAVE);
+      u32 lj = __shfl(elen, j, WAVE);
+      i64 sj = __shfl(es, j, WAVE);
+      if (l >= pj && l < pj + lj) v = pins[sj + (l - pj)];
+    }
+    v = wave_sort64(v);
+    u32 prev = __shfl_up(v, 1, WAVE);
+    bool keep = v != NONE32 && v != n && (l == 0 || prev != v);
+    u64 mask = __ballot(keep);
+    u32 pos = __popcll(mask & ((1ull << l) - 1));
+    if (keep) obuf[ooff[n] + pos] = v;
+    if (l == 0) count[n] = (u32)__popcll(mask);
+  }
+}
+
+// Gather the pins of I(n) (all of them, n included) into dst, which has room
+// for W_n keys.  Hyperedges are taken BLOCK at a time: each thread loads one
+// segment descriptor, a workgroup scan places them, and the flattened copy
+// finds its segment by binary search over the prefix.
+template <int BLOCK>
+__device__ u64 gather_pins(const i64 *e_off, const u32 *pins, const u32 *n_inc, i64 a, i64 b,
+                           u32 *dst, i64 *s_start, u32 *s_pre, u32 *s_red) {
+  u64 base = 0;
+  for (i64 c0 = a; c0 < b; c0 += BLOCK) {
+    u32 ne = (u32)((b - c0) < BLOCK ? (b - c0) : BLOCK);
+    u32 len = 0;
+    if (threadIdx.x < ne) {
+      u32 e = n_inc[c0 + threadIdx.x];
+      i64 s = e_off[e];
+      len = (u32)(e_off[e + 1] - s);
+      s_start[threadIdx.x] = s;
+    }
+    u32 tot;
+    u32 off = wg_excl_scan<BLOCK>(len, s_red, &tot);
+    if (threadIdx.x < ne) s_pre[threadIdx.x] = off;
+    if (threadIdx.x == 0) s_pre[ne] = tot;
+    __syncthreads();
+    for (u32 i = threadIdx.x; i < tot; i += BLOCK) {
+      u32 r = run_of(s_pre, ne + 1, i);
+      dst[base + i] = pins[s_start[r] + (i - s_pre[r])];
+    }
+    base += tot;
+    __syncthreads();
+  }
+  return base;
+}
+
+// Write the unique keys of sorted src[0,m) other than `skip` to out; returns
+// the count (all threads).
+template <int BLOCK>
+__device__ u32 unique_out(const u32 *src, u64 m, u32 skip, u32 *out, u32 *s_red) {
+  u32 run = 0;
+  for (u64 c0 = 0; c0 < m; c0 += BLOCK) {
+    u64 i = c0 + threadIdx.x;
+    bool keep = false;
+    u32 v = 0;
+    if (i < m) {
+      v = src[i];
+      keep = v != skip && v != NONE32 && (i == 0 || src[i - 1] != v);
+    }
+    u32 tot;
+    u32 off = wg_excl_scan<BLOCK>((u32)keep, s_red, &tot);
+    if (keep) out[run + off] = v;
+    run += tot;
+  }
+  return run;
+}
+
+template <int BLOCK, int CAP>
+__global__ __launch_bounds__(BLOCK) void k_nb_lds(const i64 *e_off, const u32 *pins,
+                                                  const i64 *n_off, const u32 *n_inc,
+                                                  const i64 *ooff, u32 *obuf, u32 *count,
+                                                  const u32 *list, const u32 *cnt) {
+  __shared__ u32 s[CAP];
+  __shared__ i64 s_start[BLOCK];
+  __shared__ u32 s_pre[BLOCK + 1];
+  __shared__ u32 s_red[BLOCK / WAVE + 1];
+  const u32 total = *cnt;
+  for (u32 w = blockIdx.x; w < total; w += gridDim.x) {
+    u32 n = list[w];
+    i64 a = n_off[n], b = n_off[n + 1];
+    const u32 m = (u32)gather_pins<BLOCK>(e_off, pins, n_inc, a, b, s, s_start, s_pre, s_red);
+    u32 p = next_pow2(m);
+    for (u32 i = m + threadIdx.x; i < p; i += BLOCK) s[i] = NONE32;
+    __syncthreads();
+    lds_bitonic<BLOCK>(s, p);
+    u32 c = unique_out<BLOCK>(s, m, n, obuf + ooff[n], s_red);
+    if (threadIdx.x == 0) count[n] = c;
+    __syncthreads();
+  }
+}
+
+template <int BLOCK, int CAP>
+__global__ __launch_bounds__(BLOCK) void k_nb_global(const i64 *e_off, const u32 *pins,
+                                                     const i64 *n_off, const u32 *n_inc,
+                                                     const i64 *ooff, u32 *obuf, u32 *count,
+                                                     const u32 *list, const u32 *cnt,
+                                                     u32 *scratch, u64 per_wg) {
+  __shared__ u32 s[CAP];
+  __shared__ i64 s_start[BLOCK];
+  __shared__ u32 s_pre[BLOCK + 1];
+  __shared__ u32 s_red[BLOCK / WAVE + 1];
+  const u32 total = *cnt;
+  u32 *A = scratch + (u64)blockIdx.x * per_wg;
+  u32 *B = A + per_wg / 2;
+  for (u32 w = blockIdx.x; w < total; w += gridDim.x) {
+    u32 n = list[w];
+    i64 a = n_off[n], b = n_off[n + 1];
+    const u64 m = gather_pins<BLOCK>(e_off, pins, n_inc, a, b, A, s_start, s_pre, s_red);
+    u32 *res = wg_sort_global<BLOCK, CAP>(A, B, m, s);
+    u32 c = unique_out<BLOCK>(res, m, n, obuf + ooff[n], s_red);
+    if (threadIdx.x == 0) count[n] = c;
+    __syncthreads();
+  }
+}
+
+// copy each node's unique list from the oversize buffer to its final place
+__global__ __launch_bounds__(256) void k_nb_compact(u32 N, const i64 *ooff, const u32 *obuf,
+                                                    const i64 *nb_off, u32 *nb) {
+  const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
+  const u32 l = lane_id();
+  for (u32 n = blockIdx.x * (blockDim.x / WAVE) + wave_id(); n < N; n += nwaves) {
+    i64 s = ooff[n], d = nb_off[n];
+    u32 c = (u32)(nb_off[n + 1] - d);
+    for (u32 i = l; i < c; i += WAVE) nb[d + i] = obuf[s + i];
+  }
+}
+
+
+}  // namespace
+
+void launch_check_edges(chp_ctx *c, u32 N, u32 E, u64 P, const i64 *e_off, const u32 *e_nsrc,
+                        const u32 *e_w, const u32 *n_size) {
+  u64 n = E > N ? E : N;
+  CHP_LAUNCH(c, "check_edges", k_check_edges, grid_for(n ? n : 1, 256), 256, 0, N, E, P, e_off,
+             e_nsrc, e_w, n_size, c->flags);
+}
+
+void launch_edges_canon(chp_ctx *c, u32 N, u32 E, const i64 *e_off, const u32 *e_nsrc,
+                        const u32 *pins_in, u32 *pins_out, u32 *bad_edges, RunLists rl) {
+  if (E == 0) return;
+  CHP_LAUNCH(c, "edges_canon", k_edges_canon, waves_grid(E), 256, 0, N, E, e_off, e_nsrc, pins_in,
+             pins_out, bad_edges, rl, c->flags);
+}
+
+void launch_sort_runs(chp_ctx *c, u32 *data, RunLists rl, const u32 *host_cnt, u32 *scratch,
+                      u64 scratch_per_wg, u32 grid_big) {
+  if (host_cnt[0])
+    CHP_LAUNCH(c, "runs_wave", k_runs_wave, waves_grid(host_cnt[0]), 256, 0, data, rl.start[0],
+               rl.len[0], rl.cnt + 0);
+  if (host_cnt[1])
+    CHP_LAUNCH(c, "runs_lds", (k_runs_lds<256, LDS_CAP_U32>), host_cnt[1] > 8192 ? 8192 : host_cnt[1], 256, 0, data, rl.start[1], rl.len[1], rl.cnt + 1);
+  if (host_cnt[2])
+    CHP_LAUNCH(c, "runs_global", (k_runs_global<256, LDS_CAP_U32>), grid_big, 256, 0, data,
+               rl.start[2], rl.len[2], rl.cnt + 2, scratch, scratch_per_wg);
+}
+
+void launch_edges_check(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
+                        const u32 *list, u32 count) {
+  if (!count) return;
+  CHP_LAUNCH(c, "edges_check", k_edges_check, waves_grid(count), 256, 0, e_off, e_nsrc, pins,
+             list, count, c->flags);
+}
+
+void launch_degrees(chp_ctx *c, u32 E, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
+                    u32 *indeg, u32 *outdeg) {
+  if (E == 0) return;
+  CHP_LAUNCH(c, "degrees", k_degrees, waves_grid(E), 256, 0, E, e_off, e_nsrc, pins, indeg,
+             outdeg);
+}
+
+void launch_node_feas(chp_ctx *c, u32 N, const u32 *indeg, const u32 *outdeg, const u32 *n_size,
+                      u64 omega, u32 delta, u32 *deg, u32 *n_nin) {
+  if (N == 0) return;
+  CHP_LAUNCH(c, "node_feas", k_node_feas, grid_for(N, 256), 256, 0, N, indeg, outdeg, n_size,
+             omega, delta, deg, n_nin, c->flags);
+}
+
+void launch_scatter(chp_ctx *c, u32 E, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
+                    const i64 *n_off, const u32 *n_nin, u32 *cur_in, u32 *cur_out, u32 *n_inc) {
+  if (E == 0) return;
+  CHP_LAUNCH(c, "scatter", k_scatter, waves_grid(E), 256, 0, E, e_off, e_nsrc, pins, n_off, n_nin,
+             cur_in, cur_out, n_inc);
+}
+
+void launch_node_runs(chp_ctx *c, u32 N, const i64 *n_off, const u32 *n_nin, RunLists rl) {
+  if (N == 0) return;
+  CHP_LAUNCH(c, "node_runs", k_node_runs, grid_for(N, 256), 256, 0, N, n_off, n_nin, rl);
+}
+
+void launch_nb_classify(chp_ctx *c, u32 N, const i64 *e_off, const i64 *n_off, const u32 *n_inc,
+                        u32 *bound, NbLists nl) {
+  if (N == 0) return;
+  CHP_LAUNCH(c, "nb_classify", k_nb_classify, grid_for(N, 256), 256, 0, N, e_off, n_off, n_inc,
+             bound, nl);
+}
+
+void launch_nb_build(chp_ctx *c, u32 N, const i64 *e_off, const u32 *pins, const i64 *n_off,
+                     const u32 *n_inc, const i64 *ooff, u32 *obuf, u32 *count, NbLists nl,
+                     const u32 *host_cnt, u32 *scratch, u64 scratch_per_wg, u32 grid_big) {
+  if (host_cnt[0])
+    CHP_LAUNCH(c, "nb_wave", k_nb_wave, waves_grid(host_cnt[0]), 256, 0, e_off, pins, n_off,
+               n_inc, ooff, obuf, count, nl.list[0], nl.cnt + 0);
+  if (host_cnt[1])
+    CHP_LAUNCH(c, "nb_lds", (k_nb_lds<256, LDS_CAP_U32>), host_cnt[1] > 8192 ? 8192 : host_cnt[1],
+               256, 0, e_off, pins, n_off, n_inc, ooff, obuf, count, nl.list[1], nl.cnt + 1);
+  if (host_cnt[2])
+    CHP_LAUNCH(c, "nb_global", (k_nb_global<256, LDS_CAP_U32>), grid_big, 256, 0, e_off, pins,
+               n_off, n_inc, ooff, obuf, count, nl.list[2], nl.cnt + 2, scratch, scratch_per_wg);
+}
+
+void launch_nb_compact(chp_ctx *c, u32 N, const i64 *ooff, const u32 *obuf, const i64 *nb_off,
+                       u32 *nb) {
+  if (N == 0) return;
+  CHP_LAUNCH(c, "nb_compact", k_nb_compact, waves_grid(N), 256, 0, N, ooff, obuf, nb_off, nb);
+}

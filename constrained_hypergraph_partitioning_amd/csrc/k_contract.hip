@@ -1,0 +1,213 @@
+// Contraction of one level ("Hypergraph Partitioning on GPU with Distinct
+// Incident Hyperedges and Size Constraints", Sec. III and V-E).
+//
+// gamma(n) is the rank of min(n, match(n)) among cluster representatives
+// (an exclusive scan of "match(n) >= n").  A coarse hyperedge keeps the id and
+// weight of its fine hyperedge; its destinations are the distinct gamma(dst)
+// and its sources the distinct gamma(src) that are not destinations (Sec. V-E
+// drops such duplicates from the sources).  Per hyperedge this is one sort of
+// 64-bit keys (gamma << 1 | is_source): in each group of equal gamma the
+// first key tells whether some destination maps there.
+#include "dev.h"
+#include "kernels.h"
+
+namespace {
+
+__global__ void k_rep(u32 N, const u32 *match, u32 *is_rep, u32 *flags) {
+  u32 n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  u32 m = match[n];
+  bool ok = m < N && match[m] == n;
+  if (!ok) atomicOr(flags, FLAG_EINVAL);
+  is_rep[n] = (ok && m >= n) ? 1u : 0u;
+}
+
+__global__ void k_gamma(u32 N, const u32 *match, const i64 *rank, const u32 *n_size, u32 *gamma,
+                        u32 *c_size) {
+  u32 n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  u32 m = match[n];
+  u32 r = m < n ? m : n;
+  u32 g = (u32)rank[r];
+  gamma[n] = g;
+  if (r == n) c_size[g] = n_size[n] + (m != n ? n_size[m] : 0u);
+}
+
+__global__ void k_edge_classify(u32 E, const i64 *e_off, EdgeLists el) {
+  u32 e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  u64 len = (u64)(e_off[e + 1] - e_off[e]);
+  int c = len <= 64 ? 0 : (len <= LDS_CAP_U64 ? 1 : 2);
+  u32 slot = atomicAdd(&el.cnt[c], 1u);
+  el.list[c][slot] = e;
+  if (c == 2) atomicMax(&el.cnt[3], (u32)len);
+}
+
+
+// small hyperedges: one wave each, keys in registers
+__global__ __launch_bounds__(256) void k_econ_wave(const i64 *e_off, const u32 *e_nsrc,
+                                                   const u32 *pins, const u32 *gamma, u32 *opins,
+                                                   u32 *olen, u32 *onsrc, const u32 *list,
+                                                   const u32 *cnt) {
+  const u32 total = *cnt;
+  const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
+  const u32 l = lane_id();
+  const u64 lt = (1ull << l) - 1;
+  for (u32 w = blockIdx.x * (blockDim.x / WAVE) + wave_id(); w < total; w += nwaves) {
+    const u32 e = list[w];
+    const i64 a = e_off[e];
+    const u32 len = (u32)(e_off[e + 1] - a), ns = e_nsrc[e];
+    u64 key = ~0ull;
+    if (l < len) key = ((u64)gamma[pins[a + l]] << 1) | (l < ns ? 1u : 0u);
+    key = wave_sort64(key);
+    const u64 prev = __shfl_up(key, 1, WAVE);
+    const bool first = l < len && (l == 0 || (prev >> 1) != (key >> 1));
+    const u64 sm = __ballot(first && (key & 1));
+    const u64 dm = __ballot(first && !(key & 1));
+    const u32 nsp = (u32)__popcll(sm);
+    if (first) {
+      const u32 pos = (key & 1) ? (u32)__popcll(sm & lt) : nsp + (u32)__popcll(dm & lt);
+      opins[a + pos] = (u32)(key >> 1);
+    }
+    if (l == 0) {
+      olen[e] = nsp + (u32)__popcll(dm);
+      onsrc[e] = nsp;
+    }
+  }
+}
+
+// Split the sorted keys s[0,m) into distinct sources (first) and distinct
+// destinations; works on LDS or global keys.
+template <int BLOCK>
+__device__ void econ_emit(const u64 *s, u32 m, u32 *out, u32 *olen, u32 *onsrc, u32 e,
+                          u32 *s_red) {
+  u32 nsrc = 0, ndst = 0;
+  for (u32 c0 = 0; c0 < m; c0 += BLOCK) {
+    u32 i = c0 + threadIdx.x;
+    bool f = i < m && (i == 0 || (s[i - 1] >> 1) != (s[i] >> 1));
+    u32 ts, td;
+    wg_excl_scan<BLOCK>((u32)(f && (s[i < m ? i : 0] & 1)), s_red, &ts);
+    wg_excl_scan<BLOCK>((u32)(f && !(s[i < m ? i : 0] & 1)), s_red, &td);
+    nsrc += ts;
+    ndst += td;
+  }
+  u32 rs = 0, rd = 0;
+  for (u32 c0 = 0; c0 < m; c0 += BLOCK) {
+    u32 i = c0 + threadIdx.x;
+    u64 k = i < m ? s[i] : 0;
+    bool f = i < m && (i == 0 || (s[i - 1] >> 1) != (k >> 1));
+    bool fs = f && (k & 1), fd = f && !(k & 1);
+    u32 ts, td;
+    u32 os = wg_excl_scan<BLOCK>((u32)fs, s_red, &ts);
+    u32 od = wg_excl_scan<BLOCK>((u32)fd, s_red, &td);
+    if (fs) out[rs + os] = (u32)(k >> 1);
+    if (fd) out[nsrc + rd + od] = (u32)(k >> 1);
+    rs += ts;
+    rd += td;
+  }
+  if (threadIdx.x == 0) {
+    olen[e] = nsrc + ndst;
+    onsrc[e] = nsrc;
+  }
+}
+
+template <int BLOCK, int CAP>
+__global__ __launch_bounds__(BLOCK) void k_econ_lds(const i64 *e_off, const u32 *e_nsrc,
+                                                    const u32 *pins, const u32 *gamma, u32 *opins,
+                                                    u32 *olen, u32 *onsrc, const u32 *list,
+                                                    const u32 *cnt) {
+  __shared__ u64 s[CAP];
+  __shared__ u32 s_red[BLOCK / WAVE + 1];
+  const u32 total = *cnt;
+  for (u32 w = blockIdx.x; w < total; w += gridDim.x) {
+    const u32 e = list[w];
+    const i64 a = e_off[e];
+    const u32 len = (u32)(e_off[e + 1] - a), ns = e_nsrc[e];
+    const u32 p = next_pow2(len);
+    for (u32 i = threadIdx.x; i < p; i += BLOCK)
+      s[i] = i < len ? (((u64)gamma[pins[a + i]] << 1) | (i < ns ? 1u : 0u)) : ~0ull;
+    __syncthreads();
+    lds_bitonic<BLOCK>(s, p);
+    econ_emit<BLOCK>(s, len, opins + a, olen, onsrc, e, s_red);
+    __syncthreads();
+  }
+}
+
+template <int BLOCK, int CAP>
+__global__ __launch_bounds__(BLOCK) void k_econ_global(const i64 *e_off, const u32 *e_nsrc,
+                                                       const u32 *pins, const u32 *gamma,
+                                                       u32 *opins, u32 *olen, u32 *onsrc,
+                                                       const u32 *list, const u32 *cnt,
+                                                       u64 *scratch, u64 per_wg) {
+  __shared__ u64 s[CAP];
+  __shared__ u32 s_red[BLOCK / WAVE + 1];
+  const u32 total = *cnt;
+  u64 *A = scratch + (u64)blockIdx.x * per_wg;
+  u64 *B = A + per_wg / 2;
+  for (u32 w = blockIdx.x; w < total; w += gridDim.x) {
+    const u32 e = list[w];
+    const i64 a = e_off[e];
+    const u32 len = (u32)(e_off[e + 1] - a), ns = e_nsrc[e];
+    for (u32 i = threadIdx.x; i < len; i += BLOCK)
+      A[i] = ((u64)gamma[pins[a + i]] << 1) | (i < ns ? 1u : 0u);
+    __syncthreads();
+    u64 *res = wg_sort_global<BLOCK, CAP>(A, B, len, s);
+    econ_emit<BLOCK>(res, len, opins + a, olen, onsrc, e, s_red);
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void k_pins_compact(u32 E, const i64 *src_off,
+                                                      const u32 *src, const i64 *dst_off,
+                                                      u32 *dst) {
+  const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
+  const u32 l = lane_id();
+  for (u32 e = blockIdx.x * (blockDim.x / WAVE) + wave_id(); e < E; e += nwaves) {
+    i64 s = src_off[e], d = dst_off[e];
+    u32 c = (u32)(dst_off[e + 1] - d);
+    for (u32 i = l; i < c; i += WAVE) dst[d + i] = src[s + i];
+  }
+}
+
+
+}  // namespace
+
+void launch_rep(chp_ctx *c, u32 N, const u32 *match, u32 *is_rep) {
+  if (N == 0) return;
+  CHP_LAUNCH(c, "rep", k_rep, grid_for(N, 256), 256, 0, N, match, is_rep, c->flags);
+}
+
+void launch_gamma(chp_ctx *c, u32 N, const u32 *match, const i64 *rank, const u32 *n_size,
+                  u32 *gamma, u32 *c_size) {
+  if (N == 0) return;
+  CHP_LAUNCH(c, "gamma", k_gamma, grid_for(N, 256), 256, 0, N, match, rank, n_size, gamma,
+             c_size);
+}
+
+void launch_edge_classify(chp_ctx *c, u32 E, const i64 *e_off, EdgeLists el) {
+  if (E == 0) return;
+  CHP_LAUNCH(c, "edge_classify", k_edge_classify, grid_for(E, 256), 256, 0, E, e_off, el);
+}
+
+void launch_edge_contract(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
+                          const u32 *gamma, u32 *opins, u32 *olen, u32 *onsrc, EdgeLists el,
+                          const u32 *host_cnt, u64 *scratch, u64 per_wg, u32 grid_big) {
+  if (host_cnt[0])
+    CHP_LAUNCH(c, "econ_wave", k_econ_wave, waves_grid(host_cnt[0]), 256, 0, e_off, e_nsrc, pins,
+               gamma, opins, olen, onsrc, (const u32 *)el.list[0], (const u32 *)el.cnt + 0);
+  if (host_cnt[1])
+    CHP_LAUNCH(c, "econ_lds", (k_econ_lds<256, LDS_CAP_U64>),
+               host_cnt[1] > 8192 ? 8192 : host_cnt[1], 256, 0, e_off, e_nsrc, pins, gamma, opins,
+               olen, onsrc, (const u32 *)el.list[1], (const u32 *)el.cnt + 1);
+  if (host_cnt[2])
+    CHP_LAUNCH(c, "econ_global", (k_econ_global<256, LDS_CAP_U64>), grid_big, 256, 0, e_off,
+               e_nsrc, pins, gamma, opins, olen, onsrc, (const u32 *)el.list[2],
+               (const u32 *)el.cnt + 2, scratch, per_wg);
+}
+
+void launch_pins_compact(chp_ctx *c, u32 E, const i64 *src_off, const u32 *src,
+                         const i64 *dst_off, u32 *dst) {
+  if (E == 0) return;
+  CHP_LAUNCH(c, "pins_compact", k_pins_compact, waves_grid(E), 256, 0, E, src_off, src, dst_off,
+             dst);
+}

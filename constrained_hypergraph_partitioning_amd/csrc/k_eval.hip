@@ -1,0 +1,196 @@
+// Partition evaluation ("Hypergraph Partitioning on GPU with Distinct
+// Incident Hyperedges and Size Constraints": connectivity, Eq. 1; cut-net,
+// Eq. 16; the per-partition size and distinct-inbound counts of Sec. II-B).
+//
+// Per hyperedge one sort of 64-bit keys (rho << 1 | is_source): the number
+// of groups of equal rho is lambda(e), and a group whose first key is a
+// destination marks a partition that e enters (it counts once towards that
+// partition's inbound set).
+#include "dev.h"
+#include "kernels.h"
+
+namespace {
+
+__global__ void k_eval_nodes(u32 N, const u32 *rho, u32 k, const u32 *n_size, u64 *part_size,
+                             u32 *part_cnt, u32 *flags) {
+  u32 n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  u32 p = rho[n];
+  if (p >= k) {
+    atomicOr(flags, FLAG_EINVAL);
+    return;
+  }
+  atomicAdd((unsigned long long *)&part_size[p], (unsigned long long)n_size[n]);
+  atomicAdd(&part_cnt[p], 1u);
+}
+
+__device__ __forceinline__ u64 eval_key(const u32 *rho, u32 k, u32 pin, bool src, u32 *flags) {
+  u32 p = rho[pin];
+  if (p >= k) {
+    atomicOr(flags, FLAG_EINVAL);
+    p = 0;
+  }
+  return ((u64)p << 1) | (src ? 1u : 0u);
+}
+
+
+__device__ __forceinline__ void flush_sums(u64 conn, u64 cut, u64 lam, u64 *summary) {
+  if (conn) atomicAdd((unsigned long long *)&summary[0], (unsigned long long)conn);
+  if (cut) atomicAdd((unsigned long long *)&summary[1], (unsigned long long)cut);
+  if (lam) atomicAdd((unsigned long long *)&summary[7], (unsigned long long)lam);
+}
+
+__global__ __launch_bounds__(256) void k_eval_wave(const i64 *e_off, const u32 *e_nsrc,
+                                                   const u32 *pins, const u32 *e_w,
+                                                   const u32 *rho, u32 k, u32 *part_inb,
+                                                   u64 *summary, const u32 *list, const u32 *cnt,
+                                                   u32 *flags) {
+  const u32 total = *cnt;
+  const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
+  const u32 l = lane_id();
+  u64 conn = 0, cut = 0, lams = 0;
+  for (u32 w = blockIdx.x * (blockDim.x / WAVE) + wave_id(); w < total; w += nwaves) {
+    const u32 e = list[w];
+    const i64 a = e_off[e];
+    const u32 len = (u32)(e_off[e + 1] - a), ns = e_nsrc[e];
+    u64 key = ~0ull;
+    if (l < len) key = eval_key(rho, k, pins[a + l], l < ns, flags);
+    key = wave_sort64(key);
+    const u64 prev = __shfl_up(key, 1, WAVE);
+    const bool first = l < len && (l == 0 || (prev >> 1) != (key >> 1));
+    if (first && !(key & 1)) atomicAdd(&part_inb[key >> 1], 1u);
+    const u64 lam = (u64)__popcll(__ballot(first));
+    if (l == 0) {
+      const u64 we = e_w[e];
+      conn += we * (lam - 1);
+      cut += lam > 1 ? we : 0;
+      lams += lam;
+    }
+  }
+  if (l == 0) flush_sums(conn, cut, lams, summary);
+}
+
+// lambda and inbound marks from sorted keys s[0,m); returns lambda (all threads)
+template <int BLOCK>
+__device__ u32 eval_groups(const u64 *s, u32 m, u32 *part_inb, u32 *s_red) {
+  u32 lam = 0;
+  for (u32 c0 = 0; c0 < m; c0 += BLOCK) {
+    u32 i = c0 + threadIdx.x;
+    bool f = false;
+    if (i < m) {
+      u64 key = s[i];
+      f = i == 0 || (s[i - 1] >> 1) != (key >> 1);
+      if (f && !(key & 1)) atomicAdd(&part_inb[key >> 1], 1u);
+    }
+    lam += wg_sum<BLOCK>((u32)f, s_red);
+  }
+  return lam;
+}
+
+template <int BLOCK, int CAP>
+__global__ __launch_bounds__(BLOCK) void k_eval_lds(const i64 *e_off, const u32 *e_nsrc,
+                                                    const u32 *pins, const u32 *e_w,
+                                                    const u32 *rho, u32 k, u32 *part_inb,
+                                                    u64 *summary, const u32 *list, const u32 *cnt,
+                                                    u32 *flags) {
+  __shared__ u64 s[CAP];
+  __shared__ u32 s_red[BLOCK / WAVE + 1];
+  const u32 total = *cnt;
+  u64 conn = 0, cut = 0, lams = 0;
+  for (u32 w = blockIdx.x; w < total; w += gridDim.x) {
+    const u32 e = list[w];
+    const i64 a = e_off[e];
+    const u32 len = (u32)(e_off[e + 1] - a), ns = e_nsrc[e];
+    const u32 p = next_pow2(len);
+    for (u32 i = threadIdx.x; i < p; i += BLOCK)
+      s[i] = i < len ? eval_key(rho, k, pins[a + i], i < ns, flags) : ~0ull;
+    __syncthreads();
+    lds_bitonic<BLOCK>(s, p);
+    const u64 lam = eval_groups<BLOCK>(s, len, part_inb, s_red);
+    const u64 we = e_w[e];
+    conn += we * (lam - 1);
+    cut += lam > 1 ? we : 0;
+    lams += lam;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) flush_sums(conn, cut, lams, summary);
+}
+
+template <int BLOCK, int CAP>
+__global__ __launch_bounds__(BLOCK) void k_eval_global(const i64 *e_off, const u32 *e_nsrc,
+                                                       const u32 *pins, const u32 *e_w,
+                                                       const u32 *rho, u32 k, u32 *part_inb,
+                                                       u64 *summary, const u32 *list,
+                                                       const u32 *cnt, u32 *flags, u64 *scratch,
+                                                       u64 per_wg) {
+  __shared__ u64 s[CAP];
+  __shared__ u32 s_red[BLOCK / WAVE + 1];
+  const u32 total = *cnt;
+  u64 *A = scratch + (u64)blockIdx.x * per_wg;
+  u64 *B = A + per_wg / 2;
+  u64 conn = 0, cut = 0, lams = 0;
+  for (u32 w = blockIdx.x; w < total; w += gridDim.x) {
+    const u32 e = list[w];
+    const i64 a = e_off[e];
+    const u32 len = (u32)(e_off[e + 1] - a), ns = e_nsrc[e];
+    for (u32 i = threadIdx.x; i < len; i += BLOCK)
+      A[i] = eval_key(rho, k, pins[a + i], i < ns, flags);
+    __syncthreads();
+    u64 *res = wg_sort_global<BLOCK, CAP>(A, B, len, s);
+    const u64 lam = eval_groups<BLOCK>(res, len, part_inb, s_red);
+    const u64 we = e_w[e];
+    conn += we * (lam - 1);
+    cut += lam > 1 ? we : 0;
+    lams += lam;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) flush_sums(conn, cut, lams, summary);
+}
+
+__global__ void k_eval_parts(u32 k, const u64 *part_size, const u32 *part_inb,
+                             const u32 *part_cnt, u64 omega, u32 delta, u64 *summary) {
+  u32 p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= k) return;
+  u64 s = part_size[p];
+  u32 in = part_inb[p];
+  if (s > omega) atomicAdd((unsigned long long *)&summary[2], 1ull);
+  if (in > delta) atomicAdd((unsigned long long *)&summary[3], 1ull);
+  if (part_cnt[p] == 0) atomicAdd((unsigned long long *)&summary[4], 1ull);
+  atomicMax((unsigned long long *)&summary[5], (unsigned long long)s);
+  atomicMax((unsigned long long *)&summary[6], (unsigned long long)in);
+}
+
+
+}  // namespace
+
+void launch_eval_nodes(chp_ctx *c, u32 N, const u32 *rho, u32 k, const u32 *n_size,
+                       u64 *part_size, u32 *part_cnt) {
+  if (N == 0) return;
+  CHP_LAUNCH(c, "eval_nodes", k_eval_nodes, grid_for(N, 256), 256, 0, N, rho, k, n_size,
+             part_size, part_cnt, c->flags);
+}
+
+void launch_eval_edges(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
+                       const u32 *e_w, const u32 *rho, u32 k, u32 *part_inb, u64 *summary,
+                       EdgeLists el, const u32 *host_cnt, u64 *scratch, u64 per_wg,
+                       u32 grid_big) {
+  if (host_cnt[0])
+    CHP_LAUNCH(c, "eval_wave", k_eval_wave, waves_grid(host_cnt[0]), 256, 0, e_off, e_nsrc, pins,
+               e_w, rho, k, part_inb, summary, (const u32 *)el.list[0], (const u32 *)el.cnt + 0,
+               c->flags);
+  if (host_cnt[1])
+    CHP_LAUNCH(c, "eval_lds", (k_eval_lds<256, LDS_CAP_U64>),
+               host_cnt[1] > 8192 ? 8192 : host_cnt[1], 256, 0, e_off, e_nsrc, pins, e_w, rho, k,
+               part_inb, summary, (const u32 *)el.list[1], (const u32 *)el.cnt + 1, c->flags);
+  if (host_cnt[2])
+    CHP_LAUNCH(c, "eval_global", (k_eval_global<256, LDS_CAP_U64>), grid_big, 256, 0, e_off,
+               e_nsrc, pins, e_w, rho, k, part_inb, summary, (const u32 *)el.list[2],
+               (const u32 *)el.cnt + 2, c->flags, scratch, per_wg);
+}
+
+void launch_eval_parts(chp_ctx *c, u32 k, const u64 *part_size, const u32 *part_inb,
+                       const u32 *part_cnt, u64 omega, u32 delta, u64 *summary) {
+  if (k == 0) return;
+  CHP_LAUNCH(c, "eval_parts", k_eval_parts, grid_for(k, 256), 256, 0, k, part_size, part_inb,
+             part_cnt, omega, delta, summary);
+}

@@ -1,0 +1,122 @@
+// Host-side launchers of the kernels (one translation unit per step).
+#pragma once
+#include "common.h"
+
+constexpr u32 LDS_CAP_U32 = 8192;   // u32 keys one workgroup sorts in LDS
+constexpr u32 LDS_CAP_U64 = 8192;   // u64 keys one workgroup sorts in LDS
+constexpr u32 RATE_SMALL_CAP = 512; // |N(n)| handled by the one-wave rating kernel
+
+// Runs to sort in place, bucketed by length: class 0 (<= 64 keys, one wave
+// each), class 1 (<= LDS_CAP_U32 keys, one workgroup in LDS), class 2
+// (longer: one workgroup, global merge sort).  cnt[0..2] = class counts,
+// cnt[3] = longest class-2 run, cnt[4] = number of queued hyperedges.
+struct RunLists {
+  i64 *start[3];
+  u32 *len[3];
+  u32 *cnt;  // device [8]
+};
+
+// Node work lists by class; cnt[0..2] counts, cnt[3] = max work of class 2.
+struct NbLists {
+  u32 *list[3];
+  u32 *cnt;  // device [8]
+};
+
+// Hyperedge work lists by |e|: <= 64 (wave), <= LDS_CAP_U64 (workgroup LDS),
+// longer (workgroup, global merge sort).  cnt[3] = longest class-2 edge.
+struct EdgeLists {
+  u32 *list[3];
+  u32 *cnt;  // device [8]
+};
+
+// ---- k_build.hip : canonical edges, incidence, neighbourhoods -------------
+void launch_check_edges(chp_ctx *c, u32 N, u32 E, u64 P, const i64 *e_off, const u32 *e_nsrc,
+                        const u32 *e_w, const u32 *n_size);
+void launch_edges_canon(chp_ctx *c, u32 N, u32 E, const i64 *e_off, const u32 *e_nsrc,
+                        const u32 *pins_in, u32 *pins_out, u32 *bad_edges, RunLists rl);
+void launch_sort_runs(chp_ctx *c, u32 *data, RunLists rl, const u32 *host_cnt, u32 *scratch,
+                      u64 scratch_per_wg, u32 grid_big);
+void launch_edges_check(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
+                        const u32 *list, u32 count);
+void launch_degrees(chp_ctx *c, u32 E, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
+                    u32 *indeg, u32 *outdeg);
+void launch_node_feas(chp_ctx *c, u32 N, const u32 *indeg, const u32 *outdeg, const u32 *n_size,
+                      u64 omega, u32 delta, u32 *deg, u32 *n_nin);
+void launch_scatter(chp_ctx *c, u32 E, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
+                    const i64 *n_off, const u32 *n_nin, u32 *cur_in, u32 *cur_out, u32 *n_inc);
+void launch_node_runs(chp_ctx *c, u32 N, const i64 *n_off, const u32 *n_nin, RunLists rl);
+void launch_nb_classify(chp_ctx *c, u32 N, const i64 *e_off, const i64 *n_off, const u32 *n_inc,
+                        u32 *bound, NbLists nl);
+void launch_nb_build(chp_ctx *c, u32 N, const i64 *e_off, const u32 *pins, const i64 *n_off,
+                     const u32 *n_inc, const i64 *ooff, u32 *obuf, u32 *count, NbLists nl,
+                     const u32 *host_cnt, u32 *scratch, u64 scratch_per_wg, u32 grid_big);
+void launch_nb_compact(chp_ctx *c, u32 N, const i64 *ooff, const u32 *obuf, const i64 *nb_off,
+                       u32 *nb);
+
+// ---- k_rate.hip : terms, noise cap, rating, handshake ---------------------
+// capinfo (device u64[4]): cap, d = cap + 1, magic = floor((2^64-1)/d), 0
+u32 terms_partials(u32 E);
+void launch_terms(chp_ctx *c, u32 E, const i64 *e_off, const u32 *e_w, u64 *t, u64 *partials,
+                  u32 nparts, u64 *capinfo);
+struct RateArgs {
+  u32 N;
+  const i64 *e_off;
+  const u32 *e_nsrc;
+  const u32 *e_pins;
+  const u64 *t;
+  const i64 *n_off;
+  const u32 *n_nin;
+  const u32 *n_inc;
+  const u32 *n_size;
+  const i64 *nb_off;
+  const u32 *nb;
+  const u64 *capinfo;
+  u64 omega;
+  u32 delta;
+  u32 noise_on;
+  u64 seed;
+  u32 *target;
+  u64 *score;
+  u32 *flags;
+};
+void launch_rate_classify(chp_ctx *c, u32 N, const i64 *nb_off, NbLists nl, u32 *target,
+                          u64 *score);
+void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, const u32 *host_cnt);
+
+struct MatchScratch {
+  u64 *bscore;  // [N] zeroed
+  u32 *bid;     // [N] filled with NONE
+  uint8_t *tk;  // [N]
+  u32 *p0, *p1; // [N] pointer-jumping buffers (fallback only)
+  uint8_t *x0, *x1;
+};
+void launch_match(chp_ctx *c, u32 N, const u32 *target, const u64 *score, MatchScratch ms,
+                  u32 *match, u32 *npairs);
+void launch_match_jump(chp_ctx *c, u32 N, const u32 *target, MatchScratch ms);
+void launch_match_write(chp_ctx *c, u32 N, const u32 *target, MatchScratch ms, u32 *match,
+                        u32 *npairs);
+
+// ---- k_contract.hip --------------------------------------------------------
+void launch_rep(chp_ctx *c, u32 N, const u32 *match, u32 *is_rep);
+void launch_gamma(chp_ctx *c, u32 N, const u32 *match, const i64 *rank, const u32 *n_size,
+                  u32 *gamma, u32 *c_size);
+void launch_edge_classify(chp_ctx *c, u32 E, const i64 *e_off, EdgeLists el);
+void launch_edge_contract(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
+                          const u32 *gamma, u32 *opins, u32 *olen, u32 *onsrc, EdgeLists el,
+                          const u32 *host_cnt, u64 *scratch, u64 per_wg, u32 grid_big);
+void launch_pins_compact(chp_ctx *c, u32 E, const i64 *src_off, const u32 *src,
+                         const i64 *dst_off, u32 *dst);
+
+// ---- k_eval.hip --------------------------------------------------------------
+void launch_eval_nodes(chp_ctx *c, u32 N, const u32 *rho, u32 k, const u32 *n_size,
+                       u64 *part_size, u32 *part_cnt);
+void launch_eval_edges(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
+                       const u32 *e_w, const u32 *rho, u32 k, u32 *part_inb, u64 *summary,
+                       EdgeLists el, const u32 *host_cnt, u64 *scratch, u64 per_wg,
+                       u32 grid_big);
+void launch_eval_parts(chp_ctx *c, u32 k, const u64 *part_size, const u32 *part_inb,
+                       const u32 *part_cnt, u64 omega, u32 delta, u64 *summary);
+
+// ---- small device fills (api.hip) -------------------------------------------
+void launch_fill_u32(chp_ctx *c, u32 *p, u64 n, u32 v);
+void launch_fill_u64(chp_ctx *c, u64 *p, u64 n, u64 v);

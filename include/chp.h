@@ -1,0 +1,200 @@
+/*
+ * chp.h -- C ABI of the constrained hypergraph coarsening library (gfx950).
+ *
+ * One coarsening level of the multi-level partitioner in
+ *   [HP]  Ronzani & Silvano, "Hypergraph Partitioning on GPU with Distinct
+ *         Incident Hyperedges and Size Constraints" (TPDS submission), and
+ *   [IC]  Ronzani & Silvano, "Incidence Constraints in Hypergraph Partitioning
+ *         on GPU" (AsHES 2026 prototype),
+ * plus the evaluation of a partition, under the two hard limits of [HP]
+ * Sec. II-B: a partition holds at most Omega node weight and at most Delta
+ * distinct inbound hyperedges.
+ *
+ * Conventions shared by every call
+ *  - Ids are uint32; 0xFFFFFFFF (CHP_NONE) means "none".  Offsets are int64.
+ *    Hyperedge weights and node sizes are uint32.  Ratings are uint64 fixed
+ *    point with 40 fractional bits (eta_fx = eta * 2^40, rounded down per
+ *    hyperedge term).
+ *  - Every array named in a struct or argument is DEVICE memory of the
+ *    context's GPU unless its name ends in _host.
+ *  - All work is enqueued on the HIP stream given to chp_create.  A call that
+ *    returns a host value or must size an allocation synchronises that stream
+ *    before it returns; the others return as soon as the work is enqueued.
+ *  - Every segment of every CSR is sorted ascending (the canonical form):
+ *    a hyperedge holds its sources then its destinations, each run sorted; an
+ *    incidence segment holds in(n) then out(n), each run sorted; N(n) sorted.
+ *  - A failing call returns a negative CHP_E* code, leaves its outputs
+ *    unspecified, never publishes a partial chp_hgraph, and stores a message
+ *    retrievable with chp_last_error.  One context must not be used by two
+ *    host threads at once.
+ */
+#ifndef CHP_H
+#define CHP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CHP_NONE 0xFFFFFFFFu
+#define CHP_FX_SHIFT 40
+
+enum {
+  CHP_OK = 0,
+  CHP_EINVAL = -1,      /* null pointer, id out of range, duplicate pin, src and dst overlap,
+                           empty hyperedge, zero weight or size, bad offsets, rho >= k */
+  CHP_ENOMEM = -2,      /* the allocator returned NULL */
+  CHP_EOVERFLOW = -3,   /* weight >= 2^24, or a node's sum of rating terms plus the noise
+                           cap reaches 2^63 */
+  CHP_EINFEASIBLE = -4, /* a single node already breaks Omega or Delta ([HP] Sec. II-B
+                           assumes a valid solution exists) */
+  CHP_ECYCLE = -5,      /* the proposal graph has a cycle longer than two ([HP] Sec. V-A
+                           proves it has none) */
+  CHP_EDEVICE = -6      /* a HIP runtime error */
+};
+
+/* Device allocator used for every buffer the library owns or needs as
+ * scratch.  alloc returns NULL on failure.  Memory is used only on the
+ * context's stream, so a stream-ordered caching allocator may recycle a
+ * block as soon as free is called. */
+typedef void *(*chp_alloc_fn)(size_t bytes, void *user);
+typedef void (*chp_free_fn)(void *ptr, void *user);
+
+typedef struct chp_ctx chp_ctx;
+
+/* Create a context bound to the current HIP device and to hip_stream (a
+ * hipStream_t; NULL = the default stream).  alloc/free may both be NULL, in
+ * which case hipMalloc/hipFree are used.  Returns CHP_OK and *out, or an
+ * error (then *out is NULL). */
+int chp_create(chp_ctx **out, void *hip_stream, chp_alloc_fn alloc, chp_free_fn free_fn,
+               void *user);
+void chp_destroy(chp_ctx *ctx);
+/* Message of the last failing call on ctx ("" if none).  Owned by ctx. */
+const char *chp_last_error(const chp_ctx *ctx);
+
+/* Hyperedge CSR supplied by the caller ([HP] Sec. IV-B, Fig. 2): segment e
+ * is e_pins[e_off[e] .. e_off[e+1]), its first e_nsrc[e] pins are src(e),
+ * the rest dst(e) ([HP] Sec. II-A).  Any order inside each run is accepted.
+ * Borrowed: must stay valid until the call that reads it has completed on
+ * the stream. */
+typedef struct {
+  uint32_t n_nodes, n_edges;
+  uint64_t n_pins;       /* == e_off[n_edges] */
+  const int64_t *e_off;  /* [E+1] */
+  const uint32_t *e_nsrc;/* [E]   */
+  const uint32_t *e_pins;/* [P]   */
+  const uint32_t *e_w;   /* [E]   omega(e) >= 1 */
+  const uint32_t *n_size;/* [N]   size(n) >= 1 (node weight) */
+} chp_edges;
+
+/* One level of a hypergraph, owned by the library (allocated through the
+ * context's allocator, released with chp_hgraph_free).  Canonical CSR:
+ *  e_*:    hyperedges as in chp_edges, each run sorted.
+ *  n_off/n_nin/n_inc: incidence ([HP] Sec. IV-B): segment n holds in(n)
+ *          ascending, then out(n) ascending; n_nin[n] = |in(n)|.
+ *  nb_off/nb: unique neighbourhoods N(n) = (U_{e in I(n)} e) \ {n}, sorted
+ *          ([HP] Sec. II-A, V-B).  NULL (nb_total 0) when not built. */
+typedef struct {
+  uint32_t n_nodes, n_edges;
+  uint64_t n_pins;
+  int64_t *e_off;
+  uint32_t *e_nsrc;
+  uint32_t *e_pins;
+  uint32_t *e_w;
+  uint32_t *n_size;
+  int64_t *n_off;
+  uint32_t *n_nin;
+  uint32_t *n_inc;
+  int64_t *nb_off;
+  uint32_t *nb;
+  uint64_t nb_total;
+} chp_hgraph;
+
+/* Limits and rating options.
+ *  omega, delta: [HP] Sec. II-B.
+ *  noise_on, noise_seed: the symmetric tie-breaking noise of [HP] Sec. V-C,
+ *    added once per neighbour pair: mix(seed, min(n,m), max(n,m)) mod (cap+1),
+ *    mix = one splitmix64 output (Steele, Lea & Flood, OOPSLA 2014) from the
+ *    state seed XOR (min * 2^32 + max), and cap = floor(sum_e t(e) / (10 |E|))
+ *    with t(e) the fixed-point per-hyperedge term of Eq. 5. */
+typedef struct {
+  uint64_t omega;
+  uint32_t delta;
+  uint32_t noise_on;
+  uint64_t noise_seed;
+} chp_params;
+
+/* build_incidence ([HP] Sec. IV-B, Fig. 2; Sec. II-A definitions).
+ * Validates `in`, copies it into canonical form (runs sorted), builds the
+ * incidence CSR and, if build_neighbors != 0, the neighbourhood CSR.
+ * Errors, by precedence: EINVAL (bad offsets, e_nsrc > |e|, empty hyperedge,
+ * weight 0, size 0, pin >= n_nodes, duplicate pin, src and dst overlap),
+ * EOVERFLOW (weight >= 2^24), EINFEASIBLE (size(n) > omega or
+ * |in(n)| > delta for some node).  Synchronises.  On success *out is a new
+ * library-owned graph. */
+int chp_build_incidence(chp_ctx *ctx, const chp_edges *in, const chp_params *prm,
+                        int build_neighbors, chp_hgraph *out);
+
+/* rate_and_match: candidate proposal ([HP] Sec. V-A, Eqs. 5-6, Sec. V-C) and
+ * the deterministic handshake matching ([IC] Sec. III-A, III-B3).
+ *  target[N]   best valid neighbour by (eta desc, id asc), CHP_NONE if none;
+ *              valid(n,m) <=> size(n)+size(m) <= omega and
+ *              |in(n) u in(m)| = |in(n)| + |in(m)| - inter(n,m) <= delta.
+ *  score_fx[N] eta_fx(n, target(n)) (noise included), 0 if none.
+ *  match[N]    partner of n, or n itself when unmatched.  Pairs are the
+ *              two-cycles of target, then every other node takes its target
+ *              iff the target is still free and n is its best proposer
+ *              (highest score, smallest id on ties), resolved top-down.
+ *  *n_pairs_host number of pairs.
+ * Requires g->nb (build with neighbours).  Errors: EINVAL, EOVERFLOW,
+ * ECYCLE.  Synchronises. */
+int chp_rate_and_match(chp_ctx *ctx, const chp_hgraph *g, const chp_params *prm,
+                       uint32_t *target, uint64_t *score_fx, uint32_t *match,
+                       uint32_t *n_pairs_host);
+
+/* contract ([HP] Sec. III and V-E; [IC] Sec. III-B4).
+ *  gamma[N]   coarse id of every node: the rank of min(n, match(n)) among
+ *             the nodes with match(n) >= n.
+ *  *coarse    new library-owned graph: size'(c) = sum of member sizes; one
+ *             coarse hyperedge per hyperedge, same id and weight, dst' =
+ *             gamma(dst), src' = gamma(src) \ dst'; incidence rebuilt; N'
+ *             rebuilt if build_neighbors != 0.
+ * match must be a symmetric involution (match[match[n]] == n), else EINVAL.
+ * Synchronises. */
+int chp_contract(chp_ctx *ctx, const chp_hgraph *g, const uint32_t *match, uint32_t *gamma,
+                 int build_neighbors, chp_hgraph *coarse);
+
+/* evaluate_partition ([HP] Eq. 1, Eq. 16, Sec. II-B).
+ *  rho[N] in [0,k).  part_size[k] = sum of sizes per part (uint64);
+ *  part_inb[k] = |{e : some d in dst(e) has rho(d) = p}|.
+ *  summary_host[8] = {connectivity sum_e w (lambda-1), cut-net sum_e w [lambda>1],
+ *                     #parts with size > omega, #parts with inbound > delta,
+ *                     #empty parts, max part size, max part inbound, sum_e lambda}.
+ * EINVAL if k == 0 (with nodes) or some rho[n] >= k.  Synchronises. */
+int chp_evaluate_partition(chp_ctx *ctx, const chp_hgraph *g, const uint32_t *rho, uint32_t k,
+                           const chp_params *prm, uint64_t *part_size, uint32_t *part_inb,
+                           uint64_t summary_host[8]);
+
+/* Release every array of g (allocated by this library) and zero *g. */
+void chp_hgraph_free(chp_ctx *ctx, chp_hgraph *g);
+
+/* Kernel timing.  With timing on, the library brackets each of its kernel
+ * launches with HIP events on the context stream and accumulates, per kernel
+ * name, the number of launches and their total duration.  chp_get_timings
+ * synchronises, fills up to max entries (names are owned by the library) and
+ * returns the number of distinct kernels; chp_reset_timings clears them. */
+typedef struct {
+  const char *name;
+  uint64_t launches;
+  double total_ms;
+} chp_timing;
+int chp_set_timing(chp_ctx *ctx, int on);
+int chp_get_timings(chp_ctx *ctx, chp_timing *out, int max);
+void chp_reset_timings(chp_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CHP_H */
