@@ -253,6 +253,53 @@ void build_neighbors_core(chp_ctx *c, Scratch &s, Owned &own, chp_hgraph *g) {
   launch_check(c, "neighbour compaction");
 }
 
+// neighbourhoods of the coarse graph cg by merging the members' lists of the
+// fine graph g (which must have them)
+void build_neighbors_merge(chp_ctx *c, Scratch &s, Owned &own, const chp_hgraph *g,
+                           chp_hgraph *cg, const u32 *match, const i64 *rank, const u32 *gamma) {
+  const u32 N = g->n_nodes, Nc = cg->n_nodes;
+  cg->nb_off = own.get<i64>((u64)Nc + 1);
+  u32 *rep_of = s.get<u32>(Nc);
+  u32 *bound = s.get<u32>(Nc);
+  NbLists nl;
+  for (int k = 0; k < 3; ++k) nl.list[k] = s.get<u32>(Nc);
+  nl.cnt = s.get<u32>(8);
+  launch_fill_u32(c, nl.cnt, 8, 0);
+  launch_nbm_classify(c, N, match, rank, g->nb_off, rep_of, bound, nl);
+  i64 *ooff = s.get<i64>((u64)Nc + 1);
+  i64 *tmp = s.get<i64>(scan_tmp_words(Nc));
+  scan_u32_to_i64(c, bound, ooff, Nc, tmp);
+  launch_check(c, "coarse neighbour classes");
+  i64 obuf_total;
+  u32 hc[8];
+  read_back(c, &obuf_total, ooff + Nc, sizeof obuf_total);
+  read_back(c, hc, nl.cnt, sizeof hc);
+  if (hc[7]) {
+    set_err(c, "%sa cluster's neighbour lists exceed 2^32 entries");
+    throw Fail{CHP_EOVERFLOW};
+  }
+  u32 *obuf = s.get<u32>((u64)obuf_total);
+  u32 *count = s.get<u32>(Nc);
+  launch_fill_u32(c, count, Nc, 0);
+  u32 *scr = nullptr;
+  u64 per_wg = 0;
+  u32 gb = grid_big_for(hc[2]);
+  if (hc[2]) {
+    per_wg = 2ull * hc[3];
+    scr = s.get<u32>(per_wg * gb);
+  }
+  launch_nbm_build(c, g->nb_off, g->nb, gamma, match, rep_of, ooff, obuf, count, nl, hc, scr,
+                   per_wg, gb);
+  scan_u32_to_i64(c, count, cg->nb_off, Nc, tmp);
+  launch_check(c, "coarse neighbours");
+  i64 total;
+  read_back(c, &total, cg->nb_off + Nc, sizeof total);
+  cg->nb = own.get<u32>((u64)total);
+  cg->nb_total = (u64)total;
+  launch_nb_compact(c, Nc, ooff, obuf, cg->nb_off, cg->nb);
+  launch_check(c, "coarse neighbour compaction");
+}
+
 EdgeLists make_edge_lists(chp_ctx *c, Scratch &s, u32 E, const i64 *e_off, u32 hc[8]) {
   EdgeLists el;
   for (int k = 0; k < 3; ++k) el.list[k] = s.get<u32>(E);
@@ -356,12 +403,16 @@ int chp_create(chp_ctx **out, void *hip_stream, chp_alloc_fn alloc, chp_free_fn 
   c->alloc = alloc;
   c->free_fn = free_fn;
   c->user = user;
+  int ncu = 0;
   if (hipGetDevice(&c->device) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, c->device) !=
+          hipSuccess ||
       hipHostMalloc((void **)&c->pinned, 64 * sizeof(u64), hipHostMallocDefault) != hipSuccess) {
     (void)hipGetLastError();
     delete c;
     return CHP_EDEVICE;
   }
+  c->n_cu = ncu > 0 ? (u32)ncu : 256;
   c->flags = (u32 *)ctx_alloc(c, 64 * sizeof(u32));
   if (!c->flags) {
     (void)hipHostFree(c->pinned);
@@ -510,8 +561,6 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
     launch_fill_u32(c, nl.cnt, 8, 0);
     launch_rate_classify(c, N, g->nb_off, nl, target, score_fx);
     launch_check(c, "rate classes");
-    u32 hc[8];
-    read_back(c, hc, nl.cnt, sizeof hc);
     RateArgs a;
     a.N = N;
     a.e_off = g->e_off;
@@ -532,7 +581,8 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
     a.target = target;
     a.score = score_fx;
     a.flags = c->flags;
-    launch_rate(c, a, nl, hc);
+    u32 *work = s.get<u32>(2);
+    launch_rate(c, a, nl, work);
     launch_check(c, "rate");
     MatchScratch ms;
     ms.bscore = s.get<u64>(N);
@@ -620,7 +670,10 @@ int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
     launch_check(c, "coarse pins");
     s.release(opins);
     build_incidence_core(c, s, own, &cg, ~0ull, NONE32);
-    if (build_neighbors) build_neighbors_core(c, s, own, &cg);
+    if (build_neighbors) {
+      if (g->nb_off && g->nb) build_neighbors_merge(c, s, own, g, &cg, match, rank, gamma);
+      else build_neighbors_core(c, s, own, &cg);
+    }
     hip_check(c, hipStreamSynchronize(c->stream), "contract");
     own.keep = true;
     *coarse = cg;

@@ -43,6 +43,7 @@ struct chp_ctx {
   chp_free_fn free_fn = nullptr;
   void *user = nullptr;
   int device = 0;
+  u32 n_cu = 256;          // compute units of the device
   std::string err;
   u32 *flags = nullptr;    // device: [0] error flags, [1..63] small counters
   u64 *pinned = nullptr;   // host pinned staging (64 words)

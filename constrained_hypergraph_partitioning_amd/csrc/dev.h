@@ -219,6 +219,18 @@ __device__ K *wg_sort_global(K *a, K *b, u64 n, K *lds) {
   return src;
 }
 
+// Append the lanes of a wave whose `pred` holds to a device list: one atomic
+// per wave on the shared counter; returns each such lane's slot.
+__device__ __forceinline__ u32 wave_append(u32 *counter, bool pred) {
+  const u64 m = __ballot(pred);
+  if (m == 0) return 0;
+  const u32 leader = (u32)__ffsll((unsigned long long)m) - 1;
+  u32 base = 0;
+  if (lane_id() == leader) base = atomicAdd(counter, (u32)__popcll(m));
+  base = __shfl(base, leader, WAVE);
+  return base + (u32)__popcll(m & ((1ull << lane_id()) - 1));
+}
+
 // Bitonic sort of one key per lane across a wave (ascending by lane).
 template <typename K>
 __device__ __forceinline__ K wave_sort64(K v) {

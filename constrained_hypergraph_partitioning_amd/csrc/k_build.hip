@@ -32,12 +32,18 @@ __global__ void k_check_edges(u32 N, u32 E, u64 P, const i64 *e_off, const u32 *
   if (f) atomicOr(flags, f);
 }
 
+// Queue a run for sorting (runs shorter than 2 need none).  Every lane of
+// the wave must call it; appends are aggregated per wave.
 __device__ __forceinline__ void push_run(RunLists rl, i64 start, u32 len) {
-  if (len < 2) return;
-  int c = len <= 64 ? 0 : (len <= LDS_CAP_U32 ? 1 : 2);
-  u32 slot = atomicAdd(&rl.cnt[c], 1u);
-  rl.start[c][slot] = start;
-  rl.len[c][slot] = len;
+  const int c = len < 2 ? 3 : (len <= 64 ? 0 : (len <= LDS_CAP_U32 ? 1 : 2));
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const u32 slot = wave_append(&rl.cnt[k], c == k);
+    if (c == k) {
+      rl.start[k][slot] = start;
+      rl.len[k][slot] = len;
+    }
+  }
   if (c == 2) atomicMax(&rl.cnt[3], len);
 }
 
@@ -207,10 +213,14 @@ __global__ __launch_bounds__(256) void k_scatter(u32 E, const i64 *e_off, const 
 }
 
 __global__ void k_node_runs(u32 N, const i64 *n_off, const u32 *n_nin, RunLists rl) {
-  u32 n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n >= N) return;
-  i64 a = n_off[n], b = n_off[n + 1];
-  u32 ni = n_nin[n];
+  const u32 n = blockIdx.x * blockDim.x + threadIdx.x;
+  i64 a = 0, b = 0;
+  u32 ni = 0;
+  if (n < N) {
+    a = n_off[n];
+    b = n_off[n + 1];
+    ni = n_nin[n];
+  }
   push_run(rl, a, ni);
   push_run(rl, a + ni, (u32)(b - a - ni));
 }
@@ -220,25 +230,80 @@ __global__ void k_node_runs(u32 N, const i64 *n_off, const u32 *n_nin, RunLists 
 // bound of |N(n)| is W_n - |I(n)| (n is a pin of each of its hyperedges).
 __global__ void k_nb_classify(u32 N, const i64 *e_off, const i64 *n_off, const u32 *n_inc,
                               u32 *bound, NbLists nl) {
-  u32 n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n >= N) return;
-  i64 a = n_off[n], b = n_off[n + 1];
-  u64 w = 0;
-  for (i64 j = a; j < b; ++j) {
-    u32 e = n_inc[j];
-    w += (u64)(e_off[e + 1] - e_off[e]);
+  const u32 n = blockIdx.x * blockDim.x + threadIdx.x;
+  u64 w = 0, bnd = 0;
+  if (n < N) {
+    const i64 a = n_off[n], b = n_off[n + 1];
+    for (i64 j = a; j < b; ++j) {
+      const u32 e = n_inc[j];
+      w += (u64)(e_off[e + 1] - e_off[e]);
+    }
+    bnd = w - (u64)(b - a);
+    if (w > 0xFFFFFFFFull) {  // per-node work must fit 32 bits
+      atomicOr(nl.cnt + 7, 1u);
+      bnd = 0;
+    }
+    bound[n] = (u32)bnd;
   }
-  u64 bnd = w - (u64)(b - a);
-  if (w > 0xFFFFFFFFull) {  // per-node work must fit 32 bits
-    atomicOr(nl.cnt + 7, 1u);
-    bnd = 0;
+  // isolated nodes (bnd 0) have an empty N(n) and join no class
+  const int c = bnd == 0 ? 3 : (w <= 64 ? 0 : (w <= LDS_CAP_U32 ? 1 : 2));
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const u32 slot = wave_append(&nl.cnt[k], c == k);
+    if (c == k) nl.list[k][slot] = n;
   }
-  bound[n] = (u32)bnd;
-  if (bnd == 0) return;  // isolated node: empty N(n)
-  int c = w <= 64 ? 0 : (w <= LDS_CAP_U32 ? 1 : 2);
-  u32 slot = atomicAdd(&nl.cnt[c], 1u);
-  nl.list[c][slot] = n;
   if (c == 2) atomicMax(&nl.cnt[3], (u32)w);
+}
+
+// Coarse neighbourhoods by merging the members' lists: for the cluster c =
+// {a, b}, N'(c) = sort-unique(gamma(N(a)) u gamma(N(b))) minus c, which is
+// N(c) on the coarse graph since a coarse hyperedge is gamma of its fine one.
+// The bound |N(a)| + |N(b)| decides the class.
+__global__ void k_nbm_classify(u32 N, const u32 *match, const i64 *rank, const i64 *nb_off,
+                               u32 *rep_of, u32 *bound, NbLists nl) {
+  const u32 n = blockIdx.x * blockDim.x + threadIdx.x;
+  u64 w = 0;
+  bool rep = false;
+  u32 cid = 0;
+  if (n < N) {
+    const u32 m = match[n];
+    rep = m >= n;
+    if (rep) {
+      cid = (u32)rank[n];
+      w = (u64)(nb_off[n + 1] - nb_off[n]);
+      if (m != n) w += (u64)(nb_off[m + 1] - nb_off[m]);
+      if (w > 0xFFFFFFFFull) {
+        atomicOr(nl.cnt + 7, 1u);
+        w = 0;
+      }
+      rep_of[cid] = n;
+      bound[cid] = (u32)w;
+    }
+  }
+  const int c = (!rep || w == 0) ? 3 : (w <= 64 ? 0 : (w <= LDS_CAP_U32 ? 1 : 2));
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const u32 slot = wave_append(&nl.cnt[k], c == k);
+    if (c == k) nl.list[k][slot] = cid;
+  }
+  if (c == 2) atomicMax(&nl.cnt[3], (u32)w);
+}
+
+// gather gamma of the members' neighbour lists into dst (m = ka + kb keys)
+template <int BLOCK>
+__device__ void gather_members(const i64 *nb_off, const u32 *nb, const u32 *gamma, u32 a, u32 b,
+                               u32 *dst, u32 *m_out) {
+  const i64 a0 = nb_off[a];
+  const u32 ka = (u32)(nb_off[a + 1] - a0);
+  i64 b0 = 0;
+  u32 kb = 0;
+  if (b != a) {
+    b0 = nb_off[b];
+    kb = (u32)(nb_off[b + 1] - b0);
+  }
+  for (u32 i = threadIdx.x; i < ka + kb; i += BLOCK)
+    dst[i] = gamma[i < ka ? nb[a0 + i] : nb[b0 + (i - ka)]];
+  *m_out = ka + kb;
 }
 
 // wave per node, W_n <= 64: gather into lanes, sort, unique, drop n
@@ -380,6 +445,83 @@ __global__ __launch_bounds__(BLOCK) void k_nb_global(const i64 *e_off, const u32
   }
 }
 
+__global__ __launch_bounds__(256) void k_nbm_wave(const i64 *nb_off, const u32 *nb,
+                                                  const u32 *gamma, const u32 *match,
+                                                  const u32 *rep_of, const i64 *ooff, u32 *obuf,
+                                                  u32 *count, const u32 *list, const u32 *cnt) {
+  const u32 total = *cnt;
+  const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
+  const u32 l = lane_id();
+  for (u32 w = blockIdx.x * (blockDim.x / WAVE) + wave_id(); w < total; w += nwaves) {
+    const u32 c = list[w];
+    const u32 a = rep_of[c], b = match[a];
+    const i64 a0 = nb_off[a];
+    const u32 ka = (u32)(nb_off[a + 1] - a0);
+    i64 b0 = 0;
+    u32 kb = 0;
+    if (b != a) {
+      b0 = nb_off[b];
+      kb = (u32)(nb_off[b + 1] - b0);
+    }
+    u32 v = NONE32;
+    if (l < ka + kb) v = gamma[l < ka ? nb[a0 + l] : nb[b0 + (l - ka)]];
+    v = wave_sort64(v);
+    const u32 prev = __shfl_up(v, 1, WAVE);
+    const bool keep = v != NONE32 && v != c && (l == 0 || prev != v);
+    const u64 mask = __ballot(keep);
+    const u32 pos = (u32)__popcll(mask & ((1ull << l) - 1));
+    if (keep) obuf[ooff[c] + pos] = v;
+    if (l == 0) count[c] = (u32)__popcll(mask);
+  }
+}
+
+template <int BLOCK, int CAP>
+__global__ __launch_bounds__(BLOCK) void k_nbm_lds(const i64 *nb_off, const u32 *nb,
+                                                   const u32 *gamma, const u32 *match,
+                                                   const u32 *rep_of, const i64 *ooff, u32 *obuf,
+                                                   u32 *count, const u32 *list, const u32 *cnt) {
+  __shared__ u32 s[CAP];
+  __shared__ u32 s_red[BLOCK / WAVE + 1];
+  const u32 total = *cnt;
+  for (u32 w = blockIdx.x; w < total; w += gridDim.x) {
+    const u32 c = list[w];
+    const u32 a = rep_of[c];
+    u32 m;
+    gather_members<BLOCK>(nb_off, nb, gamma, a, match[a], s, &m);
+    const u32 p = next_pow2(m);
+    for (u32 i = m + threadIdx.x; i < p; i += BLOCK) s[i] = NONE32;
+    __syncthreads();
+    lds_bitonic<BLOCK>(s, p);
+    const u32 k = unique_out<BLOCK>(s, m, c, obuf + ooff[c], s_red);
+    if (threadIdx.x == 0) count[c] = k;
+    __syncthreads();
+  }
+}
+
+template <int BLOCK, int CAP>
+__global__ __launch_bounds__(BLOCK) void k_nbm_global(const i64 *nb_off, const u32 *nb,
+                                                      const u32 *gamma, const u32 *match,
+                                                      const u32 *rep_of, const i64 *ooff,
+                                                      u32 *obuf, u32 *count, const u32 *list,
+                                                      const u32 *cnt, u32 *scratch, u64 per_wg) {
+  __shared__ u32 s[CAP];
+  __shared__ u32 s_red[BLOCK / WAVE + 1];
+  const u32 total = *cnt;
+  u32 *A = scratch + (u64)blockIdx.x * per_wg;
+  u32 *B = A + per_wg / 2;
+  for (u32 w = blockIdx.x; w < total; w += gridDim.x) {
+    const u32 c = list[w];
+    const u32 a = rep_of[c];
+    u32 m;
+    gather_members<BLOCK>(nb_off, nb, gamma, a, match[a], A, &m);
+    __syncthreads();
+    u32 *res = wg_sort_global<BLOCK, CAP>(A, B, m, s);
+    const u32 k = unique_out<BLOCK>(res, m, c, obuf + ooff[c], s_red);
+    if (threadIdx.x == 0) count[c] = k;
+    __syncthreads();
+  }
+}
+
 // copy each node's unique list from the oversize buffer to its final place
 __global__ __launch_bounds__(256) void k_nb_compact(u32 N, const i64 *ooff, const u32 *obuf,
                                                     const i64 *nb_off, u32 *nb) {
@@ -473,6 +615,31 @@ void launch_nb_build(chp_ctx *c, u32 N, const i64 *e_off, const u32 *pins, const
   if (host_cnt[2])
     CHP_LAUNCH(c, "nb_global", (k_nb_global<256, LDS_CAP_U32>), grid_big, 256, 0, e_off, pins,
                n_off, n_inc, ooff, obuf, count, nl.list[2], nl.cnt + 2, scratch, scratch_per_wg);
+}
+
+void launch_nbm_classify(chp_ctx *c, u32 N, const u32 *match, const i64 *rank,
+                         const i64 *nb_off, u32 *rep_of, u32 *bound, NbLists nl) {
+  if (N == 0) return;
+  CHP_LAUNCH(c, "nbm_classify", k_nbm_classify, grid_for(N, 256), 256, 0, N, match, rank, nb_off,
+             rep_of, bound, nl);
+}
+
+void launch_nbm_build(chp_ctx *c, const i64 *nb_off, const u32 *nb, const u32 *gamma,
+                      const u32 *match, const u32 *rep_of, const i64 *ooff, u32 *obuf,
+                      u32 *count, NbLists nl, const u32 *host_cnt, u32 *scratch,
+                      u64 scratch_per_wg, u32 grid_big) {
+  if (host_cnt[0])
+    CHP_LAUNCH(c, "nbm_wave", k_nbm_wave, waves_grid(host_cnt[0]), 256, 0, nb_off, nb, gamma,
+               match, rep_of, ooff, obuf, count, (const u32 *)nl.list[0],
+               (const u32 *)nl.cnt + 0);
+  if (host_cnt[1])
+    CHP_LAUNCH(c, "nbm_lds", (k_nbm_lds<256, LDS_CAP_U32>),
+               host_cnt[1] > 8192 ? 8192 : host_cnt[1], 256, 0, nb_off, nb, gamma, match, rep_of,
+               ooff, obuf, count, (const u32 *)nl.list[1], (const u32 *)nl.cnt + 1);
+  if (host_cnt[2])
+    CHP_LAUNCH(c, "nbm_global", (k_nbm_global<256, LDS_CAP_U32>), grid_big, 256, 0, nb_off, nb,
+               gamma, match, rep_of, ooff, obuf, count, (const u32 *)nl.list[2],
+               (const u32 *)nl.cnt + 2, scratch, scratch_per_wg);
 }
 
 void launch_nb_compact(chp_ctx *c, u32 N, const i64 *ooff, const u32 *obuf, const i64 *nb_off,

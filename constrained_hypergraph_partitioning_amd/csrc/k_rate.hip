@@ -82,17 +82,21 @@ __global__ void k_cap(u32 nparts, const u64 *partials, u32 E, u64 *capinfo) {
 // rating
 __global__ void k_rate_classify(u32 N, const i64 *nb_off, NbLists nl, u32 *target, u64 *score,
                                 u32 small_cap) {
-  u32 n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n >= N) return;
-  u64 K = (u64)(nb_off[n + 1] - nb_off[n]);
-  if (K == 0) {
-    target[n] = NONE32;
-    score[n] = 0;
-    return;
+  const u32 n = blockIdx.x * blockDim.x + threadIdx.x;
+  u64 K = 0;
+  if (n < N) {
+    K = (u64)(nb_off[n + 1] - nb_off[n]);
+    if (K == 0) {
+      target[n] = NONE32;
+      score[n] = 0;
+    }
   }
-  int c = K <= small_cap ? 0 : 1;
-  u32 slot = atomicAdd(&nl.cnt[c], 1u);
-  nl.list[c][slot] = n;
+  const int c = (n >= N || K == 0) ? 2 : (K <= small_cap ? 0 : 1);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const u32 slot = wave_append(&nl.cnt[k], c == k);
+    if (c == k) nl.list[k][slot] = n;
+  }
 }
 
 template <int BLOCK>
@@ -110,118 +114,297 @@ __device__ __forceinline__ u64 wg_sat_sum(u64 v, u64 *lds) {
   return t;
 }
 
-// One workgroup per node.  N(n) is taken in slices of at most CAP ids
-// (sorted, so each slice covers an id interval); the slice's eta and inter
-// accumulators live in LDS.  Incident hyperedges are taken ECH at a time:
-// each contributes a source run and a destination run (clipped to the
-// slice's id interval when N(n) needs several slices), and the pins of all
-// runs are spread evenly over the workgroup.  Each pin m finds its bin by a
-// binary search of the slice and adds t(e) to eta(n,m); a destination pin of
-// an inbound hyperedge also increments inter(n,m).
-template <int BLOCK, int CAP, int ECH>
-__global__ __launch_bounds__(BLOCK) void k_rate(RateArgs A, const u32 *list, const u32 *cnt) {
-  __shared__ u32 s_id[CAP];
-  __shared__ u64 s_eta[CAP];
-  __shared__ u32 s_int[CAP];
-  __shared__ u64 s_rs[2 * ECH];
-  __shared__ u64 s_rt[2 * ECH];
-  __shared__ u32 s_pre[2 * ECH + 1];
-  __shared__ u32 s_red32[BLOCK / WAVE + 1];
-  __shared__ u64 s_red64[BLOCK / WAVE + 1];
-  __shared__ u32 s_redi[BLOCK / WAVE + 1];
-  static_assert(ECH <= BLOCK, "one thread per hyperedge of a chunk");
-  constexpr u64 INB = 1ull << 63;
-  const u32 total = *cnt;
+// ---------------------------------------------------------------------------
+// Rating kernel: one launch per level.  A node with more than L_CAP
+// neighbours ("heavy") takes a whole workgroup, a "light" node one wave; both
+// pull nodes from a work counter, heavy ones first.
+//
+// Per node the neighbour list N(n) is loaded, a window of at most H_CAP ids at
+// a time (L_CAP for a light node, whose list always fits), into an LDS hash
+// table whose slots are the accumulation bins: eta(n,m) (u64 fixed point) and
+// inter(n,m).  Incident hyperedges are taken a chunk at a time; each brings a
+// source run and a destination run of its pin list (for a windowed node,
+// clipped by binary search to the window's id interval, as the runs and N(n)
+// are sorted).  A workgroup scan lays the runs end to end and every thread
+// walks ITEMS consecutive pins with one run lookup, adding t(e) to the bin of
+// each pin m != n and, for a destination pin of an inbound hyperedge, one to
+// inter(n,m).  The candidate scan keeps, per thread, the best valid bin by
+// (eta desc, id asc), skipping a bin whose upper bound eta + cap cannot beat
+// it before its noise and limits are evaluated.
+constexpr int RB = 256;
+constexpr int RW = RB / WAVE;
+constexpr u32 H_T = 2048, H_SHIFT = 21;  // hash slots of the heavy path
+constexpr u32 H_CAP = 1536;              // neighbours per window (load 0.75)
+constexpr int H_ECH = 128;               // hyperedges per chunk
+constexpr u32 L_T = 512, L_SHIFT = 23;   // hash slots per wave, light path
+constexpr int L_ECH = 32;
+constexpr u32 ITEMS = 4;
+constexpr u32 EMPTY = 0xFFFFFFFFu;
+constexpr u64 INB = 1ull << 63;
+static_assert(RATE_SMALL_CAP <= L_T * 3 / 4, "light window must fit its table");
+
+struct HeavySmem {
+  u64 eta[H_T];
+  u32 key[H_T];
+  u32 inter[H_T];
+  u64 rs[2 * H_ECH];
+  u64 rt[2 * H_ECH];
+  u32 pre[2 * H_ECH + 1];
+  u32 red32[RW + 1];
+  u64 red64[RW + 1];
+  u32 redi[RW + 1];
+};
+struct LightWave {
+  u64 eta[L_T];
+  u32 key[L_T];
+  u32 inter[L_T];
+  u64 rs[2 * L_ECH];
+  u64 rt[2 * L_ECH];
+  u32 pre[2 * L_ECH + 1];
+};
+union RateSmem {
+  HeavySmem h;
+  LightWave l[RW];
+};
+
+// LDS writes of this wave become visible to its other lanes
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+__device__ __forceinline__ u32 hslot(u32 m, u32 shift) { return (m * 0x9E3779B1u) >> shift; }
+
+// insert a key not yet present (linear probing, bounded)
+__device__ __forceinline__ void h_insert(u32 *key, u32 mask, u32 shift, u32 m) {
+  u32 s = hslot(m, shift);
+  for (u32 p = 0; p <= mask; ++p) {
+    if (atomicCAS(&key[s], EMPTY, m) == EMPTY) return;
+    s = (s + 1) & mask;
+  }
+}
+
+__device__ __forceinline__ u32 h_find(const u32 *key, u32 mask, u32 shift, u32 m) {
+  u32 s = hslot(m, shift);
+  for (u32 p = 0; p <= mask; ++p) {
+    const u32 k = key[s];
+    if (k == m) return s;
+    if (k == EMPTY) return EMPTY;
+    s = (s + 1) & mask;
+  }
+  return EMPTY;
+}
+
+// Walk the pins of runs [0, nruns) (flat length tot), LANES threads, t = this
+// thread's index among them.
+template <u32 LANES>
+__device__ __forceinline__ void visit_runs(const u32 *pins, const u32 *key, u32 mask, u32 shift,
+                                           u64 *eta, u32 *inter, const u64 *rs, const u64 *rt,
+                                           const u32 *pre, u32 nruns, u32 tot, u32 n, u32 t) {
+  for (u32 base = t * ITEMS; base < tot; base += LANES * ITEMS) {
+    u32 r = run_of(pre, nruns + 1, base);
+    const u32 lim = (base + ITEMS) < tot ? (base + ITEMS) : tot;
+    for (u32 idx = base; idx < lim; ++idx) {
+      while (idx >= pre[r + 1]) ++r;
+      const u64 st = rs[r];
+      const u32 m = pins[(i64)(st & ~INB) + (idx - pre[r])];
+      if (m == n) continue;
+      const u32 slot = h_find(key, mask, shift, m);
+      if (slot == EMPTY) continue;  // cannot happen for a valid N(n)
+      atomicAdd(&eta[slot], rt[r]);
+      if (st & INB) atomicAdd(&inter[slot], 1u);
+    }
+  }
+}
+
+// Descriptor of hyperedge j of n's incidence (j relative to the node
+// segment): its source and destination runs, clipped to [lo, hi] if clip.
+__device__ __forceinline__ void edge_runs(const RateArgs &A, i64 j_abs, bool isin, bool clip,
+                                          u32 lo, u32 hi, u64 *rs, u64 *rt, u32 &ls, u32 &ld,
+                                          u64 &tsum_add) {
+  const u32 e = A.n_inc[j_abs];
+  const i64 a = A.e_off[e], b = A.e_off[e + 1];
+  const i64 dm = a + A.e_nsrc[e];
+  const u64 te = A.t[e];
+  tsum_add = (b - a >= 2) ? te : 0;
+  i64 sa = a, sb = dm, da = dm, db = b;
+  if (clip) {
+    sa = lower_bound_i(A.e_pins, a, dm, lo);
+    sb = upper_bound_i(A.e_pins, sa, dm, hi);
+    da = lower_bound_i(A.e_pins, dm, b, lo);
+    db = upper_bound_i(A.e_pins, da, b, hi);
+  }
+  rs[0] = (u64)sa;
+  rs[1] = (u64)da | (isin ? INB : 0);
+  rt[0] = te;
+  rt[1] = te;
+  ls = (u32)(sb - sa);
+  ld = (u32)(db - da);
+}
+
+struct NodeBest {
+  u64 e;
+  u32 i;
+};
+
+__device__ __forceinline__ void consider(const RateArgs &A, u32 n, u32 nin, u64 size_n, u32 m,
+                                         u64 v, u32 it, u64 ub_add, u64 dmod, u64 magic,
+                                         NodeBest &b) {
+  if (!better(v + ub_add, m, b.e, b.i)) return;
+  const u64 tv = A.noise_on ? v + pair_noise(A.seed, n, m, dmod, magic) : v;
+  if (!better(tv, m, b.e, b.i)) return;
+  if (size_n + A.n_size[m] > A.omega) return;
+  if ((u64)nin + A.n_nin[m] - it > (u64)A.delta) return;
+  b.e = tv;
+  b.i = m;
+}
+
+__device__ void rate_heavy(const RateArgs &A, HeavySmem &S, u32 n, u64 cap, u64 dmod,
+                           u64 magic) {
   const u32 tid = threadIdx.x;
-  const u64 cap = A.capinfo[0], dmod = A.capinfo[1], magic = A.capinfo[2];
+  const i64 nb0 = A.nb_off[n];
+  const u32 K = (u32)(A.nb_off[n + 1] - nb0);
+  const i64 i0 = A.n_off[n], i1 = A.n_off[n + 1];
+  const u32 nin = A.n_nin[n];
+  const u64 size_n = A.n_size[n];
   const u64 ub_add = A.noise_on ? cap : 0;
-  for (u32 w = blockIdx.x; w < total; w += gridDim.x) {
-    const u32 n = list[w];
-    const i64 nb0 = A.nb_off[n];
-    const u32 K = (u32)(A.nb_off[n + 1] - nb0);
-    const i64 i0 = A.n_off[n], i1 = A.n_off[n + 1];
-    const u32 nin = A.n_nin[n];
-    const u64 size_n = A.n_size[n];
-    u64 best_e = 0;
-    u32 best_i = NONE32;
-    u64 tsum = 0;
-    for (u32 s0 = 0; s0 < K; s0 += CAP) {
-      const u32 cw = (K - s0) < (u32)CAP ? (K - s0) : (u32)CAP;
-      for (u32 i = tid; i < cw; i += BLOCK) {
-        s_id[i] = A.nb[nb0 + s0 + i];
-        s_eta[i] = 0;
-        s_int[i] = 0;
+  const bool clip = K > H_CAP;
+  NodeBest best{0, NONE32};
+  u64 tsum = 0;
+  for (u32 s0 = 0; s0 < K; s0 += H_CAP) {
+    const u32 cw = (K - s0) < H_CAP ? (K - s0) : H_CAP;
+    for (u32 i = tid; i < H_T; i += RB) {
+      S.key[i] = EMPTY;
+      S.eta[i] = 0;
+      S.inter[i] = 0;
+    }
+    __syncthreads();
+    for (u32 i = tid; i < cw; i += RB) h_insert(S.key, H_T - 1, H_SHIFT, A.nb[nb0 + s0 + i]);
+    const u32 lo = A.nb[nb0 + s0], hi = A.nb[nb0 + s0 + cw - 1];
+    __syncthreads();
+    for (i64 c0 = i0; c0 < i1; c0 += H_ECH) {
+      const u32 ne = (u32)((i1 - c0) < H_ECH ? (i1 - c0) : H_ECH);
+      u32 ls = 0, ld = 0;
+      if (tid < ne) {
+        u64 add;
+        edge_runs(A, c0 + tid, (u64)(c0 + tid - i0) < (u64)nin, clip, lo, hi, &S.rs[2 * tid],
+                  &S.rt[2 * tid], ls, ld, add);
+        if (s0 == 0) tsum = sat_add(tsum, add);
       }
+      u32 tot;
+      const u32 off = wg_excl_scan<RB>(ls + ld, S.red32, &tot);
+      if (tid < ne) {
+        S.pre[2 * tid] = off;
+        S.pre[2 * tid + 1] = off + ls;
+      }
+      if (tid == 0) S.pre[2 * ne] = tot;
       __syncthreads();
-      const u32 lo_id = s_id[0], hi_id = s_id[cw - 1];
-      const bool clip = K > (u32)CAP;
-      for (i64 c0 = i0; c0 < i1; c0 += ECH) {
-        const u32 ne = (u32)((i1 - c0) < ECH ? (i1 - c0) : ECH);
-        u32 ls = 0, ld = 0;
-        if (tid < ne) {
-          const u32 e = A.n_inc[c0 + tid];
-          const bool isin = (u64)(c0 + tid - i0) < (u64)nin;
-          const i64 a = A.e_off[e], b = A.e_off[e + 1];
-          const i64 dm = a + A.e_nsrc[e];
-          const u64 te = A.t[e];
-          if (s0 == 0 && b - a >= 2) tsum = sat_add(tsum, te);
-          i64 sa = a, sb = dm, da = dm, db = b;
-          if (clip) {
-            sa = lower_bound_i(A.e_pins, a, dm, lo_id);
-            sb = upper_bound_i(A.e_pins, sa, dm, hi_id);
-            da = lower_bound_i(A.e_pins, dm, b, lo_id);
-            db = upper_bound_i(A.e_pins, da, b, hi_id);
-          }
-          s_rs[2 * tid] = (u64)sa;
-          s_rs[2 * tid + 1] = (u64)da | (isin ? INB : 0);
-          s_rt[2 * tid] = te;
-          s_rt[2 * tid + 1] = te;
-          ls = (u32)(sb - sa);
-          ld = (u32)(db - da);
-        }
-        u32 tot;
-        const u32 off = wg_excl_scan<BLOCK>(ls + ld, s_red32, &tot);
-        if (tid < ne) {
-          s_pre[2 * tid] = off;
-          s_pre[2 * tid + 1] = off + ls;
-        }
-        if (tid == 0) s_pre[2 * ne] = tot;
-        __syncthreads();
-        for (u32 idx = tid; idx < tot; idx += BLOCK) {
-          const u32 r = run_of(s_pre, 2 * ne + 1, idx);
-          const u64 rs = s_rs[r];
-          const u32 m = A.e_pins[(i64)(rs & ~INB) + (idx - s_pre[r])];
-          if (m == n) continue;
-          const u32 pos = (u32)lower_bound_i(s_id, 0, cw, m);
-          if (pos >= cw || s_id[pos] != m) continue;  // cannot happen for a valid N(n)
-          atomicAdd(&s_eta[pos], s_rt[r]);
-          if (rs & INB) atomicAdd(&s_int[pos], 1u);
-        }
-        __syncthreads();
-      }
-      // candidates of this slice: keep the best valid (eta, -id); a bin whose
-      // upper bound eta + cap cannot beat the current best is skipped before
-      // its noise and limits are evaluated
-      for (u32 i = tid; i < cw; i += BLOCK) {
-        const u32 m = s_id[i];
-        const u64 v = s_eta[i];
-        if (!better(v + ub_add, m, best_e, best_i)) continue;
-        const u64 tv = A.noise_on ? v + pair_noise(A.seed, n, m, dmod, magic) : v;
-        if (!better(tv, m, best_e, best_i)) continue;
-        if (size_n + A.n_size[m] > A.omega) continue;
-        if ((u64)nin + A.n_nin[m] - s_int[i] > (u64)A.delta) continue;
-        best_e = tv;
-        best_i = m;
-      }
+      visit_runs<RB>(A.e_pins, S.key, H_T - 1, H_SHIFT, S.eta, S.inter, S.rs, S.rt, S.pre,
+                     2 * ne, tot, n, tid);
       __syncthreads();
     }
-    tsum = wg_sat_sum<BLOCK>(tsum, s_red64);
-    wg_best<BLOCK>(best_e, best_i, s_red64, s_redi);
-    if (tid == 0) {
-      if (sat_add(tsum, cap) >= (1ull << 63)) atomicOr(A.flags, FLAG_EOVERFLOW);
-      A.target[n] = best_i;
-      A.score[n] = best_i == NONE32 ? 0 : best_e;
+    for (u32 i = tid; i < H_T; i += RB) {
+      const u32 m = S.key[i];
+      if (m != EMPTY) consider(A, n, nin, size_n, m, S.eta[i], S.inter[i], ub_add, dmod, magic,
+                               best);
     }
+    __syncthreads();
+  }
+  tsum = wg_sat_sum<RB>(tsum, S.red64);
+  wg_best<RB>(best.e, best.i, S.red64, S.redi);
+  if (tid == 0) {
+    if (sat_add(tsum, cap) >= (1ull << 63)) atomicOr(A.flags, FLAG_EOVERFLOW);
+    A.target[n] = best.i;
+    A.score[n] = best.i == NONE32 ? 0 : best.e;
+  }
+}
+
+__device__ void rate_light(const RateArgs &A, LightWave &S, u32 n, u64 cap, u64 dmod,
+                           u64 magic) {
+  const u32 l = lane_id();
+  const i64 nb0 = A.nb_off[n];
+  const u32 K = (u32)(A.nb_off[n + 1] - nb0);
+  const i64 i0 = A.n_off[n], i1 = A.n_off[n + 1];
+  const u32 nin = A.n_nin[n];
+  const u64 size_n = A.n_size[n];
+  const u64 ub_add = A.noise_on ? cap : 0;
+  NodeBest best{0, NONE32};
+  u64 tsum = 0;
+  for (u32 i = l; i < L_T; i += WAVE) {
+    S.key[i] = EMPTY;
+    S.eta[i] = 0;
+    S.inter[i] = 0;
+  }
+  wave_sync();
+  for (u32 i = l; i < K; i += WAVE) h_insert(S.key, L_T - 1, L_SHIFT, A.nb[nb0 + i]);
+  wave_sync();
+  for (i64 c0 = i0; c0 < i1; c0 += L_ECH) {
+    const u32 ne = (u32)((i1 - c0) < L_ECH ? (i1 - c0) : L_ECH);
+    u32 ls = 0, ld = 0;
+    if (l < ne) {
+      u64 add;
+      edge_runs(A, c0 + l, (u64)(c0 + l - i0) < (u64)nin, false, 0, 0, &S.rs[2 * l],
+                &S.rt[2 * l], ls, ld, add);
+      tsum = sat_add(tsum, add);
+    }
+    const u32 v = ls + ld;
+    const u32 inc = wave_incl_scan(v);
+    const u32 tot = __shfl(inc, WAVE - 1, WAVE);
+    if (l < ne) {
+      S.pre[2 * l] = inc - v;
+      S.pre[2 * l + 1] = inc - v + ls;
+    }
+    if (l == 0) S.pre[2 * ne] = tot;
+    wave_sync();
+    visit_runs<WAVE>(A.e_pins, S.key, L_T - 1, L_SHIFT, S.eta, S.inter, S.rs, S.rt, S.pre,
+                     2 * ne, tot, n, l);
+    wave_sync();
+  }
+  for (u32 i = l; i < L_T; i += WAVE) {
+    const u32 m = S.key[i];
+    if (m != EMPTY) consider(A, n, nin, size_n, m, S.eta[i], S.inter[i], ub_add, dmod, magic,
+                             best);
+  }
+  tsum = wg_sat_sum<WAVE>(tsum, nullptr);
+  wg_best<WAVE>(best.e, best.i, nullptr, nullptr);
+  if (l == 0) {
+    if (sat_add(tsum, cap) >= (1ull << 63)) atomicOr(A.flags, FLAG_EOVERFLOW);
+    A.target[n] = best.i;
+    A.score[n] = best.i == NONE32 ? 0 : best.e;
+  }
+  wave_sync();
+}
+
+// cnt[0] light nodes in light[], cnt[1] heavy nodes in heavy[]; work[0..1]
+// are zeroed work counters
+__global__ __launch_bounds__(RB) void k_rate(RateArgs A, const u32 *light, const u32 *heavy,
+                                             const u32 *cnt, u32 *work) {
+  __shared__ RateSmem sm;
+  __shared__ u32 s_item;
+  const u32 nl = cnt[0], nh = cnt[1];
+  const u64 cap = A.capinfo[0], dmod = A.capinfo[1], magic = A.capinfo[2];
+  // Dynamic work loop.  The work index is a scalar (readfirstlane) and the
+  // body ends with a barrier, so every lane reconverges before the back edge:
+  // without it the compiler may route thread 0 (which alone stores the result
+  // and takes the next item) around the other lanes, which then re-enter the
+  // barrier on the stale item and never leave.
+  for (;;) {
+    if (threadIdx.x == 0) s_item = atomicAdd(&work[0], 1u);
+    __syncthreads();
+    const u32 w = __builtin_amdgcn_readfirstlane(s_item);
+    __syncthreads();
+    if (w >= nh) break;
+    rate_heavy(A, sm.h, heavy[w], cap, dmod, magic);
+    __syncthreads();
+  }
+  LightWave &S = sm.l[wave_id()];
+  for (;;) {
+    u32 w = 0;
+    if (lane_id() == 0) w = atomicAdd(&work[1], 1u);
+    w = __builtin_amdgcn_readfirstlane(__shfl(w, 0, WAVE));
+    if (w >= nl) break;
+    rate_light(A, S, light[w], cap, dmod, magic);
   }
 }
 
@@ -364,15 +547,10 @@ void launch_rate_classify(chp_ctx *c, u32 N, const i64 *nb_off, NbLists nl, u32 
              score, RATE_SMALL_CAP);
 }
 
-void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, const u32 *host_cnt) {
-  if (host_cnt[0])
-    CHP_LAUNCH(c, "rate_small", (k_rate<64, RATE_SMALL_CAP, 32>),
-               host_cnt[0] > 65536 ? 65536 : host_cnt[0], 64, 0, a, (const u32 *)nl.list[0],
-               (const u32 *)nl.cnt + 0);
-  if (host_cnt[1])
-    CHP_LAUNCH(c, "rate_large", (k_rate<256, 2048, 128>),
-               host_cnt[1] > 16384 ? 16384 : host_cnt[1], 256, 0, a, (const u32 *)nl.list[1],
-               (const u32 *)nl.cnt + 1);
+void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, u32 *work) {
+  launch_fill_u32(c, work, 2, 0);
+  CHP_LAUNCH(c, "rate", k_rate, c->n_cu * 4, RB, 0, a, (const u32 *)nl.list[0],
+             (const u32 *)nl.list[1], (const u32 *)nl.cnt, work);
 }
 
 void launch_match(chp_ctx *c, u32 N, const u32 *target, const u64 *score, MatchScratch ms,

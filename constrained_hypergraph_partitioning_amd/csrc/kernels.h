@@ -4,7 +4,7 @@
 
 constexpr u32 LDS_CAP_U32 = 8192;   // u32 keys one workgroup sorts in LDS
 constexpr u32 LDS_CAP_U64 = 8192;   // u64 keys one workgroup sorts in LDS
-constexpr u32 RATE_SMALL_CAP = 512; // |N(n)| handled by the one-wave rating kernel
+constexpr u32 RATE_SMALL_CAP = 384; // |N(n)| of a node rated by one wave
 
 // Runs to sort in place, bucketed by length: class 0 (<= 64 keys, one wave
 // each), class 1 (<= LDS_CAP_U32 keys, one workgroup in LDS), class 2
@@ -50,6 +50,12 @@ void launch_nb_classify(chp_ctx *c, u32 N, const i64 *e_off, const i64 *n_off, c
 void launch_nb_build(chp_ctx *c, u32 N, const i64 *e_off, const u32 *pins, const i64 *n_off,
                      const u32 *n_inc, const i64 *ooff, u32 *obuf, u32 *count, NbLists nl,
                      const u32 *host_cnt, u32 *scratch, u64 scratch_per_wg, u32 grid_big);
+void launch_nbm_classify(chp_ctx *c, u32 N, const u32 *match, const i64 *rank,
+                         const i64 *nb_off, u32 *rep_of, u32 *bound, NbLists nl);
+void launch_nbm_build(chp_ctx *c, const i64 *nb_off, const u32 *nb, const u32 *gamma,
+                      const u32 *match, const u32 *rep_of, const i64 *ooff, u32 *obuf,
+                      u32 *count, NbLists nl, const u32 *host_cnt, u32 *scratch,
+                      u64 scratch_per_wg, u32 grid_big);
 void launch_nb_compact(chp_ctx *c, u32 N, const i64 *ooff, const u32 *obuf, const i64 *nb_off,
                        u32 *nb);
 
@@ -81,7 +87,7 @@ struct RateArgs {
 };
 void launch_rate_classify(chp_ctx *c, u32 N, const i64 *nb_off, NbLists nl, u32 *target,
                           u64 *score);
-void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, const u32 *host_cnt);
+void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, u32 *work);
 
 struct MatchScratch {
   u64 *bscore;  // [N] zeroed
