@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 
 #include "kernels.h"
 
@@ -117,6 +118,28 @@ void read_back(chp_ctx *c, void *host, const void *dev, size_t n) {
   memcpy(host, c->pinned, n);
 }
 
+// several small device->host copies behind one stream synchronisation
+struct HostRead {
+  void *host;
+  const void *dev;
+  size_t n;
+};
+void read_many(chp_ctx *c, std::initializer_list<HostRead> items) {
+  size_t off = 0;
+  for (const HostRead &it : items) {
+    hip_check(c, hipMemcpyAsync((char *)c->pinned + off, it.dev, it.n, hipMemcpyDeviceToHost,
+                                c->stream),
+              "readback");
+    off += (it.n + 7) & ~(size_t)7;
+  }
+  hip_check(c, hipStreamSynchronize(c->stream), "stream synchronize");
+  off = 0;
+  for (const HostRead &it : items) {
+    memcpy(it.host, (const char *)c->pinned + off, it.n);
+    off += (it.n + 7) & ~(size_t)7;
+  }
+}
+
 void d2d(chp_ctx *c, void *dst, const void *src, size_t n) {
   if (n) hip_check(c, hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, c->stream), "copy");
 }
@@ -216,6 +239,7 @@ void build_neighbors_core(chp_ctx *c, Scratch &s, Owned &own, chp_hgraph *g) {
   u32 *bound = s.get<u32>(N);
   NbLists nl;
   for (int k = 0; k < 3; ++k) nl.list[k] = s.get<u32>(N);
+  nl.list[3] = nl.list[4] = nullptr;
   nl.cnt = s.get<u32>(8);
   launch_fill_u32(c, nl.cnt, 8, 0);
   launch_nb_classify(c, N, g->e_off, g->n_off, g->n_inc, bound, nl);
@@ -225,8 +249,7 @@ void build_neighbors_core(chp_ctx *c, Scratch &s, Owned &own, chp_hgraph *g) {
   launch_check(c, "neighbour classes");
   i64 obuf_total;
   u32 hc[8];
-  read_back(c, &obuf_total, ooff + N, sizeof obuf_total);
-  read_back(c, hc, nl.cnt, sizeof hc);
+  read_many(c, {{&obuf_total, ooff + N, sizeof obuf_total}, {hc, nl.cnt, sizeof hc}});
   if (hc[7]) {
     set_err(c, "%sa node's incident pins exceed 2^32");
     throw Fail{CHP_EOVERFLOW};
@@ -238,7 +261,7 @@ void build_neighbors_core(chp_ctx *c, Scratch &s, Owned &own, chp_hgraph *g) {
   u64 per_wg = 0;
   u32 gb = grid_big_for(hc[2]);
   if (hc[2]) {
-    per_wg = 2ull * hc[3];
+    per_wg = 2ull * hc[5];
     scr = s.get<u32>(per_wg * gb);
   }
   launch_nb_build(c, N, g->e_off, g->e_pins, g->n_off, g->n_inc, ooff, obuf, count, nl, hc, scr,
@@ -256,24 +279,23 @@ void build_neighbors_core(chp_ctx *c, Scratch &s, Owned &own, chp_hgraph *g) {
 // neighbourhoods of the coarse graph cg by merging the members' lists of the
 // fine graph g (which must have them)
 void build_neighbors_merge(chp_ctx *c, Scratch &s, Owned &own, const chp_hgraph *g,
-                           chp_hgraph *cg, const u32 *match, const i64 *rank, const u32 *gamma) {
-  const u32 N = g->n_nodes, Nc = cg->n_nodes;
+                           chp_hgraph *cg, const u32 *match, const u32 *rep_of,
+                           const u32 *gamma) {
+  const u32 Nc = cg->n_nodes;
   cg->nb_off = own.get<i64>((u64)Nc + 1);
-  u32 *rep_of = s.get<u32>(Nc);
   u32 *bound = s.get<u32>(Nc);
   NbLists nl;
-  for (int k = 0; k < 3; ++k) nl.list[k] = s.get<u32>(Nc);
+  for (int k = 0; k < 5; ++k) nl.list[k] = s.get<u32>(Nc);
   nl.cnt = s.get<u32>(8);
   launch_fill_u32(c, nl.cnt, 8, 0);
-  launch_nbm_classify(c, N, match, rank, g->nb_off, rep_of, bound, nl);
+  launch_nbm_classify(c, Nc, rep_of, match, g->nb_off, bound, nl);
   i64 *ooff = s.get<i64>((u64)Nc + 1);
   i64 *tmp = s.get<i64>(scan_tmp_words(Nc));
   scan_u32_to_i64(c, bound, ooff, Nc, tmp);
   launch_check(c, "coarse neighbour classes");
   i64 obuf_total;
   u32 hc[8];
-  read_back(c, &obuf_total, ooff + Nc, sizeof obuf_total);
-  read_back(c, hc, nl.cnt, sizeof hc);
+  read_many(c, {{&obuf_total, ooff + Nc, sizeof obuf_total}, {hc, nl.cnt, sizeof hc}});
   if (hc[7]) {
     set_err(c, "%sa cluster's neighbour lists exceed 2^32 entries");
     throw Fail{CHP_EOVERFLOW};
@@ -282,14 +304,14 @@ void build_neighbors_merge(chp_ctx *c, Scratch &s, Owned &own, const chp_hgraph 
   u32 *count = s.get<u32>(Nc);
   launch_fill_u32(c, count, Nc, 0);
   u32 *scr = nullptr;
-  u64 per_wg = 0;
-  u32 gb = grid_big_for(hc[2]);
-  if (hc[2]) {
-    per_wg = 2ull * hc[3];
-    scr = s.get<u32>(per_wg * gb);
+  u64 per_q = 0;
+  u32 gb = grid_big_for(hc[4]);
+  if (hc[4]) {
+    per_q = (u64)hc[5];
+    scr = s.get<u32>(4 * per_q * gb);
   }
   launch_nbm_build(c, g->nb_off, g->nb, gamma, match, rep_of, ooff, obuf, count, nl, hc, scr,
-                   per_wg, gb);
+                   per_q, gb);
   scan_u32_to_i64(c, count, cg->nb_off, Nc, tmp);
   launch_check(c, "coarse neighbours");
   i64 total;
@@ -298,6 +320,49 @@ void build_neighbors_merge(chp_ctx *c, Scratch &s, Owned &own, const chp_hgraph 
   cg->nb_total = (u64)total;
   launch_nb_compact(c, Nc, ooff, obuf, cg->nb_off, cg->nb);
   launch_check(c, "coarse neighbour compaction");
+}
+
+// incidence of the coarse graph cg from the members' incidence in g
+void build_incidence_merge(chp_ctx *c, Scratch &s, Owned &own, const chp_hgraph *g,
+                           chp_hgraph *cg, const u32 *match, const u32 *rep_of) {
+  const u32 Nc = cg->n_nodes;
+  cg->n_off = own.get<i64>((u64)Nc + 1);
+  cg->n_nin = own.get<u32>(Nc);
+  u32 *bound = s.get<u32>(Nc), *cnt_tot = s.get<u32>(Nc);
+  EdgeLists el;
+  for (int k = 0; k < 3; ++k) el.list[k] = s.get<u32>(Nc);
+  el.cnt = s.get<u32>(8);
+  launch_fill_u32(c, el.cnt, 8, 0);
+  launch_cinc_classify(c, Nc, rep_of, match, g->n_off, g->n_nin, bound, cg->n_nin, cnt_tot, el);
+  i64 *ooff = s.get<i64>((u64)Nc + 1);
+  i64 *tmp = s.get<i64>(scan_tmp_words(Nc));
+  scan_u32_to_i64(c, bound, ooff, Nc, tmp);
+  launch_check(c, "coarse incidence classes");
+  i64 obuf_total;
+  u32 hc[8];
+  read_many(c, {{&obuf_total, ooff + Nc, sizeof obuf_total}, {hc, el.cnt, sizeof hc}});
+  u32 *obuf = s.get<u32>((u64)obuf_total);
+  u64 *scr = nullptr;
+  u64 per_wg = 0;
+  u32 gb = grid_big_for(hc[2]);
+  if (hc[2]) {
+    per_wg = 2ull * hc[3];
+    scr = s.get<u64>(per_wg * gb);
+  }
+  launch_cinc_build(c, g->n_off, g->n_nin, g->n_inc, rep_of, match, ooff, obuf, cg->n_nin,
+                    cnt_tot, el, hc, scr, per_wg, gb);
+  scan_u32_to_i64(c, cnt_tot, cg->n_off, Nc, tmp);
+  launch_check(c, "coarse incidence");
+  i64 total;
+  read_back(c, &total, cg->n_off + Nc, sizeof total);
+  if ((u64)total != cg->n_pins) {
+    set_err(c, "%scoarse incidence does not match the coarse pins");
+    throw Fail{CHP_EDEVICE};
+  }
+  cg->n_inc = own.get<u32>((u64)total);
+  launch_cinc_compact(c, Nc, rep_of, match, g->n_off, g->n_inc, ooff, obuf, cg->n_off,
+                      cg->n_inc);
+  launch_check(c, "coarse incidence compaction");
 }
 
 EdgeLists make_edge_lists(chp_ctx *c, Scratch &s, u32 E, const i64 *e_off, u32 hc[8]) {
@@ -510,8 +575,7 @@ int chp_build_incidence(chp_ctx *c, const chp_edges *in, const chp_params *prm,
     launch_edges_canon(c, N, E, in->e_off, in->e_nsrc, in->e_pins, g.e_pins, bad, rl);
     launch_check(c, "canonical edges");
     u32 hc[8];
-    read_back(c, hc, rl.cnt, sizeof hc);
-    f = read_flags(c);
+    read_many(c, {{hc, rl.cnt, sizeof hc}, {&f, c->flags, sizeof f}});
     if (f & FLAG_EINVAL) fail_flags(c, FLAG_EINVAL, "pins");
     if (hc[4]) {
       sort_listed_runs(c, s, g.e_pins, rl);
@@ -556,7 +620,7 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
     NbLists nl;
     nl.list[0] = s.get<u32>(N);
     nl.list[1] = s.get<u32>(N);
-    nl.list[2] = nullptr;
+    nl.list[2] = nl.list[3] = nl.list[4] = nullptr;
     nl.cnt = s.get<u32>(8);
     launch_fill_u32(c, nl.cnt, 8, 0);
     launch_rate_classify(c, N, g->nb_off, nl, target, score_fx);
@@ -597,7 +661,8 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
     launch_match(c, N, target, score_fx, ms, match, npairs);
     launch_match_write(c, N, target, ms, match, npairs);
     launch_check(c, "match");
-    u32 f = read_flags(c);
+    u32 f;
+    read_many(c, {{&f, c->flags, sizeof f}, {n_pairs_host, npairs, sizeof(u32)}});
     if (f & (FLAG_EINVAL | FLAG_EOVERFLOW)) fail_flags(c, f, "rating");
     if (f & FLAG_LONGCHAIN) {
       ms.p0 = s.get<u32>(N);
@@ -608,10 +673,9 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
       launch_fill_u32(c, npairs, 1, 0);
       launch_match_write(c, N, target, ms, match, npairs);
       launch_check(c, "match (long chains)");
-      f = read_flags(c);
+      read_many(c, {{&f, c->flags, sizeof f}, {n_pairs_host, npairs, sizeof(u32)}});
       if (f & FLAG_ECYCLE) fail_flags(c, FLAG_ECYCLE, "matching");
     }
-    read_back(c, n_pairs_host, npairs, sizeof(u32));
   });
 }
 
@@ -634,8 +698,8 @@ int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
     scan_u32_to_i64(c, is_rep, rank, N, tmp);
     launch_check(c, "representatives");
     i64 nc;
-    read_back(c, &nc, rank + N, sizeof nc);
-    u32 f = read_flags(c);
+    u32 f;
+    read_many(c, {{&nc, rank + N, sizeof nc}, {&f, c->flags, sizeof f}});
     if (f & FLAG_EINVAL) fail_flags(c, FLAG_EINVAL, "match is not a symmetric pairing");
     chp_hgraph cg;
     memset(&cg, 0, sizeof cg);
@@ -646,7 +710,8 @@ int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
     cg.e_off = own.get<i64>((u64)E + 1);
     cg.e_nsrc = own.get<u32>(E);
     d2d(c, cg.e_w, g->e_w, sizeof(u32) * (size_t)E);
-    launch_gamma(c, N, match, rank, g->n_size, gamma, cg.n_size);
+    u32 *rep_of = s.get<u32>((u64)nc);
+    launch_gamma(c, N, match, rank, g->n_size, gamma, cg.n_size, rep_of);
     u32 hc[8];
     EdgeLists el = make_edge_lists(c, s, E, g->e_off, hc);
     u64 *scr = nullptr;
@@ -669,9 +734,9 @@ int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
     launch_pins_compact(c, E, g->e_off, opins, cg.e_off, cg.e_pins);
     launch_check(c, "coarse pins");
     s.release(opins);
-    build_incidence_core(c, s, own, &cg, ~0ull, NONE32);
+    build_incidence_merge(c, s, own, g, &cg, match, rep_of);
     if (build_neighbors) {
-      if (g->nb_off && g->nb) build_neighbors_merge(c, s, own, g, &cg, match, rank, gamma);
+      if (g->nb_off && g->nb) build_neighbors_merge(c, s, own, g, &cg, match, rep_of, gamma);
       else build_neighbors_core(c, s, own, &cg);
     }
     hip_check(c, hipStreamSynchronize(c->stream), "contract");
@@ -716,8 +781,8 @@ int chp_evaluate_partition(chp_ctx *c, const chp_hgraph *g, const u32 *rho, u32 
     launch_eval_parts(c, k, part_size, part_inb, part_cnt, prm->omega, prm->delta, summary);
     launch_check(c, "evaluate");
     u64 sum[8];
-    read_back(c, sum, summary, sizeof sum);
-    u32 f = read_flags(c);
+    u32 f;
+    read_many(c, {{sum, summary, sizeof sum}, {&f, c->flags, sizeof f}});
     if (f & FLAG_EINVAL) fail_flags(c, FLAG_EINVAL, "rho has an entry >= k");
     memcpy(summary_host, sum, sizeof sum);
   });

@@ -248,6 +248,78 @@ __device__ __forceinline__ K wave_sort64(K v) {
   return v;
 }
 
+// Sorted keys s[0,m) of the form (value << 1 | tag); each group of equal
+// value is represented by its first key, whose tag is the group's smallest.
+// Writes the distinct values of the groups whose first tag is FIRST_TAG to
+// out[0, n_first), then the others to out[n_first, n_total).  Works on LDS or
+// global keys; every thread of the workgroup calls it.
+template <int BLOCK, u32 FIRST_TAG>
+__device__ void group_split_emit(const u64 *s, u32 m, u32 *out, u32 &n_first, u32 &n_total,
+                                 u32 *s_red) {
+  u32 nf = 0, no = 0;
+  for (u32 c0 = 0; c0 < m; c0 += BLOCK) {
+    const u32 i = c0 + threadIdx.x;
+    const u64 k = i < m ? s[i] : 0;
+    const bool f = i < m && (i == 0 || (s[i - 1] >> 1) != (k >> 1));
+    nf += wg_sum<BLOCK>((u32)(f && (u32)(k & 1) == FIRST_TAG), s_red);
+    no += wg_sum<BLOCK>((u32)(f && (u32)(k & 1) != FIRST_TAG), s_red);
+  }
+  u32 rf = 0, ro = 0;
+  for (u32 c0 = 0; c0 < m; c0 += BLOCK) {
+    const u32 i = c0 + threadIdx.x;
+    const u64 k = i < m ? s[i] : 0;
+    const bool f = i < m && (i == 0 || (s[i - 1] >> 1) != (k >> 1));
+    const bool ff = f && (u32)(k & 1) == FIRST_TAG, fo = f && (u32)(k & 1) != FIRST_TAG;
+    u32 tf, to;
+    const u32 of = wg_excl_scan<BLOCK>((u32)ff, s_red, &tf);
+    const u32 oo = wg_excl_scan<BLOCK>((u32)fo, s_red, &to);
+    if (ff) out[rf + of] = (u32)(k >> 1);
+    if (fo) out[nf + ro + oo] = (u32)(k >> 1);
+    rf += tf;
+    ro += to;
+  }
+  n_first = nf;
+  n_total = nf + no;
+}
+
+// The same for one wave holding one key per lane (sorted across lanes, keys
+// of lanes >= m are the maximum key).
+template <u32 FIRST_TAG>
+__device__ __forceinline__ void wave_group_split_emit(u64 key, u32 m, u32 *out, u32 &n_first,
+                                                      u32 &n_total) {
+  const u32 l = lane_id();
+  const u64 prev = __shfl_up(key, 1, WAVE);
+  const bool f = l < m && (l == 0 || (prev >> 1) != (key >> 1));
+  const bool ff = f && (u32)(key & 1) == FIRST_TAG;
+  const u64 fm = __ballot(ff), om = __ballot(f && !ff);
+  const u64 lt = (1ull << l) - 1;
+  const u32 nf = (u32)__popcll(fm);
+  if (f) out[ff ? (u32)__popcll(fm & lt) : nf + (u32)__popcll(om & lt)] = (u32)(key >> 1);
+  n_first = nf;
+  n_total = nf + (u32)__popcll(om);
+}
+
+// Write the unique keys of sorted src[0,m) other than `skip` to out; returns
+// the count (all threads).
+template <int BLOCK>
+__device__ u32 unique_out(const u32 *src, u64 m, u32 skip, u32 *out, u32 *s_red) {
+  u32 run = 0;
+  for (u64 c0 = 0; c0 < m; c0 += BLOCK) {
+    u64 i = c0 + threadIdx.x;
+    bool keep = false;
+    u32 v = 0;
+    if (i < m) {
+      v = src[i];
+      keep = v != skip && v != NONE32 && (i == 0 || src[i - 1] != v);
+    }
+    u32 tot;
+    u32 off = wg_excl_scan<BLOCK>((u32)keep, s_red, &tot);
+    if (keep) out[run + off] = v;
+    run += tot;
+  }
+  return run;
+}
+
 // ---- rating noise ---------------------------------------------------------
 // One output of splitmix64 (Steele, Lea & Flood, OOPSLA 2014) from `state`.
 __device__ __forceinline__ u64 splitmix64_out(u64 state) {

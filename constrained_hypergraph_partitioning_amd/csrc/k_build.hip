@@ -252,58 +252,7 @@ __global__ void k_nb_classify(u32 N, const i64 *e_off, const i64 *n_off, const u
     const u32 slot = wave_append(&nl.cnt[k], c == k);
     if (c == k) nl.list[k][slot] = n;
   }
-  if (c == 2) atomicMax(&nl.cnt[3], (u32)w);
-}
-
-// Coarse neighbourhoods by merging the members' lists: for the cluster c =
-// {a, b}, N'(c) = sort-unique(gamma(N(a)) u gamma(N(b))) minus c, which is
-// N(c) on the coarse graph since a coarse hyperedge is gamma of its fine one.
-// The bound |N(a)| + |N(b)| decides the class.
-__global__ void k_nbm_classify(u32 N, const u32 *match, const i64 *rank, const i64 *nb_off,
-                               u32 *rep_of, u32 *bound, NbLists nl) {
-  const u32 n = blockIdx.x * blockDim.x + threadIdx.x;
-  u64 w = 0;
-  bool rep = false;
-  u32 cid = 0;
-  if (n < N) {
-    const u32 m = match[n];
-    rep = m >= n;
-    if (rep) {
-      cid = (u32)rank[n];
-      w = (u64)(nb_off[n + 1] - nb_off[n]);
-      if (m != n) w += (u64)(nb_off[m + 1] - nb_off[m]);
-      if (w > 0xFFFFFFFFull) {
-        atomicOr(nl.cnt + 7, 1u);
-        w = 0;
-      }
-      rep_of[cid] = n;
-      bound[cid] = (u32)w;
-    }
-  }
-  const int c = (!rep || w == 0) ? 3 : (w <= 64 ? 0 : (w <= LDS_CAP_U32 ? 1 : 2));
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    const u32 slot = wave_append(&nl.cnt[k], c == k);
-    if (c == k) nl.list[k][slot] = cid;
-  }
-  if (c == 2) atomicMax(&nl.cnt[3], (u32)w);
-}
-
-// gather gamma of the members' neighbour lists into dst (m = ka + kb keys)
-template <int BLOCK>
-__device__ void gather_members(const i64 *nb_off, const u32 *nb, const u32 *gamma, u32 a, u32 b,
-                               u32 *dst, u32 *m_out) {
-  const i64 a0 = nb_off[a];
-  const u32 ka = (u32)(nb_off[a + 1] - a0);
-  i64 b0 = 0;
-  u32 kb = 0;
-  if (b != a) {
-    b0 = nb_off[b];
-    kb = (u32)(nb_off[b + 1] - b0);
-  }
-  for (u32 i = threadIdx.x; i < ka + kb; i += BLOCK)
-    dst[i] = gamma[i < ka ? nb[a0 + i] : nb[b0 + (i - ka)]];
-  *m_out = ka + kb;
+  if (c == 2) atomicMax(&nl.cnt[5], (u32)w);
 }
 
 // wave per node, W_n <= 64: gather into lanes, sort, unique, drop n
@@ -376,27 +325,6 @@ __device__ u64 gather_pins(const i64 *e_off, const u32 *pins, const u32 *n_inc, 
   return base;
 }
 
-// Write the unique keys of sorted src[0,m) other than `skip` to out; returns
-// the count (all threads).
-template <int BLOCK>
-__device__ u32 unique_out(const u32 *src, u64 m, u32 skip, u32 *out, u32 *s_red) {
-  u32 run = 0;
-  for (u64 c0 = 0; c0 < m; c0 += BLOCK) {
-    u64 i = c0 + threadIdx.x;
-    bool keep = false;
-    u32 v = 0;
-    if (i < m) {
-      v = src[i];
-      keep = v != skip && v != NONE32 && (i == 0 || src[i - 1] != v);
-    }
-    u32 tot;
-    u32 off = wg_excl_scan<BLOCK>((u32)keep, s_red, &tot);
-    if (keep) out[run + off] = v;
-    run += tot;
-  }
-  return run;
-}
-
 template <int BLOCK, int CAP>
 __global__ __launch_bounds__(BLOCK) void k_nb_lds(const i64 *e_off, const u32 *pins,
                                                   const i64 *n_off, const u32 *n_inc,
@@ -441,83 +369,6 @@ __global__ __launch_bounds__(BLOCK) void k_nb_global(const i64 *e_off, const u32
     u32 *res = wg_sort_global<BLOCK, CAP>(A, B, m, s);
     u32 c = unique_out<BLOCK>(res, m, n, obuf + ooff[n], s_red);
     if (threadIdx.x == 0) count[n] = c;
-    __syncthreads();
-  }
-}
-
-__global__ __launch_bounds__(256) void k_nbm_wave(const i64 *nb_off, const u32 *nb,
-                                                  const u32 *gamma, const u32 *match,
-                                                  const u32 *rep_of, const i64 *ooff, u32 *obuf,
-                                                  u32 *count, const u32 *list, const u32 *cnt) {
-  const u32 total = *cnt;
-  const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
-  const u32 l = lane_id();
-  for (u32 w = blockIdx.x * (blockDim.x / WAVE) + wave_id(); w < total; w += nwaves) {
-    const u32 c = list[w];
-    const u32 a = rep_of[c], b = match[a];
-    const i64 a0 = nb_off[a];
-    const u32 ka = (u32)(nb_off[a + 1] - a0);
-    i64 b0 = 0;
-    u32 kb = 0;
-    if (b != a) {
-      b0 = nb_off[b];
-      kb = (u32)(nb_off[b + 1] - b0);
-    }
-    u32 v = NONE32;
-    if (l < ka + kb) v = gamma[l < ka ? nb[a0 + l] : nb[b0 + (l - ka)]];
-    v = wave_sort64(v);
-    const u32 prev = __shfl_up(v, 1, WAVE);
-    const bool keep = v != NONE32 && v != c && (l == 0 || prev != v);
-    const u64 mask = __ballot(keep);
-    const u32 pos = (u32)__popcll(mask & ((1ull << l) - 1));
-    if (keep) obuf[ooff[c] + pos] = v;
-    if (l == 0) count[c] = (u32)__popcll(mask);
-  }
-}
-
-template <int BLOCK, int CAP>
-__global__ __launch_bounds__(BLOCK) void k_nbm_lds(const i64 *nb_off, const u32 *nb,
-                                                   const u32 *gamma, const u32 *match,
-                                                   const u32 *rep_of, const i64 *ooff, u32 *obuf,
-                                                   u32 *count, const u32 *list, const u32 *cnt) {
-  __shared__ u32 s[CAP];
-  __shared__ u32 s_red[BLOCK / WAVE + 1];
-  const u32 total = *cnt;
-  for (u32 w = blockIdx.x; w < total; w += gridDim.x) {
-    const u32 c = list[w];
-    const u32 a = rep_of[c];
-    u32 m;
-    gather_members<BLOCK>(nb_off, nb, gamma, a, match[a], s, &m);
-    const u32 p = next_pow2(m);
-    for (u32 i = m + threadIdx.x; i < p; i += BLOCK) s[i] = NONE32;
-    __syncthreads();
-    lds_bitonic<BLOCK>(s, p);
-    const u32 k = unique_out<BLOCK>(s, m, c, obuf + ooff[c], s_red);
-    if (threadIdx.x == 0) count[c] = k;
-    __syncthreads();
-  }
-}
-
-template <int BLOCK, int CAP>
-__global__ __launch_bounds__(BLOCK) void k_nbm_global(const i64 *nb_off, const u32 *nb,
-                                                      const u32 *gamma, const u32 *match,
-                                                      const u32 *rep_of, const i64 *ooff,
-                                                      u32 *obuf, u32 *count, const u32 *list,
-                                                      const u32 *cnt, u32 *scratch, u64 per_wg) {
-  __shared__ u32 s[CAP];
-  __shared__ u32 s_red[BLOCK / WAVE + 1];
-  const u32 total = *cnt;
-  u32 *A = scratch + (u64)blockIdx.x * per_wg;
-  u32 *B = A + per_wg / 2;
-  for (u32 w = blockIdx.x; w < total; w += gridDim.x) {
-    const u32 c = list[w];
-    const u32 a = rep_of[c];
-    u32 m;
-    gather_members<BLOCK>(nb_off, nb, gamma, a, match[a], A, &m);
-    __syncthreads();
-    u32 *res = wg_sort_global<BLOCK, CAP>(A, B, m, s);
-    const u32 k = unique_out<BLOCK>(res, m, c, obuf + ooff[c], s_red);
-    if (threadIdx.x == 0) count[c] = k;
     __syncthreads();
   }
 }
@@ -615,31 +466,6 @@ void launch_nb_build(chp_ctx *c, u32 N, const i64 *e_off, const u32 *pins, const
   if (host_cnt[2])
     CHP_LAUNCH(c, "nb_global", (k_nb_global<256, LDS_CAP_U32>), grid_big, 256, 0, e_off, pins,
                n_off, n_inc, ooff, obuf, count, nl.list[2], nl.cnt + 2, scratch, scratch_per_wg);
-}
-
-void launch_nbm_classify(chp_ctx *c, u32 N, const u32 *match, const i64 *rank,
-                         const i64 *nb_off, u32 *rep_of, u32 *bound, NbLists nl) {
-  if (N == 0) return;
-  CHP_LAUNCH(c, "nbm_classify", k_nbm_classify, grid_for(N, 256), 256, 0, N, match, rank, nb_off,
-             rep_of, bound, nl);
-}
-
-void launch_nbm_build(chp_ctx *c, const i64 *nb_off, const u32 *nb, const u32 *gamma,
-                      const u32 *match, const u32 *rep_of, const i64 *ooff, u32 *obuf,
-                      u32 *count, NbLists nl, const u32 *host_cnt, u32 *scratch,
-                      u64 scratch_per_wg, u32 grid_big) {
-  if (host_cnt[0])
-    CHP_LAUNCH(c, "nbm_wave", k_nbm_wave, waves_grid(host_cnt[0]), 256, 0, nb_off, nb, gamma,
-               match, rep_of, ooff, obuf, count, (const u32 *)nl.list[0],
-               (const u32 *)nl.cnt + 0);
-  if (host_cnt[1])
-    CHP_LAUNCH(c, "nbm_lds", (k_nbm_lds<256, LDS_CAP_U32>),
-               host_cnt[1] > 8192 ? 8192 : host_cnt[1], 256, 0, nb_off, nb, gamma, match, rep_of,
-               ooff, obuf, count, (const u32 *)nl.list[1], (const u32 *)nl.cnt + 1);
-  if (host_cnt[2])
-    CHP_LAUNCH(c, "nbm_global", (k_nbm_global<256, LDS_CAP_U32>), grid_big, 256, 0, nb_off, nb,
-               gamma, match, rep_of, ooff, obuf, count, (const u32 *)nl.list[2],
-               (const u32 *)nl.cnt + 2, scratch, scratch_per_wg);
 }
 
 void launch_nb_compact(chp_ctx *c, u32 N, const i64 *ooff, const u32 *obuf, const i64 *nb_off,

@@ -23,14 +23,17 @@ __global__ void k_rep(u32 N, const u32 *match, u32 *is_rep, u32 *flags) {
 }
 
 __global__ void k_gamma(u32 N, const u32 *match, const i64 *rank, const u32 *n_size, u32 *gamma,
-                        u32 *c_size) {
+                        u32 *c_size, u32 *rep_of) {
   u32 n = blockIdx.x * blockDim.x + threadIdx.x;
   if (n >= N) return;
   u32 m = match[n];
   u32 r = m < n ? m : n;
   u32 g = (u32)rank[r];
   gamma[n] = g;
-  if (r == n) c_size[g] = n_size[n] + (m != n ? n_size[m] : 0u);
+  if (r == n) {
+    c_size[g] = n_size[n] + (m != n ? n_size[m] : 0u);
+    rep_of[g] = n;
+  }
 }
 
 __global__ void k_edge_classify(u32 E, const i64 *e_off, EdgeLists el) {
@@ -62,53 +65,23 @@ __global__ __launch_bounds__(256) void k_econ_wave(const i64 *e_off, const u32 *
     u64 key = ~0ull;
     if (l < len) key = ((u64)gamma[pins[a + l]] << 1) | (l < ns ? 1u : 0u);
     key = wave_sort64(key);
-    const u64 prev = __shfl_up(key, 1, WAVE);
-    const bool first = l < len && (l == 0 || (prev >> 1) != (key >> 1));
-    const u64 sm = __ballot(first && (key & 1));
-    const u64 dm = __ballot(first && !(key & 1));
-    const u32 nsp = (u32)__popcll(sm);
-    if (first) {
-      const u32 pos = (key & 1) ? (u32)__popcll(sm & lt) : nsp + (u32)__popcll(dm & lt);
-      opins[a + pos] = (u32)(key >> 1);
-    }
+    u32 nsp, ntot;
+    wave_group_split_emit<1>(key, len, opins + a, nsp, ntot);
     if (l == 0) {
-      olen[e] = nsp + (u32)__popcll(dm);
+      olen[e] = ntot;
       onsrc[e] = nsp;
     }
   }
 }
 
-// Split the sorted keys s[0,m) into distinct sources (first) and distinct
-// destinations; works on LDS or global keys.
+// distinct sources first (tag 1), then the distinct destinations
 template <int BLOCK>
 __device__ void econ_emit(const u64 *s, u32 m, u32 *out, u32 *olen, u32 *onsrc, u32 e,
                           u32 *s_red) {
-  u32 nsrc = 0, ndst = 0;
-  for (u32 c0 = 0; c0 < m; c0 += BLOCK) {
-    u32 i = c0 + threadIdx.x;
-    bool f = i < m && (i == 0 || (s[i - 1] >> 1) != (s[i] >> 1));
-    u32 ts, td;
-    wg_excl_scan<BLOCK>((u32)(f && (s[i < m ? i : 0] & 1)), s_red, &ts);
-    wg_excl_scan<BLOCK>((u32)(f && !(s[i < m ? i : 0] & 1)), s_red, &td);
-    nsrc += ts;
-    ndst += td;
-  }
-  u32 rs = 0, rd = 0;
-  for (u32 c0 = 0; c0 < m; c0 += BLOCK) {
-    u32 i = c0 + threadIdx.x;
-    u64 k = i < m ? s[i] : 0;
-    bool f = i < m && (i == 0 || (s[i - 1] >> 1) != (k >> 1));
-    bool fs = f && (k & 1), fd = f && !(k & 1);
-    u32 ts, td;
-    u32 os = wg_excl_scan<BLOCK>((u32)fs, s_red, &ts);
-    u32 od = wg_excl_scan<BLOCK>((u32)fd, s_red, &td);
-    if (fs) out[rs + os] = (u32)(k >> 1);
-    if (fd) out[nsrc + rd + od] = (u32)(k >> 1);
-    rs += ts;
-    rd += td;
-  }
+  u32 nsrc, ntot;
+  group_split_emit<BLOCK, 1>(s, m, out, nsrc, ntot, s_red);
   if (threadIdx.x == 0) {
-    olen[e] = nsrc + ndst;
+    olen[e] = ntot;
     onsrc[e] = nsrc;
   }
 }
@@ -180,10 +153,10 @@ void launch_rep(chp_ctx *c, u32 N, const u32 *match, u32 *is_rep) {
 }
 
 void launch_gamma(chp_ctx *c, u32 N, const u32 *match, const i64 *rank, const u32 *n_size,
-                  u32 *gamma, u32 *c_size) {
+                  u32 *gamma, u32 *c_size, u32 *rep_of) {
   if (N == 0) return;
   CHP_LAUNCH(c, "gamma", k_gamma, grid_for(N, 256), 256, 0, N, match, rank, n_size, gamma,
-             c_size);
+             c_size, rep_of);
 }
 
 void launch_edge_classify(chp_ctx *c, u32 E, const i64 *e_off, EdgeLists el) {

@@ -47,21 +47,38 @@ __global__ __launch_bounds__(TB) void k_terms(u32 E, const i64 *e_off, const u32
   }
 }
 
-// cap = floor(sum t / (10 |E|)), d = cap + 1, magic = floor((2^64-1)/d)
-__global__ void k_cap(u32 nparts, const u64 *partials, u32 E, u64 *capinfo) {
-  if (threadIdx.x != 0) return;
+// cap = floor(sum t / (10 |E|)), d = cap + 1, magic = floor((2^64-1)/d).
+// One workgroup adds the 128-bit partial sums, thread 0 divides.
+__global__ __launch_bounds__(TB) void k_cap(u32 nparts, const u64 *partials, u32 E,
+                                            u64 *capinfo) {
+  __shared__ u64 lo_s[TB], hi_s[TB];
   u64 lo = 0, hi = 0;
-  for (u32 i = 0; i < nparts; ++i) {
-    u64 r = lo + partials[2 * i];
+  for (u32 i = threadIdx.x; i < nparts; i += TB) {
+    const u64 r = lo + partials[2 * i];
     hi += partials[2 * i + 1] + (r < lo ? 1 : 0);
     lo = r;
   }
+  lo_s[threadIdx.x] = lo;
+  hi_s[threadIdx.x] = hi;
+  __syncthreads();
+  for (int st = TB / 2; st > 0; st >>= 1) {
+    if ((int)threadIdx.x < st) {
+      const u64 a = lo_s[threadIdx.x], b = lo_s[threadIdx.x + st];
+      const u64 r = a + b;
+      hi_s[threadIdx.x] += hi_s[threadIdx.x + st] + (r < a ? 1 : 0);
+      lo_s[threadIdx.x] = r;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x != 0) return;
+  lo = lo_s[0];
+  hi = hi_s[0];
   u64 cap = 0;
   if (E) {
     const u64 dv = 10ull * E;
     u64 rem = 0, q = 0;
     for (int bit = 127; bit >= 0; --bit) {
-      u64 b = bit >= 64 ? (hi >> (bit - 64)) & 1 : (lo >> bit) & 1;
+      const u64 b = bit >= 64 ? (hi >> (bit - 64)) & 1 : (lo >> bit) & 1;
       rem = (rem << 1) | b;
       u64 qb = 0;
       if (rem >= dv) {
@@ -272,14 +289,10 @@ __device__ void rate_heavy(const RateArgs &A, HeavySmem &S, u32 n, u64 cap, u64 
   const bool clip = K > H_CAP;
   NodeBest best{0, NONE32};
   u64 tsum = 0;
+  // the table is empty on entry (cleared at kernel start, and by every
+  // candidate scan below as it reads each slot)
   for (u32 s0 = 0; s0 < K; s0 += H_CAP) {
     const u32 cw = (K - s0) < H_CAP ? (K - s0) : H_CAP;
-    for (u32 i = tid; i < H_T; i += RB) {
-      S.key[i] = EMPTY;
-      S.eta[i] = 0;
-      S.inter[i] = 0;
-    }
-    __syncthreads();
     for (u32 i = tid; i < cw; i += RB) h_insert(S.key, H_T - 1, H_SHIFT, A.nb[nb0 + s0 + i]);
     const u32 lo = A.nb[nb0 + s0], hi = A.nb[nb0 + s0 + cw - 1];
     __syncthreads();
@@ -306,8 +319,12 @@ __device__ void rate_heavy(const RateArgs &A, HeavySmem &S, u32 n, u64 cap, u64 
     }
     for (u32 i = tid; i < H_T; i += RB) {
       const u32 m = S.key[i];
-      if (m != EMPTY) consider(A, n, nin, size_n, m, S.eta[i], S.inter[i], ub_add, dmod, magic,
-                               best);
+      if (m != EMPTY) {
+        consider(A, n, nin, size_n, m, S.eta[i], S.inter[i], ub_add, dmod, magic, best);
+        S.key[i] = EMPTY;
+        S.eta[i] = 0;
+        S.inter[i] = 0;
+      }
     }
     __syncthreads();
   }
@@ -331,12 +348,7 @@ __device__ void rate_light(const RateArgs &A, LightWave &S, u32 n, u64 cap, u64 
   const u64 ub_add = A.noise_on ? cap : 0;
   NodeBest best{0, NONE32};
   u64 tsum = 0;
-  for (u32 i = l; i < L_T; i += WAVE) {
-    S.key[i] = EMPTY;
-    S.eta[i] = 0;
-    S.inter[i] = 0;
-  }
-  wave_sync();
+  // the wave's table is empty on entry (see the candidate scan)
   for (u32 i = l; i < K; i += WAVE) h_insert(S.key, L_T - 1, L_SHIFT, A.nb[nb0 + i]);
   wave_sync();
   for (i64 c0 = i0; c0 < i1; c0 += L_ECH) {
@@ -363,8 +375,12 @@ __device__ void rate_light(const RateArgs &A, LightWave &S, u32 n, u64 cap, u64 
   }
   for (u32 i = l; i < L_T; i += WAVE) {
     const u32 m = S.key[i];
-    if (m != EMPTY) consider(A, n, nin, size_n, m, S.eta[i], S.inter[i], ub_add, dmod, magic,
-                             best);
+    if (m != EMPTY) {
+      consider(A, n, nin, size_n, m, S.eta[i], S.inter[i], ub_add, dmod, magic, best);
+      S.key[i] = EMPTY;
+      S.eta[i] = 0;
+      S.inter[i] = 0;
+    }
   }
   tsum = wg_sat_sum<WAVE>(tsum, nullptr);
   wg_best<WAVE>(best.e, best.i, nullptr, nullptr);
@@ -377,18 +393,25 @@ __device__ void rate_light(const RateArgs &A, LightWave &S, u32 n, u64 cap, u64 
 }
 
 // cnt[0] light nodes in light[], cnt[1] heavy nodes in heavy[]; work[0..1]
-// are zeroed work counters
+// are zeroed work counters.  Heavy nodes are taken one per workgroup, then
+// light ones one per wave, each from its counter (node costs are heavy
+// tailed, so a static deal leaves some workgroups far behind).  The work
+// index is a scalar (readfirstlane) and each loop body ends with a barrier (a
+// wave barrier for the light loop), so every lane reconverges before the
+// back edge: without that the compiler may route thread 0, which alone takes
+// the next item, around the other lanes, which then re-enter the loop on the
+// stale item and never leave.
 __global__ __launch_bounds__(RB) void k_rate(RateArgs A, const u32 *light, const u32 *heavy,
                                              const u32 *cnt, u32 *work) {
   __shared__ RateSmem sm;
   __shared__ u32 s_item;
   const u32 nl = cnt[0], nh = cnt[1];
   const u64 cap = A.capinfo[0], dmod = A.capinfo[1], magic = A.capinfo[2];
-  // Dynamic work loop.  The work index is a scalar (readfirstlane) and the
-  // body ends with a barrier, so every lane reconverges before the back edge:
-  // without it the compiler may route thread 0 (which alone stores the result
-  // and takes the next item) around the other lanes, which then re-enter the
-  // barrier on the stale item and never leave.
+  for (u32 i = threadIdx.x; i < H_T; i += RB) {
+    sm.h.key[i] = EMPTY;
+    sm.h.eta[i] = 0;
+    sm.h.inter[i] = 0;
+  }
   for (;;) {
     if (threadIdx.x == 0) s_item = atomicAdd(&work[0], 1u);
     __syncthreads();
@@ -399,12 +422,19 @@ __global__ __launch_bounds__(RB) void k_rate(RateArgs A, const u32 *light, const
     __syncthreads();
   }
   LightWave &S = sm.l[wave_id()];
+  for (u32 i = lane_id(); i < L_T; i += WAVE) {
+    S.key[i] = EMPTY;
+    S.eta[i] = 0;
+    S.inter[i] = 0;
+  }
+  wave_sync();
   for (;;) {
     u32 w = 0;
     if (lane_id() == 0) w = atomicAdd(&work[1], 1u);
     w = __builtin_amdgcn_readfirstlane(__shfl(w, 0, WAVE));
     if (w >= nl) break;
     rate_light(A, S, light[w], cap, dmod, magic);
+    wave_sync();
   }
 }
 
@@ -537,7 +567,7 @@ void launch_terms(chp_ctx *c, u32 E, const i64 *e_off, const u32 *e_w, u64 *t, u
                   u32 nparts, u64 *capinfo) {
   if (E)
     CHP_LAUNCH(c, "terms", k_terms, nparts, TB, 0, E, e_off, e_w, t, partials);
-  CHP_LAUNCH(c, "cap", k_cap, 1, 64, 0, E ? nparts : 0u, (const u64 *)partials, E, capinfo);
+  CHP_LAUNCH(c, "cap", k_cap, 1, TB, 0, E ? nparts : 0u, (const u64 *)partials, E, capinfo);
 }
 
 void launch_rate_classify(chp_ctx *c, u32 N, const i64 *nb_off, NbLists nl, u32 *target,

@@ -5,6 +5,7 @@
 constexpr u32 LDS_CAP_U32 = 8192;   // u32 keys one workgroup sorts in LDS
 constexpr u32 LDS_CAP_U64 = 8192;   // u64 keys one workgroup sorts in LDS
 constexpr u32 RATE_SMALL_CAP = 384; // |N(n)| of a node rated by one wave
+constexpr u32 NBM_LDS_CAP = 8192;   // largest coarse neighbour bound merged in LDS
 
 // Runs to sort in place, bucketed by length: class 0 (<= 64 keys, one wave
 // each), class 1 (<= LDS_CAP_U32 keys, one workgroup in LDS), class 2
@@ -16,9 +17,10 @@ struct RunLists {
   u32 *cnt;  // device [8]
 };
 
-// Node work lists by class; cnt[0..2] counts, cnt[3] = max work of class 2.
+// Node work lists by class: cnt[0..4] class counts, cnt[5] = largest work of
+// the last (global-memory) class, cnt[7] = overflow flag.
 struct NbLists {
-  u32 *list[3];
+  u32 *list[5];
   u32 *cnt;  // device [8]
 };
 
@@ -50,12 +52,6 @@ void launch_nb_classify(chp_ctx *c, u32 N, const i64 *e_off, const i64 *n_off, c
 void launch_nb_build(chp_ctx *c, u32 N, const i64 *e_off, const u32 *pins, const i64 *n_off,
                      const u32 *n_inc, const i64 *ooff, u32 *obuf, u32 *count, NbLists nl,
                      const u32 *host_cnt, u32 *scratch, u64 scratch_per_wg, u32 grid_big);
-void launch_nbm_classify(chp_ctx *c, u32 N, const u32 *match, const i64 *rank,
-                         const i64 *nb_off, u32 *rep_of, u32 *bound, NbLists nl);
-void launch_nbm_build(chp_ctx *c, const i64 *nb_off, const u32 *nb, const u32 *gamma,
-                      const u32 *match, const u32 *rep_of, const i64 *ooff, u32 *obuf,
-                      u32 *count, NbLists nl, const u32 *host_cnt, u32 *scratch,
-                      u64 scratch_per_wg, u32 grid_big);
 void launch_nb_compact(chp_ctx *c, u32 N, const i64 *ooff, const u32 *obuf, const i64 *nb_off,
                        u32 *nb);
 
@@ -105,13 +101,31 @@ void launch_match_write(chp_ctx *c, u32 N, const u32 *target, MatchScratch ms, u
 // ---- k_contract.hip --------------------------------------------------------
 void launch_rep(chp_ctx *c, u32 N, const u32 *match, u32 *is_rep);
 void launch_gamma(chp_ctx *c, u32 N, const u32 *match, const i64 *rank, const u32 *n_size,
-                  u32 *gamma, u32 *c_size);
+                  u32 *gamma, u32 *c_size, u32 *rep_of);
 void launch_edge_classify(chp_ctx *c, u32 E, const i64 *e_off, EdgeLists el);
 void launch_edge_contract(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
                           const u32 *gamma, u32 *opins, u32 *olen, u32 *onsrc, EdgeLists el,
                           const u32 *host_cnt, u64 *scratch, u64 per_wg, u32 grid_big);
 void launch_pins_compact(chp_ctx *c, u32 E, const i64 *src_off, const u32 *src,
                          const i64 *dst_off, u32 *dst);
+
+// ---- k_coarse.hip : coarse incidence and neighbourhoods from the members ---
+void launch_cinc_classify(chp_ctx *c, u32 Nc, const u32 *rep_of, const u32 *match,
+                          const i64 *n_off, const u32 *n_nin, u32 *bound, u32 *cnt_in,
+                          u32 *cnt_tot, EdgeLists el);
+void launch_cinc_build(chp_ctx *c, const i64 *n_off, const u32 *n_nin, const u32 *n_inc,
+                       const u32 *rep_of, const u32 *match, const i64 *ooff, u32 *obuf,
+                       u32 *cnt_in, u32 *cnt_tot, EdgeLists el, const u32 *host_cnt,
+                       u64 *scratch, u64 per_wg, u32 grid_big);
+void launch_cinc_compact(chp_ctx *c, u32 Nc, const u32 *rep_of, const u32 *match,
+                         const i64 *n_off, const u32 *n_inc, const i64 *ooff, const u32 *obuf,
+                         const i64 *c_off, u32 *c_inc);
+void launch_nbm_classify(chp_ctx *c, u32 Nc, const u32 *rep_of, const u32 *match,
+                         const i64 *nb_off, u32 *bound, NbLists nl);
+void launch_nbm_build(chp_ctx *c, const i64 *nb_off, const u32 *nb, const u32 *gamma,
+                      const u32 *match, const u32 *rep_of, const i64 *ooff, u32 *obuf,
+                      u32 *count, NbLists nl, const u32 *host_cnt, u32 *scratch, u64 per_q,
+                      u32 grid_big);
 
 // ---- k_eval.hip --------------------------------------------------------------
 void launch_eval_nodes(chp_ctx *c, u32 N, const u32 *rho, u32 k, const u32 *n_size,
