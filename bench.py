@@ -37,6 +37,9 @@ def parse():
     p.add_argument("--nodes", type=int, default=None, help="shrink the workload (testing)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-nodes", type=int, default=None)
+    p.add_argument("--copy-ref-mib", type=int, default=0,
+                   help="run one plain device copy of this size first (a reference for "
+                        "scaling hardware byte counters)")
     return p.parse_args()
 
 
@@ -119,6 +122,11 @@ def main():
     ctx = chp.Context(0)
     dev_edges = chp.upload_edges(h)
     rho_buf = torch.empty(h.n_nodes, dtype=torch.int32, device=ctx.device)
+    if args.copy_ref_mib:
+        src = torch.ones(args.copy_ref_mib << 18, dtype=torch.int32, device=ctx.device)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        del src, dst
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):

@@ -132,22 +132,29 @@ __device__ __forceinline__ u64 wg_sat_sum(u64 v, u64 *lds) {
 }
 
 // ---------------------------------------------------------------------------
-// Rating kernel: one launch per level.  A node with more than L_CAP
+// Rating kernel: one launch per level.  A node with more than RATE_SMALL_CAP
 // neighbours ("heavy") takes a whole workgroup, a "light" node one wave; both
 // pull nodes from a work counter, heavy ones first.
 //
 // Per node the neighbour list N(n) is loaded, a window of at most H_CAP ids at
-// a time (L_CAP for a light node, whose list always fits), into an LDS hash
-// table whose slots are the accumulation bins: eta(n,m) (u64 fixed point) and
-// inter(n,m).  Incident hyperedges are taken a chunk at a time; each brings a
-// source run and a destination run of its pin list (for a windowed node,
-// clipped by binary search to the window's id interval, as the runs and N(n)
-// are sorted).  A workgroup scan lays the runs end to end and every thread
+// a time (a light node's list always fits one), into an LDS hash table whose
+// slots are the bins of m in N(n):
+//   eta  u64  eta(n,m) in fixed point; bit 63 set when size(n)+size(m) > Omega
+//             (free: a node whose terms plus the noise cap reach 2^63 is an
+//             overflow error anyway),
+//   rem  u32  |in(m)| - inter(n,m) = |in(m) \ in(n)|, so the inbound limit is
+//             |in(n)| + rem <= Delta.
+// Both limits are read together with the ids, so judging a candidate needs
+// no further memory access.  Incident hyperedges are taken a chunk at a time;
+// each brings a source run and a destination run of its pin list (for a
+// windowed node, clipped by binary search to the window's id interval, as the
+// runs and N(n) are sorted).  A scan lays the runs end to end and every thread
 // walks ITEMS consecutive pins with one run lookup, adding t(e) to the bin of
-// each pin m != n and, for a destination pin of an inbound hyperedge, one to
-// inter(n,m).  The candidate scan keeps, per thread, the best valid bin by
+// each pin m != n and, for a destination pin of an inbound hyperedge, taking
+// one from rem.  The candidate scan keeps, per thread, the best valid bin by
 // (eta desc, id asc), skipping a bin whose upper bound eta + cap cannot beat
-// it before its noise and limits are evaluated.
+// it before its noise is computed; it empties each slot it reads, so the
+// table is clean for the next window or node.
 constexpr int RB = 256;
 constexpr int RW = RB / WAVE;
 constexpr u32 H_T = 2048, H_SHIFT = 21;  // hash slots of the heavy path
@@ -157,13 +164,14 @@ constexpr u32 L_T = 512, L_SHIFT = 23;   // hash slots per wave, light path
 constexpr int L_ECH = 32;
 constexpr u32 ITEMS = 4;
 constexpr u32 EMPTY = 0xFFFFFFFFu;
-constexpr u64 INB = 1ull << 63;
+constexpr u64 INB = 1ull << 63;  // run flag: destination run of an inbound hyperedge
+constexpr u64 BAD = 1ull << 63;  // bin flag: the pair breaks Omega
 static_assert(RATE_SMALL_CAP <= L_T * 3 / 4, "light window must fit its table");
 
 struct HeavySmem {
   u64 eta[H_T];
   u32 key[H_T];
-  u32 inter[H_T];
+  u32 rem[H_T];
   u64 rs[2 * H_ECH];
   u64 rt[2 * H_ECH];
   u32 pre[2 * H_ECH + 1];
@@ -174,7 +182,7 @@ struct HeavySmem {
 struct LightWave {
   u64 eta[L_T];
   u32 key[L_T];
-  u32 inter[L_T];
+  u32 rem[L_T];
   u64 rs[2 * L_ECH];
   u64 rt[2 * L_ECH];
   u32 pre[2 * L_ECH + 1];
@@ -193,64 +201,108 @@ __device__ __forceinline__ void wave_sync() {
 
 __device__ __forceinline__ u32 hslot(u32 m, u32 shift) { return (m * 0x9E3779B1u) >> shift; }
 
-// insert a key not yet present (linear probing, bounded)
-__device__ __forceinline__ void h_insert(u32 *key, u32 mask, u32 shift, u32 m) {
+// Insert neighbour m (not yet present; linear probing, bounded) into an empty
+// table slot together with its limit data.
+__device__ __forceinline__ void h_insert_bin(u32 *key, u64 *eta, u32 *rem, u32 mask, u32 shift,
+                                             u32 m, bool bad, u32 nin_m) {
   u32 s = hslot(m, shift);
   for (u32 p = 0; p <= mask; ++p) {
-    if (atomicCAS(&key[s], EMPTY, m) == EMPTY) return;
+    if (atomicCAS(&key[s], EMPTY, m) == EMPTY) {
+      eta[s] = bad ? BAD : 0;
+      rem[s] = nin_m;
+      return;
+    }
     s = (s + 1) & mask;
   }
 }
 
 __device__ __forceinline__ u32 h_find(const u32 *key, u32 mask, u32 shift, u32 m) {
   u32 s = hslot(m, shift);
-  for (u32 p = 0; p <= mask; ++p) {
-    const u32 k = key[s];
-    if (k == m) return s;
-    if (k == EMPTY) return EMPTY;
+  u32 k = key[s];
+  u32 p = 0;
+#pragma unroll 1
+  while (k != m && k != EMPTY && p < mask) {
     s = (s + 1) & mask;
+    k = key[s];
+    ++p;
   }
-  return EMPTY;
+  return k == m ? s : EMPTY;
 }
 
 // Walk the pins of runs [0, nruns) (flat length tot), LANES threads, t = this
-// thread's index among them.
+// thread's index among them.  Each thread first issues the loads of its
+// ITEMS consecutive pins, then updates their bins.
 template <u32 LANES>
 __device__ __forceinline__ void visit_runs(const u32 *pins, const u32 *key, u32 mask, u32 shift,
-                                           u64 *eta, u32 *inter, const u64 *rs, const u64 *rt,
+                                           u64 *eta, u32 *rem, const u64 *rs, const u64 *rt,
                                            const u32 *pre, u32 nruns, u32 tot, u32 n, u32 t) {
   for (u32 base = t * ITEMS; base < tot; base += LANES * ITEMS) {
     u32 r = run_of(pre, nruns + 1, base);
-    const u32 lim = (base + ITEMS) < tot ? (base + ITEMS) : tot;
-    for (u32 idx = base; idx < lim; ++idx) {
-      while (idx >= pre[r + 1]) ++r;
-      const u64 st = rs[r];
-      const u32 m = pins[(i64)(st & ~INB) + (idx - pre[r])];
-      if (m == n) continue;
-      const u32 slot = h_find(key, mask, shift, m);
+    u32 m[ITEMS];
+    u32 rr[ITEMS];
+#pragma unroll
+    for (u32 k = 0; k < ITEMS; ++k) {
+      const u32 idx = base + k;
+      m[k] = n;  // n marks "no pin": it is skipped below
+      rr[k] = r;
+      if (idx < tot) {
+        while (idx >= pre[r + 1]) ++r;
+        rr[k] = r;
+        m[k] = pins[(i64)(rs[r] & ~INB) + (idx - pre[r])];
+      }
+    }
+#pragma unroll
+    for (u32 k = 0; k < ITEMS; ++k) {
+      if (m[k] == n) continue;
+      const u32 slot = h_find(key, mask, shift, m[k]);
       if (slot == EMPTY) continue;  // cannot happen for a valid N(n)
-      atomicAdd(&eta[slot], rt[r]);
-      if (st & INB) atomicAdd(&inter[slot], 1u);
+      atomicAdd(&eta[slot], rt[rr[k]]);
+      if (rs[rr[k]] & INB) atomicSub(&rem[slot], 1u);
     }
   }
 }
 
-// Descriptor of hyperedge j of n's incidence (j relative to the node
-// segment): its source and destination runs, clipped to [lo, hi] if clip.
-__device__ __forceinline__ void edge_runs(const RateArgs &A, i64 j_abs, bool isin, bool clip,
-                                          u32 lo, u32 hi, u64 *rs, u64 *rt, u32 &ls, u32 &ld,
-                                          u64 &tsum_add) {
-  const u32 e = A.n_inc[j_abs];
-  const i64 a = A.e_off[e], b = A.e_off[e + 1];
-  const i64 dm = a + A.e_nsrc[e];
-  const u64 te = A.t[e];
-  tsum_add = (b - a >= 2) ? te : 0;
+// Insert the window nb[0, cw) into the table: UNR neighbour ids are loaded,
+// then their sizes and inbound counts, then the slots are claimed.
+template <u32 LANES>
+__device__ __forceinline__ void insert_window(const RateArgs &A, const u32 *nb, u32 cw, u64 size_n,
+                                              u32 *key, u64 *eta, u32 *rem, u32 mask, u32 shift,
+                                              u32 t) {
+  constexpr u32 UNR = 4;
+  for (u32 b0 = t; b0 < cw; b0 += LANES * UNR) {
+    u32 m[UNR], sz[UNR], ni[UNR];
+#pragma unroll
+    for (u32 k = 0; k < UNR; ++k) {
+      const u32 i = b0 + k * LANES;
+      m[k] = i < cw ? nb[i] : EMPTY;
+    }
+#pragma unroll
+    for (u32 k = 0; k < UNR; ++k) {
+      sz[k] = 0;
+      ni[k] = 0;
+      if (m[k] != EMPTY) {
+        sz[k] = A.n_size[m[k]];
+        ni[k] = A.n_nin[m[k]];
+      }
+    }
+#pragma unroll
+    for (u32 k = 0; k < UNR; ++k)
+      if (m[k] != EMPTY)
+        h_insert_bin(key, eta, rem, mask, shift, m[k], size_n + sz[k] > A.omega, ni[k]);
+  }
+}
+
+// Hyperedge segment [a, b) with destinations from dm: its source and
+// destination runs, clipped to [lo, hi] if clip.
+__device__ __forceinline__ void edge_runs(const u32 *pins, i64 a, i64 b, i64 dm, u64 te, bool isin,
+                                          bool clip, u32 lo, u32 hi, u64 *rs, u64 *rt, u32 &ls,
+                                          u32 &ld) {
   i64 sa = a, sb = dm, da = dm, db = b;
   if (clip) {
-    sa = lower_bound_i(A.e_pins, a, dm, lo);
-    sb = upper_bound_i(A.e_pins, sa, dm, hi);
-    da = lower_bound_i(A.e_pins, dm, b, lo);
-    db = upper_bound_i(A.e_pins, da, b, hi);
+    sa = lower_bound_i(pins, a, dm, lo);
+    sb = upper_bound_i(pins, sa, dm, hi);
+    da = lower_bound_i(pins, dm, b, lo);
+    db = upper_bound_i(pins, da, b, hi);
   }
   rs[0] = (u64)sa;
   rs[1] = (u64)da | (isin ? INB : 0);
@@ -260,21 +312,61 @@ __device__ __forceinline__ void edge_runs(const RateArgs &A, i64 j_abs, bool isi
   ld = (u32)(db - da);
 }
 
+struct EdgeDesc {
+  i64 a, b, dm;
+  u64 te;
+};
+
+__device__ __forceinline__ EdgeDesc load_edge(const RateArgs &A, i64 j) {
+  const u32 e = A.n_inc[j];
+  EdgeDesc d;
+  d.a = A.e_off[e];
+  d.b = A.e_off[e + 1];
+  d.dm = d.a + A.e_nsrc[e];
+  d.te = A.t[e];
+  return d;
+}
+
 struct NodeBest {
   u64 e;
   u32 i;
 };
 
-__device__ __forceinline__ void consider(const RateArgs &A, u32 n, u32 nin, u64 size_n, u32 m,
-                                         u64 v, u32 it, u64 ub_add, u64 dmod, u64 magic,
+__device__ __forceinline__ bool bin_valid(const RateArgs &A, u32 nin, u64 v, u32 rem) {
+  return !(v & BAD) && (u64)nin + rem <= (u64)A.delta;
+}
+
+// A valid bin can win only if eta + cap reaches floor, the largest raw eta
+// of a valid bin (that bin's total is at least floor); the others are
+// skipped before their noise is computed.
+__device__ __forceinline__ void consider(const RateArgs &A, u32 n, u32 nin, u32 m, u64 v, u32 rem,
+                                         u64 ub_add, u64 floor, u64 dmod, u64 magic,
                                          NodeBest &b) {
+  if (!bin_valid(A, nin, v, rem) || v + ub_add < floor) return;
   if (!better(v + ub_add, m, b.e, b.i)) return;
   const u64 tv = A.noise_on ? v + pair_noise(A.seed, n, m, dmod, magic) : v;
-  if (!better(tv, m, b.e, b.i)) return;
-  if (size_n + A.n_size[m] > A.omega) return;
-  if ((u64)nin + A.n_nin[m] - it > (u64)A.delta) return;
-  b.e = tv;
-  b.i = m;
+  if (better(tv, m, b.e, b.i)) {
+    b.e = tv;
+    b.i = m;
+  }
+}
+
+template <int BLOCK>
+__device__ __forceinline__ u64 wg_max_u64(u64 v, u64 *lds) {
+  constexpr int NW = BLOCK / WAVE;
+#pragma unroll
+  for (int d = WAVE / 2; d > 0; d >>= 1) {
+    const u64 o = __shfl_xor(v, d, WAVE);
+    v = o > v ? o : v;
+  }
+  if (NW == 1) return v;
+  if (lane_id() == 0) lds[wave_id()] = v;
+  __syncthreads();
+  u64 m = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) m = lds[w] > m ? lds[w] : m;
+  __syncthreads();
+  return m;
 }
 
 __device__ void rate_heavy(const RateArgs &A, HeavySmem &S, u32 n, u64 cap, u64 dmod,
@@ -287,23 +379,26 @@ __device__ void rate_heavy(const RateArgs &A, HeavySmem &S, u32 n, u64 cap, u64 
   const u64 size_n = A.n_size[n];
   const u64 ub_add = A.noise_on ? cap : 0;
   const bool clip = K > H_CAP;
+  const u32 ne0 = (u32)((i1 - i0) < H_ECH ? (i1 - i0) : H_ECH);
   NodeBest best{0, NONE32};
   u64 tsum = 0;
-  // the table is empty on entry (cleared at kernel start, and by every
-  // candidate scan below as it reads each slot)
   for (u32 s0 = 0; s0 < K; s0 += H_CAP) {
     const u32 cw = (K - s0) < H_CAP ? (K - s0) : H_CAP;
-    for (u32 i = tid; i < cw; i += RB) h_insert(S.key, H_T - 1, H_SHIFT, A.nb[nb0 + s0 + i]);
+    // this thread's hyperedge of the first chunk, loaded ahead of the inserts
+    EdgeDesc d0{0, 0, 0, 0};
+    if (tid < ne0) d0 = load_edge(A, i0 + tid);
+    insert_window<RB>(A, A.nb + nb0 + s0, cw, size_n, S.key, S.eta, S.rem, H_T - 1, H_SHIFT,
+                      tid);
     const u32 lo = A.nb[nb0 + s0], hi = A.nb[nb0 + s0 + cw - 1];
     __syncthreads();
     for (i64 c0 = i0; c0 < i1; c0 += H_ECH) {
       const u32 ne = (u32)((i1 - c0) < H_ECH ? (i1 - c0) : H_ECH);
       u32 ls = 0, ld = 0;
       if (tid < ne) {
-        u64 add;
-        edge_runs(A, c0 + tid, (u64)(c0 + tid - i0) < (u64)nin, clip, lo, hi, &S.rs[2 * tid],
-                  &S.rt[2 * tid], ls, ld, add);
-        if (s0 == 0) tsum = sat_add(tsum, add);
+        const EdgeDesc d = c0 == i0 ? d0 : load_edge(A, c0 + tid);
+        if (s0 == 0 && d.b - d.a >= 2) tsum = sat_add(tsum, d.te);
+        edge_runs(A.e_pins, d.a, d.b, d.dm, d.te, (u64)(c0 + tid - i0) < (u64)nin, clip, lo, hi,
+                  &S.rs[2 * tid], &S.rt[2 * tid], ls, ld);
       }
       u32 tot;
       const u32 off = wg_excl_scan<RB>(ls + ld, S.red32, &tot);
@@ -313,17 +408,22 @@ __device__ void rate_heavy(const RateArgs &A, HeavySmem &S, u32 n, u64 cap, u64 
       }
       if (tid == 0) S.pre[2 * ne] = tot;
       __syncthreads();
-      visit_runs<RB>(A.e_pins, S.key, H_T - 1, H_SHIFT, S.eta, S.inter, S.rs, S.rt, S.pre,
-                     2 * ne, tot, n, tid);
+      visit_runs<RB>(A.e_pins, S.key, H_T - 1, H_SHIFT, S.eta, S.rem, S.rs, S.rt, S.pre, 2 * ne,
+                     tot, n, tid);
       __syncthreads();
     }
+    u64 floor = 0;
+    for (u32 i = tid; i < H_T; i += RB) {
+      const u64 v = S.eta[i];
+      if (S.key[i] != EMPTY && bin_valid(A, nin, v, S.rem[i]) && v > floor) floor = v;
+    }
+    floor = wg_max_u64<RB>(floor, S.red64);
     for (u32 i = tid; i < H_T; i += RB) {
       const u32 m = S.key[i];
       if (m != EMPTY) {
-        consider(A, n, nin, size_n, m, S.eta[i], S.inter[i], ub_add, dmod, magic, best);
+        consider(A, n, nin, m, S.eta[i], S.rem[i], ub_add, floor, dmod, magic, best);
         S.key[i] = EMPTY;
         S.eta[i] = 0;
-        S.inter[i] = 0;
       }
     }
     __syncthreads();
@@ -346,19 +446,22 @@ __device__ void rate_light(const RateArgs &A, LightWave &S, u32 n, u64 cap, u64 
   const u32 nin = A.n_nin[n];
   const u64 size_n = A.n_size[n];
   const u64 ub_add = A.noise_on ? cap : 0;
+  const u32 ne0 = (u32)((i1 - i0) < L_ECH ? (i1 - i0) : L_ECH);
   NodeBest best{0, NONE32};
   u64 tsum = 0;
+  EdgeDesc d0{0, 0, 0, 0};
+  if (l < ne0) d0 = load_edge(A, i0 + l);
   // the wave's table is empty on entry (see the candidate scan)
-  for (u32 i = l; i < K; i += WAVE) h_insert(S.key, L_T - 1, L_SHIFT, A.nb[nb0 + i]);
+  insert_window<WAVE>(A, A.nb + nb0, K, size_n, S.key, S.eta, S.rem, L_T - 1, L_SHIFT, l);
   wave_sync();
   for (i64 c0 = i0; c0 < i1; c0 += L_ECH) {
     const u32 ne = (u32)((i1 - c0) < L_ECH ? (i1 - c0) : L_ECH);
     u32 ls = 0, ld = 0;
     if (l < ne) {
-      u64 add;
-      edge_runs(A, c0 + l, (u64)(c0 + l - i0) < (u64)nin, false, 0, 0, &S.rs[2 * l],
-                &S.rt[2 * l], ls, ld, add);
-      tsum = sat_add(tsum, add);
+      const EdgeDesc d = c0 == i0 ? d0 : load_edge(A, c0 + l);
+      if (d.b - d.a >= 2) tsum = sat_add(tsum, d.te);
+      edge_runs(A.e_pins, d.a, d.b, d.dm, d.te, (u64)(c0 + l - i0) < (u64)nin, false, 0, 0,
+                &S.rs[2 * l], &S.rt[2 * l], ls, ld);
     }
     const u32 v = ls + ld;
     const u32 inc = wave_incl_scan(v);
@@ -369,17 +472,22 @@ __device__ void rate_light(const RateArgs &A, LightWave &S, u32 n, u64 cap, u64 
     }
     if (l == 0) S.pre[2 * ne] = tot;
     wave_sync();
-    visit_runs<WAVE>(A.e_pins, S.key, L_T - 1, L_SHIFT, S.eta, S.inter, S.rs, S.rt, S.pre,
+    visit_runs<WAVE>(A.e_pins, S.key, L_T - 1, L_SHIFT, S.eta, S.rem, S.rs, S.rt, S.pre,
                      2 * ne, tot, n, l);
     wave_sync();
   }
+  u64 floor = 0;
+  for (u32 i = l; i < L_T; i += WAVE) {
+    const u64 v = S.eta[i];
+    if (S.key[i] != EMPTY && bin_valid(A, nin, v, S.rem[i]) && v > floor) floor = v;
+  }
+  floor = wg_max_u64<WAVE>(floor, nullptr);
   for (u32 i = l; i < L_T; i += WAVE) {
     const u32 m = S.key[i];
     if (m != EMPTY) {
-      consider(A, n, nin, size_n, m, S.eta[i], S.inter[i], ub_add, dmod, magic, best);
+      consider(A, n, nin, m, S.eta[i], S.rem[i], ub_add, floor, dmod, magic, best);
       S.key[i] = EMPTY;
       S.eta[i] = 0;
-      S.inter[i] = 0;
     }
   }
   tsum = wg_sat_sum<WAVE>(tsum, nullptr);
@@ -389,7 +497,6 @@ __device__ void rate_light(const RateArgs &A, LightWave &S, u32 n, u64 cap, u64 
     A.target[n] = best.i;
     A.score[n] = best.i == NONE32 ? 0 : best.e;
   }
-  wave_sync();
 }
 
 // cnt[0] light nodes in light[], cnt[1] heavy nodes in heavy[]; work[0..1]
@@ -410,7 +517,6 @@ __global__ __launch_bounds__(RB) void k_rate(RateArgs A, const u32 *light, const
   for (u32 i = threadIdx.x; i < H_T; i += RB) {
     sm.h.key[i] = EMPTY;
     sm.h.eta[i] = 0;
-    sm.h.inter[i] = 0;
   }
   for (;;) {
     if (threadIdx.x == 0) s_item = atomicAdd(&work[0], 1u);
@@ -425,7 +531,6 @@ __global__ __launch_bounds__(RB) void k_rate(RateArgs A, const u32 *light, const
   for (u32 i = lane_id(); i < L_T; i += WAVE) {
     S.key[i] = EMPTY;
     S.eta[i] = 0;
-    S.inter[i] = 0;
   }
   wave_sync();
   for (;;) {
