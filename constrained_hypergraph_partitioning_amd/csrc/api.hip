@@ -257,15 +257,8 @@ void build_neighbors_core(chp_ctx *c, Scratch &s, Owned &own, chp_hgraph *g) {
   u32 *obuf = s.get<u32>((u64)obuf_total);
   u32 *count = s.get<u32>(N);
   launch_fill_u32(c, count, N, 0);
-  u32 *scr = nullptr;
-  u64 per_wg = 0;
-  u32 gb = grid_big_for(hc[2]);
-  if (hc[2]) {
-    per_wg = 2ull * hc[5];
-    scr = s.get<u32>(per_wg * gb);
-  }
-  launch_nb_build(c, N, g->e_off, g->e_pins, g->n_off, g->n_inc, ooff, obuf, count, nl, hc, scr,
-                  per_wg, gb);
+  launch_nb_build(c, N, g->e_off, g->e_pins, g->n_off, g->n_inc, bound, ooff, obuf, count, nl,
+                  hc);
   scan_u32_to_i64(c, count, g->nb_off, N, tmp);
   launch_check(c, "neighbours");
   i64 total;
@@ -285,7 +278,8 @@ void build_neighbors_merge(chp_ctx *c, Scratch &s, Owned &own, const chp_hgraph 
   cg->nb_off = own.get<i64>((u64)Nc + 1);
   u32 *bound = s.get<u32>(Nc);
   NbLists nl;
-  for (int k = 0; k < 5; ++k) nl.list[k] = s.get<u32>(Nc);
+  for (int k = 0; k < 3; ++k) nl.list[k] = s.get<u32>(Nc);
+  nl.list[3] = nl.list[4] = nullptr;
   nl.cnt = s.get<u32>(8);
   launch_fill_u32(c, nl.cnt, 8, 0);
   launch_nbm_classify(c, Nc, rep_of, match, g->nb_off, bound, nl);
@@ -303,15 +297,7 @@ void build_neighbors_merge(chp_ctx *c, Scratch &s, Owned &own, const chp_hgraph 
   u32 *obuf = s.get<u32>((u64)obuf_total);
   u32 *count = s.get<u32>(Nc);
   launch_fill_u32(c, count, Nc, 0);
-  u32 *scr = nullptr;
-  u64 per_q = 0;
-  u32 gb = grid_big_for(hc[4]);
-  if (hc[4]) {
-    per_q = (u64)hc[5];
-    scr = s.get<u32>(4 * per_q * gb);
-  }
-  launch_nbm_build(c, g->nb_off, g->nb, gamma, match, rep_of, ooff, obuf, count, nl, hc, scr,
-                   per_q, gb);
+  launch_nbm_build(c, g->nb_off, g->nb, gamma, match, rep_of, ooff, obuf, count, nl, hc);
   scan_u32_to_i64(c, count, cg->nb_off, Nc, tmp);
   launch_check(c, "coarse neighbours");
   i64 total;

@@ -245,14 +245,14 @@ __global__ void k_nb_classify(u32 N, const i64 *e_off, const i64 *n_off, const u
     }
     bound[n] = (u32)bnd;
   }
-  // isolated nodes (bnd 0) have an empty N(n) and join no class
-  const int c = bnd == 0 ? 3 : (w <= 64 ? 0 : (w <= LDS_CAP_U32 ? 1 : 2));
+  // isolated nodes (bnd 0) have an empty N(n) and join no class; the others
+  // are built by one wave (W_n <= 64) or by the LDS bitmap
+  const int c = bnd == 0 ? 2 : (w <= 64 ? 0 : 1);
 #pragma unroll
-  for (int k = 0; k < 3; ++k) {
+  for (int k = 0; k < 2; ++k) {
     const u32 slot = wave_append(&nl.cnt[k], c == k);
     if (c == k) nl.list[k][slot] = n;
   }
-  if (c == 2) atomicMax(&nl.cnt[5], (u32)w);
 }
 
 // wave per node, W_n <= 64: gather into lanes, sort, unique, drop n
@@ -290,86 +290,6 @@ __global__ __launch_bounds__(256) void k_nb_wave(const i64 *e_off, const u32 *pi
     u32 pos = __popcll(mask & ((1ull << l) - 1));
     if (keep) obuf[ooff[n] + pos] = v;
     if (l == 0) count[n] = (u32)__popcll(mask);
-  }
-}
-
-// Gather the pins of I(n) (all of them, n included) into dst, which has room
-// for W_n keys.  Hyperedges are taken BLOCK at a time: each thread loads one
-// segment descriptor, a workgroup scan places them, and the flattened copy
-// finds its segment by binary search over the prefix.
-template <int BLOCK>
-__device__ u64 gather_pins(const i64 *e_off, const u32 *pins, const u32 *n_inc, i64 a, i64 b,
-                           u32 *dst, i64 *s_start, u32 *s_pre, u32 *s_red) {
-  u64 base = 0;
-  for (i64 c0 = a; c0 < b; c0 += BLOCK) {
-    u32 ne = (u32)((b - c0) < BLOCK ? (b - c0) : BLOCK);
-    u32 len = 0;
-    if (threadIdx.x < ne) {
-      u32 e = n_inc[c0 + threadIdx.x];
-      i64 s = e_off[e];
-      len = (u32)(e_off[e + 1] - s);
-      s_start[threadIdx.x] = s;
-    }
-    u32 tot;
-    u32 off = wg_excl_scan<BLOCK>(len, s_red, &tot);
-    if (threadIdx.x < ne) s_pre[threadIdx.x] = off;
-    if (threadIdx.x == 0) s_pre[ne] = tot;
-    __syncthreads();
-    for (u32 i = threadIdx.x; i < tot; i += BLOCK) {
-      u32 r = run_of(s_pre, ne + 1, i);
-      dst[base + i] = pins[s_start[r] + (i - s_pre[r])];
-    }
-    base += tot;
-    __syncthreads();
-  }
-  return base;
-}
-
-template <int BLOCK, int CAP>
-__global__ __launch_bounds__(BLOCK) void k_nb_lds(const i64 *e_off, const u32 *pins,
-                                                  const i64 *n_off, const u32 *n_inc,
-                                                  const i64 *ooff, u32 *obuf, u32 *count,
-                                                  const u32 *list, const u32 *cnt) {
-  __shared__ u32 s[CAP];
-  __shared__ i64 s_start[BLOCK];
-  __shared__ u32 s_pre[BLOCK + 1];
-  __shared__ u32 s_red[BLOCK / WAVE + 1];
-  const u32 total = *cnt;
-  for (u32 w = blockIdx.x; w < total; w += gridDim.x) {
-    u32 n = list[w];
-    i64 a = n_off[n], b = n_off[n + 1];
-    const u32 m = (u32)gather_pins<BLOCK>(e_off, pins, n_inc, a, b, s, s_start, s_pre, s_red);
-    u32 p = next_pow2(m);
-    for (u32 i = m + threadIdx.x; i < p; i += BLOCK) s[i] = NONE32;
-    __syncthreads();
-    lds_bitonic<BLOCK>(s, p);
-    u32 c = unique_out<BLOCK>(s, m, n, obuf + ooff[n], s_red);
-    if (threadIdx.x == 0) count[n] = c;
-    __syncthreads();
-  }
-}
-
-template <int BLOCK, int CAP>
-__global__ __launch_bounds__(BLOCK) void k_nb_global(const i64 *e_off, const u32 *pins,
-                                                     const i64 *n_off, const u32 *n_inc,
-                                                     const i64 *ooff, u32 *obuf, u32 *count,
-                                                     const u32 *list, const u32 *cnt,
-                                                     u32 *scratch, u64 per_wg) {
-  __shared__ u32 s[CAP];
-  __shared__ i64 s_start[BLOCK];
-  __shared__ u32 s_pre[BLOCK + 1];
-  __shared__ u32 s_red[BLOCK / WAVE + 1];
-  const u32 total = *cnt;
-  u32 *A = scratch + (u64)blockIdx.x * per_wg;
-  u32 *B = A + per_wg / 2;
-  for (u32 w = blockIdx.x; w < total; w += gridDim.x) {
-    u32 n = list[w];
-    i64 a = n_off[n], b = n_off[n + 1];
-    const u64 m = gather_pins<BLOCK>(e_off, pins, n_inc, a, b, A, s_start, s_pre, s_red);
-    u32 *res = wg_sort_global<BLOCK, CAP>(A, B, m, s);
-    u32 c = unique_out<BLOCK>(res, m, n, obuf + ooff[n], s_red);
-    if (threadIdx.x == 0) count[n] = c;
-    __syncthreads();
   }
 }
 
@@ -455,17 +375,13 @@ void launch_nb_classify(chp_ctx *c, u32 N, const i64 *e_off, const i64 *n_off, c
 }
 
 void launch_nb_build(chp_ctx *c, u32 N, const i64 *e_off, const u32 *pins, const i64 *n_off,
-                     const u32 *n_inc, const i64 *ooff, u32 *obuf, u32 *count, NbLists nl,
-                     const u32 *host_cnt, u32 *scratch, u64 scratch_per_wg, u32 grid_big) {
+                     const u32 *n_inc, const u32 *bound, const i64 *ooff, u32 *obuf, u32 *count,
+                     NbLists nl, const u32 *host_cnt) {
   if (host_cnt[0])
     CHP_LAUNCH(c, "nb_wave", k_nb_wave, waves_grid(host_cnt[0]), 256, 0, e_off, pins, n_off,
                n_inc, ooff, obuf, count, nl.list[0], nl.cnt + 0);
-  if (host_cnt[1])
-    CHP_LAUNCH(c, "nb_lds", (k_nb_lds<256, LDS_CAP_U32>), host_cnt[1] > 8192 ? 8192 : host_cnt[1],
-               256, 0, e_off, pins, n_off, n_inc, ooff, obuf, count, nl.list[1], nl.cnt + 1);
-  if (host_cnt[2])
-    CHP_LAUNCH(c, "nb_global", (k_nb_global<256, LDS_CAP_U32>), grid_big, 256, 0, e_off, pins,
-               n_off, n_inc, ooff, obuf, count, nl.list[2], nl.cnt + 2, scratch, scratch_per_wg);
+  launch_nb_bitmap(c, e_off, pins, n_off, n_inc, bound, ooff, obuf, count, nl.list[1],
+                   nl.cnt + 1, host_cnt[1]);
 }
 
 void launch_nb_compact(chp_ctx *c, u32 N, const i64 *ooff, const u32 *obuf, const i64 *nb_off,

@@ -180,20 +180,14 @@ __global__ void k_nbm_classify(u32 Nc, const u32 *rep_of, const u32 *match, cons
     }
     bound[c] = (u32)w;
   }
-  // classes: one wave in registers; one-wave, 256-thread and 256-thread
-  // large-LDS merges; global scratch beyond NBM_LDS_CAP
-  const int cls = (c >= Nc || w == 0) ? 5
-                  : w <= 64          ? 0
-                  : w <= 1024        ? 1
-                  : w <= 4096        ? 2
-                  : w <= NBM_LDS_CAP ? 3
-                                     : 4;
+  // classes: one wave in registers (<= 64); a one-wave merge (<= 1024);
+  // the LDS bitmap (larger)
+  const int cls = (c >= Nc || w == 0) ? 3 : w <= 64 ? 0 : w <= 1024 ? 1 : 2;
 #pragma unroll
-  for (int k = 0; k < 5; ++k) {
+  for (int k = 0; k < 3; ++k) {
     const u32 slot = wave_append(&nl.cnt[k], cls == k);
     if (cls == k) nl.list[k][slot] = c;
   }
-  if (cls == 4) atomicMax(&nl.cnt[5], (u32)w);
 }
 
 // bound <= 64: one wave, keys in registers
@@ -297,46 +291,6 @@ __global__ __launch_bounds__(BLOCK) void k_nbm_merge(const i64 *nb_off, const u3
   }
 }
 
-// The same with the three lists in global scratch (X, Y, Z, W of per_q ids
-// each); the second members' images are sorted by chunks in LDS and merges.
-template <int BLOCK, int SCAP>
-__global__ __launch_bounds__(BLOCK) void k_nbm_merge_global(
-    const i64 *nb_off, const u32 *nb, const u32 *gamma, const u32 *match, const u32 *rep_of,
-    const i64 *ooff, u32 *obuf, u32 *count, const u32 *list, const u32 *cnt, u32 *scratch,
-    u64 per_q) {
-  __shared__ u32 s[SCAP];
-  __shared__ u32 s_red[BLOCK / WAVE + 1];
-  const u32 total = *cnt;
-  u32 *X = scratch + (u64)blockIdx.x * 4 * per_q;
-  u32 *Y = X + per_q, *Z = Y + per_q, *W = Z + per_q;
-  for (u32 w = blockIdx.x; w < total; w += gridDim.x) {
-    const u32 c = list[w];
-    const u32 a = rep_of[c], b = match[a];
-    u32 r1 = 0, r2 = 0, q = 0;
-    const i64 a0 = nb_off[a];
-    split_reps<BLOCK>(nb + a0, (u32)(nb_off[a + 1] - a0), gamma, match, X, r1, Z, q, s_red);
-    if (b != a) {
-      const i64 b0 = nb_off[b];
-      split_reps<BLOCK>(nb + b0, (u32)(nb_off[b + 1] - b0), gamma, match, X + r1, r2, Z, q,
-                        s_red);
-    }
-    __syncthreads();
-    const u32 *Qs = wg_sort_global<BLOCK, SCAP>(Z, W, q, s);
-    const u32 *R = X;
-    if (r2) {
-      wg_merge<BLOCK>(X, r1, X + r1, r2, Y);
-      __syncthreads();
-      R = Y;
-    }
-    u32 *F = R == X ? Y : X;
-    wg_merge<BLOCK>(R, r1 + r2, Qs, q, F);
-    __syncthreads();
-    const u32 k = unique_out<BLOCK>(F, r1 + r2 + q, c, obuf + ooff[c], s_red);
-    if (threadIdx.x == 0) count[c] = k;
-    __syncthreads();
-  }
-}
-
 }  // namespace
 
 void launch_cinc_classify(chp_ctx *c, u32 Nc, const u32 *rep_of, const u32 *match,
@@ -383,8 +337,7 @@ void launch_nbm_classify(chp_ctx *c, u32 Nc, const u32 *rep_of, const u32 *match
 
 void launch_nbm_build(chp_ctx *c, const i64 *nb_off, const u32 *nb, const u32 *gamma,
                       const u32 *match, const u32 *rep_of, const i64 *ooff, u32 *obuf,
-                      u32 *count, NbLists nl, const u32 *host_cnt, u32 *scratch, u64 per_q,
-                      u32 grid_big) {
+                      u32 *count, NbLists nl, const u32 *host_cnt) {
   if (host_cnt[0])
     CHP_LAUNCH(c, "nbm_wave", k_nbm_wave, waves_grid(host_cnt[0]), 256, 0, nb_off, nb, gamma,
                match, rep_of, ooff, obuf, count, (const u32 *)nl.list[0],
@@ -393,16 +346,6 @@ void launch_nbm_build(chp_ctx *c, const i64 *nb_off, const u32 *nb, const u32 *g
     CHP_LAUNCH(c, "nbm_merge", (k_nbm_merge<64, 1024>),
                host_cnt[1] > 65536 ? 65536 : host_cnt[1], 64, 0, nb_off, nb, gamma, match, rep_of,
                ooff, obuf, count, (const u32 *)nl.list[1], (const u32 *)nl.cnt + 1);
-  if (host_cnt[2])
-    CHP_LAUNCH(c, "nbm_merge", (k_nbm_merge<256, 4096>),
-               host_cnt[2] > 8192 ? 8192 : host_cnt[2], 256, 0, nb_off, nb, gamma, match, rep_of,
-               ooff, obuf, count, (const u32 *)nl.list[2], (const u32 *)nl.cnt + 2);
-  if (host_cnt[3])
-    CHP_LAUNCH(c, "nbm_merge", (k_nbm_merge<256, NBM_LDS_CAP>),
-               host_cnt[3] > 8192 ? 8192 : host_cnt[3], 256, 0, nb_off, nb, gamma, match, rep_of,
-               ooff, obuf, count, (const u32 *)nl.list[3], (const u32 *)nl.cnt + 3);
-  if (host_cnt[4])
-    CHP_LAUNCH(c, "nbm_merge_global", (k_nbm_merge_global<256, 4096>), grid_big, 256, 0, nb_off,
-               nb, gamma, match, rep_of, ooff, obuf, count, (const u32 *)nl.list[4],
-               (const u32 *)nl.cnt + 4, scratch, per_q);
+  launch_nbm_bitmap(c, nb_off, nb, gamma, match, rep_of, ooff, obuf, count, nl.list[2],
+                    nl.cnt + 2, host_cnt[2]);
 }

@@ -50,8 +50,8 @@ void launch_node_runs(chp_ctx *c, u32 N, const i64 *n_off, const u32 *n_nin, Run
 void launch_nb_classify(chp_ctx *c, u32 N, const i64 *e_off, const i64 *n_off, const u32 *n_inc,
                         u32 *bound, NbLists nl);
 void launch_nb_build(chp_ctx *c, u32 N, const i64 *e_off, const u32 *pins, const i64 *n_off,
-                     const u32 *n_inc, const i64 *ooff, u32 *obuf, u32 *count, NbLists nl,
-                     const u32 *host_cnt, u32 *scratch, u64 scratch_per_wg, u32 grid_big);
+                     const u32 *n_inc, const u32 *bound, const i64 *ooff, u32 *obuf, u32 *count,
+                     NbLists nl, const u32 *host_cnt);
 void launch_nb_compact(chp_ctx *c, u32 N, const i64 *ooff, const u32 *obuf, const i64 *nb_off,
                        u32 *nb);
 
@@ -124,8 +124,15 @@ void launch_nbm_classify(chp_ctx *c, u32 Nc, const u32 *rep_of, const u32 *match
                          const i64 *nb_off, u32 *bound, NbLists nl);
 void launch_nbm_build(chp_ctx *c, const i64 *nb_off, const u32 *nb, const u32 *gamma,
                       const u32 *match, const u32 *rep_of, const i64 *ooff, u32 *obuf,
-                      u32 *count, NbLists nl, const u32 *host_cnt, u32 *scratch, u64 per_q,
-                      u32 grid_big);
+                      u32 *count, NbLists nl, const u32 *host_cnt);
+
+// ---- k_bitmap.hip : sorted distinct lists through an LDS bitmap ------------
+void launch_nb_bitmap(chp_ctx *c, const i64 *e_off, const u32 *pins, const i64 *n_off,
+                      const u32 *n_inc, const u32 *bound, const i64 *ooff, u32 *obuf, u32 *count,
+                      const u32 *list, const u32 *cnt, u32 host_count);
+void launch_nbm_bitmap(chp_ctx *c, const i64 *nb_off, const u32 *nb, const u32 *gamma,
+                       const u32 *match, const u32 *rep_of, const i64 *ooff, u32 *obuf,
+                       u32 *count, const u32 *list, const u32 *cnt, u32 host_count);
 
 // ---- k_eval.hip --------------------------------------------------------------
 void launch_eval_nodes(chp_ctx *c, u32 N, const u32 *rho, u32 k, const u32 *n_size,
