@@ -52,30 +52,59 @@ void hip_check(chp_ctx *c, hipError_t e, const char *what) {
 
 void launch_check(chp_ctx *c, const char *what) { hip_check(c, hipPeekAtLastError(), what); }
 
-// Scratch buffers freed when the call returns (stream order keeps later
-// reuse of the memory behind the kernels that used it).
+// Scratch memory of one call.  Requests up to ARENA_SMALL bytes are carved
+// from the context's arena (a device block reused by every call: all work is
+// on one stream, so a later call's kernels run after the earlier ones);
+// larger ones, and small ones that overflow the arena, are allocated on their
+// own and freed when the call returns.  An overflow grows the arena for the
+// next call.
+constexpr size_t ARENA_SMALL = 16u << 20;
+constexpr size_t ARENA_MAX = 512u << 20;
+
 struct Scratch {
   chp_ctx *c;
-  std::vector<void *> v;
-  explicit Scratch(chp_ctx *cc) : c(cc) {}
+  size_t mark;
+  size_t need;
+  std::vector<void *> own;
+  explicit Scratch(chp_ctx *cc) : c(cc), mark(cc->arena_top), need(cc->arena_top) {}
   ~Scratch() {
-    for (void *p : v) ctx_free(c, p);
+    for (void *p : own) ctx_free(c, p);
+    c->arena_top = mark;
+    if (need > c->arena_cap && mark == 0) {
+      size_t cap = need + need / 4;
+      if (cap > ARENA_MAX) cap = ARENA_MAX;
+      if (cap > c->arena_cap) {
+        ctx_free(c, c->arena);
+        c->arena = (char *)ctx_alloc(c, cap);
+        c->arena_cap = c->arena ? cap : 0;
+      }
+    }
   }
   template <typename T>
   T *get(u64 n) {
-    void *p = ctx_alloc(c, (size_t)(n ? n : 1) * sizeof(T));
+    const size_t bytes = (((size_t)(n ? n : 1) * sizeof(T)) + 255) & ~(size_t)255;
+    if (bytes <= ARENA_SMALL) {
+      need += bytes;
+      if (c->arena && c->arena_top + bytes <= c->arena_cap) {
+        void *p = c->arena + c->arena_top;
+        c->arena_top += bytes;
+        return (T *)p;
+      }
+    }
+    void *p = ctx_alloc(c, bytes);
     if (!p) {
-      set_err(c, "device allocation of %s%lld bytes failed", "", (long long)(n * sizeof(T)));
+      set_err(c, "device allocation of %s%lld bytes failed", "", (long long)bytes);
       throw Fail{CHP_ENOMEM};
     }
-    v.push_back(p);
+    own.push_back(p);
     return (T *)p;
   }
+  // return a large buffer early (arena pieces are reclaimed at the end)
   void release(void *p) {
-    auto it = std::find(v.begin(), v.end(), p);
-    if (it != v.end()) {
+    auto it = std::find(own.begin(), own.end(), p);
+    if (it != own.end()) {
       ctx_free(c, p);
-      v.erase(it);
+      own.erase(it);
     }
   }
 };
@@ -269,88 +298,6 @@ void build_neighbors_core(chp_ctx *c, Scratch &s, Owned &own, chp_hgraph *g) {
   launch_check(c, "neighbour compaction");
 }
 
-// neighbourhoods of the coarse graph cg by merging the members' lists of the
-// fine graph g (which must have them)
-void build_neighbors_merge(chp_ctx *c, Scratch &s, Owned &own, const chp_hgraph *g,
-                           chp_hgraph *cg, const u32 *match, const u32 *rep_of,
-                           const u32 *gamma) {
-  const u32 Nc = cg->n_nodes;
-  cg->nb_off = own.get<i64>((u64)Nc + 1);
-  u32 *bound = s.get<u32>(Nc);
-  NbLists nl;
-  for (int k = 0; k < 3; ++k) nl.list[k] = s.get<u32>(Nc);
-  nl.list[3] = nl.list[4] = nullptr;
-  nl.cnt = s.get<u32>(8);
-  launch_fill_u32(c, nl.cnt, 8, 0);
-  launch_nbm_classify(c, Nc, rep_of, match, g->nb_off, bound, nl);
-  i64 *ooff = s.get<i64>((u64)Nc + 1);
-  i64 *tmp = s.get<i64>(scan_tmp_words(Nc));
-  scan_u32_to_i64(c, bound, ooff, Nc, tmp);
-  launch_check(c, "coarse neighbour classes");
-  i64 obuf_total;
-  u32 hc[8];
-  read_many(c, {{&obuf_total, ooff + Nc, sizeof obuf_total}, {hc, nl.cnt, sizeof hc}});
-  if (hc[7]) {
-    set_err(c, "%sa cluster's neighbour lists exceed 2^32 entries");
-    throw Fail{CHP_EOVERFLOW};
-  }
-  u32 *obuf = s.get<u32>((u64)obuf_total);
-  u32 *count = s.get<u32>(Nc);
-  launch_fill_u32(c, count, Nc, 0);
-  launch_nbm_build(c, g->nb_off, g->nb, gamma, match, rep_of, ooff, obuf, count, nl, hc);
-  scan_u32_to_i64(c, count, cg->nb_off, Nc, tmp);
-  launch_check(c, "coarse neighbours");
-  i64 total;
-  read_back(c, &total, cg->nb_off + Nc, sizeof total);
-  cg->nb = own.get<u32>((u64)total);
-  cg->nb_total = (u64)total;
-  launch_nb_compact(c, Nc, ooff, obuf, cg->nb_off, cg->nb);
-  launch_check(c, "coarse neighbour compaction");
-}
-
-// incidence of the coarse graph cg from the members' incidence in g
-void build_incidence_merge(chp_ctx *c, Scratch &s, Owned &own, const chp_hgraph *g,
-                           chp_hgraph *cg, const u32 *match, const u32 *rep_of) {
-  const u32 Nc = cg->n_nodes;
-  cg->n_off = own.get<i64>((u64)Nc + 1);
-  cg->n_nin = own.get<u32>(Nc);
-  u32 *bound = s.get<u32>(Nc), *cnt_tot = s.get<u32>(Nc);
-  EdgeLists el;
-  for (int k = 0; k < 3; ++k) el.list[k] = s.get<u32>(Nc);
-  el.cnt = s.get<u32>(8);
-  launch_fill_u32(c, el.cnt, 8, 0);
-  launch_cinc_classify(c, Nc, rep_of, match, g->n_off, g->n_nin, bound, cg->n_nin, cnt_tot, el);
-  i64 *ooff = s.get<i64>((u64)Nc + 1);
-  i64 *tmp = s.get<i64>(scan_tmp_words(Nc));
-  scan_u32_to_i64(c, bound, ooff, Nc, tmp);
-  launch_check(c, "coarse incidence classes");
-  i64 obuf_total;
-  u32 hc[8];
-  read_many(c, {{&obuf_total, ooff + Nc, sizeof obuf_total}, {hc, el.cnt, sizeof hc}});
-  u32 *obuf = s.get<u32>((u64)obuf_total);
-  u64 *scr = nullptr;
-  u64 per_wg = 0;
-  u32 gb = grid_big_for(hc[2]);
-  if (hc[2]) {
-    per_wg = 2ull * hc[3];
-    scr = s.get<u64>(per_wg * gb);
-  }
-  launch_cinc_build(c, g->n_off, g->n_nin, g->n_inc, rep_of, match, ooff, obuf, cg->n_nin,
-                    cnt_tot, el, hc, scr, per_wg, gb);
-  scan_u32_to_i64(c, cnt_tot, cg->n_off, Nc, tmp);
-  launch_check(c, "coarse incidence");
-  i64 total;
-  read_back(c, &total, cg->n_off + Nc, sizeof total);
-  if ((u64)total != cg->n_pins) {
-    set_err(c, "%scoarse incidence does not match the coarse pins");
-    throw Fail{CHP_EDEVICE};
-  }
-  cg->n_inc = own.get<u32>((u64)total);
-  launch_cinc_compact(c, Nc, rep_of, match, g->n_off, g->n_inc, ooff, obuf, cg->n_off,
-                      cg->n_inc);
-  launch_check(c, "coarse incidence compaction");
-}
-
 EdgeLists make_edge_lists(chp_ctx *c, Scratch &s, u32 E, const i64 *e_off, u32 hc[8]) {
   EdgeLists el;
   for (int k = 0; k < 3; ++k) el.list[k] = s.get<u32>(E);
@@ -478,6 +425,7 @@ void chp_destroy(chp_ctx *c) {
   if (!c) return;
   (void)hipStreamSynchronize(c->stream);
   resolve_timings(c);
+  ctx_free(c, c->arena);
   for (hipEvent_t e : c->free_events) (void)hipEventDestroy(e);
   ctx_free(c, c->flags);
   (void)hipHostFree(c->pinned);
@@ -674,58 +622,134 @@ int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
     }
     const u32 N = g->n_nodes, E = g->n_edges;
     const u64 P = g->n_pins;
+    const bool merge_nb = build_neighbors && g->nb_off && g->nb;
     Scratch s(c);
     Owned own(c);
     clear_flags(c);
+    // -- representatives and hyperedge classes, then the first readback
     u32 *is_rep = s.get<u32>(N);
     i64 *rank = s.get<i64>((u64)N + 1);
     i64 *tmp = s.get<i64>(scan_tmp_words(N > E ? N : E));
     launch_rep(c, N, match, is_rep);
     scan_u32_to_i64(c, is_rep, rank, N, tmp);
+    EdgeLists el;
+    for (int k = 0; k < 3; ++k) el.list[k] = s.get<u32>(E);
+    el.cnt = s.get<u32>(8);
+    launch_fill_u32(c, el.cnt, 8, 0);
+    launch_edge_classify(c, E, g->e_off, el);
     launch_check(c, "representatives");
     i64 nc;
-    u32 f;
-    read_many(c, {{&nc, rank + N, sizeof nc}, {&f, c->flags, sizeof f}});
+    u32 f, he[8];
+    read_many(c, {{&nc, rank + N, sizeof nc}, {&f, c->flags, sizeof f}, {he, el.cnt, sizeof he}});
     if (f & FLAG_EINVAL) fail_flags(c, FLAG_EINVAL, "match is not a symmetric pairing");
+    const u32 Nc = (u32)nc;
     chp_hgraph cg;
     memset(&cg, 0, sizeof cg);
-    cg.n_nodes = (u32)nc;
+    cg.n_nodes = Nc;
     cg.n_edges = E;
-    cg.n_size = own.get<u32>((u64)nc);
+    cg.n_size = own.get<u32>(Nc);
     cg.e_w = own.get<u32>(E);
     cg.e_off = own.get<i64>((u64)E + 1);
     cg.e_nsrc = own.get<u32>(E);
+    cg.n_off = own.get<i64>((u64)Nc + 1);
+    cg.n_nin = own.get<u32>(Nc);
     d2d(c, cg.e_w, g->e_w, sizeof(u32) * (size_t)E);
-    u32 *rep_of = s.get<u32>((u64)nc);
+    u32 *rep_of = s.get<u32>(Nc);
     launch_gamma(c, N, match, rank, g->n_size, gamma, cg.n_size, rep_of);
-    u32 hc[8];
-    EdgeLists el = make_edge_lists(c, s, E, g->e_off, hc);
-    u64 *scr = nullptr;
-    u64 per_wg = 0;
-    u32 gb = grid_big_for(hc[2]);
-    if (hc[2]) {
-      per_wg = 2ull * hc[3];
-      scr = s.get<u64>(per_wg * gb);
+    // -- coarse hyperedges (oversize, then packed)
+    u64 *escr = nullptr;
+    u64 eper = 0;
+    const u32 egb = grid_big_for(he[2]);
+    if (he[2]) {
+      eper = 2ull * he[3];
+      escr = s.get<u64>(eper * egb);
     }
     u32 *opins = s.get<u32>(P);
     u32 *olen = s.get<u32>(E);
-    launch_edge_contract(c, g->e_off, g->e_nsrc, g->e_pins, gamma, opins, olen, cg.e_nsrc, el, hc,
-                         scr, per_wg, gb);
+    launch_edge_contract(c, g->e_off, g->e_nsrc, g->e_pins, gamma, opins, olen, cg.e_nsrc, el, he,
+                         escr, eper, egb);
     scan_u32_to_i64(c, olen, cg.e_off, E, tmp);
-    launch_check(c, "coarse hyperedges");
-    i64 pc;
-    read_back(c, &pc, cg.e_off + E, sizeof pc);
+    // -- coarse incidence classes: in'(c) = in(a) u in(b), out' = (out(a) u out(b)) \ in'
+    u32 *ibound = s.get<u32>(Nc), *icnt = s.get<u32>(Nc);
+    EdgeLists il;
+    for (int k = 0; k < 3; ++k) il.list[k] = s.get<u32>(Nc);
+    il.cnt = s.get<u32>(8);
+    launch_fill_u32(c, il.cnt, 8, 0);
+    launch_cinc_classify(c, Nc, rep_of, match, g->n_off, g->n_nin, ibound, cg.n_nin, icnt, il);
+    i64 *iooff = s.get<i64>((u64)Nc + 1);
+    i64 *tmp2 = s.get<i64>(scan_tmp_words(Nc));
+    scan_u32_to_i64(c, ibound, iooff, Nc, tmp2);
+    // -- coarse neighbour classes: N'(c) = gamma(N(a) u N(b)) \ {c}
+    u32 *nbound = nullptr;
+    i64 *nooff = nullptr;
+    i64 *tmp3 = nullptr;
+    NbLists nl;
+    nl.cnt = nullptr;
+    if (merge_nb) {
+      nbound = s.get<u32>(Nc);
+      for (int k = 0; k < 3; ++k) nl.list[k] = s.get<u32>(Nc);
+      nl.list[3] = nl.list[4] = nullptr;
+      nl.cnt = s.get<u32>(8);
+      launch_fill_u32(c, nl.cnt, 8, 0);
+      launch_nbm_classify(c, Nc, rep_of, match, g->nb_off, nbound, nl);
+      nooff = s.get<i64>((u64)Nc + 1);
+      tmp3 = s.get<i64>(scan_tmp_words(Nc));
+      scan_u32_to_i64(c, nbound, nooff, Nc, tmp3);
+    }
+    launch_check(c, "coarse classes");
+    i64 pc = 0, itot = 0, ntot = 0;
+    u32 hi[8] = {0}, hn[8] = {0};
+    if (merge_nb)
+      read_many(c, {{&pc, cg.e_off + E, sizeof pc},
+                    {&itot, iooff + Nc, sizeof itot},
+                    {hi, il.cnt, sizeof hi},
+                    {&ntot, nooff + Nc, sizeof ntot},
+                    {hn, nl.cnt, sizeof hn}});
+    else
+      read_many(c, {{&pc, cg.e_off + E, sizeof pc},
+                    {&itot, iooff + Nc, sizeof itot},
+                    {hi, il.cnt, sizeof hi}});
+    if (hn[7]) {
+      set_err(c, "%sa cluster's neighbour lists exceed 2^32 entries");
+      throw Fail{CHP_EOVERFLOW};
+    }
     cg.n_pins = (u64)pc;
     cg.e_pins = own.get<u32>((u64)pc);
     launch_pins_compact(c, E, g->e_off, opins, cg.e_off, cg.e_pins);
-    launch_check(c, "coarse pins");
-    s.release(opins);
-    build_incidence_merge(c, s, own, g, &cg, match, rep_of);
-    if (build_neighbors) {
-      if (g->nb_off && g->nb) build_neighbors_merge(c, s, own, g, &cg, match, rep_of, gamma);
-      else build_neighbors_core(c, s, own, &cg);
+    // -- coarse incidence
+    u32 *iobuf = s.get<u32>((u64)itot);
+    u64 *iscr = nullptr;
+    u64 iper = 0;
+    const u32 igb = grid_big_for(hi[2]);
+    if (hi[2]) {
+      iper = 2ull * hi[3];
+      iscr = s.get<u64>(iper * igb);
     }
-    hip_check(c, hipStreamSynchronize(c->stream), "contract");
+    launch_cinc_build(c, g->n_off, g->n_nin, g->n_inc, rep_of, match, iooff, iobuf, cg.n_nin,
+                      icnt, il, hi, iscr, iper, igb);
+    scan_u32_to_i64(c, icnt, cg.n_off, Nc, tmp2);
+    cg.n_inc = own.get<u32>(cg.n_pins);  // |I'| summed over clusters = pins of G'
+    launch_cinc_compact(c, Nc, rep_of, match, g->n_off, g->n_inc, iooff, iobuf, cg.n_off,
+                        cg.n_inc);
+    launch_check(c, "coarse incidence");
+    // -- coarse neighbours
+    if (merge_nb) {
+      cg.nb_off = own.get<i64>((u64)Nc + 1);
+      u32 *nobuf = s.get<u32>((u64)ntot);
+      u32 *ncount = s.get<u32>(Nc);
+      launch_fill_u32(c, ncount, Nc, 0);
+      launch_nbm_build(c, g->nb_off, g->nb, gamma, match, rep_of, nooff, nobuf, ncount, nl, hn);
+      scan_u32_to_i64(c, ncount, cg.nb_off, Nc, tmp3);
+      launch_check(c, "coarse neighbours");
+      i64 total;
+      read_back(c, &total, cg.nb_off + Nc, sizeof total);
+      cg.nb = own.get<u32>((u64)total);
+      cg.nb_total = (u64)total;
+      launch_nb_compact(c, Nc, nooff, nobuf, cg.nb_off, cg.nb);
+      launch_check(c, "coarse neighbour compaction");
+    } else if (build_neighbors) {
+      build_neighbors_core(c, s, own, &cg);
+    }
     own.keep = true;
     *coarse = cg;
   });

@@ -162,7 +162,9 @@ int chp_rate_and_match(chp_ctx *ctx, const chp_hgraph *g, const chp_params *prm,
  *             gamma(dst), src' = gamma(src) \ dst'; incidence rebuilt; N'
  *             rebuilt if build_neighbors != 0.
  * match must be a symmetric involution (match[match[n]] == n), else EINVAL.
- * Synchronises. */
+ * Synchronises to size its outputs; the last arrays of *coarse are written
+ * in stream order (use them on the same stream, or synchronise before
+ * reading them on the host). */
 int chp_contract(chp_ctx *ctx, const chp_hgraph *g, const uint32_t *match, uint32_t *gamma,
                  int build_neighbors, chp_hgraph *coarse);
 
