@@ -551,14 +551,6 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
     u64 *partials = s.get<u64>(2ull * np);
     u64 *capinfo = s.get<u64>(4);
     launch_terms(c, E, g->e_off, g->e_w, t, partials, np, capinfo);
-    NbLists nl;
-    nl.list[0] = s.get<u32>(N);
-    nl.list[1] = s.get<u32>(N);
-    nl.list[2] = nl.list[3] = nl.list[4] = nullptr;
-    nl.cnt = s.get<u32>(8);
-    launch_fill_u32(c, nl.cnt, 8, 0);
-    launch_rate_classify(c, N, g->nb_off, nl, target, score_fx);
-    launch_check(c, "rate classes");
     RateArgs a;
     a.N = N;
     a.e_off = g->e_off;
@@ -571,6 +563,7 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
     a.n_size = g->n_size;
     a.nb_off = g->nb_off;
     a.nb = g->nb;
+    a.cur = s.get<u32>(2 * g->n_pins);
     a.capinfo = capinfo;
     a.omega = prm->omega;
     a.delta = prm->delta;
@@ -579,8 +572,17 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
     a.target = target;
     a.score = score_fx;
     a.flags = c->flags;
-    u32 *work = s.get<u32>(2);
-    launch_rate(c, a, nl, work);
+    NbLists nl;
+    nl.list[0] = s.get<u32>(N);
+    nl.list[1] = nl.list[2] = nl.list[3] = nl.list[4] = nullptr;
+    nl.cnt = s.get<u32>(8);
+    NodeRec *recs = s.get<NodeRec>(N);
+    NodeRec *big = s.get<NodeRec>(N);
+    launch_fill_u32(c, nl.cnt, 8, 0);
+    launch_rate_classify(c, a, nl, recs, big);
+    launch_check(c, "rate classes");
+    u32 *work = s.get<u32>(3);
+    launch_rate(c, a, nl, recs, big, work);
     launch_check(c, "rate");
     MatchScratch ms;
     ms.bscore = s.get<u64>(N);

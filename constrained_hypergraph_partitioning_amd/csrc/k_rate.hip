@@ -97,22 +97,48 @@ __global__ __launch_bounds__(TB) void k_cap(u32 nparts, const u64 *partials, u32
 
 // ---------------------------------------------------------------------------
 // rating
-__global__ void k_rate_classify(u32 N, const i64 *nb_off, NbLists nl, u32 *target, u64 *score,
-                                u32 small_cap) {
+// Nodes by |N(n)| and |I(n)|: light (|N(n)| <= small_cap) are queued by id
+// in list[0]; the others with their record: heavy (<= heavy_cap) in recs[]
+// from the front; huge (above big_cap, at most heavy_ech hyperedges) in
+// recs[] from the back; big (the rest) in big[].  A huge node takes several
+// windows of either table; with one chunk of hyperedges a window costs the
+// small table little, and four of its workgroups share a CU.  A node without
+// neighbours gets no candidate here.
+__global__ void k_rate_classify(RateArgs A, NbLists nl, NodeRec *recs, NodeRec *big,
+                                u32 small_cap, u32 heavy_cap, u32 big_cap, u32 heavy_ech) {
   const u32 n = blockIdx.x * blockDim.x + threadIdx.x;
-  u64 K = 0;
-  if (n < N) {
-    K = (u64)(nb_off[n + 1] - nb_off[n]);
+  u64 K = 0, deg = 0;
+  if (n < A.N) {
+    K = (u64)(A.nb_off[n + 1] - A.nb_off[n]);
+    deg = (u64)(A.n_off[n + 1] - A.n_off[n]);
     if (K == 0) {
-      target[n] = NONE32;
-      score[n] = 0;
+      A.target[n] = NONE32;
+      A.score[n] = 0;
     }
   }
-  const int c = (n >= N || K == 0) ? 2 : (K <= small_cap ? 0 : 1);
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const u32 slot = wave_append(&nl.cnt[k], c == k);
-    if (c == k) nl.list[k][slot] = n;
+  const int c = (n >= A.N || K == 0)          ? 4
+                : K <= small_cap              ? 0
+                : K <= heavy_cap              ? 1
+                : K > big_cap && deg <= heavy_ech ? 3
+                                              : 2;
+  const u32 s0 = wave_append(&nl.cnt[0], c == 0);
+  if (c == 0) nl.list[0][s0] = n;
+  const u32 s1 = wave_append(&nl.cnt[1], c == 1);
+  const u32 s2 = wave_append(&nl.cnt[2], c == 2);
+  const u32 s3 = wave_append(&nl.cnt[3], c == 3);
+  if (c >= 1 && c <= 3) {
+    NodeRec r;
+    r.n = n;
+    r.K = (u32)K;
+    r.nin = A.n_nin[n];
+    r.size = A.n_size[n];
+    r.i0 = A.n_off[n];
+    r.deg = (u32)deg;
+    r.nb0 = A.nb_off[n];
+    r.pad0 = r.pad1 = r.pad2 = 0;
+    if (c == 1) recs[s1] = r;
+    else if (c == 2) big[s2] = r;
+    else recs[A.N - 1 - s3] = r;
   }
 }
 
@@ -132,52 +158,73 @@ __device__ __forceinline__ u64 wg_sat_sum(u64 v, u64 *lds) {
 }
 
 // ---------------------------------------------------------------------------
-// Rating kernel: one launch per level.  A node with more than RATE_SMALL_CAP
-// neighbours ("heavy") takes a whole workgroup, a "light" node one wave; both
-// pull nodes from a work counter, heavy ones first.
+// Rating: two launches per level.  A node with at most RATE_SMALL_CAP
+// neighbours ("light") takes one wave; a larger one a workgroup, either of
+// 256 threads with a 2048-slot table, four to a CU ("Heavy"), or, for nodes
+// whose neighbourhood would need several windows of that table, of 1024
+// threads with an 8192-slot table that fills most of the CU's LDS ("Big").
+// Every node is pulled from a work counter.
 //
-// Per node the neighbour list N(n) is loaded, a window of at most H_CAP ids at
-// a time (a light node's list always fits one), into an LDS hash table whose
-// slots are the bins of m in N(n):
+// Per node the neighbour list N(n) is loaded, a window of at most CAP ids at a
+// time, into an LDS hash table whose slots are the bins of m in N(n):
 //   eta  u64  eta(n,m) in fixed point; bit 63 set when size(n)+size(m) > Omega
 //             (free: a node whose terms plus the noise cap reach 2^63 is an
 //             overflow error anyway),
 //   rem  u32  |in(m)| - inter(n,m) = |in(m) \ in(n)|, so the inbound limit is
 //             |in(n)| + rem <= Delta.
 // Both limits are read together with the ids, so judging a candidate needs
-// no further memory access.  Incident hyperedges are taken a chunk at a time;
-// each brings a source run and a destination run of its pin list (for a
-// windowed node, clipped by binary search to the window's id interval, as the
-// runs and N(n) are sorted).  A scan lays the runs end to end and every thread
-// walks ITEMS consecutive pins with one run lookup, adding t(e) to the bin of
-// each pin m != n and, for a destination pin of an inbound hyperedge, taking
-// one from rem.  The candidate scan keeps, per thread, the best valid bin by
-// (eta desc, id asc), skipping a bin whose upper bound eta + cap cannot beat
-// it before its noise is computed; it empties each slot it reads, so the
-// table is clean for the next window or node.
-constexpr int RB = 256;
-constexpr int RW = RB / WAVE;
-constexpr u32 H_T = 2048, H_SHIFT = 21;  // hash slots of the heavy path
-constexpr u32 H_CAP = 1536;              // neighbours per window (load 0.75)
-constexpr int H_ECH = 128;               // hyperedges per chunk
+// no further memory access.  A node's header comes from a 48-byte record the
+// classification writes; its first window's ids and its first hyperedges'
+// incidence entries are loaded together, then their sizes, inbound counts and
+// descriptors, so that the opening costs two memory round trips.  The ids of
+// a window are inserted with all home-slot compare-and-swaps issued at once.
+//
+// Incident hyperedges are taken a chunk at a time; each brings a source run
+// and a destination run of its pin list (for a windowed node, the stretch of
+// each run inside the window, see rate_heavy).  A scan lays the runs end to
+// end and every thread loads up to IMAX consecutive pins, then reads their
+// home slots and their runs' terms (the destination run of an inbound
+// hyperedge carries a flag in its term), then adds t(e) to the bin of each
+// pin m != n and, for a flagged run, takes one from rem.  The candidate scan
+// keeps, per thread, the best valid bin by (eta desc, id asc), skipping a bin
+// whose upper bound eta + cap cannot beat the largest raw eta of a valid bin
+// before its noise is computed; it empties each slot it reads, so the table
+// is clean for the next window or node.
+// A heavy-path shape: B threads per node, T hash slots (T = 2^(32-SHIFT)),
+// at most CAP neighbours per window (load 0.75), ECH hyperedges per chunk.
+template <int B_, u32 T_, u32 SHIFT_, u32 CAP_, int ECH_>
+struct HCfg {
+  static constexpr int B = B_, W = B_ / WAVE, ECH = ECH_;
+  static constexpr u32 T = T_, SHIFT = SHIFT_, CAP = CAP_, UNR = CAP_ / B_;
+  static_assert(CAP_ % B_ == 0 && (1ull << (32 - SHIFT_)) == T_ && CAP_ * 4 <= T_ * 3, "shape");
+};
+// four workgroups of 256 per CU, a node of at most 1536 neighbours each
+using Heavy = HCfg<256, 2048, 21, 1536, 128>;
+// one workgroup of 1024 per CU (the table takes most of the LDS), windows of
+// 6144 neighbours: for the nodes that would need several windows above
+using Big = HCfg<1024, 8192, 19, 6144, 512>;
+constexpr int RB = Heavy::B;
+constexpr int RW = Heavy::W;
 constexpr u32 L_T = 512, L_SHIFT = 23;   // hash slots per wave, light path
 constexpr int L_ECH = 32;
-constexpr u32 ITEMS = 4;
+constexpr u32 IMAX = 8;  // pins per thread per round, at most
 constexpr u32 EMPTY = 0xFFFFFFFFu;
-constexpr u64 INB = 1ull << 63;  // run flag: destination run of an inbound hyperedge
+constexpr u64 INB = 1ull << 63;  // term flag: destination run of an inbound hyperedge
 constexpr u64 BAD = 1ull << 63;  // bin flag: the pair breaks Omega
 static_assert(RATE_SMALL_CAP <= L_T * 3 / 4, "light window must fit its table");
 
+template <class C>
 struct HeavySmem {
-  u64 eta[H_T];
-  u32 key[H_T];
-  u32 rem[H_T];
-  u64 rs[2 * H_ECH];
-  u64 rt[2 * H_ECH];
-  u32 pre[2 * H_ECH + 1];
-  u32 red32[RW + 1];
-  u64 red64[RW + 1];
-  u32 redi[RW + 1];
+  u64 eta[C::T];
+  u32 key[C::T];
+  u32 rem[C::T];
+  u64 rs[2 * C::ECH];
+  u64 rt[2 * C::ECH];
+  u32 pre[2 * C::ECH + 1];
+  u32 red32[C::W + 1];
+  u64 red64[C::W + 1];
+  u64 rede[C::W + 1];
+  u32 redi[C::W + 1];
 };
 struct LightWave {
   u64 eta[L_T];
@@ -188,7 +235,7 @@ struct LightWave {
   u32 pre[2 * L_ECH + 1];
 };
 union RateSmem {
-  HeavySmem h;
+  HeavySmem<Heavy> h;
   LightWave l[RW];
 };
 
@@ -201,18 +248,31 @@ __device__ __forceinline__ void wave_sync() {
 
 __device__ __forceinline__ u32 hslot(u32 m, u32 shift) { return (m * 0x9E3779B1u) >> shift; }
 
-// Insert neighbour m (not yet present; linear probing, bounded) into an empty
-// table slot together with its limit data.
-__device__ __forceinline__ void h_insert_bin(u32 *key, u64 *eta, u32 *rem, u32 mask, u32 shift,
-                                             u32 m, bool bad, u32 nin_m) {
-  u32 s = hslot(m, shift);
-  for (u32 p = 0; p <= mask; ++p) {
-    if (atomicCAS(&key[s], EMPTY, m) == EMPTY) {
-      eta[s] = bad ? BAD : 0;
-      rem[s] = nin_m;
-      return;
+// Insert the ids m[0, UNR) (EMPTY = none; all distinct and absent) with
+// their limit data: every id first tries its home slot (the compare-and-swaps
+// are issued together), then the ones that collided probe on.
+template <u32 UNR>
+__device__ __forceinline__ void insert_bins(u32 *key, u64 *eta, u32 *rem, u32 mask, u32 shift,
+                                            const u32 *m, const bool *bad, const u32 *ni) {
+  u32 s[UNR], got[UNR];
+#pragma unroll
+  for (u32 k = 0; k < UNR; ++k) {
+    s[k] = hslot(m[k], shift);
+    got[k] = m[k] != EMPTY ? atomicCAS(&key[s[k]], EMPTY, m[k]) : EMPTY;
+  }
+#pragma unroll
+  for (u32 k = 0; k < UNR; ++k) {
+    if (m[k] == EMPTY) continue;
+    if (got[k] != EMPTY) {
+      u32 q = (s[k] + 1) & mask;
+      for (u32 p = 0; p < mask; ++p) {
+        if (atomicCAS(&key[q], EMPTY, m[k]) == EMPTY) break;
+        q = (q + 1) & mask;
+      }
+      s[k] = q;
     }
-    s = (s + 1) & mask;
+    eta[s[k]] = bad[k] ? BAD : 0;
+    rem[s[k]] = ni[k];
   }
 }
 
@@ -230,34 +290,61 @@ __device__ __forceinline__ u32 h_find(const u32 *key, u32 mask, u32 shift, u32 m
 }
 
 // Walk the pins of runs [0, nruns) (flat length tot), LANES threads, t = this
-// thread's index among them.  Each thread first issues the loads of its
-// ITEMS consecutive pins, then updates their bins.
+// thread's index among them.  The pins are dealt in rounds of up to IMAX
+// consecutive pins per thread, as few per thread as lets one round cover
+// them all, so that no lane is left with a second round (and a second
+// memory round trip) that the others would wait for at the next barrier.
+// Each thread first issues the loads of its pins, then updates their bins.
 template <u32 LANES>
-__device__ __forceinline__ void visit_runs(const u32 *pins, const u32 *key, u32 mask, u32 shift,
-                                           u64 *eta, u32 *rem, const u64 *rs, const u64 *rt,
-                                           const u32 *pre, u32 nruns, u32 tot, u32 n, u32 t) {
-  for (u32 base = t * ITEMS; base < tot; base += LANES * ITEMS) {
+__device__ __forceinline__ void visit_runs(const u32 *__restrict__ pins,
+                                           const u32 *__restrict__ key, u32 mask, u32 shift,
+                                           u64 *__restrict__ eta, u32 *__restrict__ rem,
+                                           const u64 *__restrict__ rs, const u64 *__restrict__ rt,
+                                           const u32 *__restrict__ pre, u32 nruns, u32 tot, u32 n,
+                                           u32 t) {
+  const u32 need = (tot + LANES - 1) / LANES;
+  const u32 per = need < IMAX ? need : IMAX;
+  for (u32 base = t * per; base < tot; base += LANES * per) {
+    // the run of the first pin, its end and the pin index of flat index 0
+    // in it are kept in registers; LDS is read again only at a run boundary
     u32 r = run_of(pre, nruns + 1, base);
-    u32 m[ITEMS];
-    u32 rr[ITEMS];
+    u32 end = pre[r + 1];
+    i64 org = (i64)rs[r] - (i64)pre[r];
+    u32 m[IMAX];
+    u32 rr[IMAX];
 #pragma unroll
-    for (u32 k = 0; k < ITEMS; ++k) {
+    for (u32 k = 0; k < IMAX; ++k) {
       const u32 idx = base + k;
       m[k] = n;  // n marks "no pin": it is skipped below
       rr[k] = r;
-      if (idx < tot) {
-        while (idx >= pre[r + 1]) ++r;
+      if (k < per && idx < tot) {
+        while (idx >= end) {
+          ++r;
+          end = pre[r + 1];
+          org = (i64)rs[r] - (i64)pre[r];
+        }
         rr[k] = r;
-        m[k] = pins[(i64)(rs[r] & ~INB) + (idx - pre[r])];
+        m[k] = pins[org + idx];
       }
     }
+    // without branches, every pin's home slot and its run's term (with the
+    // inbound flag) are read together; a pin not at its home slot probes on
+    u32 sl[IMAX], kk[IMAX];
+    u64 tf[IMAX];
 #pragma unroll
-    for (u32 k = 0; k < ITEMS; ++k) {
-      if (m[k] == n) continue;
-      const u32 slot = h_find(key, mask, shift, m[k]);
-      if (slot == EMPTY) continue;  // cannot happen for a valid N(n)
-      atomicAdd(&eta[slot], rt[rr[k]]);
-      if (rs[rr[k]] & INB) atomicSub(&rem[slot], 1u);
+    for (u32 k = 0; k < IMAX; ++k) {
+      sl[k] = hslot(m[k], shift);
+      kk[k] = key[sl[k]];
+      tf[k] = rt[rr[k]];
+    }
+#pragma unroll
+    for (u32 k = 0; k < IMAX; ++k)
+      if (kk[k] != m[k] && m[k] != n) sl[k] = h_find(key, mask, shift, m[k]);
+#pragma unroll
+    for (u32 k = 0; k < IMAX; ++k) {
+      if (m[k] == n || sl[k] == EMPTY) continue;  // EMPTY cannot happen for a valid N(n)
+      atomicAdd(&eta[sl[k]], tf[k] & ~INB);
+      if (tf[k] & INB) atomicSub(&rem[sl[k]], 1u);
     }
   }
 }
@@ -277,39 +364,38 @@ __device__ __forceinline__ void insert_window(const RateArgs &A, const u32 *nb, 
       m[k] = i < cw ? nb[i] : EMPTY;
     }
 #pragma unroll
-    for (u32 k = 0; k < UNR; ++k) {
-      sz[k] = 0;
-      ni[k] = 0;
-      if (m[k] != EMPTY) {
-        sz[k] = A.n_size[m[k]];
-        ni[k] = A.n_nin[m[k]];
-      }
+    for (u32 k = 0; k < UNR; ++k) {  // branch-free: an absent id reads entry 0
+      const u32 mk = m[k] != EMPTY ? m[k] : 0;
+      sz[k] = A.n_size[mk];
+      ni[k] = A.n_nin[mk];
     }
+    bool bad[UNR];
 #pragma unroll
-    for (u32 k = 0; k < UNR; ++k)
-      if (m[k] != EMPTY)
-        h_insert_bin(key, eta, rem, mask, shift, m[k], size_n + sz[k] > A.omega, ni[k]);
+    for (u32 k = 0; k < UNR; ++k) bad[k] = size_n + sz[k] > A.omega;
+    insert_bins<UNR>(key, eta, rem, mask, shift, m, bad, ni);
   }
 }
 
-// Hyperedge segment [a, b) with destinations from dm: its source and
-// destination runs, clipped to [lo, hi] if clip.
-__device__ __forceinline__ void edge_runs(const u32 *pins, i64 a, i64 b, i64 dm, u64 te, bool isin,
-                                          bool clip, u32 lo, u32 hi, u64 *rs, u64 *rt, u32 &ls,
-                                          u32 &ld) {
-  i64 sa = a, sb = dm, da = dm, db = b;
-  if (clip) {
-    sa = lower_bound_i(pins, a, dm, lo);
-    sb = upper_bound_i(pins, sa, dm, hi);
-    da = lower_bound_i(pins, dm, b, lo);
-    db = upper_bound_i(pins, da, b, hi);
+// r1 = first index in a[lo1, hi1) with a[i] > v, r2 likewise in [lo2, hi2):
+// two binary searches in lockstep, so that each step costs one memory round
+// trip for both (a finished search reads a[0], which always exists).
+__device__ __forceinline__ void upper_bound2(const u32 *a, i64 lo1, i64 hi1, i64 lo2, i64 hi2,
+                                             u32 v, i64 &r1, i64 &r2) {
+  while (lo1 < hi1 || lo2 < hi2) {
+    const i64 m1 = lo1 + ((hi1 - lo1) >> 1), m2 = lo2 + ((hi2 - lo2) >> 1);
+    const u32 x1 = a[lo1 < hi1 ? m1 : 0];
+    const u32 x2 = a[lo2 < hi2 ? m2 : 0];
+    if (lo1 < hi1) {
+      if (x1 <= v) lo1 = m1 + 1;
+      else hi1 = m1;
+    }
+    if (lo2 < hi2) {
+      if (x2 <= v) lo2 = m2 + 1;
+      else hi2 = m2;
+    }
   }
-  rs[0] = (u64)sa;
-  rs[1] = (u64)da | (isin ? INB : 0);
-  rt[0] = te;
-  rt[1] = te;
-  ls = (u32)(sb - sa);
-  ld = (u32)(db - da);
+  r1 = lo1;
+  r2 = lo2;
 }
 
 struct EdgeDesc {
@@ -369,56 +455,128 @@ __device__ __forceinline__ u64 wg_max_u64(u64 v, u64 *lds) {
   return m;
 }
 
-__device__ void rate_heavy(const RateArgs &A, HeavySmem &S, u32 n, u64 cap, u64 dmod,
+
+// The opening of a heavy node, loaded in two stages so that each costs one
+// memory round trip: this thread's incidence entry of the first chunk and its
+// share of the first window's ids, then that hyperedge's descriptor and the
+// ids' sizes and inbound counts.
+template <class C>
+__device__ __forceinline__ void open_node(const RateArgs &A, const NodeRec &h, u32 t,
+                                          EdgeDesc &d0, u32 *m, u32 *sz, u32 *ni) {
+  const u32 ne0 = h.deg < (u32)C::ECH ? h.deg : (u32)C::ECH;
+  const u32 cw = h.K < C::CAP ? h.K : C::CAP;
+  const u32 e0 = t < ne0 ? A.n_inc[h.i0 + t] : EMPTY;
+#pragma unroll
+  for (u32 k = 0; k < C::UNR; ++k) {
+    const u32 i = t + k * C::B;
+    m[k] = i < cw ? A.nb[h.nb0 + i] : EMPTY;
+  }
+  // second stage without branches (an absent item reads entry 0), so that
+  // every load is issued before the first is waited for
+  const u32 e = e0 != EMPTY ? e0 : 0;
+  d0.a = A.e_off[e];
+  d0.b = A.e_off[e + 1];
+  d0.dm = d0.a + A.e_nsrc[e];
+  d0.te = A.t[e];
+#pragma unroll
+  for (u32 k = 0; k < C::UNR; ++k) {
+    const u32 mk = m[k] != EMPTY ? m[k] : 0;
+    sz[k] = A.n_size[mk];
+    ni[k] = A.n_nin[mk];
+  }
+}
+
+template <class C>
+__device__ void rate_heavy(const RateArgs &A, HeavySmem<C> &S, const NodeRec &h, u64 cap, u64 dmod,
                            u64 magic) {
   const u32 tid = threadIdx.x;
-  const i64 nb0 = A.nb_off[n];
-  const u32 K = (u32)(A.nb_off[n + 1] - nb0);
-  const i64 i0 = A.n_off[n], i1 = A.n_off[n + 1];
-  const u32 nin = A.n_nin[n];
-  const u64 size_n = A.n_size[n];
+  const u32 n = h.n, K = h.K, nin = h.nin;
+  const i64 nb0 = h.nb0, i0 = h.i0, i1 = h.i0 + h.deg;
+  const u64 size_n = h.size;
   const u64 ub_add = A.noise_on ? cap : 0;
-  const bool clip = K > H_CAP;
-  const u32 ne0 = (u32)((i1 - i0) < H_ECH ? (i1 - i0) : H_ECH);
   NodeBest best{0, NONE32};
   u64 tsum = 0;
-  for (u32 s0 = 0; s0 < K; s0 += H_CAP) {
-    const u32 cw = (K - s0) < H_CAP ? (K - s0) : H_CAP;
-    // this thread's hyperedge of the first chunk, loaded ahead of the inserts
-    EdgeDesc d0{0, 0, 0, 0};
-    if (tid < ne0) d0 = load_edge(A, i0 + tid);
-    insert_window<RB>(A, A.nb + nb0 + s0, cw, size_n, S.key, S.eta, S.rem, H_T - 1, H_SHIFT,
-                      tid);
-    const u32 lo = A.nb[nb0 + s0], hi = A.nb[nb0 + s0 + cw - 1];
+  EdgeDesc d0;
+  {
+    u32 m[C::UNR], sz[C::UNR], ni[C::UNR];
+    open_node<C>(A, h, tid, d0, m, sz, ni);
+    bool bad[C::UNR];
+#pragma unroll
+    for (u32 k = 0; k < C::UNR; ++k) bad[k] = size_n + sz[k] > A.omega;
+    insert_bins<C::UNR>(S.key, S.eta, S.rem, C::T - 1, C::SHIFT, m, bad, ni);
+  }
+  // Windows cover N(n) in id order.  The pins of a sorted run that fall in
+  // window w form the stretch from where window w-1 stopped (its cursor)
+  // to the first pin above the window's last id; between two windows lies
+  // no neighbour, only n itself, which the visit skips.  So a window needs
+  // one upper-bound search per run (none for the last window), started at
+  // the cursor.  Cursors of a node whose hyperedges fit one chunk stay in
+  // registers; otherwise they are kept per incidence entry in A.cur (as the
+  // number of pins left in the run).
+  const bool one_chunk = h.deg <= (u32)C::ECH;
+  i64 cs0 = 0, cd0 = 0;
+  for (u32 s0 = 0; s0 < K; s0 += C::CAP) {
+    const u32 cw = (K - s0) < C::CAP ? (K - s0) : C::CAP;
+    const bool last = s0 + C::CAP >= K;
+    if (s0 > 0)
+      insert_window<C::B>(A, A.nb + nb0 + s0, cw, size_n, S.key, S.eta, S.rem, C::T - 1, C::SHIFT,
+                        tid);
+    const u32 hi = A.nb[nb0 + s0 + cw - 1];
     __syncthreads();
-    for (i64 c0 = i0; c0 < i1; c0 += H_ECH) {
-      const u32 ne = (u32)((i1 - c0) < H_ECH ? (i1 - c0) : H_ECH);
+    for (i64 c0 = i0; c0 < i1; c0 += C::ECH) {
+      const u32 ne = (u32)((i1 - c0) < C::ECH ? (i1 - c0) : C::ECH);
       u32 ls = 0, ld = 0;
       if (tid < ne) {
         const EdgeDesc d = c0 == i0 ? d0 : load_edge(A, c0 + tid);
         if (s0 == 0 && d.b - d.a >= 2) tsum = sat_add(tsum, d.te);
-        edge_runs(A.e_pins, d.a, d.b, d.dm, d.te, (u64)(c0 + tid - i0) < (u64)nin, clip, lo, hi,
-                  &S.rs[2 * tid], &S.rt[2 * tid], ls, ld);
+        const i64 j = c0 + tid;
+        i64 sa = d.a, da = d.dm;
+        if (s0 > 0) {
+          if (one_chunk) {
+            sa = cs0;
+            da = cd0;
+          } else {
+            sa = d.dm - A.cur[2 * j];
+            da = d.b - A.cur[2 * j + 1];
+          }
+        }
+        i64 sb = d.dm, db = d.b;
+        if (!last) {
+          upper_bound2(A.e_pins, sa, d.dm, da, d.b, hi, sb, db);
+          if (one_chunk) {
+            cs0 = sb;
+            cd0 = db;
+          } else {
+            A.cur[2 * j] = (u32)(d.dm - sb);
+            A.cur[2 * j + 1] = (u32)(d.b - db);
+          }
+        }
+        S.rs[2 * tid] = (u64)sa;
+        S.rs[2 * tid + 1] = (u64)da;
+        S.rt[2 * tid] = d.te;
+        S.rt[2 * tid + 1] = d.te | ((u64)(j - i0) < (u64)nin ? INB : 0);
+        ls = (u32)(sb - sa);
+        ld = (u32)(db - da);
       }
       u32 tot;
-      const u32 off = wg_excl_scan<RB>(ls + ld, S.red32, &tot);
+      const u32 off = wg_excl_scan<C::B>(ls + ld, S.red32, &tot);
       if (tid < ne) {
         S.pre[2 * tid] = off;
         S.pre[2 * tid + 1] = off + ls;
       }
       if (tid == 0) S.pre[2 * ne] = tot;
       __syncthreads();
-      visit_runs<RB>(A.e_pins, S.key, H_T - 1, H_SHIFT, S.eta, S.rem, S.rs, S.rt, S.pre, 2 * ne,
+      visit_runs<C::B>(A.e_pins, S.key, C::T - 1, C::SHIFT, S.eta, S.rem, S.rs, S.rt, S.pre, 2 * ne,
                      tot, n, tid);
       __syncthreads();
     }
     u64 floor = 0;
-    for (u32 i = tid; i < H_T; i += RB) {
+    for (u32 i = tid; i < C::T; i += C::B) {
       const u64 v = S.eta[i];
       if (S.key[i] != EMPTY && bin_valid(A, nin, v, S.rem[i]) && v > floor) floor = v;
     }
-    floor = wg_max_u64<RB>(floor, S.red64);
-    for (u32 i = tid; i < H_T; i += RB) {
+    floor = wg_max_u64<C::B>(floor, S.red64);
+    for (u32 i = tid; i < C::T; i += C::B) {
       const u32 m = S.key[i];
       if (m != EMPTY) {
         consider(A, n, nin, m, S.eta[i], S.rem[i], ub_add, floor, dmod, magic, best);
@@ -426,11 +584,33 @@ __device__ void rate_heavy(const RateArgs &A, HeavySmem &S, u32 n, u64 cap, u64 
         S.eta[i] = 0;
       }
     }
-    __syncthreads();
+    // after the last window the reduction's barrier orders these clears
+    // before the next node's inserts
+    if (s0 + C::CAP < K) __syncthreads();
   }
-  tsum = wg_sat_sum<RB>(tsum, S.red64);
-  wg_best<RB>(best.e, best.i, S.red64, S.redi);
+  // term sum and best candidate: per wave by shuffles, then thread 0
+  // combines the waves' partials
+#pragma unroll
+  for (int d = WAVE / 2; d > 0; d >>= 1) {
+    tsum = sat_add(tsum, __shfl_xor(tsum, d, WAVE));
+    const u64 oe = __shfl_xor(best.e, d, WAVE);
+    const u32 oi = __shfl_xor(best.i, d, WAVE);
+    if (better(oe, oi, best.e, best.i)) best.e = oe, best.i = oi;
+  }
+  if (lane_id() == 0) {
+    S.red64[wave_id()] = tsum;
+    S.rede[wave_id()] = best.e;
+    S.redi[wave_id()] = best.i;
+  }
+  __syncthreads();
   if (tid == 0) {
+    tsum = 0;
+    best = NodeBest{0, NONE32};
+#pragma unroll
+    for (int w = 0; w < C::W; ++w) {
+      tsum = sat_add(tsum, S.red64[w]);
+      if (better(S.rede[w], S.redi[w], best.e, best.i)) best.e = S.rede[w], best.i = S.redi[w];
+    }
     if (sat_add(tsum, cap) >= (1ull << 63)) atomicOr(A.flags, FLAG_EOVERFLOW);
     A.target[n] = best.i;
     A.score[n] = best.i == NONE32 ? 0 : best.e;
@@ -460,8 +640,12 @@ __device__ void rate_light(const RateArgs &A, LightWave &S, u32 n, u64 cap, u64 
     if (l < ne) {
       const EdgeDesc d = c0 == i0 ? d0 : load_edge(A, c0 + l);
       if (d.b - d.a >= 2) tsum = sat_add(tsum, d.te);
-      edge_runs(A.e_pins, d.a, d.b, d.dm, d.te, (u64)(c0 + l - i0) < (u64)nin, false, 0, 0,
-                &S.rs[2 * l], &S.rt[2 * l], ls, ld);
+      S.rs[2 * l] = (u64)d.a;
+      S.rs[2 * l + 1] = (u64)d.dm;
+      S.rt[2 * l] = d.te;
+      S.rt[2 * l + 1] = d.te | ((u64)(c0 + l - i0) < (u64)nin ? INB : 0);
+      ls = (u32)(d.dm - d.a);
+      ld = (u32)(d.b - d.dm);
     }
     const u32 v = ls + ld;
     const u32 inc = wave_incl_scan(v);
@@ -499,47 +683,98 @@ __device__ void rate_light(const RateArgs &A, LightWave &S, u32 n, u64 cap, u64 
   }
 }
 
-// cnt[0] light nodes in light[], cnt[1] heavy nodes in heavy[]; work[0..1]
-// are zeroed work counters.  Heavy nodes are taken one per workgroup, then
-// light ones one per wave, each from its counter (node costs are heavy
-// tailed, so a static deal leaves some workgroups far behind).  The work
-// index is a scalar (readfirstlane) and each loop body ends with a barrier (a
-// wave barrier for the light loop), so every lane reconverges before the
-// back edge: without that the compiler may route thread 0, which alone takes
-// the next item, around the other lanes, which then re-enter the loop on the
-// stale item and never leave.
-__global__ __launch_bounds__(RB) void k_rate(RateArgs A, const u32 *light, const u32 *heavy,
+__device__ __forceinline__ u32 rfl(u32 v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ NodeRec rec_from_lds(const u32 *w) {
+  NodeRec h;
+  h.n = rfl(w[0]);
+  h.K = rfl(w[1]);
+  h.nin = rfl(w[2]);
+  h.size = rfl(w[3]);
+  h.deg = rfl(w[4]);
+  h.nb0 = (i64)((u64)rfl(w[6]) | ((u64)rfl(w[7]) << 32));
+  h.i0 = (i64)((u64)rfl(w[8]) | ((u64)rfl(w[9]) << 32));
+  return h;
+}
+
+// Work items: cnt[0] light nodes in light[]; records of cnt[1] heavy nodes
+// (one window of Heavy) at the front of recs[] and of cnt[3] huge ones (more
+// than one window of Big, one chunk of Heavy) at its back; cnt[2] big ones in
+// big[]; work[0..2] are zeroed work counters.
+// k_rate_big rates the big nodes, a workgroup of Big per node; k_rate the
+// huge then the heavy ones, a workgroup of Heavy per node, HB at a time (one
+// counter access and one load of the records per batch), then the light
+// ones, a wave per node.  Every node is taken from a counter (node costs are
+// heavy tailed, so a static deal leaves some workgroups far behind), the
+// costliest kinds first.  Work indices are scalars (readfirstlane) and each
+// loop body ends with a barrier (a wave barrier for the light loop), so every
+// lane reconverges before the back edge: without that the compiler may route
+// thread 0, which alone takes the next item, around the other lanes, which
+// then re-enter the loop on the stale item and never leave.
+constexpr u32 HB = 2;  // heavy nodes per counter access
+static_assert(HB * 12 <= RB, "record words of a batch");
+
+// rec(j) is the record of item j < nh
+template <class C, u32 NB, typename RecAt>
+__device__ __forceinline__ void heavy_loop(const RateArgs &A, HeavySmem<C> &S, u32 *s_item,
+                                           u32 *s_rec, RecAt rec, u32 nh, u32 *work, u64 cap,
+                                           u64 dmod, u64 magic) {
+  const u32 tid = threadIdx.x;
+  for (u32 i = tid; i < C::T; i += C::B) {
+    S.key[i] = EMPTY;
+    S.eta[i] = 0;
+  }
+  for (;;) {
+    if (tid == 0) *s_item = atomicAdd(work, NB);
+    __syncthreads();
+    const u32 w = rfl(*s_item);
+    if (w >= nh) break;
+    const u32 nb_ = nh - w < NB ? nh - w : NB;
+    if (tid < nb_ * 12) s_rec[tid] = reinterpret_cast<const u32 *>(rec(w + tid / 12))[tid % 12];
+    __syncthreads();
+    for (u32 j = 0; j < nb_; ++j)
+      rate_heavy<C>(A, S, rec_from_lds(s_rec + j * 12), cap, dmod, magic);
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_rate_big(RateArgs A, const NodeRec *big,
+                                                   const u32 *cnt, u32 *work) {
+  __shared__ HeavySmem<Big> S;
+  __shared__ u32 s_item;
+  __shared__ u32 s_rec[12];
+  const u64 cap = A.capinfo[0], dmod = A.capinfo[1], magic = A.capinfo[2];
+  heavy_loop<Big, 1>(A, S, &s_item, s_rec, [&](u32 j) { return big + j; }, cnt[2], &work[2], cap,
+                     dmod, magic);
+}
+
+__global__ __launch_bounds__(RB) void k_rate(RateArgs A, const u32 *light, const NodeRec *recs,
                                              const u32 *cnt, u32 *work) {
   __shared__ RateSmem sm;
   __shared__ u32 s_item;
-  const u32 nl = cnt[0], nh = cnt[1];
+  __shared__ u32 s_rec[HB * 12];
+  const u32 nl = cnt[0], nhuge = cnt[3];
   const u64 cap = A.capinfo[0], dmod = A.capinfo[1], magic = A.capinfo[2];
-  for (u32 i = threadIdx.x; i < H_T; i += RB) {
-    sm.h.key[i] = EMPTY;
-    sm.h.eta[i] = 0;
-  }
-  for (;;) {
-    if (threadIdx.x == 0) s_item = atomicAdd(&work[0], 1u);
-    __syncthreads();
-    const u32 w = __builtin_amdgcn_readfirstlane(s_item);
-    __syncthreads();
-    if (w >= nh) break;
-    rate_heavy(A, sm.h, heavy[w], cap, dmod, magic);
-    __syncthreads();
-  }
+  heavy_loop<Heavy, HB>(
+      A, sm.h, &s_item, s_rec,
+      [&](u32 j) { return j < nhuge ? recs + (A.N - 1 - j) : recs + (j - nhuge); },
+      cnt[1] + nhuge, &work[0], cap, dmod, magic);
   LightWave &S = sm.l[wave_id()];
   for (u32 i = lane_id(); i < L_T; i += WAVE) {
     S.key[i] = EMPTY;
     S.eta[i] = 0;
   }
   wave_sync();
+  u32 lw = 0;
+  if (lane_id() == 0) lw = atomicAdd(&work[1], 1u);
+  lw = __builtin_amdgcn_readfirstlane(__shfl(lw, 0, WAVE));
   for (;;) {
-    u32 w = 0;
-    if (lane_id() == 0) w = atomicAdd(&work[1], 1u);
-    w = __builtin_amdgcn_readfirstlane(__shfl(w, 0, WAVE));
-    if (w >= nl) break;
-    rate_light(A, S, light[w], cap, dmod, magic);
+    if (lw >= nl) break;
+    u32 nxt = 0;
+    if (lane_id() == 0) nxt = atomicAdd(&work[1], 1u);
+    rate_light(A, S, light[lw], cap, dmod, magic);
     wave_sync();
+    lw = __builtin_amdgcn_readfirstlane(__shfl(nxt, 0, WAVE));
   }
 }
 
@@ -675,17 +910,19 @@ void launch_terms(chp_ctx *c, u32 E, const i64 *e_off, const u32 *e_w, u64 *t, u
   CHP_LAUNCH(c, "cap", k_cap, 1, TB, 0, E ? nparts : 0u, (const u64 *)partials, E, capinfo);
 }
 
-void launch_rate_classify(chp_ctx *c, u32 N, const i64 *nb_off, NbLists nl, u32 *target,
-                          u64 *score) {
-  if (N == 0) return;
-  CHP_LAUNCH(c, "rate_classify", k_rate_classify, grid_for(N, 256), 256, 0, N, nb_off, nl, target,
-             score, RATE_SMALL_CAP);
+void launch_rate_classify(chp_ctx *c, const RateArgs &a, NbLists nl, NodeRec *recs,
+                          NodeRec *big) {
+  if (a.N == 0) return;
+  CHP_LAUNCH(c, "rate_classify", k_rate_classify, grid_for(a.N, 256), 256, 0, a, nl, recs, big,
+             RATE_SMALL_CAP, Heavy::CAP, Big::CAP, (u32)Heavy::ECH);
 }
 
-void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, u32 *work) {
-  launch_fill_u32(c, work, 2, 0);
-  CHP_LAUNCH(c, "rate", k_rate, c->n_cu * 4, RB, 0, a, (const u32 *)nl.list[0],
-             (const u32 *)nl.list[1], (const u32 *)nl.cnt, work);
+void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, const NodeRec *recs,
+                 const NodeRec *big, u32 *work) {
+  launch_fill_u32(c, work, 3, 0);
+  CHP_LAUNCH(c, "rate_big", k_rate_big, c->n_cu, Big::B, 0, a, big, (const u32 *)nl.cnt, work);
+  CHP_LAUNCH(c, "rate", k_rate, c->n_cu * 4, RB, 0, a, (const u32 *)nl.list[0], recs,
+             (const u32 *)nl.cnt, work);
 }
 
 void launch_match(chp_ctx *c, u32 N, const u32 *target, const u64 *score, MatchScratch ms,

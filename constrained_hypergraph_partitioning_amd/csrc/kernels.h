@@ -60,6 +60,15 @@ void launch_nb_compact(chp_ctx *c, u32 N, const i64 *ooff, const u32 *obuf, cons
 u32 terms_partials(u32 E);
 void launch_terms(chp_ctx *c, u32 E, const i64 *e_off, const u32 *e_w, u64 *t, u64 *partials,
                   u32 nparts, u64 *capinfo);
+// Header of a node queued for the rating kernel (48 bytes, read a word per
+// lane): n, |N(n)|, |in(n)|, size(n), |I(n)|, nb_off[n], n_off[n].
+struct NodeRec {
+  u32 n, K, nin, size, deg, pad0;
+  i64 nb0, i0;
+  u32 pad1, pad2;
+};
+static_assert(sizeof(NodeRec) == 48, "NodeRec layout");
+
 struct RateArgs {
   u32 N;
   const i64 *e_off;
@@ -72,6 +81,7 @@ struct RateArgs {
   const u32 *n_size;
   const i64 *nb_off;
   const u32 *nb;
+  u32 *cur;  // [2 * pins] window cursors of nodes whose hyperedges span several chunks
   const u64 *capinfo;
   u64 omega;
   u32 delta;
@@ -81,9 +91,10 @@ struct RateArgs {
   u64 *score;
   u32 *flags;
 };
-void launch_rate_classify(chp_ctx *c, u32 N, const i64 *nb_off, NbLists nl, u32 *target,
-                          u64 *score);
-void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, u32 *work);
+void launch_rate_classify(chp_ctx *c, const RateArgs &a, NbLists nl, NodeRec *recs,
+                          NodeRec *big);
+void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, const NodeRec *recs,
+                 const NodeRec *big, u32 *work);
 
 struct MatchScratch {
   u64 *bscore;  // [N] zeroed

@@ -174,6 +174,35 @@ def test_wide_neighbourhoods_and_big_edges(chp, ctx):
     eval_pair(chp, ctx, dg, og, rho, 37, 1 << 30, 1 << 30, "big eval")
 
 
+def test_windowed_nodes_with_many_hyperedges(chp, ctx):
+    """Nodes whose neighbourhood spans several rating windows (|N(n)| above
+    6144) and whose incident hyperedges span several chunks (more than 128,
+    and more than 512): the window cursors are then kept per incidence entry
+    in device memory.  Also nodes between one and four windows of the small
+    table, which the large-table kernel rates in one window."""
+    for n, kmin, kmax, seed in ((8000, 140, 180, 21), (2000, 520, 560, 22), (9000, 60, 80, 23)):
+        say("windowed", n, kmin, kmax)
+        spec = synth.custom(synth.UNIFORM, n, n, kmin, kmax, 8, 1, 1 << 20, 1 << 20, seed)
+        h = synth.generate(spec)
+        multilevel(chp, ctx, h, spec.omega, spec.delta, True, seed, 1, tag="windowed")
+    # hubs in 700 hyperedges of 20 pins over 10,000 nodes: |N(n)| about 7,500
+    # and more incident hyperedges than one chunk of the large table (512)
+    say("windowed hubs")
+    rng = np.random.Generator(np.random.PCG64(24))
+    n = 10000
+    el = []
+    for hub in (17, 4242, 9999, 5000, 123):
+        for _ in range(700):
+            p = rng.permutation(n)[:20]
+            p = p[p != hub][:19]
+            el.append(([int(p[0])], [hub] + [int(x) for x in p[1:]]))
+    for _ in range(3000):
+        p = rng.permutation(n)[: int(rng.integers(2, 9))]
+        el.append(([int(p[0])], [int(x) for x in p[1:]]))
+    h = synth.from_lists(n, el, rng.integers(1, 9, len(el)).tolist())
+    multilevel(chp, ctx, h, 1 << 20, 1 << 20, True, 24, 2, tag="hubs")
+
+
 def test_determinism(chp, ctx):
     spec = synth.config(2, n_nodes=20000)
     h = synth.generate(spec)
