@@ -17,6 +17,9 @@ on its stream during the timed steps.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +29,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+RATE_KERNELS = ("rate_big", "rate")
+RATE_SOURCE = os.path.join(ROOT, "constrained_hypergraph_partitioning_amd", "csrc", "k_rate.hip")
+COUNTERS_JSON = os.path.join(ROOT, "profiles", "rating_counters.json")
+COPY_REF_MIB = 256
 
 
 def parse():
@@ -40,7 +47,68 @@ def parse():
     p.add_argument("--copy-ref-mib", type=int, default=0,
                    help="run one plain device copy of this size first (a reference for "
                         "scaling hardware byte counters)")
+    p.add_argument("--counters", metavar="DIR", default=None,
+                   help="no run: summarise the rocprofv3 FETCH_SIZE and WRITE_SIZE passes "
+                        "under DIR/fetch and DIR/write into " + COUNTERS_JSON)
     return p.parse_args()
+
+
+def source_sha():
+    with open(RATE_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def kernel_base(name):
+    """'void (anonymous namespace)::k_rate<...>(args)' -> 'k_rate'."""
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0].split("<")[0].strip()
+
+
+def _counter_rows(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit("expected one counter_collection.csv under %s, found %d" % (d, len(files)))
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_counters(d, workload):
+    """HBM bytes per rating pass from two counter passes (FETCH_SIZE, then
+    WRITE_SIZE; KiB per dispatch), each scaled by what the same counter read
+    for the reference copy of COPY_REF_MIB MiB that the profiled run made
+    first (its bytes read and written are known)."""
+    out = {"source_sha256": source_sha(), "workload": workload,
+           "copy_ref_bytes": COPY_REF_MIB << 20}
+    for name, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        rows = [r for r in _counter_rows(os.path.join(d, name)) if r["Counter_Name"] == counter]
+        ref = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        rate = [r for r in rows if kernel_base(r["Kernel_Name"]) in ("k_rate", "k_rate_big")]
+        passes = sum(1 for r in rate if kernel_base(r["Kernel_Name"]) == "k_rate")
+        if not ref or not passes:
+            raise SystemExit("%s: no reference copy or no rating dispatch found" % name)
+        kib = sum(float(r["Counter_Value"]) for r in rate)
+        scale = (COPY_REF_MIB << 10) / max(ref)
+        out[name] = {"counter": counter, "kib_per_pass": kib / passes, "passes": passes,
+                     "copy_ref_kib": max(ref), "scale": scale}
+    out["traffic_bytes_per_pass"] = 1024 * (out["fetch"]["kib_per_pass"] * out["fetch"]["scale"] +
+                                            out["write"]["kib_per_pass"] * out["write"]["scale"])
+    os.makedirs(os.path.dirname(COUNTERS_JSON), exist_ok=True)
+    with open(COUNTERS_JSON, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def measured_traffic(workload):
+    """Bytes per rating pass from the committed counter summary, if it was
+    taken on this workload with the current rating source; else None."""
+    try:
+        with open(COUNTERS_JSON) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("source_sha256") != source_sha() or c.get("workload") != workload:
+        return None
+    return c.get("traffic_bytes_per_pass")
 
 
 def run_step(chp, ctx, dev_edges, spec, rho_buf):
@@ -107,6 +175,10 @@ def cpu_baseline(h, spec, workload, sample_nodes):
 
 def main():
     args = parse()
+    if args.counters:
+        import synth
+        summarize_counters(args.counters, synth.config(args.workload, n_nodes=args.nodes).name)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -146,10 +218,13 @@ def main():
     timings = ctx.timings()
     ctx.set_timing(False)
 
-    # The rating kernel ("rate", one launch per level) and its algorithmic
-    # bytes: each array it reads or writes counted once per level.
+    # The rating pass (per level one launch of "rate_big", the nodes whose
+    # neighbourhood exceeds one window of the small table, and one of
+    # "rate", all other nodes) and its algorithmic bytes: each array it reads
+    # or writes counted once per level.
     dom = max(timings.items(), key=lambda kv: kv[1][1])
-    rate_launches, rate_ms = timings.get("rate", (0, 0.0))
+    rate_launches = timings.get("rate", (0, 0.0))[0]
+    rate_ms = sum(timings.get(k, (0, 0.0))[1] for k in RATE_KERNELS)
     level_bytes = rate_level_bytes(levels, h, spec)
     rate_bytes_per_step = sum(level_bytes)
     achieved = rate_bytes_per_step * args.steps / (rate_ms / 1e3) / 1e9 if rate_ms else 0.0
@@ -175,11 +250,12 @@ def main():
                    "pins": h.n_pins, "omega": spec.omega, "delta": spec.delta,
                    "levels": len(levels), "final_nodes": levels[-1][0] - levels[-1][2]
                    if levels else h.n_nodes, "connectivity": int(summ[0])},
-        "roofline": {"bound": "hbm", "kernel": "rate",
+        "roofline": {"bound": "hbm", "kernel": "rate_big+rate (the rating pass)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "avg_launch_ms": rate_ms / max(rate_launches, 1),
-                     "alg_bytes_per_step": rate_bytes_per_step, "traffic": None},
+                     "avg_pass_ms": rate_ms / max(rate_launches, 1),
+                     "alg_bytes_per_pass": rate_bytes_per_step / max(len(levels), 1),
+                     "traffic": measured_traffic(spec.name)},
         "kernel_ms_per_step": kern_ms,
         "kernel_sum_ms_per_step": level_ms,
         "dominant_kernel": dom[0],
