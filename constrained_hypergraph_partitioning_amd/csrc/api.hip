@@ -140,34 +140,52 @@ __global__ void k_fill_u64(u64 *p, u64 n, u64 v) {
     p[i] = v;
 }
 
-// copy n bytes device->host and wait for the stream
-void read_back(chp_ctx *c, void *host, const void *dev, size_t n) {
-  hip_check(c, hipMemcpyAsync(c->pinned, dev, n, hipMemcpyDeviceToHost, c->stream), "readback");
-  hip_check(c, hipStreamSynchronize(c->stream), "stream synchronize");
-  memcpy(host, c->pinned, n);
+// Small device->host reads.  One kernel gathers the words of every item into
+// the context's pinned host buffer (mapped into the device address space),
+// then the stream is synchronised: one launch and no copy engine per call.
+constexpr u32 PUB_MAX = 12;
+struct PubDesc {
+  const u32 *src[PUB_MAX];
+  u32 off[PUB_MAX + 1];  // word offset of item k in the buffer; off[n] = total words
+  u32 n;
+};
+__global__ void k_publish(PubDesc d, u32 *dst) {
+  const u32 i = threadIdx.x;
+  if (i >= d.off[d.n]) return;
+  u32 k = 0;
+  while (i >= d.off[k + 1]) ++k;
+  dst[i] = d.src[k][i - d.off[k]];
 }
 
-// several small device->host copies behind one stream synchronisation
 struct HostRead {
   void *host;
   const void *dev;
-  size_t n;
+  size_t n;  // a multiple of 4 bytes, the item 4-byte aligned
 };
 void read_many(chp_ctx *c, std::initializer_list<HostRead> items) {
-  size_t off = 0;
+  PubDesc d;
+  d.n = 0;
+  d.off[0] = 0;
   for (const HostRead &it : items) {
-    hip_check(c, hipMemcpyAsync((char *)c->pinned + off, it.dev, it.n, hipMemcpyDeviceToHost,
-                                c->stream),
-              "readback");
-    off += (it.n + 7) & ~(size_t)7;
+    if (d.n == PUB_MAX || (it.n & 3) || ((uintptr_t)it.dev & 3)) {
+      set_err(c, "%sinternal: unsupported readback");
+      throw Fail{CHP_EDEVICE};
+    }
+    d.src[d.n] = (const u32 *)it.dev;
+    d.off[d.n + 1] = d.off[d.n] + (u32)(((it.n + 7) & ~(size_t)7) / 4);
+    ++d.n;
   }
+  if (d.off[d.n] > 64 * 2) {
+    set_err(c, "%sinternal: readback too large");
+    throw Fail{CHP_EDEVICE};
+  }
+  CHP_LAUNCH(c, "publish", k_publish, 1, 128, 0, d, c->pinned_dev);
   hip_check(c, hipStreamSynchronize(c->stream), "stream synchronize");
-  off = 0;
-  for (const HostRead &it : items) {
-    memcpy(it.host, (const char *)c->pinned + off, it.n);
-    off += (it.n + 7) & ~(size_t)7;
-  }
+  u32 k = 0;
+  for (const HostRead &it : items) memcpy(it.host, (const char *)c->pinned + 4 * d.off[k++], it.n);
 }
+
+void read_back(chp_ctx *c, void *host, const void *dev, size_t n) { read_many(c, {{host, dev, n}}); }
 
 void d2d(chp_ctx *c, void *dst, const void *src, size_t n) {
   if (n) hip_check(c, hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, c->stream), "copy");
@@ -326,6 +344,39 @@ int guarded(chp_ctx *c, F &&f) {
 
 }  // namespace
 
+__global__ void k_fills(FillDesc d) {
+  const u64 g = (u64)blockIdx.x * blockDim.x + threadIdx.x, st = (u64)gridDim.x * blockDim.x;
+  for (u32 k = 0; k < d.cnt; ++k) {
+    if (d.wide[k])
+      for (u64 i = g; i < d.n[k]; i += st) ((u64 *)d.p[k])[i] = d.v[k];
+    else
+      for (u64 i = g; i < d.n[k]; i += st) ((u32 *)d.p[k])[i] = (u32)d.v[k];
+  }
+}
+
+void launch_fills(chp_ctx *c, std::initializer_list<FillItem> items) {
+  FillDesc d;
+  d.cnt = 0;
+  u64 most = 0;
+  for (const FillItem &it : items) {
+    if (!it.n) continue;
+    if (d.cnt == 8) {
+      set_err(c, "%sinternal: too many fills in one launch");
+      throw Fail{CHP_EDEVICE};
+    }
+    d.p[d.cnt] = it.p;
+    d.n[d.cnt] = it.n;
+    d.v[d.cnt] = it.v;
+    d.wide[d.cnt] = it.wide ? 1u : 0u;
+    most = it.n > most ? it.n : most;
+    ++d.cnt;
+  }
+  if (!d.cnt) return;
+  u32 g = grid_for(most, 256);
+  if (g > 4096) g = 4096;
+  CHP_LAUNCH(c, "fill", k_fills, g, 256, 0, d);
+}
+
 void launch_fill_u32(chp_ctx *c, u32 *p, u64 n, u32 v) {
   if (!n) return;
   u32 g = grid_for(n, 256);
@@ -405,7 +456,8 @@ int chp_create(chp_ctx **out, void *hip_stream, chp_alloc_fn alloc, chp_free_fn 
   if (hipGetDevice(&c->device) != hipSuccess ||
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, c->device) !=
           hipSuccess ||
-      hipHostMalloc((void **)&c->pinned, 64 * sizeof(u64), hipHostMallocDefault) != hipSuccess) {
+      hipHostMalloc((void **)&c->pinned, 64 * sizeof(u64), hipHostMallocMapped) != hipSuccess ||
+      hipHostGetDevicePointer((void **)&c->pinned_dev, c->pinned, 0) != hipSuccess) {
     (void)hipGetLastError();
     delete c;
     return CHP_EDEVICE;
@@ -545,7 +597,6 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
     *n_pairs_host = 0;
     if (N == 0) return;
     Scratch s(c);
-    clear_flags(c);
     u64 *t = s.get<u64>(E);
     const u32 np = terms_partials(E);
     u64 *partials = s.get<u64>(2ull * np);
@@ -578,22 +629,24 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
     nl.cnt = s.get<u32>(8);
     NodeRec *recs = s.get<NodeRec>(N);
     NodeRec *big = s.get<NodeRec>(N);
-    launch_fill_u32(c, nl.cnt, 8, 0);
-    launch_rate_classify(c, a, nl, recs, big);
-    launch_check(c, "rate classes");
     u32 *work = s.get<u32>(3);
-    launch_rate(c, a, nl, recs, big, work);
-    launch_check(c, "rate");
     MatchScratch ms;
     ms.bscore = s.get<u64>(N);
     ms.bid = s.get<u32>(N);
     ms.tk = s.get<uint8_t>(N);
     ms.p0 = ms.p1 = nullptr;
     ms.x0 = ms.x1 = nullptr;
-    launch_fill_u64(c, ms.bscore, N, 0);
-    launch_fill_u32(c, ms.bid, N, NONE32);
     u32 *npairs = s.get<u32>(1);
-    launch_fill_u32(c, npairs, 1, 0);
+    launch_fills(c, {{c->flags, 64, 0, false},
+                     {nl.cnt, 8, 0, false},
+                     {work, 3, 0, false},
+                     {ms.bscore, N, 0, true},
+                     {ms.bid, N, NONE32, false},
+                     {npairs, 1, 0, false}});
+    launch_rate_classify(c, a, nl, recs, big);
+    launch_check(c, "rate classes");
+    launch_rate(c, a, nl, recs, big, work);
+    launch_check(c, "rate");
     launch_match(c, N, target, score_fx, ms, match, npairs);
     launch_match_write(c, N, target, ms, match, npairs);
     launch_check(c, "match");
@@ -627,17 +680,23 @@ int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
     const bool merge_nb = build_neighbors && g->nb_off && g->nb;
     Scratch s(c);
     Owned own(c);
-    clear_flags(c);
     // -- representatives and hyperedge classes, then the first readback
     u32 *is_rep = s.get<u32>(N);
     i64 *rank = s.get<i64>((u64)N + 1);
     i64 *tmp = s.get<i64>(scan_tmp_words(N > E ? N : E));
-    launch_rep(c, N, match, is_rep);
-    scan_u32_to_i64(c, is_rep, rank, N, tmp);
     EdgeLists el;
     for (int k = 0; k < 3; ++k) el.list[k] = s.get<u32>(E);
     el.cnt = s.get<u32>(8);
-    launch_fill_u32(c, el.cnt, 8, 0);
+    EdgeLists il;
+    il.cnt = s.get<u32>(8);
+    NbLists nl;
+    nl.cnt = s.get<u32>(8);
+    launch_fills(c, {{c->flags, 64, 0, false},
+                     {el.cnt, 8, 0, false},
+                     {il.cnt, 8, 0, false},
+                     {nl.cnt, 8, 0, false}});
+    launch_rep(c, N, match, is_rep);
+    scan_u32_to_i64(c, is_rep, rank, N, tmp);
     launch_edge_classify(c, E, g->e_off, el);
     launch_check(c, "representatives");
     i64 nc;
@@ -673,10 +732,7 @@ int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
     scan_u32_to_i64(c, olen, cg.e_off, E, tmp);
     // -- coarse incidence classes: in'(c) = in(a) u in(b), out' = (out(a) u out(b)) \ in'
     u32 *ibound = s.get<u32>(Nc), *icnt = s.get<u32>(Nc);
-    EdgeLists il;
     for (int k = 0; k < 3; ++k) il.list[k] = s.get<u32>(Nc);
-    il.cnt = s.get<u32>(8);
-    launch_fill_u32(c, il.cnt, 8, 0);
     launch_cinc_classify(c, Nc, rep_of, match, g->n_off, g->n_nin, ibound, cg.n_nin, icnt, il);
     i64 *iooff = s.get<i64>((u64)Nc + 1);
     i64 *tmp2 = s.get<i64>(scan_tmp_words(Nc));
@@ -685,14 +741,10 @@ int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
     u32 *nbound = nullptr;
     i64 *nooff = nullptr;
     i64 *tmp3 = nullptr;
-    NbLists nl;
-    nl.cnt = nullptr;
     if (merge_nb) {
       nbound = s.get<u32>(Nc);
       for (int k = 0; k < 3; ++k) nl.list[k] = s.get<u32>(Nc);
       nl.list[3] = nl.list[4] = nullptr;
-      nl.cnt = s.get<u32>(8);
-      launch_fill_u32(c, nl.cnt, 8, 0);
       launch_nbm_classify(c, Nc, rep_of, match, g->nb_off, nbound, nl);
       nooff = s.get<i64>((u64)Nc + 1);
       tmp3 = s.get<i64>(scan_tmp_words(Nc));

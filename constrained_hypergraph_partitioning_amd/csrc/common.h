@@ -48,7 +48,8 @@ struct chp_ctx {
   u32 *flags = nullptr;    // device: [0] error flags, [1..63] small counters
   char *arena = nullptr;   // device scratch reused by every call
   size_t arena_cap = 0, arena_top = 0;
-  u64 *pinned = nullptr;   // host pinned staging (64 words)
+  u64 *pinned = nullptr;   // host pinned staging (64 words), mapped
+  u32 *pinned_dev = nullptr;  // its device address
   u64 *dsmall = nullptr;   // device small buffer (64 words)
   int timing = 0;
   std::vector<TimingRec> pending;

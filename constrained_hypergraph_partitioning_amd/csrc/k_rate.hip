@@ -700,7 +700,7 @@ __device__ __forceinline__ NodeRec rec_from_lds(const u32 *w) {
 // Work items: cnt[0] light nodes in light[]; records of cnt[1] heavy nodes
 // (one window of Heavy) at the front of recs[] and of cnt[3] huge ones (more
 // than one window of Big, one chunk of Heavy) at its back; cnt[2] big ones in
-// big[]; work[0..2] are zeroed work counters.
+// big[]; work[0..2] are zeroed work counters (the caller zeroes them).
 // k_rate_big rates the big nodes, a workgroup of Big per node; k_rate the
 // huge then the heavy ones, a workgroup of Heavy per node, HB at a time (one
 // counter access and one load of the records per batch), then the light
@@ -919,7 +919,6 @@ void launch_rate_classify(chp_ctx *c, const RateArgs &a, NbLists nl, NodeRec *re
 
 void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, const NodeRec *recs,
                  const NodeRec *big, u32 *work) {
-  launch_fill_u32(c, work, 3, 0);
   CHP_LAUNCH(c, "rate_big", k_rate_big, c->n_cu, Big::B, 0, a, big, (const u32 *)nl.cnt, work);
   CHP_LAUNCH(c, "rate", k_rate, c->n_cu * 4, RB, 0, a, (const u32 *)nl.list[0], recs,
              (const u32 *)nl.cnt, work);

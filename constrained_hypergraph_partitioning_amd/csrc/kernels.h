@@ -1,5 +1,7 @@
 // Host-side launchers of the kernels (one translation unit per step).
 #pragma once
+#include <initializer_list>
+
 #include "common.h"
 
 constexpr u32 LDS_CAP_U32 = 8192;   // u32 keys one workgroup sorts in LDS
@@ -157,4 +159,20 @@ void launch_eval_parts(chp_ctx *c, u32 k, const u64 *part_size, const u32 *part_
 
 // ---- small device fills (api.hip) -------------------------------------------
 void launch_fill_u32(chp_ctx *c, u32 *p, u64 n, u32 v);
+// Several fills in one launch (at most 8 arrays): n elements of u32 (or of
+// u64 when wide) set to v.
+struct FillItem {
+  void *p;
+  u64 n;
+  u64 v;
+  bool wide;
+};
+struct FillDesc {
+  void *p[8];
+  u64 n[8];
+  u64 v[8];
+  u32 wide[8];
+  u32 cnt;
+};
+void launch_fills(chp_ctx *c, std::initializer_list<FillItem> items);
 void launch_fill_u64(chp_ctx *c, u64 *p, u64 n, u64 v);
