@@ -75,6 +75,8 @@ def _load():
             "or_contract": [E, P, P, ctypes.POINTER(u32), ctypes.POINTER(P), ctypes.POINTER(P),
                             ctypes.POINTER(P), ctypes.POINTER(P)],
             "or_evaluate": [E, P, u32, u64, u32, P, P, P],
+            "or_flags": [E, P, P, P, P, P, u64, u32, P],
+            "or_purge": [u32, P, P, P, P, P, u32, P, P, P, ctypes.POINTER(P), ctypes.POINTER(u64)],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -265,6 +267,31 @@ def evaluate(g: Graph, rho, k, omega, delta):
     return ps, pi, summ
 
 
+def flags(g: Graph, omega, delta):
+    """O10: flag[nb_total] (uint8): 1 where (n, nb[i]) is not a valid pair."""
+    f = np.empty(g.nb.shape[0], np.uint8)
+    v = g.view()
+    _check(_load().or_flags(ctypes.byref(v), _p(g.n_off), _p(g.n_nin), _p(g.n_inc), _p(g.nb_off),
+                            _p(g.nb), omega, delta, _p(f)), "flags")
+    return f
+
+
+def purge(g: Graph, flag, match_arr, gamma, cg: Graph) -> Graph:
+    """O10: cg's neighbourhoods with every coarse neighbour that a member
+    flagged removed (cg.nb_off / cg.nb replaced)."""
+    nc = cg.n_nodes
+    off = np.empty(nc + 1, np.int64)
+    ptr = ctypes.c_void_p()
+    tot = ctypes.c_uint64()
+    _check(_load().or_purge(g.n_nodes, _p(g.nb_off), _p(g.nb), _p(np.ascontiguousarray(flag)),
+                            _p(np.ascontiguousarray(match_arr, np.uint32)),
+                            _p(np.ascontiguousarray(gamma, np.uint32)), nc, _p(cg.nb_off),
+                            _p(cg.nb), _p(off), ctypes.byref(ptr), ctypes.byref(tot)), "purge")
+    cg.nb_off = off
+    cg.nb = _take(ptr.value, tot.value, np.uint32)
+    return cg
+
+
 @dataclasses.dataclass
 class Level:
     target: np.ndarray
@@ -273,19 +300,27 @@ class Level:
     n_pairs: int
     gamma: np.ndarray | None
     coarse: Graph | None
+    flags: np.ndarray | None = None
 
 
-def level(g: Graph, omega, delta, noise_on=True, seed=0, build_neighbors=True) -> Level:
-    """One coarsening level: rate, match, contract."""
+def level(g: Graph, omega, delta, noise_on=True, seed=0, build_neighbors=True,
+          purge_invalid=False) -> Level:
+    """One coarsening level: rate, match, contract.  With purge_invalid the
+    neighbour flags of g are computed (Level.flags) and the coarse
+    neighbourhoods are purged of flagged neighbours (O10)."""
     target, score = rate(g, omega, delta, noise_on, seed)
     m, npairs = match(target, score)
+    fl = flags(g, omega, delta) if purge_invalid else None
     if npairs == 0:
-        return Level(target, score, m, 0, None, None)
+        return Level(target, score, m, 0, None, None, fl)
     gamma, cg = contract(g, m, build_neighbors)
-    return Level(target, score, m, npairs, gamma, cg)
+    if purge_invalid and build_neighbors:
+        purge(g, fl, m, gamma, cg)
+    return Level(target, score, m, npairs, gamma, cg, fl)
 
 
-def coarsen(g: Graph, omega, delta, target_nodes=0, max_levels=64, noise_on=True, seed=0):
+def coarsen(g: Graph, omega, delta, target_nodes=0, max_levels=64, noise_on=True, seed=0,
+            purge_invalid=False):
     """O9: the level loop of [P1] Sec. III.  Stops at the first of: fewer than
     target_nodes nodes; at most ceil(sum size / Omega) nodes (the lowest valid
     count); a level with no pair; max_levels levels.  Returns the list of Levels and the projection
@@ -297,7 +332,7 @@ def coarsen(g: Graph, omega, delta, target_nodes=0, max_levels=64, noise_on=True
     for _ in range(max_levels):
         if cur.n_nodes < target_nodes or cur.n_nodes <= floor_nodes:
             break
-        lv = level(cur, omega, delta, noise_on, seed)
+        lv = level(cur, omega, delta, noise_on, seed, purge_invalid=purge_invalid)
         levels.append(lv)
         if lv.n_pairs == 0:
             break

@@ -378,3 +378,82 @@ def test_validation_errors():
     assert err_code([([0], [1])], 3, sizes=[1, 5, 1], omega=4) == oracle.EINFEASIBLE
     assert err_code([([0], [1]), ([2], [1])], 3, delta=1) == oracle.EINFEASIBLE
     assert err_code([([0], [1, 2])], 3, delta=1) == 0
+
+
+# ---------------------------------------------------------------- purge (O10)
+@pytest.mark.parametrize("kw", tiny_cases()[::3], ids=lambda k: "s%d" % k["seed"])
+def test_flags_and_purge_vs_brute(kw):
+    """Flags are the invalid pairs by Python set union; the purged coarse
+    neighbourhood is the full one minus the coarse images of every flagged
+    neighbour of a member, keeps every valid coarse neighbour, and leaves the
+    level's own results unchanged."""
+    h = synth.tiny(**kw)
+    edges = brute.edges_of(h.e_off, h.e_nsrc, h.e_pins)
+    ins, _ = brute.incidence_sets(h.n_nodes, edges)
+    nbs = brute.neighbor_sets(h.n_nodes, edges)
+    for omega, delta in constraint_grid(h):
+        g = load(h, omega, delta)
+        fl = oracle.flags(g, omega, delta)
+        for n in range(h.n_nodes):
+            for i in range(int(g.nb_off[n]), int(g.nb_off[n + 1])):
+                assert bool(fl[i]) == (not brute.valid(n, int(g.nb[i]), h.n_size, ins, omega,
+                                                       delta))
+        full = oracle.level(load(h, omega, delta), omega, delta, False, kw["seed"])
+        lv = oracle.level(load(h, omega, delta), omega, delta, False, kw["seed"],
+                          purge_invalid=True)
+        for k in ("target", "score", "match"):
+            assert np.array_equal(getattr(full, k), getattr(lv, k))
+        if lv.n_pairs == 0:
+            continue
+        gamma, csize, cedges, _ = brute.contract(h.n_nodes, edges, h.e_w, h.n_size, lv.match)
+        nc = len(csize)
+        cins, _ = brute.incidence_sets(nc, cedges)
+        cnbs = brute.neighbor_sets(nc, cedges)
+        killed = [set() for _ in range(nc)]
+        for n in range(h.n_nodes):
+            for m in nbs[n]:
+                if not brute.valid(n, m, h.n_size, ins, omega, delta):
+                    killed[gamma[n]].add(gamma[m])
+        cg = lv.coarse
+        for c in range(nc):
+            got = cg.nb[cg.nb_off[c]:cg.nb_off[c + 1]].tolist()
+            assert got == sorted(cnbs[c] - killed[c])
+            for d in cnbs[c]:
+                if brute.valid(c, d, csize, cins, omega, delta):
+                    assert d in got
+                else:
+                    pass  # an invalid neighbour may stay (not flagged by a member)
+            for d in cnbs[c] - set(got):
+                assert not brute.valid(c, d, csize, cins, omega, delta)
+
+
+def test_purge_multilevel_same_coarsening():
+    """Over several levels with binding limits, purging leaves target, score,
+    match, gamma and the coarse hyperedges unchanged, and only shrinks the
+    neighbourhoods."""
+    for cfg, nn, dslack in ((2, 2500, 8), (3, 3000, 16), (4, 6000, 0)):
+        spec = synth.config(cfg, n_nodes=nn)
+        h = synth.generate(spec)
+        g0 = load(h, spec.omega, spec.delta)
+        indeg = int(g0.n_nin.max())
+        delta = indeg + dslack
+        la, _, _ = oracle.coarsen(load(h, spec.omega, delta), spec.omega, delta, 0, 8, True,
+                                  spec.seed)
+        lb, _, _ = oracle.coarsen(load(h, spec.omega, delta), spec.omega, delta, 0, 8, True,
+                                  spec.seed, purge_invalid=True)
+        assert len(la) == len(lb)
+        flagged = 0
+        for x, y in zip(la, lb):
+            for k in ("target", "score", "match", "gamma"):
+                a, b = getattr(x, k), getattr(y, k)
+                assert (a is None and b is None) or np.array_equal(a, b)
+            flagged += int(y.flags.sum())
+            if x.coarse is None:
+                continue
+            for k in ("e_off", "e_nsrc", "e_pins", "n_off", "n_inc", "n_size"):
+                assert np.array_equal(getattr(x.coarse, k), getattr(y.coarse, k))
+            for c in range(x.coarse.n_nodes):
+                fa = set(x.coarse.nb[x.coarse.nb_off[c]:x.coarse.nb_off[c + 1]].tolist())
+                fb = y.coarse.nb[y.coarse.nb_off[c]:y.coarse.nb_off[c + 1]].tolist()
+                assert set(fb) <= fa and fb == sorted(fb)
+        assert flagged > 0  # the limits bind, so something was purged
