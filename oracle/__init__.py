@@ -76,7 +76,7 @@ def _load():
                             ctypes.POINTER(P), ctypes.POINTER(P)],
             "or_evaluate": [E, P, u32, u64, u32, P, P, P],
             "or_flags": [E, P, P, P, P, P, u64, u32, P],
-            "or_purge": [u32, P, P, P, P, P, u32, P, P, P, ctypes.POINTER(P), ctypes.POINTER(u64)],
+            "or_purge": [u32, P, P, P, P, P, u32, P, ctypes.POINTER(P), ctypes.POINTER(u64)],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -277,16 +277,17 @@ def flags(g: Graph, omega, delta):
 
 
 def purge(g: Graph, flag, match_arr, gamma, cg: Graph) -> Graph:
-    """O10: cg's neighbourhoods with every coarse neighbour that a member
-    flagged removed (cg.nb_off / cg.nb replaced)."""
+    """O10: cg's neighbourhoods built from the members' current lists in g,
+    without every coarse neighbour that a member flagged (cg.nb_off / cg.nb
+    replaced)."""
     nc = cg.n_nodes
     off = np.empty(nc + 1, np.int64)
     ptr = ctypes.c_void_p()
     tot = ctypes.c_uint64()
     _check(_load().or_purge(g.n_nodes, _p(g.nb_off), _p(g.nb), _p(np.ascontiguousarray(flag)),
                             _p(np.ascontiguousarray(match_arr, np.uint32)),
-                            _p(np.ascontiguousarray(gamma, np.uint32)), nc, _p(cg.nb_off),
-                            _p(cg.nb), _p(off), ctypes.byref(ptr), ctypes.byref(tot)), "purge")
+                            _p(np.ascontiguousarray(gamma, np.uint32)), nc, _p(off),
+                            ctypes.byref(ptr), ctypes.byref(tot)), "purge")
     cg.nb_off = off
     cg.nb = _take(ptr.value, tot.value, np.uint32)
     return cg

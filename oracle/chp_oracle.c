@@ -543,20 +543,22 @@ int or_contract(const or_edges *g, const uint32_t *match, uint32_t *gamma, uint3
 
 /* ------------------------------------------------------------------------ */
 /* O10: invalid-neighbour flags and the purge of coarse neighbourhoods       */
-/* ([P1] Sec. V-C, third mechanism).                                         */
+/* ([P1] Sec. V-C, third mechanism; Sec. V-B: neighbourhoods are updated in  */
+/* place from level to level).                                              */
 /*  flag[i] for entry i of N(n) (i in nb_off[n]..nb_off[n+1]) is 1 iff the   */
 /*  pair (n, nb[i]) is not valid by Eq. 6: size(n)+size(m) > Omega or        */
 /*  |in(n) u in(m)| > Delta, the union counted by merging the two sorted     */
 /*  inbound lists.                                                           */
-/*  Reading: every invalid neighbour is flagged (the rating judges them all) */
-/*  and a flag marks every occurrence of the same coarse neighbour, so for   */
-/*  c = gamma(a) = gamma(b):                                                 */
+/*  Reading: every invalid neighbour is flagged (the rating judges them all), */
+/*  a flag marks every occurrence of the same coarse neighbour, and purged   */
+/*  neighbours stay purged: the coarse lists are built from the members'     */
+/*  current (purged) lists.  For c = gamma(a) = gamma(b):                    */
 /*    N'(c) = {gamma(m) : m in N(a) u N(b)} \ {c}                            */
-/*            \ {gamma(m) : m flagged in N(a) or in N(b)}.                   */
-/*  This drops only invalid pairs: size and inbound set of a cluster contain  */
-/*  those of each member, so an invalid (a, m) stays invalid for             */
-/*  (c, gamma(m)).  or_purge filters the full coarse lists (cnb_off, cnb, as */
-/*  O3 builds them on G') into malloc'd arrays.                              */
+/*            \ {gamma(m) : m flagged in N(a) or in N(b)},                   */
+/*  which on the first level equals the definition of N' on G' minus the    */
+/*  flagged images.  Only invalid pairs are dropped: size and inbound set of */
+/*  a cluster contain those of each member, so an invalid (a, m) stays       */
+/*  invalid for (c, gamma(m)).  or_purge writes malloc'd lists.              */
 /* ------------------------------------------------------------------------ */
 int or_flags(const or_edges *g, const int64_t *n_off, const uint32_t *n_nin, const uint32_t *n_inc,
              const int64_t *nb_off, const uint32_t *nb, uint64_t omega, uint32_t delta,
@@ -576,33 +578,40 @@ int or_flags(const or_edges *g, const int64_t *n_off, const uint32_t *n_nin, con
 }
 
 int or_purge(uint32_t N, const int64_t *nb_off, const uint32_t *nb, const uint8_t *flag,
-             const uint32_t *match, const uint32_t *gamma, uint32_t nc, const int64_t *cnb_off,
-             const uint32_t *cnb, int64_t *pnb_off, uint32_t **pnb_out, uint64_t *pnb_total) {
-  /* killed[c]: the coarse ids killed for c, as a list per coarse node */
+             const uint32_t *match, const uint32_t *gamma, uint32_t nc, int64_t *pnb_off,
+             uint32_t **pnb_out, uint64_t *pnb_total) {
   uint32_t *rep_of = (uint32_t *)malloc(sizeof(uint32_t) * (nc ? nc : 1));
-  uint32_t *kill = (uint32_t *)malloc(sizeof(uint32_t) * (N ? N : 1));
-  uint32_t *out = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(cnb_off[nc] ? cnb_off[nc] : 1));
-  if (!rep_of || !kill || !out) {
-    free(rep_of), free(kill), free(out);
+  /* a cluster's entries: at most |N(a)| + |N(b)| <= 2 (N - 1) */
+  uint32_t *val = (uint32_t *)malloc(sizeof(uint32_t) * (2 * (size_t)N + 1));
+  uint32_t *kill = (uint32_t *)malloc(sizeof(uint32_t) * (2 * (size_t)N + 1));
+  uint32_t *out = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)(nb_off[N] ? nb_off[N] : 1));
+  if (!rep_of || !val || !kill || !out) {
+    free(rep_of), free(val), free(kill), free(out);
     return OR_ENOMEM;
   }
   for (uint32_t n = 0; n < N; ++n)
     if (match[n] >= n) rep_of[gamma[n]] = n;
   pnb_off[0] = 0;
   for (uint32_t c = 0; c < nc; ++c) {
-    uint32_t a = rep_of[c], b = match[a], nk = 0;
+    uint32_t a = rep_of[c], b = match[a], nv = 0, nk = 0;
     for (int k = 0; k < (b != a ? 2 : 1); ++k) {
       uint32_t x = k == 0 ? a : b;
-      for (int64_t i = nb_off[x]; i < nb_off[x + 1]; ++i)
+      for (int64_t i = nb_off[x]; i < nb_off[x + 1]; ++i) {
+        val[nv++] = gamma[nb[i]];
         if (flag[i]) kill[nk++] = gamma[nb[i]];
+      }
     }
+    qsort(val, nv, sizeof(uint32_t), cmp_u32);
     qsort(kill, nk, sizeof(uint32_t), cmp_u32);
     int64_t o = pnb_off[c];
-    for (int64_t i = cnb_off[c]; i < cnb_off[c + 1]; ++i)
-      if (!sorted_has(kill, nk, cnb[i])) out[o++] = cnb[i];
+    for (uint32_t i = 0; i < nv; ++i) {
+      if (i > 0 && val[i] == val[i - 1]) continue;
+      if (val[i] == c || sorted_has(kill, nk, val[i])) continue;
+      out[o++] = val[i];
+    }
     pnb_off[c + 1] = o;
   }
-  free(rep_of), free(kill);
+  free(rep_of), free(val), free(kill);
   *pnb_out = out;
   *pnb_total = (uint64_t)pnb_off[nc];
   return OR_OK;

@@ -452,8 +452,16 @@ def test_purge_multilevel_same_coarsening():
                 continue
             for k in ("e_off", "e_nsrc", "e_pins", "n_off", "n_inc", "n_size"):
                 assert np.array_equal(getattr(x.coarse, k), getattr(y.coarse, k))
+            # every pair dropped from a purged list is invalid on the coarse
+            # graph (flags of the full lists, themselves pinned above)
+            ff = oracle.flags(x.coarse, spec.omega, delta)
             for c in range(x.coarse.n_nodes):
-                fa = set(x.coarse.nb[x.coarse.nb_off[c]:x.coarse.nb_off[c + 1]].tolist())
+                lo, hi = int(x.coarse.nb_off[c]), int(x.coarse.nb_off[c + 1])
+                fa = x.coarse.nb[lo:hi].tolist()
                 fb = y.coarse.nb[y.coarse.nb_off[c]:y.coarse.nb_off[c + 1]].tolist()
-                assert set(fb) <= fa and fb == sorted(fb)
+                assert set(fb) <= set(fa) and fb == sorted(fb)
+                kept = set(fb)
+                for i, d in enumerate(fa):
+                    if d not in kept:
+                        assert ff[lo + i] == 1
         assert flagged > 0  # the limits bind, so something was purged
