@@ -94,9 +94,10 @@ def load_library(path: str = LIB_PATH):
                                         ctypes.POINTER(HGraphC)]
     lib.chp_build_incidence.restype = I
     lib.chp_rate_and_match.argtypes = [P, ctypes.POINTER(HGraphC), ctypes.POINTER(Params), P, P,
-                                       P, ctypes.POINTER(ctypes.c_uint32)]
+                                       P, ctypes.POINTER(ctypes.c_uint32), P]
     lib.chp_rate_and_match.restype = I
-    lib.chp_contract.argtypes = [P, ctypes.POINTER(HGraphC), P, P, I, ctypes.POINTER(HGraphC)]
+    lib.chp_contract.argtypes = [P, ctypes.POINTER(HGraphC), P, P, I, ctypes.POINTER(HGraphC),
+                                 P]
     lib.chp_contract.restype = I
     lib.chp_evaluate_partition.argtypes = [P, ctypes.POINTER(HGraphC), P, ctypes.c_uint32,
                                            ctypes.POINTER(Params), P, P,
@@ -279,7 +280,10 @@ class Context:
                     "build_incidence")
         return HGraph(self, g)
 
-    def rate_and_match(self, g: HGraph, omega, delta, noise_on=True, seed=0, out=None):
+    def rate_and_match(self, g: HGraph, omega, delta, noise_on=True, seed=0, out=None,
+                       flags=None):
+        """target, score, match, n_pairs; with flags (a uint8 tensor of
+        g.nb_total entries) the invalid-neighbour flags are written too."""
         N = g.n_nodes
         if out is None:
             out = (torch.empty(N, dtype=torch.int32, device=self.device),
@@ -290,16 +294,26 @@ class Context:
         npairs = ctypes.c_uint32()
         self._check(self.lib.chp_rate_and_match(self.h, ctypes.byref(g.c), ctypes.byref(prm),
                                                 _ptr(target), _ptr(score), _ptr(match),
-                                                ctypes.byref(npairs)), "rate_and_match")
+                                                ctypes.byref(npairs),
+                                                _ptr(flags) if flags is not None else None),
+                    "rate_and_match")
         return target, score, match, int(npairs.value)
 
-    def contract(self, g: HGraph, match, neighbors=True, gamma=None):
+    def new_flags(self, g: HGraph):
+        """A uint8 device tensor for g's invalid-neighbour flags."""
+        return torch.empty(max(g.nb_total, 1), dtype=torch.uint8, device=self.device)
+
+    def contract(self, g: HGraph, match, neighbors=True, gamma=None, flags=None):
+        """gamma and the coarse graph; with flags (from rate_and_match on g)
+        the coarse neighbourhoods are purged of flagged neighbours."""
         N = g.n_nodes
         if gamma is None:
             gamma = torch.empty(N, dtype=torch.int32, device=self.device)
         cg = HGraphC()
         self._check(self.lib.chp_contract(self.h, ctypes.byref(g.c), _ptr(match), _ptr(gamma),
-                                          1 if neighbors else 0, ctypes.byref(cg)), "contract")
+                                          1 if neighbors else 0, ctypes.byref(cg),
+                                          _ptr(flags) if flags is not None else None),
+                    "contract")
         return gamma, HGraph(self, cg)
 
     def evaluate_partition(self, g: HGraph, rho, k, omega, delta):

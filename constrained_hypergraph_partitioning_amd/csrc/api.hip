@@ -583,7 +583,7 @@ int chp_build_incidence(chp_ctx *c, const chp_edges *in, const chp_params *prm,
 }
 
 int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u32 *target,
-                       u64 *score_fx, u32 *match, u32 *n_pairs_host) {
+                       u64 *score_fx, u32 *match, u32 *n_pairs_host, uint8_t *nb_invalid) {
   return guarded(c, [&] {
     if (!g || !prm || !n_pairs_host || (g->n_nodes && (!target || !score_fx || !match))) {
       set_err(c, "%snull argument");
@@ -614,6 +614,7 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
     a.n_size = g->n_size;
     a.nb_off = g->nb_off;
     a.nb = g->nb;
+    a.flag = nb_invalid;
     a.cur = s.get<u32>(2 * g->n_pins);
     a.capinfo = capinfo;
     a.omega = prm->omega;
@@ -669,7 +670,7 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
 }
 
 int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
-                 int build_neighbors, chp_hgraph *coarse) {
+                 int build_neighbors, chp_hgraph *coarse, const uint8_t *nb_invalid) {
   return guarded(c, [&] {
     if (!g || !coarse || (g->n_nodes && (!match || !gamma))) {
       set_err(c, "%snull argument");
@@ -678,6 +679,11 @@ int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
     const u32 N = g->n_nodes, E = g->n_edges;
     const u64 P = g->n_pins;
     const bool merge_nb = build_neighbors && g->nb_off && g->nb;
+    const uint8_t *purge = merge_nb ? nb_invalid : nullptr;
+    if (purge && N >= 0x7FFFFFFFu) {
+      set_err(c, "%sneighbour purge needs fewer than 2^31 - 1 nodes");
+      throw Fail{CHP_EINVAL};
+    }
     Scratch s(c);
     Owned own(c);
     // -- representatives and hyperedge classes, then the first readback
@@ -792,7 +798,8 @@ int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
       u32 *nobuf = s.get<u32>((u64)ntot);
       u32 *ncount = s.get<u32>(Nc);
       launch_fill_u32(c, ncount, Nc, 0);
-      launch_nbm_build(c, g->nb_off, g->nb, gamma, match, rep_of, nooff, nobuf, ncount, nl, hn);
+      launch_nbm_build(c, g->nb_off, g->nb, purge, gamma, match, rep_of, nooff, nobuf, ncount, nl,
+                       hn);
       scan_u32_to_i64(c, ncount, cg.nb_off, Nc, tmp3);
       launch_check(c, "coarse neighbours");
       i64 total;

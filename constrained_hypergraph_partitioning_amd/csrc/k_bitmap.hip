@@ -137,6 +137,33 @@ __device__ u32 bitmap_distinct(BitmapSmem &S, u32 mn, u32 mx, u32 skip, u32 *out
   return cnt;
 }
 
+// The same over keys value << 1 | flag: a value is kept iff none of its
+// copies is flagged (its bit is set by every copy, then cleared by the
+// flagged ones).
+template <typename G>
+__device__ u32 bitmap_distinct_unflagged(BitmapSmem &S, u32 mn, u32 mx, u32 skip, u32 *out,
+                                         G for_keys) {
+  u32 cnt = 0;
+  if (mn > mx) return 0;
+  for (u64 lo = mn; lo <= mx; lo += (u64)BMW * 32) {
+    const u64 hi = (lo + (u64)BMW * 32 - 1) < mx ? (lo + (u64)BMW * 32 - 1) : mx;
+    const u32 nw = (u32)((hi - lo) / 32 + 1);
+    const u32 span = nw * 32, l0 = (u32)lo;
+    for_keys([&](u32 k) {
+      const u32 v = k >> 1, d = v - l0;
+      if (v != skip && d < span) atomicOr(&S.bm[d >> 5], 1u << (d & 31));
+    });
+    __syncthreads();
+    for_keys([&](u32 k) {
+      const u32 d = (k >> 1) - l0;
+      if ((k & 1) && d < span) atomicAnd(&S.bm[d >> 5], ~(1u << (d & 31)));
+    });
+    __syncthreads();
+    cnt += bitmap_emit(S.bm, nw, l0, out + cnt, S.red);
+  }
+  return cnt;
+}
+
 // Level 0: N(n) = distinct pins of I(n) other than n.  W_n = bound[n] + |I(n)|.
 __global__ __launch_bounds__(BB) void k_nb_bitmap(const i64 *e_off, const u32 *pins,
                                                   const i64 *n_off, const u32 *n_inc,
@@ -198,11 +225,13 @@ __global__ __launch_bounds__(BB) void k_nb_bitmap(const i64 *e_off, const u32 *p
   }
 }
 
-// Coarse level: N'(c) = distinct gamma(N(a) u N(b)) other than c.
+// Coarse level: N'(c) = distinct gamma(N(a) u N(b)) other than c; with the
+// invalid-neighbour flags fl, also without the images of flagged entries.
 __global__ __launch_bounds__(BB) void k_nbm_bitmap(const i64 *nb_off, const u32 *nb,
-                                                   const u32 *gamma, const u32 *match,
-                                                   const u32 *rep_of, const i64 *ooff, u32 *obuf,
-                                                   u32 *count, const u32 *list, const u32 *cnt) {
+                                                   const uint8_t *fl, const u32 *gamma,
+                                                   const u32 *match, const u32 *rep_of,
+                                                   const i64 *ooff, u32 *obuf, u32 *count,
+                                                   const u32 *list, const u32 *cnt) {
   __shared__ BitmapSmem S;
   for (u32 i = threadIdx.x; i < BMW; i += BB) S.bm[i] = 0;
   __syncthreads();
@@ -220,10 +249,17 @@ __global__ __launch_bounds__(BB) void k_nbm_bitmap(const i64 *nb_off, const u32 
     }
     const u32 m = ka + kb;
     const bool staged = m <= STG;
+    // a key is gamma, or gamma << 1 | flag with flags
+    auto key_at = [&](u32 i) {
+      const i64 j = i < ka ? a0 + i : b0 + (i - ka);
+      const u32 g = gamma[nb[j]];
+      return fl ? (g << 1) | (u32)fl[j] : g;
+    };
     u32 mn = NONE32, mx = 0;
     for (u32 i = threadIdx.x; i < m; i += BB) {
-      const u32 v = gamma[i < ka ? nb[a0 + i] : nb[b0 + (i - ka)]];
-      if (staged) S.stg[i] = v;
+      const u32 k = key_at(i);
+      if (staged) S.stg[i] = k;
+      const u32 v = fl ? k >> 1 : k;
       if (v != c) {
         mn = v < mn ? v : mn;
         mx = v > mx ? v : mx;
@@ -232,14 +268,22 @@ __global__ __launch_bounds__(BB) void k_nbm_bitmap(const i64 *nb_off, const u32 
     mn = wg_min_u32(mn, S.redx);
     mx = wg_max_u32(mx, S.redx);
     u32 k;
-    if (staged) {
+    if (fl) {
+      if (staged)
+        k = bitmap_distinct_unflagged(S, mn, mx, c, obuf + ooff[c], [&](auto f) {
+          for (u32 i = threadIdx.x; i < m; i += BB) f(S.stg[i]);
+        });
+      else
+        k = bitmap_distinct_unflagged(S, mn, mx, c, obuf + ooff[c], [&](auto f) {
+          for (u32 i = threadIdx.x; i < m; i += BB) f(key_at(i));
+        });
+    } else if (staged) {
       k = bitmap_distinct(S, mn, mx, c, obuf + ooff[c], [&](auto f) {
         for (u32 i = threadIdx.x; i < m; i += BB) f(S.stg[i]);
       });
     } else {
       k = bitmap_distinct(S, mn, mx, c, obuf + ooff[c], [&](auto f) {
-        for (u32 i = threadIdx.x; i < m; i += BB)
-          f(gamma[i < ka ? nb[a0 + i] : nb[b0 + (i - ka)]]);
+        for (u32 i = threadIdx.x; i < m; i += BB) f(key_at(i));
       });
     }
     if (threadIdx.x == 0) count[c] = k;
@@ -257,10 +301,10 @@ void launch_nb_bitmap(chp_ctx *c, const i64 *e_off, const u32 *pins, const i64 *
              BB, 0, e_off, pins, n_off, n_inc, bound, ooff, obuf, count, list, cnt);
 }
 
-void launch_nbm_bitmap(chp_ctx *c, const i64 *nb_off, const u32 *nb, const u32 *gamma,
-                       const u32 *match, const u32 *rep_of, const i64 *ooff, u32 *obuf,
-                       u32 *count, const u32 *list, const u32 *cnt, u32 host_count) {
+void launch_nbm_bitmap(chp_ctx *c, const i64 *nb_off, const u32 *nb, const uint8_t *fl,
+                       const u32 *gamma, const u32 *match, const u32 *rep_of, const i64 *ooff,
+                       u32 *obuf, u32 *count, const u32 *list, const u32 *cnt, u32 host_count) {
   if (!host_count) return;
   CHP_LAUNCH(c, "nbm_bitmap", k_nbm_bitmap, host_count < 2 * c->n_cu ? host_count : 2 * c->n_cu,
-             BB, 0, nb_off, nb, gamma, match, rep_of, ooff, obuf, count, list, cnt);
+             BB, 0, nb_off, nb, fl, gamma, match, rep_of, ooff, obuf, count, list, cnt);
 }

@@ -190,11 +190,15 @@ __global__ void k_nbm_classify(u32 Nc, const u32 *rep_of, const u32 *match, cons
   }
 }
 
-// bound <= 64: one wave, keys in registers
+// bound <= 64: one wave, keys in registers.  With flags (fl, the invalid-
+// neighbour flags of the fine lists) a key is gamma << 1 | flag: in a sorted
+// run of one coarse id the flagged copies come last, so the id is kept iff
+// the run's last key is unflagged.
 __global__ __launch_bounds__(256) void k_nbm_wave(const i64 *nb_off, const u32 *nb,
-                                                  const u32 *gamma, const u32 *match,
-                                                  const u32 *rep_of, const i64 *ooff, u32 *obuf,
-                                                  u32 *count, const u32 *list, const u32 *cnt) {
+                                                  const uint8_t *fl, const u32 *gamma,
+                                                  const u32 *match, const u32 *rep_of,
+                                                  const i64 *ooff, u32 *obuf, u32 *count,
+                                                  const u32 *list, const u32 *cnt) {
   const u32 total = *cnt;
   const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
   const u32 l = lane_id();
@@ -210,23 +214,38 @@ __global__ __launch_bounds__(256) void k_nbm_wave(const i64 *nb_off, const u32 *
       kb = (u32)(nb_off[b + 1] - b0);
     }
     u32 v = NONE32;
-    if (l < ka + kb) v = gamma[l < ka ? nb[a0 + l] : nb[b0 + (l - ka)]];
+    if (l < ka + kb) {
+      const i64 j = l < ka ? a0 + l : b0 + (l - ka);
+      v = gamma[nb[j]];
+      if (fl) v = (v << 1) | (u32)fl[j];
+    }
     v = wave_sort64(v);
-    const u32 prev = __shfl_up(v, 1, WAVE);
-    const bool keep = v != NONE32 && v != c && (l == 0 || prev != v);
+    bool keep;
+    u32 out;
+    if (!fl) {
+      const u32 prev = __shfl_up(v, 1, WAVE);
+      keep = v != NONE32 && v != c && (l == 0 || prev != v);
+      out = v;
+    } else {
+      const u32 next = __shfl_down(v, 1, WAVE);
+      const bool last = l == WAVE - 1 || (next >> 1) != (v >> 1);
+      keep = v != NONE32 && last && !(v & 1) && (v >> 1) != c;
+      out = v >> 1;
+    }
     const u64 mask = __ballot(keep);
     const u32 pos = (u32)__popcll(mask & ((1ull << l) - 1));
-    if (keep) obuf[ooff[c] + pos] = v;
+    if (keep) obuf[ooff[c] + pos] = out;
     if (l == 0) count[c] = (u32)__popcll(mask);
   }
 }
 
 // Split gamma(L) (L sorted, k ids) into the representatives' images, which
 // stay sorted (appended to R at *r), and the second members' images
-// (appended to Q at *q).
+// (appended to Q at *q).  With flags (F, L's flags) the images are keys
+// gamma << 1 | flag, in the same order.
 template <int BLOCK>
-__device__ void split_reps(const u32 *L, u32 k, const u32 *gamma, const u32 *match, u32 *R,
-                           u32 &r, u32 *Q, u32 &q, u32 *s_red) {
+__device__ void split_reps(const u32 *L, const uint8_t *F, u32 k, const u32 *gamma,
+                           const u32 *match, u32 *R, u32 &r, u32 *Q, u32 &q, u32 *s_red) {
   for (u32 base = 0; base < k; base += BLOCK) {
     const u32 i = base + threadIdx.x;
     const bool valid = i < k;
@@ -235,6 +254,7 @@ __device__ void split_reps(const u32 *L, u32 k, const u32 *gamma, const u32 *mat
     if (valid) {
       const u32 m = L[i];
       g = gamma[m];
+      if (F) g = (g << 1) | (u32)F[i];
       rep = match[m] >= m;
     }
     u32 tr, tq;
@@ -247,14 +267,38 @@ __device__ void split_reps(const u32 *L, u32 k, const u32 *gamma, const u32 *mat
   }
 }
 
+// The distinct coarse ids of the sorted keys src[0, m) (gamma << 1 | flag)
+// other than skip, an id kept iff the last key of its run is unflagged;
+// written to out in order, the count returned (all threads).
+template <int BLOCK>
+__device__ u32 unique_unflagged(const u32 *src, u32 m, u32 skip, u32 *out, u32 *s_red) {
+  u32 run = 0;
+  for (u32 c0 = 0; c0 < m; c0 += BLOCK) {
+    const u32 i = c0 + threadIdx.x;
+    bool keep = false;
+    u32 v = 0;
+    if (i < m) {
+      const u32 k = src[i];
+      v = k >> 1;
+      keep = k != NONE32 && !(k & 1) && v != skip && (i + 1 == m || (src[i + 1] >> 1) != v);
+    }
+    u32 tot;
+    const u32 off = wg_excl_scan<BLOCK>((u32)keep, s_red, &tot);
+    if (keep) out[run + off] = v;
+    run += tot;
+  }
+  return run;
+}
+
 // N'(c) by split, sort of the second members' images, and two merges.  X, Y
 // hold CAP ids each; Z holds the second members' images (sorted in place).
+// With flags the same on keys gamma << 1 | flag (see k_nbm_wave).
 template <int BLOCK, int CAP>
 __global__ __launch_bounds__(BLOCK) void k_nbm_merge(const i64 *nb_off, const u32 *nb,
-                                                     const u32 *gamma, const u32 *match,
-                                                     const u32 *rep_of, const i64 *ooff,
-                                                     u32 *obuf, u32 *count, const u32 *list,
-                                                     const u32 *cnt) {
+                                                     const uint8_t *fl, const u32 *gamma,
+                                                     const u32 *match, const u32 *rep_of,
+                                                     const i64 *ooff, u32 *obuf, u32 *count,
+                                                     const u32 *list, const u32 *cnt) {
   __shared__ u32 X[CAP], Y[CAP], Z[CAP];
   __shared__ u32 s_red[BLOCK / WAVE + 1];
   const u32 total = *cnt;
@@ -263,11 +307,12 @@ __global__ __launch_bounds__(BLOCK) void k_nbm_merge(const i64 *nb_off, const u3
     const u32 a = rep_of[c], b = match[a];
     u32 r1 = 0, r2 = 0, q = 0;
     const i64 a0 = nb_off[a];
-    split_reps<BLOCK>(nb + a0, (u32)(nb_off[a + 1] - a0), gamma, match, X, r1, Z, q, s_red);
+    split_reps<BLOCK>(nb + a0, fl ? fl + a0 : nullptr, (u32)(nb_off[a + 1] - a0), gamma, match,
+                      X, r1, Z, q, s_red);
     if (b != a) {
       const i64 b0 = nb_off[b];
-      split_reps<BLOCK>(nb + b0, (u32)(nb_off[b + 1] - b0), gamma, match, X + r1, r2, Z, q,
-                        s_red);
+      split_reps<BLOCK>(nb + b0, fl ? fl + b0 : nullptr, (u32)(nb_off[b + 1] - b0), gamma,
+                        match, X + r1, r2, Z, q, s_red);
     }
     if (q > 1) {
       const u32 p = next_pow2(q);
@@ -285,7 +330,8 @@ __global__ __launch_bounds__(BLOCK) void k_nbm_merge(const i64 *nb_off, const u3
     u32 *F = R == X ? Y : X;
     wg_merge<BLOCK>(R, r1 + r2, Z, q, F);
     __syncthreads();
-    const u32 k = unique_out<BLOCK>(F, r1 + r2 + q, c, obuf + ooff[c], s_red);
+    const u32 k = fl ? unique_unflagged<BLOCK>(F, r1 + r2 + q, c, obuf + ooff[c], s_red)
+                     : unique_out<BLOCK>(F, r1 + r2 + q, c, obuf + ooff[c], s_red);
     if (threadIdx.x == 0) count[c] = k;
     __syncthreads();
   }
@@ -335,17 +381,17 @@ void launch_nbm_classify(chp_ctx *c, u32 Nc, const u32 *rep_of, const u32 *match
              nb_off, bound, nl);
 }
 
-void launch_nbm_build(chp_ctx *c, const i64 *nb_off, const u32 *nb, const u32 *gamma,
-                      const u32 *match, const u32 *rep_of, const i64 *ooff, u32 *obuf,
-                      u32 *count, NbLists nl, const u32 *host_cnt) {
+void launch_nbm_build(chp_ctx *c, const i64 *nb_off, const u32 *nb, const uint8_t *fl,
+                      const u32 *gamma, const u32 *match, const u32 *rep_of, const i64 *ooff,
+                      u32 *obuf, u32 *count, NbLists nl, const u32 *host_cnt) {
   if (host_cnt[0])
-    CHP_LAUNCH(c, "nbm_wave", k_nbm_wave, waves_grid(host_cnt[0]), 256, 0, nb_off, nb, gamma,
+    CHP_LAUNCH(c, "nbm_wave", k_nbm_wave, waves_grid(host_cnt[0]), 256, 0, nb_off, nb, fl, gamma,
                match, rep_of, ooff, obuf, count, (const u32 *)nl.list[0],
                (const u32 *)nl.cnt + 0);
   if (host_cnt[1])
     CHP_LAUNCH(c, "nbm_merge", (k_nbm_merge<64, 1024>),
-               host_cnt[1] > 65536 ? 65536 : host_cnt[1], 64, 0, nb_off, nb, gamma, match, rep_of,
-               ooff, obuf, count, (const u32 *)nl.list[1], (const u32 *)nl.cnt + 1);
-  launch_nbm_bitmap(c, nb_off, nb, gamma, match, rep_of, ooff, obuf, count, nl.list[2],
+               host_cnt[1] > 65536 ? 65536 : host_cnt[1], 64, 0, nb_off, nb, fl, gamma, match,
+               rep_of, ooff, obuf, count, (const u32 *)nl.list[1], (const u32 *)nl.cnt + 1);
+  launch_nbm_bitmap(c, nb_off, nb, fl, gamma, match, rep_of, ooff, obuf, count, nl.list[2],
                     nl.cnt + 2, host_cnt[2]);
 }

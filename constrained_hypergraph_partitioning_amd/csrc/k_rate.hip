@@ -208,6 +208,7 @@ constexpr int RW = Heavy::W;
 constexpr u32 L_T = 512, L_SHIFT = 23;   // hash slots per wave, light path
 constexpr int L_ECH = 32;
 constexpr u32 IMAX = 8;  // pins per thread per round, at most
+constexpr u32 L_UNR = RATE_SMALL_CAP / WAVE;  // window ids per lane, light path
 constexpr u32 EMPTY = 0xFFFFFFFFu;
 constexpr u64 INB = 1ull << 63;  // term flag: destination run of an inbound hyperedge
 constexpr u64 BAD = 1ull << 63;  // bin flag: the pair breaks Omega
@@ -422,6 +423,31 @@ __device__ __forceinline__ bool bin_valid(const RateArgs &A, u32 nin, u64 v, u32
   return !(v & BAD) && (u64)nin + rem <= (u64)A.delta;
 }
 
+// Invalid-neighbour flags of a window ([HP] Sec. V-C): entry i of the
+// window nb[w0, w0 + cw) gets 1 when its bin breaks a limit.  Reads the bins
+// only; it must follow the window's last visit and precede the candidate
+// scan, whose barrier orders it before the bins are emptied.
+template <u32 LANES, u32 UNR>
+__device__ __forceinline__ void flag_window(const RateArgs &A, const u32 *key, const u64 *eta,
+                                            const u32 *rem, u32 mask, u32 shift, i64 w0, u32 cw,
+                                            u32 nin, u32 t) {
+  for (u32 b0 = 0; b0 < cw; b0 += LANES * UNR) {
+    u32 m[UNR];
+#pragma unroll
+    for (u32 k = 0; k < UNR; ++k) {  // branch-free: past the end reads the last id
+      const u32 i = b0 + t + k * LANES;
+      m[k] = A.nb[w0 + (i < cw ? i : cw - 1)];
+    }
+#pragma unroll
+    for (u32 k = 0; k < UNR; ++k) {
+      const u32 i = b0 + t + k * LANES;
+      if (i >= cw) continue;
+      const u32 sl = h_find(key, mask, shift, m[k]);
+      A.flag[w0 + i] = (sl != EMPTY && bin_valid(A, nin, eta[sl], rem[sl])) ? 0 : 1;
+    }
+  }
+}
+
 // A valid bin can win only if eta + cap reaches floor, the largest raw eta
 // of a valid bin (that bin's total is at least floor); the others are
 // skipped before their noise is computed.
@@ -570,6 +596,8 @@ __device__ void rate_heavy(const RateArgs &A, HeavySmem<C> &S, const NodeRec &h,
                      tot, n, tid);
       __syncthreads();
     }
+    if (A.flag) flag_window<C::B, C::UNR>(A, S.key, S.eta, S.rem, C::T - 1, C::SHIFT, nb0 + s0, cw,
+                                         nin, tid);
     u64 floor = 0;
     for (u32 i = tid; i < C::T; i += C::B) {
       const u64 v = S.eta[i];
@@ -660,6 +688,7 @@ __device__ void rate_light(const RateArgs &A, LightWave &S, u32 n, u64 cap, u64 
                      2 * ne, tot, n, l);
     wave_sync();
   }
+  if (A.flag) flag_window<WAVE, L_UNR>(A, S.key, S.eta, S.rem, L_T - 1, L_SHIFT, nb0, K, nin, l);
   u64 floor = 0;
   for (u32 i = l; i < L_T; i += WAVE) {
     const u64 v = S.eta[i];

@@ -84,6 +84,7 @@ struct RateArgs {
   const i64 *nb_off;
   const u32 *nb;
   u32 *cur;  // [2 * pins] window cursors of nodes whose hyperedges span several chunks
+  uint8_t *flag;  // [nb_total] invalid-neighbour flags to write, or null
   const u64 *capinfo;
   u64 omega;
   u32 delta;
@@ -135,7 +136,8 @@ void launch_cinc_compact(chp_ctx *c, u32 Nc, const u32 *rep_of, const u32 *match
                          const i64 *c_off, u32 *c_inc);
 void launch_nbm_classify(chp_ctx *c, u32 Nc, const u32 *rep_of, const u32 *match,
                          const i64 *nb_off, u32 *bound, NbLists nl);
-void launch_nbm_build(chp_ctx *c, const i64 *nb_off, const u32 *nb, const u32 *gamma,
+void launch_nbm_build(chp_ctx *c, const i64 *nb_off, const u32 *nb, const uint8_t *fl,
+                      const u32 *gamma,
                       const u32 *match, const u32 *rep_of, const i64 *ooff, u32 *obuf,
                       u32 *count, NbLists nl, const u32 *host_cnt);
 
@@ -143,7 +145,8 @@ void launch_nbm_build(chp_ctx *c, const i64 *nb_off, const u32 *nb, const u32 *g
 void launch_nb_bitmap(chp_ctx *c, const i64 *e_off, const u32 *pins, const i64 *n_off,
                       const u32 *n_inc, const u32 *bound, const i64 *ooff, u32 *obuf, u32 *count,
                       const u32 *list, const u32 *cnt, u32 host_count);
-void launch_nbm_bitmap(chp_ctx *c, const i64 *nb_off, const u32 *nb, const u32 *gamma,
+void launch_nbm_bitmap(chp_ctx *c, const i64 *nb_off, const u32 *nb, const uint8_t *fl,
+                       const u32 *gamma,
                        const u32 *match, const u32 *rep_of, const i64 *ooff, u32 *obuf,
                        u32 *count, const u32 *list, const u32 *cnt, u32 host_count);
 

@@ -148,11 +148,15 @@ int chp_build_incidence(chp_ctx *ctx, const chp_edges *in, const chp_params *prm
  *              iff the target is still free and n is its best proposer
  *              (highest score, smallest id on ties), resolved top-down.
  *  *n_pairs_host number of pairs.
+ *  nb_invalid[g->nb_total] (optional, NULL = not written): the invalid-
+ *              neighbour flags of [HP] Sec. V-C: byte i is 1 when the pair
+ *              (n, g->nb[i]) of N(n)'s entry i breaks either limit, else 0.
+ *              Handed to chp_contract they purge the coarse neighbourhoods.
  * Requires g->nb (build with neighbours).  Errors: EINVAL, EOVERFLOW,
  * ECYCLE.  Synchronises. */
 int chp_rate_and_match(chp_ctx *ctx, const chp_hgraph *g, const chp_params *prm,
                        uint32_t *target, uint64_t *score_fx, uint32_t *match,
-                       uint32_t *n_pairs_host);
+                       uint32_t *n_pairs_host, uint8_t *nb_invalid);
 
 /* contract ([HP] Sec. III and V-E; [IC] Sec. III-B4).
  *  gamma[N]   coarse id of every node: the rank of min(n, match(n)) among
@@ -161,12 +165,18 @@ int chp_rate_and_match(chp_ctx *ctx, const chp_hgraph *g, const chp_params *prm,
  *             coarse hyperedge per hyperedge, same id and weight, dst' =
  *             gamma(dst), src' = gamma(src) \ dst'; incidence rebuilt; N'
  *             rebuilt if build_neighbors != 0.
+ *  nb_invalid (optional, NULL = none): flags of g's neighbour entries as
+ *             written by chp_rate_and_match.  N'(c) then also drops
+ *             gamma(m) for every flagged entry m of N(a) or N(b) ([HP]
+ *             Sec. V-C: a flag marks every occurrence of that neighbour).
+ *             Only invalid pairs are dropped: an invalid (a, m) stays
+ *             invalid for (c, gamma(m)).  Needs n_nodes < 2^31 - 1.
  * match must be a symmetric involution (match[match[n]] == n), else EINVAL.
  * Synchronises to size its outputs; the last arrays of *coarse are written
  * in stream order (use them on the same stream, or synchronise before
  * reading them on the host). */
 int chp_contract(chp_ctx *ctx, const chp_hgraph *g, const uint32_t *match, uint32_t *gamma,
-                 int build_neighbors, chp_hgraph *coarse);
+                 int build_neighbors, chp_hgraph *coarse, const uint8_t *nb_invalid);
 
 /* evaluate_partition ([HP] Eq. 1, Eq. 16, Sec. II-B).
  *  rho[N] in [0,k).  part_size[k] = sum of sizes per part (uint64);

@@ -36,18 +36,26 @@ def assert_equal(got, want, what):
                                 got[bad[:5]].tolist(), want[bad[:5]].tolist()))
 
 
-def run_level_pair(chp, ctx, dg, og, omega, delta, noise_on, seed, neighbors=True, tag=""):
+def run_level_pair(chp, ctx, dg, og, omega, delta, noise_on, seed, neighbors=True, tag="",
+                   purge=False):
     """One level on both sides; compares target, score, match, pairs, gamma
-    and the coarse graph.  Returns (device coarse, oracle Level)."""
-    tgt, score, match, npairs = ctx.rate_and_match(dg, omega, delta, noise_on, seed)
-    lv = oracle.level(og, omega, delta, noise_on, seed, build_neighbors=neighbors)
+    and the coarse graph (with purge, also the invalid-neighbour flags, and
+    the coarse neighbourhoods purged).  Returns (device coarse, oracle
+    Level, device gamma)."""
+    flags = ctx.new_flags(dg) if purge else None
+    tgt, score, match, npairs = ctx.rate_and_match(dg, omega, delta, noise_on, seed, flags=flags)
+    lv = oracle.level(og, omega, delta, noise_on, seed, build_neighbors=neighbors,
+                      purge_invalid=purge)
     assert_equal(chp.to_host(tgt, np.uint32), lv.target, tag + " target")
     assert_equal(chp.to_host(score, np.uint64), lv.score, tag + " score")
     assert_equal(chp.to_host(match, np.uint32), lv.match, tag + " match")
+    if purge:
+        got = flags.cpu().numpy()[: og.nb.shape[0]]
+        assert_equal(got, lv.flags, tag + " flags")
     assert npairs == lv.n_pairs, tag + " pairs"
     if npairs == 0:
         return None, lv, None
-    gamma, cg = ctx.contract(dg, match, neighbors)
+    gamma, cg = ctx.contract(dg, match, neighbors, flags=flags)
     assert_equal(chp.to_host(gamma, np.uint32), lv.gamma, tag + " gamma")
     assert_graph_equal(cg, lv.coarse, tag + " coarse", neighbors)
     return cg, lv, gamma

@@ -43,7 +43,7 @@ def both(chp, ctx, h, omega, delta, neighbors=True):
 
 
 def multilevel(chp, ctx, h, omega, delta, noise_on, seed, max_levels, target_nodes=0,
-               eval_every=False, tag=""):
+               eval_every=False, tag="", purge=False):
     dg, og = both(chp, ctx, h, omega, delta)
     rho = np.arange(h.n_nodes, dtype=np.uint32)
     og0, dg0 = og, dg
@@ -53,7 +53,7 @@ def multilevel(chp, ctx, h, omega, delta, noise_on, seed, max_levels, target_nod
         if og.n_nodes < target_nodes or og.n_nodes <= floor_nodes:
             break
         cg, lv, gamma = run_level_pair(chp, ctx, dg, og, omega, delta, noise_on, seed,
-                                       tag="%s L%d" % (tag, lvl))
+                                       tag="%s L%d" % (tag, lvl), purge=purge)
         levels += 1
         if cg is None:
             break
@@ -100,6 +100,37 @@ def test_constraint_stress(chp, ctx, omega, dslack, noise_on):
     delta = int(indeg.max()) + dslack
     say("stress", omega, delta, noise_on)
     multilevel(chp, ctx, h, omega, delta, noise_on, 5, 12, tag="stress")
+
+
+@pytest.mark.parametrize("cfg,nn,levels,omega,dslack", [(1, None, 12, 4, 0), (1, None, 12, 6, 1),
+                                                        (2, 5000, 8, None, 0),
+                                                        (3, 5000, 6, None, 8),
+                                                        (4, 30000, 8, None, 2)])
+def test_purge_multilevel(chp, ctx, cfg, nn, levels, omega, dslack):
+    """Invalid-neighbour flags and purged coarse neighbourhoods over several
+    levels, Delta just above the largest in-degree so that the flags are
+    plentiful; every level's flags and coarse graph against the oracle."""
+    spec = synth.config(cfg, n_nodes=nn)
+    h = synth.generate(spec)
+    indeg = np.bincount(np.concatenate([h.e_pins[h.e_off[e] + h.e_nsrc[e]:h.e_off[e + 1]]
+                                        for e in range(h.n_edges)]), minlength=h.n_nodes)
+    delta = int(indeg.max()) + dslack
+    omega = spec.omega if omega is None else omega
+    say("purge", cfg, nn, omega, delta)
+    multilevel(chp, ctx, h, omega, delta, True, spec.seed, levels, tag="purge%d" % cfg,
+               purge=True)
+
+
+def test_purge_wide_neighbourhoods(chp, ctx):
+    """Coarse neighbourhoods above 1024 entries (the LDS bitmap path) and
+    between 64 and 1024 (the merge path), purged."""
+    spec = synth.custom(synth.UNIFORM, 5000, 5000, 40, 70, 8, 4, 40, 1 << 20, 9)
+    h = synth.generate(spec)
+    indeg = np.bincount(np.concatenate([h.e_pins[h.e_off[e] + h.e_nsrc[e]:h.e_off[e + 1]]
+                                        for e in range(h.n_edges)]), minlength=h.n_nodes)
+    delta = int(indeg.max()) + 30
+    say("purge wide", delta)
+    multilevel(chp, ctx, h, spec.omega, delta, True, 9, 3, tag="purge wide", purge=True)
 
 
 def test_tiny_graphs(chp, ctx):
