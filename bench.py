@@ -30,6 +30,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 RATE_KERNELS = ("rate_big", "rate")
+# Invalid neighbours are flagged by the rating and purged from the coarse
+# neighbourhoods (the pages' coarsening does this; --no-purge turns it off).
+PURGE = True
 RATE_SOURCE = os.path.join(ROOT, "constrained_hypergraph_partitioning_amd", "csrc", "k_rate.hip")
 COUNTERS_JSON = os.path.join(ROOT, "profiles", "rating_counters.json")
 COPY_REF_MIB = 256
@@ -47,6 +50,8 @@ def parse():
     p.add_argument("--copy-ref-mib", type=int, default=0,
                    help="run one plain device copy of this size first (a reference for "
                         "scaling hardware byte counters)")
+    p.add_argument("--no-purge", action="store_true",
+                   help="keep invalid neighbours in the coarse neighbourhoods")
     p.add_argument("--counters", metavar="DIR", default=None,
                    help="no run: summarise the rocprofv3 FETCH_SIZE and WRITE_SIZE passes "
                         "under DIR/fetch and DIR/write into " + COUNTERS_JSON)
@@ -125,11 +130,13 @@ def run_step(chp, ctx, dev_edges, spec, rho_buf):
             break
         if g.n_nodes <= floor_nodes:
             break
-        _, _, match, npairs = ctx.rate_and_match(g, spec.omega, spec.delta, True, spec.seed)
+        flags = ctx.new_flags(g) if PURGE else None
+        _, _, match, npairs = ctx.rate_and_match(g, spec.omega, spec.delta, True, spec.seed,
+                                                 flags=flags)
         levels.append((g.n_nodes, g.n_pins, npairs, g.nb_total))
         if npairs == 0:
             break
-        gamma, cg = ctx.contract(g, match, True)
+        gamma, cg = ctx.contract(g, match, True, flags=flags)
         rho = gamma.long() if rho is None else gamma.long()[rho]
         if g is not g0:
             g.free()
@@ -179,6 +186,8 @@ def main():
         import synth
         summarize_counters(args.counters, synth.config(args.workload, n_nodes=args.nodes).name)
         return
+    global PURGE
+    PURGE = not args.no_purge
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)

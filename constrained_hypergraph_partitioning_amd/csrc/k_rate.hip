@@ -97,15 +97,19 @@ __global__ __launch_bounds__(TB) void k_cap(u32 nparts, const u64 *partials, u32
 
 // ---------------------------------------------------------------------------
 // rating
-// Nodes by |N(n)| and |I(n)|: light (|N(n)| <= small_cap) are queued by id
-// in list[0]; the others with their record: heavy (<= heavy_cap) in recs[]
+// Nodes by |N(n)| and |I(n)|: light (|N(n)| <= small_cap and at most one
+// chunk of light_ech hyperedges, so that a wave's pin visits stay short) are
+// queued by id in list[0]; the others with their record: heavy (<= heavy_cap,
+// at most big_ech hyperedges: more pins are visited faster by the 1024
+// threads of the large-table kernel) in recs[]
 // from the front; huge (above big_cap, at most heavy_ech hyperedges) in
 // recs[] from the back; big (the rest) in big[].  A huge node takes several
 // windows of either table; with one chunk of hyperedges a window costs the
 // small table little, and four of its workgroups share a CU.  A node without
 // neighbours gets no candidate here.
 __global__ void k_rate_classify(RateArgs A, NbLists nl, NodeRec *recs, NodeRec *big,
-                                u32 small_cap, u32 heavy_cap, u32 big_cap, u32 heavy_ech) {
+                                u32 small_cap, u32 heavy_cap, u32 big_cap, u32 heavy_ech,
+                                u32 light_ech, u32 big_ech) {
   const u32 n = blockIdx.x * blockDim.x + threadIdx.x;
   u64 K = 0, deg = 0;
   if (n < A.N) {
@@ -116,11 +120,11 @@ __global__ void k_rate_classify(RateArgs A, NbLists nl, NodeRec *recs, NodeRec *
       A.score[n] = 0;
     }
   }
-  const int c = (n >= A.N || K == 0)          ? 4
-                : K <= small_cap              ? 0
-                : K <= heavy_cap              ? 1
-                : K > big_cap && deg <= heavy_ech ? 3
-                                              : 2;
+  const int c = (n >= A.N || K == 0)              ? 4
+                : K <= small_cap && deg <= light_ech  ? 0
+                : K <= heavy_cap && deg <= big_ech    ? 1
+                : K > big_cap && deg <= heavy_ech     ? 3
+                                                      : 2;
   const u32 s0 = wave_append(&nl.cnt[0], c == 0);
   if (c == 0) nl.list[0][s0] = n;
   const u32 s1 = wave_append(&nl.cnt[1], c == 1);
@@ -943,7 +947,7 @@ void launch_rate_classify(chp_ctx *c, const RateArgs &a, NbLists nl, NodeRec *re
                           NodeRec *big) {
   if (a.N == 0) return;
   CHP_LAUNCH(c, "rate_classify", k_rate_classify, grid_for(a.N, 256), 256, 0, a, nl, recs, big,
-             RATE_SMALL_CAP, Heavy::CAP, Big::CAP, (u32)Heavy::ECH);
+             RATE_SMALL_CAP, Heavy::CAP, Big::CAP, (u32)Heavy::ECH, (u32)L_ECH, (u32)Big::ECH);
 }
 
 void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, const NodeRec *recs,

@@ -115,8 +115,9 @@ def sampled_rate_and_nb(chp, og, dg, tgt, score, spec, rng, n_sample):
 
 
 def test_ring_100k_full_level(chp, ctx):
-    """The benchmark's workload at full size: level 0 and level 1 compared
-    array by array with the oracle, then the projected partition."""
+    """The benchmark's workload at full size, as the benchmark runs it (with
+    the purge): level 0 and level 1 compared array by array with the oracle
+    (flags included), then the projected partition."""
     spec = synth.config(2)
     say("ring 100k full")
     h = synth.generate(spec)
@@ -127,14 +128,17 @@ def test_ring_100k_full_level(chp, ctx):
     rho = np.arange(h.n_nodes, dtype=np.uint32)
     g0d, g0o = dg, og
     for lvl in range(2):
+        # as the benchmark runs it: invalid neighbours flagged and purged
+        flags = ctx.new_flags(dg)
         tgt, score, match, npairs = ctx.rate_and_match(dg, spec.omega, spec.delta, True,
-                                                       spec.seed)
-        lv = oracle.level(og, spec.omega, spec.delta, True, spec.seed)
+                                                       spec.seed, flags=flags)
+        lv = oracle.level(og, spec.omega, spec.delta, True, spec.seed, purge_invalid=True)
         assert_equal(chp.to_host(tgt, np.uint32), lv.target, "L%d target" % lvl)
         assert_equal(chp.to_host(score, np.uint64), lv.score, "L%d score" % lvl)
         assert_equal(chp.to_host(match, np.uint32), lv.match, "L%d match" % lvl)
+        assert_equal(flags.cpu().numpy()[: og.nb.shape[0]], lv.flags, "L%d flags" % lvl)
         assert npairs == lv.n_pairs
-        gamma, cg = ctx.contract(dg, match)
+        gamma, cg = ctx.contract(dg, match, flags=flags)
         assert_equal(chp.to_host(gamma, np.uint32), lv.gamma, "L%d gamma" % lvl)
         assert_graph_equal(cg, lv.coarse, "L%d coarse" % lvl)
         rho = lv.gamma[rho]
