@@ -30,7 +30,7 @@ _NAMES = {EINVAL: "EINVAL", ENOMEM: "ENOMEM", EOVERFLOW: "EOVERFLOW",
 
 EXPORTS = ["chp_create", "chp_destroy", "chp_last_error", "chp_build_incidence",
            "chp_rate_and_match", "chp_contract", "chp_evaluate_partition", "chp_hgraph_free",
-           "chp_set_timing", "chp_get_timings", "chp_reset_timings"]
+           "chp_set_timing", "chp_get_timings", "chp_reset_timings", "chp_set_batch_entries"]
 
 
 class ChpError(RuntimeError):
@@ -99,6 +99,8 @@ def load_library(path: str = LIB_PATH):
     lib.chp_contract.argtypes = [P, ctypes.POINTER(HGraphC), P, P, I, ctypes.POINTER(HGraphC),
                                  P]
     lib.chp_contract.restype = I
+    lib.chp_set_batch_entries.argtypes = [P, ctypes.c_uint64]
+    lib.chp_set_batch_entries.restype = I
     lib.chp_evaluate_partition.argtypes = [P, ctypes.POINTER(HGraphC), P, ctypes.c_uint32,
                                            ctypes.POINTER(Params), P, P,
                                            ctypes.POINTER(ctypes.c_uint64)]
@@ -325,6 +327,11 @@ class Context:
                                                     ctypes.byref(prm), _ptr(part_size),
                                                     _ptr(part_inb), summ), "evaluate_partition")
         return part_size[:k], part_inb[:k], np.array(list(summ), dtype=np.uint64)
+
+    def set_batch_entries(self, entries=0):
+        """Neighbour entries per rating batch for graphs without neighbours
+        (0 = the library default)."""
+        self._check(self.lib.chp_set_batch_entries(self.h, int(entries)), "set_batch_entries")
 
     # ---- timing ---------------------------------------------------------------
     def set_timing(self, on=True):

@@ -7,6 +7,8 @@
 #include <cstring>
 #include <initializer_list>
 
+#include <vector>
+
 #include "kernels.h"
 
 // ---------------------------------------------------------------------------
@@ -289,7 +291,7 @@ void build_neighbors_core(chp_ctx *c, Scratch &s, Owned &own, chp_hgraph *g) {
   nl.list[3] = nl.list[4] = nullptr;
   nl.cnt = s.get<u32>(8);
   launch_fill_u32(c, nl.cnt, 8, 0);
-  launch_nb_classify(c, N, g->e_off, g->n_off, g->n_inc, bound, nl);
+  launch_nb_classify(c, 0, N, g->e_off, g->n_off, g->n_inc, bound, nl);
   i64 *ooff = s.get<i64>((u64)N + 1);
   i64 *tmp = s.get<i64>(scan_tmp_words(N));
   scan_u32_to_i64(c, bound, ooff, N, tmp);
@@ -486,6 +488,12 @@ void chp_destroy(chp_ctx *c) {
 
 const char *chp_last_error(const chp_ctx *c) { return c ? c->err.c_str() : "null context"; }
 
+int chp_set_batch_entries(chp_ctx *c, uint64_t entries) {
+  if (!c) return CHP_EINVAL;
+  c->batch_entries = entries;
+  return CHP_OK;
+}
+
 int chp_set_timing(chp_ctx *c, int on) {
   if (!c) return CHP_EINVAL;
   c->timing = on ? 1 : 0;
@@ -582,6 +590,85 @@ int chp_build_incidence(chp_ctx *c, const chp_edges *in, const chp_params *prm,
   });
 }
 
+namespace {
+
+// Neighbour entries one batch may hold (oversize buffer and packed lists).
+constexpr u64 BATCH_ENTRIES = 3ull << 30;
+
+// Rating of a graph built without neighbourhoods (too many to hold at once;
+// [HP] Sec. VII-C runs the coarsening kernels over batches of nodes, keeping
+// only a few nodes' neighbourhoods in device memory).  Node ranges [lo, hi)
+// whose level-0 neighbour bounds fit the batch limit (c->batch_entries, or
+// BATCH_ENTRIES) get their N(n) built as by chp_build_incidence, into batch
+// buffers, and are rated from them; the rating reads nb_off through a
+// pointer shifted by lo.
+void rate_batched(chp_ctx *c, Scratch &s, const chp_hgraph *g, const RateArgs &a, NbLists nl,
+                  NodeRec *recs, NodeRec *big, u32 *work) {
+  const u32 N = g->n_nodes;
+  u32 *bound = s.get<u32>(N);
+  NbLists bl;
+  bl.list[0] = s.get<u32>(N);
+  bl.list[1] = s.get<u32>(N);
+  bl.list[2] = bl.list[3] = bl.list[4] = nullptr;
+  bl.cnt = s.get<u32>(8);
+  launch_fill_u32(c, bl.cnt, 8, 0);
+  launch_nb_classify(c, 0, N, g->e_off, g->n_off, g->n_inc, bound, bl);
+  i64 *ooff = s.get<i64>((u64)N + 1);
+  i64 *tmp = s.get<i64>(scan_tmp_words(N));
+  scan_u32_to_i64(c, bound, ooff, N, tmp);
+  launch_check(c, "neighbour bounds");
+  u32 hc[8];
+  read_many(c, {{hc, bl.cnt, sizeof hc}});
+  if (hc[7]) {
+    set_err(c, "%sa node's incident pins exceed 2^32");
+    throw Fail{CHP_EOVERFLOW};
+  }
+  std::vector<i64> hoff((size_t)N + 1);
+  hip_check(c, hipMemcpyAsync(hoff.data(), ooff, sizeof(i64) * ((size_t)N + 1),
+                              hipMemcpyDeviceToHost, c->stream),
+            "readback");
+  hip_check(c, hipStreamSynchronize(c->stream), "stream synchronize");
+  u64 most = 0;
+  for (u32 n = 0; n < N; ++n) {
+    const u64 b = (u64)(hoff[n + 1] - hoff[n]);
+    most = b > most ? b : most;
+  }
+  const u64 limit = c->batch_entries ? c->batch_entries : BATCH_ENTRIES;
+  const u64 budget = most > limit ? most : limit;
+  const u64 room = (u64)hoff[N] < budget ? (u64)hoff[N] : budget;
+  u32 *obuf = s.get<u32>(room ? room : 1);
+  u32 *nbb = s.get<u32>(room ? room : 1);
+  u32 *count = s.get<u32>(N);
+  i64 *nboff = s.get<i64>((u64)N + 1);
+  for (u32 lo = 0; lo < N;) {
+    u32 hi = lo + 1;
+    while (hi < N && (u64)(hoff[hi + 1] - hoff[lo]) <= budget) ++hi;
+    const u32 cnt = hi - lo;
+    // N(n) of the batch (bounds recomputed for the range, same values)
+    launch_fills(c, {{bl.cnt, 8, 0, false}, {count + lo, cnt, 0, false}});
+    launch_nb_classify(c, lo, cnt, g->e_off, g->n_off, g->n_inc, bound, bl);
+    launch_check(c, "batch neighbour classes");
+    read_many(c, {{hc, bl.cnt, sizeof hc}});
+    u32 *obs = obuf - hoff[lo];  // indexed by the whole graph's oversize offsets
+    launch_nb_build(c, N, g->e_off, g->e_pins, g->n_off, g->n_inc, bound, ooff, obs, count, bl,
+                    hc);
+    scan_u32_to_i64(c, count + lo, nboff, cnt, tmp);
+    launch_nb_compact(c, cnt, ooff + lo, obs, nboff, nbb);
+    launch_check(c, "batch neighbours");
+    // rate the batch
+    RateArgs ab = a;
+    ab.nb_off = nboff - lo;
+    ab.nb = nbb;
+    launch_fills(c, {{nl.cnt, 8, 0, false}, {work, 3, 0, false}});
+    launch_rate_classify(c, ab, lo, hi, nl, recs, big);
+    launch_rate(c, ab, nl, recs, cnt, big, work);
+    launch_check(c, "batch rate");
+    lo = hi;
+  }
+}
+
+}  // namespace
+
 int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u32 *target,
                        u64 *score_fx, u32 *match, u32 *n_pairs_host, uint8_t *nb_invalid) {
   return guarded(c, [&] {
@@ -590,8 +677,9 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
       throw Fail{CHP_EINVAL};
     }
     const u32 N = g->n_nodes, E = g->n_edges;
-    if (N && (!g->nb_off || !g->nb)) {
-      set_err(c, "%sthe graph has no neighbourhoods (build them first)");
+    const bool batched = N && (!g->nb_off || !g->nb);
+    if (batched && nb_invalid) {
+      set_err(c, "%sinvalid-neighbour flags need the graph's neighbourhoods");
       throw Fail{CHP_EINVAL};
     }
     *n_pairs_host = 0;
@@ -644,10 +732,14 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
                      {ms.bscore, N, 0, true},
                      {ms.bid, N, NONE32, false},
                      {npairs, 1, 0, false}});
-    launch_rate_classify(c, a, nl, recs, big);
-    launch_check(c, "rate classes");
-    launch_rate(c, a, nl, recs, big, work);
-    launch_check(c, "rate");
+    if (!batched) {
+      launch_rate_classify(c, a, 0, N, nl, recs, big);
+      launch_check(c, "rate classes");
+      launch_rate(c, a, nl, recs, N, big, work);
+      launch_check(c, "rate");
+    } else {
+      rate_batched(c, s, g, a, nl, recs, big, work);
+    }
     launch_match(c, N, target, score_fx, ms, match, npairs);
     launch_match_write(c, N, target, ms, match, npairs);
     launch_check(c, "match");

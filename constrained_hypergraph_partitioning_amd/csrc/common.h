@@ -50,6 +50,7 @@ struct chp_ctx {
   size_t arena_cap = 0, arena_top = 0;
   u64 *pinned = nullptr;   // host pinned staging (64 words), mapped
   u32 *pinned_dev = nullptr;  // its device address
+  u64 batch_entries = 0;      // neighbour entries per rating batch (0 = default)
   u64 *dsmall = nullptr;   // device small buffer (64 words)
   int timing = 0;
   std::vector<TimingRec> pending;

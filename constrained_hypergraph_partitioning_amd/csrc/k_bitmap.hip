@@ -19,6 +19,8 @@ constexpr int BB = 256;       // threads per workgroup
 constexpr u32 BMW = 8192;     // bitmap words (262,144 ids per window)
 constexpr u32 STG = 8192;     // values staged in LDS (larger sets are read twice)
 
+constexpr u32 NHB = 64;       // buckets of the id histogram (level 0, wide spans)
+
 struct BitmapSmem {
   u32 bm[BMW];
   u32 stg[STG];
@@ -26,6 +28,8 @@ struct BitmapSmem {
   u32 pre[BB + 1];
   u32 red[BB / WAVE + 1];
   u32 redx[BB / WAVE + 1];
+  u32 hist[NHB];
+  u32 lcnt, wlo;
 };
 
 // Emit the set bits of bm[0, nw) as ids lo + bit, ascending, to out; the
@@ -164,11 +168,89 @@ __device__ u32 bitmap_distinct_unflagged(BitmapSmem &S, u32 mn, u32 mx, u32 skip
   return cnt;
 }
 
+// Level 0 for a node whose values are not staged and whose id span exceeds
+// one window: the histogram (NHB buckets of 2^hshift ids) picks the window
+// with the most values; those set bits, the others go to a list in LDS
+// (stg), which is sorted and made unique.  Output: list values below the
+// window, the window's ids, list values above it.  Returns false (bitmap
+// clean) if the list overflows, the caller then takes every window in turn.
+__device__ bool hybrid_distinct(BitmapSmem &S, const i64 *e_off, const u32 *pins,
+                                const u32 *n_inc, i64 a, i64 b, u32 n, u32 mn, u32 mx,
+                                u32 hshift, u32 *out, u32 *count_out) {
+  const u32 span = BMW * 32;
+  const u32 wb = (span >> hshift) > 0 ? (span >> hshift) : 1;  // buckets per window
+  if (threadIdx.x == 0) {
+    u32 best = 0, bs = 0;
+    for (u32 s0 = 0; s0 < NHB; ++s0) {
+      u32 t = 0;
+      for (u32 k = s0; k < s0 + wb && k < NHB; ++k) t += S.hist[k];
+      if (t > best) best = t, bs = s0;
+    }
+    const u64 lo = (u64)bs << hshift;
+    S.wlo = lo < mn ? mn : (u32)lo;
+    S.lcnt = 0;
+  }
+  __syncthreads();
+  const u32 wlo = S.wlo;
+  const u32 whi = (u64)wlo + span - 1 < mx ? wlo + span - 1 : mx;
+  for_each_pin(e_off, pins, n_inc, a, b, S, [&](u32 v) {
+    if (v == n) return;
+    if (v >= wlo && v <= whi) {
+      const u32 d = v - wlo;
+      atomicOr(&S.bm[d >> 5], 1u << (d & 31));
+    } else {
+      const u32 i = atomicAdd(&S.lcnt, 1u);
+      if (i < STG) S.stg[i] = v;
+    }
+  });
+  __syncthreads();
+  const u32 lc = S.lcnt;
+  const u32 nw = (whi - wlo) / 32 + 1;
+  if (lc > STG) {
+    for (u32 i = threadIdx.x; i < nw; i += BB) S.bm[i] = 0;
+    __syncthreads();
+    return false;
+  }
+  // sort the list, then its distinct values get their ranks
+  if (lc > 1) {
+    const u32 p = next_pow2(lc);
+    for (u32 i = lc + threadIdx.x; i < p; i += BB) S.stg[i] = NONE32;
+    __syncthreads();
+    lds_bitonic<BB>(S.stg, p);
+  }
+  __syncthreads();
+  u32 below = 0;
+  for (u32 i = threadIdx.x; i < lc; i += BB) {
+    const u32 v = S.stg[i];
+    if (v < wlo && (i == 0 || S.stg[i - 1] != v)) ++below;
+  }
+  below = wg_sum<BB>(below, S.red);
+  const u32 nbm = bitmap_emit(S.bm, nw, wlo, out + below, S.red);
+  u32 run = 0;
+  for (u32 c0 = 0; c0 < lc; c0 += BB) {
+    const u32 i = c0 + threadIdx.x;
+    u32 v = 0;
+    bool keep = false;
+    if (i < lc) {
+      v = S.stg[i];
+      keep = i == 0 || S.stg[i - 1] != v;
+    }
+    u32 tot;
+    const u32 off = wg_excl_scan<BB>((u32)keep, S.red, &tot);
+    if (keep) out[run + off + (v < wlo ? 0 : nbm)] = v;
+    run += tot;
+  }
+  if (threadIdx.x == 0) *count_out = nbm + run;
+  __syncthreads();
+  return true;
+}
+
 // Level 0: N(n) = distinct pins of I(n) other than n.  W_n = bound[n] + |I(n)|.
 __global__ __launch_bounds__(BB) void k_nb_bitmap(const i64 *e_off, const u32 *pins,
                                                   const i64 *n_off, const u32 *n_inc,
                                                   const u32 *bound, const i64 *ooff, u32 *obuf,
-                                                  u32 *count, const u32 *list, const u32 *cnt) {
+                                                  u32 *count, const u32 *list, const u32 *cnt,
+                                                  u32 hshift) {
   __shared__ BitmapSmem S;
   for (u32 i = threadIdx.x; i < BMW; i += BB) S.bm[i] = 0;
   __syncthreads();
@@ -178,8 +260,11 @@ __global__ __launch_bounds__(BB) void k_nb_bitmap(const i64 *e_off, const u32 *p
     const i64 a = n_off[n], b = n_off[n + 1];
     const u64 W = (u64)bound[n] + (u64)(b - a);
     const bool staged = W <= STG;
+    if (!staged)
+      for (u32 i = threadIdx.x; i < NHB; i += BB) S.hist[i] = 0;
+    __syncthreads();
     u32 mn = NONE32, mx = 0;
-    // stage (when small) and take the span
+    // stage (when small) and take the span; unstaged, also the histogram
     u32 base = 0;
     for (i64 c0 = a; c0 < b; c0 += BB) {
       const u32 ne = (u32)((b - c0) < BB ? (b - c0) : BB);
@@ -202,6 +287,7 @@ __global__ __launch_bounds__(BB) void k_nb_bitmap(const i64 *e_off, const u32 *p
         if (v != n) {
           mn = v < mn ? v : mn;
           mx = v > mx ? v : mx;
+          if (!staged) atomicAdd(&S.hist[v >> hshift], 1u);
         }
       }
       base += tot;
@@ -209,18 +295,20 @@ __global__ __launch_bounds__(BB) void k_nb_bitmap(const i64 *e_off, const u32 *p
     }
     mn = wg_min_u32(mn, S.redx);
     mx = wg_max_u32(mx, S.redx);
-    u32 c;
     if (staged) {
       const u32 m = (u32)W;
-      c = bitmap_distinct(S, mn, mx, n, obuf + ooff[n], [&](auto f) {
+      const u32 c = bitmap_distinct(S, mn, mx, n, obuf + ooff[n], [&](auto f) {
         for (u32 i = threadIdx.x; i < m; i += BB) f(S.stg[i]);
       });
-    } else {
-      c = bitmap_distinct(S, mn, mx, n, obuf + ooff[n], [&](auto f) {
+      if (threadIdx.x == 0) count[n] = c;
+    } else if (mn > mx || (u64)(mx - mn) < (u64)BMW * 32 ||
+               !hybrid_distinct(S, e_off, pins, n_inc, a, b, n, mn, mx, hshift, obuf + ooff[n],
+                                count + n)) {
+      const u32 c = bitmap_distinct(S, mn, mx, n, obuf + ooff[n], [&](auto f) {
         for_each_pin(e_off, pins, n_inc, a, b, S, f);
       });
+      if (threadIdx.x == 0) count[n] = c;
     }
-    if (threadIdx.x == 0) count[n] = c;
     __syncthreads();
   }
 }
@@ -293,12 +381,14 @@ __global__ __launch_bounds__(BB) void k_nbm_bitmap(const i64 *nb_off, const u32 
 
 }  // namespace
 
-void launch_nb_bitmap(chp_ctx *c, const i64 *e_off, const u32 *pins, const i64 *n_off,
+void launch_nb_bitmap(chp_ctx *c, u32 N, const i64 *e_off, const u32 *pins, const i64 *n_off,
                       const u32 *n_inc, const u32 *bound, const i64 *ooff, u32 *obuf, u32 *count,
                       const u32 *list, const u32 *cnt, u32 host_count) {
   if (!host_count) return;
+  u32 hshift = 0;  // NHB buckets of 2^hshift ids cover [0, N)
+  while (((u64)(N ? N - 1 : 0) >> hshift) >= NHB) ++hshift;
   CHP_LAUNCH(c, "nb_bitmap", k_nb_bitmap, host_count < 2 * c->n_cu ? host_count : 2 * c->n_cu,
-             BB, 0, e_off, pins, n_off, n_inc, bound, ooff, obuf, count, list, cnt);
+             BB, 0, e_off, pins, n_off, n_inc, bound, ooff, obuf, count, list, cnt, hshift);
 }
 
 void launch_nbm_bitmap(chp_ctx *c, const i64 *nb_off, const u32 *nb, const uint8_t *fl,

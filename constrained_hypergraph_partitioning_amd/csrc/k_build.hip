@@ -228,11 +228,13 @@ __global__ void k_node_runs(u32 N, const i64 *n_off, const u32 *n_nin, RunLists 
 // ---------------------------------------------------------------------------
 // neighbourhoods: W_n = sum_{e in I(n)} |e| decides the class; the oversize
 // bound of |N(n)| is W_n - |I(n)| (n is a pin of each of its hyperedges).
-__global__ void k_nb_classify(u32 N, const i64 *e_off, const i64 *n_off, const u32 *n_inc,
-                              u32 *bound, NbLists nl) {
-  const u32 n = blockIdx.x * blockDim.x + threadIdx.x;
+// Nodes lo .. lo + N - 1.
+__global__ void k_nb_classify(u32 lo, u32 N, const i64 *e_off, const i64 *n_off,
+                              const u32 *n_inc, u32 *bound, NbLists nl) {
+  const u32 t = blockIdx.x * blockDim.x + threadIdx.x;
+  const u32 n = lo + t;
   u64 w = 0, bnd = 0;
-  if (n < N) {
+  if (t < N) {
     const i64 a = n_off[n], b = n_off[n + 1];
     for (i64 j = a; j < b; ++j) {
       const u32 e = n_inc[j];
@@ -367,11 +369,11 @@ void launch_node_runs(chp_ctx *c, u32 N, const i64 *n_off, const u32 *n_nin, Run
   CHP_LAUNCH(c, "node_runs", k_node_runs, grid_for(N, 256), 256, 0, N, n_off, n_nin, rl);
 }
 
-void launch_nb_classify(chp_ctx *c, u32 N, const i64 *e_off, const i64 *n_off, const u32 *n_inc,
-                        u32 *bound, NbLists nl) {
+void launch_nb_classify(chp_ctx *c, u32 lo, u32 N, const i64 *e_off, const i64 *n_off,
+                        const u32 *n_inc, u32 *bound, NbLists nl) {
   if (N == 0) return;
-  CHP_LAUNCH(c, "nb_classify", k_nb_classify, grid_for(N, 256), 256, 0, N, e_off, n_off, n_inc,
-             bound, nl);
+  CHP_LAUNCH(c, "nb_classify", k_nb_classify, grid_for(N, 256), 256, 0, lo, N, e_off, n_off,
+             n_inc, bound, nl);
 }
 
 void launch_nb_build(chp_ctx *c, u32 N, const i64 *e_off, const u32 *pins, const i64 *n_off,
@@ -380,7 +382,7 @@ void launch_nb_build(chp_ctx *c, u32 N, const i64 *e_off, const u32 *pins, const
   if (host_cnt[0])
     CHP_LAUNCH(c, "nb_wave", k_nb_wave, waves_grid(host_cnt[0]), 256, 0, e_off, pins, n_off,
                n_inc, ooff, obuf, count, nl.list[0], nl.cnt + 0);
-  launch_nb_bitmap(c, e_off, pins, n_off, n_inc, bound, ooff, obuf, count, nl.list[1],
+  launch_nb_bitmap(c, N, e_off, pins, n_off, n_inc, bound, ooff, obuf, count, nl.list[1],
                    nl.cnt + 1, host_cnt[1]);
 }
 

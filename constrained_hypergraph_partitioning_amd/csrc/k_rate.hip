@@ -107,12 +107,13 @@ __global__ __launch_bounds__(TB) void k_cap(u32 nparts, const u64 *partials, u32
 // windows of either table; with one chunk of hyperedges a window costs the
 // small table little, and four of its workgroups share a CU.  A node without
 // neighbours gets no candidate here.
-__global__ void k_rate_classify(RateArgs A, NbLists nl, NodeRec *recs, NodeRec *big,
-                                u32 small_cap, u32 heavy_cap, u32 big_cap, u32 heavy_ech,
-                                u32 light_ech, u32 big_ech) {
-  const u32 n = blockIdx.x * blockDim.x + threadIdx.x;
+// (nodes lo .. hi - 1; recs must hold hi - lo records)
+__global__ void k_rate_classify(RateArgs A, u32 lo, u32 hi, NbLists nl, NodeRec *recs,
+                                NodeRec *big, u32 small_cap, u32 heavy_cap, u32 big_cap,
+                                u32 heavy_ech, u32 light_ech, u32 big_ech) {
+  const u32 n = lo + blockIdx.x * blockDim.x + threadIdx.x;
   u64 K = 0, deg = 0;
-  if (n < A.N) {
+  if (n < hi) {
     K = (u64)(A.nb_off[n + 1] - A.nb_off[n]);
     deg = (u64)(A.n_off[n + 1] - A.n_off[n]);
     if (K == 0) {
@@ -120,7 +121,7 @@ __global__ void k_rate_classify(RateArgs A, NbLists nl, NodeRec *recs, NodeRec *
       A.score[n] = 0;
     }
   }
-  const int c = (n >= A.N || K == 0)              ? 4
+  const int c = (n >= hi || K == 0)               ? 4
                 : K <= small_cap && deg <= light_ech  ? 0
                 : K <= heavy_cap && deg <= big_ech    ? 1
                 : K > big_cap && deg <= heavy_ech     ? 3
@@ -142,7 +143,7 @@ __global__ void k_rate_classify(RateArgs A, NbLists nl, NodeRec *recs, NodeRec *
     r.pad0 = r.pad1 = r.pad2 = 0;
     if (c == 1) recs[s1] = r;
     else if (c == 2) big[s2] = r;
-    else recs[A.N - 1 - s3] = r;
+    else recs[hi - lo - 1 - s3] = r;
   }
 }
 
@@ -731,7 +732,7 @@ __device__ __forceinline__ NodeRec rec_from_lds(const u32 *w) {
 }
 
 // Work items: cnt[0] light nodes in light[]; records of cnt[1] heavy nodes
-// (one window of Heavy) at the front of recs[] and of cnt[3] huge ones (more
+// (one window of Heavy) at the front of recs[nrec] and of cnt[3] huge ones (more
 // than one window of Big, one chunk of Heavy) at its back; cnt[2] big ones in
 // big[]; work[0..2] are zeroed work counters (the caller zeroes them).
 // k_rate_big rates the big nodes, a workgroup of Big per node; k_rate the
@@ -782,7 +783,7 @@ __global__ __launch_bounds__(1024) void k_rate_big(RateArgs A, const NodeRec *bi
 }
 
 __global__ __launch_bounds__(RB) void k_rate(RateArgs A, const u32 *light, const NodeRec *recs,
-                                             const u32 *cnt, u32 *work) {
+                                             u32 nrec, const u32 *cnt, u32 *work) {
   __shared__ RateSmem sm;
   __shared__ u32 s_item;
   __shared__ u32 s_rec[HB * 12];
@@ -790,7 +791,7 @@ __global__ __launch_bounds__(RB) void k_rate(RateArgs A, const u32 *light, const
   const u64 cap = A.capinfo[0], dmod = A.capinfo[1], magic = A.capinfo[2];
   heavy_loop<Heavy, HB>(
       A, sm.h, &s_item, s_rec,
-      [&](u32 j) { return j < nhuge ? recs + (A.N - 1 - j) : recs + (j - nhuge); },
+      [&](u32 j) { return j < nhuge ? recs + (nrec - 1 - j) : recs + (j - nhuge); },
       cnt[1] + nhuge, &work[0], cap, dmod, magic);
   LightWave &S = sm.l[wave_id()];
   for (u32 i = lane_id(); i < L_T; i += WAVE) {
@@ -943,17 +944,18 @@ void launch_terms(chp_ctx *c, u32 E, const i64 *e_off, const u32 *e_w, u64 *t, u
   CHP_LAUNCH(c, "cap", k_cap, 1, TB, 0, E ? nparts : 0u, (const u64 *)partials, E, capinfo);
 }
 
-void launch_rate_classify(chp_ctx *c, const RateArgs &a, NbLists nl, NodeRec *recs,
-                          NodeRec *big) {
-  if (a.N == 0) return;
-  CHP_LAUNCH(c, "rate_classify", k_rate_classify, grid_for(a.N, 256), 256, 0, a, nl, recs, big,
+void launch_rate_classify(chp_ctx *c, const RateArgs &a, u32 lo, u32 hi, NbLists nl,
+                          NodeRec *recs, NodeRec *big) {
+  if (hi <= lo) return;
+  CHP_LAUNCH(c, "rate_classify", k_rate_classify, grid_for(hi - lo, 256), 256, 0, a, lo, hi, nl,
+             recs, big,
              RATE_SMALL_CAP, Heavy::CAP, Big::CAP, (u32)Heavy::ECH, (u32)L_ECH, (u32)Big::ECH);
 }
 
-void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, const NodeRec *recs,
+void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, const NodeRec *recs, u32 nrec,
                  const NodeRec *big, u32 *work) {
   CHP_LAUNCH(c, "rate_big", k_rate_big, c->n_cu, Big::B, 0, a, big, (const u32 *)nl.cnt, work);
-  CHP_LAUNCH(c, "rate", k_rate, c->n_cu * 4, RB, 0, a, (const u32 *)nl.list[0], recs,
+  CHP_LAUNCH(c, "rate", k_rate, c->n_cu * 4, RB, 0, a, (const u32 *)nl.list[0], recs, nrec,
              (const u32 *)nl.cnt, work);
 }
 

@@ -49,7 +49,8 @@ void launch_node_feas(chp_ctx *c, u32 N, const u32 *indeg, const u32 *outdeg, co
 void launch_scatter(chp_ctx *c, u32 E, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
                     const i64 *n_off, const u32 *n_nin, u32 *cur_in, u32 *cur_out, u32 *n_inc);
 void launch_node_runs(chp_ctx *c, u32 N, const i64 *n_off, const u32 *n_nin, RunLists rl);
-void launch_nb_classify(chp_ctx *c, u32 N, const i64 *e_off, const i64 *n_off, const u32 *n_inc,
+// nodes lo .. lo + N - 1
+void launch_nb_classify(chp_ctx *c, u32 lo, u32 N, const i64 *e_off, const i64 *n_off, const u32 *n_inc,
                         u32 *bound, NbLists nl);
 void launch_nb_build(chp_ctx *c, u32 N, const i64 *e_off, const u32 *pins, const i64 *n_off,
                      const u32 *n_inc, const u32 *bound, const i64 *ooff, u32 *obuf, u32 *count,
@@ -94,9 +95,10 @@ struct RateArgs {
   u64 *score;
   u32 *flags;
 };
-void launch_rate_classify(chp_ctx *c, const RateArgs &a, NbLists nl, NodeRec *recs,
-                          NodeRec *big);
-void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, const NodeRec *recs,
+// nodes lo .. hi - 1
+void launch_rate_classify(chp_ctx *c, const RateArgs &a, u32 lo, u32 hi, NbLists nl,
+                          NodeRec *recs, NodeRec *big);
+void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, const NodeRec *recs, u32 nrec,
                  const NodeRec *big, u32 *work);
 
 struct MatchScratch {
@@ -142,7 +144,7 @@ void launch_nbm_build(chp_ctx *c, const i64 *nb_off, const u32 *nb, const uint8_
                       u32 *count, NbLists nl, const u32 *host_cnt);
 
 // ---- k_bitmap.hip : sorted distinct lists through an LDS bitmap ------------
-void launch_nb_bitmap(chp_ctx *c, const i64 *e_off, const u32 *pins, const i64 *n_off,
+void launch_nb_bitmap(chp_ctx *c, u32 N, const i64 *e_off, const u32 *pins, const i64 *n_off,
                       const u32 *n_inc, const u32 *bound, const i64 *ooff, u32 *obuf, u32 *count,
                       const u32 *list, const u32 *cnt, u32 host_count);
 void launch_nbm_bitmap(chp_ctx *c, const i64 *nb_off, const u32 *nb, const uint8_t *fl,

@@ -152,8 +152,11 @@ int chp_build_incidence(chp_ctx *ctx, const chp_edges *in, const chp_params *prm
  *              neighbour flags of [HP] Sec. V-C: byte i is 1 when the pair
  *              (n, g->nb[i]) of N(n)'s entry i breaks either limit, else 0.
  *              Handed to chp_contract they purge the coarse neighbourhoods.
- * Requires g->nb (build with neighbours).  Errors: EINVAL, EOVERFLOW,
- * ECYCLE.  Synchronises. */
+ * Without g->nb (a graph built without neighbours) the neighbourhoods are
+ * built here, for batches of consecutive nodes whose neighbour lists fit the
+ * batch limit (chp_set_batch_entries), each batch rated before the next is
+ * built ([HP] Sec. VII-C); nb_invalid must then be NULL.  Errors: EINVAL,
+ * EOVERFLOW, ECYCLE.  Synchronises. */
 int chp_rate_and_match(chp_ctx *ctx, const chp_hgraph *g, const chp_params *prm,
                        uint32_t *target, uint64_t *score_fx, uint32_t *match,
                        uint32_t *n_pairs_host, uint8_t *nb_invalid);
@@ -188,6 +191,12 @@ int chp_contract(chp_ctx *ctx, const chp_hgraph *g, const uint32_t *match, uint3
 int chp_evaluate_partition(chp_ctx *ctx, const chp_hgraph *g, const uint32_t *rho, uint32_t k,
                            const chp_params *prm, uint64_t *part_size, uint32_t *part_inb,
                            uint64_t summary_host[8]);
+
+/* Neighbour entries one rating batch may hold when chp_rate_and_match
+ * builds the neighbourhoods itself (a graph without nb); 0 restores the
+ * default (3 * 2^30, 12 GiB for the lists plus as much scratch).  A node
+ * whose own list is larger gets a batch of its own. */
+int chp_set_batch_entries(chp_ctx *ctx, uint64_t entries);
 
 /* Release every array of g (allocated by this library) and zero *g. */
 void chp_hgraph_free(chp_ctx *ctx, chp_hgraph *g);

@@ -176,3 +176,60 @@ def test_large_workloads_sampled(chp, ctx, cfg, sample):
     k = 1000
     rho = synth.uniform_u32(cfg, 11, h.n_nodes, k)
     eval_pair(chp, ctx, dg, og, rho, k, spec.omega, spec.delta, spec.name + " eval")
+
+
+def test_block_4m_single_level(chp, ctx):
+    """The 4M-node SNN workload (about 1e9 pins) at full size, as its
+    description asks: one level of rate, match and contract.  Its
+    neighbourhoods (about 1.9e11 entries) cannot be held at once, so the
+    graph is built without them and the rating builds them batch by batch.
+    Sampled nodes' target and score against the oracle; the matching and the
+    coarse graph through the properties that hold at any size."""
+    spec = synth.config(5)
+    say("block 4m")
+    h = synth.generate(spec)
+    dg = ctx.build_incidence(*chp.upload_edges(h), spec.omega, spec.delta, False)
+    say("block 4m built", dg.n_pins)
+    tgt, score, match, npairs = ctx.rate_and_match(dg, spec.omega, spec.delta, True, spec.seed)
+    say("block 4m rated", npairs)
+    tgt_h, score_h = chp.to_host(tgt, np.uint32), chp.to_host(score, np.uint64)
+    match_h = chp.to_host(match, np.uint32)
+    og = oracle.build_incidence(h.e_off, h.e_nsrc, h.e_pins, h.e_w, h.n_size, spec.omega,
+                                spec.delta, build_neighbors=False)
+    say("block 4m oracle built")
+    for name in ("e_off", "e_nsrc", "n_off", "n_nin"):
+        got, want = dg.host(name), getattr(og, name)
+        assert np.array_equal(got.view(want.dtype), want), name
+    rng = np.random.default_rng(5)
+    tc = oracle.terms(og)
+    for n in rng.choice(h.n_nodes, 24, replace=False):
+        n = int(n)
+        t, s_ = oracle.rate(og, spec.omega, spec.delta, True, spec.seed, lo=n, hi=n + 1, tc=tc)
+        assert int(tgt_h[n]) == int(t[n]) and int(score_h[n]) == int(s_[n]), "node %d" % n
+
+    def in_set(a):
+        return set(og.n_inc[og.n_off[a]:og.n_off[a] + og.n_nin[a]].tolist())
+
+    check_match_properties(tgt_h, score_h, match_h, og.n_nin, in_set, h.n_size, spec.omega,
+                           spec.delta, rng, n_check=200)
+    gamma, cg = ctx.contract(dg, match, False)
+    say("block 4m contracted", cg.n_nodes)
+    gamma_h = chp.to_host(gamma, np.uint32)
+    Nc = cg.n_nodes
+    assert Nc == h.n_nodes - npairs
+    cs = cg.host("n_size").astype(np.int64)
+    assert int(cs.sum()) == int(h.n_size.astype(np.int64).sum()) and int(cs.max()) <= spec.omega
+    assert int(cg.host("n_nin").max()) <= spec.delta
+    rep = np.minimum(np.arange(h.n_nodes, dtype=np.uint32), match_h)
+    reps = np.nonzero(match_h >= np.arange(h.n_nodes, dtype=np.uint32))[0]
+    rank = np.empty(h.n_nodes, np.int64)
+    rank[reps] = np.arange(reps.size)
+    assert np.array_equal(gamma_h.astype(np.int64), rank[rep])
+    eo, ns, pins = cg.host("e_off"), cg.host("e_nsrc"), cg.host("e_pins")
+    for e in rng.choice(h.n_edges, 2000, replace=False):
+        a, b, s0 = int(eo[e]), int(eo[e + 1]), int(ns[e])
+        fa, fb, fs = int(h.e_off[e]), int(h.e_off[e + 1]), int(h.e_nsrc[e])
+        want_dst = np.unique(gamma_h[h.e_pins[fa + fs:fb]])
+        want_src = np.setdiff1d(np.unique(gamma_h[h.e_pins[fa:fa + fs]]), want_dst)
+        assert np.array_equal(pins[a + s0:b], want_dst) and np.array_equal(pins[a:a + s0],
+                                                                             want_src)

@@ -133,6 +133,45 @@ def test_purge_wide_neighbourhoods(chp, ctx):
     multilevel(chp, ctx, h, spec.omega, delta, True, 9, 3, tag="purge wide", purge=True)
 
 
+@pytest.mark.parametrize("cfg,nn,limit", [(2, 20000, 60000), (3, 20000, 200000),
+                                          (4, 20000, 30000), (5, 8192, 1000000), (1, None, 1)])
+def test_batched_neighbourhoods(chp, ctx, cfg, nn, limit):
+    """A graph built without neighbourhoods: the rating builds them itself,
+    batch by batch (a small batch limit gives many batches; limit 1 one node
+    per batch), over two levels; each level against the oracle and against
+    the unbatched device run."""
+    spec = synth.config(cfg, n_nodes=nn)
+    h = synth.generate(spec)
+    say("batched", cfg, nn, limit)
+    edges = chp.upload_edges(h)
+    dg = ctx.build_incidence(*edges, spec.omega, spec.delta, False)
+    full = ctx.build_incidence(*edges, spec.omega, spec.delta, True)
+    og = oracle.build_incidence(h.e_off, h.e_nsrc, h.e_pins, h.e_w, h.n_size, spec.omega,
+                                spec.delta, build_neighbors=False)
+    assert_graph_equal(dg, og, "batched build", neighbors=False)
+    ctx.set_batch_entries(limit)
+    try:
+        for lvl in range(2):
+            t, sc, m, npairs = ctx.rate_and_match(dg, spec.omega, spec.delta, True, spec.seed)
+            t2, sc2, m2, np2 = ctx.rate_and_match(full, spec.omega, spec.delta, True, spec.seed)
+            lv = oracle.level(og, spec.omega, spec.delta, True, spec.seed, build_neighbors=False)
+            for name, got, want in (("target", chp.to_host(t, np.uint32), lv.target),
+                                    ("score", chp.to_host(sc, np.uint64), lv.score),
+                                    ("match", chp.to_host(m, np.uint32), lv.match),
+                                    ("unbatched target", chp.to_host(t2, np.uint32), lv.target)):
+                assert_equal(got, want, "batched L%d %s" % (lvl, name))
+            assert npairs == lv.n_pairs == np2
+            if npairs == 0:
+                break
+            gamma, cg = ctx.contract(dg, m, False)
+            _, cfull = ctx.contract(full, m2, True)
+            assert_equal(chp.to_host(gamma, np.uint32), lv.gamma, "batched L%d gamma" % lvl)
+            assert_graph_equal(cg, lv.coarse, "batched L%d coarse" % lvl, neighbors=False)
+            dg, full, og = cg, cfull, lv.coarse
+    finally:
+        ctx.set_batch_entries(0)
+
+
 def test_tiny_graphs(chp, ctx):
     import test_oracle_pins as pins
     for kw in pins.tiny_cases():
