@@ -29,7 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-RATE_KERNELS = ("rate_big", "rate")
+RATE_KERNELS = ("rate_big", "rate", "rate_inc")
 # Invalid neighbours are flagged by the rating and purged from the coarse
 # neighbourhoods (the pages' coarsening does this; --no-purge turns it off).
 PURGE = True
@@ -50,6 +50,10 @@ def parse():
     p.add_argument("--copy-ref-mib", type=int, default=0,
                    help="run one plain device copy of this size first (a reference for "
                         "scaling hardware byte counters)")
+    p.add_argument("--no-neighbour-lists", action="store_true",
+                   help="build the graph without neighbour lists even where they fit")
+    p.add_argument("--progress", action="store_true",
+                   help="print a line per timed step to stderr (long workloads)")
     p.add_argument("--no-purge", action="store_true",
                    help="keep invalid neighbours in the coarse neighbourhoods")
     p.add_argument("--counters", metavar="DIR", default=None,
@@ -116,10 +120,15 @@ def measured_traffic(workload):
     return c.get("traffic_bytes_per_pass")
 
 
-def run_step(chp, ctx, dev_edges, spec, rho_buf):
+# Neighbour lists above this many bytes are not materialised for the whole
+# graph: the rating then builds them batch by batch (workload 5: ~1.9e11 ids).
+NB_BYTES_MAX = 64 << 30
+
+
+def run_step(chp, ctx, dev_edges, spec, rho_buf, with_nb=True):
     """One pass of the hot path; returns per-level pin counts and the summary."""
     import torch
-    g0 = ctx.build_incidence(*dev_edges, spec.omega, spec.delta, True)
+    g0 = ctx.build_incidence(*dev_edges, spec.omega, spec.delta, with_nb)
     total_size = int(spec_total_size(dev_edges))
     floor_nodes = -(-total_size // spec.omega)
     levels = []
@@ -130,13 +139,14 @@ def run_step(chp, ctx, dev_edges, spec, rho_buf):
             break
         if g.n_nodes <= floor_nodes:
             break
-        flags = ctx.new_flags(g) if PURGE else None
+        flags = ctx.new_flags(g) if PURGE and with_nb else None
         _, _, match, npairs = ctx.rate_and_match(g, spec.omega, spec.delta, True, spec.seed,
                                                  flags=flags)
-        levels.append((g.n_nodes, g.n_pins, npairs, g.nb_total))
+        nb_total = g.nb_total if with_nb else ctx.last_rate_stats()[0]
+        levels.append((g.n_nodes, g.n_pins, npairs, nb_total))
         if npairs == 0:
             break
-        gamma, cg = ctx.contract(g, match, True, flags=flags)
+        gamma, cg = ctx.contract(g, match, with_nb, flags=flags)
         rho = gamma.long() if rho is None else gamma.long()[rho]
         if g is not g0:
             g.free()
@@ -200,6 +210,7 @@ def main():
 
     spec = synth.config(args.workload, n_nodes=args.nodes)
     h = synth.generate(spec)
+    print("[bench] generated %s: %d pins" % (spec.name, h.n_pins), file=sys.stderr, flush=True)
     ctx = chp.Context(0)
     dev_edges = chp.upload_edges(h)
     rho_buf = torch.empty(h.n_nodes, dtype=torch.int32, device=ctx.device)
@@ -210,8 +221,14 @@ def main():
         del src, dst
     torch.cuda.synchronize()
 
-    for _ in range(args.warmup):
-        run_step(chp, ctx, dev_edges, spec, rho_buf)
+    sz = np.diff(h.e_off).astype(np.float64)
+    with_nb = float((sz * (sz - 1)).sum()) * 4 <= NB_BYTES_MAX and not args.no_neighbour_lists
+    for i in range(args.warmup):
+        t_w = time.perf_counter()
+        run_step(chp, ctx, dev_edges, spec, rho_buf, with_nb)
+        torch.cuda.synchronize()
+        print("[bench] warmup step %d: %.3f s" % (i, time.perf_counter() - t_w), file=sys.stderr,
+              flush=True)
     torch.cuda.synchronize()
     ctx.reset_timings()
     ctx.set_timing(True)
@@ -219,9 +236,11 @@ def main():
     t0 = time.perf_counter()
     pins = 0
     levels = None
-    for _ in range(args.steps):
-        levels, summ = run_step(chp, ctx, dev_edges, spec, rho_buf)
+    for i in range(args.steps):
+        levels, summ = run_step(chp, ctx, dev_edges, spec, rho_buf, with_nb)
         pins += sum(lv[1] for lv in levels)
+        if args.progress:
+            print("[bench] step %d queued" % i, file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     timings = ctx.timings()
@@ -256,10 +275,12 @@ def main():
         "dtype": "u32/u64 (integer ids, 40-bit fixed-point ratings)",
         "data": "synthetic (seeded generator shaped like the pages' SNN workloads)",
         "config": {"workload": spec.name, "nodes": h.n_nodes, "hyperedges": h.n_edges,
+                   "neighbourhoods": "whole graph" if with_nb else "built per node batch",
+                   "purge": PURGE and with_nb,
                    "pins": h.n_pins, "omega": spec.omega, "delta": spec.delta,
                    "levels": len(levels), "final_nodes": levels[-1][0] - levels[-1][2]
                    if levels else h.n_nodes, "connectivity": int(summ[0])},
-        "roofline": {"bound": "hbm", "kernel": "rate_big+rate (the rating pass)",
+        "roofline": {"bound": "hbm", "kernel": "rate_big+rate+rate_inc (the rating pass)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "avg_pass_ms": rate_ms / max(rate_launches, 1),

@@ -30,7 +30,8 @@ _NAMES = {EINVAL: "EINVAL", ENOMEM: "ENOMEM", EOVERFLOW: "EOVERFLOW",
 
 EXPORTS = ["chp_create", "chp_destroy", "chp_last_error", "chp_build_incidence",
            "chp_rate_and_match", "chp_contract", "chp_evaluate_partition", "chp_hgraph_free",
-           "chp_set_timing", "chp_get_timings", "chp_reset_timings", "chp_set_batch_entries"]
+           "chp_set_timing", "chp_get_timings", "chp_reset_timings", "chp_set_batch_entries",
+           "chp_last_rate_stats", "chp_set_incidence_rating"]
 
 
 class ChpError(RuntimeError):
@@ -101,6 +102,12 @@ def load_library(path: str = LIB_PATH):
     lib.chp_contract.restype = I
     lib.chp_set_batch_entries.argtypes = [P, ctypes.c_uint64]
     lib.chp_set_batch_entries.restype = I
+    lib.chp_last_rate_stats.argtypes = [P, ctypes.POINTER(ctypes.c_uint64),
+                                        ctypes.POINTER(ctypes.c_uint32),
+                                        ctypes.POINTER(ctypes.c_uint32)]
+    lib.chp_last_rate_stats.restype = I
+    lib.chp_set_incidence_rating.argtypes = [P, ctypes.c_uint64, ctypes.c_uint32]
+    lib.chp_set_incidence_rating.restype = I
     lib.chp_evaluate_partition.argtypes = [P, ctypes.POINTER(HGraphC), P, ctypes.c_uint32,
                                            ctypes.POINTER(Params), P, P,
                                            ctypes.POINTER(ctypes.c_uint64)]
@@ -332,6 +339,24 @@ class Context:
         """Neighbour entries per rating batch for graphs without neighbours
         (0 = the library default)."""
         self._check(self.lib.chp_set_batch_entries(self.h, int(entries)), "set_batch_entries")
+
+    def last_rate_stats(self):
+        """(neighbour entries built batch by batch, batches, nodes rated
+        straight from the incidence) of the last rate_and_match; all 0 when
+        the graph carried its neighbourhoods."""
+        n = ctypes.c_uint64()
+        b = ctypes.c_uint32()
+        f = ctypes.c_uint32()
+        self._check(self.lib.chp_last_rate_stats(self.h, ctypes.byref(n), ctypes.byref(b),
+                                                 ctypes.byref(f)), "last_rate_stats")
+        return int(n.value), int(b.value), int(f.value)
+
+    def set_incidence_rating(self, min_visits=0, hash_keys=0):
+        """Incident pins from which a node of a graph without neighbour lists
+        is rated straight from the incidence (0 = default, 2**64-1 = never),
+        and the keys a sparse window may claim (0 = its capacity)."""
+        self._check(self.lib.chp_set_incidence_rating(self.h, int(min_visits), int(hash_keys)),
+                    "set_incidence_rating")
 
     # ---- timing ---------------------------------------------------------------
     def set_timing(self, on=True):

@@ -494,6 +494,22 @@ int chp_set_batch_entries(chp_ctx *c, uint64_t entries) {
   return CHP_OK;
 }
 
+int chp_last_rate_stats(const chp_ctx *c, uint64_t *nb_entries, uint32_t *batches,
+                        uint32_t *inc_nodes) {
+  if (!c) return CHP_EINVAL;
+  if (nb_entries) *nb_entries = c->last_nb_built;
+  if (batches) *batches = c->last_batches;
+  if (inc_nodes) *inc_nodes = c->last_inc_nodes;
+  return CHP_OK;
+}
+
+int chp_set_incidence_rating(chp_ctx *c, uint64_t min_visits, uint32_t hash_keys) {
+  if (!c) return CHP_EINVAL;
+  c->inc_min_visits = min_visits;
+  c->inc_hash_keys = hash_keys;
+  return CHP_OK;
+}
+
 int chp_set_timing(chp_ctx *c, int on) {
   if (!c) return CHP_EINVAL;
   c->timing = on ? 1 : 0;
@@ -594,14 +610,19 @@ namespace {
 
 // Neighbour entries one batch may hold (oversize buffer and packed lists).
 constexpr u64 BATCH_ENTRIES = 3ull << 30;
+// Incident pins from which a node of such a graph is rated straight from the
+// incidence rather than through a neighbour list.
+constexpr u64 INC_MIN_VISITS = 16384;
 
 // Rating of a graph built without neighbourhoods (too many to hold at once;
 // [HP] Sec. VII-C runs the coarsening kernels over batches of nodes, keeping
-// only a few nodes' neighbourhoods in device memory).  Node ranges [lo, hi)
-// whose level-0 neighbour bounds fit the batch limit (c->batch_entries, or
-// BATCH_ENTRIES) get their N(n) built as by chp_build_incidence, into batch
-// buffers, and are rated from them; the rating reads nb_off through a
-// pointer shifted by lo.
+// only a few nodes' neighbourhoods in device memory).  Nodes with many
+// incident pins (c->inc_min_visits, or INC_MIN_VISITS) are rated straight from
+// the incidence, their N(n) held in LDS one id window at a time.  For the
+// others, node ranges [lo, hi) whose level-0 neighbour bounds fit the batch
+// limit (c->batch_entries, or BATCH_ENTRIES) get their N(n) built as by
+// chp_build_incidence, into batch buffers, and are rated from them; the
+// rating reads nb_off through a pointer shifted by lo.
 void rate_batched(chp_ctx *c, Scratch &s, const chp_hgraph *g, const RateArgs &a, NbLists nl,
                   NodeRec *recs, NodeRec *big, u32 *work) {
   const u32 N = g->n_nodes;
@@ -611,14 +632,26 @@ void rate_batched(chp_ctx *c, Scratch &s, const chp_hgraph *g, const RateArgs &a
   bl.list[1] = s.get<u32>(N);
   bl.list[2] = bl.list[3] = bl.list[4] = nullptr;
   bl.cnt = s.get<u32>(8);
-  launch_fill_u32(c, bl.cnt, 8, 0);
-  launch_nb_classify(c, 0, N, g->e_off, g->n_off, g->n_inc, bound, bl);
+  // nodes with many incident pins are rated straight from the incidence
+  // (after the batches); the others through per-batch neighbour lists
+  const u64 fmin = c->inc_min_visits ? c->inc_min_visits : INC_MIN_VISITS;
+  uint8_t *skip = nullptr;
+  NodeRec *frecs = nullptr;
+  u32 *fc = s.get<u32>(4);  // count, max size, max |in|, work counter
+  if (fmin != ~0ull) {
+    skip = s.get<uint8_t>(N);
+    frecs = s.get<NodeRec>(N);
+  }
+  launch_fills(c, {{bl.cnt, 8, 0, false}, {fc, 4, 0, false}});
+  if (skip) launch_inc_classify(c, a, fmin, skip, frecs, fc, fc + 1);
+  launch_nb_classify(c, 0, N, g->e_off, g->n_off, g->n_inc, bound, bl, skip);
   i64 *ooff = s.get<i64>((u64)N + 1);
   i64 *tmp = s.get<i64>(scan_tmp_words(N));
   scan_u32_to_i64(c, bound, ooff, N, tmp);
   launch_check(c, "neighbour bounds");
-  u32 hc[8];
-  read_many(c, {{hc, bl.cnt, sizeof hc}});
+  u32 hc[8], nf = 0;
+  read_many(c, {{hc, bl.cnt, sizeof hc}, {&nf, fc, sizeof nf}});
+  c->last_inc_nodes = nf;
   if (hc[7]) {
     set_err(c, "%sa node's incident pins exceed 2^32");
     throw Fail{CHP_EOVERFLOW};
@@ -640,15 +673,22 @@ void rate_batched(chp_ctx *c, Scratch &s, const chp_hgraph *g, const RateArgs &a
   u32 *nbb = s.get<u32>(room ? room : 1);
   u32 *count = s.get<u32>(N);
   i64 *nboff = s.get<i64>((u64)N + 1);
+  u32 prev = 0;  // node count of the previous batch, whose list total is read next
+  i64 built = 0;
   for (u32 lo = 0; lo < N;) {
     u32 hi = lo + 1;
     while (hi < N && (u64)(hoff[hi + 1] - hoff[lo]) <= budget) ++hi;
     const u32 cnt = hi - lo;
     // N(n) of the batch (bounds recomputed for the range, same values)
     launch_fills(c, {{bl.cnt, 8, 0, false}, {count + lo, cnt, 0, false}});
-    launch_nb_classify(c, lo, cnt, g->e_off, g->n_off, g->n_inc, bound, bl);
+    launch_nb_classify(c, lo, cnt, g->e_off, g->n_off, g->n_inc, bound, bl, skip);
     launch_check(c, "batch neighbour classes");
-    read_many(c, {{hc, bl.cnt, sizeof hc}});
+    i64 last = 0;
+    if (prev)
+      read_many(c, {{hc, bl.cnt, sizeof hc}, {&last, nboff + prev, sizeof last}});
+    else
+      read_many(c, {{hc, bl.cnt, sizeof hc}});
+    built += last;
     u32 *obs = obuf - hoff[lo];  // indexed by the whole graph's oversize offsets
     launch_nb_build(c, N, g->e_off, g->e_pins, g->n_off, g->n_inc, bound, ooff, obs, count, bl,
                     hc);
@@ -663,8 +703,15 @@ void rate_batched(chp_ctx *c, Scratch &s, const chp_hgraph *g, const RateArgs &a
     launch_rate_classify(c, ab, lo, hi, nl, recs, big);
     launch_rate(c, ab, nl, recs, cnt, big, work);
     launch_check(c, "batch rate");
+    ++c->last_batches;
+    prev = cnt;
     lo = hi;
   }
+  i64 last = 0;
+  if (prev) read_many(c, {{&last, nboff + prev, sizeof last}});
+  c->last_nb_built = (u64)(built + last);
+  launch_rate_inc(c, a, frecs, fc, fc + 1, fc + 3, nf, c->inc_hash_keys);
+  launch_check(c, "rate from the incidence");
 }
 
 }  // namespace
@@ -678,6 +725,9 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
     }
     const u32 N = g->n_nodes, E = g->n_edges;
     const bool batched = N && (!g->nb_off || !g->nb);
+    c->last_nb_built = 0;
+    c->last_batches = 0;
+    c->last_inc_nodes = 0;
     if (batched && nb_invalid) {
       set_err(c, "%sinvalid-neighbour flags need the graph's neighbourhoods");
       throw Fail{CHP_EINVAL};

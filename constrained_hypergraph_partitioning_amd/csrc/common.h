@@ -51,6 +51,11 @@ struct chp_ctx {
   u64 *pinned = nullptr;   // host pinned staging (64 words), mapped
   u32 *pinned_dev = nullptr;  // its device address
   u64 batch_entries = 0;      // neighbour entries per rating batch (0 = default)
+  u64 last_nb_built = 0;      // entries the last batched rating built
+  u32 last_batches = 0;       // and its number of batches
+  u32 last_inc_nodes = 0;     // nodes it rated straight from the incidence
+  u64 inc_min_visits = 0;     // incident pins that send a node there (0 = default)
+  u32 inc_hash_keys = 0;      // keys a sparse window there may claim (0 = all it holds)
   u64 *dsmall = nullptr;   // device small buffer (64 words)
   int timing = 0;
   std::vector<TimingRec> pending;

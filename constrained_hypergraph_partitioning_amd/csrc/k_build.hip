@@ -228,13 +228,15 @@ __global__ void k_node_runs(u32 N, const i64 *n_off, const u32 *n_nin, RunLists 
 // ---------------------------------------------------------------------------
 // neighbourhoods: W_n = sum_{e in I(n)} |e| decides the class; the oversize
 // bound of |N(n)| is W_n - |I(n)| (n is a pin of each of its hyperedges).
-// Nodes lo .. lo + N - 1.
+// Nodes lo .. lo + N - 1; a node marked in skip gets bound 0 and no class.
 __global__ void k_nb_classify(u32 lo, u32 N, const i64 *e_off, const i64 *n_off,
-                              const u32 *n_inc, u32 *bound, NbLists nl) {
+                              const u32 *n_inc, u32 *bound, NbLists nl, const uint8_t *skip) {
   const u32 t = blockIdx.x * blockDim.x + threadIdx.x;
   const u32 n = lo + t;
   u64 w = 0, bnd = 0;
-  if (t < N) {
+  if (t < N && skip && skip[n]) {
+    bound[n] = 0;  // rated without a list: none is built
+  } else if (t < N) {
     const i64 a = n_off[n], b = n_off[n + 1];
     for (i64 j = a; j < b; ++j) {
       const u32 e = n_inc[j];
@@ -370,10 +372,10 @@ void launch_node_runs(chp_ctx *c, u32 N, const i64 *n_off, const u32 *n_nin, Run
 }
 
 void launch_nb_classify(chp_ctx *c, u32 lo, u32 N, const i64 *e_off, const i64 *n_off,
-                        const u32 *n_inc, u32 *bound, NbLists nl) {
+                        const u32 *n_inc, u32 *bound, NbLists nl, const uint8_t *skip) {
   if (N == 0) return;
   CHP_LAUNCH(c, "nb_classify", k_nb_classify, grid_for(N, 256), 256, 0, lo, N, e_off, n_off,
-             n_inc, bound, nl);
+             n_inc, bound, nl, skip);
 }
 
 void launch_nb_build(chp_ctx *c, u32 N, const i64 *e_off, const u32 *pins, const i64 *n_off,

@@ -51,7 +51,8 @@ void launch_scatter(chp_ctx *c, u32 E, const i64 *e_off, const u32 *e_nsrc, cons
 void launch_node_runs(chp_ctx *c, u32 N, const i64 *n_off, const u32 *n_nin, RunLists rl);
 // nodes lo .. lo + N - 1
 void launch_nb_classify(chp_ctx *c, u32 lo, u32 N, const i64 *e_off, const i64 *n_off, const u32 *n_inc,
-                        u32 *bound, NbLists nl);
+                        u32 *bound, NbLists nl,
+                        const uint8_t *skip = nullptr);
 void launch_nb_build(chp_ctx *c, u32 N, const i64 *e_off, const u32 *pins, const i64 *n_off,
                      const u32 *n_inc, const u32 *bound, const i64 *ooff, u32 *obuf, u32 *count,
                      NbLists nl, const u32 *host_cnt);
@@ -100,6 +101,16 @@ void launch_rate_classify(chp_ctx *c, const RateArgs &a, u32 lo, u32 hi, NbLists
                           NodeRec *recs, NodeRec *big);
 void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, const NodeRec *recs, u32 nrec,
                  const NodeRec *big, u32 *work);
+// Rating straight from the incidence (graphs without neighbour lists): the
+// classification lists the nodes of [0, a.N) with 1..384 incident hyperedges
+// and min_visits .. 2^27 - 1 incident pins, sets skip[n] for them and writes
+// gmax = {max size, max |in|} (cnt and gmax zeroed before); launch_rate_inc
+// rates the listed nodes (work zeroed before; host_count = *cnt), a sparse
+// window claiming at most hash_keys keys (0 = its full capacity).
+void launch_inc_classify(chp_ctx *c, const RateArgs &a, u64 min_visits, uint8_t *skip,
+                         NodeRec *recs, u32 *cnt, u32 *gmax);
+void launch_rate_inc(chp_ctx *c, const RateArgs &a, const NodeRec *recs, const u32 *cnt,
+                     const u32 *gmax, u32 *work, u32 host_count, u32 hash_keys);
 
 struct MatchScratch {
   u64 *bscore;  // [N] zeroed

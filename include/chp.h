@@ -198,6 +198,25 @@ int chp_evaluate_partition(chp_ctx *ctx, const chp_hgraph *g, const uint32_t *rh
  * whose own list is larger gets a batch of its own. */
 int chp_set_batch_entries(chp_ctx *ctx, uint64_t entries);
 
+/* Graphs without neighbour lists: a node with 1..384 incident hyperedges and
+ * at least min_visits (and below 2^27) pins over them is rated straight from
+ * the incidence, its N(n) held in LDS one id window at a time and never
+ * written out; the rest go through the per-batch lists.  Both routes give the
+ * same target and score.  min_visits 0 restores the default (16384);
+ * UINT64_MAX sends every node through the lists.  hash_keys caps the keys a
+ * sparse window may claim before it stops and the next window resumes at the
+ * first id it could not hold (0 = the table's capacity, 4608): a lower cap
+ * only adds windows; the results do not change. */
+int chp_set_incidence_rating(chp_ctx *ctx, uint64_t min_visits, uint32_t hash_keys);
+
+/* What the last chp_rate_and_match on ctx did about neighbourhoods:
+ * *nb_entries = neighbour entries it built batch by batch, *batches = the
+ * number of batches and *inc_nodes = the nodes it rated straight from the
+ * incidence (all 0 when the graph carried its own lists).  Any pointer may
+ * be NULL.  Host values only; no device work. */
+int chp_last_rate_stats(const chp_ctx *ctx, uint64_t *nb_entries, uint32_t *batches,
+                        uint32_t *inc_nodes);
+
 /* Release every array of g (allocated by this library) and zero *g. */
 void chp_hgraph_free(chp_ctx *ctx, chp_hgraph *g);
 

@@ -5,6 +5,8 @@ synthetic hypergraphs shaped like the five workloads (scaled so the oracle
 finishes in seconds while the GPU kernels still see several tiles, ragged
 tails and every size class), plus tiny brute-force-pinned graphs, unsorted
 input, constraint-stress settings and error paths."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -133,43 +135,136 @@ def test_purge_wide_neighbourhoods(chp, ctx):
     multilevel(chp, ctx, h, spec.omega, delta, True, 9, 3, tag="purge wide", purge=True)
 
 
-@pytest.mark.parametrize("cfg,nn,limit", [(2, 20000, 60000), (3, 20000, 200000),
-                                          (4, 20000, 30000), (5, 8192, 1000000), (1, None, 1)])
-def test_batched_neighbourhoods(chp, ctx, cfg, nn, limit):
-    """A graph built without neighbourhoods: the rating builds them itself,
-    batch by batch (a small batch limit gives many batches; limit 1 one node
-    per batch), over two levels; each level against the oracle and against
-    the unbatched device run."""
-    spec = synth.config(cfg, n_nodes=nn)
-    h = synth.generate(spec)
-    say("batched", cfg, nn, limit)
+NEVER = (1 << 64) - 1       # no node rated straight from the incidence
+INC_DEFAULT = 16384         # the library's default threshold
+
+
+def fused_mask(og, min_visits):
+    """Nodes the library rates straight from the incidence: 1..384 incident
+    hyperedges and min_visits .. 2^27 - 1 pins over them."""
+    sizes = np.diff(og.e_off).astype(np.int64)
+    deg = np.diff(og.n_off)
+    cs = np.concatenate([[0], np.cumsum(sizes[og.n_inc])])
+    w = cs[og.n_off[1:]] - cs[og.n_off[:-1]]
+    return (deg >= 1) & (deg <= 384) & (w >= min_visits) & (w < 2 ** 27)
+
+
+def batched_levels(chp, ctx, h, omega, delta, seed, levels, limit, inc, hkeys=0, tag=""):
+    """Levels of a graph built without neighbourhoods: the rating builds
+    them per batch or rates straight from the incidence; every level's
+    target, score, match, gamma and coarse graph against the oracle, and the
+    rating's statistics against the definition."""
     edges = chp.upload_edges(h)
-    dg = ctx.build_incidence(*edges, spec.omega, spec.delta, False)
-    full = ctx.build_incidence(*edges, spec.omega, spec.delta, True)
-    og = oracle.build_incidence(h.e_off, h.e_nsrc, h.e_pins, h.e_w, h.n_size, spec.omega,
-                                spec.delta, build_neighbors=False)
-    assert_graph_equal(dg, og, "batched build", neighbors=False)
+    dg = ctx.build_incidence(*edges, omega, delta, False)
+    og = oracle.build_incidence(h.e_off, h.e_nsrc, h.e_pins, h.e_w, h.n_size, omega, delta,
+                                build_neighbors=False)
+    assert_graph_equal(dg, og, tag + " build", neighbors=False)
     ctx.set_batch_entries(limit)
+    ctx.set_incidence_rating(inc, hkeys)
     try:
-        for lvl in range(2):
-            t, sc, m, npairs = ctx.rate_and_match(dg, spec.omega, spec.delta, True, spec.seed)
-            t2, sc2, m2, np2 = ctx.rate_and_match(full, spec.omega, spec.delta, True, spec.seed)
-            lv = oracle.level(og, spec.omega, spec.delta, True, spec.seed, build_neighbors=False)
+        for lvl in range(levels):
+            t, sc, m, npairs = ctx.rate_and_match(dg, omega, delta, True, seed)
+            built, batches, nfused = ctx.last_rate_stats()
+            fm = fused_mask(og, inc if inc else INC_DEFAULT)
+            # entries built over the batches = sum of |N(n)| over the other nodes
+            nbo = oracle.neighbors(dataclasses.replace(og)).nb_off
+            want_nb = int(np.diff(nbo)[~fm].sum())
+            assert (nfused, built) == (int(fm.sum()), want_nb) and batches >= 1, \
+                (nfused, int(fm.sum()), built, want_nb, batches)
+            lv = oracle.level(og, omega, delta, True, seed, build_neighbors=False)
             for name, got, want in (("target", chp.to_host(t, np.uint32), lv.target),
                                     ("score", chp.to_host(sc, np.uint64), lv.score),
-                                    ("match", chp.to_host(m, np.uint32), lv.match),
-                                    ("unbatched target", chp.to_host(t2, np.uint32), lv.target)):
-                assert_equal(got, want, "batched L%d %s" % (lvl, name))
-            assert npairs == lv.n_pairs == np2
+                                    ("match", chp.to_host(m, np.uint32), lv.match)):
+                assert_equal(got, want, "%s L%d %s" % (tag, lvl, name))
+            assert npairs == lv.n_pairs
             if npairs == 0:
                 break
             gamma, cg = ctx.contract(dg, m, False)
-            _, cfull = ctx.contract(full, m2, True)
-            assert_equal(chp.to_host(gamma, np.uint32), lv.gamma, "batched L%d gamma" % lvl)
-            assert_graph_equal(cg, lv.coarse, "batched L%d coarse" % lvl, neighbors=False)
-            dg, full, og = cg, cfull, lv.coarse
+            assert_equal(chp.to_host(gamma, np.uint32), lv.gamma, "%s L%d gamma" % (tag, lvl))
+            assert_graph_equal(cg, lv.coarse, "%s L%d coarse" % (tag, lvl), neighbors=False)
+            dg, og = cg, lv.coarse
     finally:
         ctx.set_batch_entries(0)
+        ctx.set_incidence_rating(0, 0)
+
+
+INC_MODES = {"lists": (NEVER, 0), "default": (0, 0), "all": (1, 0), "all-hash64": (1, 64)}
+
+
+@pytest.mark.parametrize("mode", list(INC_MODES))
+@pytest.mark.parametrize("cfg,nn,limit", [(2, 20000, 60000), (3, 20000, 200000),
+                                          (4, 20000, 30000), (5, 8192, 1000000), (1, None, 1)])
+def test_batched_neighbourhoods(chp, ctx, cfg, nn, limit, mode):
+    """A graph built without neighbourhoods over two levels: per-batch lists
+    (a small batch limit gives many batches; limit 1 one node per batch),
+    the incidence rating for the nodes above the default threshold, for
+    every node, and for every node with a sparse window capped at 64 keys
+    (so that windows fill up and restart)."""
+    spec = synth.config(cfg, n_nodes=nn)
+    h = synth.generate(spec)
+    inc, hkeys = INC_MODES[mode]
+    say("batched", cfg, nn, limit, mode)
+    batched_levels(chp, ctx, h, spec.omega, spec.delta, spec.seed, 2, limit, inc, hkeys,
+                   tag="batched %d %s" % (cfg, mode))
+
+
+def test_incidence_rating_tiny(chp, ctx):
+    """Every node of the brute-force-pinned tiny graphs rated straight from
+    the incidence, under the limit grid (so that both limits bind)."""
+    import test_oracle_pins as pins
+    for kw in pins.tiny_cases():
+        h = synth.tiny(**kw)
+        say("inc tiny", kw["seed"])
+        for omega, delta in pins.constraint_grid(h):
+            for hkeys in (0, 2):
+                batched_levels(chp, ctx, h, omega, delta, kw["seed"], 1, 0, 1, hkeys,
+                               tag="inc tiny%d" % kw["seed"])
+
+
+@pytest.mark.parametrize("omega,dslack", [(4, 0), (6, 1), (16, 3)])
+def test_incidence_rating_stress(chp, ctx, omega, dslack):
+    """Both limits binding (Delta just above the largest in-degree), several
+    levels, every node rated straight from the incidence."""
+    spec = synth.config(1)
+    h = synth.generate(spec)
+    indeg = np.bincount(np.concatenate([h.e_pins[h.e_off[e] + h.e_nsrc[e]:h.e_off[e + 1]]
+                                        for e in range(h.n_edges)]), minlength=h.n_nodes)
+    delta = int(indeg.max()) + dslack
+    say("inc stress", omega, delta)
+    batched_levels(chp, ctx, h, omega, delta, 5, 6, 0, 1, 0, tag="inc stress")
+
+
+def test_incidence_rating_hub_and_wide_span(chp, ctx):
+    """A hub with 500 inbound hyperedges (above the 384 the incidence rating
+    takes: it goes through a list) beside nodes that take it, and a node
+    whose pins span 6,000,000 ids (histogram buckets wider than the
+    narrowest)."""
+    rng = np.random.Generator(np.random.PCG64(21))
+    n = 6000
+    edges = []
+    for j in range(500):
+        dst = {0} | set(int(x) for x in rng.integers(1, n, 6))
+        dst.discard(j + 1)
+        edges.append(([j + 1], sorted(dst)))
+    for j in range(2000):
+        s = int(rng.integers(0, n))
+        dst = set(int(x) for x in rng.integers(0, n, int(rng.integers(1, 40))))
+        dst.discard(s)
+        if dst:
+            edges.append(([s], sorted(dst)))
+    h = synth.from_lists(n, edges, weights=[1 + j % 7 for j in range(len(edges))])
+    say("inc hub")
+    batched_levels(chp, ctx, h, 1 << 20, 1 << 20, 3, 2, 0, 1, 0, tag="inc hub")
+    N = 6_000_000
+    edges = []
+    for j in range(200):
+        s = int(rng.integers(1, N))
+        dst = ({0} | set(int(x) for x in rng.integers(1, N, 30))) - {s}
+        edges.append(([s], sorted(dst)))
+    h = synth.from_lists(N, edges, weights=[1 + j % 5 for j in range(len(edges))])
+    say("inc wide span")
+    batched_levels(chp, ctx, h, 1 << 20, 1 << 20, 3, 1, 0, 1, 0, tag="inc wide")
+    batched_levels(chp, ctx, h, 1 << 20, 1 << 20, 3, 1, 0, 1, 16, tag="inc wide hash16")
 
 
 def test_tiny_graphs(chp, ctx):
