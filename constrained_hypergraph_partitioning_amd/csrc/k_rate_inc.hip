@@ -46,7 +46,7 @@ constexpr u32 FNHB = 2048;         // histogram buckets
 constexpr u32 FBS_MIN = 11;        // log2 of the narrowest bucket (FD / 4 ids)
 constexpr u32 FHTGT = FCAP * 3 / 4;  // estimated visits a hash pass aims at
 constexpr u32 FEST = 16;           // estimates count sixteenths of a visit
-constexpr u32 FU = 8;              // pins per thread per chunk
+constexpr u32 FU = 12;             // pins per thread per chunk
 constexpr u32 FCH = FB * FU;       // pins per chunk
 constexpr u32 FNBLK = FCH / WAVE;  // wave blocks per chunk
 constexpr u64 FINB = 1ull << 63;   // term flag: destination run of an inbound hyperedge
@@ -77,6 +77,7 @@ struct IncSmem {
   u32 rlen[FRUNS];
   u32 rsp[FRUNS + 1];  // first sample of each run
   u32 rs[FRUNS];       // this window: first pin of each run's stretch
+  u32 nxt[FRUNS];      // after a window: each run's first pin at or above its end
   u32 pre[FRUNS + 1];  // this window: stretch offsets
   u32 sfirst[FSMAX];
   u32 slast[FSMAX];
@@ -327,6 +328,7 @@ __device__ void rate_inc_node(const RateArgs &A, IncSmem &S, const NodeRec &h, u
   // doubled after one that did not, so a misjudged stretch costs a few
   // windows and a window of one id always fits
   u64 hspan = end - mn;
+  u64 last_hi = ~0ull;  // end of the last window, if it did not fill up (then nxt is exact)
   while (lo < end) {
     // the window: all threads take the same decision from the estimates
     const u32 b0 = (u32)((lo - mn) >> bs);
@@ -351,19 +353,22 @@ __device__ void rate_inc_node(const RateArgs &A, IncSmem &S, const NodeRec &h, u
       if (hi - lo > hspan) hi = lo + hspan;
     }
     const u32 lo32 = (u32)lo, hi32 = (u32)(hi < 0xFFFFFFFFull ? hi : 0xFFFFFFFFull);
-    // each run's stretch: whole sampled blocks that can hold a pin in [lo, hi)
+    // each run's stretch: whole sampled blocks that can hold a pin in [lo, hi),
+    // from the run's exact position when the last window ended at lo
     u32 L = 0;
     if (tid < nr) {
       const u32 g0 = S.rsp[tid], g1 = S.rsp[tid + 1];
       const u32 ks = lds_lower_bound(S.slast, g0, g1, lo32);
       const u32 ke = lds_lower_bound(S.sfirst, g0, g1, hi32);  // one past the last block
-      u32 s0 = 0;
+      u32 s0 = 0, e0 = 0;
       if (ks < ke) {
         s0 = (ks - g0) << sh;
-        const u32 e0 = ((ke - g0) << sh) < S.rlen[tid] ? ((ke - g0) << sh) : S.rlen[tid];
-        L = e0 - s0;
+        if (lo == last_hi && S.nxt[tid] > s0) s0 = S.nxt[tid];
+        e0 = ((ke - g0) << sh) < S.rlen[tid] ? ((ke - g0) << sh) : S.rlen[tid];
+        L = e0 > s0 ? e0 - s0 : 0;
       }
       S.rs[tid] = s0;
+      S.nxt[tid] = L ? e0 : 0;  // lowered below to the first pin >= hi, 0 = unknown
     }
     u32 T;
     const u32 po = wg_excl_scan<FB>(L, S.red32, &T);
@@ -393,6 +398,18 @@ __device__ void rate_inc_node(const RateArgs &A, IncSmem &S, const NodeRec &h, u
         const i64 pos = ok ? S.rstart[r] + S.rs[r] + (i - S.pre[r]) : 0;
         const u32 x = A.e_pins[pos];
         v[u] = ok ? x : 0xFFFFFFFFu;
+      }
+      // the first pin >= hi of each run's stretch (one lane per run and wave block)
+#pragma unroll
+      for (u32 u = 0; u < FU; ++u) {
+        const bool bey = v[u] != 0xFFFFFFFFu && v[u] >= hi32;
+        const u32 tag = bey ? rr[u] : 0xFFFFFFFFu;
+        const u32 ptag = __shfl_up(tag, 1, WAVE);
+        if (bey && (lane == 0 || ptag != rr[u])) {
+          const u32 r = rr[u];
+          const u32 i = c + (u * FW + wid) * WAVE + lane;
+          atomicMin(&S.nxt[r], S.rs[r] + (i - S.pre[r]));
+        }
       }
       if (direct && de) {
 #pragma unroll
@@ -496,6 +513,7 @@ __device__ void rate_inc_node(const RateArgs &A, IncSmem &S, const NodeRec &h, u
       }
     }
     const bool full = !direct && fmin < hi32;
+    last_hi = full ? ~0ull : hi;
     if (!direct) {
       if (full) {
         hspan = (hi - fmin) / 2 > 0 ? (hi - fmin) / 2 : 1;
