@@ -77,6 +77,7 @@ def _load():
             "or_evaluate": [E, P, u32, u64, u32, P, P, P],
             "or_flags": [E, P, P, P, P, P, u64, u32, P],
             "or_purge": [u32, P, P, P, P, P, u32, P, ctypes.POINTER(P), ctypes.POINTER(u64)],
+            "or_pair_leftovers": [u32, P, P, P, u64, u32, u32, P, ctypes.POINTER(u64)],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -293,6 +294,21 @@ def purge(g: Graph, flag, match_arr, gamma, cg: Graph) -> Graph:
     return cg
 
 
+LEFTOVER_WINDOW = 64  # positions a leftover node scans below its slack position
+
+
+def pair_leftovers(target, match_arr, n_size, n_nin, omega, delta, window=LEFTOVER_WINDOW):
+    """O11: best-effort pairing of the unmatched nodes without a target.
+    Returns (new match array, number of new pairs)."""
+    m = np.array(match_arr, dtype=np.uint32, copy=True)
+    t = np.ascontiguousarray(target, np.uint32)
+    npairs = ctypes.c_uint64()
+    _check(_load().or_pair_leftovers(t.shape[0], _p(t), _p(np.ascontiguousarray(n_size, np.uint32)),
+                                     _p(np.ascontiguousarray(n_nin, np.uint32)), omega, delta,
+                                     window, _p(m), ctypes.byref(npairs)), "pair_leftovers")
+    return m, int(npairs.value)
+
+
 @dataclasses.dataclass
 class Level:
     target: np.ndarray
@@ -305,12 +321,16 @@ class Level:
 
 
 def level(g: Graph, omega, delta, noise_on=True, seed=0, build_neighbors=True,
-          purge_invalid=False) -> Level:
+          purge_invalid=False, leftovers=False) -> Level:
     """One coarsening level: rate, match, contract.  With purge_invalid the
     neighbour flags of g are computed (Level.flags) and the coarse
-    neighbourhoods are purged of flagged neighbours (O10)."""
+    neighbourhoods are purged of flagged neighbours (O10); with leftovers the
+    unmatched nodes without a target are paired best-effort (O11)."""
     target, score = rate(g, omega, delta, noise_on, seed)
     m, npairs = match(target, score)
+    if leftovers:
+        m, extra = pair_leftovers(target, m, g.n_size, g.n_nin, omega, delta)
+        npairs += extra
     fl = flags(g, omega, delta) if purge_invalid else None
     if npairs == 0:
         return Level(target, score, m, 0, None, None, fl)
@@ -321,7 +341,7 @@ def level(g: Graph, omega, delta, noise_on=True, seed=0, build_neighbors=True,
 
 
 def coarsen(g: Graph, omega, delta, target_nodes=0, max_levels=64, noise_on=True, seed=0,
-            purge_invalid=False):
+            purge_invalid=False, leftovers=False):
     """O9: the level loop of [P1] Sec. III.  Stops at the first of: fewer than
     target_nodes nodes; at most ceil(sum size / Omega) nodes (the lowest valid
     count); a level with no pair; max_levels levels.  Returns the list of Levels and the projection
@@ -333,7 +353,8 @@ def coarsen(g: Graph, omega, delta, target_nodes=0, max_levels=64, noise_on=True
     for _ in range(max_levels):
         if cur.n_nodes < target_nodes or cur.n_nodes <= floor_nodes:
             break
-        lv = level(cur, omega, delta, noise_on, seed, purge_invalid=purge_invalid)
+        lv = level(cur, omega, delta, noise_on, seed, purge_invalid=purge_invalid,
+                   leftovers=leftovers)
         levels.append(lv)
         if lv.n_pairs == 0:
             break

@@ -689,3 +689,82 @@ int or_evaluate(const or_edges *g, const uint32_t *rho, uint32_t k, uint64_t ome
   free(cnt), free(mark), free(dmark);
   return OR_OK;
 }
+
+/*
+ * O11 -- best-effort pairing of the nodes left without a partner
+ * ([P1] Sec. V-C, last mechanism).  Reading (the pages leave the details
+ * open): the nodes gathered are those still unmatched after the matching
+ * whose target is undefined.  They are sorted by (size, id) ascending.  Node n
+ * finds, by binary search, the last position whose size fits its slack
+ * Omega - size(n), then takes the first node m != n, scanning down at most
+ * `window` positions from there, whose inbound count together with n's stays
+ * within Delta (the union overestimated by the sum).  A node claimed by
+ * several takes the smallest id; n pairs with its choice m when it won m and
+ * no node claimed n itself.  match is updated in place; returns the number
+ * of new pairs in *n_pairs.
+ */
+typedef struct {
+  uint32_t size, id;
+} or_sz;
+
+static int cmp_sz(const void *x, const void *y) {
+  const or_sz *a = (const or_sz *)x, *b = (const or_sz *)y;
+  if (a->size != b->size) return a->size < b->size ? -1 : 1;
+  return a->id < b->id ? -1 : (a->id > b->id ? 1 : 0);
+}
+
+int or_pair_leftovers(uint32_t N, const uint32_t *target, const uint32_t *n_size,
+                      const uint32_t *n_nin, uint64_t omega, uint32_t delta, uint32_t window,
+                      uint32_t *match, uint64_t *n_pairs) {
+  *n_pairs = 0;
+  uint32_t nl = 0;
+  for (uint32_t n = 0; n < N; ++n)
+    if (target[n] == NONE && match[n] == n) ++nl;
+  if (nl < 2) return OR_OK;
+  or_sz *L = (or_sz *)malloc(sizeof(or_sz) * nl);
+  uint32_t *choice = (uint32_t *)malloc(sizeof(uint32_t) * nl);
+  uint32_t *claim = (uint32_t *)malloc(sizeof(uint32_t) * N);
+  if (!L || !choice || !claim) {
+    free(L), free(choice), free(claim);
+    return OR_ENOMEM;
+  }
+  uint32_t k = 0;
+  for (uint32_t n = 0; n < N; ++n)
+    if (target[n] == NONE && match[n] == n) L[k].size = n_size[n], L[k].id = n, ++k;
+  qsort(L, nl, sizeof(or_sz), cmp_sz);
+  for (uint32_t n = 0; n < N; ++n) claim[n] = NONE;
+  for (uint32_t i = 0; i < nl; ++i) {
+    const uint32_t n = L[i].id;
+    choice[i] = NONE;
+    if ((uint64_t)L[i].size > omega) continue;
+    const uint64_t slack = omega - L[i].size;
+    /* binary search: number of positions whose size is <= slack */
+    uint32_t lo = 0, hi = nl;
+    while (lo < hi) {
+      uint32_t mid = lo + (hi - lo) / 2;
+      if ((uint64_t)L[mid].size <= slack) lo = mid + 1;
+      else hi = mid;
+    }
+    /* scan down from position lo - 1, at most `window` positions */
+    for (uint32_t s = 0; s < window && s < lo; ++s) {
+      const uint32_t j = lo - 1 - s;
+      if (j == i) continue;
+      const uint32_t m = L[j].id;
+      if ((uint64_t)n_nin[n] + n_nin[m] <= delta) {
+        choice[i] = m;
+        break;
+      }
+    }
+    if (choice[i] != NONE && n < claim[choice[i]]) claim[choice[i]] = n;
+  }
+  for (uint32_t i = 0; i < nl; ++i) {
+    const uint32_t n = L[i].id, m = choice[i];
+    if (m != NONE && claim[m] == n && claim[n] == NONE) {
+      match[n] = m;
+      match[m] = n;
+      ++*n_pairs;
+    }
+  }
+  free(L), free(choice), free(claim);
+  return OR_OK;
+}

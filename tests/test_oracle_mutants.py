@@ -41,6 +41,12 @@ MUTANTS = {
     "roots_not_matched_by_default": ("if (tg != NONE && target[tg] == v) { /* v in R */",
                                      "if (0) {"),
     "inbound_counts_sources": ("if (i >= d0 && dmark[p] != e) {", "if (dmark[p] != e) {"),
+    "leftover_largest_claimer": ("if (choice[i] != NONE && n < claim[choice[i]]) claim[choice[i]] = n;",
+                                 "if (choice[i] != NONE && (claim[choice[i]] == NONE || n > claim[choice[i]])) claim[choice[i]] = n;"),
+    "leftover_scan_from_bottom": ("const uint32_t j = lo - 1 - s;", "const uint32_t j = s;"),
+    "leftover_claimed_pairs_too": ("if (m != NONE && claim[m] == n && claim[n] == NONE) {",
+                                   "if (m != NONE && claim[m] == n) {"),
+    "leftover_delta_ignored": ("if ((uint64_t)n_nin[n] + n_nin[m] <= delta) {", "if (1) {"),
 }
 
 
@@ -56,6 +62,11 @@ def _checks():
         pins.test_rate_match_vs_brute(kw, True)
         pins.test_contract_evaluate_vs_brute(kw)
     pins.test_evaluate_closed_forms(1)
+    pins.test_leftovers_hand_examples()
+    pins.test_leftovers_window_bound()
+    pins.test_leftovers_only_unmatched_without_target()
+    for seed in range(6):
+        pins.test_leftovers_invariants(seed)
 
 
 def _build_mutant(name, tmpdir):

@@ -465,3 +465,113 @@ def test_purge_multilevel_same_coarsening():
                     if d not in kept:
                         assert ff[lo + i] == 1
         assert flagged > 0  # the limits bind, so something was purged
+
+
+# ---- O11: best-effort pairing of nodes left without a partner ([HP] Sec. V-C)
+NONE = 0xFFFFFFFF
+
+
+def _leftovers(sizes, nin, omega, delta, window=oracle.LEFTOVER_WINDOW, target=None, match=None):
+    n = len(sizes)
+    t = np.full(n, NONE, np.uint32) if target is None else np.asarray(target, np.uint32)
+    m = np.arange(n, dtype=np.uint32) if match is None else np.asarray(match, np.uint32)
+    return oracle.pair_leftovers(t, m, np.asarray(sizes, np.uint32), np.asarray(nin, np.uint32),
+                                 omega, delta, window)
+
+
+def _pairs(m):
+    return sorted({tuple(sorted((i, int(j)))) for i, j in enumerate(m) if int(j) != i})
+
+
+def test_leftovers_hand_examples():
+    """Worked by hand from the reading: sort by (size, id), binary-search the
+    slack, scan down for the first node within Delta, smallest claimer wins,
+    a claimed node does not pair through its own claim."""
+    # sizes 1,1,2,3 under Omega 4: 0 and 1 reach 3, 2 and 3 reach 1;
+    # 3 goes to 0 (smaller id), 1 goes to 2 (2 is not claimed)
+    m, k = _leftovers([1, 1, 2, 3], [1, 1, 1, 1], 4, 100)
+    assert _pairs(m) == [(0, 3), (1, 2)] and k == 2
+    # six equal nodes, Omega 2: all but 5 choose 5, 5 chooses 4; 0 wins 5,
+    # and 5, being claimed, does not pair with 4
+    m, k = _leftovers([1] * 6, [1] * 6, 2, 100)
+    assert _pairs(m) == [(0, 5)] and k == 1
+    # Delta binds: 0 and 1 (|in| 5) cannot join 3 (|in| 3) under Delta 7
+    m, k = _leftovers([1, 1, 1, 1], [5, 5, 1, 3], 10, 7)
+    assert _pairs(m) == [(0, 2)] and k == 1
+    # a node whose slack fits nobody but itself stays single
+    m, k = _leftovers([3, 3], [1, 1], 5, 100)
+    assert k == 0 and _pairs(m) == []
+
+
+def test_leftovers_window_bound():
+    """Nodes 1..68 can only join node 0, at the bottom of the order and more
+    than 64 positions below their slack position: they find nobody, and 0
+    pairs with 69.  With a window covering everything they all choose 0,
+    node 1 wins it, and 69 (which also wants 0) stays single."""
+    n = 70
+    nin = [10] * n
+    nin[0] = 1
+    m, k = _leftovers([1] * n, nin, 2, 11)
+    assert _pairs(m) == [(0, 69)] and k == 1
+    m, k = _leftovers([1] * n, nin, 2, 11, window=n)
+    assert _pairs(m) == [(0, 1)] and k == 1
+
+
+def test_leftovers_only_unmatched_without_target():
+    """Nodes with a target, or already matched, are neither paired nor
+    claimed; the existing pairs are kept."""
+    t = [NONE, 5, NONE, NONE, NONE, 1]
+    match = [0, 5, 2, 3, 4, 1]
+    m, k = _leftovers([1] * 6, [1] * 6, 2, 100, target=t, match=match)
+    assert m[1] == 5 and m[5] == 1
+    assert _pairs(m) == [(0, 4), (1, 5)] and k == 1
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_leftovers_invariants(seed):
+    """Random leftovers: the result is a matching that keeps every earlier
+    pair, pairs only unmatched nodes without a target, and every new pair fits
+    Omega and, with inbound sets counted as a sum, Delta."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n = int(rng.integers(2, 400))
+    sizes = rng.integers(1, 9, n).astype(np.uint32)
+    nin = rng.integers(0, 20, n).astype(np.uint32)
+    omega = int(rng.integers(8, 17))
+    delta = int(rng.integers(10, 40))
+    t = np.where(rng.random(n) < 0.6, NONE, 0).astype(np.uint32)
+    match = np.arange(n, dtype=np.uint32)
+    for i in range(0, n - 1, 7):  # some existing pairs
+        if t[i] != NONE and t[i + 1] != NONE:
+            match[i], match[i + 1] = i + 1, i
+    m, k = _leftovers(sizes, nin, omega, delta, target=t, match=match)
+    assert np.array_equal(m[m], np.arange(n))
+    new = 0
+    for i in range(n):
+        j = int(m[i])
+        if j == int(match[i]):
+            continue
+        assert int(match[i]) == i and int(match[j]) == j  # both were single
+        assert t[i] == NONE and t[j] == NONE
+        assert int(sizes[i]) + int(sizes[j]) <= omega
+        assert int(nin[i]) + int(nin[j]) <= delta
+        new += 1
+    assert new == 2 * k
+
+
+def test_leftovers_multilevel_invariants():
+    """Coarsening with the leftover pairing keeps every coarse node within
+    Omega and Delta, and its first level pairs at least as many nodes as the
+    same level without it (same rating and matching, pairs only added)."""
+    for cfg, nn in ((4, 6000), (1, None)):
+        spec = synth.config(cfg, n_nodes=nn)
+        h = synth.generate(spec)
+        la, _, _ = oracle.coarsen(load(h, spec.omega, spec.delta), spec.omega, spec.delta, 0, 6,
+                                  True, spec.seed)
+        lb, _, _ = oracle.coarsen(load(h, spec.omega, spec.delta), spec.omega, spec.delta, 0, 6,
+                                   True, spec.seed, leftovers=True)
+        assert la[0].n_pairs <= lb[0].n_pairs
+        for lv in lb:
+            if lv.coarse is None:
+                continue
+            assert int(lv.coarse.n_size.max()) <= spec.omega
+            assert int(lv.coarse.n_nin.max()) <= spec.delta
