@@ -5,7 +5,8 @@ One step = the whole hot path on the 100,000-node locality-biased ring
 workload (Poisson(32) fan-out clipped to [2,256], 80% of destinations within
 +-512 ring positions, weights 1..8, Omega 64, Delta 1024): build the canonical
 CSR, incidence and neighbourhoods; coarsen level by level (rate, handshake
-match, contract) until fewer than 10,000 nodes remain or no pair forms; then
+match, pair the nodes left without a partner, contract) until fewer than
+10,000 nodes remain or no pair forms; then
 evaluate the projected partition on the input graph.  The input edge CSR is
 resident in HBM before timing starts.
 
@@ -33,6 +34,9 @@ RATE_KERNELS = ("rate_big", "rate", "rate_inc")
 # Invalid neighbours are flagged by the rating and purged from the coarse
 # neighbourhoods (the pages' coarsening does this; --no-purge turns it off).
 PURGE = True
+# Nodes left without a partner are paired best-effort, as the pages'
+# coarsening does (--no-leftovers turns it off).
+LEFTOVERS = True
 RATE_SOURCE = os.path.join(ROOT, "constrained_hypergraph_partitioning_amd", "csrc", "k_rate.hip")
 COUNTERS_JSON = os.path.join(ROOT, "profiles", "rating_counters.json")
 COPY_REF_MIB = 256
@@ -54,6 +58,8 @@ def parse():
                    help="build the graph without neighbour lists even where they fit")
     p.add_argument("--progress", action="store_true",
                    help="print a line per timed step to stderr (long workloads)")
+    p.add_argument("--no-leftovers", action="store_true",
+                   help="do not pair the nodes left without a partner")
     p.add_argument("--no-purge", action="store_true",
                    help="keep invalid neighbours in the coarse neighbourhoods")
     p.add_argument("--counters", metavar="DIR", default=None,
@@ -140,8 +146,10 @@ def run_step(chp, ctx, dev_edges, spec, rho_buf, with_nb=True):
         if g.n_nodes <= floor_nodes:
             break
         flags = ctx.new_flags(g) if PURGE and with_nb else None
-        _, _, match, npairs = ctx.rate_and_match(g, spec.omega, spec.delta, True, spec.seed,
-                                                 flags=flags)
+        tgt, _, match, npairs = ctx.rate_and_match(g, spec.omega, spec.delta, True, spec.seed,
+                                                   flags=flags)
+        if LEFTOVERS:
+            npairs += ctx.pair_leftovers(g, tgt, match, spec.omega, spec.delta)
         nb_total = g.nb_total if with_nb else ctx.last_rate_stats()[0]
         levels.append((g.n_nodes, g.n_pins, npairs, nb_total))
         if npairs == 0:
@@ -196,8 +204,9 @@ def main():
         import synth
         summarize_counters(args.counters, synth.config(args.workload, n_nodes=args.nodes).name)
         return
-    global PURGE
+    global PURGE, LEFTOVERS
     PURGE = not args.no_purge
+    LEFTOVERS = not args.no_leftovers
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -276,7 +285,7 @@ def main():
         "data": "synthetic (seeded generator shaped like the pages' SNN workloads)",
         "config": {"workload": spec.name, "nodes": h.n_nodes, "hyperedges": h.n_edges,
                    "neighbourhoods": "whole graph" if with_nb else "built per node batch",
-                   "purge": PURGE and with_nb,
+                   "purge": PURGE and with_nb, "leftover_pairing": LEFTOVERS,
                    "pins": h.n_pins, "omega": spec.omega, "delta": spec.delta,
                    "levels": len(levels), "final_nodes": levels[-1][0] - levels[-1][2]
                    if levels else h.n_nodes, "connectivity": int(summ[0])},

@@ -31,7 +31,7 @@ _NAMES = {EINVAL: "EINVAL", ENOMEM: "ENOMEM", EOVERFLOW: "EOVERFLOW",
 EXPORTS = ["chp_create", "chp_destroy", "chp_last_error", "chp_build_incidence",
            "chp_rate_and_match", "chp_contract", "chp_evaluate_partition", "chp_hgraph_free",
            "chp_set_timing", "chp_get_timings", "chp_reset_timings", "chp_set_batch_entries",
-           "chp_last_rate_stats", "chp_set_incidence_rating"]
+           "chp_last_rate_stats", "chp_set_incidence_rating", "chp_pair_leftovers"]
 
 
 class ChpError(RuntimeError):
@@ -106,6 +106,9 @@ def load_library(path: str = LIB_PATH):
                                         ctypes.POINTER(ctypes.c_uint32),
                                         ctypes.POINTER(ctypes.c_uint32)]
     lib.chp_last_rate_stats.restype = I
+    lib.chp_pair_leftovers.argtypes = [P, ctypes.POINTER(HGraphC), ctypes.POINTER(Params), P, P,
+                                       ctypes.POINTER(ctypes.c_uint32)]
+    lib.chp_pair_leftovers.restype = I
     lib.chp_set_incidence_rating.argtypes = [P, ctypes.c_uint64, ctypes.c_uint32]
     lib.chp_set_incidence_rating.restype = I
     lib.chp_evaluate_partition.argtypes = [P, ctypes.POINTER(HGraphC), P, ctypes.c_uint32,
@@ -307,6 +310,16 @@ class Context:
                                                 _ptr(flags) if flags is not None else None),
                     "rate_and_match")
         return target, score, match, int(npairs.value)
+
+    def pair_leftovers(self, g: HGraph, target, match, omega, delta):
+        """Best-effort pairing of the unmatched nodes without a target (match
+        updated in place); returns the number of new pairs."""
+        prm = Params(omega, delta, 0, 0)
+        npairs = ctypes.c_uint32()
+        self._check(self.lib.chp_pair_leftovers(self.h, ctypes.byref(g.c), ctypes.byref(prm),
+                                                _ptr(target), _ptr(match), ctypes.byref(npairs)),
+                    "pair_leftovers")
+        return int(npairs.value)
 
     def new_flags(self, g: HGraph):
         """A uint8 device tensor for g's invalid-neighbour flags."""

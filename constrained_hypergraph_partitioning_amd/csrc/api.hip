@@ -610,6 +610,8 @@ namespace {
 
 // Neighbour entries one batch may hold (oversize buffer and packed lists).
 constexpr u64 BATCH_ENTRIES = 3ull << 30;
+// Positions a leftover node scans below its slack position.
+constexpr u32 LEFT_WINDOW = 64;
 // Incident pins from which a node of such a graph is rated straight from the
 // incidence rather than through a neighbour list.
 constexpr u64 INC_MIN_VISITS = 16384;
@@ -808,6 +810,36 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
       read_many(c, {{&f, c->flags, sizeof f}, {n_pairs_host, npairs, sizeof(u32)}});
       if (f & FLAG_ECYCLE) fail_flags(c, FLAG_ECYCLE, "matching");
     }
+  });
+}
+
+int chp_pair_leftovers(chp_ctx *c, const chp_hgraph *g, const chp_params *prm,
+                       const u32 *target, u32 *match, u32 *n_pairs_host) {
+  return guarded(c, [&] {
+    if (!g || !prm || !n_pairs_host || (g->n_nodes && (!target || !match))) {
+      set_err(c, "%snull argument");
+      throw Fail{CHP_EINVAL};
+    }
+    *n_pairs_host = 0;
+    const u32 N = g->n_nodes;
+    if (N < 2) return;
+    Scratch s(c);
+    u64 *keys = s.get<u64>(N);
+    u64 *tmp = s.get<u64>(N);
+    u32 *claim = s.get<u32>(N);
+    u32 *choice = s.get<u32>(N);
+    u32 *cnt = s.get<u32>(2);  // gathered, pairs
+    launch_fills(c, {{cnt, 2, 0, false}, {claim, N, NONE32, false}});
+    launch_left_gather(c, N, target, match, g->n_size, keys, cnt);
+    launch_check(c, "leftover gather");
+    u32 nl = 0;
+    read_many(c, {{&nl, cnt, sizeof nl}});
+    if (nl < 2) return;
+    const u64 *sorted = sort_keys_u64(c, keys, tmp, nl);
+    launch_left_pair(c, nl, sorted, g->n_nin, prm->omega, prm->delta, LEFT_WINDOW, choice, claim,
+                     match, cnt + 1);
+    launch_check(c, "leftover pairing");
+    read_many(c, {{n_pairs_host, cnt + 1, sizeof(u32)}});
   });
 }
 

@@ -101,6 +101,17 @@ void launch_rate_classify(chp_ctx *c, const RateArgs &a, u32 lo, u32 hi, NbLists
                           NodeRec *recs, NodeRec *big);
 void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, const NodeRec *recs, u32 nrec,
                  const NodeRec *big, u32 *work);
+// Device-wide sort of n distinct u64 keys; tmp holds n; returns a or tmp.
+u64 *sort_keys_u64(chp_ctx *c, u64 *a, u64 *tmp, u64 n);
+
+// Best-effort pairing of the unmatched nodes without a target: gather their
+// keys (size << 32 | id) into keys (cnt zeroed before), then, once sorted,
+// choose, claim (claim[N] filled with NONE before) and pair into match.
+void launch_left_gather(chp_ctx *c, u32 N, const u32 *target, const u32 *match,
+                        const u32 *n_size, u64 *keys, u32 *cnt);
+void launch_left_pair(chp_ctx *c, u32 nl, const u64 *keys, const u32 *n_nin, u64 omega,
+                      u32 delta, u32 window, u32 *choice, u32 *claim, u32 *match, u32 *npairs);
+
 // Rating straight from the incidence (graphs without neighbour lists): the
 // classification lists the nodes of [0, a.N) with 1..384 incident hyperedges
 // and min_visits .. 2^27 - 1 incident pins, sets skip[n] for them and writes

@@ -161,6 +161,21 @@ int chp_rate_and_match(chp_ctx *ctx, const chp_hgraph *g, const chp_params *prm,
                        uint32_t *target, uint64_t *score_fx, uint32_t *match,
                        uint32_t *n_pairs_host, uint8_t *nb_invalid);
 
+/* pair_leftovers: best-effort pairing of the nodes left without a partner
+ * ([HP] Sec. V-C, last mechanism), run after chp_rate_and_match.
+ *  target[N]  as written by chp_rate_and_match (read).
+ *  match[N]   as written by chp_rate_and_match; updated in place: nodes with
+ *             target NONE and match[n] == n may be paired among themselves.
+ *  *n_pairs_host number of new pairs.
+ * Those nodes are sorted by (size, id).  Node n binary-searches the last
+ * position whose size fits omega - size(n), then takes the first node m != n
+ * within 64 positions below it with |in(n)| + |in(m)| <= delta (the union
+ * overestimated by the sum, so every pair is valid).  A node chosen by
+ * several goes to the smallest id; n pairs with its choice when it won it and
+ * nobody chose n.  Deterministic.  Errors: EINVAL.  Synchronises. */
+int chp_pair_leftovers(chp_ctx *ctx, const chp_hgraph *g, const chp_params *prm,
+                       const uint32_t *target, uint32_t *match, uint32_t *n_pairs_host);
+
 /* contract ([HP] Sec. III and V-E; [IC] Sec. III-B4).
  *  gamma[N]   coarse id of every node: the rank of min(n, match(n)) among
  *             the nodes with match(n) >= n.

@@ -45,7 +45,7 @@ def both(chp, ctx, h, omega, delta, neighbors=True):
 
 
 def multilevel(chp, ctx, h, omega, delta, noise_on, seed, max_levels, target_nodes=0,
-               eval_every=False, tag="", purge=False):
+               eval_every=False, tag="", purge=False, leftovers=False):
     dg, og = both(chp, ctx, h, omega, delta)
     rho = np.arange(h.n_nodes, dtype=np.uint32)
     og0, dg0 = og, dg
@@ -55,7 +55,8 @@ def multilevel(chp, ctx, h, omega, delta, noise_on, seed, max_levels, target_nod
         if og.n_nodes < target_nodes or og.n_nodes <= floor_nodes:
             break
         cg, lv, gamma = run_level_pair(chp, ctx, dg, og, omega, delta, noise_on, seed,
-                                       tag="%s L%d" % (tag, lvl), purge=purge)
+                                       tag="%s L%d" % (tag, lvl), purge=purge,
+                                       leftovers=leftovers)
         levels += 1
         if cg is None:
             break
@@ -265,6 +266,45 @@ def test_incidence_rating_hub_and_wide_span(chp, ctx):
     say("inc wide span")
     batched_levels(chp, ctx, h, 1 << 20, 1 << 20, 3, 1, 0, 1, 0, tag="inc wide")
     batched_levels(chp, ctx, h, 1 << 20, 1 << 20, 3, 1, 0, 1, 16, tag="inc wide hash16")
+
+
+@pytest.mark.parametrize("cfg,nn,levels", [(4, 20000, 12), (1, None, 8), (2, 5000, 10),
+                                           (3, 5000, 4)])
+def test_leftovers_multilevel(chp, ctx, cfg, nn, levels):
+    """Coarsening with the best-effort pairing of nodes left without a
+    partner (and the purge), every level against the oracle."""
+    spec = synth.config(cfg, n_nodes=nn)
+    h = synth.generate(spec)
+    say("leftovers", cfg, nn)
+    multilevel(chp, ctx, h, spec.omega, spec.delta, True, spec.seed, levels, tag="left%d" % cfg,
+               purge=True, leftovers=True)
+
+
+@pytest.mark.parametrize("n,p_none,seed", [(2, 1.0, 0), (3, 0.5, 1), (5000, 0.3, 2),
+                                            (200000, 1.0, 3), (300001, 0.7, 4)])
+def test_leftovers_random(chp, ctx, n, p_none, seed):
+    """Leftover pairing on its own: targets drawn at random (NONE with
+    probability p_none), some nodes already paired; sizes and inbound counts
+    from a VLSI-shaped graph (sizes 1..4).  200,000 and more leftovers take
+    several merge passes of the sort."""
+    spec = synth.config(4, n_nodes=n if n >= 64 else 64)
+    h = synth.generate(spec)
+    dg = ctx.build_incidence(*chp.upload_edges(h), spec.omega, spec.delta, False)
+    og = oracle.build_incidence(h.e_off, h.e_nsrc, h.e_pins, h.e_w, h.n_size, spec.omega,
+                                spec.delta, build_neighbors=False)
+    N = og.n_nodes
+    rng = np.random.Generator(np.random.PCG64(seed))
+    tgt = np.where(rng.random(N) < p_none, 0xFFFFFFFF, 0).astype(np.uint32)
+    match = np.arange(N, dtype=np.uint32)
+    idx = rng.permutation(N)[: (N // 10) * 2].reshape(-1, 2)
+    match[idx[:, 0]], match[idx[:, 1]] = idx[:, 1], idx[:, 0]
+    for omega, delta in ((spec.omega, spec.delta), (5, 6)):
+        say("leftovers random", n, p_none, omega, delta)
+        want, wk = oracle.pair_leftovers(tgt, match, og.n_size, og.n_nin, omega, delta)
+        dm = chp.to_device(match)
+        k = ctx.pair_leftovers(dg, chp.to_device(tgt), dm, omega, delta)
+        assert k == wk
+        assert_equal(chp.to_host(dm, np.uint32), want, "leftovers %d" % n)
 
 
 def test_tiny_graphs(chp, ctx):
