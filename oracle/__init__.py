@@ -78,6 +78,7 @@ def _load():
             "or_flags": [E, P, P, P, P, P, u64, u32, P],
             "or_purge": [u32, P, P, P, P, P, u32, P, ctypes.POINTER(P), ctypes.POINTER(u64)],
             "or_pair_leftovers": [u32, P, P, P, u64, u32, u32, P, ctypes.POINTER(u64)],
+            "or_moves": [E, P, P, P, u32, u64, i32, P, P],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -292,6 +293,18 @@ def purge(g: Graph, flag, match_arr, gamma, cg: Graph) -> Graph:
     cg.nb_off = off
     cg.nb = _take(ptr.value, tot.value, np.uint32)
     return cg
+
+
+def moves(g: Graph, rho, k, omega, enforce_omega=False):
+    """O12: (move[N] uint32, gain[N] int64) of Eq. 13 for partition rho."""
+    N = g.n_nodes
+    mv = np.empty(N, np.uint32)
+    gn = np.empty(N, np.int64)
+    v = g.view()
+    _check(_load().or_moves(ctypes.byref(v), _p(g.n_off), _p(g.n_inc),
+                            _p(np.ascontiguousarray(rho, np.uint32)), k, omega,
+                            1 if enforce_omega else 0, _p(mv), _p(gn)), "moves")
+    return mv, gn
 
 
 LEFTOVER_WINDOW = 64  # positions a leftover node scans below its slack position

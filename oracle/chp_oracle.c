@@ -768,3 +768,93 @@ int or_pair_leftovers(uint32_t N, const uint32_t *target, const uint32_t *n_size
   free(L), free(choice), free(claim);
   return OR_OK;
 }
+
+/*
+ * O12 -- refinement move proposal ([P1] Sec. VI-A/B, Eq. 13).
+ *   pins(p, e) = |{m in e : rho(m) = p}|,
+ *   saving(n)  = sum of w(e) over e in I(n) with pins(rho(n), e) = 1,
+ *   loss(n, p) = sum of w(e) over e in I(n) with pins(p, e) = 0,
+ *   gain(n, p) = saving(n) - loss(n, p),
+ *   move(n)    = the partition p != rho(n) of largest gain, ties to the
+ *                smallest id (the reading of the pages' tie rule used for
+ *                targets as well); with enforce_omega only partitions with
+ *                part_size(p) + size(n) <= Omega are considered.
+ * move[n] = NONE and gain[n] = 0 when no partition qualifies.  pins(p, e) is
+ * held per hyperedge as its sorted distinct partitions with their counts.
+ */
+static int cmp_u32b(const void *a, const void *b) {
+  uint32_t x = *(const uint32_t *)a, y = *(const uint32_t *)b;
+  return x < y ? -1 : (x > y ? 1 : 0);
+}
+
+/* pins(p, e) by binary search in e's sorted partition list */
+static uint32_t pins_of(const int64_t *poff, const uint32_t *ppart, const uint32_t *pcnt,
+                        uint32_t e, uint32_t p) {
+  int64_t lo = poff[e], hi = poff[e + 1];
+  while (lo < hi) {
+    int64_t mid = lo + (hi - lo) / 2;
+    if (ppart[mid] < p) lo = mid + 1;
+    else hi = mid;
+  }
+  return (lo < poff[e + 1] && ppart[lo] == p) ? pcnt[lo] : 0;
+}
+
+int or_moves(const or_edges *g, const int64_t *n_off, const uint32_t *n_inc, const uint32_t *rho,
+             uint32_t k, uint64_t omega, int enforce_omega, uint32_t *move, int64_t *gain) {
+  const uint32_t N = g->n_nodes, E = g->n_edges;
+  const int64_t P = g->e_off[E];
+  for (uint32_t n = 0; n < N; ++n)
+    if (rho[n] >= k) return OR_EINVAL;
+  int64_t *poff = (int64_t *)malloc(sizeof(int64_t) * ((size_t)E + 1));
+  uint32_t *ppart = (uint32_t *)malloc(sizeof(uint32_t) * (P ? (size_t)P : 1));
+  uint32_t *pcnt = (uint32_t *)malloc(sizeof(uint32_t) * (P ? (size_t)P : 1));
+  uint32_t *tmp = (uint32_t *)malloc(sizeof(uint32_t) * (P ? (size_t)P : 1));
+  uint64_t *psize = (uint64_t *)calloc(k ? k : 1, sizeof(uint64_t));
+  if (!poff || !ppart || !pcnt || !tmp || !psize) {
+    free(poff), free(ppart), free(pcnt), free(tmp), free(psize);
+    return OR_ENOMEM;
+  }
+  /* pins(., e): sort the partitions of e's pins, count equal runs */
+  int64_t w = 0;
+  for (uint32_t e = 0; e < E; ++e) {
+    poff[e] = w;
+    const int64_t a = g->e_off[e], b = g->e_off[e + 1];
+    for (int64_t i = a; i < b; ++i) tmp[i - a] = rho[g->e_pins[i]];
+    qsort(tmp, (size_t)(b - a), sizeof(uint32_t), cmp_u32b);
+    for (int64_t i = 0; i < b - a; ++i) {
+      if (i == 0 || tmp[i] != tmp[i - 1]) {
+        ppart[w] = tmp[i];
+        pcnt[w] = 0;
+        ++w;
+      }
+      pcnt[w - 1]++;
+    }
+  }
+  poff[E] = w;
+  for (uint32_t n = 0; n < N; ++n) psize[rho[n]] += g->n_size[n];
+  for (uint32_t n = 0; n < N; ++n) {
+    const uint32_t pn = rho[n];
+    int64_t saving = 0;
+    for (int64_t j = n_off[n]; j < n_off[n + 1]; ++j) {
+      const uint32_t e = n_inc[j];
+      if (pins_of(poff, ppart, pcnt, e, pn) == 1) saving += g->e_w[e];
+    }
+    uint32_t best = NONE;
+    int64_t best_gain = 0;
+    for (uint32_t p = 0; p < k; ++p) {
+      if (p == pn) continue;
+      if (enforce_omega && psize[p] + g->n_size[n] > omega) continue;
+      int64_t loss = 0;
+      for (int64_t j = n_off[n]; j < n_off[n + 1]; ++j) {
+        const uint32_t e = n_inc[j];
+        if (pins_of(poff, ppart, pcnt, e, p) == 0) loss += g->e_w[e];
+      }
+      const int64_t gp = saving - loss;
+      if (best == NONE || gp > best_gain) best = p, best_gain = gp;
+    }
+    move[n] = best;
+    gain[n] = best == NONE ? 0 : best_gain;
+  }
+  free(poff), free(ppart), free(pcnt), free(tmp), free(psize);
+  return OR_OK;
+}

@@ -215,3 +215,30 @@ def evaluate(n_nodes, edges, weights, sizes, rho, k):
             part_inb[p] += 1
     empty = sum(1 for c in count if c == 0)
     return conn, cut, part_size, part_inb, empty
+
+
+def moves(n_nodes, edges, weights, sizes, rho, k, omega, enforce_omega):
+    """Eq. 13 by sets: pins(p, e) counted over e's members, every partition
+    tried, ties to the smallest partition id."""
+    members = [set(s) | set(d) for s, d in edges]
+    inc = [[e for e in range(len(edges)) if n in members[e]] for n in range(n_nodes)]
+    psize = [0] * k
+    for n in range(n_nodes):
+        psize[rho[n]] += int(sizes[n])
+
+    def pins(p, e):
+        return sum(1 for m in members[e] if rho[m] == p)
+
+    mv, gn = [], []
+    for n in range(n_nodes):
+        saving = sum(int(weights[e]) for e in inc[n] if pins(rho[n], e) == 1)
+        best, bg = None, 0
+        for p in range(k):
+            if p == rho[n] or (enforce_omega and psize[p] + int(sizes[n]) > omega):
+                continue
+            loss = sum(int(weights[e]) for e in inc[n] if pins(p, e) == 0)
+            if best is None or saving - loss > bg:
+                best, bg = p, saving - loss
+        mv.append(0xFFFFFFFF if best is None else best)
+        gn.append(0 if best is None else bg)
+    return mv, gn

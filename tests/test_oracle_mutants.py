@@ -47,6 +47,14 @@ MUTANTS = {
     "leftover_claimed_pairs_too": ("if (m != NONE && claim[m] == n && claim[n] == NONE) {",
                                    "if (m != NONE && claim[m] == n) {"),
     "leftover_delta_ignored": ("if ((uint64_t)n_nin[n] + n_nin[m] <= delta) {", "if (1) {"),
+    "moves_loss_counts_one_pin": ("if (pins_of(poff, ppart, pcnt, e, p) == 0) loss += g->e_w[e];",
+                                  "if (pins_of(poff, ppart, pcnt, e, p) <= 1) loss += g->e_w[e];"),
+    "moves_saving_any_pin": ("if (pins_of(poff, ppart, pcnt, e, pn) == 1) saving += g->e_w[e];",
+                             "if (pins_of(poff, ppart, pcnt, e, pn) >= 1) saving += g->e_w[e];"),
+    "moves_tie_largest_id": ("if (best == NONE || gp > best_gain) best = p, best_gain = gp;",
+                             "if (best == NONE || gp >= best_gain) best = p, best_gain = gp;"),
+    "moves_omega_without_node": ("if (enforce_omega && psize[p] + g->n_size[n] > omega) continue;",
+                                 "if (enforce_omega && psize[p] > omega) continue;"),
 }
 
 
@@ -67,6 +75,11 @@ def _checks():
     pins.test_leftovers_only_unmatched_without_target()
     for seed in range(6):
         pins.test_leftovers_invariants(seed)
+    pins.test_moves_hand_example()
+    for kw in pins.tiny_cases()[:24:2]:
+        pins.test_moves_vs_brute(kw)
+    for seed in range(3):
+        pins.test_moves_identity_partition(seed)
 
 
 def _build_mutant(name, tmpdir):

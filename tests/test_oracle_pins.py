@@ -575,3 +575,70 @@ def test_leftovers_multilevel_invariants():
                 continue
             assert int(lv.coarse.n_size.max()) <= spec.omega
             assert int(lv.coarse.n_nin.max()) <= spec.delta
+
+
+# ---- O12: refinement move proposal, Eq. 13 ([HP] Sec. VI-A/B)
+def _hand_moves_graph():
+    # e0: 0 -> {1, 2} weight 2; e1: 1 -> {3} weight 5
+    return synth.from_lists(4, [([0], [1, 2]), ([1], [3])], weights=[2, 5])
+
+
+def test_moves_hand_example():
+    """Worked by hand: rho = [0, 0, 1, 1].  Node 1 leaves e1 with no pin in
+    partition 0 (saving 5) and joins partition 1, where both hyperedges
+    already have pins (loss 0); node 0 saves nothing; nodes 2 and 3 save 2 and
+    5 and lose nothing in partition 0."""
+    h = _hand_moves_graph()
+    g = load(h)
+    mv, gn = oracle.moves(g, np.array([0, 0, 1, 1], np.uint32), 2, BIG)
+    assert mv.tolist() == [1, 1, 0, 0] and gn.tolist() == [0, 5, 2, 5]
+    # an empty third partition: worse for everyone (it holds no pin)
+    mv, gn = oracle.moves(g, np.array([0, 0, 1, 1], np.uint32), 3, BIG)
+    assert mv.tolist() == [1, 1, 0, 0] and gn.tolist() == [0, 5, 2, 5]
+    # Omega 2 with unit sizes: partitions 0 and 1 are full, only 2 is allowed
+    mv, gn = oracle.moves(g, np.array([0, 0, 1, 1], np.uint32), 3, 2, enforce_omega=True)
+    assert mv.tolist() == [2, 2, 2, 2] and gn.tolist() == [-2, -2, 0, 0]
+    # a single partition: nowhere to go
+    mv, gn = oracle.moves(g, np.zeros(4, np.uint32), 1, BIG)
+    assert mv.tolist() == [0xFFFFFFFF] * 4 and gn.tolist() == [0] * 4
+
+
+@pytest.mark.parametrize("kw", tiny_cases()[::2], ids=lambda k: "s%d" % k["seed"])
+def test_moves_vs_brute(kw):
+    h = synth.tiny(**kw)
+    edges = brute.edges_of(h.e_off, h.e_nsrc, h.e_pins)
+    g = load(h)
+    for k in (1, 2, 3, h.n_nodes):
+        rho = synth.uniform_u32(kw["seed"], 41, h.n_nodes, k)
+        psize = np.bincount(rho, weights=h.n_size, minlength=k)
+        for enforce, omega in ((False, BIG), (True, int(psize.max()) + 1), (True, 3)):
+            mv, gn = oracle.moves(g, rho, k, omega, enforce)
+            bm, bg = brute.moves(h.n_nodes, edges, h.e_w, h.n_size, rho.tolist(), k, omega,
+                                 enforce)
+            assert mv.tolist() == bm and gn.tolist() == bg
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_moves_identity_partition(seed):
+    """Closed form: with every node alone (rho(n) = n), saving(n) is the whole
+    weight of I(n), and the gain of joining m is the weight n and m share, so
+    the move is the neighbour of largest shared weight (smallest id on ties),
+    or, with no neighbour, the smallest other id at gain 0."""
+    kw = tiny_cases()[seed * 7 % 60]
+    h = synth.tiny(**kw)
+    edges = brute.edges_of(h.e_off, h.e_nsrc, h.e_pins)
+    n = h.n_nodes
+    g = load(h)
+    mv, gn = oracle.moves(g, np.arange(n, dtype=np.uint32), n, BIG)
+    members = [set(s) | set(d) for s, d in edges]
+    for v in range(n):
+        shared = {}
+        for e, mem in enumerate(members):
+            if v in mem:
+                for m in mem - {v}:
+                    shared[m] = shared.get(m, 0) + int(h.e_w[e])
+        if shared:
+            best = max(shared.items(), key=lambda kv: (kv[1], -kv[0]))
+            assert (int(mv[v]), int(gn[v])) == best
+        else:
+            assert (int(mv[v]), int(gn[v])) == (0 if v else 1, 0)
