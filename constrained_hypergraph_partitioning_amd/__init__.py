@@ -31,7 +31,8 @@ _NAMES = {EINVAL: "EINVAL", ENOMEM: "ENOMEM", EOVERFLOW: "EOVERFLOW",
 EXPORTS = ["chp_create", "chp_destroy", "chp_last_error", "chp_build_incidence",
            "chp_rate_and_match", "chp_contract", "chp_evaluate_partition", "chp_hgraph_free",
            "chp_set_timing", "chp_get_timings", "chp_reset_timings", "chp_set_batch_entries",
-           "chp_last_rate_stats", "chp_set_incidence_rating", "chp_pair_leftovers"]
+           "chp_last_rate_stats", "chp_set_incidence_rating", "chp_pair_leftovers",
+           "chp_propose_moves"]
 
 
 class ChpError(RuntimeError):
@@ -106,6 +107,9 @@ def load_library(path: str = LIB_PATH):
                                         ctypes.POINTER(ctypes.c_uint32),
                                         ctypes.POINTER(ctypes.c_uint32)]
     lib.chp_last_rate_stats.restype = I
+    lib.chp_propose_moves.argtypes = [P, ctypes.POINTER(HGraphC), P, ctypes.c_uint32,
+                                      ctypes.POINTER(Params), I, P, P]
+    lib.chp_propose_moves.restype = I
     lib.chp_pair_leftovers.argtypes = [P, ctypes.POINTER(HGraphC), ctypes.POINTER(Params), P, P,
                                        ctypes.POINTER(ctypes.c_uint32)]
     lib.chp_pair_leftovers.restype = I
@@ -310,6 +314,17 @@ class Context:
                                                 _ptr(flags) if flags is not None else None),
                     "rate_and_match")
         return target, score, match, int(npairs.value)
+
+    def propose_moves(self, g: HGraph, rho, k, omega, enforce_omega=False):
+        """Eq. 13 move proposal for partition rho: (move int32, gain int64)."""
+        N = g.n_nodes
+        move = torch.empty(max(N, 1), dtype=torch.int32, device=self.device)
+        gain = torch.empty(max(N, 1), dtype=torch.int64, device=self.device)
+        prm = Params(omega, 0, 0, 0)
+        self._check(self.lib.chp_propose_moves(self.h, ctypes.byref(g.c), _ptr(rho), int(k),
+                                               ctypes.byref(prm), 1 if enforce_omega else 0,
+                                               _ptr(move), _ptr(gain)), "propose_moves")
+        return move[:N], gain[:N]
 
     def pair_leftovers(self, g: HGraph, target, match, omega, delta):
         """Best-effort pairing of the unmatched nodes without a target (match

@@ -813,6 +813,62 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
   });
 }
 
+int chp_propose_moves(chp_ctx *c, const chp_hgraph *g, const u32 *rho, u32 k,
+                      const chp_params *prm, int enforce_omega, u32 *move, i64 *gain) {
+  return guarded(c, [&] {
+    if (!g || !prm || (g->n_nodes && (!rho || !move || !gain))) {
+      set_err(c, "%snull argument");
+      throw Fail{CHP_EINVAL};
+    }
+    const u32 N = g->n_nodes, E = g->n_edges;
+    if (N == 0) return;
+    if (k == 0) {
+      set_err(c, "%sk must be positive");
+      throw Fail{CHP_EINVAL};
+    }
+    Scratch s(c);
+    clear_flags(c);
+    u64 *part_size = s.get<u64>(k);
+    u32 *part_cnt = s.get<u32>(k);
+    u32 *cnt = s.get<u32>(2);
+    launch_fills(c, {{part_size, k, 0, true}, {part_cnt, k, 0, false}, {cnt, 2, 0, false}});
+    launch_eval_nodes(c, N, rho, k, g->n_size, part_size, part_cnt);
+    // pins(., e) of every hyperedge
+    u32 hc[8];
+    EdgeLists el = make_edge_lists(c, s, E, g->e_off, hc);
+    u64 *pl = s.get<u64>(g->n_pins ? g->n_pins : 1);
+    u32 *lam = s.get<u32>(E ? E : 1);
+    u64 *scr = nullptr;
+    u64 per_wg = 0;
+    const u32 gb = grid_big_for(hc[2]);
+    if (hc[2]) {
+      per_wg = 2ull * hc[3];
+      scr = s.get<u64>(per_wg * gb);
+    }
+    launch_pins_lists(c, g->e_off, g->e_pins, rho, k, pl, lam, el, hc, scr, per_wg, gb);
+    // admissible partitions (Omega enforced)
+    u32 K2 = 1;
+    while (K2 < k) K2 <<= 1;
+    u64 *tree = nullptr;
+    if (enforce_omega) {
+      tree = s.get<u64>(2ull * K2);
+      launch_free_tree(c, k, K2, part_size, prm->omega, tree);
+    }
+    u32 *lists = s.get<u32>(N);
+    launch_gains(c, N, k, K2, enforce_omega, prm->omega, g->e_off, g->e_w, pl, lam, g->n_off,
+                 g->n_inc, g->n_size, rho, part_size, tree, move, gain, lists, cnt, nullptr);
+    launch_check(c, "move classes");
+    u32 gc[2], f;
+    read_many(c, {{gc, cnt, sizeof gc}, {&f, c->flags, sizeof f}});
+    if (f & FLAG_EINVAL) fail_flags(c, FLAG_EINVAL, "rho has an entry >= k");
+    launch_gains(c, N, k, K2, enforce_omega, prm->omega, g->e_off, g->e_w, pl, lam, g->n_off,
+                 g->n_inc, g->n_size, rho, part_size, tree, move, gain, lists, cnt, gc);
+    launch_check(c, "moves");
+    read_many(c, {{&f, c->flags, sizeof f}});
+    if (f & FLAG_EINVAL) fail_flags(c, FLAG_EINVAL, "rho has an entry >= k");
+  });
+}
+
 int chp_pair_leftovers(chp_ctx *c, const chp_hgraph *g, const chp_params *prm,
                        const u32 *target, u32 *match, u32 *n_pairs_host) {
   return guarded(c, [&] {

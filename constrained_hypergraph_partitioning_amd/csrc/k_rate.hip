@@ -245,13 +245,6 @@ union RateSmem {
   LightWave l[RW];
 };
 
-// LDS writes of this wave become visible to its other lanes
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
 __device__ __forceinline__ u32 hslot(u32 m, u32 shift) { return (m * 0x9E3779B1u) >> shift; }
 
 // Insert the ids m[0, UNR) (EMPTY = none; all distinct and absent) with

@@ -101,6 +101,21 @@ void launch_rate_classify(chp_ctx *c, const RateArgs &a, u32 lo, u32 hi, NbLists
                           NodeRec *recs, NodeRec *big);
 void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, const NodeRec *recs, u32 nrec,
                  const NodeRec *big, u32 *work);
+// Refinement move proposal: pins(., e) lists (pl[P] packed p << 32 | count in
+// each hyperedge's pin range, lam[E] their lengths), the free-capacity
+// max-tree over K2 (a power of two >= k) leaves, and the per-node gains
+// (launch_gains with host_cnt null classifies into lists / cnt, zeroed
+// before; then again with the host copy of cnt).
+void launch_pins_lists(chp_ctx *c, const i64 *e_off, const u32 *pins, const u32 *rho, u32 k,
+                       u64 *pl, u32 *lam, EdgeLists el, const u32 *host_cnt, u64 *scratch,
+                       u64 per_wg, u32 grid_big);
+void launch_free_tree(chp_ctx *c, u32 k, u32 K2, const u64 *part_size, u64 omega, u64 *tree);
+void launch_gains(chp_ctx *c, u32 N, u32 k, u32 K2, int enforce, u64 omega, const i64 *e_off,
+                  const u32 *e_w, const u64 *pl, const u32 *lam, const i64 *n_off,
+                  const u32 *n_inc, const u32 *n_size, const u32 *rho, const u64 *part_size,
+                  const u64 *tree, u32 *move, i64 *gain, u32 *lists, u32 *cnt,
+                  const u32 *host_cnt);
+
 // Device-wide sort of n distinct u64 keys; tmp holds n; returns a or tmp.
 u64 *sort_keys_u64(chp_ctx *c, u64 *a, u64 *tmp, u64 n);
 

@@ -161,6 +161,20 @@ int chp_rate_and_match(chp_ctx *ctx, const chp_hgraph *g, const chp_params *prm,
                        uint32_t *target, uint64_t *score_fx, uint32_t *match,
                        uint32_t *n_pairs_host, uint8_t *nb_invalid);
 
+/* propose_moves: refinement move proposal ([HP] Sec. VI-A/B, Eq. 13) for the
+ * partition rho[N] in [0, k).  With pins(p, e) the pins of e in partition p:
+ *  saving(n)  = sum of w(e), e in I(n), pins(rho(n), e) == 1;
+ *  loss(n, p) = sum of w(e), e in I(n), pins(p, e) == 0;
+ *  move[N]    the p != rho(n) of largest saving(n) - loss(n, p), ties to the
+ *             smallest p; with enforce_omega != 0 only partitions whose size
+ *             plus size(n) stays within prm->omega; CHP_NONE if there is none
+ *             (k == 1, or every other partition full);
+ *  gain[N]    saving(n) - loss(n, move(n)) (int64), 0 with no move.
+ * Only prm->omega is read.  Errors: EINVAL (k == 0, or some rho[n] >= k).
+ * Synchronises. */
+int chp_propose_moves(chp_ctx *ctx, const chp_hgraph *g, const uint32_t *rho, uint32_t k,
+                      const chp_params *prm, int enforce_omega, uint32_t *move, int64_t *gain);
+
 /* pair_leftovers: best-effort pairing of the nodes left without a partner
  * ([HP] Sec. V-C, last mechanism), run after chp_rate_and_match.
  *  target[N]  as written by chp_rate_and_match (read).

@@ -307,6 +307,59 @@ def test_leftovers_random(chp, ctx, n, p_none, seed):
         assert_equal(chp.to_host(dm, np.uint32), want, "leftovers %d" % n)
 
 
+def moves_pair(chp, ctx, dg, og, rho, k, omega, enforce, tag):
+    mv, gn = ctx.propose_moves(dg, chp.to_device(rho), k, omega, enforce)
+    omv, ogn = oracle.moves(og, rho, k, omega, enforce)
+    assert_equal(chp.to_host(mv, np.uint32), omv, tag + " move")
+    assert_equal(chp.to_host(gn, np.uint64).view(np.int64), ogn, tag + " gain")
+
+
+def test_moves_tiny(chp, ctx):
+    """Eq. 13 moves on the brute-force-pinned tiny graphs, several k, with
+    and without Omega."""
+    import test_oracle_pins as pins
+    for kw in pins.tiny_cases():
+        h = synth.tiny(**kw)
+        say("moves tiny", kw["seed"])
+        dg, og = both(chp, ctx, h, 1 << 30, 1 << 30, neighbors=False)
+        for k in (1, 2, 3, h.n_nodes):
+            rho = synth.uniform_u32(kw["seed"], 41, h.n_nodes, k)
+            psize = np.bincount(rho, weights=h.n_size, minlength=k)
+            for enforce, omega in ((False, 1 << 30), (True, int(psize.max()) + 1), (True, 3)):
+                moves_pair(chp, ctx, dg, og, rho, k, omega, enforce, "tiny%d k%d" % (kw["seed"], k))
+
+
+@pytest.mark.parametrize("cfg,nn,k,slack", [(1, None, 200, 2), (2, 20000, 64, 0),
+                                            (2, 20000, 9000, 3), (3, 10000, 400, 1),
+                                            (4, 30000, 3000, 1), (5, 8192, 50, 1)])
+def test_moves_scaled(chp, ctx, cfg, nn, k, slack):
+    """Scaled workloads under a random partition into k parts (light nodes on
+    the wave path, nodes whose hyperedges touch many parts on the workgroup
+    path, k above one direct window of 4096), with and without Omega (set so
+    that the fullest parts cannot take a node)."""
+    spec = synth.config(cfg, n_nodes=nn)
+    h = synth.generate(spec)
+    say("moves", cfg, nn, k)
+    dg, og = both(chp, ctx, h, spec.omega, spec.delta, neighbors=False)
+    rho = synth.uniform_u32(cfg, 43, h.n_nodes, k)
+    psize = np.bincount(rho, weights=h.n_size, minlength=k)
+    omega = int(np.percentile(psize, 70)) + slack
+    for enforce, om in ((False, 1 << 40), (True, omega)):
+        moves_pair(chp, ctx, dg, og, rho, k, om, enforce, "cfg%d k%d" % (cfg, k))
+
+
+def test_moves_identity_and_one_part(chp, ctx):
+    """Every node alone (k = N: each hyperedge touches |e| parts) and a single
+    part (no move anywhere)."""
+    spec = synth.config(2, n_nodes=3000)
+    h = synth.generate(spec)
+    dg, og = both(chp, ctx, h, spec.omega, spec.delta, neighbors=False)
+    say("moves identity")
+    moves_pair(chp, ctx, dg, og, np.arange(h.n_nodes, dtype=np.uint32), h.n_nodes, 1 << 30,
+               False, "identity")
+    moves_pair(chp, ctx, dg, og, np.zeros(h.n_nodes, np.uint32), 1, 1 << 30, False, "one part")
+
+
 def test_tiny_graphs(chp, ctx):
     import test_oracle_pins as pins
     for kw in pins.tiny_cases():
