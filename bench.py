@@ -37,6 +37,10 @@ PURGE = True
 # Nodes left without a partner are paired best-effort, as the pages'
 # coarsening does (--no-leftovers turns it off).
 LEFTOVERS = True
+# The driver stops after a level that pairs fewer than this fraction of its
+# nodes (a stalled coarsening: each further level would cost a full pass for a
+# handful of pairs).
+MIN_PAIR_FRAC = 0.001
 RATE_SOURCE = os.path.join(ROOT, "constrained_hypergraph_partitioning_amd", "csrc", "k_rate.hip")
 COUNTERS_JSON = os.path.join(ROOT, "profiles", "rating_counters.json")
 COPY_REF_MIB = 256
@@ -58,6 +62,9 @@ def parse():
                    help="build the graph without neighbour lists even where they fit")
     p.add_argument("--progress", action="store_true",
                    help="print a line per timed step to stderr (long workloads)")
+    p.add_argument("--moves", action="store_true",
+                   help="also time the refinement move proposal (Eq. 13) on the input graph "
+                        "under the step's projected partition, Omega enforced")
     p.add_argument("--no-leftovers", action="store_true",
                    help="do not pair the nodes left without a partner")
     p.add_argument("--no-purge", action="store_true",
@@ -156,9 +163,12 @@ def run_step(chp, ctx, dev_edges, spec, rho_buf, with_nb=True):
             break
         gamma, cg = ctx.contract(g, match, with_nb, flags=flags)
         rho = gamma.long() if rho is None else gamma.long()[rho]
+        stalled = npairs < MIN_PAIR_FRAC * g.n_nodes
         if g is not g0:
             g.free()
         g = cg
+        if stalled:
+            break
     k = g.n_nodes
     if rho is None:
         rho = torch.arange(g0.n_nodes, device=ctx.device)
@@ -300,9 +310,36 @@ def main():
         "dominant_kernel": dom[0],
         "cpu_baseline": None,
     }
+    if args.moves:
+        out["moves"] = time_moves(ctx, dev_edges, spec, rho_buf, out["config"]["final_nodes"], h)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(h, spec, args.workload, args.cpu_sample_nodes)
     print(json.dumps(out))
+
+
+def time_moves(ctx, dev_edges, spec, rho_buf, k, h, reps=5):
+    """The Eq. 13 move proposal on the input graph under the projected
+    partition of the last step (k parts), Omega enforced: ms per call (HIP
+    events of the library, synchronised calls) and pins per second."""
+    import torch
+    g0 = ctx.build_incidence(*dev_edges, spec.omega, spec.delta, False)
+    ctx.propose_moves(g0, rho_buf, k, spec.omega, True)
+    torch.cuda.synchronize()
+    ctx.reset_timings()
+    ctx.set_timing(True)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        mv, gn = ctx.propose_moves(g0, rho_buf, k, spec.omega, True)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    tm = ctx.timings()
+    ctx.set_timing(False)
+    improving = int((gn > 0).sum().item())
+    g0.free()
+    return {"parts": k, "ms_per_call": dt * 1e3, "pins_per_s": h.n_pins / dt,
+            "improving_moves": improving,
+            "kernel_ms_per_call": {kk: round(v[1] / reps, 4) for kk, v in
+                                   sorted(tm.items(), key=lambda kv: -kv[1][1])[:8]}}
 
 
 def rate_level_bytes(levels, h, spec):

@@ -830,8 +830,8 @@ int chp_propose_moves(chp_ctx *c, const chp_hgraph *g, const u32 *rho, u32 k,
     clear_flags(c);
     u64 *part_size = s.get<u64>(k);
     u32 *part_cnt = s.get<u32>(k);
-    u32 *cnt = s.get<u32>(2);
-    launch_fills(c, {{part_size, k, 0, true}, {part_cnt, k, 0, false}, {cnt, 2, 0, false}});
+    u32 *cnt = s.get<u32>(3);  // light, heavy, heavy work counter
+    launch_fills(c, {{part_size, k, 0, true}, {part_cnt, k, 0, false}, {cnt, 3, 0, false}});
     launch_eval_nodes(c, N, rho, k, g->n_size, part_size, part_cnt);
     // pins(., e) of every hyperedge
     u32 hc[8];

@@ -15,7 +15,8 @@
 // best move is the touched admissible p of largest conn, else the smallest
 // admissible untouched p.  A light node (at most 384 list entries over its
 // hyperedges) takes a wave and an LDS hash over the partitions it touches;
-// a heavy one a workgroup and direct-mapped windows of 4096 partition ids.
+// a heavy one a workgroup and a larger hash (up to 3072 list entries), or,
+// beyond that, direct-mapped windows of 4096 partition ids.
 #include "dev.h"
 #include "kernels.h"
 
@@ -340,7 +341,66 @@ __device__ void gain_light(const GainArgs &G, GainWave &S, u32 n) {
 }
 
 constexpr int GB = 256;
-constexpr u32 GD = 4096;  // partition ids per direct window, heavy path
+constexpr u32 GD = 4096;    // partition ids per direct window, largest nodes
+constexpr u32 GM_T = 4096;  // hash slots, heavy nodes
+constexpr u32 GM_CAP = 3072;  // list entries a heavy node may bring to the hash
+
+__device__ __forceinline__ u32 gm_slot(u32 p) { return (p * 0x9E3779B1u) >> 20; }
+
+struct GainWg {
+  u64 conn[GM_T];  // the hash's counters, or a direct window over GD ids
+  u32 key[GM_T];   // p + 1, 0 = empty (hash only)
+  u64 red64[GB / WAVE];
+  u64 rede[GB / WAVE];
+  u32 redi[GB / WAVE];
+  u32 ans, item;
+};
+constexpr u32 GH_PER_CU = 3;  // workgroups of k_gain_heavy that fit a CU's LDS
+static_assert(GH_PER_CU * sizeof(GainWg) <= 160 * 1024, "LDS");
+static_assert(GD <= GM_T, "direct window in the hash's counters");
+
+__device__ __forceinline__ void gm_add(GainWg &S, u32 p, u64 w) {
+  u32 s = gm_slot(p);
+  for (;;) {
+    const u32 cur = S.key[s];
+    if (cur == p + 1) break;
+    if (cur == 0) {
+      const u32 old = atomicCAS(&S.key[s], 0u, p + 1);
+      if (old == 0 || old == p + 1) break;
+    }
+    s = (s + 1) & (GM_T - 1);
+  }
+  atomicAdd((unsigned long long *)&S.conn[s], (unsigned long long)w);
+}
+
+__device__ __forceinline__ bool gm_has(const GainWg &S, u32 p) {
+  u32 s = gm_slot(p);
+  for (;;) {
+    const u32 cur = S.key[s];
+    if (cur == p + 1) return true;
+    if (cur == 0) return false;
+    s = (s + 1) & (GM_T - 1);
+  }
+}
+
+__device__ __forceinline__ void wg_best_reduce(GainWg &S, u64 &be, u32 &bp) {
+#pragma unroll
+  for (int d = WAVE / 2; d > 0; d >>= 1) {
+    const u64 oe = __shfl_xor(be, d, WAVE);
+    const u32 oi = __shfl_xor(bp, d, WAVE);
+    if (better(oe, oi, be, bp)) be = oe, bp = oi;
+  }
+  if (lane_id() == 0) {
+    S.rede[wave_id()] = be;
+    S.redi[wave_id()] = bp;
+  }
+  __syncthreads();
+  be = S.rede[0];
+  bp = S.redi[0];
+  for (int v = 1; v < GB / WAVE; ++v)
+    if (better(S.rede[v], S.redi[v], be, bp)) be = S.rede[v], bp = S.redi[v];
+  __syncthreads();
+}
 
 __global__ __launch_bounds__(GB) void k_gain_light(GainArgs G, const u32 *lists,
                                                     const u32 *cnt) {
@@ -357,34 +417,43 @@ __global__ __launch_bounds__(GB) void k_gain_light(GainArgs G, const u32 *lists,
     gain_light(G, S, lists[w]);
 }
 
+// A workgroup per node: list entries into the LDS hash when they number at
+// most GM_CAP (then the untouched fallback as on the light path, by wave 0),
+// otherwise direct windows of GD partition ids over [0, k), each scanned in
+// full (touched or not).
+// Nodes are taken from a counter (their costs vary widely); the item is a
+// scalar and the loop body ends with a barrier.
 __global__ __launch_bounds__(GB) void k_gain_heavy(GainArgs G, const u32 *lists,
-                                                    const u32 *cnt) {
-  __shared__ u64 conn[GD];
-  __shared__ u64 red64[GB / WAVE];
-  __shared__ u64 rede[GB / WAVE];
-  __shared__ u32 redi[GB / WAVE];
+                                                    const u32 *cnt, u32 *work) {
+  __shared__ GainWg S;
   const u32 tid = threadIdx.x;
   const u32 total = cnt[1];
-  for (u32 w = blockIdx.x; w < total; w += gridDim.x) {
+  for (u32 s = tid; s < GM_T; s += GB) {
+    S.key[s] = 0;
+    S.conn[s] = 0;
+  }
+  for (;;) {
+    if (tid == 0) S.item = atomicAdd(work, 1u);
+    __syncthreads();
+    const u32 w = __builtin_amdgcn_readfirstlane(S.item);
+    if (w >= total) break;
     const u32 n = lists[G.N - 1 - w];
     const u32 pn = G.rho[n];
     const u64 size_n = G.n_size[n];
     const i64 i0 = G.n_off[n], i1 = G.n_off[n + 1];
-    u64 W = 0, saving = 0;
+    u64 W = 0, saving = 0, ent = 0;
     for (i64 j = i0 + tid; j < i1; j += GB) {
       const u32 e = G.n_inc[j];
       W += G.e_w[e];
+      ent += G.lam[e];
       if (pins_in(G, e, pn) == 1) saving += G.e_w[e];
     }
-    W = wg_sum<GB>(W, red64);
-    saving = wg_sum<GB>(saving, red64);
+    W = wg_sum<GB>(W, S.red64);
+    saving = wg_sum<GB>(saving, S.red64);
+    ent = wg_sum<GB>(ent, S.red64);
     u64 be = 0;
     u32 bp = NONE32;
-    for (u32 lo = 0; lo < G.k; lo += GD) {
-      const u32 hi = G.k - lo < GD ? G.k : lo + GD;
-      for (u32 s = tid; s < GD; s += GB) conn[s] = 0;
-      __syncthreads();
-      // every list entry of every incident hyperedge, a wave per hyperedge
+    if (ent <= GM_CAP) {
       for (i64 j = i0 + wave_id(); j < i1; j += GB / WAVE) {
         const u32 e = G.n_inc[j];
         const i64 a = G.e_off[e];
@@ -392,35 +461,76 @@ __global__ __launch_bounds__(GB) void k_gain_heavy(GainArgs G, const u32 *lists,
         const u64 we = G.e_w[e];
         for (u32 t = lane_id(); t < lm; t += WAVE) {
           const u32 p = (u32)(G.pl[a + t] >> 32);
-          if (p >= lo && p < hi && p != pn)
-            atomicAdd((unsigned long long *)&conn[p - lo], (unsigned long long)we);
+          if (p != pn) gm_add(S, p, we);
         }
       }
       __syncthreads();
-      // every partition of the window, touched or not
-      for (u32 p = lo + tid; p < hi; p += GB) {
-        const u64 cv = conn[p - lo];
-        if (p != pn && admissible(G, p, size_n) && better(cv, p, be, bp)) {
-          be = cv;
-          bp = p;
+      for (u32 s = tid; s < GM_T; s += GB) {
+        const u32 key = S.key[s];
+        if (key && admissible(G, key - 1, size_n) && better(S.conn[s], key - 1, be, bp)) {
+          be = S.conn[s];
+          bp = key - 1;
         }
       }
+      wg_best_reduce(S, be, bp);
+      if (bp == NONE32 && wave_id() == 0) {
+        // the smallest admissible partition no hyperedge of n touches
+        const u32 l = lane_id();
+        u32 found = NONE32, x = 0;
+        for (;;) {
+          if (G.enforce) x = first_free(G.tree, G.K2, x, size_n);
+          if (x == NONE32 || x >= G.k) break;
+          const u32 p = x + l;
+          const bool ok = p < G.k && p != pn && admissible(G, p, size_n) && !gm_has(S, p);
+          const u64 b = __ballot(ok);
+          if (b) {
+            found = x + (u32)__builtin_ctzll(b);
+            break;
+          }
+          if (x > 0xFFFFFFFFu - WAVE) break;
+          x += WAVE;
+        }
+        if (l == 0) S.ans = found;
+      }
       __syncthreads();
+      for (u32 s = tid; s < GM_T; s += GB) {
+        S.key[s] = 0;
+        S.conn[s] = 0;
+      }
+      if (bp == NONE32) {
+        bp = S.ans;
+        be = 0;
+      }
+    } else {
+      for (u32 lo = 0; lo < G.k; lo += GD) {
+        const u32 hi = G.k - lo < GD ? G.k : lo + GD;
+        // every list entry of every incident hyperedge, a wave per hyperedge
+        for (i64 j = i0 + wave_id(); j < i1; j += GB / WAVE) {
+          const u32 e = G.n_inc[j];
+          const i64 a = G.e_off[e];
+          const u32 lm = G.lam[e];
+          const u64 we = G.e_w[e];
+          for (u32 t = lane_id(); t < lm; t += WAVE) {
+            const u32 p = (u32)(G.pl[a + t] >> 32);
+            if (p >= lo && p < hi && p != pn)
+              atomicAdd((unsigned long long *)&S.conn[p - lo], (unsigned long long)we);
+          }
+        }
+        __syncthreads();
+        // every partition of the window, touched or not; the window is left empty
+        for (u32 p = lo + tid; p < lo + GD; p += GB) {
+          const u64 cv = S.conn[p - lo];
+          S.conn[p - lo] = 0;
+          if (p < hi && p != pn && admissible(G, p, size_n) && better(cv, p, be, bp)) {
+            be = cv;
+            bp = p;
+          }
+        }
+        __syncthreads();
+      }
+      wg_best_reduce(S, be, bp);
     }
-#pragma unroll
-    for (int d = WAVE / 2; d > 0; d >>= 1) {
-      const u64 oe = __shfl_xor(be, d, WAVE);
-      const u32 oi = __shfl_xor(bp, d, WAVE);
-      if (better(oe, oi, be, bp)) be = oe, bp = oi;
-    }
-    if (lane_id() == 0) {
-      rede[wave_id()] = be;
-      redi[wave_id()] = bp;
-    }
-    __syncthreads();
     if (tid == 0) {
-      for (int v = 1; v < GB / WAVE; ++v)
-        if (better(rede[v], redi[v], be, bp)) be = rede[v], bp = redi[v];
       G.move[n] = bp;
       G.gain[n] = bp == NONE32 ? 0 : (i64)saving - (i64)W + (i64)be;
     }
@@ -484,6 +594,7 @@ void launch_gains(chp_ctx *c, u32 N, u32 k, u32 K2, int enforce, u64 omega, cons
     CHP_LAUNCH(c, "gain_light", k_gain_light, waves_grid(host_cnt[0]), GB, 0, G,
                (const u32 *)lists, (const u32 *)cnt);
   if (host_cnt[1])
-    CHP_LAUNCH(c, "gain_heavy", k_gain_heavy, host_cnt[1] < 4 * c->n_cu ? host_cnt[1] : 4 * c->n_cu,
-               GB, 0, G, (const u32 *)lists, (const u32 *)cnt);
+    CHP_LAUNCH(c, "gain_heavy", k_gain_heavy,
+               host_cnt[1] < GH_PER_CU * c->n_cu ? host_cnt[1] : GH_PER_CU * c->n_cu, GB, 0, G,
+               (const u32 *)lists, (const u32 *)cnt, cnt + 2);
 }

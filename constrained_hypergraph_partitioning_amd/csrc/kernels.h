@@ -104,8 +104,9 @@ void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, const NodeRec *recs,
 // Refinement move proposal: pins(., e) lists (pl[P] packed p << 32 | count in
 // each hyperedge's pin range, lam[E] their lengths), the free-capacity
 // max-tree over K2 (a power of two >= k) leaves, and the per-node gains
-// (launch_gains with host_cnt null classifies into lists / cnt, zeroed
-// before; then again with the host copy of cnt).
+// (launch_gains with host_cnt null classifies into lists / cnt[0..1]; then
+// again with the host copy of cnt; cnt[0..2] zeroed before, cnt[2] being the
+// heavy path's work counter).
 void launch_pins_lists(chp_ctx *c, const i64 *e_off, const u32 *pins, const u32 *rho, u32 k,
                        u64 *pl, u32 *lam, EdgeLists el, const u32 *host_cnt, u64 *scratch,
                        u64 per_wg, u32 grid_big);
