@@ -79,6 +79,7 @@ def _load():
             "or_purge": [u32, P, P, P, P, P, u32, P, ctypes.POINTER(P), ctypes.POINTER(u64)],
             "or_pair_leftovers": [u32, P, P, P, u64, u32, u32, P, ctypes.POINTER(u64)],
             "or_moves": [E, P, P, P, u32, u64, i32, P, P],
+            "or_match_dp": [u32, P, P, P, ctypes.POINTER(u64)],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -293,6 +294,18 @@ def purge(g: Graph, flag, match_arr, gamma, cg: Graph) -> Graph:
     cg.nb_off = off
     cg.nb = _take(ptr.value, tot.value, np.uint32)
     return cg
+
+
+def match_dp(target, score):
+    """O13: exact maximum-weight matching on the proposal pseudo-forest
+    (match array, number of pairs)."""
+    t = np.ascontiguousarray(target, np.uint32)
+    sc = np.ascontiguousarray(score, np.uint64)
+    m = np.empty(t.shape[0], np.uint32)
+    npairs = ctypes.c_uint64()
+    _check(_load().or_match_dp(t.shape[0], _p(t), _p(sc), _p(m), ctypes.byref(npairs)),
+           "match_dp")
+    return m, int(npairs.value)
 
 
 def moves(g: Graph, rho, k, omega, enforce_omega=False):

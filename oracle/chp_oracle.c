@@ -858,3 +858,106 @@ int or_moves(const or_edges *g, const int64_t *n_off, const uint32_t *n_inc, con
   free(poff), free(ppart), free(pcnt), free(tmp), free(psize);
   return OR_OK;
 }
+
+/*
+ * O13 -- exact maximum-weight matching on the proposal pseudo-forest
+ * ([P1] Sec. V-D, Eqs. 7-12).  The proposal edge of n is {n, target(n)} with
+ * weight score(n).  R = the nodes in two-cycles (target(target(n)) = n); the
+ * parent of n not in R is target(n) (a node with no target tops its tree);
+ * children(n) = {c not in R : target(c) = n}.  Bottom up:
+ *   A(n)     = sum of ss0(c) over children(n),
+ *   best(n)  = max over children c of ss1(c) - ss0(c), at the smallest such c,
+ *   ss0(n)   = A(n) + max(0, best(n))        (n not matched to its target),
+ *   ss1(n)   = score(n) + A(n)                (n matched to its target).
+ * A two-cycle {n, t} matches when score(n) + A(n) + A(t) > ss0(n) + ss0(t)
+ * (strictly); otherwise, and for a node with no target, a node takes its best
+ * child when best > 0.  Top down, a node not in R pairs with its target when
+ * the target took it, and otherwise takes its best child when best > 0.
+ * Sums that do not fit 64 bits give OR_EOVERFLOW.
+ */
+int or_match_dp(uint32_t N, const uint32_t *target, const uint64_t *score, uint32_t *match,
+                uint64_t *n_pairs) {
+  *n_pairs = 0;
+  for (uint32_t n = 0; n < N; ++n)
+    if (target[n] != NONE && (target[n] >= N || target[n] == n)) return OR_EINVAL;
+  uint8_t *inR = (uint8_t *)calloc(N ? N : 1, 1);
+  uint32_t *order = (uint32_t *)malloc(sizeof(uint32_t) * (N ? N : 1));
+  uint32_t *pend = (uint32_t *)calloc(N ? N : 1, sizeof(uint32_t));
+  uint64_t *A = (uint64_t *)calloc(N ? N : 1, sizeof(uint64_t));
+  uint64_t *ss0 = (uint64_t *)calloc(N ? N : 1, sizeof(uint64_t));
+  uint64_t *ss1 = (uint64_t *)calloc(N ? N : 1, sizeof(uint64_t));
+  uint64_t *bestv = (uint64_t *)calloc(N ? N : 1, sizeof(uint64_t));
+  uint32_t *bestc = (uint32_t *)malloc(sizeof(uint32_t) * (N ? N : 1));
+  if (!inR || !order || !pend || !A || !ss0 || !ss1 || !bestv || !bestc) {
+    free(inR), free(order), free(pend), free(A), free(ss0), free(ss1), free(bestv), free(bestc);
+    return OR_ENOMEM;
+  }
+  int rc = OR_OK;
+  for (uint32_t n = 0; n < N; ++n) {
+    const uint32_t t = target[n];
+    inR[n] = t != NONE && target[t] == n;
+    bestc[n] = NONE;
+  }
+  /* children counts; leaves first (a queue over nodes whose children are done) */
+  for (uint32_t n = 0; n < N; ++n)
+    if (!inR[n] && target[n] != NONE) pend[target[n]]++;
+  uint32_t head = 0, tail = 0;
+  for (uint32_t n = 0; n < N; ++n)
+    if (pend[n] == 0) order[tail++] = n;
+  while (head < tail) {
+    const uint32_t n = order[head++];
+    /* all children of n are done: A(n), best(n) are final */
+    ss0[n] = A[n] + (bestc[n] != NONE && bestv[n] > 0 ? bestv[n] : 0);
+    if (ss0[n] < A[n]) rc = OR_EOVERFLOW;
+    if (target[n] != NONE) {
+      ss1[n] = score[n] + A[n];
+      if (ss1[n] < A[n]) rc = OR_EOVERFLOW;
+    }
+    if (!inR[n] && target[n] != NONE) {
+      const uint32_t p = target[n];
+      const uint64_t s = A[p] + ss0[n];
+      if (s < A[p]) rc = OR_EOVERFLOW;
+      A[p] = s;
+      /* ss1 >= ss0 always holds for a child (its best child scores at most
+         its own score), so the difference is well defined */
+      const uint64_t d = ss1[n] >= ss0[n] ? ss1[n] - ss0[n] : 0;
+      if (bestc[p] == NONE || d > bestv[p] || (d == bestv[p] && n < bestc[p]))
+        bestv[p] = d, bestc[p] = n;
+      if (--pend[p] == 0) order[tail++] = p;
+    }
+  }
+  if (tail != N) rc = OR_ECYCLE; /* a cycle longer than two */
+  if (rc == OR_OK) {
+    for (uint32_t n = 0; n < N; ++n) match[n] = n;
+    /* the two-cycles decide first */
+    for (uint32_t n = 0; n < N; ++n) {
+      const uint32_t t = target[n];
+      if (!inR[n] || n > t) continue;
+      const uint64_t pair = score[n] + A[n] + A[t];
+      const uint64_t apart = ss0[n] + ss0[t];
+      if (pair < A[n] || pair - A[n] < A[t] || apart < ss0[n]) rc = OR_EOVERFLOW;
+      if (pair > apart) {
+        match[n] = t, match[t] = n;
+      } else {
+        if (bestc[n] != NONE && bestv[n] > 0) match[n] = bestc[n], match[bestc[n]] = n;
+        if (bestc[t] != NONE && bestv[t] > 0) match[t] = bestc[t], match[bestc[t]] = t;
+      }
+    }
+    /* then top down: the order reversed visits every parent before its children */
+    for (uint32_t i = N; i-- > 0;) {
+      const uint32_t n = order[i];
+      const uint32_t t = target[n];
+      if (inR[n]) {
+        /* decided above */
+      } else if (t != NONE && match[t] == n) {
+        /* taken by its target: already recorded */
+      } else if (bestc[n] != NONE && bestv[n] > 0) {
+        match[n] = bestc[n], match[bestc[n]] = n;
+      }
+    }
+    for (uint32_t n = 0; n < N; ++n)
+      if (match[n] > n) ++*n_pairs;
+  }
+  free(inR), free(order), free(pend), free(A), free(ss0), free(ss1), free(bestv), free(bestc);
+  return rc;
+}

@@ -242,3 +242,28 @@ def moves(n_nodes, edges, weights, sizes, rho, k, omega, enforce_omega):
         mv.append(0xFFFFFFFF if best is None else best)
         gn.append(0 if best is None else bg)
     return mv, gn
+
+
+def max_weight_matching(target, score):
+    """Largest total weight of a matching made of proposal edges {n, target(n)}
+    (weight score(n); a two-cycle is one edge), by enumerating edge subsets."""
+    n = len(target)
+    edges = {}
+    for v in range(n):
+        t = target[v]
+        if t != 0xFFFFFFFF:
+            edges[tuple(sorted((v, t)))] = int(score[v])
+    el = list(edges.items())
+    best = 0
+    for mask in range(1 << len(el)):
+        used, total, ok = set(), 0, True
+        for i, ((a, b), w) in enumerate(el):
+            if mask >> i & 1:
+                if a in used or b in used:
+                    ok = False
+                    break
+                used.add(a), used.add(b)
+                total += w
+        if ok and total > best:
+            best = total
+    return best, edges

@@ -53,6 +53,12 @@ MUTANTS = {
                              "if (pins_of(poff, ppart, pcnt, e, pn) >= 1) saving += g->e_w[e];"),
     "moves_tie_largest_id": ("if (best == NONE || gp > best_gain) best = p, best_gain = gp;",
                              "if (best == NONE || gp >= best_gain) best = p, best_gain = gp;"),
+    "dp_roots_pair_on_tie": ("      if (pair > apart) {", "      if (pair >= apart) {"),
+    "dp_best_child_largest_id": ("if (bestc[p] == NONE || d > bestv[p] || (d == bestv[p] && n < bestc[p]))",
+                                 "if (bestc[p] == NONE || d > bestv[p] || (d == bestv[p] && n > bestc[p]))"),
+    "dp_ss1_without_children": ("      ss1[n] = score[n] + A[n];", "      ss1[n] = score[n];"),
+    "dp_roots_never_take_children": ("        if (bestc[n] != NONE && bestv[n] > 0) match[n] = bestc[n], match[bestc[n]] = n;\n        if (bestc[t] != NONE && bestv[t] > 0) match[t] = bestc[t], match[bestc[t]] = t;",
+                                     ";"),
     "moves_omega_without_node": ("if (enforce_omega && psize[p] + g->n_size[n] > omega) continue;",
                                  "if (enforce_omega && psize[p] > omega) continue;"),
 }
@@ -80,6 +86,9 @@ def _checks():
         pins.test_moves_vs_brute(kw)
     for seed in range(3):
         pins.test_moves_identity_partition(seed)
+    pins.test_match_dp_hand_examples()
+    for seed in range(12):
+        pins.test_match_dp_vs_brute(seed)
 
 
 def _build_mutant(name, tmpdir):

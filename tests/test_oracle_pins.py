@@ -642,3 +642,104 @@ def test_moves_identity_partition(seed):
             assert (int(mv[v]), int(gn[v])) == best
         else:
             assert (int(mv[v]), int(gn[v])) == (0 if v else 1, 0)
+
+
+# ---- O13: exact matching on the proposal pseudo-forest ([HP] Sec. V-D)
+def _total(match, score, target):
+    tot = 0
+    for v, m in enumerate(match.tolist()):
+        if m > v:
+            # the edge's weight: score of whichever endpoint proposed it
+            tot += int(score[v]) if int(target[v]) == m else int(score[m])
+    return tot
+
+
+def test_match_dp_hand_examples():
+    N = 0xFFFFFFFF
+    # chain a -> b -> (c <-> d): pairing the roots (10) and then a with b (8)
+    # beats b with c (9)
+    tgt = np.array([1, 2, 3, 2], np.uint32)        # a=0, b=1, c=2, d=3
+    sc = np.array([8, 9, 10, 10], np.uint64)
+    m, k = oracle.match_dp(tgt, sc)
+    assert m.tolist() == [1, 0, 3, 2] and k == 2
+    # roots worth 5 with a child each worth 5: the roots stay apart and take
+    # their children (10), where the handshake pairs the roots (5)
+    tgt = np.array([1, 0, 0, 1], np.uint32)
+    sc = np.array([5, 5, 5, 5], np.uint64)
+    m, k = oracle.match_dp(tgt, sc)
+    assert m.tolist() == [2, 3, 0, 1] and k == 2
+    hm, hk = oracle.match(tgt, sc)
+    assert hm.tolist() == [1, 0, 2, 3] and hk == 1
+    # a tie between pairing the roots (5) and the root taking its child (5):
+    # the roots pair only when strictly better
+    tgt = np.array([1, 0, 0], np.uint32)
+    sc = np.array([5, 5, 5], np.uint64)
+    m, k = oracle.match_dp(tgt, sc)
+    assert m.tolist() == [2, 1, 0] and k == 1
+    # two equal children: the smaller id is taken; a node without a target
+    # takes its best child
+    tgt = np.array([N, 0, 0, N], np.uint32)
+    sc = np.array([0, 7, 7, 0], np.uint64)
+    m, k = oracle.match_dp(tgt, sc)
+    assert m.tolist() == [1, 0, 2, 3] and k == 1
+
+
+def _forest(rng, n):
+    """A random proposal pseudo-forest: two-cycles and free tops as roots,
+    every other node under a node of score at least its own."""
+    target = np.full(n, 0xFFFFFFFF, np.uint32)
+    score = np.zeros(n, np.uint64)
+    order = rng.permutation(n)
+    placed = []
+    for v in order.tolist():
+        r = rng.random()
+        if not placed or r < 0.15:
+            placed.append(v)  # a tree top without target
+            continue
+        if r < 0.3:
+            # close a two-cycle with a free top
+            tops = [u for u in placed if target[u] == 0xFFFFFFFF and score[u] == 0]
+            if tops:
+                u = tops[int(rng.integers(0, len(tops)))]
+                s = int(rng.integers(1, 50))
+                target[u], target[v] = v, u
+                score[u] = score[v] = s
+                placed.append(v)
+                continue
+        p = placed[int(rng.integers(0, len(placed)))]
+        cap = int(score[p]) if target[p] != 0xFFFFFFFF else 50
+        target[v] = p
+        score[v] = int(rng.integers(1, max(cap, 1) + 1))
+        placed.append(v)
+    return target, score
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_match_dp_vs_brute(seed):
+    """On random pseudo-forests of at most 16 nodes the matching reaches the
+    largest total weight over all matchings of proposal edges."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n = int(rng.integers(2, 17))
+    tgt, sc = _forest(rng, n)
+    m, k = oracle.match_dp(tgt, sc)
+    assert np.array_equal(m[m], np.arange(n))
+    for v in range(n):
+        if int(m[v]) != v:
+            assert int(tgt[v]) == int(m[v]) or int(tgt[int(m[v])]) == v
+    best, _ = brute.max_weight_matching(tgt.tolist(), sc.tolist())
+    assert _total(m, sc, tgt) == best
+
+
+@pytest.mark.parametrize("kw", tiny_cases()[::3], ids=lambda k: "s%d" % k["seed"])
+def test_match_dp_on_proposals(kw):
+    """On the proposals of the tiny graphs (rating with noise): optimal, and
+    never below the handshake's total."""
+    h = synth.tiny(**kw)
+    g = load(h)
+    tgt, sc = oracle.rate(g, BIG, BIG, noise_on=True, seed=kw["seed"])
+    m, _ = oracle.match_dp(tgt, sc)
+    if h.n_nodes <= 18:
+        best, _ = brute.max_weight_matching(tgt.tolist(), sc.tolist())
+        assert _total(m, sc, tgt) == best
+    hm, _ = oracle.match(tgt, sc)
+    assert _total(m, sc, tgt) >= _total(hm, sc, tgt)
