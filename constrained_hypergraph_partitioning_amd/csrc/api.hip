@@ -503,6 +503,12 @@ int chp_last_rate_stats(const chp_ctx *c, uint64_t *nb_entries, uint32_t *batche
   return CHP_OK;
 }
 
+int chp_set_matching(chp_ctx *c, int mode) {
+  if (!c || (mode != CHP_MATCH_HANDSHAKE && mode != CHP_MATCH_OPTIMAL)) return CHP_EINVAL;
+  c->matching = (u32)mode;
+  return CHP_OK;
+}
+
 int chp_set_incidence_rating(chp_ctx *c, uint64_t min_visits, uint32_t hash_keys) {
   if (!c) return CHP_EINVAL;
   c->inc_min_visits = min_visits;
@@ -607,6 +613,51 @@ int chp_build_incidence(chp_ctx *c, const chp_edges *in, const chp_params *prm,
 }
 
 namespace {
+
+// Exact matching on the proposal pseudo-forest: depths, a host scan of the
+// per-depth counts, then one launch per depth up and one down.
+void match_optimal(chp_ctx *c, Scratch &s, u32 N, const u32 *target, const u64 *score,
+                   u32 *match, u32 *npairs, u32 *n_pairs_host) {
+  DpScratch d;
+  d.par = s.get<u32>(N);
+  d.anc = s.get<u32>(N);
+  d.dist = s.get<u32>(N);
+  d.anc2 = s.get<u32>(N);
+  d.dist2 = s.get<u32>(N);
+  d.byd = s.get<u32>(N);
+  d.bestc = s.get<u32>(N);
+  d.small = s.get<u32>(4);
+  d.A = s.get<u64>(N);
+  d.bestv = s.get<u64>(N);
+  d.ss0 = s.get<u64>(N);
+  d.diff = s.get<u64>(N);
+  launch_fill_u32(c, d.small, 4, 0);
+  launch_dp_prepare(c, N, target, d, match);
+  launch_check(c, "matching depths");
+  u32 D = 0, f = 0;
+  read_many(c, {{&D, d.small, sizeof D}, {&f, c->flags, sizeof f}});
+  if (f & (FLAG_EINVAL | FLAG_EOVERFLOW)) fail_flags(c, f, "rating");
+  if (f & FLAG_ECYCLE) fail_flags(c, FLAG_ECYCLE, "matching");
+  u32 *cntd = s.get<u32>((u64)D + 1);
+  u32 *cursor = s.get<u32>((u64)D + 1);
+  launch_fill_u32(c, cntd, (u64)D + 1, 0);
+  launch_dp_count(c, N, d.dist, cntd);
+  launch_check(c, "matching depth counts");
+  std::vector<u32> off((size_t)D + 2);
+  hip_check(c, hipMemcpyAsync(off.data() + 1, cntd, sizeof(u32) * ((size_t)D + 1),
+                              hipMemcpyDeviceToHost, c->stream),
+            "readback");
+  hip_check(c, hipStreamSynchronize(c->stream), "stream synchronize");
+  off[0] = 0;
+  for (size_t i = 1; i < off.size(); ++i) off[i] += off[i - 1];
+  hip_check(c, hipMemcpyAsync(cursor, off.data(), sizeof(u32) * ((size_t)D + 1),
+                              hipMemcpyHostToDevice, c->stream),
+            "copy");
+  launch_dp_levels(c, N, target, score, d, D, cursor, off.data(), match, npairs);
+  launch_check(c, "matching levels");
+  read_many(c, {{&f, c->flags, sizeof f}, {n_pairs_host, npairs, sizeof(u32)}});
+  if (f & FLAG_EOVERFLOW) fail_flags(c, FLAG_EOVERFLOW, "matching");
+}
 
 // Neighbour entries one batch may hold (oversize buffer and packed lists).
 constexpr u64 BATCH_ENTRIES = 3ull << 30;
@@ -791,6 +842,10 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
       launch_check(c, "rate");
     } else {
       rate_batched(c, s, g, a, nl, recs, big, work);
+    }
+    if (c->matching == CHP_MATCH_OPTIMAL) {
+      match_optimal(c, s, N, target, score_fx, match, npairs, n_pairs_host);
+      return;
     }
     launch_match(c, N, target, score_fx, ms, match, npairs);
     launch_match_write(c, N, target, ms, match, npairs);

@@ -117,6 +117,21 @@ void launch_gains(chp_ctx *c, u32 N, u32 k, u32 K2, int enforce, u64 omega, cons
                   const u64 *tree, u32 *move, i64 *gain, u32 *lists, u32 *cnt,
                   const u32 *host_cnt);
 
+// Exact matching on the proposal pseudo-forest (k_match_dp.hip): every
+// array N long except small[4] (small[0] = largest depth, zeroed before).
+struct DpScratch {
+  u32 *par, *anc, *dist, *anc2, *dist2, *byd, *bestc, *small;
+  u64 *A, *bestv, *ss0, *diff;
+};
+// depths by pointer jumping (d.dist, small[0] = the largest; flags ECYCLE
+// when a node reaches no root); match set to the identity
+void launch_dp_prepare(chp_ctx *c, u32 N, const u32 *target, DpScratch &d, u32 *match);
+void launch_dp_count(chp_ctx *c, u32 N, const u32 *dist, u32 *cntd);
+// cursor[D+1] = the host offsets offd[0..D] on the device (consumed); the
+// levels bottom up, then top down; npairs zeroed before
+void launch_dp_levels(chp_ctx *c, u32 N, const u32 *target, const u64 *score, DpScratch &d,
+                      u32 D, u32 *cursor, const u32 *offd, u32 *match, u32 *npairs);
+
 // Device-wide sort of n distinct u64 keys; tmp holds n; returns a or tmp.
 u64 *sort_keys_u64(chp_ctx *c, u64 *a, u64 *tmp, u64 n);
 

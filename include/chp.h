@@ -227,6 +227,20 @@ int chp_evaluate_partition(chp_ctx *ctx, const chp_hgraph *g, const uint32_t *rh
  * whose own list is larger gets a batch of its own. */
 int chp_set_batch_entries(chp_ctx *ctx, uint64_t entries);
 
+/* Matching used by chp_rate_and_match on ctx.  CHP_MATCH_HANDSHAKE (the
+ * default): the greedy handshake described there ([IC] Sec. III-A).
+ * CHP_MATCH_OPTIMAL: the exact maximum-weight matching of the proposal
+ * pseudo-forest ([HP] Sec. V-D, Eqs. 7-12): edges {n, target(n)} of weight
+ * score(n); bottom up ss0(n) = A(n) + max(0, best(n)) and ss1(n) = score(n) +
+ * A(n), with A the sum of the children's ss0 and best the largest ss1 - ss0
+ * of a child (smallest id on ties); a two-cycle {n, t} pairs when score(n) +
+ * A(n) + A(t) > ss0(n) + ss0(t), a node taken by its target pairs with it, any
+ * other node takes its best child when best > 0.  Its total score is the
+ * largest over all matchings of proposal edges.  EINVAL for another mode. */
+#define CHP_MATCH_HANDSHAKE 0
+#define CHP_MATCH_OPTIMAL 1
+int chp_set_matching(chp_ctx *ctx, int mode);
+
 /* Graphs without neighbour lists: a node with 1..384 incident hyperedges and
  * at least min_visits (and below 2^27) pins over them is rated straight from
  * the incidence, its N(n) held in LDS one id window at a time and never

@@ -347,13 +347,14 @@ class Level:
 
 
 def level(g: Graph, omega, delta, noise_on=True, seed=0, build_neighbors=True,
-          purge_invalid=False, leftovers=False) -> Level:
+          purge_invalid=False, leftovers=False, optimal=False) -> Level:
     """One coarsening level: rate, match, contract.  With purge_invalid the
     neighbour flags of g are computed (Level.flags) and the coarse
     neighbourhoods are purged of flagged neighbours (O10); with leftovers the
-    unmatched nodes without a target are paired best-effort (O11)."""
+    unmatched nodes without a target are paired best-effort (O11); with
+    optimal the matching is the exact one of O13 instead of the handshake."""
     target, score = rate(g, omega, delta, noise_on, seed)
-    m, npairs = match(target, score)
+    m, npairs = match_dp(target, score) if optimal else match(target, score)
     if leftovers:
         m, extra = pair_leftovers(target, m, g.n_size, g.n_nin, omega, delta)
         npairs += extra

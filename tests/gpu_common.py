@@ -37,18 +37,23 @@ def assert_equal(got, want, what):
 
 
 def run_level_pair(chp, ctx, dg, og, omega, delta, noise_on, seed, neighbors=True, tag="",
-                   purge=False, leftovers=False):
+                   purge=False, leftovers=False, optimal=False):
     """One level on both sides; compares target, score, match, pairs, gamma
     and the coarse graph (with purge, also the invalid-neighbour flags, and
     the coarse neighbourhoods purged; with leftovers, after the best-effort
     pairing of the nodes left without a partner).  Returns (device coarse,
     oracle Level, device gamma)."""
     flags = ctx.new_flags(dg) if purge else None
-    tgt, score, match, npairs = ctx.rate_and_match(dg, omega, delta, noise_on, seed, flags=flags)
+    ctx.set_matching(optimal)
+    try:
+        tgt, score, match, npairs = ctx.rate_and_match(dg, omega, delta, noise_on, seed,
+                                                       flags=flags)
+    finally:
+        ctx.set_matching(False)
     if leftovers:
         npairs += ctx.pair_leftovers(dg, tgt, match, omega, delta)
     lv = oracle.level(og, omega, delta, noise_on, seed, build_neighbors=neighbors,
-                      purge_invalid=purge, leftovers=leftovers)
+                      purge_invalid=purge, leftovers=leftovers, optimal=optimal)
     assert_equal(chp.to_host(tgt, np.uint32), lv.target, tag + " target")
     assert_equal(chp.to_host(score, np.uint64), lv.score, tag + " score")
     assert_equal(chp.to_host(match, np.uint32), lv.match, tag + " match")

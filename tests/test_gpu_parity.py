@@ -45,7 +45,7 @@ def both(chp, ctx, h, omega, delta, neighbors=True):
 
 
 def multilevel(chp, ctx, h, omega, delta, noise_on, seed, max_levels, target_nodes=0,
-               eval_every=False, tag="", purge=False, leftovers=False):
+               eval_every=False, tag="", purge=False, leftovers=False, optimal=False):
     dg, og = both(chp, ctx, h, omega, delta)
     rho = np.arange(h.n_nodes, dtype=np.uint32)
     og0, dg0 = og, dg
@@ -56,7 +56,7 @@ def multilevel(chp, ctx, h, omega, delta, noise_on, seed, max_levels, target_nod
             break
         cg, lv, gamma = run_level_pair(chp, ctx, dg, og, omega, delta, noise_on, seed,
                                        tag="%s L%d" % (tag, lvl), purge=purge,
-                                       leftovers=leftovers)
+                                       leftovers=leftovers, optimal=optimal)
         levels += 1
         if cg is None:
             break
@@ -305,6 +305,38 @@ def test_leftovers_random(chp, ctx, n, p_none, seed):
         k = ctx.pair_leftovers(dg, chp.to_device(tgt), dm, omega, delta)
         assert k == wk
         assert_equal(chp.to_host(dm, np.uint32), want, "leftovers %d" % n)
+
+
+@pytest.mark.parametrize("cfg,nn,levels", [(1, None, 10), (2, 20000, 20), (3, 5000, 4),
+                                           (4, 20000, 12), (5, 8192, 1)])
+def test_optimal_matching_multilevel(chp, ctx, cfg, nn, levels):
+    """The exact matching of the proposal pseudo-forest in place of the
+    handshake, with purge and leftovers, every level against the oracle."""
+    spec = synth.config(cfg, n_nodes=nn)
+    h = synth.generate(spec)
+    say("optimal matching", cfg, nn)
+    multilevel(chp, ctx, h, spec.omega, spec.delta, True, spec.seed, levels,
+               target_nodes=spec.target_nodes, tag="dp%d" % cfg, purge=True, leftovers=True,
+               optimal=True)
+
+
+def test_optimal_matching_tiny_and_chain(chp, ctx):
+    """Tiny graphs under the limit grid, and a path whose weights grow along
+    it (every node targets the next: one chain of 4,999 levels)."""
+    import test_oracle_pins as pins
+    for kw in pins.tiny_cases():
+        h = synth.tiny(**kw)
+        say("dp tiny", kw["seed"])
+        for omega, delta in pins.constraint_grid(h):
+            dg, og = both(chp, ctx, h, omega, delta)
+            run_level_pair(chp, ctx, dg, og, omega, delta, True, kw["seed"],
+                           tag="dp tiny%d" % kw["seed"], optimal=True)
+    n = 5000
+    h = synth.from_lists(n, [([i], [i + 1]) for i in range(n - 1)],
+                         weights=[i + 1 for i in range(n - 1)])
+    say("dp chain", n)
+    dg, og = both(chp, ctx, h, 1 << 30, 1 << 30)
+    run_level_pair(chp, ctx, dg, og, 1 << 30, 1 << 30, False, 0, tag="dp chain", optimal=True)
 
 
 def moves_pair(chp, ctx, dg, og, rho, k, omega, enforce, tag):
