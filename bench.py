@@ -62,6 +62,9 @@ def parse():
                    help="build the graph without neighbour lists even where they fit")
     p.add_argument("--progress", action="store_true",
                    help="print a line per timed step to stderr (long workloads)")
+    p.add_argument("--optimal-matching", action="store_true",
+                   help="match by the exact maximum-weight matching of the proposal graph "
+                        "instead of the greedy handshake")
     p.add_argument("--moves", action="store_true",
                    help="also time the refinement move proposal (Eq. 13) on the input graph "
                         "under the step's projected partition, Omega enforced")
@@ -231,6 +234,7 @@ def main():
     h = synth.generate(spec)
     print("[bench] generated %s: %d pins" % (spec.name, h.n_pins), file=sys.stderr, flush=True)
     ctx = chp.Context(0)
+    ctx.set_matching(args.optimal_matching)
     dev_edges = chp.upload_edges(h)
     rho_buf = torch.empty(h.n_nodes, dtype=torch.int32, device=ctx.device)
     if args.copy_ref_mib:
@@ -296,6 +300,7 @@ def main():
         "config": {"workload": spec.name, "nodes": h.n_nodes, "hyperedges": h.n_edges,
                    "neighbourhoods": "whole graph" if with_nb else "built per node batch",
                    "purge": PURGE and with_nb, "leftover_pairing": LEFTOVERS,
+                   "matching": "optimal" if args.optimal_matching else "handshake",
                    "pins": h.n_pins, "omega": spec.omega, "delta": spec.delta,
                    "levels": len(levels), "final_nodes": levels[-1][0] - levels[-1][2]
                    if levels else h.n_nodes, "connectivity": int(summ[0])},

@@ -68,14 +68,36 @@ __global__ void k_dp_depths(u32 N, const u32 *par, const u32 *anc, const u32 *di
   if (lane_id() == 0) atomicMax(maxd, d);
 }
 
+// One atomic per distinct bucket of the wave (most nodes share a few depths):
+// returns this lane's slot in bucket `key` of `ctr` (active lanes only).
+__device__ u32 wave_bucket_append(u32 *ctr, u32 key, bool active) {
+  const u32 l = lane_id();
+  u32 slot = 0;
+  u64 left = __ballot(active);
+  while (left) {
+    const u32 leader = (u32)__builtin_ctzll(left);
+    const u32 k = __shfl(key, leader, WAVE);
+    const u64 same = __ballot(active && key == k);
+    u32 base = 0;
+    if (l == leader) base = atomicAdd(ctr + k, (u32)__popcll(same));
+    base = __shfl(base, leader, WAVE);
+    if (active && key == k) slot = base + (u32)__popcll(same & ((1ull << l) - 1));
+    left &= ~same;
+  }
+  return slot;
+}
+
 __global__ void k_dp_count(u32 N, const u32 *dist, u32 *cntd) {
   const u32 n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n < N) atomicAdd(cntd + dist[n], 1u);
+  const bool ok = n < N;
+  wave_bucket_append(cntd, ok ? dist[n] : 0, ok);
 }
 
 __global__ void k_dp_scatter(u32 N, const u32 *dist, u32 *cur, u32 *byd) {
   const u32 n = blockIdx.x * blockDim.x + threadIdx.x;
-  if (n < N) byd[atomicAdd(cur + dist[n], 1u)] = n;
+  const bool ok = n < N;
+  const u32 slot = wave_bucket_append(cur, ok ? dist[n] : 0, ok);
+  if (ok) byd[slot] = n;
 }
 
 __device__ __forceinline__ void add_ovf(u64 *p, u64 v, u32 *flags) {
