@@ -32,7 +32,7 @@ EXPORTS = ["chp_create", "chp_destroy", "chp_last_error", "chp_build_incidence",
            "chp_rate_and_match", "chp_contract", "chp_evaluate_partition", "chp_hgraph_free",
            "chp_set_timing", "chp_get_timings", "chp_reset_timings", "chp_set_batch_entries",
            "chp_last_rate_stats", "chp_set_incidence_rating", "chp_pair_leftovers",
-           "chp_propose_moves", "chp_set_matching"]
+           "chp_propose_moves", "chp_set_matching", "chp_set_timing_filter"]
 
 
 class ChpError(RuntimeError):
@@ -107,6 +107,8 @@ def load_library(path: str = LIB_PATH):
                                         ctypes.POINTER(ctypes.c_uint32),
                                         ctypes.POINTER(ctypes.c_uint32)]
     lib.chp_last_rate_stats.restype = I
+    lib.chp_set_timing_filter.argtypes = [P, ctypes.c_char_p]
+    lib.chp_set_timing_filter.restype = I
     lib.chp_set_matching.argtypes = [P, I]
     lib.chp_set_matching.restype = I
     lib.chp_propose_moves.argtypes = [P, ctypes.POINTER(HGraphC), P, ctypes.c_uint32,
@@ -316,6 +318,11 @@ class Context:
                                                 _ptr(flags) if flags is not None else None),
                     "rate_and_match")
         return target, score, match, int(npairs.value)
+
+    def set_timing_filter(self, prefix=None):
+        """Time only kernels whose name starts with prefix (None = all)."""
+        self._check(self.lib.chp_set_timing_filter(self.h, prefix.encode() if prefix else None),
+                    "set_timing_filter")
 
     def set_matching(self, optimal=False):
         """Matching of rate_and_match: the greedy handshake (default) or the

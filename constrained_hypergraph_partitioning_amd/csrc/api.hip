@@ -516,6 +516,12 @@ int chp_set_incidence_rating(chp_ctx *c, uint64_t min_visits, uint32_t hash_keys
   return CHP_OK;
 }
 
+int chp_set_timing_filter(chp_ctx *c, const char *prefix) {
+  if (!c) return CHP_EINVAL;
+  c->timing_prefix = prefix ? prefix : "";
+  return CHP_OK;
+}
+
 int chp_set_timing(chp_ctx *c, int on) {
   if (!c) return CHP_EINVAL;
   c->timing = on ? 1 : 0;

@@ -59,6 +59,7 @@ struct chp_ctx {
   u32 matching = 0;           // CHP_MATCH_HANDSHAKE or CHP_MATCH_OPTIMAL
   u64 *dsmall = nullptr;   // device small buffer (64 words)
   int timing = 0;
+  std::string timing_prefix;  // time only kernels whose name starts with it ("" = all)
   std::vector<TimingRec> pending;
   std::vector<hipEvent_t> free_events;
   std::vector<TimingSum> sums;
@@ -68,16 +69,21 @@ struct chp_ctx {
 void *ctx_alloc(chp_ctx *c, size_t bytes);
 void ctx_free(chp_ctx *c, void *p);
 void timing_begin(chp_ctx *c, const char *name, hipEvent_t *a, hipEvent_t *b);
+inline bool timing_wanted(const chp_ctx *c, const char *name) {
+  return c->timing_prefix.empty() ||
+         c->timing_prefix.compare(0, std::string::npos, name, c->timing_prefix.size()) == 0;
+}
 void timing_end(chp_ctx *c, const char *name, hipEvent_t a, hipEvent_t b);
 
 // Launch helper that brackets the launch with events when timing is on.
 #define CHP_LAUNCH(ctx, name, kern, grid, block, shmem, ...)                         \
   do {                                                                               \
     hipEvent_t ev_a_ = nullptr, ev_b_ = nullptr;                                     \
-    if ((ctx)->timing) timing_begin((ctx), (name), &ev_a_, &ev_b_);                  \
+    const bool timed_ = (ctx)->timing && timing_wanted((ctx), (name));               \
+    if (timed_) timing_begin((ctx), (name), &ev_a_, &ev_b_);                         \
     hipLaunchKernelGGL(kern, dim3(grid), dim3(block), shmem, (ctx)->stream,          \
                        __VA_ARGS__);                                                 \
-    if ((ctx)->timing) timing_end((ctx), (name), ev_a_, ev_b_);                      \
+    if (timed_) timing_end((ctx), (name), ev_a_, ev_b_);                             \
   } while (0)
 
 static inline u32 grid_for(u64 n, u32 block) {

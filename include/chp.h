@@ -274,6 +274,9 @@ typedef struct {
   double total_ms;
 } chp_timing;
 int chp_set_timing(chp_ctx *ctx, int on);
+/* Time only the kernels whose name starts with prefix (NULL or "" = all);
+ * the events of the others are not recorded at all. */
+int chp_set_timing_filter(chp_ctx *ctx, const char *prefix);
 int chp_get_timings(chp_ctx *ctx, chp_timing *out, int max);
 void chp_reset_timings(chp_ctx *ctx);
 
