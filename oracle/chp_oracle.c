@@ -961,3 +961,121 @@ int or_match_dp(uint32_t N, const uint32_t *target, const uint64_t *score, uint3
   free(inR), free(order), free(pend), free(A), free(ss0), free(ss1), free(bestv), free(bestc);
   return rc;
 }
+
+/*
+ * O14 -- one refinement pass over proposed moves ([P1] Sec. VI-A, VI-C,
+ * VI-D; Eqs. 14-15).  move/gain are the in-isolation proposals of O12.
+ * Readings (the pages leave these open):
+ *  - the sequence holds every node with a proposed move, each move its own
+ *    chain (no chaining), so chains ranked by total gain order the moves by
+ *    (gain desc, id asc);
+ *  - the in-sequence gain of the i-th move is the connectivity it removes
+ *    with the moves before it already applied: for every hyperedge e of the
+ *    node, +w(e) when the node is the last pin of e left in its partition,
+ *    -w(e) when e has no pin in the destination yet (Eqs. 14-15 state the
+ *    same as corrections of the in-isolation gain);
+ *  - a partition is invalid while its size exceeds Omega or its inbound count
+ *    (hyperedges with a destination pin in it) exceeds Delta; the violation
+ *    count after a move is the number of invalid partitions then;
+ *  - the prefix applied is the one of largest cumulative gain among those
+ *    leaving no violation, the empty prefix (gain 0, nothing applied) always
+ *    eligible, ties to the shorter prefix.
+ * Outputs: seq[M] nodes in order, seq_gain[M] in-sequence gains, seq_viol[M]
+ * violation counts after each move, *n_seq = M, *n_applied = moves applied,
+ * *gain_applied = their summed gain, rho_out = rho with them applied.
+ * A simulation: the state is updated move by move and every count is taken
+ * by scanning the hyperedge's pins.
+ */
+typedef struct {
+  int64_t gain;
+  uint32_t id;
+} or_mv;
+
+static int cmp_mv(const void *x, const void *y) { /* gain descending, id ascending */
+  const or_mv *a = (const or_mv *)x, *b = (const or_mv *)y;
+  if (a->gain != b->gain) return a->gain > b->gain ? -1 : 1;
+  return a->id < b->id ? -1 : (a->id > b->id ? 1 : 0);
+}
+
+/* pins of e in partition p under part[], all pins or destinations only */
+static uint32_t count_in(const or_edges *g, const uint32_t *part, uint32_t e, uint32_t p,
+                         int dst_only) {
+  const int64_t a = g->e_off[e], b = g->e_off[e + 1], d0 = a + g->e_nsrc[e];
+  uint32_t c = 0;
+  for (int64_t i = dst_only ? d0 : a; i < b; ++i) c += part[g->e_pins[i]] == p;
+  return c;
+}
+
+int or_refine(const or_edges *g, const int64_t *n_off, const uint32_t *n_nin,
+              const uint32_t *n_inc, const uint32_t *rho, uint32_t k, uint64_t omega,
+              uint32_t delta, const uint32_t *move, const int64_t *gain, uint32_t *seq,
+              int64_t *seq_gain, uint32_t *seq_viol, uint32_t *n_seq, uint32_t *n_applied,
+              int64_t *gain_applied, uint32_t *rho_out) {
+  const uint32_t N = g->n_nodes, E = g->n_edges;
+  *n_seq = 0, *n_applied = 0, *gain_applied = 0;
+  for (uint32_t n = 0; n < N; ++n) {
+    if (rho[n] >= k) return OR_EINVAL;
+    if (move[n] != NONE && (move[n] >= k || move[n] == rho[n])) return OR_EINVAL;
+  }
+  or_mv *mv = (or_mv *)malloc(sizeof(or_mv) * (N ? N : 1));
+  uint32_t *cur = (uint32_t *)malloc(sizeof(uint32_t) * (N ? N : 1));
+  uint64_t *psize = (uint64_t *)calloc(k ? k : 1, sizeof(uint64_t));
+  uint64_t *pinb = (uint64_t *)calloc(k ? k : 1, sizeof(uint64_t));
+  uint32_t *mark = (uint32_t *)malloc(sizeof(uint32_t) * (k ? k : 1));
+  if (!mv || !cur || !psize || !pinb || !mark) {
+    free(mv), free(cur), free(psize), free(pinb), free(mark);
+    return OR_ENOMEM;
+  }
+  /* the sequence */
+  uint32_t M = 0;
+  for (uint32_t n = 0; n < N; ++n)
+    if (move[n] != NONE) mv[M].gain = gain[n], mv[M].id = n, ++M;
+  qsort(mv, M, sizeof(or_mv), cmp_mv);
+  for (uint32_t i = 0; i < M; ++i) seq[i] = mv[i].id;
+  /* the starting state */
+  for (uint32_t n = 0; n < N; ++n) cur[n] = rho[n], psize[rho[n]] += g->n_size[n];
+  for (uint32_t p = 0; p < k; ++p) mark[p] = NONE;
+  for (uint32_t e = 0; e < E; ++e)
+    for (int64_t i = g->e_off[e] + g->e_nsrc[e]; i < g->e_off[e + 1]; ++i) {
+      const uint32_t p = rho[g->e_pins[i]];
+      if (mark[p] != e) mark[p] = e, pinb[p]++;
+    }
+  uint32_t viol = 0;
+  for (uint32_t p = 0; p < k; ++p) viol += psize[p] > omega || pinb[p] > delta;
+  /* move by move */
+  for (uint32_t i = 0; i < M; ++i) {
+    const uint32_t n = seq[i], ps = cur[n], pd = move[n];
+    int64_t gi = 0;
+    for (int64_t j = n_off[n]; j < n_off[n + 1]; ++j) {
+      const uint32_t e = n_inc[j];
+      if (count_in(g, cur, e, ps, 0) == 1) gi += g->e_w[e];
+      if (count_in(g, cur, e, pd, 0) == 0) gi -= g->e_w[e];
+    }
+    viol -= psize[ps] > omega || pinb[ps] > delta;
+    viol -= psize[pd] > omega || pinb[pd] > delta;
+    for (int64_t j = n_off[n]; j < n_off[n] + n_nin[n]; ++j) { /* n is a destination of e */
+      const uint32_t e = n_inc[j];
+      if (count_in(g, cur, e, ps, 1) == 1) pinb[ps]--;
+      if (count_in(g, cur, e, pd, 1) == 0) pinb[pd]++;
+    }
+    psize[ps] -= g->n_size[n];
+    psize[pd] += g->n_size[n];
+    cur[n] = pd;
+    viol += psize[ps] > omega || pinb[ps] > delta;
+    viol += psize[pd] > omega || pinb[pd] > delta;
+    seq_gain[i] = gi;
+    seq_viol[i] = viol;
+  }
+  /* the best valid prefix */
+  int64_t run = 0, best = 0;
+  uint32_t best_len = 0;
+  for (uint32_t i = 0; i < M; ++i) {
+    run += seq_gain[i];
+    if (seq_viol[i] == 0 && run > best) best = run, best_len = i + 1;
+  }
+  for (uint32_t n = 0; n < N; ++n) rho_out[n] = rho[n];
+  for (uint32_t i = 0; i < best_len; ++i) rho_out[seq[i]] = move[seq[i]];
+  *n_seq = M, *n_applied = best_len, *gain_applied = best;
+  free(mv), free(cur), free(psize), free(pinb), free(mark);
+  return OR_OK;
+}

@@ -59,6 +59,18 @@ MUTANTS = {
     "dp_ss1_without_children": ("      ss1[n] = score[n] + A[n];", "      ss1[n] = score[n];"),
     "dp_roots_never_take_children": ("        if (bestc[n] != NONE && bestv[n] > 0) match[n] = bestc[n], match[bestc[n]] = n;\n        if (bestc[t] != NONE && bestv[t] > 0) match[t] = bestc[t], match[bestc[t]] = t;",
                                      ";"),
+    "refine_order_gain_ascending": ("if (a->gain != b->gain) return a->gain > b->gain ? -1 : 1;",
+                                    "if (a->gain != b->gain) return a->gain < b->gain ? -1 : 1;"),
+    "refine_gain_in_isolation": ("      if (count_in(g, cur, e, ps, 0) == 1) gi += g->e_w[e];\n      if (count_in(g, cur, e, pd, 0) == 0) gi -= g->e_w[e];",
+                                 "      if (count_in(g, rho, e, ps, 0) == 1) gi += g->e_w[e];\n      if (count_in(g, rho, e, pd, 0) == 0) gi -= g->e_w[e];"),
+    "refine_inbound_all_pins": ("      if (count_in(g, cur, e, ps, 1) == 1) pinb[ps]--;\n      if (count_in(g, cur, e, pd, 1) == 0) pinb[pd]++;",
+                                "      if (count_in(g, cur, e, ps, 0) == 1) pinb[ps]--;\n      if (count_in(g, cur, e, pd, 0) == 0) pinb[pd]++;"),
+    "refine_prefix_ties_longest": ("if (seq_viol[i] == 0 && run > best) best = run, best_len = i + 1;",
+                                   "if (seq_viol[i] == 0 && run >= best) best = run, best_len = i + 1;"),
+    "refine_ignores_violations": ("if (seq_viol[i] == 0 && run > best) best = run, best_len = i + 1;",
+                                  "if (run > best) best = run, best_len = i + 1;"),
+    "refine_viol_omega_off_by_one": ("    viol += psize[ps] > omega || pinb[ps] > delta;\n    viol += psize[pd] > omega || pinb[pd] > delta;",
+                                     "    viol += psize[ps] > omega + 1 || pinb[ps] > delta;\n    viol += psize[pd] > omega + 1 || pinb[pd] > delta;"),
     "moves_omega_without_node": ("if (enforce_omega && psize[p] + g->n_size[n] > omega) continue;",
                                  "if (enforce_omega && psize[p] > omega) continue;"),
 }
@@ -89,6 +101,9 @@ def _checks():
     pins.test_match_dp_hand_examples()
     for seed in range(12):
         pins.test_match_dp_vs_brute(seed)
+    pins.test_refine_hand_example()
+    for kw in pins.tiny_cases()[:24:2]:
+        pins.test_refine_vs_brute(kw)
 
 
 def _build_mutant(name, tmpdir):

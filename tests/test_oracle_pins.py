@@ -743,3 +743,105 @@ def test_match_dp_on_proposals(kw):
         assert _total(m, sc, tgt) == best
     hm, _ = oracle.match(tgt, sc)
     assert _total(m, sc, tgt) >= _total(hm, sc, tgt)
+
+
+# ---- O14: one refinement pass ([HP] Sec. VI-A, VI-C, VI-D; Eqs. 14-15)
+def test_refine_hand_example():
+    """Worked by hand on the graph of the move example, rho = [0, 0, 1, 1]:
+    proposals (1 -> 1, gain 5), (3 -> 0, 5), (2 -> 0, 2), (0 -> 1, 0) give the
+    sequence 1, 3, 2, 0.  Moving 1 first frees e1 of partition 0 (+5); then
+    3 re-enters partition 0 on e1, where 1 no longer is (-5 in sequence, +5 in
+    isolation); 2 and 0 change no lambda.  Without limits the best prefix is
+    the first move (connectivity 7 -> 2)."""
+    h = _hand_moves_graph()
+    g = load(h)
+    rho = np.array([0, 0, 1, 1], np.uint32)
+    r = oracle.refine_pass(g, rho, 2, BIG, BIG)
+    assert r.seq.tolist() == [1, 3, 2, 0]
+    assert r.seq_gain.tolist() == [5, -5, 0, 0]
+    assert r.seq_viol.tolist() == [0, 0, 0, 0]
+    assert (r.n_applied, r.gain) == (1, 5) and r.rho.tolist() == [0, 1, 1, 1]
+    # Omega 2 (unit sizes): after the first move partition 1 holds 3; the
+    # prefixes that are valid again gain nothing, so nothing is applied
+    r = oracle.refine_pass(g, rho, 2, 2, BIG)
+    assert r.seq_viol.tolist() == [1, 0, 1, 0]
+    assert (r.n_applied, r.gain) == (0, 0) and r.rho.tolist() == rho.tolist()
+    # Delta 1: partition 1 starts with two inbound hyperedges (e0 by 2, e1 by
+    # 3); after move 1, e0 has no destination left in partition 0; after move
+    # 3, e1 is inbound to 0 and 1 keeps e0 (by 1 and 2); after move 2, e0 is
+    # inbound to both
+    r = oracle.refine_pass(g, rho, 2, BIG, 1)
+    assert r.seq_viol.tolist() == [1, 0, 1, 1]
+    assert (r.n_applied, r.gain) == (0, 0)
+
+
+def _refine_brute_check(h, rho, k, omega, delta, enforce):
+    edges = brute.edges_of(h.e_off, h.e_nsrc, h.e_pins)
+    g = load(h)
+    r = oracle.refine_pass(g, rho, k, omega, delta, enforce)
+    mv, gn = oracle.moves(g, rho, k, omega, enforce)
+    want = sorted((n for n in range(h.n_nodes) if mv[n] != NONE),
+                  key=lambda n: (-int(gn[n]), n))
+    assert r.seq.tolist() == want
+
+    def state(part):
+        conn, _, psize, pinb, _ = brute.evaluate(h.n_nodes, edges, h.e_w, h.n_size, part, k)
+        return conn, sum(1 for p in range(k) if psize[p] > omega or pinb[p] > delta)
+
+    cur = rho.tolist()
+    conns = [state(cur)[0]]
+    viols = []
+    for i, n in enumerate(want):
+        cur[n] = int(mv[n])
+        c, v = state(cur)
+        conns.append(c)
+        viols.append(v)
+        assert int(r.seq_gain[i]) == conns[i] - conns[i + 1], (i, n)
+        assert int(r.seq_viol[i]) == v, (i, n)
+    # best prefix: largest connectivity drop with no violation, ties shortest
+    best, blen = 0, 0
+    for i in range(len(want)):
+        if viols[i] == 0 and conns[0] - conns[i + 1] > best:
+            best, blen = conns[0] - conns[i + 1], i + 1
+    assert (r.n_applied, r.gain) == (blen, best)
+    out = rho.tolist()
+    for n in want[:blen]:
+        out[n] = int(mv[n])
+    assert r.rho.tolist() == out
+    return r
+
+
+@pytest.mark.parametrize("kw", tiny_cases()[::2], ids=lambda k: "s%d" % k["seed"])
+def test_refine_vs_brute(kw):
+    """Every in-sequence gain equals the connectivity the move removes from the
+    partition left by the moves before it, every violation count the invalid
+    partitions then (both by the set-based evaluator), and the prefix applied
+    is the best valid one."""
+    h = synth.tiny(**kw)
+    grid = constraint_grid(h)
+    for k in (1, 2, 3, max(2, h.n_nodes // 2)):
+        rho = synth.uniform_u32(kw["seed"], 43, h.n_nodes, k)
+        psize = np.bincount(rho, weights=h.n_size, minlength=k)
+        for omega, delta in grid + [(int(psize.max()) + 1, BIG)]:
+            for enforce in (False, True):
+                _refine_brute_check(h, rho, k, omega, delta, enforce)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_refine_never_worsens(seed):
+    """Repeated passes: connectivity never rises, a valid partition stays
+    valid, and the applied gain is the connectivity drop the evaluator sees."""
+    kw = tiny_cases()[seed * 11 % 60]
+    h = synth.tiny(**kw)
+    g = load(h)
+    k = 3
+    rho = synth.uniform_u32(seed, 47, h.n_nodes, k)
+    psize = np.bincount(rho, weights=h.n_size, minlength=k)
+    omega = int(psize.max()) + 2
+    _, _, s0 = oracle.evaluate(g, rho, k, omega, BIG)
+    for _ in range(6):
+        r = oracle.refine_pass(g, rho, k, omega, BIG, enforce_omega=True)
+        _, _, s1 = oracle.evaluate(g, r.rho, k, omega, BIG)
+        assert int(s1[0]) == int(s0[0]) - r.gain and r.gain >= 0
+        assert int(s1[2]) == 0 and int(s1[3]) == 0
+        rho, s0 = r.rho, s1
