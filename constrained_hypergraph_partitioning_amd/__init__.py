@@ -32,7 +32,8 @@ EXPORTS = ["chp_create", "chp_destroy", "chp_last_error", "chp_build_incidence",
            "chp_rate_and_match", "chp_contract", "chp_evaluate_partition", "chp_hgraph_free",
            "chp_set_timing", "chp_get_timings", "chp_reset_timings", "chp_set_batch_entries",
            "chp_last_rate_stats", "chp_set_incidence_rating", "chp_pair_leftovers",
-           "chp_propose_moves", "chp_set_matching", "chp_set_timing_filter"]
+           "chp_propose_moves", "chp_set_matching", "chp_set_timing_filter",
+           "chp_refine_moves"]
 
 
 class ChpError(RuntimeError):
@@ -114,6 +115,12 @@ def load_library(path: str = LIB_PATH):
     lib.chp_propose_moves.argtypes = [P, ctypes.POINTER(HGraphC), P, ctypes.c_uint32,
                                       ctypes.POINTER(Params), I, P, P]
     lib.chp_propose_moves.restype = I
+    lib.chp_refine_moves.argtypes = [P, ctypes.POINTER(HGraphC), P, ctypes.c_uint32,
+                                     ctypes.POINTER(Params), P, P, P, P, P,
+                                     ctypes.POINTER(ctypes.c_uint32),
+                                     ctypes.POINTER(ctypes.c_uint32),
+                                     ctypes.POINTER(ctypes.c_int64)]
+    lib.chp_refine_moves.restype = I
     lib.chp_pair_leftovers.argtypes = [P, ctypes.POINTER(HGraphC), ctypes.POINTER(Params), P, P,
                                        ctypes.POINTER(ctypes.c_uint32)]
     lib.chp_pair_leftovers.restype = I
@@ -339,6 +346,35 @@ class Context:
                                                ctypes.byref(prm), 1 if enforce_omega else 0,
                                                _ptr(move), _ptr(gain)), "propose_moves")
         return move[:N], gain[:N]
+
+    def refine_moves(self, g: HGraph, rho, k, omega, delta, move, gain, details=False):
+        """One refinement pass over the proposed moves (rho updated in place).
+        Returns (moves in the sequence, prefix length applied, its gain), and
+        with details also the device arrays (seq, seq_gain, seq_viol)."""
+        N = g.n_nodes
+        prm = Params(omega, delta, 0, 0)
+        seq = sg = sv = None
+        if details:
+            seq = torch.empty(max(N, 1), dtype=torch.int32, device=self.device)
+            sg = torch.empty(max(N, 1), dtype=torch.int64, device=self.device)
+            sv = torch.empty(max(N, 1), dtype=torch.int32, device=self.device)
+        m, na = ctypes.c_uint32(), ctypes.c_uint32()
+        ga = ctypes.c_int64()
+        self._check(self.lib.chp_refine_moves(self.h, ctypes.byref(g.c), _ptr(rho), int(k),
+                                              ctypes.byref(prm), _ptr(move), _ptr(gain),
+                                              _ptr(seq), _ptr(sg), _ptr(sv), ctypes.byref(m),
+                                              ctypes.byref(na), ctypes.byref(ga)),
+                    "refine_moves")
+        M = int(m.value)
+        out = (M, int(na.value), int(ga.value))
+        if details:
+            return out + (seq[:M], sg[:M], sv[:M])
+        return out
+
+    def refine_pass(self, g: HGraph, rho, k, omega, delta, enforce_omega=False, details=False):
+        """Propose (Eq. 13) then sequence and apply: one pass of refinement."""
+        move, gain = self.propose_moves(g, rho, k, omega, enforce_omega)
+        return self.refine_moves(g, rho, k, omega, delta, move, gain, details)
 
     def pair_leftovers(self, g: HGraph, target, match, omega, delta):
         """Best-effort pairing of the unmatched nodes without a target (match

@@ -930,6 +930,112 @@ int chp_propose_moves(chp_ctx *c, const chp_hgraph *g, const u32 *rho, u32 k,
   });
 }
 
+int chp_refine_moves(chp_ctx *c, const chp_hgraph *g, u32 *rho, u32 k, const chp_params *prm,
+                     const u32 *move, const i64 *gain, u32 *seq, i64 *seq_gain, u32 *seq_viol,
+                     u32 *n_seq_host, u32 *n_applied_host, i64 *gain_host) {
+  return guarded(c, [&] {
+    if (!g || !prm || !n_seq_host || !n_applied_host || !gain_host ||
+        (g->n_nodes && (!rho || !move || !gain))) {
+      set_err(c, "%snull argument");
+      throw Fail{CHP_EINVAL};
+    }
+    *n_seq_host = 0, *n_applied_host = 0, *gain_host = 0;
+    const u32 N = g->n_nodes, E = g->n_edges;
+    if (N == 0) return;
+    if (k == 0) {
+      set_err(c, "%sk must be positive");
+      throw Fail{CHP_EINVAL};
+    }
+    if (N >= (1u << 29)) {
+      set_err(c, "%srefinement needs fewer than 2^29 nodes");
+      throw Fail{CHP_EINVAL};
+    }
+    Scratch s(c);
+    clear_flags(c);
+    // -- the sequence: nodes with a move by (gain desc, id asc)
+    u64 *keys = s.get<u64>(N);
+    u64 *ktmp = s.get<u64>(N);
+    u32 *rank = s.get<u32>(N);
+    u32 *cnt = s.get<u32>(8);  // [0] moves, [1..4] hyperedge classes, [5] v0, [6] best length
+    u64 *best = s.get<u64>(1);
+    u64 *size0 = s.get<u64>(k);
+    u32 *cnt0 = s.get<u32>(k);
+    u32 *inb0 = s.get<u32>(k);
+    u32 *lists = s.get<u32>(3ull * (E ? E : 1));
+    launch_fills(c, {{cnt, 6, 0, false}, {cnt + 6, 2, NONE32, false}, {rank, N, NONE32, false},
+                     {best, 1, 0, true}, {size0, k, 0, true}, {cnt0, k, 0, false},
+                     {inb0, k, 0, false}});
+    launch_seq_keys(c, N, k, rho, move, gain, keys, cnt);
+    if (E) launch_ev_classify(c, E, g->e_off, lists, cnt + 1);
+    launch_check(c, "move sequence keys");
+    u32 hc[8], f = 0;
+    read_many(c, {{hc, cnt, sizeof hc}, {&f, c->flags, sizeof f}});
+    if (f & FLAG_EINVAL)
+      fail_flags(c, FLAG_EINVAL, "rho or move has an entry >= k, or a move to its own partition");
+    if (f & FLAG_EOVERFLOW) fail_flags(c, FLAG_EOVERFLOW, "a gain does not fit in 32 bits");
+    const u32 M = hc[0];
+    *n_seq_host = M;
+    if (M == 0) return;
+    if (hc[4] >= (1u << 30)) {
+      set_err(c, "%srefinement needs hyperedges of fewer than 2^30 pins");
+      throw Fail{CHP_EINVAL};
+    }
+    const u64 *sk = sort_keys_u64(c, keys, ktmp, M);
+    u32 *sq = seq ? seq : s.get<u32>(M);
+    launch_seq_rank(c, M, sk, sq, rank);
+    // -- per hyperedge: in-sequence gains, inbound transitions, starting inbound counts
+    i64 *ingain = s.get<i64>(M);
+    i64 *vdelta = s.get<i64>(M);
+    u32 *dleave = s.get<u32>(M);
+    u32 *denter = s.get<u32>(M);
+    launch_fills(c, {{ingain, M, 0, true}, {vdelta, M, 0, true}, {dleave, M, 0, false},
+                     {denter, M, 0, false}});
+    launch_eval_nodes(c, N, rho, k, g->n_size, size0, cnt0);
+    u64 *escr = nullptr;
+    u32 gg = 1;
+    if (hc[3]) {
+      const u64 per = ev_global_words(hc[4]);
+      const u64 budget = (1ull << 31) / 8;  // words of scratch for the long hyperedges
+      u64 fit = budget / per;
+      gg = hc[3] < 256 ? hc[3] : 256;
+      if (fit < gg) gg = fit ? (u32)fit : 1;
+      escr = s.get<u64>(per * gg);
+    }
+    const u32 ec[4] = {hc[1], hc[2], hc[3], hc[4]};
+    launch_ev_edges(c, E, g->e_off, g->e_nsrc, g->e_pins, g->e_w, rho, move, rank, ingain, dleave,
+                    denter, inb0, lists, cnt + 1, ec, escr, gg);
+    // -- per partition: validity flips along the sequence
+    const u64 Q = 2ull * M;
+    u64 *pk = s.get<u64>(Q);
+    u64 *ptmp = s.get<u64>(Q);
+    i64 *vs = s.get<i64>(Q);
+    i64 *vi = s.get<i64>(Q);
+    i64 *Ps = s.get<i64>(Q + 1);
+    i64 *Pi = s.get<i64>(Q + 1);
+    i64 *Pg = s.get<i64>((u64)M + 1);
+    i64 *Pv = s.get<i64>((u64)M + 1);
+    i64 *stmp = s.get<i64>(scan_tmp_words(Q));
+    launch_pev(c, M, sq, rho, move, pk);
+    const u64 *spk = sort_keys_u64(c, pk, ptmp, Q);
+    launch_pev_vals(c, Q, spk, sq, g->n_size, dleave, denter, vs, vi);
+    scan_i64(c, vs, Ps, Q, stmp);
+    scan_i64(c, vi, Pi, Q, stmp);
+    launch_pev_flips(c, Q, spk, vs, vi, Ps, Pi, size0, inb0, prm->omega, prm->delta, vdelta);
+    launch_viol0(c, k, size0, inb0, prm->omega, prm->delta, cnt + 5);
+    scan_i64(c, ingain, Pg, M, stmp);
+    scan_i64(c, vdelta, Pv, M, stmp);
+    // -- the best valid prefix, applied
+    launch_prefix(c, M, ingain, Pg, vdelta, Pv, cnt + 5, seq_gain, seq_viol, best, cnt + 6, sq,
+                  move, rho);
+    launch_check(c, "refinement");
+    u32 L = NONE32;
+    u64 b = 0;
+    read_many(c, {{&L, cnt + 6, sizeof L}, {&b, best, sizeof b}});
+    *n_applied_host = L == NONE32 ? 0 : L;
+    *gain_host = (i64)b;
+  });
+}
+
 int chp_pair_leftovers(chp_ctx *c, const chp_hgraph *g, const chp_params *prm,
                        const u32 *target, u32 *match, u32 *n_pairs_host) {
   return guarded(c, [&] {

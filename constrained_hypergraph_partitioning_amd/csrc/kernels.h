@@ -135,6 +135,31 @@ void launch_dp_levels(chp_ctx *c, u32 N, const u32 *target, const u64 *score, Dp
 // Device-wide sort of n distinct u64 keys; tmp holds n; returns a or tmp.
 u64 *sort_keys_u64(chp_ctx *c, u64 *a, u64 *tmp, u64 n);
 
+// ---- k_refine.hip : one refinement pass over proposed moves -----------------
+// sequence keys (2^31 - 1 - gain) << 32 | n of the nodes with a move; flags
+// EINVAL for rho or move out of range, EOVERFLOW for a gain beyond 32 bits
+void launch_seq_keys(chp_ctx *c, u32 N, u32 k, const u32 *rho, const u32 *move, const i64 *gain,
+                     u64 *keys, u32 *cnt);
+void launch_seq_rank(chp_ctx *c, u32 M, const u64 *keys, u32 *seq, u32 *rank);
+// hyperedges by event capacity: lists[k * E ..], cnt[0..2], cnt[3] = longest class 2
+void launch_ev_classify(chp_ctx *c, u32 E, const i64 *e_off, u32 *lists, u32 *cnt);
+u64 ev_global_words(u32 max_len);  // scratch words per workgroup of class 2
+void launch_ev_edges(chp_ctx *c, u32 E, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
+                     const u32 *e_w, const u32 *rho, const u32 *move, const u32 *rank,
+                     i64 *ingain, u32 *dleave, u32 *denter, u32 *inb0, const u32 *lists,
+                     const u32 *cnt, const u32 *host_cnt, u64 *scratch, u32 grid_global);
+void launch_pev(chp_ctx *c, u32 M, const u32 *seq, const u32 *rho, const u32 *move, u64 *keys);
+void launch_pev_vals(chp_ctx *c, u64 Q, const u64 *keys, const u32 *seq, const u32 *n_size,
+                     const u32 *dleave, const u32 *denter, i64 *vs, i64 *vi);
+void launch_pev_flips(chp_ctx *c, u64 Q, const u64 *keys, const i64 *vs, const i64 *vi,
+                      const i64 *Ps, const i64 *Pi, const u64 *size0, const u32 *inb0,
+                      u64 omega, u32 delta, i64 *vdelta);
+void launch_viol0(chp_ctx *c, u32 k, const u64 *size0, const u32 *inb0, u64 omega, u32 delta,
+                  u32 *v0);
+void launch_prefix(chp_ctx *c, u32 M, const i64 *ingain, const i64 *Pg, const i64 *vdelta,
+                   const i64 *Pv, const u32 *v0, i64 *seq_gain, u32 *seq_viol, u64 *best,
+                   u32 *best_len, const u32 *seq, const u32 *move, u32 *rho);
+
 // Best-effort pairing of the unmatched nodes without a target: gather their
 // keys (size << 32 | id) into keys (cnt zeroed before), then, once sorted,
 // choose, claim (claim[N] filled with NONE before) and pair into match.

@@ -175,6 +175,34 @@ int chp_rate_and_match(chp_ctx *ctx, const chp_hgraph *g, const chp_params *prm,
 int chp_propose_moves(chp_ctx *ctx, const chp_hgraph *g, const uint32_t *rho, uint32_t k,
                       const chp_params *prm, int enforce_omega, uint32_t *move, int64_t *gain);
 
+/* refine_moves: one refinement pass over proposed moves ([HP] Sec. VI-A,
+ * VI-C, VI-D, Eqs. 14-15), run after chp_propose_moves on the same rho.
+ *  rho[N]      the partition in [0, k); updated in place with the moves applied.
+ *  move[N], gain[N]  as written by chp_propose_moves (CHP_NONE = no move).
+ * The nodes with a move form the sequence, ordered by (gain desc, id asc)
+ * (every chain of length one).  The in-sequence gain of the i-th move is the
+ * connectivity it removes from the partition left by the moves before it:
+ * w(e) for each hyperedge e of the node where it is the last pin left in its
+ * partition, minus w(e) for each one with no pin in the destination yet.  A
+ * partition is invalid while its size exceeds prm->omega or its inbound count
+ * (hyperedges with a destination pin in it) exceeds prm->delta.  The prefix
+ * applied is the one of largest summed in-sequence gain that leaves no
+ * partition invalid; applying nothing (gain 0) is always allowed and ties go
+ * to the shorter prefix.
+ *  seq[N], seq_gain[N], seq_viol[N] (each optional, NULL = not written): the
+ *              nodes in sequence order, their in-sequence gains (int64) and
+ *              the invalid partitions after each move (first *n_seq_host
+ *              entries).
+ *  *n_seq_host moves in the sequence; *n_applied_host the prefix length
+ *              applied; *gain_host its summed gain (the connectivity drop).
+ * Deterministic.  Errors: EINVAL (k == 0, rho or move >= k, a move to its own
+ * partition, N >= 2^29, a hyperedge of 2^30 pins or more), EOVERFLOW (a gain
+ * outside [-2^31, 2^31)).  Synchronises. */
+int chp_refine_moves(chp_ctx *ctx, const chp_hgraph *g, uint32_t *rho, uint32_t k,
+                     const chp_params *prm, const uint32_t *move, const int64_t *gain,
+                     uint32_t *seq, int64_t *seq_gain, uint32_t *seq_viol, uint32_t *n_seq_host,
+                     uint32_t *n_applied_host, int64_t *gain_host);
+
 /* pair_leftovers: best-effort pairing of the nodes left without a partner
  * ([HP] Sec. V-C, last mechanism), run after chp_rate_and_match.
  *  target[N]  as written by chp_rate_and_match (read).

@@ -392,6 +392,128 @@ def test_moves_identity_and_one_part(chp, ctx):
     moves_pair(chp, ctx, dg, og, np.zeros(h.n_nodes, np.uint32), 1, 1 << 30, False, "one part")
 
 
+def refine_pair(chp, ctx, dg, og, rho, k, omega, delta, enforce, tag):
+    """One pass on both sides from the same proposals (the oracle's): the
+    sequence, in-sequence gains, violation counts, prefix and partition must
+    agree.  Returns the partition after the pass."""
+    omv, ogn = oracle.moves(og, rho, k, omega, enforce)
+    want = oracle.refine(og, rho, k, omega, delta, omv, ogn)
+    drho = chp.to_device(rho)
+    M, L, G, seq, sg, sv = ctx.refine_moves(dg, drho, k, omega, delta, chp.to_device(omv),
+                                            chp.to_device(ogn), details=True)
+    assert M == want.seq.shape[0], tag + " sequence length"
+    assert_equal(chp.to_host(seq, np.uint32), want.seq, tag + " seq")
+    assert_equal(chp.to_host(sg, np.uint64).view(np.int64), want.seq_gain, tag + " seq_gain")
+    assert_equal(chp.to_host(sv, np.uint32), want.seq_viol, tag + " seq_viol")
+    assert (L, G) == (want.n_applied, want.gain), tag + " prefix"
+    assert_equal(chp.to_host(drho, np.uint32), want.rho, tag + " rho")
+    return want.rho
+
+
+def test_refine_tiny(chp, ctx):
+    """Refinement passes on the brute-force-pinned tiny graphs: several k,
+    the constraint grid (some partitions start invalid), Omega enforced or
+    not in the proposals."""
+    import test_oracle_pins as pins
+    for kw in pins.tiny_cases():
+        h = synth.tiny(**kw)
+        say("refine tiny", kw["seed"])
+        dg, og = both(chp, ctx, h, 1 << 30, 1 << 30, neighbors=False)
+        for k in (1, 2, 3, max(2, h.n_nodes // 2)):
+            rho = synth.uniform_u32(kw["seed"], 43, h.n_nodes, k)
+            for omega, delta in pins.constraint_grid(h):
+                for enforce in (False, True):
+                    refine_pair(chp, ctx, dg, og, rho, k, omega, delta, enforce,
+                                "tiny%d k%d" % (kw["seed"], k))
+
+
+def _limits(og, rho, k, slack):
+    ps, pi, _ = oracle.evaluate(og, rho, k, 1 << 40, 1 << 30)
+    return int(np.percentile(ps, 70)) + slack, int(np.percentile(pi, 70)) + slack
+
+
+@pytest.mark.parametrize("cfg,nn,k,slack", [(1, None, 200, 2), (2, 20000, 64, 0),
+                                            (2, 20000, 600, 3), (3, 5000, 100, 1),
+                                            (4, 30000, 3000, 1), (5, 8192, 50, 1)])
+def test_refine_scaled(chp, ctx, cfg, nn, k, slack):
+    """Scaled workloads under a random partition: one pass with no limits and
+    its details compared, then two chained passes end to end (device
+    proposals, then the device pass) with Omega enforced and Omega and Delta
+    at the 70th percentile of the starting parts, so some parts start invalid
+    and validity flips along the sequence."""
+    spec = synth.config(cfg, n_nodes=nn)
+    h = synth.generate(spec)
+    say("refine", cfg, nn, k)
+    dg, og = both(chp, ctx, h, spec.omega, spec.delta, neighbors=False)
+    rho = synth.uniform_u32(cfg, 47, h.n_nodes, k)
+    omega, delta = _limits(og, rho, k, slack)
+    refine_pair(chp, ctx, dg, og, rho, k, 1 << 40, 1 << 30, False, "cfg%d detail" % cfg)
+    drho = chp.to_device(rho)
+    for it in range(2):
+        want = oracle.refine_pass(og, rho, k, omega, delta, True)
+        M, L, G = ctx.refine_pass(dg, drho, k, omega, delta, True)
+        tag = "cfg%d pass%d" % (cfg, it)
+        assert (M, L, G) == (want.seq.shape[0], want.n_applied, want.gain), tag
+        assert_equal(chp.to_host(drho, np.uint32), want.rho, tag + " rho")
+        rho = want.rho
+
+
+def test_refine_long_hyperedges(chp, ctx):
+    """Hyperedges in all three event classes (up to 85 pins, up to 2730, and
+    longer: a global sort), many of their pins moving."""
+    say("refine long hyperedges")
+    rng = np.random.Generator(np.random.PCG64(8))
+    n = 12000
+    el = []
+    for ln in (3000, 9000, 2700, 200, 86, 85):
+        p = rng.permutation(n)[:ln]
+        el.append(([int(p[0])], [int(x) for x in p[1:]]))
+    for _ in range(6000):
+        p = rng.permutation(n)[: int(rng.integers(2, 12))]
+        el.append(([int(p[0])], [int(x) for x in p[1:]]))
+    h = synth.from_lists(n, el, rng.integers(1, 5, len(el)).tolist())
+    dg, og = both(chp, ctx, h, 1 << 30, 1 << 30, neighbors=False)
+    for k in (3, 40, 2000):
+        rho = synth.uniform_u32(k, 5, n, k)
+        omega, delta = _limits(og, rho, k, 1)
+        refine_pair(chp, ctx, dg, og, rho, k, 1 << 40, 1 << 30, False, "long k%d" % k)
+        refine_pair(chp, ctx, dg, og, rho, k, omega, delta, True, "long lim k%d" % k)
+
+
+def test_refine_edge_cases(chp, ctx):
+    """One part (no move), one node, every node alone, and the error paths
+    (a move to its own part, rho out of range)."""
+    spec = synth.config(2, n_nodes=3000)
+    h = synth.generate(spec)
+    dg, og = both(chp, ctx, h, spec.omega, spec.delta, neighbors=False)
+    say("refine one part")
+    z = np.zeros(h.n_nodes, np.uint32)
+    assert refine_pair(chp, ctx, dg, og, z, 1, 1 << 30, 1 << 30, False, "one part").tolist() \
+        == z.tolist()
+    say("refine identity")
+    ident = np.arange(h.n_nodes, dtype=np.uint32)
+    refine_pair(chp, ctx, dg, og, ident, h.n_nodes, 1 << 30, 1 << 30, False, "identity")
+    refine_pair(chp, ctx, dg, og, ident, h.n_nodes, 2, 1 << 30, True, "identity omega")
+    say("refine one node")
+    h1 = synth.from_lists(1, [], [])
+    dg1, og1 = both(chp, ctx, h1, 4, 4, neighbors=False)
+    refine_pair(chp, ctx, dg1, og1, np.zeros(1, np.uint32), 2, 4, 4, False, "one node")
+    say("refine errors")
+    mv = np.zeros(h.n_nodes, np.uint32)
+    gn = np.zeros(h.n_nodes, np.int64)
+    with pytest.raises(chp.ChpError) as ex:
+        ctx.refine_moves(dg, chp.to_device(z), 2, 1 << 30, 1 << 30, chp.to_device(mv),
+                         chp.to_device(gn))
+    assert ex.value.code == -1
+    bad = z.copy()
+    bad[7] = 5
+    with pytest.raises(chp.ChpError) as ex:
+        ctx.refine_moves(dg, chp.to_device(bad), 2, 1 << 30, 1 << 30,
+                         chp.to_device(np.full(h.n_nodes, 0xFFFFFFFF, np.uint32)),
+                         chp.to_device(gn))
+    assert ex.value.code == -1
+
+
 def test_tiny_graphs(chp, ctx):
     import test_oracle_pins as pins
     for kw in pins.tiny_cases():
