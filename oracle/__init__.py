@@ -80,7 +80,7 @@ def _load():
             "or_pair_leftovers": [u32, P, P, P, u64, u32, u32, P, ctypes.POINTER(u64)],
             "or_moves": [E, P, P, P, u32, u64, i32, P, P],
             "or_match_dp": [u32, P, P, P, ctypes.POINTER(u64)],
-            "or_refine": [E, P, P, P, P, u32, u64, u32, P, P, P, P, P,
+            "or_refine": [E, P, P, P, P, u32, u64, u32, P, P, i32, P, P, P, P,
                           ctypes.POINTER(u32), ctypes.POINTER(u32),
                           ctypes.POINTER(ctypes.c_int64), P],
         }
@@ -327,18 +327,21 @@ def moves(g: Graph, rho, k, omega, enforce_omega=False):
 class Refinement:
     rho: np.ndarray        # the partition after the pass
     seq: np.ndarray        # nodes in sequence order
+    seq_chain: np.ndarray  # rank of each position's chain
     seq_gain: np.ndarray   # in-sequence gain of each move (int64)
     seq_viol: np.ndarray   # invalid partitions after each move
     n_applied: int         # length of the prefix applied
     gain: int              # its summed in-sequence gain
 
 
-def refine(g: Graph, rho, k, omega, delta, move, gain) -> Refinement:
-    """O14: sequence the proposed moves, take their in-sequence gains and the
-    violations after every prefix, and apply the best valid prefix."""
+def refine(g: Graph, rho, k, omega, delta, move, gain, chained=True) -> Refinement:
+    """O14: sequence the proposed moves (as chains, O15, or by gain alone),
+    take their in-sequence gains and the violations after every prefix, and
+    apply the best valid prefix."""
     N = g.n_nodes
     r = np.ascontiguousarray(rho, np.uint32)
     seq = np.empty(N, np.uint32)
+    sc = np.empty(N, np.uint32)
     sg = np.empty(N, np.int64)
     sv = np.empty(N, np.uint32)
     out = np.empty(N, np.uint32)
@@ -346,18 +349,20 @@ def refine(g: Graph, rho, k, omega, delta, move, gain) -> Refinement:
     v = g.view()
     _check(_load().or_refine(ctypes.byref(v), _p(g.n_off), _p(g.n_nin), _p(g.n_inc), _p(r), k,
                              omega, delta, _p(np.ascontiguousarray(move, np.uint32)),
-                             _p(np.ascontiguousarray(gain, np.int64)), _p(seq), _p(sg), _p(sv),
+                             _p(np.ascontiguousarray(gain, np.int64)), 1 if chained else 0,
+                             _p(seq), _p(sc), _p(sg), _p(sv),
                              ctypes.byref(m), ctypes.byref(na), ctypes.byref(ga), _p(out)),
            "refine")
     M = int(m.value)
-    return Refinement(out if N else r.copy(), seq[:M], sg[:M], sv[:M], int(na.value),
+    return Refinement(out if N else r.copy(), seq[:M], sc[:M], sg[:M], sv[:M], int(na.value),
                       int(ga.value))
 
 
-def refine_pass(g: Graph, rho, k, omega, delta, enforce_omega=False) -> Refinement:
+def refine_pass(g: Graph, rho, k, omega, delta, enforce_omega=False,
+                chained=True) -> Refinement:
     """One pass of refinement: propose (O12), then sequence and apply (O14)."""
     mv, gn = moves(g, rho, k, omega, enforce_omega)
-    return refine(g, rho, k, omega, delta, mv, gn)
+    return refine(g, rho, k, omega, delta, mv, gn, chained)
 
 
 LEFTOVER_WINDOW = 64  # positions a leftover node scans below its slack position

@@ -997,6 +997,148 @@ static int cmp_mv(const void *x, const void *y) { /* gain descending, id ascendi
   return a->id < b->id ? -1 : (a->id > b->id ? 1 : 0);
 }
 
+/*
+ * O15 -- move chains ([P1] Sec. VI-C, Fig. 5): the sequence as chains of
+ * moves, each departing from the destination of the one before.
+ *  - The moves are sorted by (source partition, gain desc, id asc).
+ *  - Each move gets at most one predecessor and one successor.  In a round,
+ *    every move without a successor (a free end) looks at the first
+ *    CHAIN_WINDOW moves of the sorted run leaving its destination, takes
+ *    those still without a predecessor, and picks the one of largest grade
+ *      gain(m) - 1e-6 |size(n) - size(m)| - 1e-7 ||in(n)| - |in(m)||
+ *    (kept exact as 10^7 times that, an integer; ties to the smaller id m).
+ *    A move picked by several goes to the largest (grade, picker id); the
+ *    winner links to it.  Rounds repeat up to CHAIN_ROUNDS times, or until a
+ *    round links nothing.
+ *  - The links form disjoint paths and cycles.  A path starts at its move
+ *    without a predecessor, a cycle at its smallest node id; both follow the
+ *    successor links.  Chains are ranked by total gain (desc), then by their
+ *    first node (asc), and concatenated.
+ * seq[M] gets the nodes in order and seq_chain[M] (optional) the rank of
+ * each one's chain.  The window, the tie rules and where a cycle starts are
+ * readings; the pages fix the grade, its weights, the window size of 256
+ * and the 16 rounds.
+ */
+#define CHAIN_WINDOW 256
+#define CHAIN_ROUNDS 16
+
+typedef struct {
+  uint32_t part, id;
+  int64_t gain;
+} or_smv;
+
+static int cmp_smv(const void *x, const void *y) { /* part asc, gain desc, id asc */
+  const or_smv *a = (const or_smv *)x, *b = (const or_smv *)y;
+  if (a->part != b->part) return a->part < b->part ? -1 : 1;
+  if (a->gain != b->gain) return a->gain > b->gain ? -1 : 1;
+  return a->id < b->id ? -1 : (a->id > b->id ? 1 : 0);
+}
+
+typedef struct {
+  int64_t total;
+  uint32_t first, len, start; /* first node, members, position of the first in order[] */
+} or_chain;
+
+static int cmp_chain(const void *x, const void *y) { /* total desc, first node asc */
+  const or_chain *a = (const or_chain *)x, *b = (const or_chain *)y;
+  if (a->total != b->total) return a->total > b->total ? -1 : 1;
+  return a->first < b->first ? -1 : (a->first > b->first ? 1 : 0);
+}
+
+static int64_t grade_fx(uint32_t n, uint32_t m, const uint32_t *size, const uint32_t *nin,
+                        const int64_t *gain) {
+  const int64_t ds = size[n] > size[m] ? (int64_t)size[n] - size[m] : (int64_t)size[m] - size[n];
+  const int64_t di = nin[n] > nin[m] ? (int64_t)nin[n] - nin[m] : (int64_t)nin[m] - nin[n];
+  return 10000000ll * gain[m] - 10 * ds - di;
+}
+
+static int or_chain_order(uint32_t N, const uint32_t *size, const uint32_t *nin,
+                          const uint32_t *rho, uint32_t k, const uint32_t *move,
+                          const int64_t *gain, uint32_t *seq, uint32_t *seq_chain) {
+  or_smv *srt = (or_smv *)malloc(sizeof(or_smv) * (N ? N : 1));
+  int64_t *pstart = (int64_t *)malloc(sizeof(int64_t) * ((size_t)k + 1));
+  uint32_t *pred = (uint32_t *)malloc(sizeof(uint32_t) * (N ? N : 1));
+  uint32_t *succ = (uint32_t *)malloc(sizeof(uint32_t) * (N ? N : 1));
+  uint32_t *pick = (uint32_t *)malloc(sizeof(uint32_t) * (N ? N : 1));
+  uint32_t *winner = (uint32_t *)malloc(sizeof(uint32_t) * (N ? N : 1));
+  int64_t *wgrade = (int64_t *)malloc(sizeof(int64_t) * (N ? N : 1));
+  uint8_t *seen = (uint8_t *)calloc(N ? N : 1, 1);
+  or_chain *ch = (or_chain *)malloc(sizeof(or_chain) * (N ? N : 1));
+  uint32_t *order = (uint32_t *)malloc(sizeof(uint32_t) * (N ? N : 1));
+  if (!srt || !pstart || !pred || !succ || !pick || !winner || !wgrade || !seen || !ch || !order) {
+    free(srt), free(pstart), free(pred), free(succ), free(pick), free(winner), free(wgrade);
+    free(seen), free(ch), free(order);
+    return OR_ENOMEM;
+  }
+  uint32_t M = 0;
+  for (uint32_t n = 0; n < N; ++n) {
+    pred[n] = succ[n] = NONE;
+    if (move[n] != NONE) srt[M].part = rho[n], srt[M].id = n, srt[M].gain = gain[n], ++M;
+  }
+  qsort(srt, M, sizeof(or_smv), cmp_smv);
+  /* pstart[p] = first position whose source partition is >= p */
+  uint32_t i = 0;
+  for (uint32_t p = 0; p <= k; ++p) {
+    while (i < M && srt[i].part < p) ++i;
+    pstart[p] = i;
+  }
+  for (int round = 0; round < CHAIN_ROUNDS; ++round) {
+    for (uint32_t n = 0; n < N; ++n) pick[n] = NONE, winner[n] = NONE;
+    /* every free end picks from its window, with the links of the round before */
+    for (uint32_t j = 0; j < M; ++j) {
+      const uint32_t n = srt[j].id;
+      if (succ[n] != NONE) continue;
+      const uint32_t d = move[n];
+      int64_t a = pstart[d], b = pstart[d + 1];
+      if (b - a > CHAIN_WINDOW) b = a + CHAIN_WINDOW;
+      int64_t bg = 0;
+      for (int64_t t = a; t < b; ++t) {
+        const uint32_t m = srt[t].id;
+        if (pred[m] != NONE) continue;
+        const int64_t gr = grade_fx(n, m, size, nin, gain);
+        if (pick[n] == NONE || gr > bg || (gr == bg && m < pick[n])) pick[n] = m, bg = gr;
+      }
+    }
+    /* each picked move goes to the largest (grade, picker) */
+    for (uint32_t n = 0; n < N; ++n) {
+      const uint32_t m = pick[n];
+      if (m == NONE) continue;
+      const int64_t gr = grade_fx(n, m, size, nin, gain);
+      if (winner[m] == NONE || gr > wgrade[m] || (gr == wgrade[m] && n > winner[m]))
+        winner[m] = n, wgrade[m] = gr;
+    }
+    uint32_t links = 0;
+    for (uint32_t m = 0; m < N; ++m)
+      if (winner[m] != NONE) succ[winner[m]] = m, pred[m] = winner[m], ++links;
+    if (links == 0) break;
+  }
+  /* chains: paths from their head, then cycles from their smallest node */
+  uint32_t nch = 0, pos = 0;
+  for (int pass = 0; pass < 2; ++pass)
+    for (uint32_t n = 0; n < N; ++n) {
+      if (move[n] == NONE || seen[n]) continue;
+      if (pass == 0 && pred[n] != NONE) continue; /* not a path head */
+      ch[nch].first = n, ch[nch].start = pos, ch[nch].len = 0, ch[nch].total = 0;
+      for (uint32_t v = n; v != NONE && !seen[v]; v = succ[v]) {
+        seen[v] = 1;
+        order[pos++] = v;
+        ch[nch].len++;
+        ch[nch].total += gain[v];
+      }
+      ++nch;
+    }
+  qsort(ch, nch, sizeof(or_chain), cmp_chain);
+  uint32_t o = 0;
+  for (uint32_t c = 0; c < nch; ++c)
+    for (uint32_t t = 0; t < ch[c].len; ++t) {
+      if (seq_chain) seq_chain[o] = c;
+      seq[o++] = order[ch[c].start + t];
+    }
+  free(srt), free(pstart), free(pred), free(succ), free(pick), free(winner), free(wgrade);
+  free(seen), free(ch), free(order);
+  return o == M ? OR_OK : OR_EINTERNAL;
+}
+
 /* pins of e in partition p under part[], all pins or destinations only */
 static uint32_t count_in(const or_edges *g, const uint32_t *part, uint32_t e, uint32_t p,
                          int dst_only) {
@@ -1008,9 +1150,9 @@ static uint32_t count_in(const or_edges *g, const uint32_t *part, uint32_t e, ui
 
 int or_refine(const or_edges *g, const int64_t *n_off, const uint32_t *n_nin,
               const uint32_t *n_inc, const uint32_t *rho, uint32_t k, uint64_t omega,
-              uint32_t delta, const uint32_t *move, const int64_t *gain, uint32_t *seq,
-              int64_t *seq_gain, uint32_t *seq_viol, uint32_t *n_seq, uint32_t *n_applied,
-              int64_t *gain_applied, uint32_t *rho_out) {
+              uint32_t delta, const uint32_t *move, const int64_t *gain, int chained,
+              uint32_t *seq, uint32_t *seq_chain, int64_t *seq_gain, uint32_t *seq_viol,
+              uint32_t *n_seq, uint32_t *n_applied, int64_t *gain_applied, uint32_t *rho_out) {
   const uint32_t N = g->n_nodes, E = g->n_edges;
   *n_seq = 0, *n_applied = 0, *gain_applied = 0;
   for (uint32_t n = 0; n < N; ++n) {
@@ -1030,8 +1172,19 @@ int or_refine(const or_edges *g, const int64_t *n_off, const uint32_t *n_nin,
   uint32_t M = 0;
   for (uint32_t n = 0; n < N; ++n)
     if (move[n] != NONE) mv[M].gain = gain[n], mv[M].id = n, ++M;
-  qsort(mv, M, sizeof(or_mv), cmp_mv);
-  for (uint32_t i = 0; i < M; ++i) seq[i] = mv[i].id;
+  if (chained) {
+    const int rc = or_chain_order(N, g->n_size, n_nin, rho, k, move, gain, seq, seq_chain);
+    if (rc != OR_OK) {
+      free(mv), free(cur), free(psize), free(pinb), free(mark);
+      return rc;
+    }
+  } else {
+    qsort(mv, M, sizeof(or_mv), cmp_mv);
+    for (uint32_t i = 0; i < M; ++i) {
+      seq[i] = mv[i].id;
+      if (seq_chain) seq_chain[i] = i;
+    }
+  }
   /* the starting state */
   for (uint32_t n = 0; n < N; ++n) cur[n] = rho[n], psize[rho[n]] += g->n_size[n];
   for (uint32_t p = 0; p < k; ++p) mark[p] = NONE;

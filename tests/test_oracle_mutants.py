@@ -59,8 +59,8 @@ MUTANTS = {
     "dp_ss1_without_children": ("      ss1[n] = score[n] + A[n];", "      ss1[n] = score[n];"),
     "dp_roots_never_take_children": ("        if (bestc[n] != NONE && bestv[n] > 0) match[n] = bestc[n], match[bestc[n]] = n;\n        if (bestc[t] != NONE && bestv[t] > 0) match[t] = bestc[t], match[bestc[t]] = t;",
                                      ";"),
-    "refine_order_gain_ascending": ("if (a->gain != b->gain) return a->gain > b->gain ? -1 : 1;",
-                                    "if (a->gain != b->gain) return a->gain < b->gain ? -1 : 1;"),
+    "refine_order_gain_ascending": ("const or_mv *a = (const or_mv *)x, *b = (const or_mv *)y;\n  if (a->gain != b->gain) return a->gain > b->gain ? -1 : 1;",
+                                    "const or_mv *a = (const or_mv *)x, *b = (const or_mv *)y;\n  if (a->gain != b->gain) return a->gain < b->gain ? -1 : 1;"),
     "refine_gain_in_isolation": ("      if (count_in(g, cur, e, ps, 0) == 1) gi += g->e_w[e];\n      if (count_in(g, cur, e, pd, 0) == 0) gi -= g->e_w[e];",
                                  "      if (count_in(g, rho, e, ps, 0) == 1) gi += g->e_w[e];\n      if (count_in(g, rho, e, pd, 0) == 0) gi -= g->e_w[e];"),
     "refine_inbound_all_pins": ("      if (count_in(g, cur, e, ps, 1) == 1) pinb[ps]--;\n      if (count_in(g, cur, e, pd, 1) == 0) pinb[pd]++;",
@@ -71,6 +71,25 @@ MUTANTS = {
                                   "if (run > best) best = run, best_len = i + 1;"),
     "refine_viol_omega_off_by_one": ("    viol += psize[ps] > omega || pinb[ps] > delta;\n    viol += psize[pd] > omega || pinb[pd] > delta;",
                                      "    viol += psize[ps] > omega + 1 || pinb[ps] > delta;\n    viol += psize[pd] > omega + 1 || pinb[pd] > delta;"),
+    "chain_window_255": ("#define CHAIN_WINDOW 256", "#define CHAIN_WINDOW 255"),
+    "chain_window_257": ("#define CHAIN_WINDOW 256", "#define CHAIN_WINDOW 257"),
+    "chain_one_round": ("#define CHAIN_ROUNDS 16", "#define CHAIN_ROUNDS 1"),
+    "chain_conflict_smaller_picker": ("if (winner[m] == NONE || gr > wgrade[m] || (gr == wgrade[m] && n > winner[m]))",
+                                      "if (winner[m] == NONE || gr > wgrade[m] || (gr == wgrade[m] && n < winner[m]))"),
+    "chain_pick_larger_id": ("if (pick[n] == NONE || gr > bg || (gr == bg && m < pick[n])) pick[n] = m, bg = gr;",
+                             "if (pick[n] == NONE || gr > bg || (gr == bg && m > pick[n])) pick[n] = m, bg = gr;"),
+    "chain_grade_no_inbound": ("return 10000000ll * gain[m] - 10 * ds - di;", "return 10000000ll * gain[m] - 10 * ds;"),
+    "chain_grade_alpha_equals_beta": ("return 10000000ll * gain[m] - 10 * ds - di;", "return 10000000ll * gain[m] - ds - di;"),
+    "chain_grade_alpha_large": ("return 10000000ll * gain[m] - 10 * ds - di;", "return 10000000ll * gain[m] - 100 * ds - di;"),
+    "chain_grade_gain_scale": ("return 10000000ll * gain[m] - 10 * ds - di;", "return 100000000ll * gain[m] - 10 * ds - di;"),
+    "chain_grade_of_picker": ("return 10000000ll * gain[m] - 10 * ds - di;", "return 10000000ll * gain[n] - 10 * ds - di;"),
+    "chain_rank_ascending": ("if (a->total != b->total) return a->total > b->total ? -1 : 1;",
+                             "if (a->total != b->total) return a->total < b->total ? -1 : 1;"),
+    "chain_rank_ties_larger_first": ("return a->first < b->first ? -1 : (a->first > b->first ? 1 : 0);\n}\n\nstatic int64_t grade_fx",
+                                     "return a->first > b->first ? -1 : (a->first < b->first ? 1 : 0);\n}\n\nstatic int64_t grade_fx"),
+    "chain_window_of_source": ("const uint32_t d = move[n];\n      int64_t a = pstart[d]", "const uint32_t d = rho[n];\n      int64_t a = pstart[d]"),
+    "chain_sorted_gain_ascending": ("if (a->gain != b->gain) return a->gain > b->gain ? -1 : 1;\n  return a->id < b->id ? -1 : (a->id > b->id ? 1 : 0);\n}\n\ntypedef struct {\n  int64_t total;",
+                                    "if (a->gain != b->gain) return a->gain < b->gain ? -1 : 1;\n  return a->id < b->id ? -1 : (a->id > b->id ? 1 : 0);\n}\n\ntypedef struct {\n  int64_t total;"),
     "moves_omega_without_node": ("if (enforce_omega && psize[p] + g->n_size[n] > omega) continue;",
                                  "if (enforce_omega && psize[p] > omega) continue;"),
 }
@@ -102,8 +121,12 @@ def _checks():
     for seed in range(12):
         pins.test_match_dp_vs_brute(seed)
     pins.test_refine_hand_example()
+    pins.test_chain_hand_examples()
+    pins.test_chain_window()
+    pins.test_chain_grade_weights()
     for kw in pins.tiny_cases()[:24:2]:
-        pins.test_refine_vs_brute(kw)
+        pins.test_refine_vs_brute(kw, False)
+        pins.test_refine_vs_brute(kw, True)
 
 
 def _build_mutant(name, tmpdir):

@@ -748,41 +748,157 @@ def test_match_dp_on_proposals(kw):
 # ---- O14: one refinement pass ([HP] Sec. VI-A, VI-C, VI-D; Eqs. 14-15)
 def test_refine_hand_example():
     """Worked by hand on the graph of the move example, rho = [0, 0, 1, 1]:
-    proposals (1 -> 1, gain 5), (3 -> 0, 5), (2 -> 0, 2), (0 -> 1, 0) give the
-    sequence 1, 3, 2, 0.  Moving 1 first frees e1 of partition 0 (+5); then
-    3 re-enters partition 0 on e1, where 1 no longer is (-5 in sequence, +5 in
-    isolation); 2 and 0 change no lambda.  Without limits the best prefix is
-    the first move (connectivity 7 -> 2)."""
+    proposals (1 -> 1, gain 5), (3 -> 0, 5), (2 -> 0, 2), (0 -> 1, 0).
+
+    By gain alone the sequence is 1, 3, 2, 0.  Moving 1 first frees e1 of
+    partition 0 (+5); then 3 re-enters partition 0 on e1, where 1 no longer is
+    (-5 in sequence, +5 in isolation); 2 and 0 change no lambda.  Without
+    limits the best prefix is the first move (connectivity 7 -> 2).
+
+    As chains (|in| of nodes 0..3 is 0, 1, 1, 1; all sizes 1): 1 and 3 pick
+    each other (grade 5e7 each; 0's bid for 3 is 1e-7 lower), 2's bid for 1
+    ties 3's and loses to the larger id; next round 0 and 2 pick each other.
+    Two swaps: [1, 3] (total 10), then [0, 2] (total 2), so 1, 3, 0, 2 with
+    in-sequence gains 5, -5, 2, -2."""
     h = _hand_moves_graph()
     g = load(h)
     rho = np.array([0, 0, 1, 1], np.uint32)
-    r = oracle.refine_pass(g, rho, 2, BIG, BIG)
+    r = oracle.refine_pass(g, rho, 2, BIG, BIG, chained=False)
     assert r.seq.tolist() == [1, 3, 2, 0]
     assert r.seq_gain.tolist() == [5, -5, 0, 0]
     assert r.seq_viol.tolist() == [0, 0, 0, 0]
     assert (r.n_applied, r.gain) == (1, 5) and r.rho.tolist() == [0, 1, 1, 1]
     # Omega 2 (unit sizes): after the first move partition 1 holds 3; the
     # prefixes that are valid again gain nothing, so nothing is applied
-    r = oracle.refine_pass(g, rho, 2, 2, BIG)
+    r = oracle.refine_pass(g, rho, 2, 2, BIG, chained=False)
     assert r.seq_viol.tolist() == [1, 0, 1, 0]
     assert (r.n_applied, r.gain) == (0, 0) and r.rho.tolist() == rho.tolist()
     # Delta 1: partition 1 starts with two inbound hyperedges (e0 by 2, e1 by
     # 3); after move 1, e0 has no destination left in partition 0; after move
     # 3, e1 is inbound to 0 and 1 keeps e0 (by 1 and 2); after move 2, e0 is
     # inbound to both
-    r = oracle.refine_pass(g, rho, 2, BIG, 1)
+    r = oracle.refine_pass(g, rho, 2, BIG, 1, chained=False)
     assert r.seq_viol.tolist() == [1, 0, 1, 1]
     assert (r.n_applied, r.gain) == (0, 0)
+    # the chained order
+    r = oracle.refine_pass(g, rho, 2, BIG, BIG)
+    assert r.seq.tolist() == [1, 3, 0, 2] and r.seq_chain.tolist() == [0, 0, 1, 1]
+    assert r.seq_gain.tolist() == [5, -5, 2, -2]
+    assert (r.n_applied, r.gain) == (1, 5)
+    # Delta 1: moving source-only node 0 keeps both partitions at one inbound
+    # hyperedge, so the prefix 1, 3, 0 is valid and gains 2
+    r = oracle.refine_pass(g, rho, 2, BIG, 1)
+    assert r.seq_viol.tolist() == [1, 0, 0, 1]
+    assert (r.n_applied, r.gain) == (3, 2) and r.rho.tolist() == [1, 1, 1, 0]
 
 
-def _refine_brute_check(h, rho, k, omega, delta, enforce):
+def _chain(n, rho, move, gain, edges=(), sizes=None):
+    h = synth.from_lists(n, list(edges), [1] * len(edges), sizes)
+    g = load(h)
+    k = max(max(rho), max(m for m in move if m != NONE)) + 1
+    r = oracle.refine(g, np.array(rho, np.uint32), k, BIG, BIG,
+                      np.array(move, np.uint32), np.array(gain, np.int64))
+    return r.seq.tolist(), r.seq_chain.tolist()
+
+
+def test_chain_hand_examples():
+    """Chains worked by hand (unit sizes, no hyperedges, so grades are 1e7
+    times the successor's gain).  Moves 0: 0->1 (5), 1: 1->0 (3), 2: 1->2 (4),
+    3: 2->0 (1), 4: 0->2 (2).  Round 1: 0 picks 2; 4 and 2 both pick 3 (equal
+    grades, the larger picker 4 wins); 1 and 3 both pick 0 (3 wins).  Round 2:
+    1 picks 4, the only move out of partition 0 still without a predecessor;
+    2 finds none.  One path 1, 4, 3, 0, 2."""
+    seq, ch = _chain(5, [0, 1, 1, 2, 0], [1, 0, 2, 0, 2], [5, 3, 4, 1, 2])
+    assert seq == [1, 4, 3, 0, 2] and ch == [0] * 5
+    # a picker with two equal candidates takes the smaller id: 0 -> 1, then 2
+    seq, ch = _chain(3, [0, 1, 1], [1, 2, 2], [0, 0, 0])
+    assert seq == [0, 1, 2] and ch == [0, 0, 1]
+    # a swap is a two-cycle, started at its smaller node
+    seq, ch = _chain(2, [1, 0], [0, 1], [1, 1])
+    assert seq == [0, 1] and ch == [0, 0]
+    # moves 0: 0->1 (1), 1: 1->0 (2), 2: 2->3 (0), 3: 3->2 (3), 4: 4->0 (0),
+    # 5: 5->4 (0).  1 and 4 both bid 1e7 for 0 and 4 wins; 2 and 3 swap.  The
+    # path 5, 4, 0, 1 and the cycle 2, 3 both total 3: the cycle's first node
+    # (2) is smaller, so it goes first
+    seq, ch = _chain(6, [0, 1, 2, 3, 4, 5], [1, 0, 3, 2, 0, 4], [1, 2, 0, 3, 0, 0])
+    assert seq == [2, 3, 5, 4, 0, 1] and ch == [0, 0, 1, 1, 1, 1]
+
+
+def test_chain_window():
+    """The window is the first 256 moves (by gain desc, id asc) leaving the
+    destination.  Nodes 0..299 move 0 -> 1 with gain 0; node 300 moves 1 -> 0.
+    Node 300 (size 100) picks, among ids 0..255, the closest size: 255 (102);
+    256 (101) and 280 (100) lie outside.  Every move out of 0 bids for 300 and
+    280 wins (grade 0).  One chain 280, 300, 255; the rest alone, by id."""
+    n = 301
+    sizes = [105] * n
+    sizes[255], sizes[256], sizes[280], sizes[300] = 102, 101, 100, 100
+    rho = [0] * 300 + [1]
+    move = [1] * 300 + [0]
+    seq, ch = _chain(n, rho, move, [0] * n, sizes=sizes)
+    want = [v for v in range(280) if v != 255] + [280, 300, 255] + list(range(281, 300))
+    assert seq == want
+    assert ch[278:283] == [278, 279, 279, 279, 280]
+    # the window holds the highest gains: nodes 200..299 gain 1 and come
+    # first, then 0..155.  Node 300 picks 290 (gain 1, same size), 290 wins
+    # the bids for 300: a two-cycle of total 1, ranked among the gain-1 nodes
+    gain = [0] * 200 + [1] * 100 + [0]
+    sizes = [105] * n
+    sizes[290] = sizes[300] = 100
+    seq, ch = _chain(n, rho, move, gain, sizes=sizes)
+    assert seq == list(range(200, 290)) + [290, 300] + list(range(291, 300)) + list(range(200))
+
+
+def test_chain_grade_weights():
+    """The grade gain - 1e-6 |size diff| - 1e-7 ||in| diff|, exactly.  Node 0
+    (size 10, |in| 0) moves 0 -> 1; candidates 1 and 2 move 1 -> 0 (gain 0)
+    and node 3 holds the hyperedges that give |in|."""
+    def case(size1, nin2, gain1=0):
+        edges = [([3], [2])] * nin2
+        sizes = [10, size1, 10, 1]
+        return _chain(4, [0, 1, 1, 0], [1, 0, 0, 0xFFFFFFFF], [0, gain1, 0, 0],
+                      edges, sizes)[0]
+    # size off by 1 (-10e-7) against |in| off by 9 (-9e-7): 2 is closer
+    assert case(11, 9) == [0, 2, 1]
+    # against |in| off by 11: 1 is closer
+    assert case(11, 11) == [0, 1, 2]
+    # gain 1 (1e7 e-7) against a size gap of 1,000,001 (1e7 + 10 e-7): 2
+    assert case(10 + 1000001, 0, gain1=1) == [1, 0, 2]
+
+
+def _refine_brute_check(h, rho, k, omega, delta, enforce, chained):
     edges = brute.edges_of(h.e_off, h.e_nsrc, h.e_pins)
     g = load(h)
-    r = oracle.refine_pass(g, rho, k, omega, delta, enforce)
+    r = oracle.refine_pass(g, rho, k, omega, delta, enforce, chained)
     mv, gn = oracle.moves(g, rho, k, omega, enforce)
-    want = sorted((n for n in range(h.n_nodes) if mv[n] != NONE),
-                  key=lambda n: (-int(gn[n]), n))
-    assert r.seq.tolist() == want
+    moving = [n for n in range(h.n_nodes) if mv[n] != NONE]
+    seq = r.seq.tolist()
+    assert sorted(seq) == moving
+    if not chained:
+        assert seq == sorted(moving, key=lambda n: (-int(gn[n]), n))
+    else:
+        # chains: consecutive members link (source of the next = destination
+        # of the one before) to a successor within the window; chains ranked
+        # by total gain desc, then first node asc
+        srt = sorted(moving, key=lambda n: (int(rho[n]), -int(gn[n]), n))
+        pos = {n: i for i, n in enumerate(srt)}
+        first = {}
+        for n in srt:
+            first.setdefault(int(rho[n]), pos[n])
+        ch = r.seq_chain.tolist()
+        assert ch == sorted(ch) and (not ch or ch[0] == 0)
+        for i in range(1, len(seq)):
+            if ch[i] == ch[i - 1]:
+                a, b = seq[i - 1], seq[i]
+                assert int(rho[b]) == int(mv[a])
+                assert pos[b] - first[int(rho[b])] < 256
+        totals = {}
+        heads = {}
+        for c, n in zip(ch, seq):
+            totals[c] = totals.get(c, 0) + int(gn[n])
+            heads.setdefault(c, n)
+        keys = [(-totals[c], heads[c]) for c in sorted(totals)]
+        assert keys == sorted(keys)
 
     def state(part):
         conn, _, psize, pinb, _ = brute.evaluate(h.n_nodes, edges, h.e_w, h.n_size, part, k)
@@ -791,7 +907,7 @@ def _refine_brute_check(h, rho, k, omega, delta, enforce):
     cur = rho.tolist()
     conns = [state(cur)[0]]
     viols = []
-    for i, n in enumerate(want):
+    for i, n in enumerate(seq):
         cur[n] = int(mv[n])
         c, v = state(cur)
         conns.append(c)
@@ -800,23 +916,25 @@ def _refine_brute_check(h, rho, k, omega, delta, enforce):
         assert int(r.seq_viol[i]) == v, (i, n)
     # best prefix: largest connectivity drop with no violation, ties shortest
     best, blen = 0, 0
-    for i in range(len(want)):
+    for i in range(len(seq)):
         if viols[i] == 0 and conns[0] - conns[i + 1] > best:
             best, blen = conns[0] - conns[i + 1], i + 1
     assert (r.n_applied, r.gain) == (blen, best)
     out = rho.tolist()
-    for n in want[:blen]:
+    for n in seq[:blen]:
         out[n] = int(mv[n])
     assert r.rho.tolist() == out
     return r
 
 
+@pytest.mark.parametrize("chained", [False, True])
 @pytest.mark.parametrize("kw", tiny_cases()[::2], ids=lambda k: "s%d" % k["seed"])
-def test_refine_vs_brute(kw):
+def test_refine_vs_brute(kw, chained):
     """Every in-sequence gain equals the connectivity the move removes from the
     partition left by the moves before it, every violation count the invalid
     partitions then (both by the set-based evaluator), and the prefix applied
-    is the best valid one."""
+    is the best valid one; the order is by gain, or chains that link and are
+    ranked as stated."""
     h = synth.tiny(**kw)
     grid = constraint_grid(h)
     for k in (1, 2, 3, max(2, h.n_nodes // 2)):
@@ -824,7 +942,7 @@ def test_refine_vs_brute(kw):
         psize = np.bincount(rho, weights=h.n_size, minlength=k)
         for omega, delta in grid + [(int(psize.max()) + 1, BIG)]:
             for enforce in (False, True):
-                _refine_brute_check(h, rho, k, omega, delta, enforce)
+                _refine_brute_check(h, rho, k, omega, delta, enforce, chained)
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -839,8 +957,8 @@ def test_refine_never_worsens(seed):
     psize = np.bincount(rho, weights=h.n_size, minlength=k)
     omega = int(psize.max()) + 2
     _, _, s0 = oracle.evaluate(g, rho, k, omega, BIG)
-    for _ in range(6):
-        r = oracle.refine_pass(g, rho, k, omega, BIG, enforce_omega=True)
+    for it in range(6):
+        r = oracle.refine_pass(g, rho, k, omega, BIG, enforce_omega=True, chained=it % 2 == 0)
         _, _, s1 = oracle.evaluate(g, r.rho, k, omega, BIG)
         assert int(s1[0]) == int(s0[0]) - r.gain and r.gain >= 0
         assert int(s1[2]) == 0 and int(s1[3]) == 0
