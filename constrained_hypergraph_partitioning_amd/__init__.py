@@ -33,7 +33,7 @@ EXPORTS = ["chp_create", "chp_destroy", "chp_last_error", "chp_build_incidence",
            "chp_set_timing", "chp_get_timings", "chp_reset_timings", "chp_set_batch_entries",
            "chp_last_rate_stats", "chp_set_incidence_rating", "chp_pair_leftovers",
            "chp_propose_moves", "chp_set_matching", "chp_set_timing_filter",
-           "chp_refine_moves"]
+           "chp_refine_moves", "chp_set_move_order"]
 
 
 class ChpError(RuntimeError):
@@ -121,6 +121,8 @@ def load_library(path: str = LIB_PATH):
                                      ctypes.POINTER(ctypes.c_uint32),
                                      ctypes.POINTER(ctypes.c_int64)]
     lib.chp_refine_moves.restype = I
+    lib.chp_set_move_order.argtypes = [P, I]
+    lib.chp_set_move_order.restype = I
     lib.chp_pair_leftovers.argtypes = [P, ctypes.POINTER(HGraphC), ctypes.POINTER(Params), P, P,
                                        ctypes.POINTER(ctypes.c_uint32)]
     lib.chp_pair_leftovers.restype = I
@@ -346,6 +348,10 @@ class Context:
                                                ctypes.byref(prm), 1 if enforce_omega else 0,
                                                _ptr(move), _ptr(gain)), "propose_moves")
         return move[:N], gain[:N]
+
+    def set_move_order(self, chained=True):
+        """Sequence moves as chains (the default) or by gain alone."""
+        self._check(self.lib.chp_set_move_order(self.h, 0 if chained else 1), "set_move_order")
 
     def refine_moves(self, g: HGraph, rho, k, omega, delta, move, gain, details=False):
         """One refinement pass over the proposed moves (rho updated in place).

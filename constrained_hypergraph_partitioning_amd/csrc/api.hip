@@ -509,6 +509,12 @@ int chp_set_matching(chp_ctx *c, int mode) {
   return CHP_OK;
 }
 
+int chp_set_move_order(chp_ctx *c, int order) {
+  if (!c || (order != CHP_ORDER_CHAINS && order != CHP_ORDER_GAIN)) return CHP_EINVAL;
+  c->move_order = (u32)order;
+  return CHP_OK;
+}
+
 int chp_set_incidence_rating(chp_ctx *c, uint64_t min_visits, uint32_t hash_keys) {
   if (!c) return CHP_EINVAL;
   c->inc_min_visits = min_visits;
@@ -930,6 +936,53 @@ int chp_propose_moves(chp_ctx *c, const chp_hgraph *g, const u32 *rho, u32 k,
   });
 }
 
+// Chains over the moves in gain order sq (rank = their positions): sq and
+// rank are rewritten in chain order.
+void build_chains(chp_ctx *c, Scratch &s, const chp_hgraph *g, u32 M, const u32 *rho,
+                  const u32 *move, const i64 *gain, u32 *sq, u32 *rank) {
+  ChainBufs B;
+  u32 **u32s[] = {&B.node, &B.size, &B.nin, &B.dest, &B.pred, &B.succ, &B.pick, &B.wid,
+                  &B.anc, &B.anc2, &B.mn, &B.mn2, &B.cut, &B.dist, &B.clen, &B.cstart};
+  for (u32 **p : u32s) *p = s.get<u32>(M);
+  B.posn = s.get<u32>(g->n_nodes);
+  B.gain = s.get<i64>(M);
+  B.pgr = s.get<i64>(M);
+  B.wgr = s.get<i64>(M);
+  B.ctot = s.get<i64>(M);
+  u64 *ck = s.get<u64>(M);
+  u64 *ctmp = s.get<u64>(M);
+  u32 *cc = s.get<u32>(2);  // links of a round, chain heads
+  launch_fills(c, {{B.ctot, M, 0, true}, {B.clen, M, 0, false}, {cc, 2, 0, false}});
+  const u64 *sorted = nullptr;
+  launch_chain_setup(c, M, sq, rho, move, g->n_size, g->n_nin, gain, ck, ctmp, B, &sorted);
+  for (u32 round = 0; round < CHAIN_ROUNDS; ++round) {
+    launch_fill_u32(c, cc, 1, 0);
+    launch_chain_round(c, M, sorted, B, cc);
+    launch_check(c, "chain round");
+    u32 links = 0;
+    read_many(c, {{&links, cc, sizeof links}});
+    if (links == 0) break;
+  }
+  launch_chain_walk(c, M, B);
+  u32 *heads = s.get<u32>(M);
+  u64 *hk = s.get<u64>(M);
+  u64 *htmp = s.get<u64>(M);
+  launch_chain_heads(c, M, B, heads, hk, cc + 1);
+  launch_check(c, "chain heads");
+  u32 H = 0;
+  read_many(c, {{&H, cc + 1, sizeof H}});
+  const u64 *tot = sort_keys_u64(c, hk, htmp, H);
+  u64 *rk = tot == hk ? htmp : hk;  // the array the sort left free
+  launch_chain_rank_keys(c, H, heads, B, tot, ck);
+  const u64 *order = sort_keys_u64(c, ck, rk, H);
+  u32 *lens = B.mn;  // free after the walk
+  launch_chain_lens(c, H, order, B, lens);
+  i64 *coff = s.get<i64>((u64)H + 1);
+  i64 *stmp = s.get<i64>(scan_tmp_words(H));
+  scan_u32_to_i64(c, lens, coff, H, stmp);
+  launch_chain_place(c, M, H, order, coff, B, sq, rank);
+}
+
 int chp_refine_moves(chp_ctx *c, const chp_hgraph *g, u32 *rho, u32 k, const chp_params *prm,
                      const u32 *move, const i64 *gain, u32 *seq, i64 *seq_gain, u32 *seq_viol,
                      u32 *n_seq_host, u32 *n_applied_host, i64 *gain_host) {
@@ -983,6 +1036,7 @@ int chp_refine_moves(chp_ctx *c, const chp_hgraph *g, u32 *rho, u32 k, const chp
     const u64 *sk = sort_keys_u64(c, keys, ktmp, M);
     u32 *sq = seq ? seq : s.get<u32>(M);
     launch_seq_rank(c, M, sk, sq, rank);
+    if (c->move_order == CHP_ORDER_CHAINS) build_chains(c, s, g, M, rho, move, gain, sq, rank);
     // -- per hyperedge: in-sequence gains, inbound transitions, starting inbound counts
     i64 *ingain = s.get<i64>(M);
     i64 *vdelta = s.get<i64>(M);

@@ -2,9 +2,18 @@
 // with Distinct Incident Hyperedges and Size Constraints", Sec. VI-A, VI-C,
 // VI-D, Eqs. 14-15).
 //
-// Sequence.  Every node with a proposed move is one chain of its own; chains
-// ranked by gain put the moves in (gain desc, id asc) order, sorted here as
-// u64 keys (2^31 - 1 - gain) << 32 | n.
+// Sequence.  By gain alone: the moves in (gain desc, id asc) order, sorted as
+// u64 keys (2^31 - 1 - gain) << 32 | n.  As chains (Sec. VI-C, Fig. 5): the
+// moves sorted by (source partition, gain rank) give every partition a run of
+// the moves leaving it.  In each round every move without a successor scans
+// the first 256 of the run leaving its destination for moves still without a
+// predecessor and picks the largest grade (gain - 1e-6 |size diff| - 1e-7
+// ||in| diff|, held exactly as 10^7 times that; ties to the smaller node); a
+// move picked by several goes to the largest grade, then the largest picker
+// (two atomic maxima).  The links form paths and cycles: pointer jumping
+// finds each cycle's smallest node, the cycle is cut there, and a second
+// jumping gives every move its chain head and position.  Chains are ranked
+// by (total gain desc, first node asc) and laid out by a scan.
 //
 // In-sequence gains and inbound transitions (per hyperedge).  Hyperedge e
 // holds one base event per pin, (rho(v), pin index), and two per moving pin
@@ -59,6 +68,193 @@ __global__ void k_seq_rank(u32 M, const u64 *keys, u32 *seq, u32 *rank) {
   const u32 n = (u32)keys[i];
   seq[i] = n;
   rank[n] = i;
+}
+
+// ---- chains -----------------------------------------------------------------------
+constexpr u32 CHAIN_WINDOW = 256;
+
+struct ChainPos {  // per position of the (source partition, gain rank) order
+  u32 *node, *size, *nin, *dest;
+  i64 *gain;
+  u32 *pred, *succ;  // positions
+};
+
+__global__ void k_chain_keys(u32 M, const u32 *seq, const u32 *rho, u64 *keys) {
+  const u32 r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= M) return;
+  keys[r] = ((u64)rho[seq[r]] << 32) | r;
+}
+
+__global__ void k_chain_setup(u32 M, const u64 *keys, const u32 *seq, const u32 *move,
+                              const u32 *n_size, const u32 *n_nin, const i64 *gain, ChainPos C,
+                              u32 *posn) {
+  const u32 t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= M) return;
+  const u32 n = seq[(u32)keys[t]];
+  C.node[t] = n;
+  C.size[t] = n_size[n];
+  C.nin[t] = n_nin[n];
+  C.dest[t] = move[n];
+  C.gain[t] = gain[n];
+  C.pred[t] = NONE32;
+  C.succ[t] = NONE32;
+  posn[n] = t;
+}
+
+__device__ __forceinline__ u32 lower_bound_u64(const u64 *a, u32 n, u64 v) {
+  u32 lo = 0, hi = n;
+  while (lo < hi) {
+    const u32 mid = (lo + hi) >> 1;
+    if (a[mid] < v) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ i64 grade_fx(const ChainPos &C, u32 t, u32 u) {
+  const i64 ds = C.size[t] > C.size[u] ? (i64)C.size[t] - C.size[u] : (i64)C.size[u] - C.size[t];
+  const i64 di = C.nin[t] > C.nin[u] ? (i64)C.nin[t] - C.nin[u] : (i64)C.nin[u] - C.nin[t];
+  return 10000000ll * C.gain[u] - 10 * ds - di;
+}
+
+__global__ void k_chain_pick(u32 M, const u64 *keys, ChainPos C, u32 *pick, i64 *pgr,
+                             i64 *wgr) {
+  const u32 t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= M) return;
+  u32 best = NONE32;
+  i64 bg = 0;
+  if (C.succ[t] == NONE32) {
+    const u32 d = C.dest[t];
+    const u32 a = lower_bound_u64(keys, M, (u64)d << 32);
+    const u32 e = lower_bound_u64(keys, M, ((u64)d + 1) << 32);
+    const u32 b = e - a > CHAIN_WINDOW ? a + CHAIN_WINDOW : e;
+    for (u32 u = a; u < b; ++u) {
+      if (C.pred[u] != NONE32) continue;
+      const i64 g = grade_fx(C, t, u);
+      if (best == NONE32 || g > bg || (g == bg && C.node[u] < C.node[best])) {
+        best = u;
+        bg = g;
+      }
+    }
+  }
+  pick[t] = best;
+  if (best != NONE32) {
+    pgr[t] = bg;
+    atomicMax((long long *)(wgr + best), (long long)bg);
+  }
+}
+
+__global__ void k_chain_claim(u32 M, const u32 *pick, const i64 *pgr, const i64 *wgr,
+                              const u32 *node, u32 *wid) {
+  const u32 t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= M) return;
+  const u32 u = pick[t];
+  if (u != NONE32 && pgr[t] == wgr[u]) atomicMax(wid + u, node[t] + 1);
+}
+
+__global__ void k_chain_link(u32 M, const u32 *pick, const u32 *wid, ChainPos C, u32 *links) {
+  const u32 t = blockIdx.x * blockDim.x + threadIdx.x;
+  bool won = false;
+  if (t < M) {
+    const u32 u = pick[t];
+    if (u != NONE32 && wid[u] == C.node[t] + 1) {
+      C.succ[t] = u;
+      C.pred[u] = t;
+      won = true;
+    }
+  }
+  const u64 b = __ballot(won);
+  if (lane_id() == 0 && b) atomicAdd(links, (u32)__popcll(b));
+}
+
+// jumping over predecessors: ancestor, and the smallest node on the way
+__global__ void k_cj_init(u32 M, const u32 *pred, const u32 *node, u32 *anc, u32 *mn) {
+  const u32 t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= M) return;
+  anc[t] = pred[t] == NONE32 ? t : pred[t];
+  mn[t] = node[t];
+}
+
+__global__ void k_cj_jump_min(u32 M, const u32 *anc, const u32 *mn, u32 *anc2, u32 *mn2) {
+  const u32 t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= M) return;
+  const u32 a = anc[t];
+  anc2[t] = anc[a];
+  mn2[t] = mn[a] < mn[t] ? mn[a] : mn[t];
+}
+
+// cut every cycle before its smallest node; then ancestors and distances
+__global__ void k_cj_cut(u32 M, const u32 *pred, const u32 *node, const u32 *anc, const u32 *mn,
+                         u32 *cut, u32 *anc2, u32 *dist) {
+  const u32 t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= M) return;
+  u32 p = pred[t];
+  const bool in_cycle = pred[anc[t]] != NONE32;
+  if (in_cycle && mn[t] == node[t]) p = NONE32;
+  cut[t] = p;
+  anc2[t] = p == NONE32 ? t : p;
+  dist[t] = p == NONE32 ? 0 : 1;
+}
+
+__global__ void k_cj_jump_dist(u32 M, const u32 *anc, const u32 *dist, u32 *anc2, u32 *dist2) {
+  const u32 t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= M) return;
+  const u32 a = anc[t];
+  anc2[t] = anc[a];
+  dist2[t] = dist[t] + dist[a];
+}
+
+__global__ void k_chain_totals(u32 M, const u32 *anc, const i64 *gain, i64 *ctot, u32 *clen) {
+  const u32 t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= M) return;
+  const u32 h = anc[t];
+  atomicAdd((unsigned long long *)(ctot + h), (unsigned long long)gain[t]);
+  atomicAdd(clen + h, 1u);
+}
+
+__device__ __forceinline__ u64 desc_key(i64 v) { return (u64)(-v) ^ (1ull << 63); }
+
+__global__ void k_chain_heads(u32 M, const u32 *cut, const i64 *ctot, u32 *heads, u64 *hk,
+                              u32 *cnt) {
+  const u32 t = blockIdx.x * blockDim.x + threadIdx.x;
+  const bool h = t < M && cut[t] == NONE32;
+  const u32 s = wave_append(cnt, h);
+  if (h) {
+    heads[s] = t;
+    hk[s] = desc_key(ctot[t]);
+  }
+}
+
+// (rank of the total among the sorted totals) << 32 | first node: distinct
+__global__ void k_chain_rank_keys(u32 H, const u32 *heads, const i64 *ctot, const u64 *sorted,
+                                  const u32 *node, u64 *keys) {
+  const u32 i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= H) return;
+  const u32 t = heads[i];
+  keys[i] = ((u64)lower_bound_u64(sorted, H, desc_key(ctot[t])) << 32) | node[t];
+}
+
+__global__ void k_chain_lens(u32 H, const u64 *keys, const u32 *posn, const u32 *clen,
+                             u32 *lens) {
+  const u32 c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= H) return;
+  lens[c] = clen[posn[(u32)keys[c]]];
+}
+
+__global__ void k_chain_starts(u32 H, const u64 *keys, const u32 *posn, const i64 *coff,
+                               u32 *cstart) {
+  const u32 c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= H) return;
+  cstart[posn[(u32)keys[c]]] = (u32)coff[c];
+}
+
+__global__ void k_chain_place(u32 M, const u32 *anc, const u32 *dist, const u32 *cstart,
+                              const u32 *node, u32 *seq, u32 *rank) {
+  const u32 t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= M) return;
+  const u32 p = cstart[anc[t]] + dist[t];
+  seq[p] = node[t];
+  rank[node[t]] = p;
 }
 
 // ---- hyperedge events -------------------------------------------------------------
@@ -404,4 +600,76 @@ void launch_prefix(chp_ctx *c, u32 M, const i64 *ingain, const i64 *Pg, const i6
   CHP_LAUNCH(c, "prefix_pick", k_prefix_pick, g, RB, 0, M, ingain, Pg, vdelta, Pv, v0,
              (const u64 *)best, best_len);
   CHP_LAUNCH(c, "apply_moves", k_apply, g, RB, 0, M, seq, move, (const u32 *)best_len, rho);
+}
+
+// ---- chain launchers -----------------------------------------------------------------
+void launch_chain_setup(chp_ctx *c, u32 M, const u32 *seq, const u32 *rho, const u32 *move,
+                        const u32 *n_size, const u32 *n_nin, const i64 *gain, u64 *keys,
+                        u64 *ktmp, ChainBufs &B, const u64 **sorted) {
+  CHP_LAUNCH(c, "chain_keys", k_chain_keys, grid_for(M, RB), RB, 0, M, seq, rho, keys);
+  const u64 *sk = sort_keys_u64(c, keys, ktmp, M);
+  *sorted = sk;
+  ChainPos C{B.node, B.size, B.nin, B.dest, B.gain, B.pred, B.succ};
+  CHP_LAUNCH(c, "chain_setup", k_chain_setup, grid_for(M, RB), RB, 0, M, sk, seq, move, n_size,
+             n_nin, gain, C, B.posn);
+}
+
+void launch_chain_round(chp_ctx *c, u32 M, const u64 *sorted, ChainBufs &B, u32 *links) {
+  ChainPos C{B.node, B.size, B.nin, B.dest, B.gain, B.pred, B.succ};
+  const u32 g = grid_for(M, RB);
+  launch_fills(c, {{B.wgr, M, 0x8000000000000000ull, true}, {B.wid, M, 0, false}});
+  CHP_LAUNCH(c, "chain_pick", k_chain_pick, g, RB, 0, M, sorted, C, B.pick, B.pgr, B.wgr);
+  CHP_LAUNCH(c, "chain_claim", k_chain_claim, g, RB, 0, M, (const u32 *)B.pick,
+             (const i64 *)B.pgr, (const i64 *)B.wgr, (const u32 *)B.node, B.wid);
+  CHP_LAUNCH(c, "chain_link", k_chain_link, g, RB, 0, M, (const u32 *)B.pick,
+             (const u32 *)B.wid, C, links);
+}
+
+void launch_chain_walk(chp_ctx *c, u32 M, ChainBufs &B) {
+  const u32 g = grid_for(M, RB);
+  u32 rounds = 1;
+  while ((1ull << rounds) < (u64)M + 1) ++rounds;
+  CHP_LAUNCH(c, "cj_init", k_cj_init, g, RB, 0, M, (const u32 *)B.pred, (const u32 *)B.node,
+             B.anc, B.mn);
+  for (u32 r = 0; r < rounds; ++r) {
+    CHP_LAUNCH(c, "cj_jump_min", k_cj_jump_min, g, RB, 0, M, (const u32 *)B.anc,
+               (const u32 *)B.mn, B.anc2, B.mn2);
+    std::swap(B.anc, B.anc2);
+    std::swap(B.mn, B.mn2);
+  }
+  CHP_LAUNCH(c, "cj_cut", k_cj_cut, g, RB, 0, M, (const u32 *)B.pred, (const u32 *)B.node,
+             (const u32 *)B.anc, (const u32 *)B.mn, B.cut, B.anc2, B.dist);
+  std::swap(B.anc, B.anc2);
+  for (u32 r = 0; r < rounds; ++r) {
+    CHP_LAUNCH(c, "cj_jump_dist", k_cj_jump_dist, g, RB, 0, M, (const u32 *)B.anc,
+               (const u32 *)B.dist, B.anc2, B.mn2);
+    std::swap(B.anc, B.anc2);
+    std::swap(B.dist, B.mn2);
+  }
+  CHP_LAUNCH(c, "chain_totals", k_chain_totals, g, RB, 0, M, (const u32 *)B.anc,
+             (const i64 *)B.gain, B.ctot, B.clen);
+}
+
+void launch_chain_heads(chp_ctx *c, u32 M, ChainBufs &B, u32 *heads, u64 *hk, u32 *cnt) {
+  CHP_LAUNCH(c, "chain_heads", k_chain_heads, grid_for(M, RB), RB, 0, M, (const u32 *)B.cut,
+             (const i64 *)B.ctot, heads, hk, cnt);
+}
+
+void launch_chain_rank_keys(chp_ctx *c, u32 H, const u32 *heads, ChainBufs &B,
+                            const u64 *sorted_totals, u64 *keys) {
+  CHP_LAUNCH(c, "chain_rank_keys", k_chain_rank_keys, grid_for(H, RB), RB, 0, H, heads,
+             (const i64 *)B.ctot, sorted_totals, (const u32 *)B.node, keys);
+}
+
+void launch_chain_lens(chp_ctx *c, u32 H, const u64 *keys, ChainBufs &B, u32 *lens) {
+  CHP_LAUNCH(c, "chain_lens", k_chain_lens, grid_for(H, RB), RB, 0, H, keys,
+             (const u32 *)B.posn, (const u32 *)B.clen, lens);
+}
+
+void launch_chain_place(chp_ctx *c, u32 M, u32 H, const u64 *keys, const i64 *coff,
+                        ChainBufs &B, u32 *seq, u32 *rank) {
+  CHP_LAUNCH(c, "chain_starts", k_chain_starts, grid_for(H, RB), RB, 0, H, keys,
+             (const u32 *)B.posn, coff, B.cstart);
+  CHP_LAUNCH(c, "chain_place", k_chain_place, grid_for(M, RB), RB, 0, M, (const u32 *)B.anc,
+             (const u32 *)B.dist, (const u32 *)B.cstart, (const u32 *)B.node, seq, rank);
 }

@@ -141,6 +141,28 @@ u64 *sort_keys_u64(chp_ctx *c, u64 *a, u64 *tmp, u64 n);
 void launch_seq_keys(chp_ctx *c, u32 N, u32 k, const u32 *rho, const u32 *move, const i64 *gain,
                      u64 *keys, u32 *cnt);
 void launch_seq_rank(chp_ctx *c, u32 M, const u64 *keys, u32 *seq, u32 *rank);
+// move chains: buffers per position of the (source partition, gain rank)
+// order, except posn (by node)
+constexpr u32 CHAIN_ROUNDS = 16;  // linking rounds at most
+struct ChainBufs {
+  u32 *node, *size, *nin, *dest, *pred, *succ, *posn;
+  i64 *gain;
+  u32 *pick, *wid;
+  i64 *pgr, *wgr;
+  u32 *anc, *anc2, *mn, *mn2, *cut, *dist, *clen, *cstart;
+  i64 *ctot;
+};
+void launch_chain_setup(chp_ctx *c, u32 M, const u32 *seq, const u32 *rho, const u32 *move,
+                        const u32 *n_size, const u32 *n_nin, const i64 *gain, u64 *keys,
+                        u64 *ktmp, ChainBufs &B, const u64 **sorted);
+void launch_chain_round(chp_ctx *c, u32 M, const u64 *sorted, ChainBufs &B, u32 *links);
+void launch_chain_walk(chp_ctx *c, u32 M, ChainBufs &B);
+void launch_chain_heads(chp_ctx *c, u32 M, ChainBufs &B, u32 *heads, u64 *hk, u32 *cnt);
+void launch_chain_rank_keys(chp_ctx *c, u32 H, const u32 *heads, ChainBufs &B,
+                            const u64 *sorted_totals, u64 *keys);
+void launch_chain_lens(chp_ctx *c, u32 H, const u64 *keys, ChainBufs &B, u32 *lens);
+void launch_chain_place(chp_ctx *c, u32 M, u32 H, const u64 *keys, const i64 *coff,
+                        ChainBufs &B, u32 *seq, u32 *rank);
 // hyperedges by event capacity: lists[k * E ..], cnt[0..2], cnt[3] = longest class 2
 void launch_ev_classify(chp_ctx *c, u32 E, const i64 *e_off, u32 *lists, u32 *cnt);
 u64 ev_global_words(u32 max_len);  // scratch words per workgroup of class 2

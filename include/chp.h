@@ -179,8 +179,8 @@ int chp_propose_moves(chp_ctx *ctx, const chp_hgraph *g, const uint32_t *rho, ui
  * VI-C, VI-D, Eqs. 14-15), run after chp_propose_moves on the same rho.
  *  rho[N]      the partition in [0, k); updated in place with the moves applied.
  *  move[N], gain[N]  as written by chp_propose_moves (CHP_NONE = no move).
- * The nodes with a move form the sequence, ordered by (gain desc, id asc)
- * (every chain of length one).  The in-sequence gain of the i-th move is the
+ * The nodes with a move form the sequence, ordered as chp_set_move_order
+ * sets (chains by default).  The in-sequence gain of the i-th move is the
  * connectivity it removes from the partition left by the moves before it:
  * w(e) for each hyperedge e of the node where it is the last pin left in its
  * partition, minus w(e) for each one with no pin in the destination yet.  A
@@ -198,6 +198,25 @@ int chp_propose_moves(chp_ctx *ctx, const chp_hgraph *g, const uint32_t *rho, ui
  * Deterministic.  Errors: EINVAL (k == 0, rho or move >= k, a move to its own
  * partition, N >= 2^29, a hyperedge of 2^30 pins or more), EOVERFLOW (a gain
  * outside [-2^31, 2^31)).  Synchronises. */
+/* Order of the move sequence used by chp_refine_moves on ctx.
+ * CHP_ORDER_CHAINS (the default): chains of moves ([HP] Sec. VI-C, Fig. 5).
+ *   The moves are sorted by (source partition, gain desc, id asc).  In up to
+ *   16 rounds (fewer when a round links nothing), every move n without a
+ *   successor looks at the first 256 moves leaving its destination, takes
+ *   those without a predecessor and picks the m of largest grade
+ *   gain(m) - 1e-6 |size(n) - size(m)| - 1e-7 ||in(n)| - |in(m)|| (computed
+ *   exactly, in units of 1e-7; ties to the smaller m); a move picked by
+ *   several becomes the successor of the largest (grade, picker id).  The
+ *   links form paths (started at the move without a predecessor) and cycles
+ *   (started at their smallest node); chains, each in successor order, are
+ *   ranked by total gain (desc) then first node (asc) and concatenated.
+ * CHP_ORDER_GAIN: (gain desc, id asc), every chain of length one (the
+ *   pages' ablation without chaining).
+ * EINVAL for another value. */
+#define CHP_ORDER_CHAINS 0
+#define CHP_ORDER_GAIN 1
+int chp_set_move_order(chp_ctx *ctx, int order);
+
 int chp_refine_moves(chp_ctx *ctx, const chp_hgraph *g, uint32_t *rho, uint32_t k,
                      const chp_params *prm, const uint32_t *move, const int64_t *gain,
                      uint32_t *seq, int64_t *seq_gain, uint32_t *seq_viol, uint32_t *n_seq_host,

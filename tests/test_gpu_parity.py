@@ -392,15 +392,22 @@ def test_moves_identity_and_one_part(chp, ctx):
     moves_pair(chp, ctx, dg, og, np.zeros(h.n_nodes, np.uint32), 1, 1 << 30, False, "one part")
 
 
-def refine_pair(chp, ctx, dg, og, rho, k, omega, delta, enforce, tag):
-    """One pass on both sides from the same proposals (the oracle's): the
-    sequence, in-sequence gains, violation counts, prefix and partition must
-    agree.  Returns the partition after the pass."""
-    omv, ogn = oracle.moves(og, rho, k, omega, enforce)
-    want = oracle.refine(og, rho, k, omega, delta, omv, ogn)
+def refine_pair(chp, ctx, dg, og, rho, k, omega, delta, enforce, tag, chained=True,
+                move=None, gain=None):
+    """One pass on both sides from the same proposals (the oracle's unless
+    given): the sequence, in-sequence gains, violation counts, prefix and
+    partition must agree.  Returns the partition after the pass."""
+    if move is None:
+        move, gain = oracle.moves(og, rho, k, omega, enforce)
+    want = oracle.refine(og, rho, k, omega, delta, move, gain, chained)
     drho = chp.to_device(rho)
-    M, L, G, seq, sg, sv = ctx.refine_moves(dg, drho, k, omega, delta, chp.to_device(omv),
-                                            chp.to_device(ogn), details=True)
+    ctx.set_move_order(chained)
+    try:
+        M, L, G, seq, sg, sv = ctx.refine_moves(dg, drho, k, omega, delta, chp.to_device(move),
+                                                chp.to_device(gain), details=True)
+    finally:
+        ctx.set_move_order(True)
+    tag += " chains" if chained else " by gain"
     assert M == want.seq.shape[0], tag + " sequence length"
     assert_equal(chp.to_host(seq, np.uint32), want.seq, tag + " seq")
     assert_equal(chp.to_host(sg, np.uint64).view(np.int64), want.seq_gain, tag + " seq_gain")
@@ -411,9 +418,9 @@ def refine_pair(chp, ctx, dg, og, rho, k, omega, delta, enforce, tag):
 
 
 def test_refine_tiny(chp, ctx):
-    """Refinement passes on the brute-force-pinned tiny graphs: several k,
-    the constraint grid (some partitions start invalid), Omega enforced or
-    not in the proposals."""
+    """Refinement passes on the brute-force-pinned tiny graphs: both orders,
+    several k, the constraint grid (some partitions start invalid), Omega
+    enforced or not in the proposals."""
     import test_oracle_pins as pins
     for kw in pins.tiny_cases():
         h = synth.tiny(**kw)
@@ -423,8 +430,36 @@ def test_refine_tiny(chp, ctx):
             rho = synth.uniform_u32(kw["seed"], 43, h.n_nodes, k)
             for omega, delta in pins.constraint_grid(h):
                 for enforce in (False, True):
-                    refine_pair(chp, ctx, dg, og, rho, k, omega, delta, enforce,
-                                "tiny%d k%d" % (kw["seed"], k))
+                    for chained in (False, True):
+                        refine_pair(chp, ctx, dg, og, rho, k, omega, delta, enforce,
+                                    "tiny%d k%d" % (kw["seed"], k), chained)
+
+
+def test_refine_chain_examples(chp, ctx):
+    """The hand-worked chains (two rounds, ties, cycles, the 256-move window
+    from both sides, the grade weights) through the device."""
+    cases = [
+        (5, [0, 1, 1, 2, 0], [1, 0, 2, 0, 2], [5, 3, 4, 1, 2], [], None),
+        (3, [0, 1, 1], [1, 2, 2], [0, 0, 0], [], None),
+        (2, [1, 0], [0, 1], [1, 1], [], None),
+        (6, [0, 1, 2, 3, 4, 5], [1, 0, 3, 2, 0, 4], [1, 2, 0, 3, 0, 0], [], None),
+    ]
+    sizes = [105] * 301
+    sizes[255], sizes[256], sizes[280], sizes[300] = 102, 101, 100, 100
+    cases.append((301, [0] * 300 + [1], [1] * 300 + [0], [0] * 301, [], sizes))
+    sizes = [105] * 301
+    sizes[290] = sizes[300] = 100
+    cases.append((301, [0] * 300 + [1], [1] * 300 + [0], [0] * 200 + [1] * 100 + [0], [], sizes))
+    for size1, nin2, gain1 in ((11, 9, 0), (11, 11, 0), (10 + 1000001, 0, 1)):
+        cases.append((4, [0, 1, 1, 0], [1, 0, 0, 0xFFFFFFFF], [0, gain1, 0, 0],
+                      [([3], [2])] * nin2, [10, size1, 10, 1]))
+    for i, (n, rho, move, gain, edges, sz) in enumerate(cases):
+        say("chain example", i)
+        h = synth.from_lists(n, edges, [1] * len(edges), sz)
+        dg, og = both(chp, ctx, h, 1 << 30, 1 << 30, neighbors=False)
+        k = max(max(rho), max(m for m in move if m != 0xFFFFFFFF)) + 1
+        refine_pair(chp, ctx, dg, og, np.array(rho, np.uint32), k, 1 << 30, 1 << 30, False,
+                    "example%d" % i, True, np.array(move, np.uint32), np.array(gain, np.int64))
 
 
 def _limits(og, rho, k, slack):
@@ -436,18 +471,21 @@ def _limits(og, rho, k, slack):
                                             (2, 20000, 600, 3), (3, 5000, 100, 1),
                                             (4, 30000, 3000, 1), (5, 8192, 50, 1)])
 def test_refine_scaled(chp, ctx, cfg, nn, k, slack):
-    """Scaled workloads under a random partition: one pass with no limits and
-    its details compared, then two chained passes end to end (device
-    proposals, then the device pass) with Omega enforced and Omega and Delta
-    at the 70th percentile of the starting parts, so some parts start invalid
-    and validity flips along the sequence."""
+    """Scaled workloads under a random partition: one pass in each order with
+    no limits and its details compared, then two chained passes end to end
+    (device proposals, then the device pass, chains) with Omega enforced and
+    Omega and Delta at the 70th percentile of the starting parts, so some
+    parts start invalid and validity flips along the sequence."""
     spec = synth.config(cfg, n_nodes=nn)
     h = synth.generate(spec)
     say("refine", cfg, nn, k)
     dg, og = both(chp, ctx, h, spec.omega, spec.delta, neighbors=False)
     rho = synth.uniform_u32(cfg, 47, h.n_nodes, k)
     omega, delta = _limits(og, rho, k, slack)
-    refine_pair(chp, ctx, dg, og, rho, k, 1 << 40, 1 << 30, False, "cfg%d detail" % cfg)
+    mv, gn = oracle.moves(og, rho, k, 1 << 40, False)
+    for chained in (False, True):
+        refine_pair(chp, ctx, dg, og, rho, k, 1 << 40, 1 << 30, False, "cfg%d detail" % cfg,
+                    chained, mv, gn)
     drho = chp.to_device(rho)
     for it in range(2):
         want = oracle.refine_pass(og, rho, k, omega, delta, True)
@@ -476,13 +514,16 @@ def test_refine_long_hyperedges(chp, ctx):
     for k in (3, 40, 2000):
         rho = synth.uniform_u32(k, 5, n, k)
         omega, delta = _limits(og, rho, k, 1)
-        refine_pair(chp, ctx, dg, og, rho, k, 1 << 40, 1 << 30, False, "long k%d" % k)
-        refine_pair(chp, ctx, dg, og, rho, k, omega, delta, True, "long lim k%d" % k)
+        for chained in (False, True):
+            refine_pair(chp, ctx, dg, og, rho, k, 1 << 40, 1 << 30, False, "long k%d" % k,
+                        chained)
+            refine_pair(chp, ctx, dg, og, rho, k, omega, delta, True, "long lim k%d" % k,
+                        chained)
 
 
 def test_refine_edge_cases(chp, ctx):
     """One part (no move), one node, every node alone, and the error paths
-    (a move to its own part, rho out of range)."""
+    (a move to its own part, rho out of range, an unknown order)."""
     spec = synth.config(2, n_nodes=3000)
     h = synth.generate(spec)
     dg, og = both(chp, ctx, h, spec.omega, spec.delta, neighbors=False)
@@ -492,8 +533,11 @@ def test_refine_edge_cases(chp, ctx):
         == z.tolist()
     say("refine identity")
     ident = np.arange(h.n_nodes, dtype=np.uint32)
-    refine_pair(chp, ctx, dg, og, ident, h.n_nodes, 1 << 30, 1 << 30, False, "identity")
-    refine_pair(chp, ctx, dg, og, ident, h.n_nodes, 2, 1 << 30, True, "identity omega")
+    for chained in (False, True):
+        refine_pair(chp, ctx, dg, og, ident, h.n_nodes, 1 << 30, 1 << 30, False, "identity",
+                    chained)
+        refine_pair(chp, ctx, dg, og, ident, h.n_nodes, 2, 1 << 30, True, "identity omega",
+                    chained)
     say("refine one node")
     h1 = synth.from_lists(1, [], [])
     dg1, og1 = both(chp, ctx, h1, 4, 4, neighbors=False)
@@ -512,6 +556,7 @@ def test_refine_edge_cases(chp, ctx):
                          chp.to_device(np.full(h.n_nodes, 0xFFFFFFFF, np.uint32)),
                          chp.to_device(gn))
     assert ex.value.code == -1
+    assert ctx.lib.chp_set_move_order(ctx.h, 7) == -1
 
 
 def test_tiny_graphs(chp, ctx):
