@@ -70,6 +70,10 @@ def parse():
     p.add_argument("--moves", action="store_true",
                    help="also time the refinement move proposal (Eq. 13) on the input graph "
                         "under the step's projected partition, Omega enforced")
+    p.add_argument("--refine", type=int, default=0, metavar="THETA",
+                   help="also time THETA refinement passes (proposal, chained sequence, "
+                        "in-sequence gains, event validity, best prefix) on the input graph "
+                        "from the step's projected partition, Omega enforced")
     p.add_argument("--no-leftovers", action="store_true",
                    help="do not pair the nodes left without a partner")
     p.add_argument("--no-purge", action="store_true",
@@ -328,6 +332,9 @@ def main():
     }
     if args.moves:
         out["moves"] = time_moves(ctx, dev_edges, spec, rho_buf, out["config"]["final_nodes"], h)
+    if args.refine:
+        out["refine"] = time_refine(ctx, dev_edges, spec, rho_buf, out["config"]["final_nodes"],
+                                    h, args.refine)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(h, spec, args.workload, args.cpu_sample_nodes)
     print(json.dumps(out))
@@ -356,6 +363,48 @@ def time_moves(ctx, dev_edges, spec, rho_buf, k, h, reps=5):
             "improving_moves": improving,
             "kernel_ms_per_call": {kk: round(v[1] / reps, 4) for kk, v in
                                    sorted(tm.items(), key=lambda kv: -kv[1][1])[:8]}}
+
+
+def time_refine(ctx, dev_edges, spec, rho_buf, k, h, theta):
+    """theta refinement passes on the input graph from the projected partition
+    of the last step (k parts), Omega enforced, chained move order: ms per
+    pass (synchronised calls), the connectivity before and after, the moves
+    applied, and the per-kernel breakdown (library HIP events, one extra run
+    of the same passes)."""
+    import torch
+    g0 = ctx.build_incidence(*dev_edges, spec.omega, spec.delta, False)
+    rho0 = rho_buf.clone()
+
+    def run(timed):
+        rho = rho0.clone()
+        applied = gain = 0
+        ms = []
+        for _ in range(theta):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            _, na, ga = ctx.refine_pass(g0, rho, k, spec.omega, spec.delta, True)
+            torch.cuda.synchronize()
+            ms.append((time.perf_counter() - t0) * 1e3)
+            applied += na
+            gain += ga
+        return rho, applied, gain, ms
+
+    run(False)  # warm-up
+    rho, applied, gain, ms = run(True)
+    ctx.reset_timings()
+    ctx.set_timing(True)
+    run(False)
+    tm = ctx.timings()
+    ctx.set_timing(False)
+    _, _, s0 = ctx.evaluate_partition(g0, rho0, k, spec.omega, spec.delta)
+    _, _, s1 = ctx.evaluate_partition(g0, rho, k, spec.omega, spec.delta)
+    g0.free()
+    return {"passes": theta, "parts": k, "ms_per_pass": sum(ms) / theta,
+            "ms_first_pass": ms[0], "moves_applied": applied, "gain": gain,
+            "connectivity_before": int(s0[0]), "connectivity_after": int(s1[0]),
+            "parts_over_omega": int(s1[2]), "parts_over_delta": int(s1[3]),
+            "kernel_ms_per_pass": {kk: round(v[1] / theta, 4) for kk, v in
+                                   sorted(tm.items(), key=lambda kv: -kv[1][1])[:10]}}
 
 
 def rate_level_bytes(levels, h, spec):
