@@ -938,13 +938,15 @@ int chp_propose_moves(chp_ctx *c, const chp_hgraph *g, const u32 *rho, u32 k,
 
 // Chains over the moves in gain order sq (rank = their positions): sq and
 // rank are rewritten in chain order.
-void build_chains(chp_ctx *c, Scratch &s, const chp_hgraph *g, u32 M, const u32 *rho,
+void build_chains(chp_ctx *c, Scratch &s, const chp_hgraph *g, u32 M, u32 k, const u32 *rho,
                   const u32 *move, const i64 *gain, u32 *sq, u32 *rank) {
   ChainBufs B;
   u32 **u32s[] = {&B.node, &B.size, &B.nin, &B.dest, &B.pred, &B.succ, &B.pick, &B.wid,
                   &B.anc, &B.anc2, &B.mn, &B.mn2, &B.cut, &B.dist, &B.clen, &B.cstart};
   for (u32 **p : u32s) *p = s.get<u32>(M);
   B.posn = s.get<u32>(g->n_nodes);
+  B.pstart = s.get<u32>((u64)k + 1);
+  B.done = s.get<u32>(M);
   B.gain = s.get<i64>(M);
   B.pgr = s.get<i64>(M);
   B.wgr = s.get<i64>(M);
@@ -952,12 +954,13 @@ void build_chains(chp_ctx *c, Scratch &s, const chp_hgraph *g, u32 M, const u32 
   u64 *ck = s.get<u64>(M);
   u64 *ctmp = s.get<u64>(M);
   u32 *cc = s.get<u32>(2);  // links of a round, chain heads
-  launch_fills(c, {{B.ctot, M, 0, true}, {B.clen, M, 0, false}, {cc, 2, 0, false}});
+  launch_fills(c, {{B.ctot, M, 0, true}, {B.clen, M, 0, false}, {cc, 2, 0, false},
+                   {B.done, M, 0, false}});
   const u64 *sorted = nullptr;
-  launch_chain_setup(c, M, sq, rho, move, g->n_size, g->n_nin, gain, ck, ctmp, B, &sorted);
+  launch_chain_setup(c, M, k, sq, rho, move, g->n_size, g->n_nin, gain, ck, ctmp, B, &sorted);
   for (u32 round = 0; round < CHAIN_ROUNDS; ++round) {
     launch_fill_u32(c, cc, 1, 0);
-    launch_chain_round(c, M, sorted, B, cc);
+    launch_chain_round(c, M, B, cc);
     launch_check(c, "chain round");
     u32 links = 0;
     read_many(c, {{&links, cc, sizeof links}});
@@ -1036,7 +1039,7 @@ int chp_refine_moves(chp_ctx *c, const chp_hgraph *g, u32 *rho, u32 k, const chp
     const u64 *sk = sort_keys_u64(c, keys, ktmp, M);
     u32 *sq = seq ? seq : s.get<u32>(M);
     launch_seq_rank(c, M, sk, sq, rank);
-    if (c->move_order == CHP_ORDER_CHAINS) build_chains(c, s, g, M, rho, move, gain, sq, rank);
+    if (c->move_order == CHP_ORDER_CHAINS) build_chains(c, s, g, M, k, rho, move, gain, sq, rank);
     // -- per hyperedge: in-sequence gains, inbound transitions, starting inbound counts
     i64 *ingain = s.get<i64>(M);
     i64 *vdelta = s.get<i64>(M);

@@ -111,36 +111,69 @@ __device__ __forceinline__ u32 lower_bound_u64(const u64 *a, u32 n, u64 v) {
   return lo;
 }
 
-__device__ __forceinline__ i64 grade_fx(const ChainPos &C, u32 t, u32 u) {
-  const i64 ds = C.size[t] > C.size[u] ? (i64)C.size[t] - C.size[u] : (i64)C.size[u] - C.size[t];
-  const i64 di = C.nin[t] > C.nin[u] ? (i64)C.nin[t] - C.nin[u] : (i64)C.nin[u] - C.nin[t];
-  return 10000000ll * C.gain[u] - 10 * ds - di;
-}
 
-__global__ void k_chain_pick(u32 M, const u64 *keys, ChainPos C, u32 *pick, i64 *pgr,
-                             i64 *wgr) {
+// first position of every source partition's run (k + 1 entries)
+__global__ void k_chain_pstart(u32 M, u32 k, const u64 *keys, u32 *pstart) {
   const u32 t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= M) return;
-  u32 best = NONE32;
-  i64 bg = 0;
-  if (C.succ[t] == NONE32) {
+  const u32 p = (u32)(keys[t] >> 32);
+  const u32 q0 = t ? (u32)(keys[t - 1] >> 32) + 1 : 0;
+  for (u32 q = q0; q <= p; ++q) pstart[q] = t;
+  if (t == M - 1)
+    for (u32 q = p + 1; q <= k; ++q) pstart[q] = M;
+}
+
+// One wave per free end: its window's candidates a lane each, then the
+// largest grade (smallest node on ties) by shuffles.  A window with no
+// candidate left stays so (predecessors are never removed): the picker is
+// marked exhausted and skipped in later rounds.
+constexpr int CPB = 256;
+__global__ __launch_bounds__(CPB) void k_chain_pick(u32 M, const u32 *pstart, ChainPos C,
+                                                    u32 *done, u32 *pick, i64 *pgr, i64 *wgr) {
+  const u32 l = lane_id();
+  const u32 nw = gridDim.x * (CPB / WAVE);
+  for (u32 t = blockIdx.x * (CPB / WAVE) + wave_id(); t < M; t += nw) {
+    if (C.succ[t] != NONE32 || done[t]) {
+      if (l == 0) pick[t] = NONE32;
+      continue;
+    }
     const u32 d = C.dest[t];
-    const u32 a = lower_bound_u64(keys, M, (u64)d << 32);
-    const u32 e = lower_bound_u64(keys, M, ((u64)d + 1) << 32);
+    const u32 a = pstart[d], e = pstart[d + 1];
     const u32 b = e - a > CHAIN_WINDOW ? a + CHAIN_WINDOW : e;
-    for (u32 u = a; u < b; ++u) {
+    const u32 ts = C.size[t], tn = C.nin[t];
+    i64 bg = 0;
+    u32 bu = NONE32, bn = NONE32;
+    for (u32 u = a + l; u < b; u += WAVE) {
       if (C.pred[u] != NONE32) continue;
-      const i64 g = grade_fx(C, t, u);
-      if (best == NONE32 || g > bg || (g == bg && C.node[u] < C.node[best])) {
-        best = u;
+      const u32 us = C.size[u], un = C.nin[u], node = C.node[u];
+      const i64 ds = ts > us ? (i64)ts - us : (i64)us - ts;
+      const i64 di = tn > un ? (i64)tn - un : (i64)un - tn;
+      const i64 g = 10000000ll * C.gain[u] - 10 * ds - di;
+      if (bu == NONE32 || g > bg || (g == bg && node < bn)) {
         bg = g;
+        bu = u;
+        bn = node;
       }
     }
-  }
-  pick[t] = best;
-  if (best != NONE32) {
-    pgr[t] = bg;
-    atomicMax((long long *)(wgr + best), (long long)bg);
+#pragma unroll
+    for (int s = WAVE / 2; s > 0; s >>= 1) {
+      const i64 og = __shfl_xor(bg, s, WAVE);
+      const u32 ou = __shfl_xor(bu, s, WAVE), on = __shfl_xor(bn, s, WAVE);
+      if (ou != NONE32 && (bu == NONE32 || og > bg || (og == bg && on < bn))) {
+        bg = og;
+        bu = ou;
+        bn = on;
+      }
+    }
+    if (l == 0) {
+      pick[t] = bu;
+      if (bu != NONE32) {
+        pgr[t] = bg;
+        atomicMax((long long *)(wgr + bu), (long long)bg);
+      } else {
+        done[t] = 1;
+      }
+    }
   }
 }
 
@@ -603,22 +636,25 @@ void launch_prefix(chp_ctx *c, u32 M, const i64 *ingain, const i64 *Pg, const i6
 }
 
 // ---- chain launchers -----------------------------------------------------------------
-void launch_chain_setup(chp_ctx *c, u32 M, const u32 *seq, const u32 *rho, const u32 *move,
-                        const u32 *n_size, const u32 *n_nin, const i64 *gain, u64 *keys,
-                        u64 *ktmp, ChainBufs &B, const u64 **sorted) {
+void launch_chain_setup(chp_ctx *c, u32 M, u32 k, const u32 *seq, const u32 *rho,
+                        const u32 *move, const u32 *n_size, const u32 *n_nin, const i64 *gain,
+                        u64 *keys, u64 *ktmp, ChainBufs &B, const u64 **sorted) {
   CHP_LAUNCH(c, "chain_keys", k_chain_keys, grid_for(M, RB), RB, 0, M, seq, rho, keys);
   const u64 *sk = sort_keys_u64(c, keys, ktmp, M);
   *sorted = sk;
   ChainPos C{B.node, B.size, B.nin, B.dest, B.gain, B.pred, B.succ};
   CHP_LAUNCH(c, "chain_setup", k_chain_setup, grid_for(M, RB), RB, 0, M, sk, seq, move, n_size,
              n_nin, gain, C, B.posn);
+  CHP_LAUNCH(c, "chain_pstart", k_chain_pstart, grid_for(M, RB), RB, 0, M, k, sk, B.pstart);
 }
 
-void launch_chain_round(chp_ctx *c, u32 M, const u64 *sorted, ChainBufs &B, u32 *links) {
+void launch_chain_round(chp_ctx *c, u32 M, ChainBufs &B, u32 *links) {
   ChainPos C{B.node, B.size, B.nin, B.dest, B.gain, B.pred, B.succ};
   const u32 g = grid_for(M, RB);
   launch_fills(c, {{B.wgr, M, 0x8000000000000000ull, true}, {B.wid, M, 0, false}});
-  CHP_LAUNCH(c, "chain_pick", k_chain_pick, g, RB, 0, M, sorted, C, B.pick, B.pgr, B.wgr);
+  const u32 waves = M < 64u * c->n_cu * (CPB / WAVE) ? M : 64u * c->n_cu * (CPB / WAVE);
+  CHP_LAUNCH(c, "chain_pick", k_chain_pick, (waves + CPB / WAVE - 1) / (CPB / WAVE), CPB, 0, M,
+             (const u32 *)B.pstart, C, B.done, B.pick, B.pgr, B.wgr);
   CHP_LAUNCH(c, "chain_claim", k_chain_claim, g, RB, 0, M, (const u32 *)B.pick,
              (const i64 *)B.pgr, (const i64 *)B.wgr, (const u32 *)B.node, B.wid);
   CHP_LAUNCH(c, "chain_link", k_chain_link, g, RB, 0, M, (const u32 *)B.pick,

@@ -151,11 +151,13 @@ struct ChainBufs {
   i64 *pgr, *wgr;
   u32 *anc, *anc2, *mn, *mn2, *cut, *dist, *clen, *cstart;
   i64 *ctot;
+  u32 *pstart;  // [k + 1] first position of each source partition's run
+  u32 *done;    // pickers whose window has no candidate left
 };
-void launch_chain_setup(chp_ctx *c, u32 M, const u32 *seq, const u32 *rho, const u32 *move,
-                        const u32 *n_size, const u32 *n_nin, const i64 *gain, u64 *keys,
-                        u64 *ktmp, ChainBufs &B, const u64 **sorted);
-void launch_chain_round(chp_ctx *c, u32 M, const u64 *sorted, ChainBufs &B, u32 *links);
+void launch_chain_setup(chp_ctx *c, u32 M, u32 k, const u32 *seq, const u32 *rho,
+                        const u32 *move, const u32 *n_size, const u32 *n_nin, const i64 *gain,
+                        u64 *keys, u64 *ktmp, ChainBufs &B, const u64 **sorted);
+void launch_chain_round(chp_ctx *c, u32 M, ChainBufs &B, u32 *links);
 void launch_chain_walk(chp_ctx *c, u32 M, ChainBufs &B);
 void launch_chain_heads(chp_ctx *c, u32 M, ChainBufs &B, u32 *heads, u64 *hk, u32 *cnt);
 void launch_chain_rank_keys(chp_ctx *c, u32 H, const u32 *heads, ChainBufs &B,
