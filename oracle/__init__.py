@@ -80,6 +80,8 @@ def _load():
             "or_pair_leftovers": [u32, P, P, P, u64, u32, u32, P, ctypes.POINTER(u64)],
             "or_moves": [E, P, P, P, u32, u64, i32, P, P],
             "or_match_dp": [u32, P, P, P, ctypes.POINTER(u64)],
+            "or_rate_top": [E, P, P, P, P, u64, u64, u32, i32, u64, u32, P, P],
+            "or_match_rounds": [u32, u32, P, P, i32, P, ctypes.POINTER(u64)],
             "or_refine": [E, P, P, P, P, u32, u64, u32, P, P, i32, P, P, P, P,
                           ctypes.POINTER(u32), ctypes.POINTER(u32),
                           ctypes.POINTER(ctypes.c_int64), P],
@@ -221,6 +223,32 @@ def rate(g: Graph, omega, delta, noise_on=True, seed=0, lo=0, hi=None, tc=None):
                            omega, delta, 1 if noise_on else 0, seed, lo, hi, _p(target),
                            _p(score)), "rate")
     return target, score
+
+
+def rate_top(g: Graph, omega, delta, noise_on=True, seed=0, pi=4):
+    """Top-pi valid candidates of every node: (targets (pi, N) uint32, scores
+    (pi, N) uint64), row r the (r+1)-th best by (score desc, id asc)."""
+    N = g.n_nodes
+    t, cap = terms(g)
+    target = np.full((pi, N), NONE, np.uint32)
+    score = np.zeros((pi, N), np.uint64)
+    v = g.view()
+    _check(_load().or_rate_top(ctypes.byref(v), _p(g.n_off), _p(g.n_nin), _p(g.n_inc), _p(t), cap,
+                               omega, delta, 1 if noise_on else 0, seed, pi, _p(target),
+                               _p(score)), "rate_top")
+    return target, score
+
+
+def match_rounds(targets, scores, optimal=False):
+    """O16: pi matching rounds over the top-pi lists (match, number of pairs)."""
+    tg = np.ascontiguousarray(targets, np.uint32)
+    sc = np.ascontiguousarray(scores, np.uint64)
+    pi, N = tg.shape
+    m = np.empty(N, np.uint32)
+    npairs = ctypes.c_uint64()
+    _check(_load().or_match_rounds(N, pi, _p(tg), _p(sc), 1 if optimal else 0, _p(m),
+                                   ctypes.byref(npairs)), "match_rounds")
+    return m, int(npairs.value)
 
 
 def match(target, score):
@@ -392,14 +420,21 @@ class Level:
 
 
 def level(g: Graph, omega, delta, noise_on=True, seed=0, build_neighbors=True,
-          purge_invalid=False, leftovers=False, optimal=False) -> Level:
+          purge_invalid=False, leftovers=False, optimal=False, pi=1) -> Level:
     """One coarsening level: rate, match, contract.  With purge_invalid the
     neighbour flags of g are computed (Level.flags) and the coarse
     neighbourhoods are purged of flagged neighbours (O10); with leftovers the
     unmatched nodes without a target are paired best-effort (O11); with
-    optimal the matching is the exact one of O13 instead of the handshake."""
-    target, score = rate(g, omega, delta, noise_on, seed)
-    m, npairs = match_dp(target, score) if optimal else match(target, score)
+    optimal the matching is the exact one of O13 instead of the handshake;
+    with pi > 1 the matching takes pi rounds over the top-pi candidates (O16)
+    and target/score are the best candidates."""
+    if pi > 1:
+        tl, sl = rate_top(g, omega, delta, noise_on, seed, pi)
+        target, score = tl[0].copy(), sl[0].copy()
+        m, npairs = match_rounds(tl, sl, optimal)
+    else:
+        target, score = rate(g, omega, delta, noise_on, seed)
+        m, npairs = match_dp(target, score) if optimal else match(target, score)
     if leftovers:
         m, extra = pair_leftovers(target, m, g.n_size, g.n_nin, omega, delta)
         npairs += extra

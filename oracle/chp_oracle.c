@@ -287,9 +287,13 @@ static int cmp_cand(const void *x, const void *y) { /* eta descending, id ascend
 /* A node with no valid neighbour gets target NONE and score 0.              */
 /* EOVERFLOW if some node's sum of terms plus cap reaches 2^63.              */
 /* ------------------------------------------------------------------------ */
-int or_rate(const or_edges *g, const int64_t *n_off, const uint32_t *n_nin, const uint32_t *n_inc,
-            const uint64_t *t, uint64_t cap, uint64_t omega, uint32_t delta, int noise_on,
-            uint64_t seed, uint32_t lo, uint32_t hi, uint32_t *target, uint64_t *score) {
+/* The top pi valid candidates ([P1] Sec. V-D: the top-Pi valid neighbours of
+ * each histogram) go to target[r * N + n], score[r * N + n] for r < pi, in the
+ * order of Eq. 6 (score desc, id asc); missing ones are NONE / 0. */
+static int rate_top(const or_edges *g, const int64_t *n_off, const uint32_t *n_nin,
+                    const uint32_t *n_inc, const uint64_t *t, uint64_t cap, uint64_t omega,
+                    uint32_t delta, int noise_on, uint64_t seed, uint32_t lo, uint32_t hi,
+                    uint32_t pi, uint32_t *target, uint64_t *score) {
   uint32_t N = g->n_nodes;
   if (hi > N || lo > hi) return OR_EINVAL;
   uint64_t *eta = (uint64_t *)calloc(N ? N : 1, sizeof(uint64_t));
@@ -338,10 +342,13 @@ int or_rate(const or_edges *g, const int64_t *n_off, const uint32_t *n_nin, cons
       cl[c].eta = eta[m];
     }
     qsort(cl, cnt, sizeof(cand), cmp_cand);
-    target[n] = NONE;
-    score[n] = 0;
+    for (uint32_t r = 0; r < pi; ++r) {
+      target[(size_t)r * N + n] = NONE;
+      score[(size_t)r * N + n] = 0;
+    }
     const uint32_t *in_n = n_inc + n_off[n];
-    for (uint32_t c = 0; c < cnt; ++c) {
+    uint32_t got = 0;
+    for (uint32_t c = 0; c < cnt && got < pi; ++c) {
       uint32_t m = cl[c].id;
       if ((uint64_t)g->n_size[n] + g->n_size[m] > omega) continue;
       uint64_t u = union_size(in_n, nin, n_inc + n_off[m], n_nin[m]);
@@ -350,13 +357,29 @@ int or_rate(const or_edges *g, const int64_t *n_off, const uint32_t *n_nin, cons
         break;
       }
       if (u > delta) continue;
-      target[n] = m;
-      score[n] = cl[c].eta;
-      break;
+      target[(size_t)got * N + n] = m;
+      score[(size_t)got * N + n] = cl[c].eta;
+      ++got;
     }
   }
   free(eta), free(inter), free(seen), free(cl);
   return rc;
+}
+
+int or_rate(const or_edges *g, const int64_t *n_off, const uint32_t *n_nin, const uint32_t *n_inc,
+            const uint64_t *t, uint64_t cap, uint64_t omega, uint32_t delta, int noise_on,
+            uint64_t seed, uint32_t lo, uint32_t hi, uint32_t *target, uint64_t *score) {
+  return rate_top(g, n_off, n_nin, n_inc, t, cap, omega, delta, noise_on, seed, lo, hi, 1, target,
+                  score);
+}
+
+int or_rate_top(const or_edges *g, const int64_t *n_off, const uint32_t *n_nin,
+                const uint32_t *n_inc, const uint64_t *t, uint64_t cap, uint64_t omega,
+                uint32_t delta, int noise_on, uint64_t seed, uint32_t pi, uint32_t *target,
+                uint64_t *score) {
+  if (pi == 0) return OR_EINVAL;
+  return rate_top(g, n_off, n_nin, n_inc, t, cap, omega, delta, noise_on, seed, 0, g->n_nodes, pi,
+                  target, score);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -1231,4 +1254,51 @@ int or_refine(const or_edges *g, const int64_t *n_off, const uint32_t *n_nin,
   *n_seq = M, *n_applied = best_len, *gain_applied = best;
   free(mv), free(cur), free(psize), free(pinb), free(mark);
   return OR_OK;
+}
+
+/*
+ * O16 -- Pi matching rounds over the top-Pi candidates ([P1] Sec. V-D).
+ * Reading: in round r every node still unmatched proposes to the first entry
+ * of its top-Pi list (score desc, id asc) that is still unmatched, with that
+ * entry's score; matched nodes propose nothing and, being nobody's choice,
+ * are left alone.  Each round's proposal graph then keeps the invariant of
+ * Sec. V-A (no cycle longer than two: along a cycle the scores could not
+ * drop and the ids would have to fall strictly).  The round's matching (the
+ * handshake of O6, or the exact matching of O13 when optimal) adds its pairs.
+ * Round 1 is the single-candidate level.  target/score are the pi x N arrays
+ * of or_rate_top.
+ */
+int or_match_rounds(uint32_t N, uint32_t pi, const uint32_t *target, const uint64_t *score,
+                    int optimal, uint32_t *match, uint64_t *n_pairs) {
+  *n_pairs = 0;
+  uint32_t *tr = (uint32_t *)malloc(sizeof(uint32_t) * (N ? N : 1));
+  uint64_t *sr = (uint64_t *)malloc(sizeof(uint64_t) * (N ? N : 1));
+  uint32_t *mr = (uint32_t *)malloc(sizeof(uint32_t) * (N ? N : 1));
+  if (!tr || !sr || !mr) {
+    free(tr), free(sr), free(mr);
+    return OR_ENOMEM;
+  }
+  for (uint32_t n = 0; n < N; ++n) match[n] = n;
+  int rc = OR_OK;
+  for (uint32_t r = 0; r < pi && rc == OR_OK; ++r) {
+    for (uint32_t n = 0; n < N; ++n) {
+      tr[n] = NONE, sr[n] = 0;
+      if (match[n] != n) continue;
+      for (uint32_t j = 0; j < pi; ++j) {
+        const uint32_t m = target[(size_t)j * N + n];
+        if (m != NONE && match[m] == m) {
+          tr[n] = m, sr[n] = score[(size_t)j * N + n];
+          break;
+        }
+      }
+    }
+    uint64_t np = 0;
+    rc = optimal ? or_match_dp(N, tr, sr, mr, &np) : or_match(N, tr, sr, mr, &np);
+    if (rc != OR_OK) break;
+    for (uint32_t n = 0; n < N; ++n)
+      if (mr[n] != n) match[n] = mr[n];
+    *n_pairs += np;
+  }
+  free(tr), free(sr), free(mr);
+  return rc;
 }

@@ -124,6 +124,22 @@ def rate(n_nodes, edges, weights, sizes, omega, delta, noise_on=False, seed=0):
     return target, score
 
 
+def rate_top(n_nodes, edges, weights, sizes, omega, delta, noise_on, seed, pi):
+    """The pi best valid neighbours of every node, by (eta desc, id asc), via
+    a full sort of all neighbours: lists of (m, eta)."""
+    ins, _ = incidence_sets(n_nodes, edges)
+    eta = eta_fx(n_nodes, edges, weights, noise_on, seed)
+    per = [[] for _ in range(n_nodes)]
+    for (n, m), v in eta.items():
+        per[n].append((v, m))
+    out = []
+    for n in range(n_nodes):
+        top = [(m, v) for v, m in sorted(per[n], key=lambda x: (-x[0], x[1]))
+               if valid(n, m, sizes, ins, omega, delta)]
+        out.append(top[:pi])
+    return out
+
+
 def handshake(target, score):
     """The prototype's matching procedure, simulated literally and sequentially.
 

@@ -90,6 +90,15 @@ MUTANTS = {
     "chain_window_of_source": ("const uint32_t d = move[n];\n      int64_t a = pstart[d]", "const uint32_t d = rho[n];\n      int64_t a = pstart[d]"),
     "chain_sorted_gain_ascending": ("if (a->gain != b->gain) return a->gain > b->gain ? -1 : 1;\n  return a->id < b->id ? -1 : (a->id > b->id ? 1 : 0);\n}\n\ntypedef struct {\n  int64_t total;",
                                     "if (a->gain != b->gain) return a->gain < b->gain ? -1 : 1;\n  return a->id < b->id ? -1 : (a->id > b->id ? 1 : 0);\n}\n\ntypedef struct {\n  int64_t total;"),
+    "top_pi_keeps_invalid": ("      if (u > delta) continue;\n      target[(size_t)got * N + n] = m;",
+                             "      target[(size_t)got * N + n] = m;"),
+    "rounds_propose_to_matched": ("if (m != NONE && match[m] == m) {\n          tr[n] = m, sr[n] = score[(size_t)j * N + n];",
+                                  "if (m != NONE) {\n          tr[n] = m, sr[n] = score[(size_t)j * N + n];"),
+    "rounds_matched_keep_proposing": ("      if (match[n] != n) continue;\n      for (uint32_t j = 0; j < pi; ++j) {",
+                                      "      for (uint32_t j = 0; j < pi; ++j) {"),
+    "rounds_last_entry_first": ("        const uint32_t m = target[(size_t)j * N + n];",
+                                "        const uint32_t m = target[(size_t)(pi - 1 - j) * N + n];"),
+    "rounds_one_round": ("for (uint32_t r = 0; r < pi && rc == OR_OK; ++r) {", "for (uint32_t r = 0; r < 1 && rc == OR_OK; ++r) {"),
     "moves_omega_without_node": ("if (enforce_omega && psize[p] + g->n_size[n] > omega) continue;",
                                  "if (enforce_omega && psize[p] > omega) continue;"),
 }
@@ -120,6 +129,9 @@ def _checks():
     pins.test_match_dp_hand_examples()
     for seed in range(12):
         pins.test_match_dp_vs_brute(seed)
+    pins.test_rounds_hand_example()
+    for kw in pins.tiny_cases()[:24:4]:
+        pins.test_rate_top_and_rounds_vs_brute(kw, True)
     pins.test_refine_hand_example()
     pins.test_chain_hand_examples()
     pins.test_chain_window()

@@ -963,3 +963,121 @@ def test_refine_never_worsens(seed):
         assert int(s1[0]) == int(s0[0]) - r.gain and r.gain >= 0
         assert int(s1[2]) == 0 and int(s1[3]) == 0
         rho, s0 = r.rho, s1
+
+
+# ---- O16: top-Pi candidates and Pi matching rounds ([HP] Sec. V-D)
+def _brute_rounds(lists, n, pi, optimal):
+    """The rounds with the set-based handshake (or, for the exact matching,
+    the brute-force best total checked per round): every unmatched node
+    proposes to its first still-unmatched list entry."""
+    match = list(range(n))
+    totals = []
+    for _ in range(pi):
+        tg = [NONE] * n
+        sc = [0] * n
+        for v in range(n):
+            if match[v] != v:
+                continue
+            for m, s in lists[v]:
+                if match[m] == m:
+                    tg[v], sc[v] = m, s
+                    break
+        if optimal:
+            totals.append((tg, sc))
+            mr, _ = oracle.match_dp(np.array(tg, np.uint32), np.array(sc, np.uint64))
+            mr = mr.tolist()
+        else:
+            mr = brute.handshake(tg, sc)
+        for v in range(n):
+            if mr[v] != v:
+                match[v] = mr[v]
+    return match, totals
+
+
+@pytest.mark.parametrize("kw", tiny_cases()[::2], ids=lambda k: "s%d" % k["seed"])
+@pytest.mark.parametrize("noise_on", [False, True])
+def test_rate_top_and_rounds_vs_brute(kw, noise_on):
+    """The top-4 lists against a full sort of every node's valid neighbours;
+    row 0 is the single-candidate rating; the rounds against the set-based
+    handshake round by round, and (exact matching) each round's total against
+    the brute-force best over its proposal edges."""
+    h = synth.tiny(**kw)
+    edges = brute.edges_of(h.e_off, h.e_nsrc, h.e_pins)
+    for omega, delta in constraint_grid(h):
+        g = load(h, omega, delta)
+        tl, sl = oracle.rate_top(g, omega, delta, noise_on, kw["seed"], pi=4)
+        want = brute.rate_top(h.n_nodes, edges, h.e_w, h.n_size, omega, delta, noise_on,
+                              kw["seed"], 4)
+        for v in range(h.n_nodes):
+            got = [(int(tl[r, v]), int(sl[r, v])) for r in range(4) if tl[r, v] != NONE]
+            assert got == want[v]
+            assert all(tl[r, v] == NONE and sl[r, v] == 0 for r in range(len(got), 4))
+        t1, s1 = oracle.rate(g, omega, delta, noise_on=noise_on, seed=kw["seed"])
+        assert tl[0].tolist() == t1.tolist() and sl[0].tolist() == s1.tolist()
+        for pi in (1, 2, 4):
+            m, npairs = oracle.match_rounds(tl[:pi], sl[:pi])
+            lists = [w[:pi] for w in want]
+            bm, _ = _brute_rounds(lists, h.n_nodes, pi, False)
+            assert m.tolist() == bm
+            assert npairs == sum(1 for v in range(h.n_nodes) if m[v] != v) // 2
+            if pi == 1:
+                assert m.tolist() == oracle.match(t1, s1)[0].tolist()
+            mo, _ = oracle.match_rounds(tl[:pi], sl[:pi], optimal=True)
+            bo, graphs = _brute_rounds(lists, h.n_nodes, pi, True)
+            assert mo.tolist() == bo
+            if h.n_nodes <= 14:
+                for tg, sc in graphs:
+                    best, _ = brute.max_weight_matching(tg, sc)
+                    mr, _ = oracle.match_dp(np.array(tg, np.uint32), np.array(sc, np.uint64))
+                    assert _total(mr, np.array(sc), np.array(tg, np.uint32)) == best
+
+
+def test_rounds_hand_example():
+    """Unit sizes, Omega 2 (a node pairs once), every hyperedge of two pins
+    (eta = w / 2).  A path 0 - 1 - 2 (weights 4, 2): 0 and 1 pick each other
+    and pair; 2 picks 1, which is taken, and nobody picks 2; its list holds
+    only 1, so round 2 adds nothing.
+
+    Two stars: centre 1 with leaves 0 (eta 4) and 2 (eta 3), centre 4 with
+    leaves 5 (4) and 3 (3), and 2 - 3 joined weakly (eta 1).  Round 1 pairs
+    0-1 and 4-5; 2 and 3 picked their centres, were not picked, and stay
+    alone.  Round 2: the first unmatched entries of 2's and 3's lists are each
+    other: they pair."""
+    h = synth.from_lists(3, [([0], [1]), ([1], [2])], [4, 2])
+    g = load(h, 2, BIG)
+    tl, sl = oracle.rate_top(g, 2, BIG, False, 0, pi=2)
+    assert tl[0].tolist() == [1, 0, 1] and tl[1].tolist() == [NONE, 2, NONE]
+    m, npairs = oracle.match_rounds(tl, sl)
+    assert m.tolist() == [1, 0, 2] and npairs == 1
+    h = synth.from_lists(6, [([0], [1]), ([2], [1]), ([5], [4]), ([3], [4]), ([2], [3])],
+                         [8, 6, 8, 6, 2])
+    g = load(h, 2, BIG)
+    tl, sl = oracle.rate_top(g, 2, BIG, False, 0, pi=2)
+    assert tl[0].tolist() == [1, 0, 1, 4, 5, 4]
+    assert tl[1].tolist() == [NONE, 2, 3, 2, 3, NONE]
+    m1, p1 = oracle.match_rounds(tl[:1], sl[:1])
+    assert m1.tolist() == [1, 0, 2, 3, 5, 4] and p1 == 2
+    m, npairs = oracle.match_rounds(tl, sl)
+    assert m.tolist() == [1, 0, 3, 2, 5, 4] and npairs == 3
+    mo, po = oracle.match_rounds(tl, sl, optimal=True)
+    assert mo.tolist() == [1, 0, 3, 2, 5, 4] and po == 3
+
+
+def test_rounds_more_pairs_multilevel():
+    """Over several levels of a scaled workload: four rounds never pair fewer
+    nodes on the first level than one, every pair is valid, and the
+    coarsening reaches at most as many nodes after the same number of levels
+    on that first level."""
+    spec = synth.config(1)
+    h = synth.generate(spec)
+    g = load(h, spec.omega, spec.delta)
+    l1 = oracle.level(g, spec.omega, spec.delta, True, 3)
+    l4 = oracle.level(g, spec.omega, spec.delta, True, 3, pi=4)
+    assert l4.n_pairs >= l1.n_pairs
+    assert l4.target.tolist() == l1.target.tolist()
+    m = l4.match
+    assert np.array_equal(m[m], np.arange(h.n_nodes))
+    for v in range(h.n_nodes):
+        u = int(m[v])
+        if u != v:
+            assert int(h.n_size[v]) + int(h.n_size[u]) <= spec.omega
