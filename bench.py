@@ -39,6 +39,8 @@ PURGE = True
 # Nodes left without a partner are paired best-effort, as the pages'
 # coarsening does (--no-leftovers turns it off).
 LEFTOVERS = True
+# candidates kept per node; above 1, that many matching rounds (--pi)
+PI = 1
 # The driver stops after a level that pairs fewer than this fraction of its
 # nodes (a stalled coarsening: each further level would cost a full pass for a
 # handful of pairs).
@@ -67,6 +69,9 @@ def parse():
     p.add_argument("--optimal-matching", action="store_true",
                    help="match by the exact maximum-weight matching of the proposal graph "
                         "instead of the greedy handshake")
+    p.add_argument("--pi", type=int, default=1,
+                   help="candidates kept per node (1..4); above 1 the matching takes that many "
+                        "rounds over the top-pi lists")
     p.add_argument("--moves", action="store_true",
                    help="also time the refinement move proposal (Eq. 13) on the input graph "
                         "under the step's projected partition, Omega enforced")
@@ -162,8 +167,13 @@ def run_step(chp, ctx, dev_edges, spec, rho_buf, with_nb=True):
         if g.n_nodes <= floor_nodes:
             break
         flags = ctx.new_flags(g) if PURGE and with_nb else None
-        tgt, _, match, npairs = ctx.rate_and_match(g, spec.omega, spec.delta, True, spec.seed,
-                                                   flags=flags)
+        if PI > 1:
+            tl, _, match, npairs = ctx.rate_top_and_match(g, PI, spec.omega, spec.delta, True,
+                                                          spec.seed, flags=flags)
+            tgt = tl[0]
+        else:
+            tgt, _, match, npairs = ctx.rate_and_match(g, spec.omega, spec.delta, True,
+                                                       spec.seed, flags=flags)
         if LEFTOVERS:
             npairs += ctx.pair_leftovers(g, tgt, match, spec.omega, spec.delta)
         nb_total = g.nb_total if with_nb else ctx.last_rate_stats()[0]
@@ -223,7 +233,8 @@ def main():
         import synth
         summarize_counters(args.counters, synth.config(args.workload, n_nodes=args.nodes).name)
         return
-    global PURGE, LEFTOVERS
+    global PURGE, LEFTOVERS, PI
+    PI = args.pi
     PURGE = not args.no_purge
     LEFTOVERS = not args.no_leftovers
     if args.gpus != 1:
@@ -316,6 +327,7 @@ def main():
                    "neighbourhoods": "whole graph" if with_nb else "built per node batch",
                    "purge": PURGE and with_nb, "leftover_pairing": LEFTOVERS,
                    "matching": "optimal" if args.optimal_matching else "handshake",
+                   "candidates_pi": PI,
                    "pins": h.n_pins, "omega": spec.omega, "delta": spec.delta,
                    "levels": len(levels), "final_nodes": levels[-1][0] - levels[-1][2]
                    if levels else h.n_nodes, "connectivity": int(summ[0])},

@@ -33,7 +33,7 @@ EXPORTS = ["chp_create", "chp_destroy", "chp_last_error", "chp_build_incidence",
            "chp_set_timing", "chp_get_timings", "chp_reset_timings", "chp_set_batch_entries",
            "chp_last_rate_stats", "chp_set_incidence_rating", "chp_pair_leftovers",
            "chp_propose_moves", "chp_set_matching", "chp_set_timing_filter",
-           "chp_refine_moves", "chp_set_move_order"]
+           "chp_refine_moves", "chp_set_move_order", "chp_rate_top_and_match"]
 
 
 class ChpError(RuntimeError):
@@ -99,6 +99,10 @@ def load_library(path: str = LIB_PATH):
     lib.chp_rate_and_match.argtypes = [P, ctypes.POINTER(HGraphC), ctypes.POINTER(Params), P, P,
                                        P, ctypes.POINTER(ctypes.c_uint32), P]
     lib.chp_rate_and_match.restype = I
+    lib.chp_rate_top_and_match.argtypes = [P, ctypes.POINTER(HGraphC), ctypes.POINTER(Params),
+                                           ctypes.c_uint32, P, P, P,
+                                           ctypes.POINTER(ctypes.c_uint32), P]
+    lib.chp_rate_top_and_match.restype = I
     lib.chp_contract.argtypes = [P, ctypes.POINTER(HGraphC), P, P, I, ctypes.POINTER(HGraphC),
                                  P]
     lib.chp_contract.restype = I
@@ -326,6 +330,27 @@ class Context:
                                                 ctypes.byref(npairs),
                                                 _ptr(flags) if flags is not None else None),
                     "rate_and_match")
+        return target, score, match, int(npairs.value)
+
+    def rate_top_and_match(self, g: HGraph, pi, omega, delta, noise_on=True, seed=0, out=None,
+                           flags=None):
+        """target and score as (pi, N) tensors (row r: every node's (r+1)-th
+        best valid neighbour), match after pi matching rounds, n_pairs."""
+        N = g.n_nodes
+        if out is None:
+            out = (torch.empty((pi, N), dtype=torch.int32, device=self.device),
+                   torch.empty((pi, N), dtype=torch.int64, device=self.device),
+                   torch.empty(N, dtype=torch.int32, device=self.device))
+        target, score, match = out
+        if target.numel() < pi * N or score.numel() < pi * N or match.numel() < N:
+            raise ValueError("target and score need pi * N entries, match N")
+        prm = Params(omega, delta, 1 if noise_on else 0, seed)
+        npairs = ctypes.c_uint32()
+        self._check(self.lib.chp_rate_top_and_match(self.h, ctypes.byref(g.c), ctypes.byref(prm),
+                                                    pi, _ptr(target), _ptr(score), _ptr(match),
+                                                    ctypes.byref(npairs),
+                                                    _ptr(flags) if flags is not None else None),
+                    "rate_top_and_match")
         return target, score, match, int(npairs.value)
 
     def set_timing_filter(self, prefix=None):

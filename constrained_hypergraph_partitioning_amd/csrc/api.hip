@@ -779,13 +779,49 @@ void rate_batched(chp_ctx *c, Scratch &s, const chp_hgraph *g, const RateArgs &a
   launch_check(c, "rate from the incidence");
 }
 
-}  // namespace
+// One matching of the proposal graph (tr, sr) into mr, by the context's
+// mode; *np gets its pair count.  Fails on the flags the rating or the
+// matching raised.
+void match_proposals(chp_ctx *c, Scratch &s, u32 N, const u32 *tr, const u64 *sr,
+                     MatchScratch ms, u32 *npairs, u32 *mr, u32 *np) {
+  if (c->matching == CHP_MATCH_OPTIMAL) {
+    launch_fill_u32(c, npairs, 1, 0);
+    match_optimal(c, s, N, tr, sr, mr, npairs, np);
+    return;
+  }
+  launch_fills(c, {{ms.bscore, N, 0, true}, {ms.bid, N, NONE32, false}, {npairs, 1, 0, false}});
+  launch_match(c, N, tr, sr, ms, mr, npairs);
+  launch_match_write(c, N, tr, ms, mr, npairs);
+  launch_check(c, "match");
+  u32 f;
+  read_many(c, {{&f, c->flags, sizeof f}, {np, npairs, sizeof(u32)}});
+  if (f & (FLAG_EINVAL | FLAG_EOVERFLOW)) fail_flags(c, f, "rating");
+  if (f & FLAG_LONGCHAIN) {
+    if (!ms.p0) {
+      ms.p0 = s.get<u32>(N);
+      ms.p1 = s.get<u32>(N);
+      ms.x0 = s.get<uint8_t>(N);
+      ms.x1 = s.get<uint8_t>(N);
+    }
+    launch_match_jump(c, N, tr, ms);
+    launch_fill_u32(c, npairs, 1, 0);
+    launch_match_write(c, N, tr, ms, mr, npairs);
+    launch_check(c, "match (long chains)");
+    read_many(c, {{&f, c->flags, sizeof f}, {np, npairs, sizeof(u32)}});
+    if (f & FLAG_ECYCLE) fail_flags(c, FLAG_ECYCLE, "matching");
+  }
+}
 
-int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u32 *target,
-                       u64 *score_fx, u32 *match, u32 *n_pairs_host, uint8_t *nb_invalid) {
+int rate_top_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u32 pi,
+                       u32 *target, u64 *score_fx, u32 *match, u32 *n_pairs_host,
+                       uint8_t *nb_invalid) {
   return guarded(c, [&] {
     if (!g || !prm || !n_pairs_host || (g->n_nodes && (!target || !score_fx || !match))) {
       set_err(c, "%snull argument");
+      throw Fail{CHP_EINVAL};
+    }
+    if (pi < 1 || pi > RATE_MAX_PI) {
+      set_err(c, "%spi must be 1 .. 4");
       throw Fail{CHP_EINVAL};
     }
     const u32 N = g->n_nodes, E = g->n_edges;
@@ -826,6 +862,7 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
     a.seed = prm->noise_seed;
     a.target = target;
     a.score = score_fx;
+    a.pi = pi;
     a.flags = c->flags;
     NbLists nl;
     nl.list[0] = s.get<u32>(N);
@@ -841,12 +878,7 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
     ms.p0 = ms.p1 = nullptr;
     ms.x0 = ms.x1 = nullptr;
     u32 *npairs = s.get<u32>(1);
-    launch_fills(c, {{c->flags, 64, 0, false},
-                     {nl.cnt, 8, 0, false},
-                     {work, 3, 0, false},
-                     {ms.bscore, N, 0, true},
-                     {ms.bid, N, NONE32, false},
-                     {npairs, 1, 0, false}});
+    launch_fills(c, {{c->flags, 64, 0, false}, {nl.cnt, 8, 0, false}, {work, 3, 0, false}});
     if (!batched) {
       launch_rate_classify(c, a, 0, N, nl, recs, big);
       launch_check(c, "rate classes");
@@ -855,29 +887,42 @@ int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
     } else {
       rate_batched(c, s, g, a, nl, recs, big, work);
     }
-    if (c->matching == CHP_MATCH_OPTIMAL) {
-      match_optimal(c, s, N, target, score_fx, match, npairs, n_pairs_host);
+    if (pi == 1) {
+      match_proposals(c, s, N, target, score_fx, ms, npairs, match, n_pairs_host);
       return;
     }
-    launch_match(c, N, target, score_fx, ms, match, npairs);
-    launch_match_write(c, N, target, ms, match, npairs);
-    launch_check(c, "match");
-    u32 f;
-    read_many(c, {{&f, c->flags, sizeof f}, {n_pairs_host, npairs, sizeof(u32)}});
-    if (f & (FLAG_EINVAL | FLAG_EOVERFLOW)) fail_flags(c, f, "rating");
-    if (f & FLAG_LONGCHAIN) {
-      ms.p0 = s.get<u32>(N);
-      ms.p1 = s.get<u32>(N);
-      ms.x0 = s.get<uint8_t>(N);
-      ms.x1 = s.get<uint8_t>(N);
-      launch_match_jump(c, N, target, ms);
-      launch_fill_u32(c, npairs, 1, 0);
-      launch_match_write(c, N, target, ms, match, npairs);
-      launch_check(c, "match (long chains)");
-      read_many(c, {{&f, c->flags, sizeof f}, {n_pairs_host, npairs, sizeof(u32)}});
-      if (f & FLAG_ECYCLE) fail_flags(c, FLAG_ECYCLE, "matching");
+    // pi rounds; a round that pairs nothing leaves the next one's proposals,
+    // and so its matching, unchanged, so the rounds stop there
+    u32 *tr = s.get<u32>(N);
+    u64 *sr = s.get<u64>(N);
+    u32 *mr = s.get<u32>(N);
+    launch_iota(c, N, match);
+    u32 total = 0;
+    for (u32 r = 0; r < pi; ++r) {
+      launch_round_prep(c, N, pi, target, score_fx, match, tr, sr);
+      u32 np = 0;
+      match_proposals(c, s, N, tr, sr, ms, npairs, mr, &np);
+      if (np == 0) break;
+      launch_round_merge(c, N, mr, match);
+      total += np;
+      launch_fill_u32(c, c->flags, 1, 0);  // a long chain of this round is not the next one's
     }
+    launch_check(c, "matching rounds");
+    *n_pairs_host = total;
   });
+}
+
+}  // namespace
+
+int chp_rate_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u32 *target,
+                       u64 *score_fx, u32 *match, u32 *n_pairs_host, uint8_t *nb_invalid) {
+  return rate_top_and_match(c, g, prm, 1, target, score_fx, match, n_pairs_host, nb_invalid);
+}
+
+int chp_rate_top_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, uint32_t pi,
+                           u32 *target, u64 *score_fx, u32 *match, u32 *n_pairs_host,
+                           uint8_t *nb_invalid) {
+  return rate_top_and_match(c, g, prm, pi, target, score_fx, match, n_pairs_host, nb_invalid);
 }
 
 int chp_propose_moves(chp_ctx *c, const chp_hgraph *g, const u32 *rho, u32 k,

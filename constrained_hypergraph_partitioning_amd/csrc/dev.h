@@ -85,6 +85,46 @@ __device__ __forceinline__ bool better(u64 e1, u32 i1, u64 e2, u32 i2) {
   return e1 > e2 || (e1 == e2 && i1 < i2);
 }
 
+// The MP best (eta, id) seen by one thread, sorted by `better`; an empty
+// entry is {0, NONE32}, which every candidate beats (eta > 0 for any node
+// that shares a hyperedge).  All indices are compile-time, so the list stays
+// in registers.
+template <int MP>
+struct TopList {
+  u64 e[MP];
+  u32 i[MP];
+  __device__ __forceinline__ void clear() {
+#pragma unroll
+    for (int k = 0; k < MP; ++k) e[k] = 0, i[k] = NONE32;
+  }
+  // could (ev, iv) enter the list?
+  __device__ __forceinline__ bool admits(u64 ev, u32 iv) const {
+    return better(ev, iv, e[MP - 1], i[MP - 1]);
+  }
+  // insert an admitted (ev, iv); the last entry falls out
+  __device__ __forceinline__ void insert(u64 ev, u32 iv) {
+    bool placed = false;
+#pragma unroll
+    for (int k = MP - 1; k > 0; --k) {
+      if (!placed) {
+        if (better(ev, iv, e[k - 1], i[k - 1])) {
+          e[k] = e[k - 1], i[k] = i[k - 1];
+        } else {
+          e[k] = ev, i[k] = iv;
+          placed = true;
+        }
+      }
+    }
+    if (!placed) e[0] = ev, i[0] = iv;
+  }
+  // drop the head
+  __device__ __forceinline__ void pop() {
+#pragma unroll
+    for (int k = 0; k + 1 < MP; ++k) e[k] = e[k + 1], i[k] = i[k + 1];
+    e[MP - 1] = 0, i[MP - 1] = NONE32;
+  }
+};
+
 // Workgroup argmax of (eta, id) under `better`; result broadcast to all.
 template <int BLOCK>
 __device__ __forceinline__ void wg_best(u64 &eta, u32 &id, u64 *lds_e, u32 *lds_i) {
@@ -104,6 +144,26 @@ __device__ __forceinline__ void wg_best(u64 &eta, u32 &id, u64 *lds_e, u32 *lds_
   for (int w = 1; w < NW; ++w)
     if (better(lds_e[w], lds_i[w], eta, id)) eta = lds_e[w], id = lds_i[w];
   __syncthreads();
+}
+
+// The pi (<= MP) best entries over every thread's list, in order: one
+// workgroup argmax of the heads per row, after which the thread holding the
+// winner drops it (a node's neighbours sit in one bin each, so ids are
+// distinct across threads).  `lead` writes row r of target/score at node n
+// (rows of stride N); rows past the candidates get NONE32 and 0.
+template <int BLOCK, int MP>
+__device__ __forceinline__ void emit_top(TopList<MP> &b, u32 pi, u64 *lds_e, u32 *lds_i,
+                                         bool lead, u32 *target, u64 *score, u64 N, u32 n) {
+  for (u32 r = 0; r < pi; ++r) {
+    u64 e = b.e[0];
+    u32 id = b.i[0];
+    wg_best<BLOCK>(e, id, lds_e, lds_i);
+    if (id != NONE32 && b.i[0] == id) b.pop();
+    if (lead) {
+      target[r * N + n] = id;
+      score[r * N + n] = id == NONE32 ? 0 : e;
+    }
+  }
 }
 
 // ---- binary searches -----------------------------------------------------

@@ -40,11 +40,15 @@ __device__ __forceinline__ void flush_sums(u64 conn, u64 cut, u64 lam, u64 *summ
   if (lam) atomicAdd((unsigned long long *)&summary[7], (unsigned long long)lam);
 }
 
+// A wave per hyperedge of at most 64 pins.  The sums are gathered per
+// workgroup and flushed by one thread (three atomics per workgroup: the grid
+// is a few workgroups per CU, so the shared summary words see few atomics).
 __global__ __launch_bounds__(256) void k_eval_wave(const i64 *e_off, const u32 *e_nsrc,
                                                    const u32 *pins, const u32 *e_w,
                                                    const u32 *rho, u32 k, u32 *part_inb,
                                                    u64 *summary, const u32 *list, const u32 *cnt,
                                                    u32 *flags) {
+  __shared__ u64 s_sum[3][256 / WAVE];
   const u32 total = *cnt;
   const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
   const u32 l = lane_id();
@@ -67,7 +71,20 @@ __global__ __launch_bounds__(256) void k_eval_wave(const i64 *e_off, const u32 *
       lams += lam;
     }
   }
-  if (l == 0) flush_sums(conn, cut, lams, summary);
+  if (l == 0) {
+    s_sum[0][wave_id()] = conn;
+    s_sum[1][wave_id()] = cut;
+    s_sum[2][wave_id()] = lams;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 256 / WAVE; ++w) {
+      conn += s_sum[0][w];
+      cut += s_sum[1][w];
+      lams += s_sum[2][w];
+    }
+    flush_sums(conn, cut, lams, summary);
+  }
 }
 
 // lambda and inbound marks from sorted keys s[0,m); returns lambda (all threads)
@@ -147,15 +164,32 @@ __global__ __launch_bounds__(BLOCK) void k_eval_global(const i64 *e_off, const u
   if (threadIdx.x == 0) flush_sums(conn, cut, lams, summary);
 }
 
+// Violations, empty partitions and maxima, reduced per wave before the
+// atomics on the shared summary words.
 __global__ void k_eval_parts(u32 k, const u64 *part_size, const u32 *part_inb,
                              const u32 *part_cnt, u64 omega, u32 delta, u64 *summary) {
-  u32 p = blockIdx.x * blockDim.x + threadIdx.x;
-  if (p >= k) return;
-  u64 s = part_size[p];
-  u32 in = part_inb[p];
-  if (s > omega) atomicAdd((unsigned long long *)&summary[2], 1ull);
-  if (in > delta) atomicAdd((unsigned long long *)&summary[3], 1ull);
-  if (part_cnt[p] == 0) atomicAdd((unsigned long long *)&summary[4], 1ull);
+  const u32 p = blockIdx.x * blockDim.x + threadIdx.x;
+  u64 s = 0;
+  u32 in = 0, ov = 0, dv = 0, em = 0;
+  if (p < k) {
+    s = part_size[p];
+    in = part_inb[p];
+    ov = s > omega ? 1 : 0;
+    dv = in > delta ? 1 : 0;
+    em = part_cnt[p] == 0 ? 1 : 0;
+  }
+  const u64 bov = __ballot(ov), bdv = __ballot(dv), bem = __ballot(em);
+#pragma unroll
+  for (int d = WAVE / 2; d > 0; d >>= 1) {
+    const u64 os = __shfl_xor(s, d, WAVE);
+    const u32 oi = __shfl_xor(in, d, WAVE);
+    s = os > s ? os : s;
+    in = oi > in ? oi : in;
+  }
+  if (lane_id() != 0) return;
+  if (bov) atomicAdd((unsigned long long *)&summary[2], (unsigned long long)__popcll(bov));
+  if (bdv) atomicAdd((unsigned long long *)&summary[3], (unsigned long long)__popcll(bdv));
+  if (bem) atomicAdd((unsigned long long *)&summary[4], (unsigned long long)__popcll(bem));
   atomicMax((unsigned long long *)&summary[5], (unsigned long long)s);
   atomicMax((unsigned long long *)&summary[6], (unsigned long long)in);
 }
@@ -175,7 +209,9 @@ void launch_eval_edges(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const u3
                        EdgeLists el, const u32 *host_cnt, u64 *scratch, u64 per_wg,
                        u32 grid_big) {
   if (host_cnt[0])
-    CHP_LAUNCH(c, "eval_wave", k_eval_wave, waves_grid(host_cnt[0]), 256, 0, e_off, e_nsrc, pins,
+    CHP_LAUNCH(c, "eval_wave", k_eval_wave,
+               waves_grid(host_cnt[0]) < 8 * c->n_cu ? waves_grid(host_cnt[0]) : 8 * c->n_cu, 256,
+               0, e_off, e_nsrc, pins,
                e_w, rho, k, part_inb, summary, (const u32 *)el.list[0], (const u32 *)el.cnt + 0,
                c->flags);
   if (host_cnt[1])

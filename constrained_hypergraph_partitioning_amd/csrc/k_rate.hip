@@ -117,8 +117,10 @@ __global__ void k_rate_classify(RateArgs A, u32 lo, u32 hi, NbLists nl, NodeRec 
     K = (u64)(A.nb_off[n + 1] - A.nb_off[n]);
     deg = (u64)(A.n_off[n + 1] - A.n_off[n]);
     if (K == 0) {
-      A.target[n] = NONE32;
-      A.score[n] = 0;
+      for (u32 r = 0; r < A.pi; ++r) {
+        A.target[(u64)r * A.N + n] = NONE32;
+        A.score[(u64)r * A.N + n] = 0;
+      }
     }
   }
   const int c = (n >= hi || K == 0)               ? 4
@@ -412,11 +414,6 @@ __device__ __forceinline__ EdgeDesc load_edge(const RateArgs &A, i64 j) {
   return d;
 }
 
-struct NodeBest {
-  u64 e;
-  u32 i;
-};
-
 __device__ __forceinline__ bool bin_valid(const RateArgs &A, u32 nin, u64 v, u32 rem) {
   return !(v & BAD) && (u64)nin + rem <= (u64)A.delta;
 }
@@ -449,16 +446,15 @@ __device__ __forceinline__ void flag_window(const RateArgs &A, const u32 *key, c
 // A valid bin can win only if eta + cap reaches floor, the largest raw eta
 // of a valid bin (that bin's total is at least floor); the others are
 // skipped before their noise is computed.
+// With MP > 1 the floor is 0 and only the thread's own list prunes.
+template <int MP>
 __device__ __forceinline__ void consider(const RateArgs &A, u32 n, u32 nin, u32 m, u64 v, u32 rem,
                                          u64 ub_add, u64 floor, u64 dmod, u64 magic,
-                                         NodeBest &b) {
+                                         TopList<MP> &b) {
   if (!bin_valid(A, nin, v, rem) || v + ub_add < floor) return;
-  if (!better(v + ub_add, m, b.e, b.i)) return;
+  if (!b.admits(v + ub_add, m)) return;
   const u64 tv = A.noise_on ? v + pair_noise(A.seed, n, m, dmod, magic) : v;
-  if (better(tv, m, b.e, b.i)) {
-    b.e = tv;
-    b.i = m;
-  }
+  if (b.admits(tv, m)) b.insert(tv, m);
 }
 
 template <int BLOCK>
@@ -510,7 +506,7 @@ __device__ __forceinline__ void open_node(const RateArgs &A, const NodeRec &h, u
   }
 }
 
-template <class C>
+template <class C, int MP>
 __device__ void rate_heavy(const RateArgs &A, HeavySmem<C> &S, const NodeRec &h, u64 cap, u64 dmod,
                            u64 magic) {
   const u32 tid = threadIdx.x;
@@ -518,7 +514,8 @@ __device__ void rate_heavy(const RateArgs &A, HeavySmem<C> &S, const NodeRec &h,
   const i64 nb0 = h.nb0, i0 = h.i0, i1 = h.i0 + h.deg;
   const u64 size_n = h.size;
   const u64 ub_add = A.noise_on ? cap : 0;
-  NodeBest best{0, NONE32};
+  TopList<MP> best;
+  best.clear();
   u64 tsum = 0;
   EdgeDesc d0;
   {
@@ -594,14 +591,21 @@ __device__ void rate_heavy(const RateArgs &A, HeavySmem<C> &S, const NodeRec &h,
                      tot, n, tid);
       __syncthreads();
     }
-    if (A.flag) flag_window<C::B, C::UNR>(A, S.key, S.eta, S.rem, C::T - 1, C::SHIFT, nb0 + s0, cw,
-                                         nin, tid);
-    u64 floor = 0;
-    for (u32 i = tid; i < C::T; i += C::B) {
-      const u64 v = S.eta[i];
-      if (S.key[i] != EMPTY && bin_valid(A, nin, v, S.rem[i]) && v > floor) floor = v;
+    if (A.flag) {
+      flag_window<C::B, C::UNR>(A, S.key, S.eta, S.rem, C::T - 1, C::SHIFT, nb0 + s0, cw, nin,
+                                tid);
+      // without the floor's reduction, a barrier orders the flag reads
+      // before the candidate scan empties the slots
+      if (MP > 1) __syncthreads();
     }
-    floor = wg_max_u64<C::B>(floor, S.red64);
+    u64 floor = 0;
+    if (MP == 1) {
+      for (u32 i = tid; i < C::T; i += C::B) {
+        const u64 v = S.eta[i];
+        if (S.key[i] != EMPTY && bin_valid(A, nin, v, S.rem[i]) && v > floor) floor = v;
+      }
+      floor = wg_max_u64<C::B>(floor, S.red64);
+    }
     for (u32 i = tid; i < C::T; i += C::B) {
       const u32 m = S.key[i];
       if (m != EMPTY) {
@@ -614,35 +618,45 @@ __device__ void rate_heavy(const RateArgs &A, HeavySmem<C> &S, const NodeRec &h,
     // before the next node's inserts
     if (s0 + C::CAP < K) __syncthreads();
   }
+  if (MP > 1) {
+    tsum = wg_sat_sum<C::B>(tsum, S.red64);
+    if (tid == 0 && sat_add(tsum, cap) >= (1ull << 63)) atomicOr(A.flags, FLAG_EOVERFLOW);
+    emit_top<C::B, MP>(best, A.pi, S.rede, S.redi, tid == 0, A.target, A.score, A.N, n);
+    return;
+  }
   // term sum and best candidate: per wave by shuffles, then thread 0
   // combines the waves' partials
+  u64 be = best.e[0];
+  u32 bi = best.i[0];
 #pragma unroll
   for (int d = WAVE / 2; d > 0; d >>= 1) {
     tsum = sat_add(tsum, __shfl_xor(tsum, d, WAVE));
-    const u64 oe = __shfl_xor(best.e, d, WAVE);
-    const u32 oi = __shfl_xor(best.i, d, WAVE);
-    if (better(oe, oi, best.e, best.i)) best.e = oe, best.i = oi;
+    const u64 oe = __shfl_xor(be, d, WAVE);
+    const u32 oi = __shfl_xor(bi, d, WAVE);
+    if (better(oe, oi, be, bi)) be = oe, bi = oi;
   }
   if (lane_id() == 0) {
     S.red64[wave_id()] = tsum;
-    S.rede[wave_id()] = best.e;
-    S.redi[wave_id()] = best.i;
+    S.rede[wave_id()] = be;
+    S.redi[wave_id()] = bi;
   }
   __syncthreads();
   if (tid == 0) {
     tsum = 0;
-    best = NodeBest{0, NONE32};
+    be = 0;
+    bi = NONE32;
 #pragma unroll
     for (int w = 0; w < C::W; ++w) {
       tsum = sat_add(tsum, S.red64[w]);
-      if (better(S.rede[w], S.redi[w], best.e, best.i)) best.e = S.rede[w], best.i = S.redi[w];
+      if (better(S.rede[w], S.redi[w], be, bi)) be = S.rede[w], bi = S.redi[w];
     }
     if (sat_add(tsum, cap) >= (1ull << 63)) atomicOr(A.flags, FLAG_EOVERFLOW);
-    A.target[n] = best.i;
-    A.score[n] = best.i == NONE32 ? 0 : best.e;
+    A.target[n] = bi;
+    A.score[n] = bi == NONE32 ? 0 : be;
   }
 }
 
+template <int MP>
 __device__ void rate_light(const RateArgs &A, LightWave &S, u32 n, u64 cap, u64 dmod,
                            u64 magic) {
   const u32 l = lane_id();
@@ -653,7 +667,8 @@ __device__ void rate_light(const RateArgs &A, LightWave &S, u32 n, u64 cap, u64 
   const u64 size_n = A.n_size[n];
   const u64 ub_add = A.noise_on ? cap : 0;
   const u32 ne0 = (u32)((i1 - i0) < L_ECH ? (i1 - i0) : L_ECH);
-  NodeBest best{0, NONE32};
+  TopList<MP> best;
+  best.clear();
   u64 tsum = 0;
   EdgeDesc d0{0, 0, 0, 0};
   if (l < ne0) d0 = load_edge(A, i0 + l);
@@ -686,13 +701,18 @@ __device__ void rate_light(const RateArgs &A, LightWave &S, u32 n, u64 cap, u64 
                      2 * ne, tot, n, l);
     wave_sync();
   }
-  if (A.flag) flag_window<WAVE, L_UNR>(A, S.key, S.eta, S.rem, L_T - 1, L_SHIFT, nb0, K, nin, l);
-  u64 floor = 0;
-  for (u32 i = l; i < L_T; i += WAVE) {
-    const u64 v = S.eta[i];
-    if (S.key[i] != EMPTY && bin_valid(A, nin, v, S.rem[i]) && v > floor) floor = v;
+  if (A.flag) {
+    flag_window<WAVE, L_UNR>(A, S.key, S.eta, S.rem, L_T - 1, L_SHIFT, nb0, K, nin, l);
+    if (MP > 1) wave_sync();
   }
-  floor = wg_max_u64<WAVE>(floor, nullptr);
+  u64 floor = 0;
+  if (MP == 1) {
+    for (u32 i = l; i < L_T; i += WAVE) {
+      const u64 v = S.eta[i];
+      if (S.key[i] != EMPTY && bin_valid(A, nin, v, S.rem[i]) && v > floor) floor = v;
+    }
+    floor = wg_max_u64<WAVE>(floor, nullptr);
+  }
   for (u32 i = l; i < L_T; i += WAVE) {
     const u32 m = S.key[i];
     if (m != EMPTY) {
@@ -702,12 +722,8 @@ __device__ void rate_light(const RateArgs &A, LightWave &S, u32 n, u64 cap, u64 
     }
   }
   tsum = wg_sat_sum<WAVE>(tsum, nullptr);
-  wg_best<WAVE>(best.e, best.i, nullptr, nullptr);
-  if (l == 0) {
-    if (sat_add(tsum, cap) >= (1ull << 63)) atomicOr(A.flags, FLAG_EOVERFLOW);
-    A.target[n] = best.i;
-    A.score[n] = best.i == NONE32 ? 0 : best.e;
-  }
+  if (l == 0 && sat_add(tsum, cap) >= (1ull << 63)) atomicOr(A.flags, FLAG_EOVERFLOW);
+  emit_top<WAVE, MP>(best, A.pi, nullptr, nullptr, l == 0, A.target, A.score, A.N, n);
 }
 
 __device__ __forceinline__ u32 rfl(u32 v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -742,7 +758,7 @@ constexpr u32 HB = 2;  // heavy nodes per counter access
 static_assert(HB * 12 <= RB, "record words of a batch");
 
 // rec(j) is the record of item j < nh
-template <class C, u32 NB, typename RecAt>
+template <class C, u32 NB, int MP, typename RecAt>
 __device__ __forceinline__ void heavy_loop(const RateArgs &A, HeavySmem<C> &S, u32 *s_item,
                                            u32 *s_rec, RecAt rec, u32 nh, u32 *work, u64 cap,
                                            u64 dmod, u64 magic) {
@@ -760,21 +776,23 @@ __device__ __forceinline__ void heavy_loop(const RateArgs &A, HeavySmem<C> &S, u
     if (tid < nb_ * 12) s_rec[tid] = reinterpret_cast<const u32 *>(rec(w + tid / 12))[tid % 12];
     __syncthreads();
     for (u32 j = 0; j < nb_; ++j)
-      rate_heavy<C>(A, S, rec_from_lds(s_rec + j * 12), cap, dmod, magic);
+      rate_heavy<C, MP>(A, S, rec_from_lds(s_rec + j * 12), cap, dmod, magic);
     __syncthreads();
   }
 }
 
+template <int MP>
 __global__ __launch_bounds__(1024) void k_rate_big(RateArgs A, const NodeRec *big,
                                                    const u32 *cnt, u32 *work) {
   __shared__ HeavySmem<Big> S;
   __shared__ u32 s_item;
   __shared__ u32 s_rec[12];
   const u64 cap = A.capinfo[0], dmod = A.capinfo[1], magic = A.capinfo[2];
-  heavy_loop<Big, 1>(A, S, &s_item, s_rec, [&](u32 j) { return big + j; }, cnt[2], &work[2], cap,
+  heavy_loop<Big, 1, MP>(A, S, &s_item, s_rec, [&](u32 j) { return big + j; }, cnt[2], &work[2], cap,
                      dmod, magic);
 }
 
+template <int MP>
 __global__ __launch_bounds__(RB) void k_rate(RateArgs A, const u32 *light, const NodeRec *recs,
                                              u32 nrec, const u32 *cnt, u32 *work) {
   __shared__ RateSmem sm;
@@ -782,7 +800,7 @@ __global__ __launch_bounds__(RB) void k_rate(RateArgs A, const u32 *light, const
   __shared__ u32 s_rec[HB * 12];
   const u32 nl = cnt[0], nhuge = cnt[3];
   const u64 cap = A.capinfo[0], dmod = A.capinfo[1], magic = A.capinfo[2];
-  heavy_loop<Heavy, HB>(
+  heavy_loop<Heavy, HB, MP>(
       A, sm.h, &s_item, s_rec,
       [&](u32 j) { return j < nhuge ? recs + (nrec - 1 - j) : recs + (j - nhuge); },
       cnt[1] + nhuge, &work[0], cap, dmod, magic);
@@ -799,7 +817,7 @@ __global__ __launch_bounds__(RB) void k_rate(RateArgs A, const u32 *light, const
     if (lw >= nl) break;
     u32 nxt = 0;
     if (lane_id() == 0) nxt = atomicAdd(&work[1], 1u);
-    rate_light(A, S, light[lw], cap, dmod, magic);
+    rate_light<MP>(A, S, light[lw], cap, dmod, magic);
     wave_sync();
     lw = __builtin_amdgcn_readfirstlane(__shfl(nxt, 0, WAVE));
   }
@@ -908,6 +926,44 @@ __global__ void k_jump_finish(u32 N, const u32 *p, const uint8_t *x, uint8_t *tk
   tk[v] = x[v];
 }
 
+// Pi matching rounds ([HP] Sec. V-D): in each round a node still unmatched
+// proposes to the first entry of its top-pi list (rows of target/score,
+// stride N) that is still unmatched, with that entry's score; a matched node
+// proposes nothing.  Along a cycle of these proposals the scores could not
+// fall and the ids would have to fall strictly, so each round's proposal
+// graph again has no cycle longer than two.  The round's matching gives mr;
+// its pairs join match.  Before the first round match is the identity.
+__global__ void k_round_prep(u32 N, u32 pi, const u32 *target, const u64 *score,
+                             const u32 *match, u32 *tr, u64 *sr) {
+  const u32 n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  u32 t = NONE32;
+  u64 sc = 0;
+  if (match[n] == n) {
+    for (u32 j = 0; j < pi; ++j) {
+      const u32 m = target[(u64)j * N + n];
+      if (m == NONE32) break;  // rows are filled best first
+      if (match[m] == m) {
+        t = m;
+        sc = score[(u64)j * N + n];
+        break;
+      }
+    }
+  }
+  tr[n] = t;
+  sr[n] = sc;
+}
+
+__global__ void k_round_merge(u32 N, const u32 *mr, u32 *match) {
+  const u32 n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n < N && mr[n] != n) match[n] = mr[n];
+}
+
+__global__ void k_iota(u32 N, u32 *p) {
+  const u32 n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n < N) p[n] = n;
+}
+
 // match(n) = target(n) if taken(n); else its best proposer if any; else n.
 __global__ __launch_bounds__(256) void k_match(u32 N, const u32 *target, const u32 *bid,
                                                const uint8_t *tk, u32 *match, u32 *npairs) {
@@ -947,8 +1003,15 @@ void launch_rate_classify(chp_ctx *c, const RateArgs &a, u32 lo, u32 hi, NbLists
 
 void launch_rate(chp_ctx *c, const RateArgs &a, NbLists nl, const NodeRec *recs, u32 nrec,
                  const NodeRec *big, u32 *work) {
-  CHP_LAUNCH(c, "rate_big", k_rate_big, c->n_cu, Big::B, 0, a, big, (const u32 *)nl.cnt, work);
-  CHP_LAUNCH(c, "rate", k_rate, c->n_cu * 4, RB, 0, a, (const u32 *)nl.list[0], recs, nrec,
+  if (a.pi > 1) {  // top-pi lists (pi <= RATE_MAX_PI)
+    CHP_LAUNCH(c, "rate_big", k_rate_big<RATE_MAX_PI>, c->n_cu, Big::B, 0, a, big,
+               (const u32 *)nl.cnt, work);
+    CHP_LAUNCH(c, "rate", k_rate<RATE_MAX_PI>, c->n_cu * 4, RB, 0, a, (const u32 *)nl.list[0],
+               recs, nrec, (const u32 *)nl.cnt, work);
+    return;
+  }
+  CHP_LAUNCH(c, "rate_big", k_rate_big<1>, c->n_cu, Big::B, 0, a, big, (const u32 *)nl.cnt, work);
+  CHP_LAUNCH(c, "rate", k_rate<1>, c->n_cu * 4, RB, 0, a, (const u32 *)nl.list[0], recs, nrec,
              (const u32 *)nl.cnt, work);
 }
 
@@ -985,4 +1048,21 @@ void launch_match_write(chp_ctx *c, u32 N, const u32 *target, MatchScratch ms, u
   if (N == 0) return;
   CHP_LAUNCH(c, "match", k_match, grid_for(N, 256), 256, 0, N, target, (const u32 *)ms.bid,
              (const uint8_t *)ms.tk, match, npairs);
+}
+
+void launch_round_prep(chp_ctx *c, u32 N, u32 pi, const u32 *target, const u64 *score,
+                       const u32 *match, u32 *tr, u64 *sr) {
+  if (N == 0) return;
+  CHP_LAUNCH(c, "round_prep", k_round_prep, grid_for(N, 256), 256, 0, N, pi, target, score, match,
+             tr, sr);
+}
+
+void launch_round_merge(chp_ctx *c, u32 N, const u32 *mr, u32 *match) {
+  if (N == 0) return;
+  CHP_LAUNCH(c, "round_merge", k_round_merge, grid_for(N, 256), 256, 0, N, mr, match);
+}
+
+void launch_iota(chp_ctx *c, u32 N, u32 *p) {
+  if (N == 0) return;
+  CHP_LAUNCH(c, "iota", k_iota, grid_for(N, 256), 256, 0, N, p);
 }

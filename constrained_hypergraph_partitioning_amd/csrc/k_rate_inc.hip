@@ -169,25 +169,20 @@ __device__ __forceinline__ T wg_reduce(T v, T *lds, Op op) {
   return r;
 }
 
-struct Best {
-  u64 e;
-  u32 i;
-};
-
-// m with raw eta v and inter c: judged and, if it can still win, noised
+// m with raw eta v and inter c: judged and, if it can still enter the
+// thread's list, noised
+template <int MP>
 __device__ __forceinline__ void take(const RateArgs &A, u32 n, u64 size_n, u32 nin, bool om,
                                      bool de, u32 m, u64 v, u32 c, u32 sz, u32 ni, u64 ub,
-                                     u64 dmod, u64 magic, Best &b) {
+                                     u64 dmod, u64 magic, TopList<MP> &b) {
   if (om && size_n + sz > A.omega) return;
   if (de && (u64)nin + ni - c > (u64)A.delta) return;
-  if (!better(v + ub, m, b.e, b.i)) return;
+  if (!b.admits(v + ub, m)) return;
   const u64 tv = A.noise_on ? v + pair_noise(A.seed, n, m, dmod, magic) : v;
-  if (better(tv, m, b.e, b.i)) {
-    b.e = tv;
-    b.i = m;
-  }
+  if (b.admits(tv, m)) b.insert(tv, m);
 }
 
+template <int MP>
 __device__ void rate_inc_node(const RateArgs &A, IncSmem &S, const NodeRec &h, u32 max_size,
                               u32 max_nin, u32 hcap, u64 cap, u64 dmod, u64 magic) {
   const u32 tid = threadIdx.x, lane = lane_id(), wid = wave_id();
@@ -321,7 +316,8 @@ __device__ void rate_inc_node(const RateArgs &A, IncSmem &S, const NodeRec &h, u
     __syncthreads();
   }
   // -- windows over [mn, mx]
-  Best best{0, NONE32};
+  TopList<MP> best;
+  best.clear();
   const u64 end = (u64)mx + 1;
   u64 lo = mn;
   // id span a hash window may take: halved after a window that filled up,
@@ -527,37 +523,55 @@ __device__ void rate_inc_node(const RateArgs &A, IncSmem &S, const NodeRec &h, u
     // the next window's first barrier orders these slot clears before its
     // visits, and the reads of fail_min before its reset
   }
+  if (MP > 1) {
+#pragma unroll
+    for (int d = WAVE / 2; d > 0; d >>= 1) tsum = sat_add(tsum, __shfl_xor(tsum, d, WAVE));
+    if (lane == 0) S.red64[wid] = tsum;
+    __syncthreads();
+    if (tid == 0) {
+      tsum = 0;
+#pragma unroll
+      for (int w = 0; w < FW; ++w) tsum = sat_add(tsum, S.red64[w]);
+      if (sat_add(tsum, cap) >= (1ull << 63)) atomicOr(A.flags, FLAG_EOVERFLOW);
+    }
+    emit_top<FB, MP>(best, A.pi, S.rede, S.redi, tid == 0, A.target, A.score, A.N, n);
+    return;
+  }
   // -- term sum and best candidate: per wave by shuffles, then thread 0
+  u64 be = best.e[0];
+  u32 bi = best.i[0];
 #pragma unroll
   for (int d = WAVE / 2; d > 0; d >>= 1) {
     tsum = sat_add(tsum, __shfl_xor(tsum, d, WAVE));
-    const u64 oe = __shfl_xor(best.e, d, WAVE);
-    const u32 oi = __shfl_xor(best.i, d, WAVE);
-    if (better(oe, oi, best.e, best.i)) best.e = oe, best.i = oi;
+    const u64 oe = __shfl_xor(be, d, WAVE);
+    const u32 oi = __shfl_xor(bi, d, WAVE);
+    if (better(oe, oi, be, bi)) be = oe, bi = oi;
   }
   if (lane == 0) {
     S.red64[wid] = tsum;
-    S.rede[wid] = best.e;
-    S.redi[wid] = best.i;
+    S.rede[wid] = be;
+    S.redi[wid] = bi;
   }
   __syncthreads();
   if (tid == 0) {
     tsum = 0;
-    best = Best{0, NONE32};
+    be = 0;
+    bi = NONE32;
 #pragma unroll
     for (int w = 0; w < FW; ++w) {
       tsum = sat_add(tsum, S.red64[w]);
-      if (better(S.rede[w], S.redi[w], best.e, best.i)) best.e = S.rede[w], best.i = S.redi[w];
+      if (better(S.rede[w], S.redi[w], be, bi)) be = S.rede[w], bi = S.redi[w];
     }
     if (sat_add(tsum, cap) >= (1ull << 63)) atomicOr(A.flags, FLAG_EOVERFLOW);
-    A.target[n] = best.i;
-    A.score[n] = best.i == NONE32 ? 0 : best.e;
+    A.target[n] = bi;
+    A.score[n] = bi == NONE32 ? 0 : be;
   }
 }
 
 // Nodes are taken one at a time from a counter (thread 0 takes the item, a
 // barrier publishes it, and the loop body ends with a barrier so that every
 // lane reconverges before the back edge).
+template <int MP>
 __global__ __launch_bounds__(FB) void k_rate_inc(RateArgs A, const NodeRec *recs, const u32 *cnt,
                                                  const u32 *gmax, u32 *work, u32 hcap) {
   __shared__ IncSmem S;
@@ -579,7 +593,7 @@ __global__ __launch_bounds__(FB) void k_rate_inc(RateArgs A, const NodeRec *recs
     h.deg = rfl(h.deg);
     h.nin = rfl(h.nin);
     h.size = rfl(h.size);
-    rate_inc_node(A, S, h, max_size, max_nin, hcap, cap, dmod, magic);
+    rate_inc_node<MP>(A, S, h, max_size, max_nin, hcap, cap, dmod, magic);
     __syncthreads();
   }
 }
@@ -648,5 +662,8 @@ void launch_rate_inc(chp_ctx *c, const RateArgs &a, const NodeRec *recs, const u
   if (!host_count) return;
   const u32 g = host_count < c->n_cu ? host_count : c->n_cu;
   const u32 hcap = hash_keys && hash_keys < FCAP ? hash_keys : FCAP;
-  CHP_LAUNCH(c, "rate_inc", k_rate_inc, g, FB, 0, a, recs, cnt, gmax, work, hcap);
+  if (a.pi > 1)
+    CHP_LAUNCH(c, "rate_inc", k_rate_inc<RATE_MAX_PI>, g, FB, 0, a, recs, cnt, gmax, work, hcap);
+  else
+    CHP_LAUNCH(c, "rate_inc", k_rate_inc<1>, g, FB, 0, a, recs, cnt, gmax, work, hcap);
 }

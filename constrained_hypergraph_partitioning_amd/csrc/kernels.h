@@ -7,6 +7,7 @@
 constexpr u32 LDS_CAP_U32 = 8192;   // u32 keys one workgroup sorts in LDS
 constexpr u32 LDS_CAP_U64 = 8192;   // u64 keys one workgroup sorts in LDS
 constexpr u32 RATE_SMALL_CAP = 384; // |N(n)| of a node rated by one wave
+constexpr u32 RATE_MAX_PI = 4;      // candidates a node may keep ([HP] Sec. V-D uses 4)
 constexpr u32 NBM_LDS_CAP = 8192;   // largest coarse neighbour bound merged in LDS
 
 // Runs to sort in place, bucketed by length: class 0 (<= 64 keys, one wave
@@ -92,8 +93,9 @@ struct RateArgs {
   u32 delta;
   u32 noise_on;
   u64 seed;
-  u32 *target;
-  u64 *score;
+  u32 *target;  // [pi * N]: row r holds every node's (r+1)-th best valid candidate
+  u64 *score;   // [pi * N]
+  u32 pi;       // rows, 1 .. RATE_MAX_PI
   u32 *flags;
 };
 // nodes lo .. hi - 1
@@ -266,6 +268,15 @@ void launch_eval_parts(chp_ctx *c, u32 k, const u64 *part_size, const u32 *part_
 
 // ---- small device fills (api.hip) -------------------------------------------
 void launch_fill_u32(chp_ctx *c, u32 *p, u64 n, u32 v);
+// p[n] = n for n < N
+void launch_iota(chp_ctx *c, u32 N, u32 *p);
+// One of the pi matching rounds over top-pi lists (rows of stride N): each
+// node still unmatched in match proposes to its first still-unmatched entry
+// (tr/sr, NONE32/0 otherwise); after the round's matching mr, its pairs join
+// match.
+void launch_round_prep(chp_ctx *c, u32 N, u32 pi, const u32 *target, const u64 *score,
+                       const u32 *match, u32 *tr, u64 *sr);
+void launch_round_merge(chp_ctx *c, u32 N, const u32 *mr, u32 *match);
 // Several fills in one launch (at most 8 arrays): n elements of u32 (or of
 // u64 when wide) set to v.
 struct FillItem {

@@ -161,6 +161,30 @@ int chp_rate_and_match(chp_ctx *ctx, const chp_hgraph *g, const chp_params *prm,
                        uint32_t *target, uint64_t *score_fx, uint32_t *match,
                        uint32_t *n_pairs_host, uint8_t *nb_invalid);
 
+/* rate_top_and_match: the top-pi candidates with pi matching rounds
+ * ([HP] Sec. V-D).  As chp_rate_and_match (which is this call with pi = 1),
+ * except:
+ *  target[pi * N], score_fx[pi * N]  row r (entries r*N .. r*N + N - 1) holds
+ *              every node's (r+1)-th best valid neighbour by (eta desc, id
+ *              asc) and its eta_fx; CHP_NONE and 0 past the node's valid
+ *              neighbours.  Row 0 is chp_rate_and_match's target/score_fx.
+ *  match[N]    built over pi rounds.  In each round every node not yet
+ *              matched proposes to the first entry of its list that is not yet
+ *              matched, with that entry's score; matched nodes propose
+ *              nothing.  The round's proposals are matched as
+ *              chp_rate_and_match matches its targets (the handshake, or the
+ *              exact matching under CHP_MATCH_OPTIMAL), and its pairs join
+ *              match.  Each round's proposals again form two-cycles at most:
+ *              along a longer cycle the scores could not fall and the ids would
+ *              have to fall strictly.  Rounds stop early after one that pairs
+ *              nothing (the next would propose the same).
+ *  *n_pairs_host pairs over all rounds.
+ * chp_pair_leftovers then reads row 0 as its target.  pi must be 1 .. 4
+ * (EINVAL otherwise).  Synchronises. */
+int chp_rate_top_and_match(chp_ctx *ctx, const chp_hgraph *g, const chp_params *prm, uint32_t pi,
+                           uint32_t *target, uint64_t *score_fx, uint32_t *match,
+                           uint32_t *n_pairs_host, uint8_t *nb_invalid);
+
 /* propose_moves: refinement move proposal ([HP] Sec. VI-A/B, Eq. 13) for the
  * partition rho[N] in [0, k).  With pins(p, e) the pins of e in partition p:
  *  saving(n)  = sum of w(e), e in I(n), pins(rho(n), e) == 1;

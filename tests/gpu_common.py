@@ -37,23 +37,35 @@ def assert_equal(got, want, what):
 
 
 def run_level_pair(chp, ctx, dg, og, omega, delta, noise_on, seed, neighbors=True, tag="",
-                   purge=False, leftovers=False, optimal=False):
+                   purge=False, leftovers=False, optimal=False, pi=1):
     """One level on both sides; compares target, score, match, pairs, gamma
     and the coarse graph (with purge, also the invalid-neighbour flags, and
     the coarse neighbourhoods purged; with leftovers, after the best-effort
     pairing of the nodes left without a partner).  Returns (device coarse,
-    oracle Level, device gamma)."""
+    oracle Level, device gamma).  With pi > 1 the device call is
+    rate_top_and_match and the whole (pi, N) candidate lists are compared
+    with the oracle's top-pi rating; target/score below are then row 0."""
     flags = ctx.new_flags(dg) if purge else None
     ctx.set_matching(optimal)
     try:
-        tgt, score, match, npairs = ctx.rate_and_match(dg, omega, delta, noise_on, seed,
-                                                       flags=flags)
+        if pi > 1:
+            tl, sl, match, npairs = ctx.rate_top_and_match(dg, pi, omega, delta, noise_on, seed,
+                                                           flags=flags)
+            otl, osl = oracle.rate_top(og, omega, delta, noise_on, seed, pi)
+            assert_equal(chp.to_host(tl, np.uint32).reshape(-1), otl.reshape(-1),
+                         tag + " top-pi targets")
+            assert_equal(chp.to_host(sl, np.uint64).reshape(-1), osl.reshape(-1),
+                         tag + " top-pi scores")
+            tgt, score = tl[0], sl[0]
+        else:
+            tgt, score, match, npairs = ctx.rate_and_match(dg, omega, delta, noise_on, seed,
+                                                           flags=flags)
     finally:
         ctx.set_matching(False)
     if leftovers:
         npairs += ctx.pair_leftovers(dg, tgt, match, omega, delta)
     lv = oracle.level(og, omega, delta, noise_on, seed, build_neighbors=neighbors,
-                      purge_invalid=purge, leftovers=leftovers, optimal=optimal)
+                      purge_invalid=purge, leftovers=leftovers, optimal=optimal, pi=pi)
     assert_equal(chp.to_host(tgt, np.uint32), lv.target, tag + " target")
     assert_equal(chp.to_host(score, np.uint64), lv.score, tag + " score")
     assert_equal(chp.to_host(match, np.uint32), lv.match, tag + " match")

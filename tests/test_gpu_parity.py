@@ -45,7 +45,7 @@ def both(chp, ctx, h, omega, delta, neighbors=True):
 
 
 def multilevel(chp, ctx, h, omega, delta, noise_on, seed, max_levels, target_nodes=0,
-               eval_every=False, tag="", purge=False, leftovers=False, optimal=False):
+               eval_every=False, tag="", purge=False, leftovers=False, optimal=False, pi=1):
     dg, og = both(chp, ctx, h, omega, delta)
     rho = np.arange(h.n_nodes, dtype=np.uint32)
     og0, dg0 = og, dg
@@ -56,7 +56,7 @@ def multilevel(chp, ctx, h, omega, delta, noise_on, seed, max_levels, target_nod
             break
         cg, lv, gamma = run_level_pair(chp, ctx, dg, og, omega, delta, noise_on, seed,
                                        tag="%s L%d" % (tag, lvl), purge=purge,
-                                       leftovers=leftovers, optimal=optimal)
+                                       leftovers=leftovers, optimal=optimal, pi=pi)
         levels += 1
         if cg is None:
             break
@@ -150,7 +150,7 @@ def fused_mask(og, min_visits):
     return (deg >= 1) & (deg <= 384) & (w >= min_visits) & (w < 2 ** 27)
 
 
-def batched_levels(chp, ctx, h, omega, delta, seed, levels, limit, inc, hkeys=0, tag=""):
+def batched_levels(chp, ctx, h, omega, delta, seed, levels, limit, inc, hkeys=0, tag="", pi=1):
     """Levels of a graph built without neighbourhoods: the rating builds
     them per batch or rates straight from the incidence; every level's
     target, score, match, gamma and coarse graph against the oracle, and the
@@ -164,7 +164,16 @@ def batched_levels(chp, ctx, h, omega, delta, seed, levels, limit, inc, hkeys=0,
     ctx.set_incidence_rating(inc, hkeys)
     try:
         for lvl in range(levels):
-            t, sc, m, npairs = ctx.rate_and_match(dg, omega, delta, True, seed)
+            if pi > 1:
+                tl, sl, m, npairs = ctx.rate_top_and_match(dg, pi, omega, delta, True, seed)
+                otl, osl = oracle.rate_top(og, omega, delta, True, seed, pi)
+                assert_equal(chp.to_host(tl, np.uint32).reshape(-1), otl.reshape(-1),
+                             "%s L%d top-pi targets" % (tag, lvl))
+                assert_equal(chp.to_host(sl, np.uint64).reshape(-1), osl.reshape(-1),
+                             "%s L%d top-pi scores" % (tag, lvl))
+                t, sc = tl[0], sl[0]
+            else:
+                t, sc, m, npairs = ctx.rate_and_match(dg, omega, delta, True, seed)
             built, batches, nfused = ctx.last_rate_stats()
             fm = fused_mask(og, inc if inc else INC_DEFAULT)
             # entries built over the batches = sum of |N(n)| over the other nodes
@@ -172,7 +181,7 @@ def batched_levels(chp, ctx, h, omega, delta, seed, levels, limit, inc, hkeys=0,
             want_nb = int(np.diff(nbo)[~fm].sum())
             assert (nfused, built) == (int(fm.sum()), want_nb) and batches >= 1, \
                 (nfused, int(fm.sum()), built, want_nb, batches)
-            lv = oracle.level(og, omega, delta, True, seed, build_neighbors=False)
+            lv = oracle.level(og, omega, delta, True, seed, build_neighbors=False, pi=pi)
             for name, got, want in (("target", chp.to_host(t, np.uint32), lv.target),
                                     ("score", chp.to_host(sc, np.uint64), lv.score),
                                     ("match", chp.to_host(m, np.uint32), lv.match)):
@@ -337,6 +346,96 @@ def test_optimal_matching_tiny_and_chain(chp, ctx):
     say("dp chain", n)
     dg, og = both(chp, ctx, h, 1 << 30, 1 << 30)
     run_level_pair(chp, ctx, dg, og, 1 << 30, 1 << 30, False, 0, tag="dp chain", optimal=True)
+
+
+@pytest.mark.parametrize("pi", [2, 4])
+def test_top_pi_tiny(chp, ctx, pi):
+    """Top-pi lists and pi matching rounds on the tiny graphs under the limit
+    grid, with the handshake and with the exact matching, noise on and off."""
+    import test_oracle_pins as pins
+    for kw in pins.tiny_cases():
+        h = synth.tiny(**kw)
+        say("top-pi tiny", pi, kw["seed"])
+        for omega, delta in pins.constraint_grid(h):
+            dg, og = both(chp, ctx, h, omega, delta)
+            for optimal in (False, True):
+                for noise_on in (True, False):
+                    run_level_pair(chp, ctx, dg, og, omega, delta, noise_on, kw["seed"],
+                                   tag="top%d tiny%d" % (pi, kw["seed"]), optimal=optimal, pi=pi)
+
+
+@pytest.mark.parametrize("cfg,nn,levels,optimal", [(1, None, 10, False), (2, 20000, 20, False),
+                                                   (3, 5000, 4, False), (4, 20000, 12, False),
+                                                   (5, 8192, 1, False), (2, 20000, 8, True),
+                                                   (4, 20000, 6, True)])
+def test_top_pi_multilevel(chp, ctx, cfg, nn, levels, optimal):
+    """Pi = 4 rounds on the scaled workloads, several levels, with purge and
+    leftovers: every level's lists, match and coarse graph against the
+    oracle."""
+    spec = synth.config(cfg, n_nodes=nn)
+    h = synth.generate(spec)
+    say("top-pi multilevel", cfg, nn, optimal)
+    multilevel(chp, ctx, h, spec.omega, spec.delta, True, spec.seed, levels,
+               target_nodes=spec.target_nodes, tag="top4 %d" % cfg, purge=True, leftovers=True,
+               optimal=optimal, pi=4)
+
+
+def test_top_pi_wide_and_windowed(chp, ctx):
+    """Top-4 lists of nodes rated by every kernel shape: several windows of
+    the small and the large table, hyperedges over several chunks, hubs."""
+    for n, kmin, kmax, seed in ((12000, 60, 140, 9), (2000, 520, 560, 22)):
+        say("top-pi windowed", n, kmin, kmax)
+        spec = synth.custom(synth.UNIFORM, n, n, kmin, kmax, 8, 1, 1 << 20, 1 << 20, seed)
+        h = synth.generate(spec)
+        multilevel(chp, ctx, h, spec.omega, spec.delta, True, seed, 2, tag="top4 wide", pi=4)
+    say("top-pi hubs")
+    rng = np.random.Generator(np.random.PCG64(24))
+    n = 10000
+    el = []
+    for hub in (17, 4242, 9999):
+        for _ in range(700):
+            p = rng.permutation(n)[:20]
+            p = p[p != hub][:19]
+            el.append(([int(p[0])], [hub] + [int(x) for x in p[1:]]))
+    for _ in range(3000):
+        p = rng.permutation(n)[: int(rng.integers(2, 9))]
+        el.append(([int(p[0])], [int(x) for x in p[1:]]))
+    h = synth.from_lists(n, el, rng.integers(1, 9, len(el)).tolist())
+    multilevel(chp, ctx, h, 1 << 20, 1 << 20, True, 24, 2, tag="top4 hubs", pi=4)
+
+
+@pytest.mark.parametrize("mode", ["lists", "all", "all-hash64"])
+@pytest.mark.parametrize("cfg,nn,limit", [(2, 20000, 60000), (5, 8192, 1000000)])
+def test_top_pi_without_lists(chp, ctx, cfg, nn, limit, mode):
+    """Top-4 lists of a graph built without neighbourhoods, through the
+    per-batch lists and straight from the incidence (sparse windows capped
+    at 64 keys too)."""
+    spec = synth.config(cfg, n_nodes=nn)
+    h = synth.generate(spec)
+    inc, hkeys = INC_MODES[mode]
+    say("top-pi batched", cfg, nn, limit, mode)
+    batched_levels(chp, ctx, h, spec.omega, spec.delta, spec.seed, 2, limit, inc, hkeys,
+                   tag="top4 batched %d %s" % (cfg, mode), pi=4)
+
+
+def test_top_pi_one_and_errors(chp, ctx):
+    """pi = 1 through the top-pi call is chp_rate_and_match; pi outside
+    1 .. 4 is rejected."""
+    spec = synth.config(2, n_nodes=20000)
+    h = synth.generate(spec)
+    say("top-pi one")
+    dg, og = both(chp, ctx, h, spec.omega, spec.delta)
+    t1, s1, m1, p1 = ctx.rate_and_match(dg, spec.omega, spec.delta, True, 3)
+    tl, sl, m2, p2 = ctx.rate_top_and_match(dg, 1, spec.omega, spec.delta, True, 3)
+    assert_equal(chp.to_host(tl[0], np.uint32), chp.to_host(t1, np.uint32), "pi 1 target")
+    assert_equal(chp.to_host(sl[0], np.uint64), chp.to_host(s1, np.uint64), "pi 1 score")
+    assert_equal(chp.to_host(m2, np.uint32), chp.to_host(m1, np.uint32), "pi 1 match")
+    assert p1 == p2
+    for bad in (0, 5):
+        with pytest.raises(chp.ChpError) as ei:
+            ctx.rate_top_and_match(dg, bad, spec.omega, spec.delta, True, 3,
+                                   out=(tl, sl, m2) if bad == 0 else None)
+        assert ei.value.code == chp.EINVAL
 
 
 def moves_pair(chp, ctx, dg, og, rho, k, omega, enforce, tag):
