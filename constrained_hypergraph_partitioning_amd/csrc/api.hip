@@ -291,7 +291,7 @@ void build_neighbors_core(chp_ctx *c, Scratch &s, Owned &own, chp_hgraph *g) {
   nl.list[3] = nl.list[4] = nullptr;
   nl.cnt = s.get<u32>(8);
   launch_fill_u32(c, nl.cnt, 8, 0);
-  launch_nb_classify(c, 0, N, g->e_off, g->n_off, g->n_inc, bound, nl);
+  launch_nb_classify(c, 0, N, g->e_off, g->e_nsrc, g->e_pins, g->n_off, g->n_inc, bound, nl);
   i64 *ooff = s.get<i64>((u64)N + 1);
   i64 *tmp = s.get<i64>(scan_tmp_words(N));
   scan_u32_to_i64(c, bound, ooff, N, tmp);
@@ -695,7 +695,8 @@ void rate_batched(chp_ctx *c, Scratch &s, const chp_hgraph *g, const RateArgs &a
   NbLists bl;
   bl.list[0] = s.get<u32>(N);
   bl.list[1] = s.get<u32>(N);
-  bl.list[2] = bl.list[3] = bl.list[4] = nullptr;
+  bl.list[2] = s.get<u32>(N);
+  bl.list[3] = bl.list[4] = nullptr;
   bl.cnt = s.get<u32>(8);
   // nodes with many incident pins are rated straight from the incidence
   // (after the batches); the others through per-batch neighbour lists
@@ -709,7 +710,8 @@ void rate_batched(chp_ctx *c, Scratch &s, const chp_hgraph *g, const RateArgs &a
   }
   launch_fills(c, {{bl.cnt, 8, 0, false}, {fc, 4, 0, false}});
   if (skip) launch_inc_classify(c, a, fmin, skip, frecs, fc, fc + 1);
-  launch_nb_classify(c, 0, N, g->e_off, g->n_off, g->n_inc, bound, bl, skip);
+  launch_nb_classify(c, 0, N, g->e_off, g->e_nsrc, g->e_pins, g->n_off, g->n_inc, bound, bl,
+                     skip);
   i64 *ooff = s.get<i64>((u64)N + 1);
   i64 *tmp = s.get<i64>(scan_tmp_words(N));
   scan_u32_to_i64(c, bound, ooff, N, tmp);
@@ -746,7 +748,8 @@ void rate_batched(chp_ctx *c, Scratch &s, const chp_hgraph *g, const RateArgs &a
     const u32 cnt = hi - lo;
     // N(n) of the batch (bounds recomputed for the range, same values)
     launch_fills(c, {{bl.cnt, 8, 0, false}, {count + lo, cnt, 0, false}});
-    launch_nb_classify(c, lo, cnt, g->e_off, g->n_off, g->n_inc, bound, bl, skip);
+    launch_nb_classify(c, lo, cnt, g->e_off, g->e_nsrc, g->e_pins, g->n_off, g->n_inc, bound,
+                       bl, skip);
     launch_check(c, "batch neighbour classes");
     i64 last = 0;
     if (prev)

@@ -229,8 +229,14 @@ __global__ void k_node_runs(u32 N, const i64 *n_off, const u32 *n_nin, RunLists 
 // neighbourhoods: W_n = sum_{e in I(n)} |e| decides the class; the oversize
 // bound of |N(n)| is W_n - |I(n)| (n is a pin of each of its hyperedges).
 // Nodes lo .. lo + N - 1; a node marked in skip gets bound 0 and no class.
-__global__ void k_nb_classify(u32 lo, u32 N, const i64 *e_off, const i64 *n_off,
-                              const u32 *n_inc, u32 *bound, NbLists nl, const uint8_t *skip) {
+// Classes: one wave (W_n <= 64); a workgroup sort (W_n <= NB_SORT_CAP and
+// the pins' id span needs more bitmap words than there are pins: the bitmap
+// would mostly scan empty words); the LDS bitmap (the rest).  The span comes
+// from the ends of each hyperedge's two sorted runs.
+constexpr u32 NB_SORT_CAP = 1024;
+__global__ void k_nb_classify(u32 lo, u32 N, const i64 *e_off, const u32 *e_nsrc,
+                              const u32 *pins, const i64 *n_off, const u32 *n_inc, u32 *bound,
+                              NbLists nl, const uint8_t *skip) {
   const u32 t = blockIdx.x * blockDim.x + threadIdx.x;
   const u32 n = lo + t;
   u64 w = 0, bnd = 0;
@@ -249,11 +255,28 @@ __global__ void k_nb_classify(u32 lo, u32 N, const i64 *e_off, const i64 *n_off,
     }
     bound[n] = (u32)bnd;
   }
-  // isolated nodes (bnd 0) have an empty N(n) and join no class; the others
-  // are built by one wave (W_n <= 64) or by the LDS bitmap
-  const int c = bnd == 0 ? 2 : (w <= 64 ? 0 : 1);
+  bool sparse = false;
+  if (bnd != 0 && w > 64 && w <= NB_SORT_CAP) {
+    const i64 a = n_off[n], b = n_off[n + 1];
+    u32 mn = NONE32, mx = 0;
+    for (i64 j = a; j < b; ++j) {
+      const u32 e = n_inc[j];
+      const i64 s0 = e_off[e], s1 = e_off[e + 1], d0 = s0 + e_nsrc[e];
+      if (d0 > s0) {  // source run
+        mn = pins[s0] < mn ? pins[s0] : mn;
+        mx = pins[d0 - 1] > mx ? pins[d0 - 1] : mx;
+      }
+      if (s1 > d0) {  // destination run
+        mn = pins[d0] < mn ? pins[d0] : mn;
+        mx = pins[s1 - 1] > mx ? pins[s1 - 1] : mx;
+      }
+    }
+    sparse = (u64)(mx - mn) / 32 + 1 > w;
+  }
+  // isolated nodes (bnd 0) have an empty N(n) and join no class
+  const int c = bnd == 0 ? 3 : (w <= 64 ? 0 : sparse ? 2 : 1);
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < 3; ++k) {
     const u32 slot = wave_append(&nl.cnt[k], c == k);
     if (c == k) nl.list[k][slot] = n;
   }
@@ -294,6 +317,54 @@ __global__ __launch_bounds__(256) void k_nb_wave(const i64 *e_off, const u32 *pi
     u32 pos = __popcll(mask & ((1ull << l) - 1));
     if (keep) obuf[ooff[n] + pos] = v;
     if (l == 0) count[n] = (u32)__popcll(mask);
+  }
+}
+
+// A workgroup per node of the sort class: the pins of I(n) (at most CAP) are
+// gathered into LDS hyperedge by hyperedge (a scan lays the segments end to
+// end), sorted (bitonic) and written without repeats and without n.
+template <int BLOCK, int CAP>
+__global__ __launch_bounds__(BLOCK) void k_nb_sort(const i64 *e_off, const u32 *pins,
+                                                   const i64 *n_off, const u32 *n_inc,
+                                                   const i64 *ooff, u32 *obuf, u32 *count,
+                                                   const u32 *list, const u32 *cnt) {
+  __shared__ u32 s[CAP];
+  __shared__ i64 st[BLOCK];
+  __shared__ u32 pre[BLOCK + 1];
+  __shared__ u32 s_red[BLOCK / WAVE + 1];
+  const u32 total = *cnt;
+  for (u32 w = blockIdx.x; w < total; w += gridDim.x) {
+    const u32 n = list[w];
+    const i64 a = n_off[n], b = n_off[n + 1];
+    u32 fill = 0;
+    for (i64 c0 = a; c0 < b; c0 += BLOCK) {
+      const u32 ne = (u32)((b - c0) < BLOCK ? (b - c0) : BLOCK);
+      u32 len = 0;
+      if (threadIdx.x < ne) {
+        const u32 e = n_inc[c0 + threadIdx.x];
+        const i64 e0 = e_off[e];
+        len = (u32)(e_off[e + 1] - e0);
+        st[threadIdx.x] = e0;
+      }
+      u32 tot;
+      const u32 off = wg_excl_scan<BLOCK>(len, s_red, &tot);
+      if (threadIdx.x < ne) pre[threadIdx.x] = off;
+      if (threadIdx.x == 0) pre[ne] = tot;
+      __syncthreads();
+      for (u32 i = threadIdx.x; i < tot; i += BLOCK) {
+        const u32 r = run_of(pre, ne + 1, i);
+        s[fill + i] = pins[st[r] + (i - pre[r])];
+      }
+      fill += tot;
+      __syncthreads();
+    }
+    const u32 p = next_pow2(fill);
+    for (u32 i = fill + threadIdx.x; i < p; i += BLOCK) s[i] = NONE32;
+    __syncthreads();
+    lds_bitonic<BLOCK>(s, p);
+    const u32 k = unique_out<BLOCK>(s, fill, n, obuf + ooff[n], s_red);
+    if (threadIdx.x == 0) count[n] = k;
+    __syncthreads();
   }
 }
 
@@ -371,11 +442,12 @@ void launch_node_runs(chp_ctx *c, u32 N, const i64 *n_off, const u32 *n_nin, Run
   CHP_LAUNCH(c, "node_runs", k_node_runs, grid_for(N, 256), 256, 0, N, n_off, n_nin, rl);
 }
 
-void launch_nb_classify(chp_ctx *c, u32 lo, u32 N, const i64 *e_off, const i64 *n_off,
-                        const u32 *n_inc, u32 *bound, NbLists nl, const uint8_t *skip) {
+void launch_nb_classify(chp_ctx *c, u32 lo, u32 N, const i64 *e_off, const u32 *e_nsrc,
+                        const u32 *pins, const i64 *n_off, const u32 *n_inc, u32 *bound,
+                        NbLists nl, const uint8_t *skip) {
   if (N == 0) return;
-  CHP_LAUNCH(c, "nb_classify", k_nb_classify, grid_for(N, 256), 256, 0, lo, N, e_off, n_off,
-             n_inc, bound, nl, skip);
+  CHP_LAUNCH(c, "nb_classify", k_nb_classify, grid_for(N, 256), 256, 0, lo, N, e_off, e_nsrc,
+             pins, n_off, n_inc, bound, nl, skip);
 }
 
 void launch_nb_build(chp_ctx *c, u32 N, const i64 *e_off, const u32 *pins, const i64 *n_off,
@@ -384,6 +456,10 @@ void launch_nb_build(chp_ctx *c, u32 N, const i64 *e_off, const u32 *pins, const
   if (host_cnt[0])
     CHP_LAUNCH(c, "nb_wave", k_nb_wave, waves_grid(host_cnt[0]), 256, 0, e_off, pins, n_off,
                n_inc, ooff, obuf, count, nl.list[0], nl.cnt + 0);
+  if (host_cnt[2])
+    CHP_LAUNCH(c, "nb_sort", (k_nb_sort<256, NB_SORT_CAP>),
+               host_cnt[2] < 8 * c->n_cu ? host_cnt[2] : 8 * c->n_cu, 256, 0, e_off, pins, n_off,
+               n_inc, ooff, obuf, count, (const u32 *)nl.list[2], (const u32 *)nl.cnt + 2);
   launch_nb_bitmap(c, N, e_off, pins, n_off, n_inc, bound, ooff, obuf, count, nl.list[1],
                    nl.cnt + 1, host_cnt[1]);
 }

@@ -51,9 +51,10 @@ void launch_scatter(chp_ctx *c, u32 E, const i64 *e_off, const u32 *e_nsrc, cons
                     const i64 *n_off, const u32 *n_nin, u32 *cur_in, u32 *cur_out, u32 *n_inc);
 void launch_node_runs(chp_ctx *c, u32 N, const i64 *n_off, const u32 *n_nin, RunLists rl);
 // nodes lo .. lo + N - 1
-void launch_nb_classify(chp_ctx *c, u32 lo, u32 N, const i64 *e_off, const i64 *n_off, const u32 *n_inc,
-                        u32 *bound, NbLists nl,
-                        const uint8_t *skip = nullptr);
+// classes: list[0] one wave, list[1] LDS bitmap, list[2] workgroup sort
+void launch_nb_classify(chp_ctx *c, u32 lo, u32 N, const i64 *e_off, const u32 *e_nsrc,
+                        const u32 *pins, const i64 *n_off, const u32 *n_inc, u32 *bound,
+                        NbLists nl, const uint8_t *skip = nullptr);
 void launch_nb_build(chp_ctx *c, u32 N, const i64 *e_off, const u32 *pins, const i64 *n_off,
                      const u32 *n_inc, const u32 *bound, const i64 *ooff, u32 *obuf, u32 *count,
                      NbLists nl, const u32 *host_cnt);

@@ -146,6 +146,33 @@ def test_ring_100k_full_level(chp, ctx):
     eval_pair(chp, ctx, g0d, g0o, rho, og.n_nodes, spec.omega, spec.delta, "projected")
 
 
+def test_ring_100k_top4_level(chp, ctx):
+    """The ring at full size as `bench.py --pi 4` runs its first level: the
+    top-4 lists of every node, the four matching rounds (with the purge
+    flags and the leftover pairing) and the coarse graph, array by array."""
+    spec = synth.config(2)
+    say("ring 100k top-4")
+    h = synth.generate(spec)
+    dg = ctx.build_incidence(*chp.upload_edges(h), spec.omega, spec.delta)
+    og = oracle.build_incidence(h.e_off, h.e_nsrc, h.e_pins, h.e_w, h.n_size, spec.omega,
+                                spec.delta)
+    flags = ctx.new_flags(dg)
+    tl, sl, match, npairs = ctx.rate_top_and_match(dg, 4, spec.omega, spec.delta, True,
+                                                   spec.seed, flags=flags)
+    npairs += ctx.pair_leftovers(dg, tl[0], match, spec.omega, spec.delta)
+    otl, osl = oracle.rate_top(og, spec.omega, spec.delta, True, spec.seed, 4)
+    assert_equal(chp.to_host(tl, np.uint32).reshape(-1), otl.reshape(-1), "top-4 targets")
+    assert_equal(chp.to_host(sl, np.uint64).reshape(-1), osl.reshape(-1), "top-4 scores")
+    lv = oracle.level(og, spec.omega, spec.delta, True, spec.seed, purge_invalid=True,
+                      leftovers=True, pi=4)
+    assert_equal(chp.to_host(match, np.uint32), lv.match, "top-4 match")
+    assert_equal(flags.cpu().numpy()[: og.nb.shape[0]], lv.flags, "top-4 flags")
+    assert npairs == lv.n_pairs
+    gamma, cg = ctx.contract(dg, match, flags=flags)
+    assert_equal(chp.to_host(gamma, np.uint32), lv.gamma, "top-4 gamma")
+    assert_graph_equal(cg, lv.coarse, "top-4 coarse")
+
+
 @pytest.mark.parametrize("cfg,sample", [(3, 64), (4, 400)])
 def test_large_workloads_sampled(chp, ctx, cfg, sample):
     """1M-node layered SNN and 2M-node VLSI netlist at full size."""

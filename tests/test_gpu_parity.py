@@ -730,6 +730,41 @@ def test_wide_neighbourhoods_and_big_edges(chp, ctx):
     eval_pair(chp, ctx, dg, og, rho, 37, 1 << 30, 1 << 30, "big eval")
 
 
+def test_sparse_span_neighbourhoods(chp, ctx):
+    """Level-0 neighbourhoods of nodes whose pins spread over a wide id span
+    (the workgroup-sort class: 64 < W_n <= 1024 and more bitmap words than
+    pins), at the class bounds W_n = 65 and W_n = 1024, with pins repeated
+    across a node's hyperedges, beside dense-span nodes of the same W_n."""
+    rng = np.random.Generator(np.random.PCG64(31))
+    n = 300000
+    el = []
+    hubs = [5, 150000, 299999, 77777, 123]
+    # hub k: hyperedges whose pins (other than the hub) total W_n - |I| over
+    # the whole id range, some pins shared between the hub's hyperedges
+    for hub, w_n, ne in zip(hubs, (65, 1024, 300, 1024, 512), (1, 8, 5, 16, 2)):
+        per = (w_n - ne) // ne
+        extra = (w_n - ne) - per * ne
+        pool = rng.choice(n, 3 * w_n, replace=False)
+        pool = pool[pool != hub]
+        for j in range(ne):
+            k = per + (1 if j < extra else 0)
+            pins = rng.choice(pool[: max(k + 8, w_n // 2)], k, replace=False)
+            el.append(([hub], [int(x) for x in pins]))
+    # dense-span nodes: the same sizes within a narrow id range
+    for base, w_n in ((200000, 65), (210000, 1024)):
+        el.append(([base], [base + 1 + i for i in range(w_n - 1)]))
+    special = set(hubs) | {200000, 210000}
+    while len(el) < 20000:  # small hyperedges that leave the nodes above alone
+        p = rng.choice(n, int(rng.integers(2, 6)), replace=False)
+        if not special.intersection(p.tolist()):
+            el.append(([int(p[0])], [int(x) for x in p[1:]]))
+    h = synth.from_lists(n, el, rng.integers(1, 5, len(el)).tolist())
+    say("sparse spans")
+    multilevel(chp, ctx, h, 1 << 20, 1 << 20, True, 31, 2, tag="sparse")
+    say("sparse spans, batched")
+    batched_levels(chp, ctx, h, 1 << 20, 1 << 20, 31, 1, 100000, NEVER, 0, tag="sparse batched")
+
+
 def test_windowed_nodes_with_many_hyperedges(chp, ctx):
     """Nodes whose neighbourhood spans several rating windows (|N(n)| above
     6144) and whose incident hyperedges span several chunks (more than 128,
