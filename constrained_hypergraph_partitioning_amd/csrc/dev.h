@@ -298,6 +298,40 @@ __device__ __forceinline__ u32 wave_append(u32 *counter, bool pred) {
   return base + (u32)__popcll(m & ((1ull << lane_id()) - 1));
 }
 
+// Workgroup-aggregated append into NC class lists: a thread of class cls
+// (0 <= cls < NC; any other value appends nothing) gets a slot unique within
+// its class.  One atomic per class per workgroup (shared counters serialise
+// their atomics, so per-wave appends cost ~1 ms per million items); every
+// thread of the workgroup must call it.  lds holds NC * (BLOCK / WAVE) + NC
+// words.
+template <int BLOCK, int NC>
+__device__ __forceinline__ u32 block_append(u32 *counters, int cls, u32 *lds) {
+  constexpr int NW = BLOCK / WAVE;
+  const u32 w = wave_id(), l = lane_id();
+  u32 rank = 0;
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const u64 m = __ballot(cls == k);
+    if (cls == k) rank = (u32)__popcll(m & ((1ull << l) - 1));
+    if (l == 0) lds[k * NW + w] = (u32)__popcll(m);
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < NC) {
+    const int k = threadIdx.x;
+    u32 tot = 0;
+    for (int i = 0; i < NW; ++i) {
+      const u32 c = lds[k * NW + i];
+      lds[k * NW + i] = tot;
+      tot += c;
+    }
+    lds[NC * NW + k] = tot ? atomicAdd(&counters[k], tot) : 0u;
+  }
+  __syncthreads();
+  const u32 slot = (cls >= 0 && cls < NC) ? lds[NC * NW + cls] + lds[cls * NW + w] + rank : 0u;
+  __syncthreads();
+  return slot;
+}
+
 // Bitonic sort of one key per lane across a wave (ascending by lane).
 template <typename K>
 __device__ __forceinline__ K wave_sort64(K v) {

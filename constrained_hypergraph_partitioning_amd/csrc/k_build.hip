@@ -234,9 +234,12 @@ __global__ void k_node_runs(u32 N, const i64 *n_off, const u32 *n_nin, RunLists 
 // would mostly scan empty words); the LDS bitmap (the rest).  The span comes
 // from the ends of each hyperedge's two sorted runs.
 constexpr u32 NB_SORT_CAP = 1024;
-__global__ void k_nb_classify(u32 lo, u32 N, const i64 *e_off, const u32 *e_nsrc,
-                              const u32 *pins, const i64 *n_off, const u32 *n_inc, u32 *bound,
-                              NbLists nl, const uint8_t *skip) {
+__global__ __launch_bounds__(256) void k_nb_classify(u32 lo, u32 N, const i64 *e_off,
+                                                     const u32 *e_nsrc, const u32 *pins,
+                                                     const i64 *n_off, const u32 *n_inc,
+                                                     u32 *bound, NbLists nl,
+                                                     const uint8_t *skip) {
+  __shared__ u32 s_app[3 * (256 / WAVE) + 3];
   const u32 t = blockIdx.x * blockDim.x + threadIdx.x;
   const u32 n = lo + t;
   u64 w = 0, bnd = 0;
@@ -275,11 +278,8 @@ __global__ void k_nb_classify(u32 lo, u32 N, const i64 *e_off, const u32 *e_nsrc
   }
   // isolated nodes (bnd 0) have an empty N(n) and join no class
   const int c = bnd == 0 ? 3 : (w <= 64 ? 0 : sparse ? 2 : 1);
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    const u32 slot = wave_append(&nl.cnt[k], c == k);
-    if (c == k) nl.list[k][slot] = n;
-  }
+  const u32 slot = block_append<256, 3>(nl.cnt, c, s_app);
+  if (c < 3) nl.list[c][slot] = n;
 }
 
 // wave per node, W_n <= 64: gather into lanes, sort, unique, drop n

@@ -25,9 +25,11 @@ namespace {
 // the compaction pass; a pair gets the bound |I(a)| + |I(b)| in the oversize
 // buffer and is merged by one sort of 64-bit keys (edge << 1 | is_out): in
 // each group of equal edge the first key tells whether it is inbound.
-__global__ void k_cinc_classify(u32 Nc, const u32 *rep_of, const u32 *match, const i64 *n_off,
-                                const u32 *n_nin, u32 *bound, u32 *cnt_in, u32 *cnt_tot,
-                                EdgeLists el) {
+__global__ __launch_bounds__(256) void k_cinc_classify(u32 Nc, const u32 *rep_of,
+                                                       const u32 *match, const i64 *n_off,
+                                                       const u32 *n_nin, u32 *bound,
+                                                       u32 *cnt_in, u32 *cnt_tot, EdgeLists el) {
+  __shared__ u32 s_app[3 * (256 / WAVE) + 3];
   const u32 c = blockIdx.x * blockDim.x + threadIdx.x;
   int cls = 3;
   u64 w = 0;
@@ -44,11 +46,8 @@ __global__ void k_cinc_classify(u32 Nc, const u32 *rep_of, const u32 *match, con
       cls = w <= 64 ? 0 : (w <= LDS_CAP_U64 ? 1 : 2);
     }
   }
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    const u32 slot = wave_append(&el.cnt[k], cls == k);
-    if (cls == k) el.list[k][slot] = c;
-  }
+  const u32 slot = block_append<256, 3>(el.cnt, cls, s_app);
+  if (cls < 3) el.list[cls][slot] = c;
   if (cls == 2) atomicMax(&el.cnt[3], (u32)w);
 }
 
@@ -166,8 +165,10 @@ __global__ __launch_bounds__(256) void k_cinc_compact(u32 Nc, const u32 *rep_of,
 
 // ---------------------------------------------------------------------------
 // coarse neighbourhoods
-__global__ void k_nbm_classify(u32 Nc, const u32 *rep_of, const u32 *match, const i64 *nb_off,
-                               u32 *bound, NbLists nl) {
+__global__ __launch_bounds__(256) void k_nbm_classify(u32 Nc, const u32 *rep_of,
+                                                      const u32 *match, const i64 *nb_off,
+                                                      u32 *bound, NbLists nl) {
+  __shared__ u32 s_app[3 * (256 / WAVE) + 3];
   const u32 c = blockIdx.x * blockDim.x + threadIdx.x;
   u64 w = 0;
   if (c < Nc) {
@@ -183,11 +184,8 @@ __global__ void k_nbm_classify(u32 Nc, const u32 *rep_of, const u32 *match, cons
   // classes: one wave in registers (<= 64); a one-wave merge (<= 1024);
   // the LDS bitmap (larger)
   const int cls = (c >= Nc || w == 0) ? 3 : w <= 64 ? 0 : w <= 1024 ? 1 : 2;
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    const u32 slot = wave_append(&nl.cnt[k], cls == k);
-    if (cls == k) nl.list[k][slot] = c;
-  }
+  const u32 slot = block_append<256, 3>(nl.cnt, cls, s_app);
+  if (cls < 3) nl.list[cls][slot] = c;
 }
 
 // bound <= 64: one wave, keys in registers.  With flags (fl, the invalid-

@@ -36,16 +36,14 @@ __global__ void k_gamma(u32 N, const u32 *match, const i64 *rank, const u32 *n_s
   }
 }
 
-__global__ void k_edge_classify(u32 E, const i64 *e_off, EdgeLists el) {
+__global__ __launch_bounds__(256) void k_edge_classify(u32 E, const i64 *e_off, EdgeLists el) {
+  __shared__ u32 s_app[3 * (256 / WAVE) + 3];
   const u32 e = blockIdx.x * blockDim.x + threadIdx.x;
   u64 len = 0;
   if (e < E) len = (u64)(e_off[e + 1] - e_off[e]);
   const int c = e >= E ? 3 : (len <= 64 ? 0 : (len <= LDS_CAP_U64 ? 1 : 2));
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    const u32 slot = wave_append(&el.cnt[k], c == k);
-    if (c == k) el.list[k][slot] = e;
-  }
+  const u32 slot = block_append<256, 3>(el.cnt, c, s_app);
+  if (c < 3) el.list[c][slot] = e;
   if (c == 2) atomicMax(&el.cnt[3], (u32)len);
 }
 

@@ -108,9 +108,12 @@ __global__ __launch_bounds__(TB) void k_cap(u32 nparts, const u64 *partials, u32
 // small table little, and four of its workgroups share a CU.  A node without
 // neighbours gets no candidate here.
 // (nodes lo .. hi - 1; recs must hold hi - lo records)
-__global__ void k_rate_classify(RateArgs A, u32 lo, u32 hi, NbLists nl, NodeRec *recs,
-                                NodeRec *big, u32 small_cap, u32 heavy_cap, u32 big_cap,
-                                u32 heavy_ech, u32 light_ech, u32 big_ech) {
+__global__ __launch_bounds__(256) void k_rate_classify(RateArgs A, u32 lo, u32 hi, NbLists nl,
+                                                       NodeRec *recs, NodeRec *big,
+                                                       u32 small_cap, u32 heavy_cap, u32 big_cap,
+                                                       u32 heavy_ech, u32 light_ech,
+                                                       u32 big_ech) {
+  __shared__ u32 s_app[4 * (256 / WAVE) + 4];
   const u32 n = lo + blockIdx.x * blockDim.x + threadIdx.x;
   u64 K = 0, deg = 0;
   if (n < hi) {
@@ -128,11 +131,8 @@ __global__ void k_rate_classify(RateArgs A, u32 lo, u32 hi, NbLists nl, NodeRec 
                 : K <= heavy_cap && deg <= big_ech    ? 1
                 : K > big_cap && deg <= heavy_ech     ? 3
                                                       : 2;
-  const u32 s0 = wave_append(&nl.cnt[0], c == 0);
-  if (c == 0) nl.list[0][s0] = n;
-  const u32 s1 = wave_append(&nl.cnt[1], c == 1);
-  const u32 s2 = wave_append(&nl.cnt[2], c == 2);
-  const u32 s3 = wave_append(&nl.cnt[3], c == 3);
+  const u32 slot = block_append<256, 4>(nl.cnt, c, s_app);
+  if (c == 0) nl.list[0][slot] = n;
   if (c >= 1 && c <= 3) {
     NodeRec r;
     r.n = n;
@@ -143,9 +143,9 @@ __global__ void k_rate_classify(RateArgs A, u32 lo, u32 hi, NbLists nl, NodeRec 
     r.deg = (u32)deg;
     r.nb0 = A.nb_off[n];
     r.pad0 = r.pad1 = r.pad2 = 0;
-    if (c == 1) recs[s1] = r;
-    else if (c == 2) big[s2] = r;
-    else recs[hi - lo - 1 - s3] = r;
+    if (c == 1) recs[slot] = r;
+    else if (c == 2) big[slot] = r;
+    else recs[hi - lo - 1 - slot] = r;
   }
 }
 
@@ -755,6 +755,11 @@ __device__ __forceinline__ NodeRec rec_from_lds(const u32 *w) {
 // thread 0, which alone takes the next item, around the other lanes, which
 // then re-enter the loop on the stale item and never leave.
 constexpr u32 HB = 2;  // heavy nodes per counter access
+// Light nodes per counter access: one while the light queue is short (a
+// batch would leave waves idle at its end), up to LB_MAX when it holds many
+// times more nodes than there are waves (each access is an atomic on one
+// shared word, which millions of light nodes would otherwise serialise).
+constexpr u32 LB_MAX = 8, LB_PER_WAVE = 16;
 static_assert(HB * 12 <= RB, "record words of a batch");
 
 // rec(j) is the record of item j < nh
@@ -810,15 +815,20 @@ __global__ __launch_bounds__(RB) void k_rate(RateArgs A, const u32 *light, const
     S.eta[i] = 0;
   }
   wave_sync();
+  const u32 q = nl / (gridDim.x * RW * LB_PER_WAVE);
+  const u32 lb = rfl(q < 1 ? 1 : q > LB_MAX ? LB_MAX : q);
   u32 lw = 0;
-  if (lane_id() == 0) lw = atomicAdd(&work[1], 1u);
+  if (lane_id() == 0) lw = atomicAdd(&work[1], lb);
   lw = __builtin_amdgcn_readfirstlane(__shfl(lw, 0, WAVE));
   for (;;) {
     if (lw >= nl) break;
     u32 nxt = 0;
-    if (lane_id() == 0) nxt = atomicAdd(&work[1], 1u);
-    rate_light<MP>(A, S, light[lw], cap, dmod, magic);
-    wave_sync();
+    if (lane_id() == 0) nxt = atomicAdd(&work[1], lb);
+    const u32 end = rfl(nl - lw < lb ? nl : lw + lb);
+    for (u32 j = lw; j < end; ++j) {
+      rate_light<MP>(A, S, light[j], cap, dmod, magic);
+      wave_sync();
+    }
     lw = __builtin_amdgcn_readfirstlane(__shfl(nxt, 0, WAVE));
   }
 }
