@@ -47,6 +47,71 @@ __global__ __launch_bounds__(256) void k_edge_classify(u32 E, const i64 *e_off, 
   if (c == 2) atomicMax(&el.cnt[3], (u32)len);
 }
 
+// Hyperedges of at most TINY pins (most nets of a netlist): one thread each,
+// the keys (gamma << 1 | is_source) sorted in registers by a 19-comparator
+// sorting network, then the groups written as the wave kernel writes them
+// (distinct sources first, then the distinct destinations).  The other
+// hyperedges of the wave class are passed on in rest[] (count *rest_cnt,
+// zeroed before) to k_econ_wave.  One thread per entry of list[0, *cnt).
+constexpr u32 TINY = 8;
+__device__ __forceinline__ void cswap(u64 &x, u64 &y) {
+  const u64 lo = x < y ? x : y, hi = x < y ? y : x;
+  x = lo;
+  y = hi;
+}
+__global__ __launch_bounds__(256) void k_econ_tiny(const i64 *e_off, const u32 *e_nsrc,
+                                                   const u32 *pins, const u32 *gamma, u32 *opins,
+                                                   u32 *olen, u32 *onsrc, const u32 *list,
+                                                   const u32 *cnt, u32 *rest, u32 *rest_cnt) {
+  __shared__ u32 s_app[256 / WAVE + 1];
+  const u32 total = *cnt;
+  const u32 i = blockIdx.x * blockDim.x + threadIdx.x;
+  u32 e = 0, len = 0, ns = 0;
+  i64 a = 0;
+  if (i < total) {
+    e = list[i];
+    a = e_off[e];
+    len = (u32)(e_off[e + 1] - a);
+    ns = e_nsrc[e];
+  }
+  const bool tiny = i < total && len <= TINY;
+  const int cls = (i < total && !tiny) ? 0 : 1;
+  const u32 slot = block_append<256, 1>(rest_cnt, cls, s_app);
+  if (cls == 0) rest[slot] = e;
+  if (!tiny) return;
+  u64 k[TINY];
+#pragma unroll
+  for (u32 j = 0; j < TINY; ++j)
+    k[j] = j < len ? ((u64)gamma[pins[a + j]] << 1) | (j < ns ? 1u : 0u) : ~0ull;
+  cswap(k[0], k[1]), cswap(k[2], k[3]), cswap(k[4], k[5]), cswap(k[6], k[7]);
+  cswap(k[0], k[2]), cswap(k[1], k[3]), cswap(k[4], k[6]), cswap(k[5], k[7]);
+  cswap(k[1], k[2]), cswap(k[5], k[6]), cswap(k[0], k[4]), cswap(k[3], k[7]);
+  cswap(k[1], k[5]), cswap(k[2], k[6]);
+  cswap(k[1], k[4]), cswap(k[3], k[6]);
+  cswap(k[2], k[4]), cswap(k[3], k[5]);
+  cswap(k[3], k[4]);
+  // a group of equal gamma is a source' iff its first (smallest) key is a source
+  u32 nsp = 0, ntot = 0;
+#pragma unroll
+  for (u32 j = 0; j < TINY; ++j) {
+    const bool first = k[j] != ~0ull && (j == 0 || (k[j - 1] >> 1) != (k[j] >> 1));
+    ntot += first ? 1u : 0u;
+    nsp += (first && (k[j] & 1)) ? 1u : 0u;
+  }
+  u32 *out = opins + a;
+  u32 ps = 0, pd = nsp;
+#pragma unroll
+  for (u32 j = 0; j < TINY; ++j) {
+    const bool first = k[j] != ~0ull && (j == 0 || (k[j - 1] >> 1) != (k[j] >> 1));
+    if (first) {
+      if (k[j] & 1) out[ps++] = (u32)(k[j] >> 1);
+      else out[pd++] = (u32)(k[j] >> 1);
+    }
+  }
+  olen[e] = ntot;
+  onsrc[e] = nsp;
+}
+
 // small hyperedges: one wave each, keys in registers
 __global__ __launch_bounds__(256) void k_econ_wave(const i64 *e_off, const u32 *e_nsrc,
                                                    const u32 *pins, const u32 *gamma, u32 *opins,
@@ -164,10 +229,17 @@ void launch_edge_classify(chp_ctx *c, u32 E, const i64 *e_off, EdgeLists el) {
 
 void launch_edge_contract(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
                           const u32 *gamma, u32 *opins, u32 *olen, u32 *onsrc, EdgeLists el,
-                          const u32 *host_cnt, u64 *scratch, u64 per_wg, u32 grid_big) {
-  if (host_cnt[0])
+                          const u32 *host_cnt, u64 *scratch, u64 per_wg, u32 grid_big,
+                          u32 *rest) {
+  if (host_cnt[0]) {
+    // el.cnt[5] counts the wave-class hyperedges above TINY pins (zeroed by
+    // the classification's fill)
+    CHP_LAUNCH(c, "econ_tiny", k_econ_tiny, grid_for(host_cnt[0], 256), 256, 0, e_off, e_nsrc,
+               pins, gamma, opins, olen, onsrc, (const u32 *)el.list[0],
+               (const u32 *)el.cnt + 0, rest, el.cnt + 5);
     CHP_LAUNCH(c, "econ_wave", k_econ_wave, waves_grid(host_cnt[0]), 256, 0, e_off, e_nsrc, pins,
-               gamma, opins, olen, onsrc, (const u32 *)el.list[0], (const u32 *)el.cnt + 0);
+               gamma, opins, olen, onsrc, (const u32 *)rest, (const u32 *)el.cnt + 5);
+  }
   if (host_cnt[1])
     CHP_LAUNCH(c, "econ_lds", (k_econ_lds<256, LDS_CAP_U64>),
                host_cnt[1] > 8192 ? 8192 : host_cnt[1], 256, 0, e_off, e_nsrc, pins, gamma, opins,

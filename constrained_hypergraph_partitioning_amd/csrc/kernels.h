@@ -226,7 +226,8 @@ void launch_gamma(chp_ctx *c, u32 N, const u32 *match, const i64 *rank, const u3
 void launch_edge_classify(chp_ctx *c, u32 E, const i64 *e_off, EdgeLists el);
 void launch_edge_contract(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
                           const u32 *gamma, u32 *opins, u32 *olen, u32 *onsrc, EdgeLists el,
-                          const u32 *host_cnt, u64 *scratch, u64 per_wg, u32 grid_big);
+                          const u32 *host_cnt, u64 *scratch, u64 per_wg, u32 grid_big,
+                          u32 *rest);
 void launch_pins_compact(chp_ctx *c, u32 E, const i64 *src_off, const u32 *src,
                          const i64 *dst_off, u32 *dst);
 
