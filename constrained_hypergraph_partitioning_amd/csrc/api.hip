@@ -321,6 +321,7 @@ void build_neighbors_core(chp_ctx *c, Scratch &s, Owned &own, chp_hgraph *g) {
 EdgeLists make_edge_lists(chp_ctx *c, Scratch &s, u32 E, const i64 *e_off, u32 hc[8]) {
   EdgeLists el;
   for (int k = 0; k < 3; ++k) el.list[k] = s.get<u32>(E);
+  el.list[3] = nullptr;
   el.cnt = s.get<u32>(8);
   launch_fill_u32(c, el.cnt, 8, 0);
   launch_edge_classify(c, E, e_off, el);
@@ -1194,6 +1195,7 @@ int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
     i64 *tmp = s.get<i64>(scan_tmp_words(N > E ? N : E));
     EdgeLists el;
     for (int k = 0; k < 3; ++k) el.list[k] = s.get<u32>(E);
+    el.list[3] = nullptr;
     el.cnt = s.get<u32>(8);
     EdgeLists il;
     il.cnt = s.get<u32>(8);
@@ -1241,7 +1243,7 @@ int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
     scan_u32_to_i64(c, olen, cg.e_off, E, tmp);
     // -- coarse incidence classes: in'(c) = in(a) u in(b), out' = (out(a) u out(b)) \ in'
     u32 *ibound = s.get<u32>(Nc), *icnt = s.get<u32>(Nc);
-    for (int k = 0; k < 3; ++k) il.list[k] = s.get<u32>(Nc);
+    for (int k = 0; k < 4; ++k) il.list[k] = s.get<u32>(Nc);
     launch_cinc_classify(c, Nc, rep_of, match, g->n_off, g->n_nin, ibound, cg.n_nin, icnt, il);
     i64 *iooff = s.get<i64>((u64)Nc + 1);
     i64 *tmp2 = s.get<i64>(scan_tmp_words(Nc));
@@ -1285,7 +1287,7 @@ int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
     u64 iper = 0;
     const u32 igb = grid_big_for(hi[2]);
     if (hi[2]) {
-      iper = 2ull * hi[3];
+      iper = 2ull * hi[4];  // the largest bound of the global class
       iscr = s.get<u64>(iper * igb);
     }
     launch_cinc_build(c, g->n_off, g->n_nin, g->n_inc, rep_of, match, iooff, iobuf, cg.n_nin,

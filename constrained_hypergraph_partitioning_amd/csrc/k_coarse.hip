@@ -25,13 +25,16 @@ namespace {
 // the compaction pass; a pair gets the bound |I(a)| + |I(b)| in the oversize
 // buffer and is merged by one sort of 64-bit keys (edge << 1 | is_out): in
 // each group of equal edge the first key tells whether it is inbound.
+// Classes by that bound: one wave (<= 64), a workgroup with an LDS table of
+// CINC_SMALL keys (8 KB, many per CU), one of LDS_CAP_U64 keys, global.
+constexpr u32 CINC_SMALL = 1024;
 __global__ __launch_bounds__(256) void k_cinc_classify(u32 Nc, const u32 *rep_of,
                                                        const u32 *match, const i64 *n_off,
                                                        const u32 *n_nin, u32 *bound,
                                                        u32 *cnt_in, u32 *cnt_tot, EdgeLists el) {
-  __shared__ u32 s_app[3 * (256 / WAVE) + 3];
+  __shared__ u32 s_app[4 * (256 / WAVE) + 4];
   const u32 c = blockIdx.x * blockDim.x + threadIdx.x;
-  int cls = 3;
+  int cls = 4;
   u64 w = 0;
   if (c < Nc) {
     const u32 a = rep_of[c], b = match[a];
@@ -43,12 +46,12 @@ __global__ __launch_bounds__(256) void k_cinc_classify(u32 Nc, const u32 *rep_of
     } else {
       w = da + (u64)(n_off[b + 1] - n_off[b]);
       bound[c] = (u32)w;
-      cls = w <= 64 ? 0 : (w <= LDS_CAP_U64 ? 1 : 2);
+      cls = w <= 64 ? 0 : w <= CINC_SMALL ? 1 : w <= LDS_CAP_U64 ? 3 : 2;
     }
   }
-  const u32 slot = block_append<256, 3>(el.cnt, cls, s_app);
-  if (cls < 3) el.list[cls][slot] = c;
-  if (cls == 2) atomicMax(&el.cnt[3], (u32)w);
+  const u32 slot = block_append<256, 4>(el.cnt, cls, s_app);
+  if (cls < 4) el.list[cls][slot] = c;
+  if (cls == 2) atomicMax(&el.cnt[4], (u32)w);
 }
 
 __device__ __forceinline__ u64 inc_key(const i64 *n_off, const u32 *n_nin, const u32 *n_inc,
@@ -354,10 +357,15 @@ void launch_cinc_build(chp_ctx *c, const i64 *n_off, const u32 *n_nin, const u32
                rep_of, match, ooff, obuf, cnt_in, cnt_tot, (const u32 *)el.list[0],
                (const u32 *)el.cnt + 0);
   if (host_cnt[1])
-    CHP_LAUNCH(c, "cinc_lds", (k_cinc_lds<256, LDS_CAP_U64>),
+    CHP_LAUNCH(c, "cinc_lds", (k_cinc_lds<256, CINC_SMALL>),
                host_cnt[1] > 8192 ? 8192 : host_cnt[1], 256, 0, n_off, n_nin, n_inc, rep_of,
                match, ooff, obuf, cnt_in, cnt_tot, (const u32 *)el.list[1],
                (const u32 *)el.cnt + 1);
+  if (host_cnt[3])
+    CHP_LAUNCH(c, "cinc_lds", (k_cinc_lds<256, LDS_CAP_U64>),
+               host_cnt[3] > 8192 ? 8192 : host_cnt[3], 256, 0, n_off, n_nin, n_inc, rep_of,
+               match, ooff, obuf, cnt_in, cnt_tot, (const u32 *)el.list[3],
+               (const u32 *)el.cnt + 3);
   if (host_cnt[2])
     CHP_LAUNCH(c, "cinc_global", (k_cinc_global<256, LDS_CAP_U64>), grid_big, 256, 0, n_off,
                n_nin, n_inc, rep_of, match, ooff, obuf, cnt_in, cnt_tot,

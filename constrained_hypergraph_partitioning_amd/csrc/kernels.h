@@ -30,7 +30,7 @@ struct NbLists {
 // Hyperedge work lists by |e|: <= 64 (wave), <= LDS_CAP_U64 (workgroup LDS),
 // longer (workgroup, global merge sort).  cnt[3] = longest class-2 edge.
 struct EdgeLists {
-  u32 *list[3];
+  u32 *list[4];  // list[3]: only the coarse incidence's larger LDS class
   u32 *cnt;  // device [8]
 };
 
