@@ -347,13 +347,25 @@ __global__ __launch_bounds__(BB) void k_nbm_bitmap(const i64 *nb_off, const u32 
       return fl ? (g << 1) | (u32)fl[j] : g;
     };
     u32 mn = NONE32, mx = 0;
-    for (u32 i = threadIdx.x; i < m; i += BB) {
-      const u32 k = key_at(i);
-      if (staged) S.stg[i] = k;
-      const u32 v = fl ? k >> 1 : k;
-      if (v != c) {
-        mn = v < mn ? v : mn;
-        mx = v > mx ? v : mx;
+    // KU keys per thread per pass, their loads issued together
+    constexpr u32 KU = 4;
+    for (u32 i0 = threadIdx.x; i0 < m; i0 += BB * KU) {
+      u32 kv[KU];
+#pragma unroll
+      for (u32 u = 0; u < KU; ++u) {
+        const u32 i = i0 + u * BB;
+        kv[u] = key_at(i < m ? i : 0);
+      }
+#pragma unroll
+      for (u32 u = 0; u < KU; ++u) {
+        const u32 i = i0 + u * BB;
+        if (i >= m) continue;
+        if (staged) S.stg[i] = kv[u];
+        const u32 v = fl ? kv[u] >> 1 : kv[u];
+        if (v != c) {
+          mn = v < mn ? v : mn;
+          mx = v > mx ? v : mx;
+        }
       }
     }
     mn = wg_min_u32(mn, S.redx);

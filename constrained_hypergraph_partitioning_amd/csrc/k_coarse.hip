@@ -243,28 +243,39 @@ __global__ __launch_bounds__(256) void k_nbm_wave(const i64 *nb_off, const u32 *
 // Split gamma(L) (L sorted, k ids) into the representatives' images, which
 // stay sorted (appended to R at *r), and the second members' images
 // (appended to Q at *q).  With flags (F, L's flags) the images are keys
-// gamma << 1 | flag, in the same order.
-template <int BLOCK>
+// gamma << 1 | flag, in the same order.  Ids are taken U per thread at a
+// time: all their loads and gathers are issued before the first scan, so a
+// batch costs one chain of memory round trips, not U of them.
+template <int BLOCK, int U>
 __device__ void split_reps(const u32 *L, const uint8_t *F, u32 k, const u32 *gamma,
                            const u32 *match, u32 *R, u32 &r, u32 *Q, u32 &q, u32 *s_red) {
-  for (u32 base = 0; base < k; base += BLOCK) {
-    const u32 i = base + threadIdx.x;
-    const bool valid = i < k;
-    u32 g = 0;
-    bool rep = false;
-    if (valid) {
-      const u32 m = L[i];
-      g = gamma[m];
-      if (F) g = (g << 1) | (u32)F[i];
-      rep = match[m] >= m;
+  for (u32 base = 0; base < k; base += BLOCK * U) {
+    u32 m[U], g[U], pm[U], fv[U];
+#pragma unroll
+    for (u32 j = 0; j < U; ++j) {  // branch-free: past the end reads entry 0
+      const u32 i = base + j * BLOCK + threadIdx.x;
+      m[j] = L[i < k ? i : 0];
+      fv[j] = F ? (u32)F[i < k ? i : 0] : 0u;
     }
-    u32 tr, tq;
-    const u32 orr = wg_excl_scan<BLOCK>((u32)(valid && rep), s_red, &tr);
-    const u32 oq = wg_excl_scan<BLOCK>((u32)(valid && !rep), s_red, &tq);
-    if (valid && rep) R[r + orr] = g;
-    if (valid && !rep) Q[q + oq] = g;
-    r += tr;
-    q += tq;
+#pragma unroll
+    for (u32 j = 0; j < U; ++j) {
+      g[j] = gamma[m[j]];
+      pm[j] = match[m[j]];
+    }
+#pragma unroll
+    for (u32 j = 0; j < U; ++j) {
+      const u32 i = base + j * BLOCK + threadIdx.x;
+      const bool valid = i < k;
+      const u32 key = F ? (g[j] << 1) | fv[j] : g[j];
+      const bool rep = pm[j] >= m[j];
+      u32 tr, tq;
+      const u32 orr = wg_excl_scan<BLOCK>((u32)(valid && rep), s_red, &tr);
+      const u32 oq = wg_excl_scan<BLOCK>((u32)(valid && !rep), s_red, &tq);
+      if (valid && rep) R[r + orr] = key;
+      if (valid && !rep) Q[q + oq] = key;
+      r += tr;
+      q += tq;
+    }
   }
 }
 
@@ -308,12 +319,12 @@ __global__ __launch_bounds__(BLOCK) void k_nbm_merge(const i64 *nb_off, const u3
     const u32 a = rep_of[c], b = match[a];
     u32 r1 = 0, r2 = 0, q = 0;
     const i64 a0 = nb_off[a];
-    split_reps<BLOCK>(nb + a0, fl ? fl + a0 : nullptr, (u32)(nb_off[a + 1] - a0), gamma, match,
-                      X, r1, Z, q, s_red);
+    split_reps<BLOCK, CAP / BLOCK>(nb + a0, fl ? fl + a0 : nullptr, (u32)(nb_off[a + 1] - a0),
+                                   gamma, match, X, r1, Z, q, s_red);
     if (b != a) {
       const i64 b0 = nb_off[b];
-      split_reps<BLOCK>(nb + b0, fl ? fl + b0 : nullptr, (u32)(nb_off[b + 1] - b0), gamma,
-                        match, X + r1, r2, Z, q, s_red);
+      split_reps<BLOCK, CAP / BLOCK>(nb + b0, fl ? fl + b0 : nullptr, (u32)(nb_off[b + 1] - b0),
+                                     gamma, match, X + r1, r2, Z, q, s_red);
     }
     if (q > 1) {
       const u32 p = next_pow2(q);
