@@ -1157,13 +1157,16 @@ int chp_pair_leftovers(chp_ctx *c, const chp_hgraph *g, const chp_params *prm,
     u64 *tmp = s.get<u64>(N);
     u32 *claim = s.get<u32>(N);
     u32 *choice = s.get<u32>(N);
-    u32 *cnt = s.get<u32>(2);  // gathered, pairs
-    launch_fills(c, {{cnt, 2, 0, false}, {claim, N, NONE32, false}});
-    launch_left_gather(c, N, target, match, g->n_size, keys, cnt);
+    u32 *cnt = s.get<u32>(4);  // gathered, pairs, smallest size, smallest |in|
+    launch_fills(c, {{cnt, 2, 0, false}, {cnt + 2, 2, NONE32, false}});
+    launch_left_gather(c, N, target, match, g->n_size, g->n_nin, keys, cnt);
     launch_check(c, "leftover gather");
-    u32 nl = 0;
-    read_many(c, {{&nl, cnt, sizeof nl}});
-    if (nl < 2) return;
+    u32 hc[4] = {0, 0, 0, 0};
+    read_many(c, {{hc, cnt, sizeof hc}});
+    const u32 nl = hc[0];
+    // no two gathered nodes fit together: nothing to pair
+    if (nl < 2 || 2 * (u64)hc[2] > prm->omega || 2 * (u64)hc[3] > (u64)prm->delta) return;
+    launch_fill_u32(c, claim, N, NONE32);
     const u64 *sorted = sort_keys_u64(c, keys, tmp, nl);
     launch_left_pair(c, nl, sorted, g->n_nin, prm->omega, prm->delta, LEFT_WINDOW, choice, claim,
                      match, cnt + 1);

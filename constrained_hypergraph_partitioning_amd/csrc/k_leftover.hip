@@ -14,13 +14,32 @@ namespace {
 
 constexpr int LB = 256;
 
-// keys (size << 32 | n) of the unmatched nodes without a target
-__global__ void k_left_gather(u32 N, const u32 *target, const u32 *match, const u32 *n_size,
-                              u64 *keys, u32 *cnt) {
+// keys (size << 32 | n) of the unmatched nodes without a target; cnt[2] and
+// cnt[3] (filled with NONE32 before) get their smallest size and smallest
+// inbound count: when twice either exceeds its limit, no two of them can pair
+__global__ __launch_bounds__(LB) void k_left_gather(u32 N, const u32 *target, const u32 *match,
+                                                    const u32 *n_size, const u32 *n_nin,
+                                                    u64 *keys, u32 *cnt) {
+  __shared__ u32 s_app[LB / WAVE + 1];
   const u32 n = blockIdx.x * blockDim.x + threadIdx.x;
   const bool take = n < N && target[n] == NONE32 && match[n] == n;
-  const u32 s = wave_append(cnt, take);
-  if (take) keys[s] = ((u64)n_size[n] << 32) | n;
+  const u32 s = block_append<LB, 1>(cnt, take ? 0 : 1, s_app);
+  u32 sz = NONE32, ni = NONE32;
+  if (take) {
+    sz = n_size[n];
+    ni = n_nin[n];
+    keys[s] = ((u64)sz << 32) | n;
+  }
+#pragma unroll
+  for (int d = WAVE / 2; d > 0; d >>= 1) {
+    const u32 o1 = __shfl_xor(sz, d, WAVE), o2 = __shfl_xor(ni, d, WAVE);
+    sz = o1 < sz ? o1 : sz;
+    ni = o2 < ni ? o2 : ni;
+  }
+  if (lane_id() == 0 && sz != NONE32) {
+    atomicMin(cnt + 2, sz);
+    atomicMin(cnt + 3, ni);
+  }
 }
 
 __global__ void k_left_choose(u32 nl, const u64 *keys, const u32 *n_nin, u64 omega, u32 delta,
@@ -72,10 +91,10 @@ __global__ void k_left_pair(u32 nl, const u64 *keys, const u32 *choice, const u3
 }  // namespace
 
 void launch_left_gather(chp_ctx *c, u32 N, const u32 *target, const u32 *match,
-                        const u32 *n_size, u64 *keys, u32 *cnt) {
+                        const u32 *n_size, const u32 *n_nin, u64 *keys, u32 *cnt) {
   if (N == 0) return;
   CHP_LAUNCH(c, "left_gather", k_left_gather, grid_for(N, LB), LB, 0, N, target, match, n_size,
-             keys, cnt);
+             n_nin, keys, cnt);
 }
 
 void launch_left_pair(chp_ctx *c, u32 nl, const u64 *keys, const u32 *n_nin, u64 omega,

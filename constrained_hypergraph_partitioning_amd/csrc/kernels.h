@@ -188,10 +188,12 @@ void launch_prefix(chp_ctx *c, u32 M, const i64 *ingain, const i64 *Pg, const i6
                    u32 *best_len, const u32 *seq, const u32 *move, u32 *rho);
 
 // Best-effort pairing of the unmatched nodes without a target: gather their
-// keys (size << 32 | id) into keys (cnt zeroed before), then, once sorted,
-// choose, claim (claim[N] filled with NONE before) and pair into match.
+// keys (size << 32 | id) into keys (cnt[0..1] zeroed and cnt[2..3] filled
+// with NONE before: the gathered nodes' smallest size and |in| go there),
+// then, once sorted, choose, claim (claim[N] filled with NONE before) and
+// pair into match.
 void launch_left_gather(chp_ctx *c, u32 N, const u32 *target, const u32 *match,
-                        const u32 *n_size, u64 *keys, u32 *cnt);
+                        const u32 *n_size, const u32 *n_nin, u64 *keys, u32 *cnt);
 void launch_left_pair(chp_ctx *c, u32 nl, const u64 *keys, const u32 *n_nin, u64 omega,
                       u32 delta, u32 window, u32 *choice, u32 *claim, u32 *match, u32 *npairs);
 
