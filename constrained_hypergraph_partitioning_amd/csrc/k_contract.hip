@@ -51,8 +51,10 @@ __global__ __launch_bounds__(256) void k_edge_classify(u32 E, const i64 *e_off, 
 // the keys (gamma << 1 | is_source) sorted in registers by a 19-comparator
 // sorting network, then the groups written as the wave kernel writes them
 // (distinct sources first, then the distinct destinations).  The other
-// hyperedges of the wave class are passed on in rest[] (count *rest_cnt,
-// zeroed before) to k_econ_wave.  One thread per entry of list[0, *cnt).
+// hyperedges of the wave class are passed on: those of at most 32 pins in
+// rest[0, rest_cnt[0]) to k_econ_half, the others in rest[T, T + rest_cnt[1])
+// to k_econ_wave, with T = *cnt; rest holds 2 T entries and rest_cnt[0..1]
+// are zeroed before.  One thread per entry of list[0, *cnt).
 constexpr u32 TINY = 8;
 __device__ __forceinline__ void cswap(u64 &x, u64 &y) {
   const u64 lo = x < y ? x : y, hi = x < y ? y : x;
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(256) void k_econ_tiny(const i64 *e_off, const u32 *
                                                    const u32 *pins, const u32 *gamma, u32 *opins,
                                                    u32 *olen, u32 *onsrc, const u32 *list,
                                                    const u32 *cnt, u32 *rest, u32 *rest_cnt) {
-  __shared__ u32 s_app[256 / WAVE + 1];
+  __shared__ u32 s_app[2 * (256 / WAVE) + 2];
   const u32 total = *cnt;
   const u32 i = blockIdx.x * blockDim.x + threadIdx.x;
   u32 e = 0, len = 0, ns = 0;
@@ -75,9 +77,10 @@ __global__ __launch_bounds__(256) void k_econ_tiny(const i64 *e_off, const u32 *
     ns = e_nsrc[e];
   }
   const bool tiny = i < total && len <= TINY;
-  const int cls = (i < total && !tiny) ? 0 : 1;
-  const u32 slot = block_append<256, 1>(rest_cnt, cls, s_app);
+  const int cls = (i >= total || tiny) ? 2 : len <= 32 ? 0 : 1;
+  const u32 slot = block_append<256, 2>(rest_cnt, cls, s_app);
   if (cls == 0) rest[slot] = e;
+  if (cls == 1) rest[total + slot] = e;
   if (!tiny) return;
   u64 k[TINY];
 #pragma unroll
@@ -110,6 +113,56 @@ __global__ __launch_bounds__(256) void k_econ_tiny(const i64 *e_off, const u32 *
   }
   olen[e] = ntot;
   onsrc[e] = nsp;
+}
+
+// Hyperedges of 9 to 32 pins: two per wave, one per half, each sorted by the
+// bitonic network over its 32 lanes and emitted within its half.
+__global__ __launch_bounds__(256) void k_econ_half(const i64 *e_off, const u32 *e_nsrc,
+                                                   const u32 *pins, const u32 *gamma, u32 *opins,
+                                                   u32 *olen, u32 *onsrc, const u32 *list,
+                                                   const u32 *cnt) {
+  const u32 total = *cnt;
+  const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
+  const u32 l = lane_id(), h = l >> 5, hl = l & 31;
+  const u64 half = 0xFFFFFFFFull << (32 * h);
+  const u64 lt = (1ull << l) - 1;
+  for (u32 w0 = 2 * (blockIdx.x * (blockDim.x / WAVE) + wave_id()); w0 < total;
+       w0 += 2 * nwaves) {
+    const u32 w = w0 + h;
+    u32 e = 0, len = 0, ns = 0;
+    i64 a = 0;
+    if (w < total) {
+      e = list[w];
+      a = e_off[e];
+      len = (u32)(e_off[e + 1] - a);
+      ns = e_nsrc[e];
+    }
+    u64 key = ~0ull;
+    if (hl < len) key = ((u64)gamma[pins[a + hl]] << 1) | (hl < ns ? 1u : 0u);
+    // bitonic sort within each 32-lane half, both halves ascending
+#pragma unroll
+    for (u32 k = 2; k <= 32; k <<= 1) {
+#pragma unroll
+      for (u32 j = k >> 1; j > 0; j >>= 1) {
+        const u64 o = __shfl_xor(key, j, WAVE);
+        const bool up = k == 32 || (hl & k) == 0;
+        const bool lower = (hl & j) == 0;
+        key = (lower == up) ? (key < o ? key : o) : (key < o ? o : key);
+      }
+    }
+    // groups within the half: sources first, then destinations
+    const u64 prev = __shfl_up(key, 1, WAVE);
+    const bool f = hl < len && (hl == 0 || (prev >> 1) != (key >> 1));
+    const bool ff = f && (key & 1);
+    const u64 fm = __ballot(ff) & half, om = __ballot(f && !ff) & half;
+    const u32 nf = (u32)__popcll(fm);
+    if (f)
+      opins[a + (ff ? (u32)__popcll(fm & lt) : nf + (u32)__popcll(om & lt))] = (u32)(key >> 1);
+    if (hl == 0 && w < total) {
+      olen[e] = nf + (u32)__popcll(om);
+      onsrc[e] = nf;
+    }
+  }
 }
 
 // small hyperedges: one wave each, keys in registers
@@ -232,13 +285,17 @@ void launch_edge_contract(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const
                           const u32 *host_cnt, u64 *scratch, u64 per_wg, u32 grid_big,
                           u32 *rest) {
   if (host_cnt[0]) {
-    // el.cnt[5] counts the wave-class hyperedges above TINY pins (zeroed by
-    // the classification's fill)
+    // el.cnt[5] and el.cnt[6] count the wave-class hyperedges of 9..32 and
+    // 33..64 pins (zeroed by the classification's fill)
     CHP_LAUNCH(c, "econ_tiny", k_econ_tiny, grid_for(host_cnt[0], 256), 256, 0, e_off, e_nsrc,
                pins, gamma, opins, olen, onsrc, (const u32 *)el.list[0],
                (const u32 *)el.cnt + 0, rest, el.cnt + 5);
+    CHP_LAUNCH(c, "econ_half", k_econ_half, waves_grid((host_cnt[0] + 1) / 2), 256, 0, e_off,
+               e_nsrc, pins, gamma, opins, olen, onsrc, (const u32 *)rest,
+               (const u32 *)el.cnt + 5);
     CHP_LAUNCH(c, "econ_wave", k_econ_wave, waves_grid(host_cnt[0]), 256, 0, e_off, e_nsrc, pins,
-               gamma, opins, olen, onsrc, (const u32 *)rest, (const u32 *)el.cnt + 5);
+               gamma, opins, olen, onsrc, (const u32 *)(rest + host_cnt[0]),
+               (const u32 *)el.cnt + 6);
   }
   if (host_cnt[1])
     CHP_LAUNCH(c, "econ_lds", (k_econ_lds<256, LDS_CAP_U64>),
