@@ -1240,7 +1240,9 @@ int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
     }
     u32 *opins = s.get<u32>(P);
     u32 *olen = s.get<u32>(E);
-    u32 *erest = s.get<u32>(he[0] ? 2ull * he[0] : 1);  // wave-class ones above the tiny size
+    // the wave class above the tiny size (twice its count), then the LDS class
+    // split by size (twice its count)
+    u32 *erest = s.get<u32>(2ull * he[0] + 2ull * he[1] + 1);
     launch_edge_contract(c, g->e_off, g->e_nsrc, g->e_pins, gamma, opins, olen, cg.e_nsrc, el, he,
                          escr, eper, egb, erest);
     scan_u32_to_i64(c, olen, cg.e_off, E, tmp);

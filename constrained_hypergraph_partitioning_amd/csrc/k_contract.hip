@@ -115,6 +115,28 @@ __global__ __launch_bounds__(256) void k_econ_tiny(const i64 *e_off, const u32 *
   onsrc[e] = nsp;
 }
 
+// The LDS class (65 .. LDS_CAP_U64 pins) split by size: those of at most
+// ECON_SMALL pins go to small[0, small_cnt[0]) for a workgroup with an 8 KB
+// table (many per CU), the others to big[0, small_cnt[1]) for the 64 KB one
+// (two per CU).  small_cnt[0..1] zeroed before; one thread per list entry.
+constexpr u32 ECON_SMALL = 1024;
+__global__ __launch_bounds__(256) void k_econ_split(const i64 *e_off, const u32 *list,
+                                                    const u32 *cnt, u32 *small, u32 *big,
+                                                    u32 *small_cnt) {
+  __shared__ u32 s_app[2 * (256 / WAVE) + 2];
+  const u32 total = *cnt;
+  const u32 i = blockIdx.x * blockDim.x + threadIdx.x;
+  u32 e = 0;
+  int cls = 2;
+  if (i < total) {
+    e = list[i];
+    cls = (u64)(e_off[e + 1] - e_off[e]) <= ECON_SMALL ? 0 : 1;
+  }
+  const u32 slot = block_append<256, 2>(small_cnt, cls, s_app);
+  if (cls == 0) small[slot] = e;
+  if (cls == 1) big[slot] = e;
+}
+
 // Hyperedges of 9 to 32 pins: two per wave, one per half, each sorted by the
 // bitonic network over its 32 lanes and emitted within its half.
 __global__ __launch_bounds__(256) void k_econ_half(const i64 *e_off, const u32 *e_nsrc,
@@ -285,22 +307,31 @@ void launch_edge_contract(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const
                           const u32 *host_cnt, u64 *scratch, u64 per_wg, u32 grid_big,
                           u32 *rest) {
   if (host_cnt[0]) {
-    // el.cnt[5] and el.cnt[6] count the wave-class hyperedges of 9..32 and
+    // el.cnt[4] and el.cnt[5] count the wave-class hyperedges of 9..32 and
     // 33..64 pins (zeroed by the classification's fill)
     CHP_LAUNCH(c, "econ_tiny", k_econ_tiny, grid_for(host_cnt[0], 256), 256, 0, e_off, e_nsrc,
                pins, gamma, opins, olen, onsrc, (const u32 *)el.list[0],
-               (const u32 *)el.cnt + 0, rest, el.cnt + 5);
+               (const u32 *)el.cnt + 0, rest, el.cnt + 4);
     CHP_LAUNCH(c, "econ_half", k_econ_half, waves_grid((host_cnt[0] + 1) / 2), 256, 0, e_off,
                e_nsrc, pins, gamma, opins, olen, onsrc, (const u32 *)rest,
-               (const u32 *)el.cnt + 5);
+               (const u32 *)el.cnt + 4);
     CHP_LAUNCH(c, "econ_wave", k_econ_wave, waves_grid(host_cnt[0]), 256, 0, e_off, e_nsrc, pins,
                gamma, opins, olen, onsrc, (const u32 *)(rest + host_cnt[0]),
-               (const u32 *)el.cnt + 6);
+               (const u32 *)el.cnt + 5);
   }
-  if (host_cnt[1])
+  if (host_cnt[1]) {
+    // el.cnt[6] and el.cnt[7] count the LDS-class hyperedges of at most
+    // ECON_SMALL pins and the larger ones (zeroed by the classification's fill)
+    u32 *small = rest + 2ull * host_cnt[0], *big = small + host_cnt[1];
+    CHP_LAUNCH(c, "econ_split", k_econ_split, grid_for(host_cnt[1], 256), 256, 0, e_off,
+               (const u32 *)el.list[1], (const u32 *)el.cnt + 1, small, big, el.cnt + 6);
+    CHP_LAUNCH(c, "econ_lds", (k_econ_lds<256, ECON_SMALL>),
+               host_cnt[1] > 8192 ? 8192 : host_cnt[1], 256, 0, e_off, e_nsrc, pins, gamma, opins,
+               olen, onsrc, (const u32 *)small, (const u32 *)el.cnt + 6);
     CHP_LAUNCH(c, "econ_lds", (k_econ_lds<256, LDS_CAP_U64>),
                host_cnt[1] > 8192 ? 8192 : host_cnt[1], 256, 0, e_off, e_nsrc, pins, gamma, opins,
-               olen, onsrc, (const u32 *)el.list[1], (const u32 *)el.cnt + 1);
+               olen, onsrc, (const u32 *)big, (const u32 *)el.cnt + 7);
+  }
   if (host_cnt[2])
     CHP_LAUNCH(c, "econ_global", (k_econ_global<256, LDS_CAP_U64>), grid_big, 256, 0, e_off,
                e_nsrc, pins, gamma, opins, olen, onsrc, (const u32 *)el.list[2],
