@@ -337,6 +337,9 @@ def main():
                      "avg_pass_ms": rate_ms / max(rate_launches, 1),
                      "alg_bytes_per_pass": rate_bytes_per_step / max(len(levels), 1),
                      "traffic": measured_traffic(spec.name)},
+        "per_level": {"nodes": [lv[0] for lv in levels], "pins": [lv[1] for lv in levels],
+                      "pairs": [lv[2] for lv in levels],
+                      "neighbour_entries": [lv[3] for lv in levels]},
         "kernel_ms_per_step": kern_ms,
         "kernel_sum_ms_per_step": level_ms,
         "dominant_kernel": dom[0],
