@@ -768,6 +768,7 @@ __device__ __forceinline__ void heavy_loop(const RateArgs &A, HeavySmem<C> &S, u
                                            u32 *s_rec, RecAt rec, u32 nh, u32 *work, u64 cap,
                                            u64 dmod, u64 magic) {
   const u32 tid = threadIdx.x;
+  if (nh == 0) return;  // uniform: no table to clear for an empty queue
   for (u32 i = tid; i < C::T; i += C::B) {
     S.key[i] = EMPTY;
     S.eta[i] = 0;
