@@ -904,11 +904,11 @@ int rate_top_and_match(chp_ctx *c, const chp_hgraph *g, const chp_params *prm, u
     u32 total = 0;
     for (u32 r = 0; r < pi; ++r) {
       launch_round_prep(c, N, pi, target, score_fx, match, tr, sr);
-      u32 np = 0;
-      match_proposals(c, s, N, tr, sr, ms, npairs, mr, &np);
-      if (np == 0) break;
+      u32 round_pairs = 0;
+      match_proposals(c, s, N, tr, sr, ms, npairs, mr, &round_pairs);
+      if (round_pairs == 0) break;
       launch_round_merge(c, N, mr, match);
-      total += np;
+      total += round_pairs;
       launch_fill_u32(c, c->flags, 1, 0);  // a long chain of this round is not the next one's
     }
     launch_check(c, "matching rounds");
