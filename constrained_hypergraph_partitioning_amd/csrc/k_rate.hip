@@ -799,7 +799,7 @@ __global__ __launch_bounds__(1024) void k_rate_big(RateArgs A, const NodeRec *bi
 }
 
 template <int MP>
-__global__ __launch_bounds__(RB) void k_rate(RateArgs A, const u32 *light, const NodeRec *recs,
+__global__ __launch_bounds__(RB, 4) void k_rate(RateArgs A, const u32 *light, const NodeRec *recs,
                                              u32 nrec, const u32 *cnt, u32 *work) {
   __shared__ RateSmem sm;
   __shared__ u32 s_item;
