@@ -1259,8 +1259,8 @@ int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
     i64 *tmp3 = nullptr;
     if (merge_nb) {
       nbound = s.get<u32>(Nc);
-      for (int k = 0; k < 3; ++k) nl.list[k] = s.get<u32>(Nc);
-      nl.list[3] = nl.list[4] = nullptr;
+      for (int k = 0; k < 4; ++k) nl.list[k] = s.get<u32>(Nc);
+      nl.list[4] = nullptr;
       launch_nbm_classify(c, Nc, rep_of, match, g->nb_off, nbound, nl);
       nooff = s.get<i64>((u64)Nc + 1);
       tmp3 = s.get<i64>(scan_tmp_words(Nc));

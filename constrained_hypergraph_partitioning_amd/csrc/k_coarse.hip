@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void k_cinc_compact(u32 Nc, const u32 *rep_of,
 __global__ __launch_bounds__(256) void k_nbm_classify(u32 Nc, const u32 *rep_of,
                                                       const u32 *match, const i64 *nb_off,
                                                       u32 *bound, NbLists nl) {
-  __shared__ u32 s_app[3 * (256 / WAVE) + 3];
+  __shared__ u32 s_app[4 * (256 / WAVE) + 4];
   const u32 c = blockIdx.x * blockDim.x + threadIdx.x;
   u64 w = 0;
   if (c < Nc) {
@@ -184,11 +184,12 @@ __global__ __launch_bounds__(256) void k_nbm_classify(u32 Nc, const u32 *rep_of,
     }
     bound[c] = (u32)w;
   }
-  // classes: one wave in registers (<= 64); a one-wave merge (<= 1024);
-  // the LDS bitmap (larger)
-  const int cls = (c >= Nc || w == 0) ? 3 : w <= 64 ? 0 : w <= 1024 ? 1 : 2;
-  const u32 slot = block_append<256, 3>(nl.cnt, cls, s_app);
-  if (cls < 3) nl.list[cls][slot] = c;
+  // classes: one wave in registers (<= 64); a one-wave merge with tables of
+  // 256 (class 3: few registers, many waves per CU) or 1024 ids; the LDS
+  // bitmap (larger)
+  const int cls = (c >= Nc || w == 0) ? 4 : w <= 64 ? 0 : w <= 256 ? 3 : w <= 1024 ? 1 : 2;
+  const u32 slot = block_append<256, 4>(nl.cnt, cls, s_app);
+  if (cls < 4) nl.list[cls][slot] = c;
 }
 
 // bound <= 64: one wave, keys in registers.  With flags (fl, the invalid-
@@ -405,6 +406,10 @@ void launch_nbm_build(chp_ctx *c, const i64 *nb_off, const u32 *nb, const uint8_
     CHP_LAUNCH(c, "nbm_wave", k_nbm_wave, waves_grid(host_cnt[0]), 256, 0, nb_off, nb, fl, gamma,
                match, rep_of, ooff, obuf, count, (const u32 *)nl.list[0],
                (const u32 *)nl.cnt + 0);
+  if (host_cnt[3])
+    CHP_LAUNCH(c, "nbm_merge", (k_nbm_merge<64, 256>),
+               host_cnt[3] > 65536 ? 65536 : host_cnt[3], 64, 0, nb_off, nb, fl, gamma, match,
+               rep_of, ooff, obuf, count, (const u32 *)nl.list[3], (const u32 *)nl.cnt + 3);
   if (host_cnt[1])
     CHP_LAUNCH(c, "nbm_merge", (k_nbm_merge<64, 1024>),
                host_cnt[1] > 65536 ? 65536 : host_cnt[1], 64, 0, nb_off, nb, fl, gamma, match,
