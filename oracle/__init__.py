@@ -49,7 +49,8 @@ def build(force: bool = False) -> str:
     """Compile the oracle with gcc (no GPU code involved)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-shared", "-fPIC", "-std=gnu11", "-o", tmp, _SRC])
+        subprocess.check_call(["gcc", "-O2", "-shared", "-fPIC", "-std=gnu11", "-pthread", "-o", tmp,
+                               _SRC])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -81,6 +82,8 @@ def _load():
             "or_moves": [E, P, P, P, u32, u64, i32, P, P],
             "or_match_dp": [u32, P, P, P, ctypes.POINTER(u64)],
             "or_rate_top": [E, P, P, P, P, u64, u64, u32, i32, u64, u32, P, P],
+            "or_rate_top_mt": [E, P, P, P, P, u64, u64, u32, i32, u64, u32, u32, u32, u32, P,
+                               P],
             "or_match_rounds": [u32, u32, P, P, i32, P, ctypes.POINTER(u64)],
             "or_refine": [E, P, P, P, P, u32, u64, u32, P, P, i32, P, P, P, P,
                           ctypes.POINTER(u32), ctypes.POINTER(u32),
@@ -210,32 +213,29 @@ def noise(seed: int, cap: int, n: int, m: int) -> int:
     return int(_load().or_noise(seed, cap, n, m))
 
 
-def rate(g: Graph, omega, delta, noise_on=True, seed=0, lo=0, hi=None, tc=None):
+def rate(g: Graph, omega, delta, noise_on=True, seed=0, lo=0, hi=None, tc=None, threads=1):
     """O5: target[N] (uint32, NONE if no valid neighbour) and score[N] (uint64).
-    Only nodes lo..hi-1 are rated; other entries stay NONE / 0."""
+    Only nodes lo..hi-1 are rated; other entries stay NONE / 0.  threads > 1
+    splits the node loop (the result does not depend on it)."""
+    t, s = rate_top(g, omega, delta, noise_on, seed, 1, lo, hi, tc, threads)
+    return t[0], s[0]
+
+
+def rate_top(g: Graph, omega, delta, noise_on=True, seed=0, pi=4, lo=0, hi=None, tc=None,
+             threads=1):
+    """Top-pi valid candidates of every node: (targets (pi, N) uint32, scores
+    (pi, N) uint64), row r the (r+1)-th best by (score desc, id asc).  Only
+    nodes lo..hi-1 are rated (the others stay NONE / 0), over `threads`
+    threads."""
     N = g.n_nodes
     hi = N if hi is None else hi
     t, cap = terms(g) if tc is None else tc
-    target = np.full(N, NONE, np.uint32)
-    score = np.zeros(N, np.uint64)
-    v = g.view()
-    _check(_load().or_rate(ctypes.byref(v), _p(g.n_off), _p(g.n_nin), _p(g.n_inc), _p(t), cap,
-                           omega, delta, 1 if noise_on else 0, seed, lo, hi, _p(target),
-                           _p(score)), "rate")
-    return target, score
-
-
-def rate_top(g: Graph, omega, delta, noise_on=True, seed=0, pi=4):
-    """Top-pi valid candidates of every node: (targets (pi, N) uint32, scores
-    (pi, N) uint64), row r the (r+1)-th best by (score desc, id asc)."""
-    N = g.n_nodes
-    t, cap = terms(g)
     target = np.full((pi, N), NONE, np.uint32)
     score = np.zeros((pi, N), np.uint64)
     v = g.view()
-    _check(_load().or_rate_top(ctypes.byref(v), _p(g.n_off), _p(g.n_nin), _p(g.n_inc), _p(t), cap,
-                               omega, delta, 1 if noise_on else 0, seed, pi, _p(target),
-                               _p(score)), "rate_top")
+    _check(_load().or_rate_top_mt(ctypes.byref(v), _p(g.n_off), _p(g.n_nin), _p(g.n_inc), _p(t),
+                                  cap, omega, delta, 1 if noise_on else 0, seed, lo, hi, pi,
+                                  threads, _p(target), _p(score)), "rate_top")
     return target, score
 
 

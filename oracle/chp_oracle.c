@@ -1,7 +1,7 @@
 /*
  * CPU ORACLE -- test infrastructure only.
  *
- * A plain, slow, single-threaded statement of what one constrained coarsening
+ * A plain, slow statement of what one constrained coarsening
  * level and the partition evaluation compute, written from the definitions in
  *   [P1] Ronzani & Silvano, "Hypergraph Partitioning on GPU with Distinct
  *        Incident Hyperedges and Size Constraints" (TPDS submission), and
@@ -18,6 +18,7 @@
  * stated next to each function; the same readings are listed in the design
  * notes of the repository.
  */
+#include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -289,88 +290,168 @@ static int cmp_cand(const void *x, const void *y) { /* eta descending, id ascend
 /* ------------------------------------------------------------------------ */
 /* The top pi valid candidates ([P1] Sec. V-D: the top-Pi valid neighbours of
  * each histogram) go to target[r * N + n], score[r * N + n] for r < pi, in the
- * order of Eq. 6 (score desc, id asc); missing ones are NONE / 0. */
-static int rate_top(const or_edges *g, const int64_t *n_off, const uint32_t *n_nin,
-                    const uint32_t *n_inc, const uint64_t *t, uint64_t cap, uint64_t omega,
-                    uint32_t delta, int noise_on, uint64_t seed, uint32_t lo, uint32_t hi,
-                    uint32_t pi, uint32_t *target, uint64_t *score) {
+ * order of Eq. 6 (score desc, id asc); missing ones are NONE / 0.
+ *
+ * Every node is rated on its own (its accumulator is cleared per node), so the
+ * node loop may be split over threads: each thread owns its accumulators and
+ * takes blocks of consecutive nodes from a shared counter.  The outputs do not
+ * depend on the number of threads; the error returned is that of the smallest
+ * node that fails. */
+typedef struct {
+  const or_edges *g;
+  const int64_t *n_off;
+  const uint32_t *n_nin, *n_inc;
+  const uint64_t *t;
+  uint64_t cap, omega, seed;
+  uint32_t delta, lo, hi, pi;
+  int noise_on;
+  uint32_t *target;
+  uint64_t *score;
+  uint32_t next;     /* next node to hand out (atomic) */
+  uint32_t bad_node; /* smallest failing node (atomic min), NONE if none */
+  int bad_rc;        /* its error (written under bad_mu) */
+  pthread_mutex_t bad_mu;
+} rate_job;
+
+#define RATE_BLOCK 16 /* nodes a thread takes at a time */
+
+/* Rate node n with the caller's accumulators (eta, inter, seen: one entry
+ * per node id; cl: one per node id).  Returns OR_OK or an error. */
+static int rate_node(const rate_job *J, uint32_t n, uint64_t *eta, uint32_t *inter,
+                     uint32_t *seen, cand *cl) {
+  const or_edges *g = J->g;
+  const int64_t *n_off = J->n_off;
+  const uint32_t *n_nin = J->n_nin, *n_inc = J->n_inc;
+  const uint64_t *t = J->t;
   uint32_t N = g->n_nodes;
-  if (hi > N || lo > hi) return OR_EINVAL;
+  /* overflow guard */
+  unsigned __int128 bound = J->cap;
+  for (int64_t j = n_off[n]; j < n_off[n + 1]; ++j) {
+    uint32_t e = n_inc[j];
+    if (g->e_off[e + 1] - g->e_off[e] >= 2) bound += t[e];
+  }
+  if (bound >= ((unsigned __int128)1 << 63)) return OR_EOVERFLOW;
+  uint32_t cnt = 0;
+  int64_t nin = n_nin[n];
+  for (int64_t j = n_off[n]; j < n_off[n + 1]; ++j) {
+    uint32_t e = n_inc[j];
+    int e_is_in = (j - n_off[n]) < nin; /* e in in(n) */
+    int64_t a = g->e_off[e], b = g->e_off[e + 1], d0 = a + g->e_nsrc[e];
+    for (int64_t i = a; i < b; ++i) {
+      uint32_t m = g->e_pins[i];
+      if (m == n) continue;
+      if (seen[m] != n) {
+        seen[m] = n;
+        eta[m] = 0;
+        inter[m] = 0;
+        cl[cnt++].id = m;
+      }
+      eta[m] += t[e];
+      if (e_is_in && i >= d0) inter[m]++; /* e in in(n) and m in dst(e) */
+    }
+  }
+  for (uint32_t c = 0; c < cnt; ++c) {
+    uint32_t m = cl[c].id;
+    if (J->noise_on) eta[m] += or_noise(J->seed, J->cap, n, m);
+    cl[c].eta = eta[m];
+  }
+  qsort(cl, cnt, sizeof(cand), cmp_cand);
+  for (uint32_t r = 0; r < J->pi; ++r) {
+    J->target[(size_t)r * N + n] = NONE;
+    J->score[(size_t)r * N + n] = 0;
+  }
+  const uint32_t *in_n = n_inc + n_off[n];
+  uint32_t got = 0;
+  for (uint32_t c = 0; c < cnt && got < J->pi; ++c) {
+    uint32_t m = cl[c].id;
+    if ((uint64_t)g->n_size[n] + g->n_size[m] > J->omega) continue;
+    uint64_t u = union_size(in_n, nin, n_inc + n_off[m], n_nin[m]);
+    if (u != (uint64_t)n_nin[n] + n_nin[m] - inter[m]) return OR_EINTERNAL;
+    if (u > J->delta) continue;
+    J->target[(size_t)got * N + n] = m;
+    J->score[(size_t)got * N + n] = cl[c].eta;
+    ++got;
+  }
+  return OR_OK;
+}
+
+static void *rate_worker(void *arg) {
+  rate_job *J = (rate_job *)arg;
+  uint32_t N = J->g->n_nodes;
   uint64_t *eta = (uint64_t *)calloc(N ? N : 1, sizeof(uint64_t));
   uint32_t *inter = (uint32_t *)calloc(N ? N : 1, sizeof(uint32_t));
   uint32_t *seen = (uint32_t *)malloc(sizeof(uint32_t) * (N ? N : 1));
   cand *cl = (cand *)malloc(sizeof(cand) * (N ? N : 1));
   if (!eta || !inter || !seen || !cl) {
+    pthread_mutex_lock(&J->bad_mu);
+    if (J->lo < __atomic_load_n(&J->bad_node, __ATOMIC_RELAXED) || !J->bad_rc) {
+      J->bad_node = J->lo;
+      J->bad_rc = OR_ENOMEM;
+    }
+    pthread_mutex_unlock(&J->bad_mu);
     free(eta), free(inter), free(seen), free(cl);
-    return OR_ENOMEM;
+    return NULL;
   }
   for (uint32_t i = 0; i < N; ++i) seen[i] = NONE;
-  int rc = OR_OK;
-  for (uint32_t n = lo; n < hi && rc == OR_OK; ++n) {
-    /* overflow guard */
-    unsigned __int128 bound = cap;
-    for (int64_t j = n_off[n]; j < n_off[n + 1]; ++j) {
-      uint32_t e = n_inc[j];
-      if (g->e_off[e + 1] - g->e_off[e] >= 2) bound += t[e];
-    }
-    if (bound >= ((unsigned __int128)1 << 63)) {
-      rc = OR_EOVERFLOW;
-      break;
-    }
-    uint32_t cnt = 0;
-    int64_t nin = n_nin[n];
-    for (int64_t j = n_off[n]; j < n_off[n + 1]; ++j) {
-      uint32_t e = n_inc[j];
-      int e_is_in = (j - n_off[n]) < nin; /* e in in(n) */
-      int64_t a = g->e_off[e], b = g->e_off[e + 1], d0 = a + g->e_nsrc[e];
-      for (int64_t i = a; i < b; ++i) {
-        uint32_t m = g->e_pins[i];
-        if (m == n) continue;
-        if (seen[m] != n) {
-          seen[m] = n;
-          eta[m] = 0;
-          inter[m] = 0;
-          cl[cnt++].id = m;
+  for (;;) {
+    uint32_t b = __atomic_fetch_add(&J->next, RATE_BLOCK, __ATOMIC_RELAXED);
+    if (b >= J->hi || b < J->lo) break;
+    uint32_t e = J->hi - b < RATE_BLOCK ? J->hi : b + RATE_BLOCK;
+    for (uint32_t n = b; n < e; ++n) {
+      if (n > __atomic_load_n(&J->bad_node, __ATOMIC_RELAXED)) break;
+      int rc = rate_node(J, n, eta, inter, seen, cl);
+      if (rc != OR_OK) {
+        pthread_mutex_lock(&J->bad_mu);
+        if (n < J->bad_node) {
+          J->bad_node = n;
+          J->bad_rc = rc;
         }
-        eta[m] += t[e];
-        if (e_is_in && i >= d0) inter[m]++; /* e in in(n) and m in dst(e) */
-      }
-    }
-    for (uint32_t c = 0; c < cnt; ++c) {
-      uint32_t m = cl[c].id;
-      if (noise_on) eta[m] += or_noise(seed, cap, n, m);
-      cl[c].eta = eta[m];
-    }
-    qsort(cl, cnt, sizeof(cand), cmp_cand);
-    for (uint32_t r = 0; r < pi; ++r) {
-      target[(size_t)r * N + n] = NONE;
-      score[(size_t)r * N + n] = 0;
-    }
-    const uint32_t *in_n = n_inc + n_off[n];
-    uint32_t got = 0;
-    for (uint32_t c = 0; c < cnt && got < pi; ++c) {
-      uint32_t m = cl[c].id;
-      if ((uint64_t)g->n_size[n] + g->n_size[m] > omega) continue;
-      uint64_t u = union_size(in_n, nin, n_inc + n_off[m], n_nin[m]);
-      if (u != (uint64_t)n_nin[n] + n_nin[m] - inter[m]) {
-        rc = OR_EINTERNAL;
+        pthread_mutex_unlock(&J->bad_mu);
         break;
       }
-      if (u > delta) continue;
-      target[(size_t)got * N + n] = m;
-      score[(size_t)got * N + n] = cl[c].eta;
-      ++got;
     }
   }
   free(eta), free(inter), free(seen), free(cl);
-  return rc;
+  return NULL;
+}
+
+static int rate_top(const or_edges *g, const int64_t *n_off, const uint32_t *n_nin,
+                    const uint32_t *n_inc, const uint64_t *t, uint64_t cap, uint64_t omega,
+                    uint32_t delta, int noise_on, uint64_t seed, uint32_t lo, uint32_t hi,
+                    uint32_t pi, uint32_t nthreads, uint32_t *target, uint64_t *score) {
+  uint32_t N = g->n_nodes;
+  if (hi > N || lo > hi || nthreads == 0) return OR_EINVAL;
+  rate_job J;
+  memset(&J, 0, sizeof J);
+  J.g = g, J.n_off = n_off, J.n_nin = n_nin, J.n_inc = n_inc, J.t = t;
+  J.cap = cap, J.omega = omega, J.seed = seed, J.delta = delta;
+  J.lo = lo, J.hi = hi, J.pi = pi, J.noise_on = noise_on;
+  J.target = target, J.score = score;
+  J.next = lo;
+  J.bad_node = NONE;
+  J.bad_rc = OR_OK;
+  pthread_mutex_init(&J.bad_mu, NULL);
+  uint32_t nt = nthreads;
+  if (nt > 256) nt = 256;
+  if (nt == 1) {
+    rate_worker(&J);
+  } else {
+    pthread_t th[256];
+    uint32_t started = 0;
+    for (; started < nt; ++started)
+      if (pthread_create(&th[started], NULL, rate_worker, &J) != 0) break;
+    if (started == 0) rate_worker(&J);
+    for (uint32_t i = 0; i < started; ++i) pthread_join(th[i], NULL);
+  }
+  pthread_mutex_destroy(&J.bad_mu);
+  return J.bad_rc;
 }
 
 int or_rate(const or_edges *g, const int64_t *n_off, const uint32_t *n_nin, const uint32_t *n_inc,
             const uint64_t *t, uint64_t cap, uint64_t omega, uint32_t delta, int noise_on,
             uint64_t seed, uint32_t lo, uint32_t hi, uint32_t *target, uint64_t *score) {
-  return rate_top(g, n_off, n_nin, n_inc, t, cap, omega, delta, noise_on, seed, lo, hi, 1, target,
-                  score);
+  return rate_top(g, n_off, n_nin, n_inc, t, cap, omega, delta, noise_on, seed, lo, hi, 1, 1,
+                  target, score);
 }
 
 int or_rate_top(const or_edges *g, const int64_t *n_off, const uint32_t *n_nin,
@@ -379,7 +460,18 @@ int or_rate_top(const or_edges *g, const int64_t *n_off, const uint32_t *n_nin,
                 uint64_t *score) {
   if (pi == 0) return OR_EINVAL;
   return rate_top(g, n_off, n_nin, n_inc, t, cap, omega, delta, noise_on, seed, 0, g->n_nodes, pi,
-                  target, score);
+                  1, target, score);
+}
+
+/* The same ratings with the node loop over nthreads threads, for nodes
+ * lo..hi-1 (other entries untouched). */
+int or_rate_top_mt(const or_edges *g, const int64_t *n_off, const uint32_t *n_nin,
+                   const uint32_t *n_inc, const uint64_t *t, uint64_t cap, uint64_t omega,
+                   uint32_t delta, int noise_on, uint64_t seed, uint32_t lo, uint32_t hi,
+                   uint32_t pi, uint32_t nthreads, uint32_t *target, uint64_t *score) {
+  if (pi == 0) return OR_EINVAL;
+  return rate_top(g, n_off, n_nin, n_inc, t, cap, omega, delta, noise_on, seed, lo, hi, pi,
+                  nthreads, target, score);
 }
 
 /* ------------------------------------------------------------------------ */

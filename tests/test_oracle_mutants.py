@@ -19,15 +19,15 @@ MUTANTS = {
     "target_tie_largest_id": ("return (a->id > b->id) - (a->id < b->id);",
                               "return (a->id < b->id) - (a->id > b->id);"),
     "inter_counts_out_edges": ("if (e_is_in && i >= d0) inter[m]++;", "if (i >= d0) inter[m]++;"),
-    "delta_off_by_one": ("if (u > delta) continue;", "if (u > (uint64_t)delta + 1) continue;"),
-    "omega_ignored": ("if ((uint64_t)g->n_size[n] + g->n_size[m] > omega) continue;",
-                      "if ((uint64_t)g->n_size[n] > omega) continue;"),
+    "delta_off_by_one": ("if (u > J->delta) continue;", "if (u > (uint64_t)J->delta + 1) continue;"),
+    "omega_ignored": ("if ((uint64_t)g->n_size[n] + g->n_size[m] > J->omega) continue;",
+                      "if ((uint64_t)g->n_size[n] > J->omega) continue;"),
     "term_wrong_size": ("t[e] = ((uint64_t)g->e_w[e] << FX_SHIFT) / sz;",
                         "t[e] = ((uint64_t)g->e_w[e] << FX_SHIFT) / (sz > 1 ? sz - 1 : 1);"),
     "noise_asymmetric": ("uint32_t a = n < m ? n : m, b = n < m ? m : n;",
                          "uint32_t a = n, b = m;"),
-    "noise_twice": ("if (noise_on) eta[m] += or_noise(seed, cap, n, m);",
-                    "if (noise_on) eta[m] += 2 * or_noise(seed, cap, n, m);"),
+    "noise_twice": ("if (J->noise_on) eta[m] += or_noise(J->seed, J->cap, n, m);",
+                    "if (J->noise_on) eta[m] += 2 * or_noise(J->seed, J->cap, n, m);"),
     "src_keeps_dst_dups": ("if (sorted_has(tmp, ud, sl[i])) continue;", ";"),
     "gamma_rank_by_max": ("uint32_t rep = n < match[n] ? n : match[n];\n    if (rep == n)",
                           "uint32_t rep = n > match[n] ? n : match[n];\n    if (rep == n)"),
@@ -90,8 +90,8 @@ MUTANTS = {
     "chain_window_of_source": ("const uint32_t d = move[n];\n      int64_t a = pstart[d]", "const uint32_t d = rho[n];\n      int64_t a = pstart[d]"),
     "chain_sorted_gain_ascending": ("if (a->gain != b->gain) return a->gain > b->gain ? -1 : 1;\n  return a->id < b->id ? -1 : (a->id > b->id ? 1 : 0);\n}\n\ntypedef struct {\n  int64_t total;",
                                     "if (a->gain != b->gain) return a->gain < b->gain ? -1 : 1;\n  return a->id < b->id ? -1 : (a->id > b->id ? 1 : 0);\n}\n\ntypedef struct {\n  int64_t total;"),
-    "top_pi_keeps_invalid": ("      if (u > delta) continue;\n      target[(size_t)got * N + n] = m;",
-                             "      target[(size_t)got * N + n] = m;"),
+    "top_pi_keeps_invalid": ("    if (u > J->delta) continue;\n    J->target[(size_t)got * N + n] = m;",
+                             "    J->target[(size_t)got * N + n] = m;"),
     "rounds_propose_to_matched": ("if (m != NONE && match[m] == m) {\n          tr[n] = m, sr[n] = score[(size_t)j * N + n];",
                                   "if (m != NONE) {\n          tr[n] = m, sr[n] = score[(size_t)j * N + n];"),
     "rounds_matched_keep_proposing": ("      if (match[n] != n) continue;\n      for (uint32_t j = 0; j < pi; ++j) {",

@@ -357,6 +357,40 @@ def test_determinism():
     assert np.array_equal(a.match, b.match) and np.array_equal(a.coarse.e_pins, b.coarse.e_pins)
 
 
+@pytest.mark.parametrize("threads", [2, 3, 8])
+def test_threaded_rating_is_the_single_threaded_one(threads):
+    """The rating's node loop split over threads (each node is rated on its
+    own accumulators) gives bit-identical top-pi lists for any thread count:
+    on a scaled ring, a scaled block graph, every tiny graph, and node
+    ranges; an overflowing node fails the same way."""
+    for cfg, nn in ((2, 20000), (5, 4096)):
+        spec = synth.config(cfg, n_nodes=nn)
+        g = load(synth.generate(spec), spec.omega, spec.delta, neighbors=False)
+        for pi in (1, 4):
+            a = oracle.rate_top(g, spec.omega, spec.delta, True, spec.seed, pi)
+            b = oracle.rate_top(g, spec.omega, spec.delta, True, spec.seed, pi, threads=threads)
+            assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        lo, hi = 1234, 3456
+        a = oracle.rate(g, spec.omega, spec.delta, True, spec.seed, lo=lo, hi=hi)
+        b = oracle.rate(g, spec.omega, spec.delta, True, spec.seed, lo=lo, hi=hi, threads=threads)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        assert np.all(b[0][:lo] == NONE) and np.all(b[0][hi:] == NONE)
+    for kw in tiny_cases()[::4]:
+        g = load(synth.tiny(**kw), neighbors=False)
+        a = oracle.rate_top(g, BIG, BIG, True, 3, 4)
+        b = oracle.rate_top(g, BIG, BIG, True, 3, 4, threads=threads)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    # node 5 sits in two 2-pin hyperedges of weight 2^24 - 1: its terms sum
+    # past 2^63
+    edges = [([i], [i + 1]) for i in range(4)] + [([5], [6]), ([7], [5])]
+    g = load(synth.from_lists(9, edges, [1, 1, 1, 1, (1 << 24) - 1, (1 << 24) - 1]),
+             neighbors=False)
+    for th in (1, threads):
+        with pytest.raises(oracle.OracleError) as ei:
+            oracle.rate(g, BIG, BIG, True, 0, threads=th)
+        assert ei.value.code == oracle.EOVERFLOW
+
+
 # ---------------------------------------------------------------- error paths
 def err_code(edges, n, w=None, sizes=None, omega=BIG, delta=BIG):
     h = synth.from_lists(n, edges, w, sizes)
