@@ -1,21 +1,26 @@
-"""Benchmark: constrained coarsening of a synthetic SNN-style hypergraph on
-one MI355X.
+"""Benchmark: one constrained coarsening level of a synthetic SNN-style
+hypergraph on one MI355X.
 
-One step = the whole hot path on the 100,000-node locality-biased ring
-workload (Poisson(32) fan-out clipped to [2,256], 80% of destinations within
-+-512 ring positions, weights 1..8, Omega 64, Delta 1024): build the canonical
-CSR, incidence and neighbourhoods; coarsen level by level (rate, handshake
-match, pair the nodes left without a partner, contract) until fewer than
-10,000 nodes remain or no pair forms; then
-evaluate the projected partition on the input graph.  The input edge CSR is
-resident in HBM before timing starts.
+Default workload: the 4,000,000-node block SNN graph (Poisson(250) fan-out
+clipped to [2,4096], 90% of destinations in the source's aligned block of
+65,536 ids, weights 1..8, Omega 1,024, Delta 16,384; about 1.0e9 pins), the
+largest configuration, whose description asks for one timed level of rate +
+match + contract.  `--workload 1..4` selects the smaller ones (the 100k-node
+ring, the layered 1M-node graph and the 2M-node VLSI netlist run their whole
+coarsening; the netlist evaluates its projected partition after every level).
+
+One step = the whole hot path: build the canonical CSR and incidence (and
+the neighbourhoods where they fit in 64 GB); coarsen level by level (rate,
+handshake match, pair the nodes left without a partner, contract) until the
+workload's stop rule; then evaluate the projected partition on the input
+graph.  The input edge CSR is resident in HBM before timing starts.
 
 value = pins processed by the coarsening levels (sum over levels of the
 level's pin count) per second of whole-step time (build and evaluation
 included).  The rating kernels' durations come from HIP events the library
 records on its stream during the timed steps (only those kernels are
-bracketed there); the per-kernel breakdown of every kernel comes from one
-more step, run after the timed ones with every launch bracketed.
+bracketed there); the per-kernel breakdown, the per-level times and the pin
+visits per level come from one more step run after the timed ones.
 """
 from __future__ import annotations
 
@@ -45,9 +50,17 @@ PI = 1
 # nodes (a stalled coarsening: each further level would cost a full pass for a
 # handful of pairs).
 MIN_PAIR_FRAC = 0.001
-RATE_SOURCE = os.path.join(ROOT, "constrained_hypergraph_partitioning_amd", "csrc", "k_rate.hip")
-COUNTERS_JSON = os.path.join(ROOT, "profiles", "rating_counters.json")
+# workloads whose projected partition is evaluated after every level (the
+# VLSI netlist's description asks for it), not only after the last
+EVAL_EVERY_LEVEL = {4}
+CSRC = os.path.join(ROOT, "constrained_hypergraph_partitioning_amd", "csrc")
+RATE_SOURCES = [os.path.join(CSRC, f) for f in ("k_rate.hip", "k_rate_inc.hip", "dev.h")]
 COPY_REF_MIB = 256
+# Pin visits per second the LDS can absorb: every visit is one 64-bit atomic
+# add into an LDS slot; 256 CUs x 2.4 GHz x 128 bytes of LDS per clock per CU
+# / 8 bytes per add (the derivation and its measurement are in the design
+# notes).
+LDS_VISIT_PEAK = 256 * 2.4e9 * 128 / 8
 
 
 def parse():
@@ -55,10 +68,15 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=2)
-    p.add_argument("--workload", type=int, default=2, help="workload index 1..5")
+    p.add_argument("--workload", type=int, default=5, help="workload index 1..5")
     p.add_argument("--nodes", type=int, default=None, help="shrink the workload (testing)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-nodes", type=int, default=None)
+    p.add_argument("--cpu-sample-nodes", type=int, default=None,
+                   help="workloads 1-4: rate a smaller instance; workload 5: nodes of the "
+                        "full graph the oracle rates")
+    p.add_argument("--cpu-threads", type=int, default=None,
+                   help="threads of the oracle's rating in the CPU baseline (default: "
+                        "min(16, cpus) for workload 5, 1 otherwise)")
     p.add_argument("--copy-ref-mib", type=int, default=0,
                    help="run one plain device copy of this size first (a reference for "
                         "scaling hardware byte counters)")
@@ -85,13 +103,23 @@ def parse():
                    help="keep invalid neighbours in the coarse neighbourhoods")
     p.add_argument("--counters", metavar="DIR", default=None,
                    help="no run: summarise the rocprofv3 FETCH_SIZE and WRITE_SIZE passes "
-                        "under DIR/fetch and DIR/write into " + COUNTERS_JSON)
+                        "under DIR/fetch and DIR/write into profiles/rating_counters_"
+                        "<workload>.json")
     return p.parse_args()
 
 
 def source_sha():
-    with open(RATE_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """Hash of the rating kernels' sources (counter summaries are valid for
+    them only)."""
+    h = hashlib.sha256()
+    for p in RATE_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counters_json(workload):
+    return os.path.join(ROOT, "profiles", "rating_counters_%s.json" % workload)
 
 
 def kernel_base(name):
@@ -118,8 +146,12 @@ def summarize_counters(d, workload):
     for name, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
         rows = [r for r in _counter_rows(os.path.join(d, name)) if r["Counter_Name"] == counter]
         ref = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
-        rate = [r for r in rows if kernel_base(r["Kernel_Name"]) in ("k_rate", "k_rate_big")]
-        passes = sum(1 for r in rate if kernel_base(r["Kernel_Name"]) == "k_rate")
+        rate = [r for r in rows
+                if kernel_base(r["Kernel_Name"]) in ("k_rate", "k_rate_big", "k_rate_inc")]
+        # one rating pass per level: a k_rate launch, or k_rate_inc where
+        # every node of the level is rated from the incidence
+        passes = max(sum(1 for r in rate if kernel_base(r["Kernel_Name"]) == k)
+                     for k in ("k_rate", "k_rate_inc"))
         if not ref or not passes:
             raise SystemExit("%s: no reference copy or no rating dispatch found" % name)
         kib = sum(float(r["Counter_Value"]) for r in rate)
@@ -128,8 +160,9 @@ def summarize_counters(d, workload):
                      "copy_ref_kib": max(ref), "scale": scale}
     out["traffic_bytes_per_pass"] = 1024 * (out["fetch"]["kib_per_pass"] * out["fetch"]["scale"] +
                                             out["write"]["kib_per_pass"] * out["write"]["scale"])
-    os.makedirs(os.path.dirname(COUNTERS_JSON), exist_ok=True)
-    with open(COUNTERS_JSON, "w") as f:
+    path = counters_json(workload)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 
@@ -138,7 +171,7 @@ def measured_traffic(workload):
     """Bytes per rating pass from the committed counter summary, if it was
     taken on this workload with the current rating source; else None."""
     try:
-        with open(COUNTERS_JSON) as f:
+        with open(counters_json(workload)) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
@@ -152,13 +185,17 @@ def measured_traffic(workload):
 NB_BYTES_MAX = 64 << 30
 
 
-def run_step(chp, ctx, dev_edges, spec, rho_buf, with_nb=True):
-    """One pass of the hot path; returns per-level pin counts and the summary."""
+def run_step(chp, ctx, dev_edges, spec, rho_buf, with_nb=True, eval_every=False, detail=False):
+    """One pass of the hot path.  Returns the per-level records (nodes, pins,
+    pairs, neighbour entries, and with detail: ms and pin visits), the final
+    evaluation summary and, with eval_every, the connectivity of the projected
+    partition after each level."""
     import torch
     g0 = ctx.build_incidence(*dev_edges, spec.omega, spec.delta, with_nb)
     total_size = int(spec_total_size(dev_edges))
     floor_nodes = -(-total_size // spec.omega)
     levels = []
+    level_conn = []
     g = g0
     rho = None
     for lvl in range(spec.levels):
@@ -166,6 +203,9 @@ def run_step(chp, ctx, dev_edges, spec, rho_buf, with_nb=True):
             break
         if g.n_nodes <= floor_nodes:
             break
+        if detail:
+            torch.cuda.synchronize()
+            t_l = time.perf_counter()
         flags = ctx.new_flags(g) if PURGE and with_nb else None
         if PI > 1:
             tl, _, match, npairs = ctx.rate_top_and_match(g, PI, spec.omega, spec.delta, True,
@@ -177,11 +217,22 @@ def run_step(chp, ctx, dev_edges, spec, rho_buf, with_nb=True):
         if LEFTOVERS:
             npairs += ctx.pair_leftovers(g, tgt, match, spec.omega, spec.delta)
         nb_total = g.nb_total if with_nb else ctx.last_rate_stats()[0]
-        levels.append((g.n_nodes, g.n_pins, npairs, nb_total))
+        rec = [g.n_nodes, g.n_pins, npairs, nb_total]
+        levels.append(rec)
         if npairs == 0:
+            if detail:
+                torch.cuda.synchronize()
+                rec += [(time.perf_counter() - t_l) * 1e3, level_visits(g)]
             break
         gamma, cg = ctx.contract(g, match, with_nb, flags=flags)
         rho = gamma.long() if rho is None else gamma.long()[rho]
+        if detail:
+            torch.cuda.synchronize()
+            rec += [(time.perf_counter() - t_l) * 1e3, level_visits(g)]
+        if eval_every:
+            rho_buf.copy_(rho.to(torch.int32))
+            _, _, s_l = ctx.evaluate_partition(g0, rho_buf, cg.n_nodes, spec.omega, spec.delta)
+            level_conn.append(int(s_l[0]))
         stalled = npairs < MIN_PAIR_FRAC * g.n_nodes
         if g is not g0:
             g.free()
@@ -196,7 +247,15 @@ def run_step(chp, ctx, dev_edges, spec, rho_buf, with_nb=True):
     if g is not g0:
         g.free()
     g0.free()
-    return levels, summ
+    return levels, summ, level_conn
+
+
+def level_visits(g):
+    """Pin visits of a rating pass over g: every node visits every pin of
+    every hyperedge it belongs to, so sum over hyperedges of |e|^2."""
+    import torch
+    sz = torch.diff(g.tensor("e_off")).double()
+    return float((sz * sz).sum().item())
 
 
 _size_cache = {}
@@ -209,22 +268,59 @@ def spec_total_size(dev_edges):
     return _size_cache[key]
 
 
-def cpu_baseline(h, spec, workload, sample_nodes):
-    """The CPU oracle, single-threaded, on level 0 of the same workload (or a
-    smaller instance of it): build + rate + match + contract."""
+def cpu_info():
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return os.cpu_count(), model
+
+
+def cpu_baseline(h, spec, workload, sample_nodes, threads):
+    """The CPU oracle on a bounded sample of the same workload.
+    Workloads 1-4: level 0 (build incidence + neighbours, rate, match,
+    contract) of the workload or of a smaller instance, single-threaded.
+    Workload 5: the oracle builds the full graph's incidence (not timed), then
+    rates nodes 0..R-1 (the level's dominant step) over `threads` threads; the
+    value scales that rate to the level's pins (P * R / N per second)."""
     import oracle
     import synth
+    nproc, model = cpu_info()
+    if workload == 5:
+        R = sample_nodes or 65536
+        threads = threads or min(16, nproc or 1)
+        g = oracle.build_incidence(h.e_off, h.e_nsrc, h.e_pins, h.e_w, h.n_size, spec.omega,
+                                   spec.delta, False)
+        tc = oracle.terms(g)
+        t0 = time.perf_counter()
+        oracle.rate(g, spec.omega, spec.delta, True, spec.seed, lo=0, hi=R, tc=tc,
+                    threads=threads)
+        dt = time.perf_counter() - t0
+        del g
+        return {"value": h.n_pins * (R / h.n_nodes) / dt, "unit": "pins/s", "cores": threads,
+                "kind": "oracle", "nproc": nproc, "cpu_model": model,
+                "sample": "oracle rating of nodes 0..%d of the full %s graph (%d nodes, %d "
+                          "pins; the level's dominant step, incidence built beforehand, not "
+                          "timed): %.1f s over %d threads, scaled to the level as P*R/N per "
+                          "second" % (R - 1, h.spec.name, h.n_nodes, h.n_pins, dt, threads)}
+    threads = threads or 1
     if sample_nodes and sample_nodes < h.n_nodes:
         h = synth.generate(synth.config(workload, n_nodes=sample_nodes))
     t0 = time.perf_counter()
     g = oracle.build_incidence(h.e_off, h.e_nsrc, h.e_pins, h.e_w, h.n_size, spec.omega,
                                spec.delta)
-    lv = oracle.level(g, spec.omega, spec.delta, True, spec.seed)
+    oracle.level(g, spec.omega, spec.delta, True, spec.seed, threads=threads)
     dt = time.perf_counter() - t0
-    return {"value": h.n_pins / dt, "unit": "pins/s", "cores": 1, "kind": "oracle",
+    return {"value": h.n_pins / dt, "unit": "pins/s", "cores": threads, "kind": "oracle",
+            "nproc": nproc, "cpu_model": model,
             "sample": "level 0 (build incidence+neighbours, rate, match, contract) of %s: "
-                      "%d nodes, %d pins, %.1f s single-threaded"
-                      % (h.spec.name, h.n_nodes, h.n_pins, dt)}
+                      "%d nodes, %d pins, %.1f s, rating over %d thread(s)"
+                      % (h.spec.name, h.n_nodes, h.n_pins, dt, threads)}
 
 
 def main():
@@ -263,9 +359,10 @@ def main():
 
     sz = np.diff(h.e_off).astype(np.float64)
     with_nb = float((sz * (sz - 1)).sum()) * 4 <= NB_BYTES_MAX and not args.no_neighbour_lists
+    eval_every = args.workload in EVAL_EVERY_LEVEL
     for i in range(args.warmup):
         t_w = time.perf_counter()
-        run_step(chp, ctx, dev_edges, spec, rho_buf, with_nb)
+        run_step(chp, ctx, dev_edges, spec, rho_buf, with_nb, eval_every)
         torch.cuda.synchronize()
         print("[bench] warmup step %d: %.3f s" % (i, time.perf_counter() - t_w), file=sys.stderr,
               flush=True)
@@ -280,28 +377,35 @@ def main():
     pins = 0
     levels = None
     for i in range(args.steps):
-        levels, summ = run_step(chp, ctx, dev_edges, spec, rho_buf, with_nb)
+        levels, summ, level_conn = run_step(chp, ctx, dev_edges, spec, rho_buf, with_nb,
+                                            eval_every)
         pins += sum(lv[1] for lv in levels)
         if args.progress:
             print("[bench] step %d queued" % i, file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     timings = ctx.timings()
-    # one more step, untimed, with every kernel timed: the per-kernel breakdown
+    # one more step, untimed, with every kernel timed: the per-kernel
+    # breakdown; then one with a synchronisation around each level: the
+    # per-level times and pin visits
     ctx.reset_timings()
     ctx.set_timing_filter(None)
-    run_step(chp, ctx, dev_edges, spec, rho_buf, with_nb)
+    run_step(chp, ctx, dev_edges, spec, rho_buf, with_nb, eval_every)
     torch.cuda.synchronize()
     all_timings = ctx.timings()
     ctx.set_timing(False)
+    detail, _, _ = run_step(chp, ctx, dev_edges, spec, rho_buf, with_nb, eval_every, True)
+    torch.cuda.synchronize()
 
     # The rating pass (per level one launch of "rate_big", the nodes whose
     # neighbourhood exceeds one window of the small table, and one of
     # "rate", all other nodes) and its algorithmic bytes: each array it reads
     # or writes counted once per level.
     dom = max(all_timings.items(), key=lambda kv: kv[1][1])
-    rate_launches = timings.get("rate", (0, 0.0))[0]
+    passes = len(levels) * args.steps  # one rating pass per level
     rate_ms = sum(timings.get(k, (0, 0.0))[1] for k in RATE_KERNELS)
+    visits_per_step = sum(lv[5] for lv in detail)
+    visits_s = visits_per_step * args.steps / (rate_ms / 1e3) if rate_ms else 0.0
     level_bytes = rate_level_bytes(levels, h, spec)
     rate_bytes_per_step = sum(level_bytes)
     achieved = rate_bytes_per_step * args.steps / (rate_ms / 1e3) / 1e9 if rate_ms else 0.0
@@ -334,24 +438,33 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "rate_big+rate+rate_inc (the rating pass)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "avg_pass_ms": rate_ms / max(rate_launches, 1),
+                     "avg_pass_ms": rate_ms / max(passes, 1),
                      "alg_bytes_per_pass": rate_bytes_per_step / max(len(levels), 1),
                      "traffic": measured_traffic(spec.name)},
+        "roofline_visits": {"bound": "lds", "kernel": "rate_big+rate+rate_inc (the rating pass)",
+                            "achieved": visits_s, "peak": LDS_VISIT_PEAK, "unit": "visits/s",
+                            "frac": visits_s / LDS_VISIT_PEAK,
+                            "visits_per_pass": visits_per_step / max(len(levels), 1)},
         "per_level": {"nodes": [lv[0] for lv in levels], "pins": [lv[1] for lv in levels],
                       "pairs": [lv[2] for lv in levels],
-                      "neighbour_entries": [lv[3] for lv in levels]},
+                      "neighbour_entries": [lv[3] for lv in levels],
+                      "visits": [lv[5] for lv in detail],
+                      "ms": [round(lv[4], 3) for lv in detail]},
         "kernel_ms_per_step": kern_ms,
         "kernel_sum_ms_per_step": level_ms,
         "dominant_kernel": dom[0],
         "cpu_baseline": None,
     }
+    if eval_every:
+        out["per_level"]["projected_connectivity"] = level_conn
     if args.moves:
         out["moves"] = time_moves(ctx, dev_edges, spec, rho_buf, out["config"]["final_nodes"], h)
     if args.refine:
         out["refine"] = time_refine(ctx, dev_edges, spec, rho_buf, out["config"]["final_nodes"],
                                     h, args.refine)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(h, spec, args.workload, args.cpu_sample_nodes)
+        out["cpu_baseline"] = cpu_baseline(h, spec, args.workload, args.cpu_sample_nodes,
+                                           args.cpu_threads)
     print(json.dumps(out))
 
 

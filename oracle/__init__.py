@@ -420,20 +420,21 @@ class Level:
 
 
 def level(g: Graph, omega, delta, noise_on=True, seed=0, build_neighbors=True,
-          purge_invalid=False, leftovers=False, optimal=False, pi=1) -> Level:
+          purge_invalid=False, leftovers=False, optimal=False, pi=1, threads=1) -> Level:
     """One coarsening level: rate, match, contract.  With purge_invalid the
     neighbour flags of g are computed (Level.flags) and the coarse
     neighbourhoods are purged of flagged neighbours (O10); with leftovers the
     unmatched nodes without a target are paired best-effort (O11); with
     optimal the matching is the exact one of O13 instead of the handshake;
     with pi > 1 the matching takes pi rounds over the top-pi candidates (O16)
-    and target/score are the best candidates."""
+    and target/score are the best candidates.  threads splits the rating's
+    node loop (the result does not depend on it)."""
     if pi > 1:
-        tl, sl = rate_top(g, omega, delta, noise_on, seed, pi)
+        tl, sl = rate_top(g, omega, delta, noise_on, seed, pi, threads=threads)
         target, score = tl[0].copy(), sl[0].copy()
         m, npairs = match_rounds(tl, sl, optimal)
     else:
-        target, score = rate(g, omega, delta, noise_on, seed)
+        target, score = rate(g, omega, delta, noise_on, seed, threads=threads)
         m, npairs = match_dp(target, score) if optimal else match(target, score)
     if leftovers:
         m, extra = pair_leftovers(target, m, g.n_size, g.n_nin, omega, delta)
@@ -448,11 +449,15 @@ def level(g: Graph, omega, delta, noise_on=True, seed=0, build_neighbors=True,
 
 
 def coarsen(g: Graph, omega, delta, target_nodes=0, max_levels=64, noise_on=True, seed=0,
-            purge_invalid=False, leftovers=False):
+            purge_invalid=False, leftovers=False, min_pair_frac=0.0, on_level=None,
+            threads=1, build_neighbors=True):
     """O9: the level loop of [P1] Sec. III.  Stops at the first of: fewer than
     target_nodes nodes; at most ceil(sum size / Omega) nodes (the lowest valid
-    count); a level with no pair; max_levels levels.  Returns the list of Levels and the projection
-    rho = gamma_l o ... o gamma_1 onto the finest nodes."""
+    count); a level with no pair; max_levels levels; after a level that pairs
+    fewer than min_pair_frac of its nodes (a stalled coarsening: 0 = never).
+    on_level(index, fine graph, Level, rho) is called after each level.
+    Returns the list of Levels and the projection rho = gamma_l o ... o
+    gamma_1 onto the finest nodes."""
     levels = []
     rho = np.arange(g.n_nodes, dtype=np.uint32)
     floor_nodes = -(-int(g.n_size.astype(np.uint64).sum()) // omega)
@@ -460,11 +465,18 @@ def coarsen(g: Graph, omega, delta, target_nodes=0, max_levels=64, noise_on=True
     for _ in range(max_levels):
         if cur.n_nodes < target_nodes or cur.n_nodes <= floor_nodes:
             break
-        lv = level(cur, omega, delta, noise_on, seed, purge_invalid=purge_invalid,
-                   leftovers=leftovers)
+        lv = level(cur, omega, delta, noise_on, seed, build_neighbors=build_neighbors,
+                   purge_invalid=purge_invalid, leftovers=leftovers, threads=threads)
         levels.append(lv)
         if lv.n_pairs == 0:
+            if on_level:
+                on_level(len(levels) - 1, cur, lv, rho)
             break
         rho = lv.gamma[rho]
+        if on_level:
+            on_level(len(levels) - 1, cur, lv, rho)
+        stalled = lv.n_pairs < min_pair_frac * cur.n_nodes
         cur = lv.coarse
+        if stalled:
+            break
     return levels, rho, cur
