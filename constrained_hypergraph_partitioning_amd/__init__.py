@@ -33,7 +33,8 @@ EXPORTS = ["chp_create", "chp_destroy", "chp_last_error", "chp_build_incidence",
            "chp_set_timing", "chp_get_timings", "chp_reset_timings", "chp_set_batch_entries",
            "chp_last_rate_stats", "chp_set_incidence_rating", "chp_pair_leftovers",
            "chp_propose_moves", "chp_set_matching", "chp_set_timing_filter",
-           "chp_refine_moves", "chp_set_move_order", "chp_rate_top_and_match"]
+           "chp_refine_moves", "chp_set_move_order", "chp_rate_top_and_match",
+           "chp_evaluate_partition_noalloc"]
 
 
 class ChpError(RuntimeError):
@@ -136,6 +137,8 @@ def load_library(path: str = LIB_PATH):
                                            ctypes.POINTER(Params), P, P,
                                            ctypes.POINTER(ctypes.c_uint64)]
     lib.chp_evaluate_partition.restype = I
+    lib.chp_evaluate_partition_noalloc.argtypes = lib.chp_evaluate_partition.argtypes
+    lib.chp_evaluate_partition_noalloc.restype = I
     lib.chp_hgraph_free.argtypes = [P, ctypes.POINTER(HGraphC)]
     lib.chp_hgraph_free.restype = None
     lib.chp_set_timing.argtypes = [P, I]
@@ -251,8 +254,10 @@ class Context:
         torch.cuda.set_device(self.device)
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         self._blocks = {}
+        self.n_allocs = 0  # calls of the allocation callback so far
 
         def _alloc(nbytes, user):
+            self.n_allocs += 1
             try:
                 with torch.cuda.stream(self.stream):
                     t = torch.empty(int(nbytes), dtype=torch.uint8, device=self.device)
@@ -443,6 +448,17 @@ class Context:
                                                     ctypes.byref(prm), _ptr(part_size),
                                                     _ptr(part_inb), summ), "evaluate_partition")
         return part_size[:k], part_inb[:k], np.array(list(summ), dtype=np.uint64)
+
+    def evaluate_partition_noalloc(self, g: HGraph, rho, k, omega, delta, part_size, part_inb):
+        """chp_evaluate_partition_noalloc: the evaluation into caller-owned
+        part_size (int64, >= k) and part_inb (int32, >= k), with the
+        library's fixed scratch (no device allocation); returns the summary."""
+        summ = (ctypes.c_uint64 * 8)()
+        prm = Params(omega, delta, 0, 0)
+        self._check(self.lib.chp_evaluate_partition_noalloc(
+            self.h, ctypes.byref(g.c), _ptr(rho), k, ctypes.byref(prm), _ptr(part_size),
+            _ptr(part_inb), summ), "evaluate_partition_noalloc")
+        return np.array(list(summ), dtype=np.uint64)
 
     def set_batch_entries(self, entries=0):
         """Neighbour entries per rating batch for graphs without neighbours

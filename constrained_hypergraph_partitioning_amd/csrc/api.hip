@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 
 #include <vector>
 
@@ -68,8 +69,15 @@ struct Scratch {
   size_t mark;
   size_t need;
   std::vector<void *> own;
+  // fixed mode: every request is carved from [fixed, fixed + fixed_cap) and
+  // nothing is ever allocated; a request that does not fit is an error
+  char *fixed = nullptr;
+  size_t fixed_cap = 0, fixed_top = 0;
   explicit Scratch(chp_ctx *cc) : c(cc), mark(cc->arena_top), need(cc->arena_top) {}
+  Scratch(chp_ctx *cc, char *base, size_t cap)
+      : c(cc), mark(cc->arena_top), need(cc->arena_top), fixed(base), fixed_cap(cap) {}
   ~Scratch() {
+    if (fixed) return;
     for (void *p : own) ctx_free(c, p);
     c->arena_top = mark;
     if (need > c->arena_cap && mark == 0) {
@@ -85,6 +93,16 @@ struct Scratch {
   template <typename T>
   T *get(u64 n) {
     const size_t bytes = (((size_t)(n ? n : 1) * sizeof(T)) + 255) & ~(size_t)255;
+    if (fixed) {
+      if (bytes > fixed_cap - fixed_top) {
+        set_err(c, "%sthe call needs more than the %lld bytes of its fixed scratch", "",
+                (long long)fixed_cap);
+        throw Fail{CHP_EINVAL};
+      }
+      void *p = fixed + fixed_top;
+      fixed_top += bytes;
+      return (T *)p;
+    }
     if (bytes <= ARENA_SMALL) {
       need += bytes;
       if (c->arena && c->arena_top + bytes <= c->arena_cap) {
@@ -441,6 +459,37 @@ void timing_end(chp_ctx *c, const char *name, hipEvent_t a, hipEvent_t b) {
 }
 
 // ---------------------------------------------------------------------------
+// Fixed scratch of the entry points that allocate nothing
+// (chp_evaluate_partition_noalloc).  Every GPU the library runs on holds its
+// own copy for the life of the process.  In host code the array's name is not
+// a device address: its address on each device is taken once, with that
+// device current, when the first context on that device is created, and only
+// that address is ever handed to kernels.
+constexpr size_t FIXED_SCRATCH_BYTES = 64u << 20;
+static __device__ __align__(256) char scratch[FIXED_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+char *g_scratch_ptr[MAX_DEVICES] = {};
+
+// this device's address of scratch (the device current); nullptr on error
+char *fixed_scratch_of(int dev) {
+  if (dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = (char *)ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+// ---------------------------------------------------------------------------
 // C ABI
 
 extern "C" {
@@ -460,8 +509,10 @@ int chp_create(chp_ctx **out, void *hip_stream, chp_alloc_fn alloc, chp_free_fn 
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, c->device) !=
           hipSuccess ||
       hipHostMalloc((void **)&c->pinned, 64 * sizeof(u64), hipHostMallocMapped) != hipSuccess ||
-      hipHostGetDevicePointer((void **)&c->pinned_dev, c->pinned, 0) != hipSuccess) {
+      hipHostGetDevicePointer((void **)&c->pinned_dev, c->pinned, 0) != hipSuccess ||
+      !(c->fixed_scratch = fixed_scratch_of(c->device))) {
     (void)hipGetLastError();
+    if (c->pinned) (void)hipHostFree(c->pinned);
     delete c;
     return CHP_EDEVICE;
   }
@@ -1326,47 +1377,91 @@ int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
   });
 }
 
+}  // extern "C"
+
+namespace {
+
+void check_eval_args(chp_ctx *c, const chp_hgraph *g, const u32 *rho, u32 k,
+                     const chp_params *prm, u64 *part_size, u32 *part_inb, u64 *summary_host) {
+  if (!g || !prm || !summary_host || (g->n_nodes && !rho) || (k && (!part_size || !part_inb))) {
+    set_err(c, "%snull argument");
+    throw Fail{CHP_EINVAL};
+  }
+  if (g->n_nodes && k == 0) {
+    set_err(c, "%sk must be positive");
+    throw Fail{CHP_EINVAL};
+  }
+}
+
+// The evaluation with every scratch buffer taken from s.
+void evaluate_with(chp_ctx *c, Scratch &s, const chp_hgraph *g, const u32 *rho, u32 k,
+                   const chp_params *prm, u64 *part_size, u32 *part_inb, u64 *summary_host) {
+  const u32 N = g->n_nodes, E = g->n_edges;
+  clear_flags(c);
+  u64 *summary = s.get<u64>(8);
+  u32 *part_cnt = s.get<u32>(k);
+  launch_fill_u64(c, summary, 8, 0);
+  launch_fill_u64(c, part_size, k, 0);
+  launch_fill_u32(c, part_inb, k, 0);
+  launch_fill_u32(c, part_cnt, k, 0);
+  launch_eval_nodes(c, N, rho, k, g->n_size, part_size, part_cnt);
+  u32 hc[8];
+  EdgeLists el = make_edge_lists(c, s, E, g->e_off, hc);
+  u64 *scr = nullptr;
+  u64 per_wg = 0;
+  u32 gb = grid_big_for(hc[2]);
+  if (hc[2]) {
+    per_wg = 2ull * hc[3];
+    scr = s.get<u64>(per_wg * gb);
+  }
+  launch_eval_edges(c, g->e_off, g->e_nsrc, g->e_pins, g->e_w, rho, k, part_inb, summary, el,
+                    hc, scr, per_wg, gb);
+  launch_eval_parts(c, k, part_size, part_inb, part_cnt, prm->omega, prm->delta, summary);
+  launch_check(c, "evaluate");
+  u64 sum[8];
+  u32 f;
+  read_many(c, {{sum, summary, sizeof sum}, {&f, c->flags, sizeof f}});
+  if (f & FLAG_EINVAL) fail_flags(c, FLAG_EINVAL, "rho has an entry >= k");
+  memcpy(summary_host, sum, sizeof sum);
+}
+
+}  // namespace
+
+extern "C" {
+
 int chp_evaluate_partition(chp_ctx *c, const chp_hgraph *g, const u32 *rho, u32 k,
                            const chp_params *prm, u64 *part_size, u32 *part_inb,
                            u64 summary_host[8]) {
   return guarded(c, [&] {
-    if (!g || !prm || !summary_host || (g->n_nodes && !rho) || (k && (!part_size || !part_inb))) {
-      set_err(c, "%snull argument");
-      throw Fail{CHP_EINVAL};
-    }
-    const u32 N = g->n_nodes, E = g->n_edges;
-    if (N && k == 0) {
-      set_err(c, "%sk must be positive");
-      throw Fail{CHP_EINVAL};
-    }
+    check_eval_args(c, g, rho, k, prm, part_size, part_inb, summary_host);
     Scratch s(c);
-    clear_flags(c);
-    u64 *summary = s.get<u64>(8);
-    u32 *part_cnt = s.get<u32>(k);
-    launch_fill_u64(c, summary, 8, 0);
-    launch_fill_u64(c, part_size, k, 0);
-    launch_fill_u32(c, part_inb, k, 0);
-    launch_fill_u32(c, part_cnt, k, 0);
-    launch_eval_nodes(c, N, rho, k, g->n_size, part_size, part_cnt);
-    u32 hc[8];
-    EdgeLists el = make_edge_lists(c, s, E, g->e_off, hc);
-    u64 *scr = nullptr;
-    u64 per_wg = 0;
-    u32 gb = grid_big_for(hc[2]);
-    if (hc[2]) {
-      per_wg = 2ull * hc[3];
-      scr = s.get<u64>(per_wg * gb);
-    }
-    launch_eval_edges(c, g->e_off, g->e_nsrc, g->e_pins, g->e_w, rho, k, part_inb, summary, el,
-                      hc, scr, per_wg, gb);
-    launch_eval_parts(c, k, part_size, part_inb, part_cnt, prm->omega, prm->delta, summary);
-    launch_check(c, "evaluate");
-    u64 sum[8];
-    u32 f;
-    read_many(c, {{sum, summary, sizeof sum}, {&f, c->flags, sizeof f}});
-    if (f & FLAG_EINVAL) fail_flags(c, FLAG_EINVAL, "rho has an entry >= k");
-    memcpy(summary_host, sum, sizeof sum);
+    evaluate_with(c, s, g, rho, k, prm, part_size, part_inb, summary_host);
   });
+}
+
+int chp_evaluate_partition_noalloc(chp_ctx *c, const chp_hgraph *g, const u32 *rho, u32 k,
+                                   const chp_params *prm, u64 *part_size, u32 *part_inb,
+                                   u64 summary_host[8]) {
+  if (!c) return CHP_EINVAL;
+  // no timing events are recorded inside this call
+  const int timing = c->timing;
+  c->timing = 0;
+  const int rc = guarded(c, [&] {
+    check_eval_args(c, g, rho, k, prm, part_size, part_inb, summary_host);
+    // everything but the long-hyperedge buffer is known before any work:
+    // the summary, k counters, three hyperedge class lists and their counts
+    const u64 need = 256 + (((u64)k * 4 + 255) & ~255ull) +
+                     3 * (((u64)g->n_edges * 4 + 255) & ~255ull) + 256;
+    if (need > FIXED_SCRATCH_BYTES) {
+      set_err(c, "%sk and the hyperedge count need %lld bytes of scratch, above the fixed "
+                 "67108864", "", (long long)need);
+      throw Fail{CHP_EINVAL};
+    }
+    Scratch s(c, c->fixed_scratch, FIXED_SCRATCH_BYTES);
+    evaluate_with(c, s, g, rho, k, prm, part_size, part_inb, summary_host);
+  });
+  c->timing = timing;
+  return rc;
 }
 
 }  // extern "C"

@@ -59,6 +59,7 @@ struct chp_ctx {
   u32 matching = 0;           // CHP_MATCH_HANDSHAKE or CHP_MATCH_OPTIMAL
   u32 move_order = 0;         // CHP_ORDER_CHAINS or CHP_ORDER_GAIN
   u64 *dsmall = nullptr;   // device small buffer (64 words)
+  char *fixed_scratch = nullptr;  // this device's copy of the library's fixed scratch array
   int timing = 0;
   std::string timing_prefix;  // time only kernels whose name starts with it ("" = all)
   std::vector<TimingRec> pending;

@@ -292,6 +292,26 @@ int chp_evaluate_partition(chp_ctx *ctx, const chp_hgraph *g, const uint32_t *rh
                            const chp_params *prm, uint64_t *part_size, uint32_t *part_inb,
                            uint64_t summary_host[8]);
 
+/* evaluate_partition_noalloc: chp_evaluate_partition for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, outputs and errors; the
+ * caller still supplies rho, part_size and part_inb.  Every scratch buffer
+ * comes from a fixed 64 MiB array that the library holds on each GPU it runs
+ * on until the process ends (its device address is taken once per device
+ * when the first context on that device is created); the call makes no
+ * hipMalloc, hipFree or other allocating call and records no timing events.
+ * Limits: k * 4 + 3 * n_edges * 4 bytes (each rounded up to 256) plus 512
+ * must fit the 64 MiB, else EINVAL before any work; the buffer of hyperedges
+ * too long for LDS (2 * their largest pin count * 8 bytes per workgroup, at
+ * most 256 workgroups) must fit what is left, else EINVAL.  All calls on one
+ * GPU share that GPU's array, whose contents persist between calls (every
+ * counter the call needs is cleared by the call itself): calls that overlap
+ * in time on one GPU, from any context or stream, race and give wrong
+ * results.  Synchronises. */
+int chp_evaluate_partition_noalloc(chp_ctx *ctx, const chp_hgraph *g, const uint32_t *rho,
+                                   uint32_t k, const chp_params *prm, uint64_t *part_size,
+                                   uint32_t *part_inb, uint64_t summary_host[8]);
+
 /* Neighbour entries one rating batch may hold when chp_rate_and_match
  * builds the neighbourhoods itself (a graph without nb); 0 restores the
  * default (3 * 2^30, 12 GiB for the lists plus as much scratch).  A node
