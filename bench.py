@@ -37,7 +37,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-RATE_KERNELS = ("rate_big", "rate", "rate_inc")
+RATE_KERNELS = ("rate_big", "rate", "rate_inc", "rate_incq")
+RATE_PASS = "+".join(RATE_KERNELS) + " (the rating pass)"
 # Invalid neighbours are flagged by the rating and purged from the coarse
 # neighbourhoods (the pages' coarsening does this; --no-purge turns it off).
 PURGE = True
@@ -54,7 +55,8 @@ MIN_PAIR_FRAC = 0.001
 # VLSI netlist's description asks for it), not only after the last
 EVAL_EVERY_LEVEL = {4}
 CSRC = os.path.join(ROOT, "constrained_hypergraph_partitioning_amd", "csrc")
-RATE_SOURCES = [os.path.join(CSRC, f) for f in ("k_rate.hip", "k_rate_inc.hip", "dev.h")]
+RATE_SOURCES = [os.path.join(CSRC, f) for f in ("k_rate.hip", "k_rate_inc.hip", "k_rate_incq.hip",
+                                                 "dev.h")]
 COPY_REF_MIB = 256
 # Pin visits per second the LDS can absorb: every visit is one 64-bit atomic
 # add into an LDS slot; 256 CUs x 2.4 GHz x 128 bytes of LDS per clock per CU
@@ -147,11 +149,12 @@ def summarize_counters(d, workload):
         rows = [r for r in _counter_rows(os.path.join(d, name)) if r["Counter_Name"] == counter]
         ref = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
         rate = [r for r in rows
-                if kernel_base(r["Kernel_Name"]) in ("k_rate", "k_rate_big", "k_rate_inc")]
+                if kernel_base(r["Kernel_Name"]) in ("k_rate", "k_rate_big", "k_rate_inc",
+                                                     "k_rate_incq")]
         # one rating pass per level: a k_rate launch, or k_rate_inc where
         # every node of the level is rated from the incidence
         passes = max(sum(1 for r in rate if kernel_base(r["Kernel_Name"]) == k)
-                     for k in ("k_rate", "k_rate_inc"))
+                     for k in ("k_rate", "k_rate_inc", "k_rate_incq"))
         if not ref or not passes:
             raise SystemExit("%s: no reference copy or no rating dispatch found" % name)
         kib = sum(float(r["Counter_Value"]) for r in rate)
@@ -435,13 +438,13 @@ def main():
                    "pins": h.n_pins, "omega": spec.omega, "delta": spec.delta,
                    "levels": len(levels), "final_nodes": levels[-1][0] - levels[-1][2]
                    if levels else h.n_nodes, "connectivity": int(summ[0])},
-        "roofline": {"bound": "hbm", "kernel": "rate_big+rate+rate_inc (the rating pass)",
+        "roofline": {"bound": "hbm", "kernel": RATE_PASS,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "avg_pass_ms": rate_ms / max(passes, 1),
                      "alg_bytes_per_pass": rate_bytes_per_step / max(len(levels), 1),
                      "traffic": measured_traffic(spec.name)},
-        "roofline_visits": {"bound": "lds", "kernel": "rate_big+rate+rate_inc (the rating pass)",
+        "roofline_visits": {"bound": "lds", "kernel": RATE_PASS,
                             "achieved": visits_s, "peak": LDS_VISIT_PEAK, "unit": "visits/s",
                             "frac": visits_s / LDS_VISIT_PEAK,
                             "visits_per_pass": visits_per_step / max(len(levels), 1)},

@@ -34,7 +34,7 @@ EXPORTS = ["chp_create", "chp_destroy", "chp_last_error", "chp_build_incidence",
            "chp_last_rate_stats", "chp_set_incidence_rating", "chp_pair_leftovers",
            "chp_propose_moves", "chp_set_matching", "chp_set_timing_filter",
            "chp_refine_moves", "chp_set_move_order", "chp_rate_top_and_match",
-           "chp_evaluate_partition_noalloc"]
+           "chp_evaluate_partition_noalloc", "chp_set_incidence_bins"]
 
 
 class ChpError(RuntimeError):
@@ -133,6 +133,8 @@ def load_library(path: str = LIB_PATH):
     lib.chp_pair_leftovers.restype = I
     lib.chp_set_incidence_rating.argtypes = [P, ctypes.c_uint64, ctypes.c_uint32]
     lib.chp_set_incidence_rating.restype = I
+    lib.chp_set_incidence_bins.argtypes = [P, I]
+    lib.chp_set_incidence_bins.restype = I
     lib.chp_evaluate_partition.argtypes = [P, ctypes.POINTER(HGraphC), P, ctypes.c_uint32,
                                            ctypes.POINTER(Params), P, P,
                                            ctypes.POINTER(ctypes.c_uint64)]
@@ -475,6 +477,12 @@ class Context:
         self._check(self.lib.chp_last_rate_stats(self.h, ctypes.byref(n), ctypes.byref(b),
                                                  ctypes.byref(f)), "last_rate_stats")
         return int(n.value), int(b.value), int(f.value)
+
+    def set_incidence_bins(self, bits=32):
+        """Bins of the rating from the incidence: 32 (quantised sums, exact
+        eta for the neighbours in reach; the default) or 64 (exact eta)."""
+        mode = {32: 0, 64: 1}[bits]
+        self._check(self.lib.chp_set_incidence_bins(self.h, mode), "set_incidence_bins")
 
     def set_incidence_rating(self, min_visits=0, hash_keys=0):
         """Incident pins from which a node of a graph without neighbour lists

@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libchp.so")
 OBJDIR = os.path.join(ROOT, "_build", "chp")
 SOURCES = ["api.hip", "k_scan.hip", "k_build.hip", "k_rate.hip", "k_contract.hip", "k_coarse.hip",
-           "k_bitmap.hip", "k_eval.hip", "k_rate_inc.hip",
+           "k_bitmap.hip", "k_eval.hip", "k_rate_inc.hip", "k_rate_incq.hip",
            "k_sort.hip", "k_leftover.hip", "k_gain.hip", "k_match_dp.hip",
            "k_refine.hip"]
 ARCH = "gfx950"

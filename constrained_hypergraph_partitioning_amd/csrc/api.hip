@@ -574,6 +574,12 @@ int chp_set_incidence_rating(chp_ctx *c, uint64_t min_visits, uint32_t hash_keys
   return CHP_OK;
 }
 
+int chp_set_incidence_bins(chp_ctx *c, int bins) {
+  if (!c || (bins != CHP_INC_BINS_32 && bins != CHP_INC_BINS_64)) return CHP_EINVAL;
+  c->inc_bins = (u32)bins;
+  return CHP_OK;
+}
+
 int chp_set_timing_filter(chp_ctx *c, const char *prefix) {
   if (!c) return CHP_EINVAL;
   c->timing_prefix = prefix ? prefix : "";
@@ -830,7 +836,16 @@ void rate_batched(chp_ctx *c, Scratch &s, const chp_hgraph *g, const RateArgs &a
   i64 last = 0;
   if (prev) read_many(c, {{&last, nboff + prev, sizeof last}});
   c->last_nb_built = (u64)(built + last);
-  launch_rate_inc(c, a, frecs, fc, fc + 1, fc + 3, nf, c->inc_hash_keys);
+  if (nf && a.pi == 1 && c->inc_bins == CHP_INC_BINS_32) {
+    // 32-bit bins first; the nodes they cannot rate go to the 64-bit kernel
+    NodeRec *spill = s.get<NodeRec>(nf);
+    u32 *sc = s.get<u32>(2);  // spill count, work counter of the second launch
+    launch_fill_u32(c, sc, 2, 0);
+    launch_rate_incq(c, a, frecs, fc, fc + 1, fc + 3, nf, c->inc_hash_keys, spill, sc);
+    launch_rate_inc(c, a, spill, sc, fc + 1, sc + 1, c->n_cu, c->inc_hash_keys);
+  } else {
+    launch_rate_inc(c, a, frecs, fc, fc + 1, fc + 3, nf, c->inc_hash_keys);
+  }
   launch_check(c, "rate from the incidence");
 }
 

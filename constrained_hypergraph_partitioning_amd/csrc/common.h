@@ -56,6 +56,7 @@ struct chp_ctx {
   u32 last_inc_nodes = 0;     // nodes it rated straight from the incidence
   u64 inc_min_visits = 0;     // incident pins that send a node there (0 = default)
   u32 inc_hash_keys = 0;      // keys a sparse window there may claim (0 = all it holds)
+  u32 inc_bins = 0;           // CHP_INC_BINS_32 (default) or CHP_INC_BINS_64 there
   u32 matching = 0;           // CHP_MATCH_HANDSHAKE or CHP_MATCH_OPTIMAL
   u32 move_order = 0;         // CHP_ORDER_CHAINS or CHP_ORDER_GAIN
   u64 *dsmall = nullptr;   // device small buffer (64 words)

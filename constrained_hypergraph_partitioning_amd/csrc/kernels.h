@@ -207,6 +207,12 @@ void launch_inc_classify(chp_ctx *c, const RateArgs &a, u64 min_visits, uint8_t 
                          NodeRec *recs, u32 *cnt, u32 *gmax);
 void launch_rate_inc(chp_ctx *c, const RateArgs &a, const NodeRec *recs, const u32 *cnt,
                      const u32 *gmax, u32 *work, u32 host_count, u32 hash_keys);
+// The same nodes with 32-bit bins (k_rate_incq.hip) where Delta cannot bind
+// for the node; the nodes it cannot rate are appended to spill / *spill_cnt
+// (zeroed before) for launch_rate_inc.
+void launch_rate_incq(chp_ctx *c, const RateArgs &a, const NodeRec *recs, const u32 *cnt,
+                      const u32 *gmax, u32 *work, u32 host_count, u32 hash_keys, NodeRec *spill,
+                      u32 *spill_cnt);
 
 struct MatchScratch {
   u64 *bscore;  // [N] zeroed

@@ -150,7 +150,8 @@ def fused_mask(og, min_visits):
     return (deg >= 1) & (deg <= 384) & (w >= min_visits) & (w < 2 ** 27)
 
 
-def batched_levels(chp, ctx, h, omega, delta, seed, levels, limit, inc, hkeys=0, tag="", pi=1):
+def batched_levels(chp, ctx, h, omega, delta, seed, levels, limit, inc, hkeys=0, tag="", pi=1,
+                   bins=32, noise_on=True):
     """Levels of a graph built without neighbourhoods: the rating builds
     them per batch or rates straight from the incidence; every level's
     target, score, match, gamma and coarse graph against the oracle, and the
@@ -162,18 +163,19 @@ def batched_levels(chp, ctx, h, omega, delta, seed, levels, limit, inc, hkeys=0,
     assert_graph_equal(dg, og, tag + " build", neighbors=False)
     ctx.set_batch_entries(limit)
     ctx.set_incidence_rating(inc, hkeys)
+    ctx.set_incidence_bins(bins)
     try:
         for lvl in range(levels):
             if pi > 1:
-                tl, sl, m, npairs = ctx.rate_top_and_match(dg, pi, omega, delta, True, seed)
-                otl, osl = oracle.rate_top(og, omega, delta, True, seed, pi)
+                tl, sl, m, npairs = ctx.rate_top_and_match(dg, pi, omega, delta, noise_on, seed)
+                otl, osl = oracle.rate_top(og, omega, delta, noise_on, seed, pi)
                 assert_equal(chp.to_host(tl, np.uint32).reshape(-1), otl.reshape(-1),
                              "%s L%d top-pi targets" % (tag, lvl))
                 assert_equal(chp.to_host(sl, np.uint64).reshape(-1), osl.reshape(-1),
                              "%s L%d top-pi scores" % (tag, lvl))
                 t, sc = tl[0], sl[0]
             else:
-                t, sc, m, npairs = ctx.rate_and_match(dg, omega, delta, True, seed)
+                t, sc, m, npairs = ctx.rate_and_match(dg, omega, delta, noise_on, seed)
             built, batches, nfused = ctx.last_rate_stats()
             fm = fused_mask(og, inc if inc else INC_DEFAULT)
             # entries built over the batches = sum of |N(n)| over the other nodes
@@ -181,7 +183,7 @@ def batched_levels(chp, ctx, h, omega, delta, seed, levels, limit, inc, hkeys=0,
             want_nb = int(np.diff(nbo)[~fm].sum())
             assert (nfused, built) == (int(fm.sum()), want_nb) and batches >= 1, \
                 (nfused, int(fm.sum()), built, want_nb, batches)
-            lv = oracle.level(og, omega, delta, True, seed, build_neighbors=False, pi=pi)
+            lv = oracle.level(og, omega, delta, noise_on, seed, build_neighbors=False, pi=pi)
             for name, got, want in (("target", chp.to_host(t, np.uint32), lv.target),
                                     ("score", chp.to_host(sc, np.uint64), lv.score),
                                     ("match", chp.to_host(m, np.uint32), lv.match)):
@@ -196,9 +198,12 @@ def batched_levels(chp, ctx, h, omega, delta, seed, levels, limit, inc, hkeys=0,
     finally:
         ctx.set_batch_entries(0)
         ctx.set_incidence_rating(0, 0)
+        ctx.set_incidence_bins(32)
 
 
-INC_MODES = {"lists": (NEVER, 0), "default": (0, 0), "all": (1, 0), "all-hash64": (1, 64)}
+INC_MODES = {"lists": (NEVER, 0, 32), "default": (0, 0, 32), "all": (1, 0, 32),
+             "all-hash64": (1, 64, 32), "all-bins64": (1, 0, 64),
+             "all-bins64-hash64": (1, 64, 64)}
 
 
 @pytest.mark.parametrize("mode", list(INC_MODES))
@@ -212,39 +217,50 @@ def test_batched_neighbourhoods(chp, ctx, cfg, nn, limit, mode):
     (so that windows fill up and restart)."""
     spec = synth.config(cfg, n_nodes=nn)
     h = synth.generate(spec)
-    inc, hkeys = INC_MODES[mode]
+    inc, hkeys, bins = INC_MODES[mode]
     say("batched", cfg, nn, limit, mode)
     batched_levels(chp, ctx, h, spec.omega, spec.delta, spec.seed, 2, limit, inc, hkeys,
-                   tag="batched %d %s" % (cfg, mode))
+                   tag="batched %d %s" % (cfg, mode), bins=bins)
 
 
-def test_incidence_rating_tiny(chp, ctx):
+@pytest.mark.parametrize("bins", [32, 64])
+def test_incidence_rating_tiny(chp, ctx, bins):
     """Every node of the brute-force-pinned tiny graphs rated straight from
-    the incidence, under the limit grid (so that both limits bind)."""
+    the incidence, under the limit grid (so that both limits bind), with the
+    32-bit bins (where Delta cannot bind) and the 64-bit ones; and the same
+    graphs with weights up to 2^18, whose term sums need a shift of the
+    32-bit bins (so that their bounds are not exact)."""
     import test_oracle_pins as pins
     for kw in pins.tiny_cases():
         h = synth.tiny(**kw)
-        say("inc tiny", kw["seed"])
+        say("inc tiny", bins, kw["seed"])
         for omega, delta in pins.constraint_grid(h):
             for hkeys in (0, 2):
                 batched_levels(chp, ctx, h, omega, delta, kw["seed"], 1, 0, 1, hkeys,
-                               tag="inc tiny%d" % kw["seed"])
+                               tag="inc tiny%d b%d" % (kw["seed"], bins), bins=bins)
+        heavy = dict(kw, max_w=1 << 18)
+        h = synth.tiny(**heavy)
+        batched_levels(chp, ctx, h, 1 << 30, 1 << 30, kw["seed"], 1, 0, 1, 0,
+                       tag="inc tiny-heavy%d b%d" % (kw["seed"], bins), bins=bins)
 
 
-@pytest.mark.parametrize("omega,dslack", [(4, 0), (6, 1), (16, 3)])
-def test_incidence_rating_stress(chp, ctx, omega, dslack):
+@pytest.mark.parametrize("bins", [32, 64])
+@pytest.mark.parametrize("omega,dslack", [(4, 0), (6, 1), (16, 3), (16, 1 << 20)])
+def test_incidence_rating_stress(chp, ctx, omega, dslack, bins):
     """Both limits binding (Delta just above the largest in-degree), several
-    levels, every node rated straight from the incidence."""
+    levels, every node rated straight from the incidence; with Delta out of
+    reach the 32-bit bins take every node."""
     spec = synth.config(1)
     h = synth.generate(spec)
     indeg = np.bincount(np.concatenate([h.e_pins[h.e_off[e] + h.e_nsrc[e]:h.e_off[e + 1]]
                                         for e in range(h.n_edges)]), minlength=h.n_nodes)
     delta = int(indeg.max()) + dslack
-    say("inc stress", omega, delta)
-    batched_levels(chp, ctx, h, omega, delta, 5, 6, 0, 1, 0, tag="inc stress")
+    say("inc stress", omega, delta, bins)
+    batched_levels(chp, ctx, h, omega, delta, 5, 6, 0, 1, 0, tag="inc stress", bins=bins)
 
 
-def test_incidence_rating_hub_and_wide_span(chp, ctx):
+@pytest.mark.parametrize("bins", [32, 64])
+def test_incidence_rating_hub_and_wide_span(chp, ctx, bins):
     """A hub with 500 inbound hyperedges (above the 384 the incidence rating
     takes: it goes through a list) beside nodes that take it, and a node
     whose pins span 6,000,000 ids (histogram buckets wider than the
@@ -263,8 +279,8 @@ def test_incidence_rating_hub_and_wide_span(chp, ctx):
         if dst:
             edges.append(([s], sorted(dst)))
     h = synth.from_lists(n, edges, weights=[1 + j % 7 for j in range(len(edges))])
-    say("inc hub")
-    batched_levels(chp, ctx, h, 1 << 20, 1 << 20, 3, 2, 0, 1, 0, tag="inc hub")
+    say("inc hub", bins)
+    batched_levels(chp, ctx, h, 1 << 20, 1 << 20, 3, 2, 0, 1, 0, tag="inc hub", bins=bins)
     N = 6_000_000
     edges = []
     for j in range(200):
@@ -272,9 +288,31 @@ def test_incidence_rating_hub_and_wide_span(chp, ctx):
         dst = ({0} | set(int(x) for x in rng.integers(1, N, 30))) - {s}
         edges.append(([s], sorted(dst)))
     h = synth.from_lists(N, edges, weights=[1 + j % 5 for j in range(len(edges))])
-    say("inc wide span")
-    batched_levels(chp, ctx, h, 1 << 20, 1 << 20, 3, 1, 0, 1, 0, tag="inc wide")
-    batched_levels(chp, ctx, h, 1 << 20, 1 << 20, 3, 1, 0, 1, 16, tag="inc wide hash16")
+    say("inc wide span", bins)
+    batched_levels(chp, ctx, h, 1 << 20, 1 << 20, 3, 1, 0, 1, 0, tag="inc wide", bins=bins)
+    batched_levels(chp, ctx, h, 1 << 20, 1 << 20, 3, 1, 0, 1, 16, tag="inc wide hash16",
+                   bins=bins)
+
+
+def test_incidence_bins_many_ties(chp, ctx):
+    """Nodes whose neighbours tie in eta by the thousand (one hyperedge of
+    1,500 equal-weight pins among few small ones): every neighbour stays in
+    reach of the 32-bit bins' bounds, the list of contenders overflows and
+    those nodes are rated by the 64-bit bins instead, with the same result;
+    noise on and off."""
+    rng = np.random.Generator(np.random.PCG64(5))
+    n = 2000
+    edges = [([0], [int(x) for x in range(1, 1501)])]
+    for j in range(300):
+        s = int(rng.integers(0, n))
+        dst = set(int(x) for x in rng.integers(0, n, int(rng.integers(1, 6)))) - {s}
+        if dst:
+            edges.append(([s], sorted(dst)))
+    h = synth.from_lists(n, edges, weights=[3] + [1 + j % 4 for j in range(len(edges) - 1)])
+    for noise_on in (True, False):
+        say("inc ties", noise_on)
+        batched_levels(chp, ctx, h, 1 << 20, 1 << 20, 3, 2, 0, 1, 0, tag="inc ties",
+                       noise_on=noise_on)
 
 
 @pytest.mark.parametrize("cfg,nn,levels", [(4, 20000, 12), (1, None, 8), (2, 5000, 10),
@@ -348,6 +386,41 @@ def test_optimal_matching_tiny_and_chain(chp, ctx):
     run_level_pair(chp, ctx, dg, og, 1 << 30, 1 << 30, False, 0, tag="dp chain", optimal=True)
 
 
+def chain_forest(lengths):
+    """Disjoint paths i -> i+1 whose weights grow along each path: every node
+    targets the next one, so each path is one chain of winning links ending
+    in a two-cycle at its top."""
+    edges, weights, base = [], [], 0
+    for length in lengths:
+        for i in range(length - 1):
+            edges.append(([base + i], [base + i + 1]))
+            weights.append(i + 1)
+        base += length
+    return synth.from_lists(base, edges, weights)
+
+
+@pytest.mark.parametrize("pi", [1, 2])
+def test_handshake_long_chains(chp, ctx, pi):
+    """The handshake on chains of winning links longer than the per-node walk
+    bound (256 links): one path of 5,000 nodes, and a forest of paths below,
+    at and above the bound.  The pointer-jumping fallback must run, and the
+    matching equal the oracle's; with pi = 2 the fallback's flag is raised
+    and cleared round by round."""
+    for lengths in ([5000], [3, 100, 255, 256, 257, 258, 300, 513, 1000, 2000]):
+        h = chain_forest(lengths)
+        say("handshake chains", pi, len(lengths))
+        dg, og = both(chp, ctx, h, 1 << 30, 1 << 30)
+        ctx.reset_timings()
+        ctx.set_timing(True)
+        try:
+            run_level_pair(chp, ctx, dg, og, 1 << 30, 1 << 30, False, 0,
+                           tag="chains %d pi%d" % (len(lengths), pi), pi=pi)
+            tm = ctx.timings()
+        finally:
+            ctx.set_timing(False)
+        assert "jump_round" in tm and "jump_finish" in tm, sorted(tm)
+
+
 @pytest.mark.parametrize("pi", [2, 4])
 def test_top_pi_tiny(chp, ctx, pi):
     """Top-pi lists and pi matching rounds on the tiny graphs under the limit
@@ -412,10 +485,10 @@ def test_top_pi_without_lists(chp, ctx, cfg, nn, limit, mode):
     at 64 keys too)."""
     spec = synth.config(cfg, n_nodes=nn)
     h = synth.generate(spec)
-    inc, hkeys = INC_MODES[mode]
+    inc, hkeys, bins = INC_MODES[mode]
     say("top-pi batched", cfg, nn, limit, mode)
     batched_levels(chp, ctx, h, spec.omega, spec.delta, spec.seed, 2, limit, inc, hkeys,
-                   tag="top4 batched %d %s" % (cfg, mode), pi=4)
+                   tag="top4 batched %d %s" % (cfg, mode), pi=4, bins=bins)
 
 
 def test_top_pi_one_and_errors(chp, ctx):

@@ -391,6 +391,24 @@ def test_threaded_rating_is_the_single_threaded_one(threads):
         assert ei.value.code == oracle.EOVERFLOW
 
 
+def test_coarsen_stall_rule():
+    """The driver's stall rule: with min_pair_frac f the coarsening ends after
+    the first level that pairs fewer than f of its nodes, and the levels up to
+    it are the levels of the run without the rule."""
+    spec = synth.config(2, n_nodes=5000)
+    h = synth.generate(spec)
+    full, _, _ = oracle.coarsen(load(h, spec.omega, spec.delta), spec.omega, spec.delta, 0, 64,
+                                True, spec.seed, leftovers=True)
+    for f in (0.02, 0.05, 0.2):
+        stop = next((i for i, lv in enumerate(full)
+                     if lv.n_pairs < f * lv.target.shape[0]), len(full) - 1)
+        got, _, _ = oracle.coarsen(load(h, spec.omega, spec.delta), spec.omega, spec.delta, 0,
+                                   64, True, spec.seed, leftovers=True, min_pair_frac=f)
+        assert len(got) == stop + 1, (f, len(got), stop)
+        for a, b in zip(got, full):
+            assert np.array_equal(a.match, b.match) and a.n_pairs == b.n_pairs
+
+
 # ---------------------------------------------------------------- error paths
 def err_code(edges, n, w=None, sizes=None, omega=BIG, delta=BIG):
     h = synth.from_lists(n, edges, w, sizes)
