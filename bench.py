@@ -99,6 +99,11 @@ def parse():
                    help="also time THETA refinement passes (proposal, chained sequence, "
                         "in-sequence gains, event validity, best prefix) on the input graph "
                         "from the step's projected partition, Omega enforced")
+    p.add_argument("--vcycle", type=int, default=0, metavar="THETA",
+                   help="also time the whole V-cycle: the coarsening as the step runs it, "
+                        "then the coarsest nodes as partitions, THETA refinement passes per "
+                        "level (the first half proposing without Omega) and projection down "
+                        "to the input graph")
     p.add_argument("--no-leftovers", action="store_true",
                    help="do not pair the nodes left without a partner")
     p.add_argument("--no-purge", action="store_true",
@@ -465,6 +470,8 @@ def main():
     if args.refine:
         out["refine"] = time_refine(ctx, dev_edges, spec, rho_buf, out["config"]["final_nodes"],
                                     h, args.refine)
+    if args.vcycle:
+        out["vcycle"] = time_vcycle(ctx, dev_edges, spec, with_nb, args.vcycle)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(h, spec, args.workload, args.cpu_sample_nodes,
                                            args.cpu_threads)
@@ -536,6 +543,64 @@ def time_refine(ctx, dev_edges, spec, rho_buf, k, h, theta):
             "parts_over_omega": int(s1[2]), "parts_over_delta": int(s1[3]),
             "kernel_ms_per_pass": {kk: round(v[1] / theta, 4) for kk, v in
                                    sorted(tm.items(), key=lambda kv: -kv[1][1])[:10]}}
+
+
+def time_vcycle(ctx, dev_edges, spec, with_nb, theta):
+    """The whole multi-level scheme ([HP] Sec. III) on the input graph: the
+    coarsening as run_step runs it (keeping every level), the coarsest nodes
+    as the initial partitions, then from the coarsest level down theta
+    refinement passes per level and the projection to the level below.
+    Reports the two phases' times (synchronised), the time per level of the
+    uncoarsening, and the connectivity after each phase."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g0 = ctx.build_incidence(*dev_edges, spec.omega, spec.delta, with_nb)
+    floor_nodes = -(-int(spec_total_size(dev_edges)) // spec.omega)
+    graphs, gammas = [g0], []
+    for _ in range(spec.levels):
+        g = graphs[-1]
+        if (spec.target_nodes and g.n_nodes < spec.target_nodes) or g.n_nodes <= floor_nodes:
+            break
+        flags = ctx.new_flags(g) if PURGE and with_nb else None
+        tgt, _, match, npairs = ctx.rate_and_match(g, spec.omega, spec.delta, True, spec.seed,
+                                                   flags=flags)
+        if LEFTOVERS:
+            npairs += ctx.pair_leftovers(g, tgt, match, spec.omega, spec.delta)
+        if npairs == 0:
+            break
+        gamma, cg = ctx.contract(g, match, with_nb, flags=flags)
+        graphs.append(cg)
+        gammas.append(gamma)
+        if npairs < MIN_PAIR_FRAC * g.n_nodes:
+            break
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    k = graphs[-1].n_nodes
+    rho = torch.arange(k, dtype=torch.int32, device=ctx.device)
+    _, _, s_init = ctx.evaluate_partition(graphs[-1], rho, k, spec.omega, spec.delta)
+    applied = gain = 0
+    level_ms = []
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for d in range(len(graphs) - 1, -1, -1):
+        ta = time.perf_counter()
+        na, ga = ctx.refine_level(graphs[d], rho, k, spec.omega, spec.delta, theta)
+        applied += na
+        gain += ga
+        if d:
+            rho = ctx.project_partition(gammas[d - 1], rho, graphs[d].n_nodes)
+        torch.cuda.synchronize()
+        level_ms.append(round((time.perf_counter() - ta) * 1e3, 3))
+    t3 = time.perf_counter()
+    _, _, s_fin = ctx.evaluate_partition(g0, rho, k, spec.omega, spec.delta)
+    for g in graphs:
+        g.free()
+    return {"theta": theta, "levels": len(graphs) - 1, "parts": k,
+            "coarsening_ms": (t1 - t0) * 1e3, "uncoarsening_ms": (t3 - t2) * 1e3,
+            "uncoarsening_ms_per_level": level_ms, "moves_applied": applied, "gain": gain,
+            "connectivity_initial": int(s_init[0]), "connectivity_final": int(s_fin[0]),
+            "parts_over_omega": int(s_fin[2]), "parts_over_delta": int(s_fin[3])}
 
 
 def rate_level_bytes(levels, h, spec):

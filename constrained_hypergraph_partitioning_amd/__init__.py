@@ -34,7 +34,8 @@ EXPORTS = ["chp_create", "chp_destroy", "chp_last_error", "chp_build_incidence",
            "chp_last_rate_stats", "chp_set_incidence_rating", "chp_pair_leftovers",
            "chp_propose_moves", "chp_set_matching", "chp_set_timing_filter",
            "chp_refine_moves", "chp_set_move_order", "chp_rate_top_and_match",
-           "chp_evaluate_partition_noalloc", "chp_set_incidence_bins"]
+           "chp_evaluate_partition_noalloc", "chp_set_incidence_bins", "chp_project_partition",
+           "chp_refine_level"]
 
 
 class ChpError(RuntimeError):
@@ -135,6 +136,13 @@ def load_library(path: str = LIB_PATH):
     lib.chp_set_incidence_rating.restype = I
     lib.chp_set_incidence_bins.argtypes = [P, I]
     lib.chp_set_incidence_bins.restype = I
+    lib.chp_project_partition.argtypes = [P, ctypes.c_uint32, P, ctypes.c_uint32, P, P]
+    lib.chp_project_partition.restype = I
+    lib.chp_refine_level.argtypes = [P, ctypes.POINTER(HGraphC), P, ctypes.c_uint32,
+                                     ctypes.POINTER(Params), ctypes.c_uint32,
+                                     ctypes.POINTER(ctypes.c_uint32),
+                                     ctypes.POINTER(ctypes.c_int64)]
+    lib.chp_refine_level.restype = I
     lib.chp_evaluate_partition.argtypes = [P, ctypes.POINTER(HGraphC), P, ctypes.c_uint32,
                                            ctypes.POINTER(Params), P, P,
                                            ctypes.POINTER(ctypes.c_uint64)]
@@ -461,6 +469,26 @@ class Context:
             self.h, ctypes.byref(g.c), _ptr(rho), k, ctypes.byref(prm), _ptr(part_size),
             _ptr(part_inb), summ), "evaluate_partition_noalloc")
         return np.array(list(summ), dtype=np.uint64)
+
+    def project_partition(self, gamma, rho_coarse, n_coarse):
+        """rho of the finer level: rho_coarse[gamma[n]] (a new int32 tensor)."""
+        n = int(gamma.numel())
+        out = torch.empty(max(n, 1), dtype=torch.int32, device=self.device)
+        self._check(self.lib.chp_project_partition(self.h, n, _ptr(gamma), n_coarse,
+                                                   _ptr(rho_coarse), _ptr(out)),
+                    "project_partition")
+        return out[:n]
+
+    def refine_level(self, g: HGraph, rho, k, omega, delta, theta=16):
+        """theta refinement passes on g (rho updated in place): (moves
+        applied, summed gain)."""
+        na = ctypes.c_uint32()
+        ga = ctypes.c_int64()
+        prm = Params(omega, delta, 0, 0)
+        self._check(self.lib.chp_refine_level(self.h, ctypes.byref(g.c), _ptr(rho), k,
+                                              ctypes.byref(prm), theta, ctypes.byref(na),
+                                              ctypes.byref(ga)), "refine_level")
+        return int(na.value), int(ga.value)
 
     def set_batch_entries(self, entries=0):
         """Neighbour entries per rating batch for graphs without neighbours

@@ -160,6 +160,20 @@ __global__ void k_fill_u64(u64 *p, u64 n, u64 v) {
     p[i] = v;
 }
 
+// rho_fine[n] = rho_coarse[gamma[n]]; a coarse id out of range raises EINVAL
+__global__ void k_project(u32 n_fine, const u32 *gamma, u32 n_coarse, const u32 *rho_coarse,
+                          u32 *rho_fine, u32 *flags) {
+  const u32 n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= n_fine) return;
+  const u32 c = gamma[n];
+  if (c >= n_coarse) {
+    atomicOr(flags, FLAG_EINVAL);
+    rho_fine[n] = 0;
+    return;
+  }
+  rho_fine[n] = rho_coarse[c];
+}
+
 // Small device->host reads.  One kernel gathers the words of every item into
 // the context's pinned host buffer (mapped into the device address space),
 // then the stream is synchronised: one launch and no copy engine per call.
@@ -1205,6 +1219,54 @@ int chp_refine_moves(chp_ctx *c, const chp_hgraph *g, u32 *rho, u32 k, const chp
     read_many(c, {{&L, cnt + 6, sizeof L}, {&b, best, sizeof b}});
     *n_applied_host = L == NONE32 ? 0 : L;
     *gain_host = (i64)b;
+  });
+}
+
+int chp_project_partition(chp_ctx *c, uint32_t n_fine, const uint32_t *gamma, uint32_t n_coarse,
+                          const uint32_t *rho_coarse, uint32_t *rho_fine) {
+  return guarded(c, [&] {
+    if (n_fine && (!gamma || !rho_coarse || !rho_fine)) {
+      set_err(c, "%snull argument");
+      throw Fail{CHP_EINVAL};
+    }
+    if (n_fine == 0) return;
+    clear_flags(c);
+    CHP_LAUNCH(c, "project", k_project, grid_for(n_fine, 256), 256, 0, n_fine, gamma, n_coarse,
+               rho_coarse, rho_fine, c->flags);
+    launch_check(c, "project");
+    if (read_flags(c) & FLAG_EINVAL) fail_flags(c, FLAG_EINVAL, "gamma has an id >= n_coarse");
+  });
+}
+
+int chp_refine_level(chp_ctx *c, const chp_hgraph *g, uint32_t *rho, uint32_t k,
+                     const chp_params *prm, uint32_t theta, uint32_t *n_applied_host,
+                     int64_t *gain_host) {
+  return guarded(c, [&] {
+    if (!g || !prm || !n_applied_host || !gain_host || (g->n_nodes && !rho)) {
+      set_err(c, "%snull argument");
+      throw Fail{CHP_EINVAL};
+    }
+    *n_applied_host = 0;
+    *gain_host = 0;
+    const u32 N = g->n_nodes;
+    if (N == 0 || theta == 0) return;
+    Scratch s(c);
+    u32 *move = s.get<u32>(N);
+    i64 *gain = s.get<i64>(N);
+    for (u32 r = 0; r < theta; ++r) {
+      // the first half of the passes may propose moves that overfill a
+      // partition; the second half only moves that fit (both apply valid
+      // prefixes only)
+      int rc = chp_propose_moves(c, g, rho, k, prm, r >= theta / 2 ? 1 : 0, move, gain);
+      if (rc != CHP_OK) throw Fail{rc};
+      u32 nseq = 0, na = 0;
+      i64 ga = 0;
+      rc = chp_refine_moves(c, g, rho, k, prm, move, gain, nullptr, nullptr, nullptr, &nseq, &na,
+                            &ga);
+      if (rc != CHP_OK) throw Fail{rc};
+      *n_applied_host += na;
+      *gain_host += ga;
+    }
   });
 }
 

@@ -47,14 +47,16 @@ constexpr u32 QNHB = 1024;            // estimate buckets
 constexpr u32 QBS_MIN = 12;           // log2 of the narrowest bucket
 constexpr u32 QHTGT = QCAP * 3 / 4;   // estimated visits a hash window aims at
 constexpr u32 QEST = 16;              // estimates count sixteenths of a visit
-constexpr u32 QU = 16;                // pins per thread per chunk
+constexpr u32 QU = 16384 / QB;        // pins per thread per chunk
 constexpr u32 QCH = QB * QU;          // pins per chunk
 constexpr u32 QNBLK = QCH / WAVE;     // wave blocks per chunk
 constexpr u32 QCONT = 256;            // contenders a node may keep
 constexpr u32 QFAIL = 0xFFFFFFFFu;
 static_assert(QB - 1 + QCAP < QHS, "claims in flight never fill the table");
-static_assert(QRUNS <= QB && QNBLK <= QB && QNHB <= QB, "one item per thread");
-static_assert(QNHB == 32 * 32, "two-level dense bitmap");
+static_assert(QE <= QB && QNBLK <= QB, "one hyperedge (its two runs) and one block per thread");
+constexpr u32 QBPT = QNHB / QB;       // estimate buckets per thread
+static_assert(QNHB % QB == 0 && QBPT <= 2 && QNHB == 32 * 32,
+              "one or two buckets per thread; two-level dense bitmap");
 static_assert(QD % QB == 0 && QHS % QB == 0 && QSMAX % QB == 0, "slots per thread");
 
 struct QSmem {
@@ -82,12 +84,15 @@ struct QSmem {
   u32 cq[QRUNS];
   u32 cnext[QRUNS];    // stretch index of its first pin at or above the window's end
   u32 bfirst[QNBLK];   // stretch of the first pin of each wave block of a chunk
+  u64 sbits[QNBLK];    // bit p of word b: a stretch starts at chunk position 64 b + p
   u32 cum[QNHB + 1];   // estimated visits below each bucket (sixteenths)
   u32 dbits[32];       // bucket b starts a dense window
   u32 dsum;            // dbits word w is not zero
   u32 cid[QCONT];      // contenders: id, upper bound of eta + noise
   u64 cub[QCONT];
-  u64 red64[QW];
+  u64 red64[QW + 1];
+  u64 wbl[2][QW];      // per wave: best lower bound of a window (by window parity)
+  u32 wvmax[QW];       // per wave: largest bin a window's visits left
   u32 redi[QW];
   u32 red32[QW + 1];
   u32 fail_min;
@@ -101,6 +106,10 @@ __device__ __forceinline__ u32 rfl(u32 v) { return __builtin_amdgcn_readfirstlan
 __device__ __forceinline__ u64 rfl64(u64 v) {
   return ((u64)rfl((u32)(v >> 32)) << 32) | rfl((u32)v);
 }
+
+// a value known to be the same on every lane, moved to scalar registers
+__device__ __forceinline__ u32 uni(u32 v) { return rfl(v); }
+__device__ __forceinline__ u64 uni(u64 v) { return rfl64(v); }
 
 __device__ __forceinline__ u32 qslot(u32 m) { return (u32)(((u64)(m * 0x9E3779B1u) * QHS) >> 32); }
 
@@ -163,10 +172,34 @@ __device__ __forceinline__ T q_reduce(T v, T *lds, Op op) {
 #pragma unroll
   for (int w = 1; w < QW; ++w) r = op(r, lds[w]);
   __syncthreads();
-  return r;
+  return uni(r);
 }
 
 __device__ __forceinline__ u64 umax64(u64 a, u64 b) { return a > b ? a : b; }
+
+// Two reductions over the workgroup with one pair of barriers; lds holds 2 QW.
+template <typename T, typename Op1, typename Op2>
+__device__ __forceinline__ void q_reduce2(T &v1, T &v2, T *lds, Op1 op1, Op2 op2) {
+#pragma unroll
+  for (int d = WAVE / 2; d > 0; d >>= 1) {
+    v1 = op1(v1, (T)__shfl_xor(v1, d, WAVE));
+    v2 = op2(v2, (T)__shfl_xor(v2, d, WAVE));
+  }
+  if (lane_id() == 0) {
+    lds[wave_id()] = v1;
+    lds[QW + wave_id()] = v2;
+  }
+  __syncthreads();
+  T r1 = lds[0], r2 = lds[QW];
+#pragma unroll
+  for (int w = 1; w < QW; ++w) {
+    r1 = op1(r1, lds[w]);
+    r2 = op2(r2, lds[QW + w]);
+  }
+  __syncthreads();
+  v1 = uni(r1);
+  v2 = uni(r2);
+}
 
 // One candidate m with bin value V (valid, V > 0): judged against the
 // threshold T; a contender is appended, the thread's best lower bound kept.
@@ -192,7 +225,12 @@ __device__ __forceinline__ void q_judge(const RateArgs &A, QSmem &S, u32 n, u32 
 // node must go to k_rate_inc instead.
 __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 max_size,
                             u32 max_nin, u32 hcap, u64 cap, u64 dmod, u64 magic) {
-  const u32 tid = threadIdx.x, lane = lane_id(), wid = wave_id();
+  // the thread index is re-read per node through an empty asm, so that the
+  // compiler recomputes the slot addresses derived from it inside each node
+  // instead of holding dozens of them in registers across the node loop
+  u32 tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  u32 lane = tid & (WAVE - 1), wid = tid / WAVE;
   const u32 n = h.n, deg = h.deg, nin = h.nin, nr = 2 * deg;
   const u64 size_n = h.size, W = (u64)h.nb0;
   const bool om = size_n + max_size > A.omega;  // Omega can reject a neighbour
@@ -216,9 +254,9 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     S.ens[tid] = ns;
     S.elen[tid] = (u32)(b - a);
   }
-  const u64 tsum = q_reduce<u64>(counts ? te : 0, S.red64, [](u64 x, u64 y) { return sat_add(x, y); });
-  const u64 tmin = q_reduce<u64>(counts ? te : ~0ull, S.red64,
-                                 [](u64 x, u64 y) { return x < y ? x : y; });
+  u64 tsum = counts ? te : 0, tmin = counts ? te : ~0ull;
+  q_reduce2<u64>(tsum, tmin, S.cub, [](u64 x, u64 y) { return sat_add(x, y); },
+                 [](u64 x, u64 y) { return x < y ? x : y; });
   if (sat_add(tsum, cap) >= (1ull << 63)) {
     if (tid == 0) {
       atomicOr(A.flags, FLAG_EOVERFLOW);
@@ -239,11 +277,15 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
   const u32 c0 = (l0 + (1u << sh) - 1) >> sh, c1 = (l1 + (1u << sh) - 1) >> sh;
   u32 ts;
   const u32 so = wg_excl_scan<QB>(c0 + c1, S.red32, &ts);
+  ts = rfl(ts);
   if (tid < deg) {
     S.rsp[2 * tid] = so;
     S.rsp[2 * tid + 1] = so + c0;
   }
-  if (tid < nr) S.rcur[tid] = 0;  // every pin is >= the first window's low end
+  if (tid < deg) {  // every pin is >= the first window's low end
+    S.rcur[2 * tid] = 0;
+    S.rcur[2 * tid + 1] = 0;
+  }
   if (tid == 0) S.rsp[nr] = ts;
   for (u32 b = tid; b <= QNHB; b += QB) S.cum[b] = 0;
   __syncthreads();
@@ -277,8 +319,8 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       mx = sl[k] > mx ? sl[k] : mx;
     }
   }
-  mn = q_reduce<u32>(mn, S.red32, [](u32 a, u32 b) { return a < b ? a : b; });
-  mx = q_reduce<u32>(mx, S.red32, [](u32 a, u32 b) { return a > b ? a : b; });
+  q_reduce2<u32>(mn, mx, S.cid, [](u32 a, u32 b) { return a < b ? a : b; },
+                 [](u32 a, u32 b) { return a > b ? a : b; });
   // -- estimated visits over buckets of 2^bs ids from mn, in 1/16 of a visit:
   // each block's pins spread evenly over the buckets from its first pin's to
   // its last pin's (a difference array, then two scans)
@@ -299,25 +341,29 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
   }
   __syncthreads();
   {
-    const u32 d0 = tid < QNHB ? S.cum[tid] : 0;
+    const u32 d0 = S.cum[QBPT * tid], d1 = QBPT > 1 ? S.cum[QBPT * tid + 1] : 0;
     u32 tot;
-    const u32 e = wg_excl_scan<QB>(d0, S.red32, &tot);  // mod 2^32: the sums are exact
-    const u32 v0 = e + d0;                               // estimate of bucket tid
-    const u32 off = wg_excl_scan<QB>(v0, S.red32, &tot);
-    if (tid < QNHB) S.cum[tid] = off;
+    const u32 e = wg_excl_scan<QB>(d0 + d1, S.red32, &tot);  // mod 2^32: the sums are exact
+    const u32 v0 = e + d0, v1 = e + d0 + d1;                  // estimates of the buckets
+    const u32 off = wg_excl_scan<QB>(QBPT > 1 ? v0 + v1 : v0, S.red32, &tot);
+    S.cum[QBPT * tid] = off;
+    if (QBPT > 1) S.cum[QBPT * tid + 1] = off + v0;
     if (tid == 0) S.cum[QNHB] = tot;
   }
   __syncthreads();
   const u32 dense = QD / 8 * QEST;  // estimated visits that make a window direct
   {
     const u32 wb = (QD >> bs) > 0 ? (QD >> bs) : 1;  // buckets of a direct window
-    const u32 b = tid;
-    const u32 bend = b + wb < nbk ? b + wb : nbk;
-    const bool dn = b < nbk && S.cum[bend] - S.cum[b] >= dense;
-    const u64 bal = __ballot(dn);
-    if (lane == 0 && wid < QNHB / WAVE) {
-      S.dbits[2 * wid] = (u32)bal;
-      S.dbits[2 * wid + 1] = (u32)(bal >> 32);
+#pragma unroll
+    for (u32 h2 = 0; h2 < QBPT; ++h2) {
+      const u32 b = tid + h2 * QB;
+      const u32 bend = b + wb < nbk ? b + wb : nbk;
+      const bool dn = b < nbk && S.cum[bend] - S.cum[b] >= dense;
+      const u64 bal = __ballot(dn);
+      if (lane == 0) {
+        S.dbits[(b >> 5)] = (u32)bal;
+        S.dbits[(b >> 5) + 1] = (u32)(bal >> 32);
+      }
     }
     __syncthreads();
     if (wid == 0) {
@@ -325,6 +371,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       if (lane == 0) S.dsum = (u32)b2;
     }
     if (tid == 0) S.ncont = 0;
+    if (tid < 2 * QW) S.wbl[tid / QW][tid % QW] = 0;
     __syncthreads();
   }
   // -- windows over [mn, mx]
@@ -333,7 +380,13 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
   u64 lo = mn;
   u64 hspan = end - mn;  // id span a hash window may take (halved after one fills)
   u64 last_hi = mn;      // end of the last window if it did not fill (cursors exact)
+  u32 par = 0;           // parity of the window (the wbl buffer it writes)
   while (lo < end) {
+    // (the same re-read per window: what derives from the thread index is
+    // recomputed here rather than held across windows)
+    asm volatile("" : "+v"(tid));
+    lane = tid & (WAVE - 1);
+    wid = tid / WAVE;
     const u32 b0 = (u32)((lo - mn) >> bs);
     const u64 dhi = lo + QD < end ? lo + QD : end;
     const u32 bde = (u32)((dhi - 1 - mn) >> bs) + 1;
@@ -359,58 +412,109 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     // each run's stretch: from its cursor (or, after a window that filled, the
     // sampled block holding its first pin >= lo) to the first sampled block
     // starting at or above hi
-    u32 L = 0, cur = 0;
-    if (tid < nr) {
-      const u32 g0 = S.rsp[tid], g1 = S.rsp[tid + 1];
-      const u32 ke = tid >> 1;
-      const u32 len = (tid & 1) ? S.elen[ke] - S.ens[ke] : S.ens[ke];
-      if (exact) {
-        cur = S.rcur[tid];
-      } else {
-        const u32 kb = q_lower_bound(S.sfirst, g0, g1, lo32);
-        cur = kb > g0 ? (kb - 1 - g0) << sh : 0;
+    // (thread tid holds hyperedge tid's source run 2 tid and destination run
+    // 2 tid + 1)
+    u32 L[2] = {0, 0}, cur[2] = {0, 0};
+    if (tid < deg) {
+#pragma unroll
+      for (u32 j = 0; j < 2; ++j) {
+        const u32 r = 2 * tid + j;
+        const u32 g0 = S.rsp[r], g1 = S.rsp[r + 1];
+        const u32 len = j ? S.elen[tid] - S.ens[tid] : S.ens[tid];
+        if (exact) {
+          cur[j] = S.rcur[r];
+        } else {
+          const u32 kb = q_lower_bound(S.sfirst, g0, g1, lo32);
+          cur[j] = kb > g0 ? (kb - 1 - g0) << sh : 0;
+        }
+        const u32 kh = q_lower_bound(S.sfirst, g0, g1, hi32);
+        const u32 e0 = ((kh - g0) << sh) < len ? ((kh - g0) << sh) : len;
+        L[j] = e0 > cur[j] ? e0 - cur[j] : 0;
       }
-      const u32 kh = q_lower_bound(S.sfirst, g0, g1, hi32);
-      const u32 e0 = ((kh - g0) << sh) < len ? ((kh - g0) << sh) : len;
-      L = e0 > cur ? e0 - cur : 0;
     }
-    u32 T, K;
-    const u32 po = wg_excl_scan<QB>(L, S.red32, &T);
-    const u32 ko = wg_excl_scan<QB>(L ? 1u : 0u, S.red32, &K);
-    T = rfl(T);
-    K = rfl(K);
-    if (L) {
-      const u32 ke = tid >> 1;
-      S.caddr[ko] = S.eoff[ke] + ((tid & 1) ? S.ens[ke] : 0) + cur - (i64)po;
-      S.cpre[ko] = po;
-      S.cq[ko] = S.q[ke];
-      S.cnext[ko] = L;
+    // one scan of (pins << 32 | non-empty): offsets and compacted indices
+    u64 tk;
+    const u64 pk = wg_excl_scan<QB, u64>(((u64)(L[0] + L[1]) << 32) |
+                                             ((L[0] ? 1u : 0u) + (L[1] ? 1u : 0u)),
+                                         S.red64, &tk);
+    const u32 T = rfl((u32)(tk >> 32)), K = rfl((u32)tk);
+    u32 po[2], ko[2];
+    po[0] = (u32)(pk >> 32);
+    ko[0] = (u32)pk;
+    po[1] = po[0] + L[0];
+    ko[1] = ko[0] + (L[0] ? 1u : 0u);
+#pragma unroll
+    for (u32 j = 0; j < 2; ++j) {
+      if (L[j]) {
+        S.caddr[ko[j]] = S.eoff[tid] + (j ? S.ens[tid] : 0) + cur[j] - (i64)po[j];
+        S.cpre[ko[j]] = po[j];
+        S.cq[ko[j]] = S.q[tid];
+        S.cnext[ko[j]] = L[j];
+      }
     }
     if (tid == 0) {
       S.cpre[K] = T;
       S.fail_min = 0xFFFFFFFFu;
       S.nkeys = 0;
     }
+    if (tid < QW) S.wvmax[tid] = 0;
     __syncthreads();
+    u32 vmax = 0;  // largest bin left by this thread's visits (Omega cannot bind)
     for (u32 c = 0; c < T; c += QCH) {
       const u32 cn = T - c < QCH ? T - c : QCH;
       const u32 nblk = (cn + WAVE - 1) / WAVE;
-      if (tid < nblk) S.bfirst[tid] = run_of(S.cpre, K, c + tid * WAVE);
+      // where the stretches start in this chunk: the stretch of position i is
+      // the one holding its wave block's first position plus the starts after
+      // that position and up to i
+      if (tid < nblk) {
+        S.bfirst[tid] = run_of(S.cpre, K, c + tid * WAVE);
+        S.sbits[tid] = 0;
+      }
       __syncthreads();
-      u32 v[QU], kk[QU];
+      for (u32 k = tid; k < K; k += QB) {
+        if (S.cpre[k] >= c && S.cpre[k] - c < cn) {
+          const u32 o = S.cpre[k] - c;
+          atomicOr((unsigned long long *)&S.sbits[o >> 6], 1ull << (o & 63));
+        }
+      }
+      __syncthreads();
+      // lane u (< QU) of the wave reads the first stretch and the start bits of
+      // the wave's block of u; every u then takes them from that lane into
+      // scalar registers, so one LDS read per pin remains (its stretch's
+      // address) and all of them issue before the first wait
+      static_assert(QU <= WAVE, "one lane per u");
+      const u32 myq = lane * QW + wid;
+      const u32 myc = lane < QU && myq < nblk ? myq : 0;
+      const u32 bf_l = S.bfirst[myc];
+      const u64 sb_l = S.sbits[myc];
+      // phase by phase for all u: stretch of each pin, its address, the pin
+      u32 kk[QU], v[QU];
+      u32 okm = 0;  // bit u: position of u is in the chunk
 #pragma unroll
       for (u32 u = 0; u < QU; ++u) {
         const u32 qb = u * QW + wid;
         const u32 i = c + qb * WAVE + lane;
         const bool ok = qb < nblk && i < T;
-        u32 k = ok ? S.bfirst[qb] : 0;
-        if (ok)
-          while (S.cpre[k + 1] <= i) ++k;
-        kk[u] = k;
-        const i64 pos = ok ? S.caddr[k] + (i64)i : 0;
-        const u32 x = A.e_pins[pos];
-        v[u] = ok ? x : 0xFFFFFFFFu;
+        const u32 k0 = __builtin_amdgcn_readlane(bf_l, u);
+        // starts at block positions 1 .. lane: the set bits of bits >> 1 below
+        // this lane (the lane-mask count)
+        const u32 blo = __builtin_amdgcn_readlane((u32)sb_l, u);
+        const u32 bhi = __builtin_amdgcn_readlane((u32)(sb_l >> 32), u);
+        const u32 k = k0 + __builtin_amdgcn_mbcnt_hi(bhi >> 1, __builtin_amdgcn_mbcnt_lo(
+                                                                   (blo >> 1) | (bhi << 31), 0u));
+        kk[u] = ok ? k : 0;
+        okm |= (ok ? 1u : 0u) << u;
       }
+      i64 ca[QU];
+#pragma unroll
+      for (u32 u = 0; u < QU; ++u) ca[u] = S.caddr[kk[u]];
+#pragma unroll
+      for (u32 u = 0; u < QU; ++u) {
+        const u32 i = c + (u * QW + wid) * WAVE + lane;
+        v[u] = A.e_pins[(okm >> u) & 1u ? ca[u] + (i64)i : 0];
+      }
+#pragma unroll
+      for (u32 u = 0; u < QU; ++u) v[u] = (okm >> u) & 1u ? v[u] : 0xFFFFFFFFu;
       // the first pin >= hi of each stretch (one lane per stretch and wave block)
 #pragma unroll
       for (u32 u = 0; u < QU; ++u) {
@@ -422,12 +526,29 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
           atomicMin(&S.cnext[kk[u]], i - S.cpre[kk[u]]);
         }
       }
-      if (direct) {
+      u32 qv[QU];
+#pragma unroll
+      for (u32 u = 0; u < QU; ++u) qv[u] = S.cq[kk[u]];
+      if (direct && om) {
 #pragma unroll
         for (u32 u = 0; u < QU; ++u) {
           const u32 x = v[u];
-          if (x >= lo32 && x < hi32 && x != n) atomicAdd(&S.t.bin[x - lo32], S.cq[kk[u]]);
+          if (x >= lo32 && x < hi32 && x != n) atomicAdd(&S.t.bin[x - lo32], qv[u]);
         }
+      } else if (direct) {
+        // every lane adds (0 to a slot of its own when its pin is not in the
+        // window), so the returned sums need no branch: each is a partial sum
+        // of some neighbour, a lower bound of its eta
+        u32 o[QU];
+#pragma unroll
+        for (u32 u = 0; u < QU; ++u) {
+          const u32 x = v[u];
+          const bool in = x >= lo32 && x < hi32 && x != n;
+          const u32 q = in ? qv[u] : 0;
+          o[u] = atomicAdd(&S.t.bin[in ? x - lo32 : lane], q) + q;
+        }
+#pragma unroll
+        for (u32 u = 0; u < QU; ++u) vmax = o[u] > vmax ? o[u] : vmax;
       } else {
 #pragma unroll
         for (u32 u = 0; u < QU; ++u) {
@@ -438,67 +559,98 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
               atomicMin(&S.fail_min, x);
               continue;
             }
-            atomicAdd(&S.t.h.bin[sl2], S.cq[kk[u]]);
+            const u32 q = qv[u];
+            const u32 o = atomicAdd(&S.t.h.bin[sl2], q) + q;
+            vmax = o > vmax ? o : vmax;
           }
         }
+      }
+      if (!om) {
+        u32 wv = vmax;
+#pragma unroll
+        for (int d = WAVE / 2; d > 0; d >>= 1) {
+          const u32 o = __shfl_xor(wv, d, WAVE);
+          wv = o > wv ? o : wv;
+        }
+        if (lane == 0) S.wvmax[wid] = wv;
       }
       __syncthreads();
     }
     // next cursors: exact first pin >= hi of every run
-    if (tid < nr) S.rcur[tid] = L ? cur + S.cnext[ko] : cur;
+    if (tid < deg) {
+#pragma unroll
+      for (u32 j = 0; j < 2; ++j) S.rcur[2 * tid + j] = L[j] ? cur[j] + S.cnext[ko[j]] : cur[j];
+    }
     const u32 fmin = rfl(S.fail_min);
     // candidates of the window: the largest valid bin, then the valid bins
     // that can still reach it; every slot is read and left empty
+    // the best lower bound of the windows before (their per-wave maxima were
+    // published by the barriers since)
+#pragma unroll
+    for (int w = 0; w < QW; ++w) lstar = umax64(lstar, S.wbl[par ^ 1][w]);
+    lstar = uni(lstar);
+    // candidates: the largest valid bin bounds the winner's eta + noise from
+    // below; the valid bins that can still reach that bound are judged.  Every
+    // slot is read and left empty.
+    u32 vstar = 0;
     u64 bl = 0;
-    if (direct) {
-      // pass 1: the largest valid bin (validity kept as a bit per slot)
-      constexpr u32 NS = QD / QB;
-      u32 vmax = 0, bad = 0;
-#pragma unroll 4
-      for (u32 j = 0; j < NS; ++j) {
-        const u32 V = S.t.bin[tid + j * QB];
-        bool ok = V != 0;
-        if (om && ok) ok = size_n + A.n_size[lo32 + tid + j * QB] <= A.omega;
-        if (!ok) bad |= 1u << j;
-        else vmax = V > vmax ? V : vmax;
+    if (om) {
+      // Omega can reject neighbours: the largest valid bin needs a pass of its own
+      if (direct) {
+        for (u32 j = 0; j < QD / QB; ++j) {
+          const u32 V = S.t.bin[tid + j * QB];
+          if (V && size_n + A.n_size[lo32 + tid + j * QB] <= A.omega) vstar = V > vstar ? V : vstar;
+        }
+      } else {
+        for (u32 j = 0; j < QHS / QB; ++j) {
+          const u32 key = S.t.h.key[tid + j * QB];
+          const u32 V = S.t.h.bin[tid + j * QB];
+          if (key != 0 && key - 1 < fmin && V && size_n + A.n_size[key - 1] <= A.omega)
+            vstar = V > vstar ? V : vstar;
+        }
       }
-      vmax = q_reduce<u32>(vmax, S.red32, [](u32 a, u32 b) { return a > b ? a : b; });
-      const u64 T2 = umax64((u64)vmax << s, lstar);
-      // pass 2: the bins that can still reach it; every slot left empty
+      vstar = q_reduce<u32>(vstar, S.red32, [](u32 a, u32 b) { return a > b ? a : b; });
+    } else {
+      // every neighbour is valid; the visits' returned sums gave the largest
+      // bin (a key dropped by a full hash window holds a partial sum, still a
+      // lower bound of a valid neighbour's eta)
+#pragma unroll
+      for (int w = 0; w < QW; ++w) vstar = S.wvmax[w] > vstar ? S.wvmax[w] : vstar;
+      vstar = uni(vstar);
+    }
+    const u64 T2 = umax64((u64)vstar << s, lstar);
+    if (direct) {
 #pragma unroll 4
-      for (u32 j = 0; j < NS; ++j) {
+      for (u32 j = 0; j < QD / QB; ++j) {
         const u32 sl2 = tid + j * QB;
         const u32 V = S.t.bin[sl2];
-        S.t.bin[sl2] = 0;
-        if (!((bad >> j) & 1u))
-          q_judge(A, S, n, lo32 + sl2, V, s, qmin, errunit, ub, T2, dmod, magic, bl);
+        if (V) {
+          S.t.bin[sl2] = 0;
+          const u32 m = lo32 + sl2;
+          if (!om || size_n + A.n_size[m] <= A.omega)
+            q_judge(A, S, n, m, V, s, qmin, errunit, ub, T2, dmod, magic, bl);
+        }
       }
     } else {
-      constexpr u32 NS = QHS / QB;
-      u32 vmax = 0, bad = 0;
 #pragma unroll 4
-      for (u32 j = 0; j < NS; ++j) {
+      for (u32 j = 0; j < QHS / QB; ++j) {
         const u32 sl2 = tid + j * QB;
         const u32 key = S.t.h.key[sl2];
-        const u32 V = S.t.h.bin[sl2];
-        bool ok = key != 0 && key - 1 < fmin && V != 0;
-        if (om && ok) ok = size_n + A.n_size[key - 1] <= A.omega;
-        if (!ok) bad |= 1u << j;
-        else vmax = V > vmax ? V : vmax;
-      }
-      vmax = q_reduce<u32>(vmax, S.red32, [](u32 a, u32 b) { return a > b ? a : b; });
-      const u64 T2 = umax64((u64)vmax << s, lstar);
-#pragma unroll 4
-      for (u32 j = 0; j < NS; ++j) {
-        const u32 sl2 = tid + j * QB;
-        const u32 key = S.t.h.key[sl2];
-        const u32 V = S.t.h.bin[sl2];
-        S.t.h.key[sl2] = 0;
-        S.t.h.bin[sl2] = 0;
-        if (!((bad >> j) & 1u)) q_judge(A, S, n, key - 1, V, s, qmin, errunit, ub, T2, dmod, magic, bl);
+        if (key) {
+          const u32 V = S.t.h.bin[sl2];
+          S.t.h.key[sl2] = 0;
+          S.t.h.bin[sl2] = 0;
+          const u32 m = key - 1;
+          if (m < fmin && V && (!om || size_n + A.n_size[m] <= A.omega))
+            q_judge(A, S, n, m, V, s, qmin, errunit, ub, T2, dmod, magic, bl);
+        }
       }
     }
-    lstar = umax64(lstar, q_reduce<u64>(bl, S.red64, [](u64 a, u64 b) { return umax64(a, b); }));
+    // this window's best lower bound, per wave (read after the next barrier)
+#pragma unroll
+    for (int d = WAVE / 2; d > 0; d >>= 1) bl = umax64(bl, __shfl_xor(bl, d, WAVE));
+    if (lane == 0) S.wbl[par][wid] = bl;
+    par ^= 1;
     const bool full = !direct && fmin < hi32;
     last_hi = full ? ~0ull : hi;
     if (!direct) {
@@ -510,9 +662,13 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     }
     lo = rfl64(full ? (u64)fmin : hi);
     hspan = rfl64(hspan);
-    // the reduction's barriers order the slot clears before the next window's
-    // visits and the reads of fail_min before its reset
+    // the next window's scan barriers order the slot clears before its
+    // visits, and the reads of fail_min, wvmax and wbl before their reuse
   }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < QW; ++w) lstar = umax64(lstar, S.wbl[par ^ 1][w]);
+  lstar = uni(lstar);
   const u32 nc = rfl(S.ncont);
   if (nc > QCONT) return false;
   // -- exact eta of the contenders still in reach: t(e) summed over the

@@ -246,6 +246,30 @@ int chp_refine_moves(chp_ctx *ctx, const chp_hgraph *g, uint32_t *rho, uint32_t 
                      uint32_t *seq, int64_t *seq_gain, uint32_t *seq_viol, uint32_t *n_seq_host,
                      uint32_t *n_applied_host, int64_t *gain_host);
 
+/* project_partition ([HP] Sec. III: the partition of a level is carried to
+ * the level below through that level's coarsening map).
+ *  gamma[n_fine]       coarse id of every node of the finer graph, as written
+ *                      by chp_contract.
+ *  rho_coarse[n_coarse] partition of every coarse node.
+ *  rho_fine[n_fine]    written: rho_coarse[gamma[n]].
+ * Errors: EINVAL (null pointer, some gamma[n] >= n_coarse).  Synchronises. */
+int chp_project_partition(chp_ctx *ctx, uint32_t n_fine, const uint32_t *gamma, uint32_t n_coarse,
+                          const uint32_t *rho_coarse, uint32_t *rho_fine);
+
+/* refine_level: the refinement of one level of the uncoarsening ([HP]
+ * Sec. VI-A: the proposal and the application of moves repeat theta times
+ * per level, 16 by default; Sec. VI-B: the first half of the repetitions may
+ * propose moves that overfill a partition, the second half only moves that fit
+ * Omega, and every application keeps only valid prefixes).  Pass r runs
+ * chp_propose_moves(enforce_omega = r >= theta / 2), then chp_refine_moves
+ * with the context's move order, on rho[N] in place (partitions in [0, k)).
+ *  *n_applied_host  moves applied over the passes;
+ *  *gain_host       their summed in-sequence gain (the connectivity drop).
+ * Errors: those of the two calls.  Synchronises. */
+int chp_refine_level(chp_ctx *ctx, const chp_hgraph *g, uint32_t *rho, uint32_t k,
+                     const chp_params *prm, uint32_t theta, uint32_t *n_applied_host,
+                     int64_t *gain_host);
+
 /* pair_leftovers: best-effort pairing of the nodes left without a partner
  * ([HP] Sec. V-C, last mechanism), run after chp_rate_and_match.
  *  target[N]  as written by chp_rate_and_match (read).

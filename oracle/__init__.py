@@ -393,6 +393,43 @@ def refine_pass(g: Graph, rho, k, omega, delta, enforce_omega=False,
     return refine(g, rho, k, omega, delta, mv, gn, chained)
 
 
+def refine_level(g: Graph, rho, k, omega, delta, theta=16, chained=True):
+    """The refinement of one level ([P1] Sec. VI-A: theta repetitions of
+    proposal and application; Sec. VI-B: the first half proposes without the
+    size limit, the second half within it).  Returns (rho after the passes,
+    moves applied, summed gain)."""
+    r = np.ascontiguousarray(rho, np.uint32)
+    applied = gain = 0
+    for p in range(theta):
+        ref = refine_pass(g, r, k, omega, delta, enforce_omega=p >= theta // 2, chained=chained)
+        r = ref.rho
+        applied += ref.n_applied
+        gain += ref.gain
+    return r, applied, gain
+
+
+def uncoarsen(levels, g0: Graph, omega, delta, theta=16, on_level=None):
+    """The uncoarsening phase of [P1] Sec. III: the coarsest level's nodes are
+    the initial partitions (rho = identity there, k their number); each level
+    from the coarsest down is refined (refine_level), then its partition is
+    projected to the level below through that level's coarsening map.
+    `levels` is coarsen()'s list (its last entry may have no pairs).
+    on_level(depth, graph, rho) after each level's refinement.  Returns the
+    partition of g0 and k."""
+    graphs = [g0] + [lv.coarse for lv in levels if lv.n_pairs]
+    gammas = [lv.gamma for lv in levels if lv.n_pairs]
+    top = graphs[-1]
+    k = top.n_nodes
+    rho = np.arange(k, dtype=np.uint32)
+    for d in range(len(graphs) - 1, -1, -1):
+        rho, _, _ = refine_level(graphs[d], rho, k, omega, delta, theta)
+        if on_level:
+            on_level(d, graphs[d], rho)
+        if d:
+            rho = rho[gammas[d - 1]]
+    return rho, k
+
+
 LEFTOVER_WINDOW = 64  # positions a leftover node scans below its slack position
 
 

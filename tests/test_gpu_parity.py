@@ -421,6 +421,67 @@ def test_handshake_long_chains(chp, ctx, pi):
         assert "jump_round" in tm and "jump_finish" in tm, sorted(tm)
 
 
+@pytest.mark.parametrize("cfg,nn,theta", [(1, None, 16), (4, 5000, 8), (2, 2000, 1),
+                                           (5, 2048, 2)])
+def test_uncoarsening_vcycle(chp, ctx, cfg, nn, theta):
+    """The whole V-cycle ([HP] Sec. III): coarsening as the benchmark runs it
+    (leftover pairing, the stall rule), every level compared with the oracle;
+    then the coarsest level's nodes as the initial partitions, every level
+    from the coarsest down refined by theta passes (the first half proposing
+    without Omega) and projected to the level below; the partition after every
+    level's refinement, and the moves and gain it applied, equal the
+    oracle's."""
+    import torch
+    spec = synth.config(cfg, n_nodes=nn)
+    h = synth.generate(spec)
+    say("vcycle", cfg, nn, theta)
+    dg, og = both(chp, ctx, h, spec.omega, spec.delta)
+    dgs, ogs, dgam, ogam = [dg], [og], [], []
+    floor_nodes = -(-int(h.n_size.astype(np.uint64).sum()) // spec.omega)
+    for lvl in range(64):
+        g = ogs[-1]
+        if (spec.target_nodes and g.n_nodes < spec.target_nodes) or g.n_nodes <= floor_nodes:
+            break
+        cg, lv, gamma = run_level_pair(chp, ctx, dgs[-1], g, spec.omega, spec.delta, True,
+                                       spec.seed, tag="vcycle %d L%d" % (cfg, lvl),
+                                       leftovers=True)
+        if cg is None:
+            break
+        dgs.append(cg)
+        ogs.append(lv.coarse)
+        dgam.append(gamma)
+        ogam.append(lv.gamma)
+        if lv.n_pairs < 0.001 * g.n_nodes:
+            break
+    k = ogs[-1].n_nodes
+    rho_d = torch.arange(k, dtype=torch.int32, device=ctx.device)
+    rho_o = np.arange(k, dtype=np.uint32)
+    for d in range(len(dgs) - 1, -1, -1):
+        na, ga = ctx.refine_level(dgs[d], rho_d, k, spec.omega, spec.delta, theta)
+        rho_o, oa, og_ = oracle.refine_level(ogs[d], rho_o, k, spec.omega, spec.delta, theta)
+        assert_equal(chp.to_host(rho_d, np.uint32), rho_o, "vcycle %d depth %d rho" % (cfg, d))
+        assert (na, ga) == (oa, og_), (d, na, ga, oa, og_)
+        if d:
+            rho_d = ctx.project_partition(dgam[d - 1], rho_d, dgs[d].n_nodes)
+            rho_o = rho_o[ogam[d - 1]]
+            assert_equal(chp.to_host(rho_d, np.uint32), rho_o, "vcycle %d depth %d projected"
+                         % (cfg, d - 1))
+    eval_pair(chp, ctx, dg, og, rho_o, k, spec.omega, spec.delta, "vcycle %d final" % cfg)
+
+
+def test_project_partition_errors(chp, ctx):
+    """A coarse id out of range is refused."""
+    import torch
+    gamma = chp.to_device(np.array([0, 1, 5], dtype=np.uint32))
+    rho = chp.to_device(np.array([2, 3], dtype=np.uint32))
+    with pytest.raises(chp.ChpError) as ei:
+        ctx.project_partition(gamma, rho, 2)
+    assert ei.value.code == chp.EINVAL
+    out = ctx.project_partition(gamma[:2], rho, 2)
+    assert chp.to_host(out, np.uint32).tolist() == [2, 3]
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("pi", [2, 4])
 def test_top_pi_tiny(chp, ctx, pi):
     """Top-pi lists and pi matching rounds on the tiny graphs under the limit

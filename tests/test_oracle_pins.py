@@ -409,6 +409,46 @@ def test_coarsen_stall_rule():
             assert np.array_equal(a.match, b.match) and a.n_pairs == b.n_pairs
 
 
+@pytest.mark.parametrize("cfg,nn,theta", [(4, 2000, 4), (4, 3000, 8), (1, None, 4)])
+def test_uncoarsen_invariants(cfg, nn, theta):
+    """The uncoarsening driver against the evaluator: the coarsest level's
+    identity partition is valid, projection keeps every partition's size,
+    inbound count and the connectivity (evaluated on the finer graph), each
+    level's refinement lowers the connectivity by exactly the gains it
+    applied and never leaves a partition invalid."""
+    spec = synth.config(cfg, n_nodes=nn)
+    h = synth.generate(spec)
+    g0 = load(h, spec.omega, spec.delta)
+    levels, _, _ = oracle.coarsen(g0, spec.omega, spec.delta, spec.target_nodes, 64, True,
+                                  spec.seed, leftovers=True)
+    graphs = [g0] + [lv.coarse for lv in levels if lv.n_pairs]
+    gammas = [lv.gamma for lv in levels if lv.n_pairs]
+    k = graphs[-1].n_nodes
+    rho = np.arange(k, dtype=np.uint32)
+    prev = oracle.evaluate(graphs[-1], rho, k, spec.omega, spec.delta)
+    assert int(prev[2][2]) == 0 and int(prev[2][3]) == 0
+    seen = []
+    for d in range(len(graphs) - 1, -1, -1):
+        g = graphs[d]
+        before = oracle.evaluate(g, rho, k, spec.omega, spec.delta)
+        # projection keeps sizes, inbound counts and connectivity
+        assert np.array_equal(before[0], prev[0]) and np.array_equal(before[1], prev[1])
+        assert int(before[2][0]) == int(prev[2][0])
+        rho2, applied, gain = oracle.refine_level(g, rho, k, spec.omega, spec.delta, theta)
+        after = oracle.evaluate(g, rho2, k, spec.omega, spec.delta)
+        assert int(before[2][0]) - int(after[2][0]) == gain and gain >= 0
+        assert int(after[2][2]) == 0 and int(after[2][3]) == 0
+        seen.append(rho2.copy())
+        prev = after
+        rho = rho2[gammas[d - 1]] if d else rho2
+    # moves were applied somewhere (these workloads have improving moves)
+    assert any(not np.array_equal(a, b) for a, b in zip(seen[1:], [
+        r[gm] for r, gm in zip(seen[:-1], reversed(gammas))]))
+    # the driver composes the same steps
+    got, kk = oracle.uncoarsen(levels, g0, spec.omega, spec.delta, theta)
+    assert kk == k and np.array_equal(got, rho)
+
+
 # ---------------------------------------------------------------- error paths
 def err_code(edges, n, w=None, sizes=None, omega=BIG, delta=BIG):
     h = synth.from_lists(n, edges, w, sizes)
