@@ -661,7 +661,8 @@ void launch_rate_inc(chp_ctx *c, const RateArgs &a, const NodeRec *recs, const u
                      const u32 *gmax, u32 *work, u32 host_count, u32 hash_keys) {
   if (!host_count) return;
   const u32 g = host_count < c->n_cu ? host_count : c->n_cu;
-  const u32 hcap = hash_keys && hash_keys < FCAP ? hash_keys : FCAP;
+  // (at least 2: a window of one id then never fills)
+  const u32 hcap = hash_keys && hash_keys < FCAP ? (hash_keys < 2 ? 2 : hash_keys) : FCAP;
   if (a.pi > 1)
     CHP_LAUNCH(c, "rate_inc", k_rate_inc<RATE_MAX_PI>, g, FB, 0, a, recs, cnt, gmax, work, hcap);
   else

@@ -20,6 +20,15 @@
 // target.  The result is the exact argmax of the definition; the bounds only
 // decide how few neighbours need their exact sum.
 //
+// The windows run from the first dense one to the largest id, then from the
+// smallest id up to that window, so that in most graphs the neighbours that
+// share the most hyperedges with n (the dense ids) bound the winner first.
+// Once a valid neighbour's lower bound is known, a sparse window is a sketch:
+// its bins are indexed by a hash of the id and hold no keys, and a bin's sum
+// bounds the quantised sum of every id that falls in it.  When no bin can
+// reach the best lower bound, no id of the window can win and the window is
+// done; otherwise the same window is visited again with a hash table.
+//
 // Run stretches are exact at their start: every run carries its cursor, the
 // first pin at or above the window's low end, found during the visits of the
 // window before (the first pin at or above that window's end).  Only the end
@@ -47,6 +56,7 @@ constexpr u32 QNHB = 1024;            // estimate buckets
 constexpr u32 QBS_MIN = 12;           // log2 of the narrowest bucket
 constexpr u32 QHTGT = QCAP * 3 / 4;   // estimated visits a hash window aims at
 constexpr u32 QEST = 16;              // estimates count sixteenths of a visit
+constexpr u32 QSK = 12288;            // estimated visits a sketch window aims at
 constexpr u32 QU = 16384 / QB;        // pins per thread per chunk
 constexpr u32 QCH = QB * QU;          // pins per chunk
 constexpr u32 QNBLK = QCH / WAVE;     // wave blocks per chunk
@@ -112,6 +122,7 @@ __device__ __forceinline__ u32 uni(u32 v) { return rfl(v); }
 __device__ __forceinline__ u64 uni(u64 v) { return rfl64(v); }
 
 __device__ __forceinline__ u32 qslot(u32 m) { return (u32)(((u64)(m * 0x9E3779B1u) * QHS) >> 32); }
+__device__ __forceinline__ u32 qsketch(u32 m) { return (u32)(((u64)(m * 0x9E3779B1u) * QD) >> 32); }
 
 // Slot of m in the hash table, claimed if absent; QFAIL when the table has
 // reached its claim limit hcap and m is not in it.
@@ -374,37 +385,60 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     if (tid < 2 * QW) S.wbl[tid / QW][tid % QW] = 0;
     __syncthreads();
   }
-  // -- windows over [mn, mx]
+  // -- windows over [mn, mx]: from the first dense window to mx, then from mn
+  // up to that window, so that the dense ones (in most graphs the best
+  // neighbours) set a high bound before the sparse ones are visited
   u64 lstar = 0;  // best lower bound of eta + noise so far (a valid neighbour's)
   const u64 end = (u64)mx + 1;
-  u64 lo = mn;
+  const u32 bd0 = q_first_dense(S, 0, nbk);
+  const u64 start = bd0 < nbk ? (u64)mn + ((u64)bd0 << bs) : (u64)mn;
+  u64 lo = start, wend = end;
+  bool wrapped = start == mn;
   u64 hspan = end - mn;  // id span a hash window may take (halved after one fills)
-  u64 last_hi = mn;      // end of the last window if it did not fill (cursors exact)
+  u64 last_hi = start == mn ? mn : ~0ull;  // end of the last window if it did not fill
   u32 par = 0;           // parity of the window (the wbl buffer it writes)
-  while (lo < end) {
+  bool redo = false;     // the last window was a sketch with a hot slot: hash it
+  for (;;) {
+    if (lo >= wend) {
+      if (wrapped) break;
+      wrapped = true;
+      lo = mn;
+      wend = start;
+      last_hi = mn;
+      if (tid < deg) {  // every pin is >= mn: the cursors restart at the runs' starts
+        S.rcur[2 * tid] = 0;
+        S.rcur[2 * tid + 1] = 0;
+      }
+    }
     // (the same re-read per window: what derives from the thread index is
     // recomputed here rather than held across windows)
     asm volatile("" : "+v"(tid));
     lane = tid & (WAVE - 1);
     wid = tid / WAVE;
     const u32 b0 = (u32)((lo - mn) >> bs);
-    const u64 dhi = lo + QD < end ? lo + QD : end;
+    const u64 dhi = lo + QD < wend ? lo + QD : wend;
     const u32 bde = (u32)((dhi - 1 - mn) >> bs) + 1;
     const u32 est = S.cum[bde < nbk ? bde : nbk] - S.cum[b0];
     const bool direct =
         rfl(est >= dense || S.cum[b0 + 1] - S.cum[b0] > QHTGT * QEST ? 1u : 0u) != 0;
+    // a sparse window is a sketch (bins indexed by a hash of the id, no keys)
+    // once some valid neighbour bounds the winner from below: every id of a
+    // slot whose sum cannot reach that bound is out of the running
+    const bool sk = !direct && lstar != 0 && !redo;
     u64 hi = dhi;
     if (!direct) {
+      const u32 tgt = (sk ? QSK : QHTGT) * QEST;
       u32 l = b0 + 1, r = nbk;
       while (l < r) {
         const u32 mid = (l + r + 1) >> 1;
-        if (S.cum[mid] - S.cum[b0] <= QHTGT * QEST) l = mid;
+        if (S.cum[mid] - S.cum[b0] <= tgt) l = mid;
         else r = mid - 1;
       }
       const u32 bd = q_first_dense(S, b0 + 1, nbk);
       const u32 b1 = bd < l ? bd : l;
-      hi = b1 >= nbk ? end : (u64)mn + ((u64)b1 << bs);
-      if (hi - lo > hspan) hi = lo + hspan;
+      hi = b1 >= nbk ? wend : (u64)mn + ((u64)b1 << bs);
+      hi = hi < wend ? hi : wend;
+      if (!sk && hi - lo > hspan) hi = lo + hspan;
     }
     hi = rfl64(hi);
     const u32 lo32 = (u32)lo, hi32 = (u32)(hi < 0xFFFFFFFFull ? hi : 0xFFFFFFFFull);
@@ -535,6 +569,12 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
           const u32 x = v[u];
           if (x >= lo32 && x < hi32 && x != n) atomicAdd(&S.t.bin[x - lo32], qv[u]);
         }
+      } else if (sk) {
+#pragma unroll
+        for (u32 u = 0; u < QU; ++u) {
+          const u32 x = v[u];
+          if (x >= lo32 && x < hi32 && x != n) atomicAdd(&S.t.bin[qsketch(x)], qv[u]);
+        }
       } else if (direct) {
         // every lane adds (0 to a slot of its own when its pin is not in the
         // window), so the returned sums need no branch: each is a partial sum
@@ -565,7 +605,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
           }
         }
       }
-      if (!om) {
+      if (!om && !sk) {
         u32 wv = vmax;
 #pragma unroll
         for (int d = WAVE / 2; d > 0; d >>= 1) {
@@ -576,6 +616,36 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       }
       __syncthreads();
     }
+    if (sk) {
+      // the sketch: a slot whose sum, as an upper bound for every id in it,
+      // can reach the best lower bound makes the window a hash window (from
+      // the same cursors); every slot is read and left empty
+#pragma unroll
+      for (int w = 0; w < QW; ++w) lstar = umax64(lstar, S.wbl[par ^ 1][w]);
+      lstar = uni(lstar);
+      u32 hot = 0;
+#pragma unroll 4
+      for (u32 j = 0; j < QD / QB; ++j) {
+        const u32 sl2 = tid + j * QB;
+        const u32 V = S.t.bin[sl2];
+        if (V) {
+          S.t.bin[sl2] = 0;
+          if (((u64)V << s) + (u64)(V / qmin) * errunit + ub >= lstar) hot = 1;
+        }
+      }
+      hot = q_reduce<u32>(hot, S.red32, [](u32 a, u32 b) { return a | b; });
+      redo = hot != 0;
+      if (!redo) {
+        if (tid < deg) {
+#pragma unroll
+          for (u32 j = 0; j < 2; ++j) S.rcur[2 * tid + j] = L[j] ? cur[j] + S.cnext[ko[j]] : cur[j];
+        }
+        last_hi = hi;  // (the cursors found above are exact in any case)
+        lo = hi;
+      }
+      continue;
+    }
+    redo = false;
     // next cursors: exact first pin >= hi of every run
     if (tid < deg) {
 #pragma unroll

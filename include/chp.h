@@ -363,8 +363,8 @@ int chp_set_matching(chp_ctx *ctx, int mode);
  * same target and score.  min_visits 0 restores the default (16384);
  * UINT64_MAX sends every node through the lists.  hash_keys caps the keys a
  * sparse window may claim before it stops and the next window resumes at the
- * first id it could not hold (0 = the table's capacity, 4608): a lower cap
- * only adds windows; the results do not change. */
+ * first id it could not hold (0 = the table's capacity, 4608; 1 is taken as
+ * 2): a lower cap only adds windows; the results do not change. */
 int chp_set_incidence_rating(chp_ctx *ctx, uint64_t min_visits, uint32_t hash_keys);
 
 /* Bins of the rating from the incidence (chp_set_incidence_rating).
