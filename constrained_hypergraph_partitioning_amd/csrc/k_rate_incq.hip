@@ -1,4 +1,4 @@
-// Rating straight from the incidence with 32-bit bins: candidate proposal
+// Rating straight from the incidence with quantised bins: candidate proposal
 // ("Hypergraph Partitioning on GPU with Distinct Incident Hyperedges and Size
 // Constraints", Sec. V-A Eqs. 5-6 and Sec. V-C) for nodes of a graph whose
 // neighbour lists are not held in memory (Sec. VII-C), when Delta cannot reject
@@ -6,11 +6,12 @@
 //
 // Windows over the node's neighbour ids are visited as in k_rate_inc.hip (a
 // sample of every run steers dense windows, slot m - lo, and sparse ones, a
-// hash table), but a bin holds a 32-bit sum of the quantised terms
-// q(e) = t(e) >> s, where s is the smallest shift that keeps the node's whole
-// term sum below 2^32.  A bin is then twice as small as an exact 64-bit eta,
-// so a window covers twice the ids.  The bins only bound eta: with V the bin
-// and c the number of hyperedges n and m share (at most V / q_min),
+// hash table), but a bin holds a sum of the quantised terms q(e) = t(e) >> s,
+// where s is the smallest shift that keeps the node's whole term sum below
+// 2^16.  A direct window's bin then takes 16 bits, two ids to a 32-bit word,
+// so it covers four times the ids of an exact 64-bit eta (the hash and sketch
+// windows keep 32-bit bins).  The bins only bound eta: with V the bin and c
+// the number of hyperedges n and m share (at most V / q_min),
 //     V << s  <=  eta(n, m)  <=  (V << s) + c * (2^s - 1).
 // Each window keeps every valid neighbour whose upper bound (noise at most the
 // cap) can still reach the best lower bound seen so far: the contenders.  At
@@ -46,7 +47,8 @@ namespace {
 
 constexpr int QB = 1024;              // threads per node
 constexpr int QW = QB / WAVE;
-constexpr u32 QD = 24576;             // ids of a direct window (one u32 bin each)
+constexpr u32 QD = 24576;             // 32-bit words of the bins
+constexpr u32 QDD = 2 * QD;           // ids of a direct window (a 16-bit bin each)
 constexpr u32 QHS = QD / 2;           // slots of the hash table (key, bin)
 constexpr u32 QCAP = QHS * 3 / 4;     // keys a hash window claims before it reports full
 constexpr u32 QE = 384;               // incident hyperedges
@@ -212,6 +214,19 @@ __device__ __forceinline__ void q_reduce2(T &v1, T &v2, T *lds, Op1 op1, Op2 op2
   v2 = uni(r2);
 }
 
+// A bin value below which no bin can reach T: every V < q_vthr(...) has
+// (V << s) + floor(V / qmin) * errunit + ub < T.  The real bound
+// V * (2^s + errunit / qmin) + ub is at least that sum, so V below
+// x = (T - ub) / (2^s + errunit / qmin) cannot reach T; floor(x) - 1 keeps
+// the double's rounding of x on the safe side.  Bins at or above it are
+// judged exactly.
+__device__ __forceinline__ u32 q_vthr(u64 T, u32 s, u32 qmin, u64 errunit, u64 ub) {
+  if (T <= ub) return 0;
+  const double x = (double)(T - ub) / ((double)(1ull << s) + (double)errunit / (double)qmin);
+  const double f = floor(x) - 1.0;
+  return f <= 0.0 ? 0u : f >= 4294967295.0 ? 0xFFFFFFFFu : (u32)f;
+}
+
 // One candidate m with bin value V (valid, V > 0): judged against the
 // threshold T; a contender is appended, the thread's best lower bound kept.
 __device__ __forceinline__ void q_judge(const RateArgs &A, QSmem &S, u32 n, u32 m, u32 V, u32 s,
@@ -276,8 +291,10 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     }
     return true;
   }
-  // the bit length of tsum >> 32, so that tsum >> s < 2^32
-  const u32 s = tsum >> 32 ? 64u - (u32)__builtin_clzll(tsum >> 32) : 0u;
+  // the bit length of tsum >> 16, so that tsum >> s < 2^16: no id's sum of
+  // quantised terms reaches 2^16, so a direct window packs two ids' bins in
+  // each 32-bit word (its adds never carry from one half into the other)
+  const u32 s = tsum >> 16 ? 64u - (u32)__builtin_clzll(tsum >> 16) : 0u;
   const u32 qmin = (u32)(tmin >> s);
   if (tsum && qmin == 0) return false;
   const u64 errunit = (1ull << s) - 1;
@@ -362,9 +379,9 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     if (tid == 0) S.cum[QNHB] = tot;
   }
   __syncthreads();
-  const u32 dense = QD / 8 * QEST;  // estimated visits that make a window direct
+  const u32 dense = QDD / 8 * QEST;  // estimated visits that make a window direct
   {
-    const u32 wb = (QD >> bs) > 0 ? (QD >> bs) : 1;  // buckets of a direct window
+    const u32 wb = (QDD >> bs) > 0 ? (QDD >> bs) : 1;  // buckets of a direct window
 #pragma unroll
     for (u32 h2 = 0; h2 < QBPT; ++h2) {
       const u32 b = tid + h2 * QB;
@@ -416,7 +433,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     lane = tid & (WAVE - 1);
     wid = tid / WAVE;
     const u32 b0 = (u32)((lo - mn) >> bs);
-    const u64 dhi = lo + QD < wend ? lo + QD : wend;
+    const u64 dhi = lo + QDD < wend ? lo + QDD : wend;
     const u32 bde = (u32)((dhi - 1 - mn) >> bs) + 1;
     const u32 est = S.cum[bde < nbk ? bde : nbk] - S.cum[b0];
     const bool direct =
@@ -424,10 +441,10 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     // a sparse window is a sketch (bins indexed by a hash of the id, no keys)
     // once some valid neighbour bounds the winner from below: every id of a
     // slot whose sum cannot reach that bound is out of the running
-    const bool sk = !direct && lstar != 0 && !redo;
+    const bool sk0 = !direct && lstar != 0 && !redo;
     u64 hi = dhi;
     if (!direct) {
-      const u32 tgt = (sk ? QSK : QHTGT) * QEST;
+      const u32 tgt = (sk0 ? QSK : QHTGT) * QEST;
       u32 l = b0 + 1, r = nbk;
       while (l < r) {
         const u32 mid = (l + r + 1) >> 1;
@@ -438,7 +455,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       const u32 b1 = bd < l ? bd : l;
       hi = b1 >= nbk ? wend : (u64)mn + ((u64)b1 << bs);
       hi = hi < wend ? hi : wend;
-      if (!sk && hi - lo > hspan) hi = lo + hspan;
+      if (!sk0 && hi - lo > hspan) hi = lo + hspan;
     }
     hi = rfl64(hi);
     const u32 lo32 = (u32)lo, hi32 = (u32)(hi < 0xFFFFFFFFull ? hi : 0xFFFFFFFFull);
@@ -472,6 +489,9 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
                                              ((L[0] ? 1u : 0u) + (L[1] ? 1u : 0u)),
                                          S.red64, &tk);
     const u32 T = rfl((u32)(tk >> 32)), K = rfl((u32)tk);
+    // a sketch slot's sum stays below 2^32: each of fewer than 2^16 pins adds
+    // less than 2^16 (otherwise the window takes the hash table)
+    const bool sk = sk0 && T < (1u << 16);
     u32 po[2], ko[2];
     po[0] = (u32)(pk >> 32);
     ko[0] = (u32)pk;
@@ -567,7 +587,8 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
 #pragma unroll
         for (u32 u = 0; u < QU; ++u) {
           const u32 x = v[u];
-          if (x >= lo32 && x < hi32 && x != n) atomicAdd(&S.t.bin[x - lo32], qv[u]);
+          if (x >= lo32 && x < hi32 && x != n)
+            atomicAdd(&S.t.bin[(x - lo32) >> 1], qv[u] << (((x - lo32) & 1u) << 4));
         }
       } else if (sk) {
 #pragma unroll
@@ -584,8 +605,9 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
         for (u32 u = 0; u < QU; ++u) {
           const u32 x = v[u];
           const bool in = x >= lo32 && x < hi32 && x != n;
-          const u32 q = in ? qv[u] : 0;
-          o[u] = atomicAdd(&S.t.bin[in ? x - lo32 : lane], q) + q;
+          const u32 h = in ? ((x - lo32) & 1u) << 4 : 0u;
+          const u32 q = in ? qv[u] << h : 0;
+          o[u] = ((atomicAdd(&S.t.bin[in ? (x - lo32) >> 1 : lane], q) + q) >> h) & 0xFFFFu;
         }
 #pragma unroll
         for (u32 u = 0; u < QU; ++u) vmax = o[u] > vmax ? o[u] : vmax;
@@ -623,14 +645,17 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
 #pragma unroll
       for (int w = 0; w < QW; ++w) lstar = umax64(lstar, S.wbl[par ^ 1][w]);
       lstar = uni(lstar);
+      // (a slot at or above the real-valued bound counts as hot: at worst a
+      // window more is hashed)
       u32 hot = 0;
+      const u32 vthr = q_vthr(lstar, s, qmin, errunit, ub);
 #pragma unroll 4
       for (u32 j = 0; j < QD / QB; ++j) {
         const u32 sl2 = tid + j * QB;
         const u32 V = S.t.bin[sl2];
         if (V) {
           S.t.bin[sl2] = 0;
-          if (((u64)V << s) + (u64)(V / qmin) * errunit + ub >= lstar) hot = 1;
+          if (V >= vthr) hot = 1;
         }
       }
       hot = q_reduce<u32>(hot, S.red32, [](u32 a, u32 b) { return a | b; });
@@ -668,8 +693,11 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       // Omega can reject neighbours: the largest valid bin needs a pass of its own
       if (direct) {
         for (u32 j = 0; j < QD / QB; ++j) {
-          const u32 V = S.t.bin[tid + j * QB];
-          if (V && size_n + A.n_size[lo32 + tid + j * QB] <= A.omega) vstar = V > vstar ? V : vstar;
+          const u32 w = S.t.bin[tid + j * QB];
+          const u32 m = lo32 + 2 * (tid + j * QB);
+          const u32 V0 = w & 0xFFFFu, V1 = w >> 16;
+          if (V0 && size_n + A.n_size[m] <= A.omega) vstar = V0 > vstar ? V0 : vstar;
+          if (V1 && size_n + A.n_size[m + 1] <= A.omega) vstar = V1 > vstar ? V1 : vstar;
         }
       } else {
         for (u32 j = 0; j < QHS / QB; ++j) {
@@ -689,16 +717,21 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       vstar = uni(vstar);
     }
     const u64 T2 = umax64((u64)vstar << s, lstar);
+    const u32 vthr = q_vthr(T2, s, qmin, errunit, ub);
     if (direct) {
 #pragma unroll 4
       for (u32 j = 0; j < QD / QB; ++j) {
         const u32 sl2 = tid + j * QB;
-        const u32 V = S.t.bin[sl2];
-        if (V) {
+        const u32 w = S.t.bin[sl2];
+        if (w) {
           S.t.bin[sl2] = 0;
-          const u32 m = lo32 + sl2;
-          if (!om || size_n + A.n_size[m] <= A.omega)
-            q_judge(A, S, n, m, V, s, qmin, errunit, ub, T2, dmod, magic, bl);
+#pragma unroll
+          for (u32 b = 0; b < 2; ++b) {
+            const u32 V = (w >> (16 * b)) & 0xFFFFu;
+            const u32 m = lo32 + 2 * sl2 + b;
+            if (V && V >= vthr && (!om || size_n + A.n_size[m] <= A.omega))
+              q_judge(A, S, n, m, V, s, qmin, errunit, ub, T2, dmod, magic, bl);
+          }
         }
       }
     } else {
@@ -711,7 +744,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
           S.t.h.key[sl2] = 0;
           S.t.h.bin[sl2] = 0;
           const u32 m = key - 1;
-          if (m < fmin && V && (!om || size_n + A.n_size[m] <= A.omega))
+          if (m < fmin && V && V >= vthr && (!om || size_n + A.n_size[m] <= A.omega))
             q_judge(A, S, n, m, V, s, qmin, errunit, ub, T2, dmod, magic, bl);
         }
       }

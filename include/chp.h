@@ -368,15 +368,17 @@ int chp_set_matching(chp_ctx *ctx, int mode);
 int chp_set_incidence_rating(chp_ctx *ctx, uint64_t min_visits, uint32_t hash_keys);
 
 /* Bins of the rating from the incidence (chp_set_incidence_rating).
- * CHP_INC_BINS_32 (the default): for a node whose Delta cannot reject any
- *   neighbour (|in(n)| + the largest |in| of the graph <= delta) and with
- *   pi == 1, each bin holds a 32-bit sum of the terms t(e) shifted right by
- *   the smallest s that keeps the node's term sum below 2^32, so an LDS window
- *   covers twice the ids; those sums bound eta from below and above, and the
- *   neighbours whose bounds can still reach the best get their exact eta
- *   (t(e) summed over the hyperedges n and m share) at the node's end.  Other
- *   nodes (and one whose quantised terms would lose a hyperedge, or with more
- *   than 256 neighbours in reach) go to the 64-bit bins.
+ * CHP_INC_BINS_32 (the default; quantised bins in 32-bit LDS words): for a
+ *   node whose Delta cannot reject any neighbour (|in(n)| + the largest |in|
+ *   of the graph <= delta) and with pi == 1, each bin holds a sum of the terms
+ *   t(e) shifted right by the smallest s that keeps the node's term sum below
+ *   2^16, two ids to a word in dense id windows (four times the ids of the
+ *   64-bit bins); sparse windows hash ids into 32-bit slots.  Those sums bound
+ *   eta from below and above, and the neighbours whose bounds can still reach
+ *   the best get their exact eta (t(e) summed over the hyperedges n and m
+ *   share) at the node's end.  Other nodes (and one whose quantised terms
+ *   would lose a hyperedge, or with more than 256 neighbours in reach) go to
+ *   the 64-bit bins.
  * CHP_INC_BINS_64: every node through 64-bit bins of exact eta.
  * Both give the same target and score.  EINVAL for another value. */
 #define CHP_INC_BINS_32 0
