@@ -850,8 +850,9 @@ void rate_batched(chp_ctx *c, Scratch &s, const chp_hgraph *g, const RateArgs &a
   i64 last = 0;
   if (prev) read_many(c, {{&last, nboff + prev, sizeof last}});
   c->last_nb_built = (u64)(built + last);
-  if (nf && a.pi == 1 && c->inc_bins == CHP_INC_BINS_32) {
-    // 32-bit bins first; the nodes they cannot rate go to the 64-bit kernel
+  if (nf && a.pi == 1 && c->inc_bins == CHP_INC_BINS_32 && g->n_pins < (1ull << 31)) {
+    // quantised bins first (their stretch addresses take 32 bits); the nodes
+    // they cannot rate go to the 64-bit kernel
     NodeRec *spill = s.get<NodeRec>(nf);
     u32 *sc = s.get<u32>(2);  // spill count, work counter of the second launch
     launch_fill_u32(c, sc, 2, 0);

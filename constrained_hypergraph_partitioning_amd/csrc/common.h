@@ -11,6 +11,7 @@
 typedef uint32_t u32;
 typedef uint64_t u64;
 typedef int64_t i64;
+typedef int32_t i32;
 
 #define NONE32 0xFFFFFFFFu
 #define FX_SHIFT 40

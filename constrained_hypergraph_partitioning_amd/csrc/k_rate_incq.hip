@@ -91,12 +91,13 @@ struct QSmem {
   u32 rsp[QRUNS + 1];  // first sample of each run
   u32 sfirst[QSMAX];   // first pin of each sampled block
   // the window's non-empty stretches
-  i64 caddr[QRUNS];    // e_pins index of flat position 0 of stretch k
+  i32 caddr[QRUNS];    // e_pins index of flat position 0 of stretch k (fewer than 2^31 pins)
   u32 cpre[QRUNS + 1];
   u32 cq[QRUNS];
   u32 cnext[QRUNS];    // stretch index of its first pin at or above the window's end
-  u32 bfirst[QNBLK];   // stretch of the first pin of each wave block of a chunk
-  u64 sbits[QNBLK];    // bit p of word b: a stretch starts at chunk position 64 b + p
+  // two buffers: chunk c's and, built while chunk c is visited, chunk c + 1's
+  u32 bfirst[2][QNBLK];  // stretch of the first pin of each wave block of a chunk
+  u64 sbits[2][QNBLK];   // bit p of word b: a stretch starts at chunk position 64 b + p
   u32 cum[QNHB + 1];   // estimated visits below each bucket (sixteenths)
   u32 dbits[32];       // bucket b starts a dense window
   u32 dsum;            // dbits word w is not zero
@@ -157,6 +158,21 @@ __device__ __forceinline__ u32 q_lower_bound(const u32 *a, u32 lo, u32 hi, u32 v
   }
   return lo;
 }
+
+// largest i in [0, n) with pre[i] <= v (pre[0] <= v, pre ascending, n <= 2^STEPS),
+// in STEPS fixed steps
+template <u32 STEPS>
+__device__ __forceinline__ u32 q_run_of(const u32 *pre, u32 n, u32 v) {
+  u32 lo = 0;
+#pragma unroll
+  for (int b = (int)STEPS - 1; b >= 0; --b) {
+    const u32 mid = lo + (1u << b);
+    if (mid < n && pre[mid] <= v) lo = mid;
+  }
+  return lo;
+}
+constexpr u32 QRUN_STEPS = 10;
+static_assert(QRUNS <= (1u << QRUN_STEPS), "stretches in QRUN_STEPS steps");
 
 // first bucket >= b that starts a dense window, else nbk
 __device__ __forceinline__ u32 q_first_dense(const QSmem &S, u32 b, u32 nbk) {
@@ -497,13 +513,20 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     ko[0] = (u32)pk;
     po[1] = po[0] + L[0];
     ko[1] = ko[0] + (L[0] ? 1u : 0u);
+    // (and the first chunk's stretch starts: the wave blocks whose first
+    // position the stretch holds, and its start bit; the words are clear)
 #pragma unroll
     for (u32 j = 0; j < 2; ++j) {
       if (L[j]) {
-        S.caddr[ko[j]] = S.eoff[tid] + (j ? S.ens[tid] : 0) + cur[j] - (i64)po[j];
+        S.caddr[ko[j]] = (i32)(S.eoff[tid] + (j ? S.ens[tid] : 0) + cur[j] - (i64)po[j]);
         S.cpre[ko[j]] = po[j];
         S.cq[ko[j]] = S.q[tid];
         S.cnext[ko[j]] = L[j];
+        const u32 pe = po[j] + L[j];
+        for (u32 b = (po[j] + WAVE - 1) / WAVE; b < QNBLK && b * WAVE < pe; ++b)
+          S.bfirst[0][b] = ko[j];
+        if (po[j] < QCH)
+          atomicOr((unsigned long long *)&S.sbits[0][po[j] >> 6], 1ull << (po[j] & 63));
       }
     }
     if (tid == 0) {
@@ -514,24 +537,25 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     if (tid < QW) S.wvmax[tid] = 0;
     __syncthreads();
     u32 vmax = 0;  // largest bin left by this thread's visits (Omega cannot bind)
-    for (u32 c = 0; c < T; c += QCH) {
+    u32 cb = 0;    // buffer of this chunk's stretch starts
+    for (u32 c = 0; c < T; c += QCH, cb ^= 1) {
       const u32 cn = T - c < QCH ? T - c : QCH;
       const u32 nblk = (cn + WAVE - 1) / WAVE;
-      // where the stretches start in this chunk: the stretch of position i is
-      // the one holding its wave block's first position plus the starts after
-      // that position and up to i
-      if (tid < nblk) {
-        S.bfirst[tid] = run_of(S.cpre, K, c + tid * WAVE);
-        S.sbits[tid] = 0;
-      }
-      __syncthreads();
-      for (u32 k = tid; k < K; k += QB) {
-        if (S.cpre[k] >= c && S.cpre[k] - c < cn) {
-          const u32 o = S.cpre[k] - c;
-          atomicOr((unsigned long long *)&S.sbits[o >> 6], 1ull << (o & 63));
+      // where the stretches start in the next chunk, into the other buffer
+      // (cleared by the lanes that read it, two chunks ago): the stretch of
+      // position i is the one holding its wave block's first position plus
+      // the starts after that position and up to i
+      if (c + QCH < T) {
+        const u32 c2 = c + QCH, cn2 = T - c2 < QCH ? T - c2 : QCH;
+        if (tid < (cn2 + WAVE - 1) / WAVE)
+          S.bfirst[cb ^ 1][tid] = q_run_of<QRUN_STEPS>(S.cpre, K, c2 + tid * WAVE);
+        for (u32 k = tid; k < K; k += QB) {
+          const u32 p = S.cpre[k];
+          if (p >= c2 && p - c2 < cn2)
+            atomicOr((unsigned long long *)&S.sbits[cb ^ 1][(p - c2) >> 6],
+                     1ull << ((p - c2) & 63));
         }
       }
-      __syncthreads();
       // lane u (< QU) of the wave reads the first stretch and the start bits of
       // the wave's block of u; every u then takes them from that lane into
       // scalar registers, so one LDS read per pin remains (its stretch's
@@ -539,8 +563,9 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       static_assert(QU <= WAVE, "one lane per u");
       const u32 myq = lane * QW + wid;
       const u32 myc = lane < QU && myq < nblk ? myq : 0;
-      const u32 bf_l = S.bfirst[myc];
-      const u64 sb_l = S.sbits[myc];
+      const u32 bf_l = S.bfirst[cb][myc];
+      const u64 sb_l = S.sbits[cb][myc];
+      if (lane < QU && myq < nblk) S.sbits[cb][myq] = 0;  // read once: left clear
       // phase by phase for all u: stretch of each pin, its address, the pin
       u32 kk[QU], v[QU];
       u32 okm = 0;  // bit u: position of u is in the chunk
@@ -559,13 +584,13 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
         kk[u] = ok ? k : 0;
         okm |= (ok ? 1u : 0u) << u;
       }
-      i64 ca[QU];
+      i32 ca[QU];
 #pragma unroll
       for (u32 u = 0; u < QU; ++u) ca[u] = S.caddr[kk[u]];
 #pragma unroll
       for (u32 u = 0; u < QU; ++u) {
         const u32 i = c + (u * QW + wid) * WAVE + lane;
-        v[u] = A.e_pins[(okm >> u) & 1u ? ca[u] + (i64)i : 0];
+        v[u] = A.e_pins[(okm >> u) & 1u ? (u32)(ca[u] + (i32)i) : 0u];
       }
 #pragma unroll
       for (u32 u = 0; u < QU; ++u) v[u] = (okm >> u) & 1u ? v[u] : 0xFFFFFFFFu;
@@ -824,6 +849,8 @@ __global__ __launch_bounds__(QB) void k_rate_incq(RateArgs A, const NodeRec *rec
   const u32 max_size = gmax[0], max_nin = gmax[1];
   const u32 total = *cnt;
   for (u32 i = tid; i < QD; i += QB) S.t.bin[i] = 0;
+  // the start bits are left clear by their readers from here on
+  for (u32 i = tid; i < 2 * QNBLK; i += QB) S.sbits[i / QNBLK][i % QNBLK] = 0;
   for (;;) {
     if (tid == 0) S.item = atomicAdd(work, 1u);
     __syncthreads();
