@@ -94,7 +94,7 @@ struct QSmem {
   i32 caddr[QRUNS];    // e_pins index of flat position 0 of stretch k (fewer than 2^31 pins)
   u32 cpre[QRUNS + 1];
   u32 cq[QRUNS];
-  u32 cnext[QRUNS];    // stretch index of its first pin at or above the window's end
+  u32 cnext[QRUNS];    // flat position of stretch k's first pin at or above the window's end
   // two buffers: chunk c's and, built while chunk c is visited, chunk c + 1's
   u32 bfirst[2][QNBLK];  // stretch of the first pin of each wave block of a chunk
   u64 sbits[2][QNBLK];   // bit p of word b: a stretch starts at chunk position 64 b + p
@@ -521,7 +521,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
         S.caddr[ko[j]] = (i32)(S.eoff[tid] + (j ? S.ens[tid] : 0) + cur[j] - (i64)po[j]);
         S.cpre[ko[j]] = po[j];
         S.cq[ko[j]] = S.q[tid];
-        S.cnext[ko[j]] = L[j];
+        S.cnext[ko[j]] = po[j] + L[j];
         const u32 pe = po[j] + L[j];
         for (u32 b = (po[j] + WAVE - 1) / WAVE; b < QNBLK && b * WAVE < pe; ++b)
           S.bfirst[0][b] = ko[j];
@@ -566,60 +566,63 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       const u32 bf_l = S.bfirst[cb][myc];
       const u64 sb_l = S.sbits[cb][myc];
       if (lane < QU && myq < nblk) S.sbits[cb][myq] = 0;  // read once: left clear
-      // phase by phase for all u: stretch of each pin, its address, the pin
+      // phase by phase for all u: stretch of each pin, its address, the pin.
+      // The block of u starts at flat position pb(u) = c + (u QW + ws) 64 and
+      // holds room(u) positions of the chunk (scalar values); lane < room(u)
+      // says the lane's position is in the chunk
+      const u32 ws = rfl(wid);
+      auto pbase = [&](u32 u) { return c + (u * QW + ws) * WAVE; };
+      auto room = [&](u32 u) {
+        return u * QW + ws < nblk && pbase(u) < T ? T - pbase(u) : 0u;
+      };
       u32 kk[QU], v[QU];
-      u32 okm = 0;  // bit u: position of u is in the chunk
 #pragma unroll
       for (u32 u = 0; u < QU; ++u) {
-        const u32 qb = u * QW + wid;
-        const u32 i = c + qb * WAVE + lane;
-        const bool ok = qb < nblk && i < T;
         const u32 k0 = __builtin_amdgcn_readlane(bf_l, u);
         // starts at block positions 1 .. lane: the set bits of bits >> 1 below
         // this lane (the lane-mask count)
-        const u32 blo = __builtin_amdgcn_readlane((u32)sb_l, u);
-        const u32 bhi = __builtin_amdgcn_readlane((u32)(sb_l >> 32), u);
-        const u32 k = k0 + __builtin_amdgcn_mbcnt_hi(bhi >> 1, __builtin_amdgcn_mbcnt_lo(
-                                                                   (blo >> 1) | (bhi << 31), 0u));
-        kk[u] = ok ? k : 0;
-        okm |= (ok ? 1u : 0u) << u;
+        const u64 sb = ((u64)(u32)__builtin_amdgcn_readlane((u32)(sb_l >> 32), u) << 32 |
+                        (u32)__builtin_amdgcn_readlane((u32)sb_l, u)) >> 1;
+        const u32 k = k0 + __builtin_amdgcn_mbcnt_hi((u32)(sb >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((u32)sb, 0u));
+        kk[u] = lane < room(u) ? k : 0;
       }
       i32 ca[QU];
 #pragma unroll
       for (u32 u = 0; u < QU; ++u) ca[u] = S.caddr[kk[u]];
 #pragma unroll
-      for (u32 u = 0; u < QU; ++u) {
-        const u32 i = c + (u * QW + wid) * WAVE + lane;
-        v[u] = A.e_pins[(okm >> u) & 1u ? (u32)(ca[u] + (i32)i) : 0u];
-      }
+      for (u32 u = 0; u < QU; ++u)
+        v[u] = A.e_pins[lane < room(u) ? (u32)(ca[u] + (i32)(pbase(u) + lane)) : 0u];
 #pragma unroll
-      for (u32 u = 0; u < QU; ++u) v[u] = (okm >> u) & 1u ? v[u] : 0xFFFFFFFFu;
-      // the first pin >= hi of each stretch (one lane per stretch and wave block)
+      for (u32 u = 0; u < QU; ++u) v[u] = lane < room(u) ? v[u] : 0xFFFFFFFFu;
+      // the first pin >= hi of each stretch: a lane whose pin is >= hi while
+      // the lane before holds a pin < hi of the same stretch does not qualify
+      // (one lane per stretch and wave block; the block's first position
+      // counts as a stretch start)
 #pragma unroll
       for (u32 u = 0; u < QU; ++u) {
-        const bool bey = v[u] != 0xFFFFFFFFu && v[u] >= hi32;
-        const u32 tag = bey ? kk[u] : 0xFFFFFFFFu;
-        const u32 ptag = __shfl_up(tag, 1, WAVE);
-        if (bey && (lane == 0 || ptag != kk[u])) {
-          const u32 i = c + (u * QW + wid) * WAVE + lane;
-          atomicMin(&S.cnext[kk[u]], i - S.cpre[kk[u]]);
-        }
+        const u64 B = __builtin_amdgcn_ballot_w64(v[u] != 0xFFFFFFFFu && v[u] >= hi32);
+        const u64 st = ((u64)(u32)__builtin_amdgcn_readlane((u32)(sb_l >> 32), u) << 32 |
+                        (u32)__builtin_amdgcn_readlane((u32)sb_l, u)) | 1ull;
+        const u64 first = B & ~((B << 1) & ~st);
+        if (__builtin_amdgcn_inverse_ballot_w64(first))
+          atomicMin(&S.cnext[kk[u]], pbase(u) + lane);
       }
       u32 qv[QU];
 #pragma unroll
       for (u32 u = 0; u < QU; ++u) qv[u] = S.cq[kk[u]];
+      const u32 span = hi32 - lo32;
       if (direct && om) {
 #pragma unroll
         for (u32 u = 0; u < QU; ++u) {
-          const u32 x = v[u];
-          if (x >= lo32 && x < hi32 && x != n)
-            atomicAdd(&S.t.bin[(x - lo32) >> 1], qv[u] << (((x - lo32) & 1u) << 4));
+          const u32 r = v[u] - lo32;
+          if (r < span && v[u] != n) atomicAdd(&S.t.bin[r >> 1], qv[u] << ((r & 1u) << 4));
         }
       } else if (sk) {
 #pragma unroll
         for (u32 u = 0; u < QU; ++u) {
           const u32 x = v[u];
-          if (x >= lo32 && x < hi32 && x != n) atomicAdd(&S.t.bin[qsketch(x)], qv[u]);
+          if (x - lo32 < span && x != n) atomicAdd(&S.t.bin[qsketch(x)], qv[u]);
         }
       } else if (direct) {
         // every lane adds (0 to a slot of its own when its pin is not in the
@@ -628,11 +631,11 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
         u32 o[QU];
 #pragma unroll
         for (u32 u = 0; u < QU; ++u) {
-          const u32 x = v[u];
-          const bool in = x >= lo32 && x < hi32 && x != n;
-          const u32 h = in ? ((x - lo32) & 1u) << 4 : 0u;
+          const u32 r = v[u] - lo32;
+          const bool in = r < span && v[u] != n;
+          const u32 h = (r & 1u) << 4;  // (any half of slot lane when not in)
           const u32 q = in ? qv[u] << h : 0;
-          o[u] = ((atomicAdd(&S.t.bin[in ? (x - lo32) >> 1 : lane], q) + q) >> h) & 0xFFFFu;
+          o[u] = __builtin_amdgcn_ubfe(atomicAdd(&S.t.bin[in ? r >> 1 : lane], q) + q, h, 16);
         }
 #pragma unroll
         for (u32 u = 0; u < QU; ++u) vmax = o[u] > vmax ? o[u] : vmax;
@@ -688,7 +691,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       if (!redo) {
         if (tid < deg) {
 #pragma unroll
-          for (u32 j = 0; j < 2; ++j) S.rcur[2 * tid + j] = L[j] ? cur[j] + S.cnext[ko[j]] : cur[j];
+          for (u32 j = 0; j < 2; ++j) S.rcur[2 * tid + j] = L[j] ? cur[j] + (S.cnext[ko[j]] - po[j]) : cur[j];
         }
         last_hi = hi;  // (the cursors found above are exact in any case)
         lo = hi;
@@ -699,7 +702,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     // next cursors: exact first pin >= hi of every run
     if (tid < deg) {
 #pragma unroll
-      for (u32 j = 0; j < 2; ++j) S.rcur[2 * tid + j] = L[j] ? cur[j] + S.cnext[ko[j]] : cur[j];
+      for (u32 j = 0; j < 2; ++j) S.rcur[2 * tid + j] = L[j] ? cur[j] + (S.cnext[ko[j]] - po[j]) : cur[j];
     }
     const u32 fmin = rfl(S.fail_min);
     // candidates of the window: the largest valid bin, then the valid bins
