@@ -70,9 +70,23 @@ constexpr u32 QBPT = QNHB / QB;       // estimate buckets per thread
 static_assert(QNHB % QB == 0 && QBPT <= 2 && QNHB == 32 * 32,
               "one or two buckets per thread; two-level dense bitmap");
 static_assert(QD % QB == 0 && QHS % QB == 0 && QSMAX % QB == 0, "slots per thread");
+static_assert(QD % (4 * QB) == 0 && QHS % (4 * QB) == 0, "four slots per thread and step");
+
+typedef unsigned short q_u16x2 __attribute__((ext_vector_type(2)));
+// the slots (4 words from w0, 16-byte aligned) read and left empty
+__device__ __forceinline__ uint4 q_take4(u32 *a, u32 w0) {
+  const uint4 x = *reinterpret_cast<const uint4 *>(a + w0);
+  *reinterpret_cast<uint4 *>(a + w0) = make_uint4(0u, 0u, 0u, 0u);
+  return x;
+}
+// some 16-bit half of w is above vt (packed saturating subtraction)
+__device__ __forceinline__ bool q_half_above(u32 w, u32 vt) {
+  const q_u16x2 t = {(unsigned short)vt, (unsigned short)vt};
+  return __builtin_bit_cast(u32, __builtin_elementwise_sub_sat(__builtin_bit_cast(q_u16x2, w), t)) != 0;
+}
 
 struct QSmem {
-  union {
+  union alignas(16) {
     u32 bin[QD];
     struct {
       u32 key[QHS];  // m + 1, 0 = empty
@@ -677,14 +691,11 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       // window more is hashed)
       u32 hot = 0;
       const u32 vthr = q_vthr(lstar, s, qmin, errunit, ub);
-#pragma unroll 4
-      for (u32 j = 0; j < QD / QB; ++j) {
-        const u32 sl2 = tid + j * QB;
-        const u32 V = S.t.bin[sl2];
-        if (V) {
-          S.t.bin[sl2] = 0;
-          if (V >= vthr) hot = 1;
-        }
+      const u32 vt = vthr ? vthr - 1 : 0;  // a non-empty slot of at least vthr: above vt
+#pragma unroll
+      for (u32 j = 0; j < QD / (4 * QB); ++j) {
+        const uint4 x = q_take4(S.t.bin, 4 * (tid + j * QB));
+        hot |= (x.x > vt) | (x.y > vt) | (x.z > vt) | (x.w > vt);
       }
       hot = q_reduce<u32>(hot, S.red32, [](u32 a, u32 b) { return a | b; });
       redo = hot != 0;
@@ -746,34 +757,39 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     }
     const u64 T2 = umax64((u64)vstar << s, lstar);
     const u32 vthr = q_vthr(T2, s, qmin, errunit, ub);
+    // (four slots per thread and step; a slot is looked at only when its
+    // value, or one of its two 16-bit bins, is non-zero and reaches vthr)
+    const u32 vt = vthr ? vthr - 1 : 0;
     if (direct) {
-#pragma unroll 4
-      for (u32 j = 0; j < QD / QB; ++j) {
-        const u32 sl2 = tid + j * QB;
-        const u32 w = S.t.bin[sl2];
-        if (w) {
-          S.t.bin[sl2] = 0;
+      const u32 vt16 = vt < 0xFFFFu ? vt : 0xFFFFu;
+#pragma unroll 1
+      for (u32 j = 0; j < QD / (4 * QB); ++j) {
+        const u32 w0 = 4 * (tid + j * QB);
+        const uint4 x = q_take4(S.t.bin, w0);
+        const u32 xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (u32 e = 0; e < 4; ++e) {
+          if (!q_half_above(xs[e], vt16)) continue;
 #pragma unroll
           for (u32 b = 0; b < 2; ++b) {
-            const u32 V = (w >> (16 * b)) & 0xFFFFu;
-            const u32 m = lo32 + 2 * sl2 + b;
-            if (V && V >= vthr && (!om || size_n + A.n_size[m] <= A.omega))
+            const u32 V = (xs[e] >> (16 * b)) & 0xFFFFu;
+            const u32 m = lo32 + 2 * (w0 + e) + b;
+            if (V > vt && (!om || size_n + A.n_size[m] <= A.omega))
               q_judge(A, S, n, m, V, s, qmin, errunit, ub, T2, dmod, magic, bl);
           }
         }
       }
     } else {
-#pragma unroll 4
-      for (u32 j = 0; j < QHS / QB; ++j) {
-        const u32 sl2 = tid + j * QB;
-        const u32 key = S.t.h.key[sl2];
-        if (key) {
-          const u32 V = S.t.h.bin[sl2];
-          S.t.h.key[sl2] = 0;
-          S.t.h.bin[sl2] = 0;
-          const u32 m = key - 1;
-          if (m < fmin && V && V >= vthr && (!om || size_n + A.n_size[m] <= A.omega))
-            q_judge(A, S, n, m, V, s, qmin, errunit, ub, T2, dmod, magic, bl);
+#pragma unroll 1
+      for (u32 j = 0; j < QHS / (4 * QB); ++j) {
+        const u32 w0 = 4 * (tid + j * QB);
+        const uint4 kx = q_take4(S.t.h.key, w0), bx = q_take4(S.t.h.bin, w0);
+        const u32 ks[4] = {kx.x, kx.y, kx.z, kx.w}, vs[4] = {bx.x, bx.y, bx.z, bx.w};
+#pragma unroll
+        for (u32 e = 0; e < 4; ++e) {
+          const u32 m = ks[e] - 1;  // (a key of 0: no id, m = 0xFFFFFFFF >= fmin)
+          if (m < fmin && vs[e] > vt && (!om || size_n + A.n_size[m] <= A.omega))
+            q_judge(A, S, n, m, vs[e], s, qmin, errunit, ub, T2, dmod, magic, bl);
         }
       }
     }
