@@ -141,7 +141,7 @@ def check_digests(rec, got, tag):
     assert fullsize.sha("part_inb", got["part_inb"]) == ev["part_inb"], tag + " part inbound"
 
 
-@pytest.mark.parametrize("cfg", [3, 4])
+@pytest.mark.parametrize("cfg", [3, 4, 5])
 def test_fullsize_vs_stored_oracle(chp, ctx, cfg):
     """Workloads 3 (two levels), 4 (the whole coarsening) and 5 (one level)
     at full size, as the benchmark runs them, against the oracle's digests."""
