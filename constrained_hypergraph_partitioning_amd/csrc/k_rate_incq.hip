@@ -163,6 +163,31 @@ __device__ __forceinline__ u32 q_insert(QSmem &S, u32 m, u32 hcap) {
   }
 }
 
+// The node's hyperedges, hashed into the emptied bins for the contenders'
+// exact sums: slot i is the 16 bytes from word 4 i, (e + 1, 0, t(e) low, high)
+constexpr u32 QEH = 2048;
+static_assert(4 * QEH <= QD && QE <= QEH / 4, "the hyperedge table fits the bins, a quarter full");
+__device__ __forceinline__ u32 q_eslot(u32 e) { return (e * 0x9E3779B1u) >> 21; }
+static_assert(QEH == 1u << 11, "slot hash");
+
+// e's slot, claimed (the hyperedges of a node are distinct)
+__device__ __forceinline__ u32 q_einsert(QSmem &S, u32 e, u64 te) {
+  u32 i = q_eslot(e);
+  while (atomicCAS(&S.t.bin[4 * i], 0u, e + 1) != 0) i = (i + 1) & (QEH - 1);
+  S.t.bin[4 * i + 2] = (u32)te;
+  S.t.bin[4 * i + 3] = (u32)(te >> 32);
+  return i;
+}
+
+// t(e) if e is one of the node's hyperedges, else 0
+__device__ __forceinline__ u64 q_efind(const QSmem &S, u32 e) {
+  for (u32 i = q_eslot(e);; i = (i + 1) & (QEH - 1)) {
+    const uint4 x = *reinterpret_cast<const uint4 *>(&S.t.bin[4 * i]);
+    if (x.x == e + 1) return (u64)x.w << 32 | x.z;
+    if (x.x == 0) return 0;
+  }
+}
+
 // first index in a[lo, hi) with a[i] >= v (LDS)
 __device__ __forceinline__ u32 q_lower_bound(const u32 *a, u32 lo, u32 hi, u32 v) {
   while (lo < hi) {
@@ -474,12 +499,21 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     const bool sk0 = !direct && lstar != 0 && !redo;
     u64 hi = dhi;
     if (!direct) {
+      // the last bucket l in [b0 + 1, nbk] whose estimate from b0 stays within
+      // tgt (b0 + 1 when none does), 64 candidates a step, one per lane (the
+      // estimates grow with l, so the lanes that hold are a prefix)
       const u32 tgt = (sk0 ? QSK : QHTGT) * QEST;
+      const u32 cb0 = S.cum[b0];
       u32 l = b0 + 1, r = nbk;
       while (l < r) {
-        const u32 mid = (l + r + 1) >> 1;
-        if (S.cum[mid] - S.cum[b0] <= tgt) l = mid;
-        else r = mid - 1;
+        const u32 step = (r - l + WAVE) / WAVE;
+        const u32 idx = l + lane * step;
+        const u32 cnt = (u32)__builtin_popcountll(
+            __builtin_amdgcn_ballot_w64(idx <= r && S.cum[idx] - cb0 <= tgt));
+        if (cnt == 0) break;
+        l += (cnt - 1) * step;
+        r = l + step - 1 < r ? l + step - 1 : r;
+        if (step == 1) break;
       }
       const u32 bd = q_first_dense(S, b0 + 1, nbk);
       const u32 b1 = bd < l ? bd : l;
@@ -819,24 +853,37 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
   const u32 nc = rfl(S.ncont);
   if (nc > QCONT) return false;
   // -- exact eta of the contenders still in reach: t(e) summed over the
-  // hyperedges of I(m) that are in I(n); the best by (eta + noise, -id)
+  // hyperedges of I(m) that are in I(n); the best by (eta + noise, -id).
+  // I(n) is hashed into the bins (empty after the windows, and left empty)
   u64 be = 0;
   u32 bi = NONE32;
-  for (u32 j = wid; j < nc; j += QW) {
-    const u32 m = S.cid[j];
-    if (S.cub[j] < lstar) continue;
-    const i64 a = A.n_off[m], b = A.n_off[m + 1];
-    u64 sum = 0;
-    for (i64 p = a + lane; p < b; p += WAVE) {
-      const u32 e = A.n_inc[p];
-      u32 k = q_lower_bound(S.eid, 0, nin, e);
-      if (k == nin || S.eid[k] != e) k = q_lower_bound(S.eid, nin, deg, e);
-      if (k < deg && S.eid[k] == e) sum += S.tx[k];
-    }
+  if (nc) {
+    u32 mine = QFAIL;
+    if (tid < deg) mine = q_einsert(S, S.eid[tid], S.tx[tid]);
+    __syncthreads();
+    for (u32 j = wid; j < nc; j += QW) {
+      const u32 m = S.cid[j];
+      if (S.cub[j] < lstar) continue;
+      const i64 a = A.n_off[m], b = A.n_off[m + 1];
+      u64 sum = 0;
+      for (i64 p0 = a; p0 < b; p0 += 4 * WAVE) {
+        u32 e4[4];  // (four loads in flight per lane)
 #pragma unroll
-    for (int d = WAVE / 2; d > 0; d >>= 1) sum += __shfl_xor(sum, d, WAVE);
-    const u64 key = sum + (A.noise_on ? pair_noise(A.seed, n, m, dmod, magic) : 0);
-    if (better(key, m, be, bi)) be = key, bi = m;
+        for (u32 i = 0; i < 4; ++i) {
+          const i64 p = p0 + i * WAVE + lane;
+          e4[i] = p < b ? A.n_inc[p] : 0xFFFFFFFFu;
+        }
+#pragma unroll
+        for (u32 i = 0; i < 4; ++i)
+          if (e4[i] != 0xFFFFFFFFu) sum += q_efind(S, e4[i]);
+      }
+#pragma unroll
+      for (int d = WAVE / 2; d > 0; d >>= 1) sum += __shfl_xor(sum, d, WAVE);
+      const u64 key = sum + (A.noise_on ? pair_noise(A.seed, n, m, dmod, magic) : 0);
+      if (better(key, m, be, bi)) be = key, bi = m;
+    }
+    __syncthreads();
+    if (mine != QFAIL) *reinterpret_cast<uint4 *>(&S.t.bin[4 * mine]) = make_uint4(0u, 0u, 0u, 0u);
   }
   if (lane == 0) {
     S.red64[wid] = be;
