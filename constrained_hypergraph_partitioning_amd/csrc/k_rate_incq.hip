@@ -114,7 +114,7 @@ struct QSmem {
   u64 sbits[2][QNBLK];   // bit p of word b: a stretch starts at chunk position 64 b + p
   u32 cum[QNHB + 1];   // estimated visits below each bucket (sixteenths)
   u32 dbits[32];       // bucket b starts a dense window
-  u32 dsum;            // dbits word w is not zero
+
   u32 cid[QCONT];      // contenders: id, upper bound of eta + noise
   u64 cub[QCONT];
   u64 red64[QW + 1];
@@ -214,14 +214,14 @@ constexpr u32 QRUN_STEPS = 10;
 static_assert(QRUNS <= (1u << QRUN_STEPS), "stretches in QRUN_STEPS steps");
 
 // first bucket >= b that starts a dense window, else nbk
-__device__ __forceinline__ u32 q_first_dense(const QSmem &S, u32 b, u32 nbk) {
+__device__ __forceinline__ u32 q_first_dense(const QSmem &S, u32 dsum, u32 b, u32 nbk) {
   if (b >= nbk) return nbk;
   u32 w = b >> 5;
   u32 m = S.dbits[w] & (~0u << (b & 31));
   if (!m) {
     const u32 ws = w + 1;
     if (ws >= 32) return nbk;
-    const u32 m2 = S.dsum & (~0u << ws);
+    const u32 m2 = dsum & (~0u << ws);
     if (!m2) return nbk;
     w = (u32)__builtin_ctz(m2);
     m = S.dbits[w];
@@ -230,7 +230,10 @@ __device__ __forceinline__ u32 q_first_dense(const QSmem &S, u32 b, u32 nbk) {
   return r < nbk ? r : nbk;
 }
 
-template <typename T, typename Op>
+// Workgroup reductions and scans over the per-wave partials in lds.  With
+// TRAIL false they end without the barrier that protects lds from the next
+// writer: the caller then uses another buffer before the next barrier.
+template <bool TRAIL = true, typename T, typename Op>
 __device__ __forceinline__ T q_reduce(T v, T *lds, Op op) {
 #pragma unroll
   for (int d = WAVE / 2; d > 0; d >>= 1) v = op(v, (T)__shfl_xor(v, d, WAVE));
@@ -239,14 +242,31 @@ __device__ __forceinline__ T q_reduce(T v, T *lds, Op op) {
   T r = lds[0];
 #pragma unroll
   for (int w = 1; w < QW; ++w) r = op(r, lds[w]);
-  __syncthreads();
+  if (TRAIL) __syncthreads();
   return uni(r);
+}
+
+// exclusive prefix of v over the workgroup, *total the sum (lds: QW entries)
+template <typename T>
+__device__ __forceinline__ T q_scan(T v, T *lds, T *total) {
+  const T inc = wave_incl_scan(v);
+  if (lane_id() == WAVE - 1) lds[wave_id()] = inc;
+  __syncthreads();
+  T off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < QW; ++w) {
+    const T x = lds[w];
+    off += w < (int)wave_id() ? x : (T)0;
+    tot += x;
+  }
+  *total = tot;
+  return off + inc - v;
 }
 
 __device__ __forceinline__ u64 umax64(u64 a, u64 b) { return a > b ? a : b; }
 
 // Two reductions over the workgroup with one pair of barriers; lds holds 2 QW.
-template <typename T, typename Op1, typename Op2>
+template <bool TRAIL = true, typename T, typename Op1, typename Op2>
 __device__ __forceinline__ void q_reduce2(T &v1, T &v2, T *lds, Op1 op1, Op2 op2) {
 #pragma unroll
   for (int d = WAVE / 2; d > 0; d >>= 1) {
@@ -264,7 +284,7 @@ __device__ __forceinline__ void q_reduce2(T &v1, T &v2, T *lds, Op1 op1, Op2 op2
     r1 = op1(r1, lds[w]);
     r2 = op2(r2, lds[QW + w]);
   }
-  __syncthreads();
+  if (TRAIL) __syncthreads();
   v1 = uni(r1);
   v2 = uni(r2);
 }
@@ -336,8 +356,10 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     S.elen[tid] = (u32)(b - a);
   }
   u64 tsum = counts ? te : 0, tmin = counts ? te : ~0ull;
-  q_reduce2<u64>(tsum, tmin, S.cub, [](u64 x, u64 y) { return sat_add(x, y); },
-                 [](u64 x, u64 y) { return x < y ? x : y; });
+  // (the buffers of consecutive reductions and scans alternate, so that no
+  // barrier is needed after each)
+  q_reduce2<false>(tsum, tmin, S.cub, [](u64 x, u64 y) { return sat_add(x, y); },
+                   [](u64 x, u64 y) { return x < y ? x : y; });
   if (sat_add(tsum, cap) >= (1ull << 63)) {
     if (tid == 0) {
       atomicOr(A.flags, FLAG_EOVERFLOW);
@@ -359,7 +381,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
   while (((u64)(QSMAX - nr) << sh) < W) ++sh;
   const u32 c0 = (l0 + (1u << sh) - 1) >> sh, c1 = (l1 + (1u << sh) - 1) >> sh;
   u32 ts;
-  const u32 so = wg_excl_scan<QB>(c0 + c1, S.red32, &ts);
+  const u32 so = q_scan<u32>(c0 + c1, S.red32, &ts);
   ts = rfl(ts);
   if (tid < deg) {
     S.rsp[2 * tid] = so;
@@ -402,7 +424,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       mx = sl[k] > mx ? sl[k] : mx;
     }
   }
-  q_reduce2<u32>(mn, mx, S.cid, [](u32 a, u32 b) { return a < b ? a : b; },
+  q_reduce2<false>(mn, mx, S.cid, [](u32 a, u32 b) { return a < b ? a : b; },
                  [](u32 a, u32 b) { return a > b ? a : b; });
   // -- estimated visits over buckets of 2^bs ids from mn, in 1/16 of a visit:
   // each block's pins spread evenly over the buckets from its first pin's to
@@ -426,9 +448,9 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
   {
     const u32 d0 = S.cum[QBPT * tid], d1 = QBPT > 1 ? S.cum[QBPT * tid + 1] : 0;
     u32 tot;
-    const u32 e = wg_excl_scan<QB>(d0 + d1, S.red32, &tot);  // mod 2^32: the sums are exact
+    const u32 e = q_scan<u32>(d0 + d1, S.red32, &tot);  // mod 2^32: the sums are exact
     const u32 v0 = e + d0, v1 = e + d0 + d1;                  // estimates of the buckets
-    const u32 off = wg_excl_scan<QB>(QBPT > 1 ? v0 + v1 : v0, S.red32, &tot);
+    const u32 off = q_scan<u32>(QBPT > 1 ? v0 + v1 : v0, S.cid, &tot);
     S.cum[QBPT * tid] = off;
     if (QBPT > 1) S.cum[QBPT * tid + 1] = off + v0;
     if (tid == 0) S.cum[QNHB] = tot;
@@ -448,21 +470,18 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
         S.dbits[(b >> 5) + 1] = (u32)(bal >> 32);
       }
     }
-    __syncthreads();
-    if (wid == 0) {
-      const u64 b2 = __ballot(lane < 32 && S.dbits[lane & 31] != 0);
-      if (lane == 0) S.dsum = (u32)b2;
-    }
     if (tid == 0) S.ncont = 0;
     if (tid < 2 * QW) S.wbl[tid / QW][tid % QW] = 0;
     __syncthreads();
   }
+  // bit w: dense bits word w is not zero (each wave finds it)
+  const u32 dsum = (u32)__builtin_amdgcn_ballot_w64(lane < 32 && S.dbits[lane & 31] != 0);
   // -- windows over [mn, mx]: from the first dense window to mx, then from mn
   // up to that window, so that the dense ones (in most graphs the best
   // neighbours) set a high bound before the sparse ones are visited
   u64 lstar = 0;  // best lower bound of eta + noise so far (a valid neighbour's)
   const u64 end = (u64)mx + 1;
-  const u32 bd0 = q_first_dense(S, 0, nbk);
+  const u32 bd0 = q_first_dense(S, dsum, 0, nbk);
   const u64 start = bd0 < nbk ? (u64)mn + ((u64)bd0 << bs) : (u64)mn;
   u64 lo = start, wend = end;
   bool wrapped = start == mn;
@@ -515,7 +534,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
         r = l + step - 1 < r ? l + step - 1 : r;
         if (step == 1) break;
       }
-      const u32 bd = q_first_dense(S, b0 + 1, nbk);
+      const u32 bd = q_first_dense(S, dsum, b0 + 1, nbk);
       const u32 b1 = bd < l ? bd : l;
       hi = b1 >= nbk ? wend : (u64)mn + ((u64)b1 << bs);
       hi = hi < wend ? hi : wend;
@@ -549,7 +568,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     }
     // one scan of (pins << 32 | non-empty): offsets and compacted indices
     u64 tk;
-    const u64 pk = wg_excl_scan<QB, u64>(((u64)(L[0] + L[1]) << 32) |
+    const u64 pk = q_scan<u64>(((u64)(L[0] + L[1]) << 32) |
                                              ((L[0] ? 1u : 0u) + (L[1] ? 1u : 0u)),
                                          S.red64, &tk);
     const u32 T = rfl((u32)(tk >> 32)), K = rfl((u32)tk);
@@ -731,7 +750,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
         const uint4 x = q_take4(S.t.bin, 4 * (tid + j * QB));
         hot |= (x.x > vt) | (x.y > vt) | (x.z > vt) | (x.w > vt);
       }
-      hot = q_reduce<u32>(hot, S.red32, [](u32 a, u32 b) { return a | b; });
+      hot = q_reduce<false>(hot, S.red32, [](u32 a, u32 b) { return a | b; });
       redo = hot != 0;
       if (!redo) {
         if (tid < deg) {
@@ -780,7 +799,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
             vstar = V > vstar ? V : vstar;
         }
       }
-      vstar = q_reduce<u32>(vstar, S.red32, [](u32 a, u32 b) { return a > b ? a : b; });
+      vstar = q_reduce<false>(vstar, S.red32, [](u32 a, u32 b) { return a > b ? a : b; });
     } else {
       // every neighbour is valid; the visits' returned sums gave the largest
       // bin (a key dropped by a full hash window holds a partial sum, still a
