@@ -634,14 +634,15 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       const u64 sb_l = S.sbits[cb][myc];
       if (lane < QU && myq < nblk) S.sbits[cb][myq] = 0;  // read once: left clear
       // phase by phase for all u: stretch of each pin, its address, the pin.
-      // The block of u starts at flat position pb(u) = c + (u QW + ws) 64 and
-      // holds room(u) positions of the chunk (scalar values); lane < room(u)
-      // says the lane's position is in the chunk
+      // The block of u starts at flat position pbase(u) = c + (u QW + ws) 64
+      // (a scalar value)
       const u32 ws = rfl(wid);
       auto pbase = [&](u32 u) { return c + (u * QW + ws) * WAVE; };
-      auto room = [&](u32 u) {
-        return u * QW + ws < nblk && pbase(u) < T ? T - pbase(u) : 0u;
-      };
+      // a lane's position is in the chunk when it is below T (the blocks of
+      // u all lie below c + QCH)
+      auto lim = [&](u32 u) { return (int)(T - pbase(u)); };
+      // (a lane outside the chunk gets some stretch of the chunk, read but
+      // unused; its load is redirected and its pin reads as 0xFFFFFFFF)
       u32 kk[QU], v[QU];
 #pragma unroll
       for (u32 u = 0; u < QU; ++u) {
@@ -652,16 +653,16 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
                         (u32)__builtin_amdgcn_readlane((u32)sb_l, u)) >> 1;
         const u32 k = k0 + __builtin_amdgcn_mbcnt_hi((u32)(sb >> 32),
                                                      __builtin_amdgcn_mbcnt_lo((u32)sb, 0u));
-        kk[u] = lane < room(u) ? k : 0;
+        kk[u] = k;
       }
       i32 ca[QU];
 #pragma unroll
       for (u32 u = 0; u < QU; ++u) ca[u] = S.caddr[kk[u]];
 #pragma unroll
       for (u32 u = 0; u < QU; ++u)
-        v[u] = A.e_pins[lane < room(u) ? (u32)(ca[u] + (i32)(pbase(u) + lane)) : 0u];
+        v[u] = A.e_pins[(int)lane < lim(u) ? (u32)(ca[u] + (i32)(pbase(u) + lane)) : 0u];
 #pragma unroll
-      for (u32 u = 0; u < QU; ++u) v[u] = lane < room(u) ? v[u] : 0xFFFFFFFFu;
+      for (u32 u = 0; u < QU; ++u) v[u] = (int)lane < lim(u) ? v[u] : 0xFFFFFFFFu;
       // the first pin >= hi of each stretch: a lane whose pin is >= hi while
       // the lane before holds a pin < hi of the same stretch does not qualify
       // (one lane per stretch and wave block; the block's first position
