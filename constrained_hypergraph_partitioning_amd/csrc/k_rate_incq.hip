@@ -138,6 +138,47 @@ __device__ __forceinline__ u64 rfl64(u64 v) {
 __device__ __forceinline__ u32 uni(u32 v) { return rfl(v); }
 __device__ __forceinline__ u64 uni(u64 v) { return rfl64(v); }
 
+// Row operations on the 16 lanes of a DPP row (one per wave of the
+// workgroup): a value moved from another lane of the row, zero where the
+// source lies outside it.
+static_assert(QW == 16, "one DPP row holds a value per wave");
+template <int C>
+__device__ __forceinline__ u32 q_dpp(u32 v) {
+  return (u32)__builtin_amdgcn_update_dpp(0, (int)v, C, 0xF, 0xF, true);
+}
+template <int C>
+__device__ __forceinline__ u64 q_dpp(u64 v) {
+  return (u64)q_dpp<C>((u32)(v >> 32)) << 32 | q_dpp<C>((u32)v);
+}
+// every lane of a row ends with op over the row's 16 values
+template <typename T, typename Op>
+__device__ __forceinline__ T q_row_reduce(T v, Op op) {
+  v = op(v, q_dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = op(v, q_dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = op(v, q_dpp<0x141>(v));  // row_half_mirror
+  v = op(v, q_dpp<0x140>(v));  // row_mirror
+  return v;
+}
+// lane i of a row ends with the sum of the row's values 0 .. i
+template <typename T>
+__device__ __forceinline__ T q_row_scan(T v) {
+  v += q_dpp<0x111>(v);  // row_shr:1
+  v += q_dpp<0x112>(v);  // row_shr:2
+  v += q_dpp<0x114>(v);  // row_shr:4
+  v += q_dpp<0x118>(v);  // row_shr:8
+  return v;
+}
+__device__ __forceinline__ u32 q_lane(u32 v, u32 l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ u64 q_lane(u64 v, u32 l) {
+  return (u64)(u32)__builtin_amdgcn_readlane((u32)(v >> 32), l) << 32 |
+         (u32)__builtin_amdgcn_readlane((u32)v, l);
+}
+// op over the 16 per-wave values of a[], in every lane
+template <typename T, typename Op>
+__device__ __forceinline__ T q_fold(const T *a, Op op) {
+  return q_lane(q_row_reduce(a[lane_id() & (QW - 1)], op), 0u);
+}
+
 __device__ __forceinline__ u32 qslot(u32 m) { return (u32)(((u64)(m * 0x9E3779B1u) * QHS) >> 32); }
 __device__ __forceinline__ u32 qsketch(u32 m) { return (u32)(((u64)(m * 0x9E3779B1u) * QD) >> 32); }
 
@@ -239,11 +280,9 @@ __device__ __forceinline__ T q_reduce(T v, T *lds, Op op) {
   for (int d = WAVE / 2; d > 0; d >>= 1) v = op(v, (T)__shfl_xor(v, d, WAVE));
   if (lane_id() == 0) lds[wave_id()] = v;
   __syncthreads();
-  T r = lds[0];
-#pragma unroll
-  for (int w = 1; w < QW; ++w) r = op(r, lds[w]);
+  const T r = q_fold(lds, op);
   if (TRAIL) __syncthreads();
-  return uni(r);
+  return r;
 }
 
 // exclusive prefix of v over the workgroup, *total the sum (lds: QW entries)
@@ -252,15 +291,10 @@ __device__ __forceinline__ T q_scan(T v, T *lds, T *total) {
   const T inc = wave_incl_scan(v);
   if (lane_id() == WAVE - 1) lds[wave_id()] = inc;
   __syncthreads();
-  T off = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < QW; ++w) {
-    const T x = lds[w];
-    off += w < (int)wave_id() ? x : (T)0;
-    tot += x;
-  }
-  *total = tot;
-  return off + inc - v;
+  const T x = q_row_scan(lds[lane_id() & (QW - 1)]);
+  const u32 ws = rfl(wave_id());
+  *total = q_lane(x, QW - 1);
+  return (ws ? q_lane(x, ws - 1) : (T)0) + inc - v;
 }
 
 __device__ __forceinline__ u64 umax64(u64 a, u64 b) { return a > b ? a : b; }
@@ -278,15 +312,9 @@ __device__ __forceinline__ void q_reduce2(T &v1, T &v2, T *lds, Op1 op1, Op2 op2
     lds[QW + wave_id()] = v2;
   }
   __syncthreads();
-  T r1 = lds[0], r2 = lds[QW];
-#pragma unroll
-  for (int w = 1; w < QW; ++w) {
-    r1 = op1(r1, lds[w]);
-    r2 = op2(r2, lds[QW + w]);
-  }
+  v1 = q_fold(lds, op1);
+  v2 = q_fold(lds + QW, op2);
   if (TRAIL) __syncthreads();
-  v1 = uni(r1);
-  v2 = uni(r2);
 }
 
 // A bin value below which no bin can reach T: every V < q_vthr(...) has
@@ -738,9 +766,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       // the sketch: a slot whose sum, as an upper bound for every id in it,
       // can reach the best lower bound makes the window a hash window (from
       // the same cursors); every slot is read and left empty
-#pragma unroll
-      for (int w = 0; w < QW; ++w) lstar = umax64(lstar, S.wbl[par ^ 1][w]);
-      lstar = uni(lstar);
+      lstar = umax64(lstar, q_fold(S.wbl[par ^ 1], umax64));
       // (a slot at or above the real-valued bound counts as hot: at worst a
       // window more is hashed)
       u32 hot = 0;
@@ -774,9 +800,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     // that can still reach it; every slot is read and left empty
     // the best lower bound of the windows before (their per-wave maxima were
     // published by the barriers since)
-#pragma unroll
-    for (int w = 0; w < QW; ++w) lstar = umax64(lstar, S.wbl[par ^ 1][w]);
-    lstar = uni(lstar);
+    lstar = umax64(lstar, q_fold(S.wbl[par ^ 1], umax64));
     // candidates: the largest valid bin bounds the winner's eta + noise from
     // below; the valid bins that can still reach that bound are judged.  Every
     // slot is read and left empty.
@@ -805,9 +829,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       // every neighbour is valid; the visits' returned sums gave the largest
       // bin (a key dropped by a full hash window holds a partial sum, still a
       // lower bound of a valid neighbour's eta)
-#pragma unroll
-      for (int w = 0; w < QW; ++w) vstar = S.wvmax[w] > vstar ? S.wvmax[w] : vstar;
-      vstar = uni(vstar);
+      vstar = q_fold(S.wvmax, [](u32 a, u32 b) { return a > b ? a : b; });
     }
     const u64 T2 = umax64((u64)vstar << s, lstar);
     const u32 vthr = q_vthr(T2, s, qmin, errunit, ub);
@@ -867,9 +889,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     // visits, and the reads of fail_min, wvmax and wbl before their reuse
   }
   __syncthreads();
-#pragma unroll
-  for (int w = 0; w < QW; ++w) lstar = umax64(lstar, S.wbl[par ^ 1][w]);
-  lstar = uni(lstar);
+  lstar = umax64(lstar, q_fold(S.wbl[par ^ 1], umax64));
   const u32 nc = rfl(S.ncont);
   if (nc > QCONT) return false;
   // -- exact eta of the contenders still in reach: t(e) summed over the
