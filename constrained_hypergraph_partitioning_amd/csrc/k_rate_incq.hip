@@ -708,7 +708,8 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
 #pragma unroll
       for (u32 u = 0; u < QU; ++u) qv[u] = S.cq[kk[u]];
       const u32 span = hi32 - lo32;
-      if (direct && om) {
+      if (direct) {
+        // (the largest bin is found by the candidate pass)
 #pragma unroll
         for (u32 u = 0; u < QU; ++u) {
           const u32 r = v[u] - lo32;
@@ -720,21 +721,6 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
           const u32 x = v[u];
           if (x - lo32 < span && x != n) atomicAdd(&S.t.bin[qsketch(x)], qv[u]);
         }
-      } else if (direct) {
-        // every lane adds (0 to a slot of its own when its pin is not in the
-        // window), so the returned sums need no branch: each is a partial sum
-        // of some neighbour, a lower bound of its eta
-        u32 o[QU];
-#pragma unroll
-        for (u32 u = 0; u < QU; ++u) {
-          const u32 r = v[u] - lo32;
-          const bool in = r < span && v[u] != n;
-          const u32 h = (r & 1u) << 4;  // (any half of slot lane when not in)
-          const u32 q = in ? qv[u] << h : 0;
-          o[u] = __builtin_amdgcn_ubfe(atomicAdd(&S.t.bin[in ? r >> 1 : lane], q) + q, h, 16);
-        }
-#pragma unroll
-        for (u32 u = 0; u < QU; ++u) vmax = o[u] > vmax ? o[u] : vmax;
       } else {
 #pragma unroll
         for (u32 u = 0; u < QU; ++u) {
@@ -751,7 +737,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
           }
         }
       }
-      if (!om && !sk) {
+      if (!om && !sk && !direct) {
         u32 wv = vmax;
 #pragma unroll
         for (int d = WAVE / 2; d > 0; d >>= 1) {
@@ -825,6 +811,19 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
         }
       }
       vstar = q_reduce<false>(vstar, S.red32, [](u32 a, u32 b) { return a > b ? a : b; });
+    } else if (direct) {
+      // every neighbour is valid: the largest 16-bit bin, a pass of its own
+      q_u16x2 m2 = {0, 0};
+#pragma unroll
+      for (u32 j = 0; j < QD / (4 * QB); ++j) {
+        const uint4 x = *reinterpret_cast<const uint4 *>(&S.t.bin[4 * (tid + j * QB)]);
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(q_u16x2, x.x));
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(q_u16x2, x.y));
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(q_u16x2, x.z));
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(q_u16x2, x.w));
+      }
+      vstar = q_reduce<false>(m2[0] > m2[1] ? (u32)m2[0] : (u32)m2[1], S.red32,
+                              [](u32 a, u32 b) { return a > b ? a : b; });
     } else {
       // every neighbour is valid; the visits' returned sums gave the largest
       // bin (a key dropped by a full hash window holds a partial sum, still a
