@@ -368,10 +368,12 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
   // -- incident hyperedges; the term sum and the smallest term decide s
   u64 te = 0;
   u32 l0 = 0, l1 = 0;
+  i64 a = 0, b = 0;
   bool counts = false;
   if (tid < deg) {
     const u32 e = A.n_inc[h.i0 + tid];
-    const i64 a = A.e_off[e], b = A.e_off[e + 1];
+    a = A.e_off[e];
+    b = A.e_off[e + 1];
     const u32 ns = A.e_nsrc[e];
     te = A.t[e];
     counts = b - a >= 2;
@@ -422,15 +424,27 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
   if (tid == 0) S.rsp[nr] = ts;
   for (u32 b = tid; b <= QNHB; b += QB) S.cum[b] = 0;
   __syncthreads();
+  // (only the first pin of a block is read; a block's pins then lie between
+  // it and the next block's first pin, or the run's last pin, read by the
+  // run's thread into rlast, which is cnext until the windows)
+  u32 *const rlast = S.cnext;
   constexpr u32 SPT = QSMAX / QB;
-  u32 sf[SPT], sl[SPT], sw[SPT];
+  u32 sf[SPT], sw[SPT], sr[SPT];
   u32 mn = 0xFFFFFFFFu, mx = 0;
+  if (tid < deg) {
+    if (l0) mx = rlast[2 * tid] = A.e_pins[a + l0 - 1];
+    if (l1) {
+      const u32 x = A.e_pins[b - 1];
+      rlast[2 * tid + 1] = x;
+      mx = x > mx ? x : mx;
+    }
+  }
 #pragma unroll
   for (u32 k = 0; k < SPT; ++k) {
     const u32 g = tid + k * QB;
     sf[k] = 0;
-    sl[k] = 0;
     sw[k] = 0;
+    sr[k] = 0;
     if (g < ts) {
       const u32 r = run_of(S.rsp, nr, g);
       const u32 ke = r >> 1;
@@ -439,8 +453,8 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       const u32 p0 = (g - S.rsp[r]) << sh;
       const u32 p1 = (p0 + (1u << sh) < len ? p0 + (1u << sh) : len) - 1;
       sf[k] = A.e_pins[base + p0];
-      sl[k] = A.e_pins[base + p1];
       sw[k] = p1 + 1 - p0;
+      sr[k] = r;
     }
   }
 #pragma unroll
@@ -449,14 +463,13 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     if (g < ts) {
       S.sfirst[g] = sf[k];
       mn = sf[k] < mn ? sf[k] : mn;
-      mx = sl[k] > mx ? sl[k] : mx;
     }
   }
   q_reduce2<false>(mn, mx, S.cid, [](u32 a, u32 b) { return a < b ? a : b; },
                  [](u32 a, u32 b) { return a > b ? a : b; });
   // -- estimated visits over buckets of 2^bs ids from mn, in 1/16 of a visit:
   // each block's pins spread evenly over the buckets from its first pin's to
-  // its last pin's (a difference array, then two scans)
+  // its last pin's bound (a difference array, then two scans)
   u32 bs = QBS_MIN;
   while (((mx - mn) >> bs) >= QNHB) ++bs;
   const u32 nbk = ((mx - mn) >> bs) + 1;
@@ -464,7 +477,9 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
   for (u32 k = 0; k < SPT; ++k) {
     const u32 g = tid + k * QB;
     if (g < ts) {
-      const u32 bf = (sf[k] - mn) >> bs, bl = (sl[k] - mn) >> bs;
+      const u32 r = sr[k];
+      const u32 last = g + 1 < S.rsp[r + 1] ? S.sfirst[g + 1] - 1 : rlast[r];
+      const u32 bf = (sf[k] - mn) >> bs, bl = (last - mn) >> bs;
       const u32 unit = sw[k] * QEST, span = bl - bf + 1;
       const u32 qd = unit / span, rem = unit - qd * span;
       atomicAdd(&S.cum[bf], qd + rem);
