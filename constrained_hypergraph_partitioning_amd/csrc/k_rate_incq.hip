@@ -70,6 +70,7 @@ constexpr u32 QBPT = QNHB / QB;       // estimate buckets per thread
 static_assert(QNHB % QB == 0 && QBPT <= 2 && QNHB == 32 * 32,
               "one or two buckets per thread; two-level dense bitmap");
 static_assert(QD % QB == 0 && QHS % QB == 0 && QSMAX % QB == 0, "slots per thread");
+static_assert(QSMAX <= QD, "the samples' run table fits the bins");
 static_assert(QD % (4 * QB) == 0 && QHS % (4 * QB) == 0, "four slots per thread and step");
 
 typedef unsigned short q_u16x2 __attribute__((ext_vector_type(2)));
@@ -416,6 +417,8 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
   if (tid < deg) {
     S.rsp[2 * tid] = so;
     S.rsp[2 * tid + 1] = so + c0;
+    // the run of every sample, in the (empty) bins until the samples are read
+    for (u32 g = so; g < so + c0 + c1; ++g) S.t.bin[g] = g < so + c0 ? 2 * tid : 2 * tid + 1;
   }
   if (tid < deg) {  // every pin is >= the first window's low end
     S.rcur[2 * tid] = 0;
@@ -446,7 +449,8 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     sw[k] = 0;
     sr[k] = 0;
     if (g < ts) {
-      const u32 r = run_of(S.rsp, nr, g);
+      const u32 r = S.t.bin[g];
+      S.t.bin[g] = 0;  // (the bins are empty again before the windows)
       const u32 ke = r >> 1;
       const u32 len = (r & 1) ? S.elen[ke] - S.ens[ke] : S.ens[ke];
       const i64 base = S.eoff[ke] + ((r & 1) ? S.ens[ke] : 0);
@@ -481,7 +485,12 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       const u32 last = g + 1 < S.rsp[r + 1] ? S.sfirst[g + 1] - 1 : rlast[r];
       const u32 bf = (sf[k] - mn) >> bs, bl = (last - mn) >> bs;
       const u32 unit = sw[k] * QEST, span = bl - bf + 1;
-      const u32 qd = unit / span, rem = unit - qd * span;
+      // floor(unit / span) from a reciprocal (unit < 2^20: one step of
+      // correction either way makes it exact)
+      u32 qd = (u32)((float)unit * __builtin_amdgcn_rcpf((float)span));
+      qd -= qd * span > unit ? 1u : 0u;
+      qd += (qd + 1) * span <= unit ? 1u : 0u;
+      const u32 rem = unit - qd * span;
       atomicAdd(&S.cum[bf], qd + rem);
       atomicSub(&S.cum[bf + 1], rem);
       atomicSub(&S.cum[bl + 1], qd);
@@ -685,7 +694,8 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       // u all lie below c + QCH)
       auto lim = [&](u32 u) { return (int)(T - pbase(u)); };
       // (a lane outside the chunk gets some stretch of the chunk, read but
-      // unused; its load is redirected and its pin reads as 0xFFFFFFFF)
+      // unused; its load is redirected and its pin reads as hi: in no
+      // window, and past the end of every stretch of the chunk)
       u32 kk[QU], v[QU];
 #pragma unroll
       for (u32 u = 0; u < QU; ++u) {
@@ -705,14 +715,14 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       for (u32 u = 0; u < QU; ++u)
         v[u] = A.e_pins[(int)lane < lim(u) ? (u32)(ca[u] + (i32)(pbase(u) + lane)) : 0u];
 #pragma unroll
-      for (u32 u = 0; u < QU; ++u) v[u] = (int)lane < lim(u) ? v[u] : 0xFFFFFFFFu;
+      for (u32 u = 0; u < QU; ++u) v[u] = (int)lane < lim(u) ? v[u] : hi32;
       // the first pin >= hi of each stretch: a lane whose pin is >= hi while
       // the lane before holds a pin < hi of the same stretch does not qualify
       // (one lane per stretch and wave block; the block's first position
       // counts as a stretch start)
 #pragma unroll
       for (u32 u = 0; u < QU; ++u) {
-        const u64 B = __builtin_amdgcn_ballot_w64(v[u] != 0xFFFFFFFFu && v[u] >= hi32);
+        const u64 B = __builtin_amdgcn_ballot_w64(v[u] >= hi32);
         const u64 st = ((u64)(u32)__builtin_amdgcn_readlane((u32)(sb_l >> 32), u) << 32 |
                         (u32)__builtin_amdgcn_readlane((u32)sb_l, u)) | 1ull;
         const u64 first = B & ~((B << 1) & ~st);
