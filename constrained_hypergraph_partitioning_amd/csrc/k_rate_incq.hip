@@ -169,6 +169,19 @@ __device__ __forceinline__ T q_row_scan(T v) {
   v += q_dpp<0x118>(v);  // row_shr:8
   return v;
 }
+// inclusive prefix over the whole wave: the row prefix, then row 0's total
+// into row 1 and row 2's into row 3 (row_bcast:15), then the total of rows
+// 0-1 into rows 2 and 3 (row_bcast:31); rows left out keep their value
+__device__ __forceinline__ u32 q_wave_scan(u32 v) {
+  v = q_row_scan(v);
+  v += (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);
+  v += (u32)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);
+  return v;
+}
+// the same for two independent 32-bit halves (their sums never carry)
+__device__ __forceinline__ u64 q_wave_scan(u64 v) {
+  return (u64)q_wave_scan((u32)(v >> 32)) << 32 | q_wave_scan((u32)v);
+}
 __device__ __forceinline__ u32 q_lane(u32 v, u32 l) { return __builtin_amdgcn_readlane(v, l); }
 __device__ __forceinline__ u64 q_lane(u64 v, u32 l) {
   return (u64)(u32)__builtin_amdgcn_readlane((u32)(v >> 32), l) << 32 |
@@ -286,10 +299,11 @@ __device__ __forceinline__ T q_reduce(T v, T *lds, Op op) {
   return r;
 }
 
-// exclusive prefix of v over the workgroup, *total the sum (lds: QW entries)
+// exclusive prefix of v over the workgroup, *total the sum (lds: QW entries);
+// a 64-bit v is two 32-bit counts whose sums stay below 2^32
 template <typename T>
 __device__ __forceinline__ T q_scan(T v, T *lds, T *total) {
-  const T inc = wave_incl_scan(v);
+  const T inc = q_wave_scan(v);
   if (lane_id() == WAVE - 1) lds[wave_id()] = inc;
   __syncthreads();
   const T x = q_row_scan(lds[lane_id() & (QW - 1)]);
