@@ -2,10 +2,12 @@
 // Incident Hyperedges and Size Constraints": connectivity, Eq. 1; cut-net,
 // Eq. 16; the per-partition size and distinct-inbound counts of Sec. II-B).
 //
-// Per hyperedge one sort of 64-bit keys (rho << 1 | is_source): the number
-// of groups of equal rho is lambda(e), and a group whose first key is a
-// destination marks a partition that e enters (it counts once towards that
-// partition's inbound set).
+// Per hyperedge the distinct partitions of its pins: lambda(e) is their
+// number, and each one holding a destination pin is a partition that e
+// enters (e counts once towards that partition's inbound set).  Hyperedges of
+// at most 64 pins and those above 512 sort 64-bit keys (rho << 1 | is_source:
+// a group of equal rho whose first key is a destination is entered); the
+// others insert rho into a hash table per wave, destinations first.
 #include "dev.h"
 #include "kernels.h"
 
@@ -104,6 +106,106 @@ __device__ u32 eval_groups(const u64 *s, u32 m, u32 *part_inb, u32 *s_red) {
   return lam;
 }
 
+// Hyperedges of 65 .. EH_MAX pins, a wave each, without a sort: the
+// partitions of the pins go into the wave's own LDS table (open addressing,
+// key p + 1, 0 = empty, at most half full).  The destinations go in first, so
+// every partition holding a destination pin is claimed by one (the claiming
+// lane counts e towards that partition's inbound set), then the sources;
+// lambda(e) is the number of claims.  Each lane gathers all its pins' rho
+// before its first insert.
+constexpr u32 EH_MAX = 512;          // pins of the largest hyperedge hashed per wave
+constexpr u32 EH_SLOTS = 2 * EH_MAX;  // table slots per wave
+constexpr u32 EH_PER = EH_MAX / WAVE;
+
+template <int BLOCK>
+__global__ __launch_bounds__(BLOCK) void k_eval_hash(const i64 *e_off, const u32 *e_nsrc,
+                                                     const u32 *pins, const u32 *e_w,
+                                                     const u32 *rho, u32 k, u32 *part_inb,
+                                                     u64 *summary, const u32 *list,
+                                                     const u32 *cnt, u32 *flags) {
+  __shared__ u32 tab[BLOCK / WAVE][EH_SLOTS];
+  __shared__ u64 s_sum[3][BLOCK / WAVE];
+  const u32 total = *cnt;
+  const u32 nwaves = gridDim.x * (BLOCK / WAVE);
+  const u32 l = lane_id();
+  u32 *t = tab[wave_id()];
+  for (u32 i = l; i < EH_SLOTS; i += WAVE) t[i] = 0;
+  u64 conn = 0, cut = 0, lams = 0;
+  for (u32 w = blockIdx.x * (BLOCK / WAVE) + wave_id(); w < total; w += nwaves) {
+    const u32 e = list[w];
+    const i64 a = e_off[e];
+    const u32 len = (u32)(e_off[e + 1] - a), ns = e_nsrc[e];
+    if (len > EH_MAX) continue;  // (the workgroup sort's)
+    const u32 hs = next_pow2(2 * len);
+    const u32 sh = 32 - (31 - __builtin_clz(hs));
+    u32 p[EH_PER];
+#pragma unroll
+    for (u32 j = 0; j < EH_PER; ++j) {
+      const u32 i = l + j * WAVE;
+      p[j] = i < len ? pins[a + i] : 0;
+    }
+#pragma unroll
+    for (u32 j = 0; j < EH_PER; ++j) {
+      const u32 i = l + j * WAVE;
+      if (i < len) {
+        p[j] = rho[p[j]];
+        if (p[j] >= k) {
+          atomicOr(flags, FLAG_EINVAL);
+          p[j] = 0;
+        }
+      }
+    }
+    u32 claims = 0;
+#pragma unroll
+    for (u32 pass = 0; pass < 2; ++pass) {
+      // pass 0: destinations (pins ns .. len - 1); pass 1: sources
+#pragma unroll
+      for (u32 j = 0; j < EH_PER; ++j) {
+        const u32 i = l + j * WAVE;
+        if (i < len && (pass ? i < ns : i >= ns)) {
+          const u32 key = p[j] + 1;
+          u32 s = (p[j] * 0x9E3779B1u) >> sh;
+          for (;;) {
+            const u32 o = atomicCAS(&t[s], 0u, key);
+            if (o == 0) {
+              ++claims;
+              if (!pass) atomicAdd(&part_inb[p[j]], 1u);
+              break;
+            }
+            if (o == key) break;
+            s = (s + 1) & (hs - 1);
+          }
+        }
+      }
+    }
+    const u64 lam = wave_sum(claims);
+    for (u32 i = l; i < hs; i += WAVE) t[i] = 0;
+    if (l == 0) {
+      const u64 we = e_w[e];
+      conn += we * (lam - 1);
+      cut += lam > 1 ? we : 0;
+      lams += lam;
+    }
+  }
+  if (l == 0) {
+    s_sum[0][wave_id()] = conn;
+    s_sum[1][wave_id()] = cut;
+    s_sum[2][wave_id()] = lams;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < BLOCK / WAVE; ++w) {
+      conn += s_sum[0][w];
+      cut += s_sum[1][w];
+      lams += s_sum[2][w];
+    }
+    flush_sums(conn, cut, lams, summary);
+  }
+}
+
+// The hyperedges of EH_MAX + 1 .. CAP pins: a workgroup sort of the keys.
+// The workgroup reads BLOCK entries of the list at a time and sorts the long
+// ones among them, one after the other.
 template <int BLOCK, int CAP>
 __global__ __launch_bounds__(BLOCK) void k_eval_lds(const i64 *e_off, const u32 *e_nsrc,
                                                     const u32 *pins, const u32 *e_w,
@@ -112,23 +214,36 @@ __global__ __launch_bounds__(BLOCK) void k_eval_lds(const i64 *e_off, const u32 
                                                     u32 *flags) {
   __shared__ u64 s[CAP];
   __shared__ u32 s_red[BLOCK / WAVE + 1];
+  __shared__ u32 s_long[BLOCK];
+  __shared__ u32 s_nlong;
   const u32 total = *cnt;
   u64 conn = 0, cut = 0, lams = 0;
-  for (u32 w = blockIdx.x; w < total; w += gridDim.x) {
-    const u32 e = list[w];
-    const i64 a = e_off[e];
-    const u32 len = (u32)(e_off[e + 1] - a), ns = e_nsrc[e];
-    const u32 p = next_pow2(len);
-    for (u32 i = threadIdx.x; i < p; i += BLOCK)
-      s[i] = i < len ? eval_key(rho, k, pins[a + i], i < ns, flags) : ~0ull;
+  for (u32 base = blockIdx.x * BLOCK; base < total; base += gridDim.x * BLOCK) {
+    if (threadIdx.x == 0) s_nlong = 0;
     __syncthreads();
-    lds_bitonic<BLOCK>(s, p);
-    const u64 lam = eval_groups<BLOCK>(s, len, part_inb, s_red);
-    const u64 we = e_w[e];
-    conn += we * (lam - 1);
-    cut += lam > 1 ? we : 0;
-    lams += lam;
+    const u32 w = base + threadIdx.x;
+    if (w < total) {
+      const u32 e = list[w];
+      if (e_off[e + 1] - e_off[e] > (i64)EH_MAX) s_long[atomicAdd(&s_nlong, 1u)] = e;
+    }
     __syncthreads();
+    const u32 nl = s_nlong;
+    for (u32 j = 0; j < nl; ++j) {
+      const u32 e = s_long[j];
+      const i64 a = e_off[e];
+      const u32 len = (u32)(e_off[e + 1] - a), ns = e_nsrc[e];
+      const u32 p = next_pow2(len);
+      for (u32 i = threadIdx.x; i < p; i += BLOCK)
+        s[i] = i < len ? eval_key(rho, k, pins[a + i], i < ns, flags) : ~0ull;
+      __syncthreads();
+      lds_bitonic<BLOCK>(s, p);
+      const u64 lam = eval_groups<BLOCK>(s, len, part_inb, s_red);
+      const u64 we = e_w[e];
+      conn += we * (lam - 1);
+      cut += lam > 1 ? we : 0;
+      lams += lam;
+      __syncthreads();
+    }
   }
   if (threadIdx.x == 0) flush_sums(conn, cut, lams, summary);
 }
@@ -214,10 +329,16 @@ void launch_eval_edges(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const u3
                0, e_off, e_nsrc, pins,
                e_w, rho, k, part_inb, summary, (const u32 *)el.list[0], (const u32 *)el.cnt + 0,
                c->flags);
-  if (host_cnt[1])
-    CHP_LAUNCH(c, "eval_lds", (k_eval_lds<256, LDS_CAP_U64>),
-               host_cnt[1] > 8192 ? 8192 : host_cnt[1], 256, 0, e_off, e_nsrc, pins, e_w, rho, k,
-               part_inb, summary, (const u32 *)el.list[1], (const u32 *)el.cnt + 1, c->flags);
+  if (host_cnt[1]) {
+    const u32 gh = (host_cnt[1] + 3) / 4;
+    CHP_LAUNCH(c, "eval_hash", k_eval_hash<256>, gh < 32 * c->n_cu ? gh : 32 * c->n_cu, 256, 0,
+               e_off, e_nsrc, pins, e_w, rho, k, part_inb, summary, (const u32 *)el.list[1],
+               (const u32 *)el.cnt + 1, c->flags);
+    const u32 gl = (host_cnt[1] + 255) / 256;
+    CHP_LAUNCH(c, "eval_lds", (k_eval_lds<256, LDS_CAP_U64>), gl < 8192 ? gl : 8192, 256, 0,
+               e_off, e_nsrc, pins, e_w, rho, k, part_inb, summary, (const u32 *)el.list[1],
+               (const u32 *)el.cnt + 1, c->flags);
+  }
   if (host_cnt[2])
     CHP_LAUNCH(c, "eval_global", (k_eval_global<256, LDS_CAP_U64>), grid_big, 256, 0, e_off,
                e_nsrc, pins, e_w, rho, k, part_inb, summary, (const u32 *)el.list[2],
