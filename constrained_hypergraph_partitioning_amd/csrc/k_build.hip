@@ -169,17 +169,62 @@ __global__ __launch_bounds__(BLOCK) void k_runs_global(u32 *data, const i64 *sta
 
 // ---------------------------------------------------------------------------
 // incidence: degrees, feasibility, scatter, per-node runs
-__global__ __launch_bounds__(256) void k_degrees(u32 E, const i64 *e_off, const u32 *e_nsrc,
-                                                 const u32 *pins, u32 *indeg, u32 *outdeg) {
-  const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
+// Degrees and the scatter take the hyperedges in chunks of DW_EDGES
+// consecutive ones, a workgroup of DW_BLOCK threads each (a wave per
+// hyperedge, the lanes over its pins).  A destination whose id falls in the
+// chunk's window of DW_IDS ids counts in LDS (16-bit counts, two a word);
+// where hyperedges are local to their sources (nodes of a ring, a block, a
+// grid) most do, and a chunk then costs one global atomic per id of the
+// window it touched instead of one per pin.  The window is centred on the
+// median of 64 pins sampled evenly from the chunk.  A chunk adds at most
+// DW_EDGES to an id's count (an id is a destination of a valid hyperedge at
+// most once).  Sources, and destinations outside the window, count in global
+// memory directly.
+constexpr u32 DW_EDGES = 2048, DW_IDS = 65536, DW_BLOCK = 1024;
+
+// The low end of the chunk's window into *s_wb (wave 0; the caller waits).
+__device__ __forceinline__ void chunk_window(const u32 *pins, i64 a0, i64 a1, u32 *s_wb) {
+  if (wave_id() != 0) return;
   const u32 l = lane_id();
-  for (u32 e = blockIdx.x * (blockDim.x / WAVE) + wave_id(); e < E; e += nwaves) {
-    i64 a = e_off[e], b = e_off[e + 1];
-    u32 ns = e_nsrc[e];
-    for (u32 i = l; i < (u32)(b - a); i += WAVE) {
-      u32 v = pins[a + i];
-      atomicAdd(i < ns ? &outdeg[v] : &indeg[v], 1u);
+  const u64 span = (u64)(a1 - a0);
+  u64 key = ~0ull;
+  if (span) key = pins[a0 + (i64)(span * l / WAVE)];
+  key = wave_sort64(key);
+  const u32 med = (u32)__shfl(key, WAVE / 2, WAVE);
+  if (l == 0) *s_wb = span == 0 ? 0u : (med > DW_IDS / 2 ? med - DW_IDS / 2 : 0u);
+}
+
+__global__ __launch_bounds__(DW_BLOCK) void k_degrees(u32 E, const i64 *e_off,
+                                                      const u32 *e_nsrc, const u32 *pins,
+                                                      u32 *indeg, u32 *outdeg) {
+  __shared__ u32 h[DW_IDS / 2];
+  __shared__ u32 s_wb;
+  const u32 nch = (E + DW_EDGES - 1) / DW_EDGES;
+  const u32 l = lane_id();
+  for (u32 ch = blockIdx.x; ch < nch; ch += gridDim.x) {
+    const u32 e0 = ch * DW_EDGES, e1 = E - e0 < DW_EDGES ? E : e0 + DW_EDGES;
+    for (u32 i = threadIdx.x; i < DW_IDS / 2; i += DW_BLOCK) h[i] = 0;
+    chunk_window(pins, e_off[e0], e_off[e1], &s_wb);
+    __syncthreads();
+    const u32 wb = s_wb;
+    for (u32 e = e0 + wave_id(); e < e1; e += DW_BLOCK / WAVE) {
+      const i64 a = e_off[e], b = e_off[e + 1];
+      const u32 ns = e_nsrc[e];
+      for (u32 i = l; i < (u32)(b - a); i += WAVE) {
+        const u32 v = pins[a + i];
+        const u32 r = v - wb;
+        if (i < ns) atomicAdd(&outdeg[v], 1u);
+        else if (r < DW_IDS) atomicAdd(&h[r >> 1], 1u << ((r & 1) << 4));
+        else atomicAdd(&indeg[v], 1u);
+      }
     }
+    __syncthreads();
+    for (u32 i = threadIdx.x; i < DW_IDS / 2; i += DW_BLOCK) {
+      const u32 x = h[i];
+      if (x & 0xFFFFu) atomicAdd(&indeg[wb + 2 * i], x & 0xFFFFu);
+      if (x >> 16) atomicAdd(&indeg[wb + 2 * i + 1], x >> 16);
+    }
+    __syncthreads();
   }
 }
 
@@ -193,22 +238,70 @@ __global__ void k_node_feas(u32 N, const u32 *indeg, const u32 *outdeg, const u3
   if ((u64)n_size[n] > omega || di > delta) atomicOr(flags, FLAG_EINFEASIBLE);
 }
 
-__global__ __launch_bounds__(256) void k_scatter(u32 E, const i64 *e_off, const u32 *e_nsrc,
-                                                 const u32 *pins, const i64 *n_off,
-                                                 const u32 *n_nin, u32 *cur_in, u32 *cur_out,
-                                                 u32 *n_inc) {
-  const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
+// The scatter in two passes over a chunk: the destinations in the window
+// are counted in LDS; then each id of the window with a count reserves its
+// places in one atomic on its cursor and the LDS word takes the first one,
+// which the second pass hands out (an LDS atomic per pin).  An id whose
+// in-degree may not fit 16 bits (n_nin >= 0xFFFF) is marked 0xFFFF and its
+// pins take the global cursor one by one, as outside the window.
+__global__ __launch_bounds__(DW_BLOCK) void k_scatter(u32 E, const i64 *e_off,
+                                                      const u32 *e_nsrc, const u32 *pins,
+                                                      const i64 *n_off, const u32 *n_nin,
+                                                      u32 *cur_in, u32 *cur_out, u32 *n_inc) {
+  __shared__ u32 h[DW_IDS / 2];
+  __shared__ u32 s_wb;
+  const u32 nch = (E + DW_EDGES - 1) / DW_EDGES;
   const u32 l = lane_id();
-  for (u32 e = blockIdx.x * (blockDim.x / WAVE) + wave_id(); e < E; e += nwaves) {
-    i64 a = e_off[e], b = e_off[e + 1];
-    u32 ns = e_nsrc[e];
-    for (u32 i = l; i < (u32)(b - a); i += WAVE) {
-      u32 v = pins[a + i];
-      i64 pos;
-      if (i < ns) pos = n_off[v] + n_nin[v] + atomicAdd(&cur_out[v], 1u);
-      else pos = n_off[v] + atomicAdd(&cur_in[v], 1u);
-      n_inc[pos] = e;
+  for (u32 ch = blockIdx.x; ch < nch; ch += gridDim.x) {
+    const u32 e0 = ch * DW_EDGES, e1 = E - e0 < DW_EDGES ? E : e0 + DW_EDGES;
+    for (u32 i = threadIdx.x; i < DW_IDS / 2; i += DW_BLOCK) h[i] = 0;
+    chunk_window(pins, e_off[e0], e_off[e1], &s_wb);
+    __syncthreads();
+    const u32 wb = s_wb;
+    for (u32 e = e0 + wave_id(); e < e1; e += DW_BLOCK / WAVE) {
+      const i64 a = e_off[e], b = e_off[e + 1];
+      const u32 ns = e_nsrc[e];
+      for (u32 i = ns + l; i < (u32)(b - a); i += WAVE) {
+        const u32 r = pins[a + i] - wb;
+        if (r < DW_IDS) atomicAdd(&h[r >> 1], 1u << ((r & 1) << 4));
+      }
     }
+    __syncthreads();
+    for (u32 i = threadIdx.x; i < DW_IDS / 2; i += DW_BLOCK) {
+      const u32 x = h[i];
+      if (!x) continue;
+      u32 y = 0;
+#pragma unroll
+      for (u32 j = 0; j < 2; ++j) {
+        const u32 cnt = (x >> (16 * j)) & 0xFFFFu;
+        if (!cnt) continue;
+        const u32 v = wb + 2 * i + j;
+        const u32 first = n_nin[v] < 0xFFFFu ? atomicAdd(&cur_in[v], cnt) : 0xFFFFu;
+        y |= first << (16 * j);
+      }
+      h[i] = y;
+    }
+    __syncthreads();
+    for (u32 e = e0 + wave_id(); e < e1; e += DW_BLOCK / WAVE) {
+      const i64 a = e_off[e], b = e_off[e + 1];
+      const u32 ns = e_nsrc[e];
+      for (u32 i = l; i < (u32)(b - a); i += WAVE) {
+        const u32 v = pins[a + i];
+        const u32 r = v - wb;
+        i64 pos;
+        if (i < ns) {
+          pos = n_off[v] + n_nin[v] + atomicAdd(&cur_out[v], 1u);
+        } else {
+          const u32 sh = (r & 1) << 4;
+          if (r < DW_IDS && ((h[r >> 1] >> sh) & 0xFFFFu) != 0xFFFFu)
+            pos = n_off[v] + ((atomicAdd(&h[r >> 1], 1u << sh) >> sh) & 0xFFFFu);
+          else
+            pos = n_off[v] + atomicAdd(&cur_in[v], 1u);
+        }
+        n_inc[pos] = e;
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -419,8 +512,8 @@ void launch_edges_check(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const u
 void launch_degrees(chp_ctx *c, u32 E, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
                     u32 *indeg, u32 *outdeg) {
   if (E == 0) return;
-  CHP_LAUNCH(c, "degrees", k_degrees, waves_grid(E), 256, 0, E, e_off, e_nsrc, pins, indeg,
-             outdeg);
+  const u32 nch = (E + DW_EDGES - 1) / DW_EDGES;
+  CHP_LAUNCH(c, "degrees", k_degrees, nch, DW_BLOCK, 0, E, e_off, e_nsrc, pins, indeg, outdeg);
 }
 
 void launch_node_feas(chp_ctx *c, u32 N, const u32 *indeg, const u32 *outdeg, const u32 *n_size,
@@ -433,7 +526,8 @@ void launch_node_feas(chp_ctx *c, u32 N, const u32 *indeg, const u32 *outdeg, co
 void launch_scatter(chp_ctx *c, u32 E, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
                     const i64 *n_off, const u32 *n_nin, u32 *cur_in, u32 *cur_out, u32 *n_inc) {
   if (E == 0) return;
-  CHP_LAUNCH(c, "scatter", k_scatter, waves_grid(E), 256, 0, E, e_off, e_nsrc, pins, n_off, n_nin,
+  const u32 nch = (E + DW_EDGES - 1) / DW_EDGES;
+  CHP_LAUNCH(c, "scatter", k_scatter, nch, DW_BLOCK, 0, E, e_off, e_nsrc, pins, n_off, n_nin,
              cur_in, cur_out, n_inc);
 }
 
