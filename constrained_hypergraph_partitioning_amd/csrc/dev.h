@@ -349,6 +349,72 @@ __device__ __forceinline__ K wave_sort64(K v) {
   return v;
 }
 
+// Bitonic sort of 64 PER keys across a wave, PER a lane (afterwards lane l
+// holds sorted positions PER l .. PER l + PER - 1, ascending; where each key
+// starts does not matter): the compare-exchanges at distances below PER stay
+// within a lane, the others pair lanes l and l ^ (j / PER).
+template <typename K, int PER>
+__device__ __forceinline__ void wave_sort_regs(K (&v)[PER]) {
+  const u32 l = lane_id();
+#pragma unroll
+  for (u32 k = 2; k <= 64 * PER; k <<= 1) {
+#pragma unroll
+    for (u32 j = k >> 1; j > 0; j >>= 1) {
+      if (j >= (u32)PER) {
+#pragma unroll
+        for (u32 r = 0; r < (u32)PER; ++r) {
+          const u32 i = PER * l + r;
+          const K w = __shfl_xor(v[r], (int)(j / PER), WAVE);
+          const bool up = (i & k) == 0, lower = (i & j) == 0;
+          v[r] = (lower == up) ? (v[r] < w ? v[r] : w) : (v[r] < w ? w : v[r]);
+        }
+      } else {
+#pragma unroll
+        for (u32 r = 0; r < (u32)PER; ++r) {
+          if (r & j) continue;
+          const bool up = ((PER * l + r) & k) == 0;
+          const K a = v[r], b = v[r | j];
+          const bool sw = up ? b < a : a < b;
+          v[r] = sw ? b : a;
+          v[r | j] = sw ? a : b;
+        }
+      }
+    }
+  }
+}
+
+// wave_group_split_emit for m sorted keys held PER a lane as wave_sort_regs
+// leaves them (value << 1 | tag; a group of equal value is represented by its
+// first key): the values of the groups whose first tag is FIRST_TAG go to
+// out[0, n_first), the others to out[n_first, n_total), each in order.
+template <u32 FIRST_TAG, int PER>
+__device__ __forceinline__ void wave_group_split_emit_regs(const u64 (&v)[PER], u32 m, u32 *out,
+                                                           u32 &n_first, u32 &n_total) {
+  const u32 l = lane_id();
+  const u64 prev_last = __shfl_up(v[PER - 1], 1, WAVE);
+  u32 fmask = 0, omask = 0;
+#pragma unroll
+  for (u32 r = 0; r < (u32)PER; ++r) {
+    const u32 i = PER * l + r;
+    const u64 pk = r ? v[r - 1] : prev_last;
+    const bool f = i < m && (i == 0 || (pk >> 1) != (v[r] >> 1));
+    const bool ff = f && (u32)(v[r] & 1) == FIRST_TAG;
+    fmask |= (ff ? 1u : 0u) << r;
+    omask |= (f && !ff ? 1u : 0u) << r;
+  }
+  const u32 cf = (u32)__builtin_popcount(fmask), co = (u32)__builtin_popcount(omask);
+  const u32 incf = wave_incl_scan(cf), inco = wave_incl_scan(co);
+  const u32 nf = __shfl(incf, WAVE - 1, WAVE), no = __shfl(inco, WAVE - 1, WAVE);
+  u32 pf = incf - cf, po = nf + inco - co;
+#pragma unroll
+  for (u32 r = 0; r < (u32)PER; ++r) {
+    if ((fmask >> r) & 1) out[pf++] = (u32)(v[r] >> 1);
+    else if ((omask >> r) & 1) out[po++] = (u32)(v[r] >> 1);
+  }
+  n_first = nf;
+  n_total = nf + no;
+}
+
 // Sorted keys s[0,m) of the form (value << 1 | tag); each group of equal
 // value is represented by its first key, whose tag is the group's smallest.
 // Writes the distinct values of the groups whose first tag is FIRST_TAG to

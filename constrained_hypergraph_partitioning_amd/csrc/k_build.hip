@@ -133,20 +133,63 @@ __global__ __launch_bounds__(256) void k_runs_wave(u32 *data, const i64 *start, 
   }
 }
 
+// Runs of 65 .. RUN_W ids: a wave each, sorted in registers (4, 8 or 16
+// ids a lane, by the run's length).
+constexpr u32 RUN_W = 1024;
+template <int PER>
+__device__ __forceinline__ void sort_run_regs(u32 *data, i64 s, u32 m) {
+  const u32 l = lane_id();
+  u32 v[PER];
+#pragma unroll
+  for (u32 q = 0; q < (u32)PER; ++q) v[q] = q * WAVE + l < m ? data[s + q * WAVE + l] : NONE32;
+  wave_sort_regs<u32, PER>(v);
+#pragma unroll
+  for (u32 q = 0; q < (u32)PER; ++q)
+    if (PER * l + q < m) data[s + PER * l + q] = v[q];
+}
+
+__global__ __launch_bounds__(256) void k_runs_wreg(u32 *data, const i64 *start, const u32 *len,
+                                                   const u32 *cnt) {
+  const u32 n = *cnt;
+  const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
+  for (u32 r = blockIdx.x * (blockDim.x / WAVE) + wave_id(); r < n; r += nwaves) {
+    const u32 m = len[r];
+    if (m > RUN_W) continue;  // (the workgroup sort's)
+    const i64 s = start[r];
+    if (m <= 4 * WAVE) sort_run_regs<4>(data, s, m);
+    else if (m <= 8 * WAVE) sort_run_regs<8>(data, s, m);
+    else sort_run_regs<16>(data, s, m);
+  }
+}
+
+// Runs of RUN_W + 1 .. CAP ids: a workgroup bitonic sort in LDS.  The
+// workgroup reads BLOCK entries of the list at a time and sorts the long ones
+// among them, one after the other.
 template <int BLOCK, int CAP>
 __global__ __launch_bounds__(BLOCK) void k_runs_lds(u32 *data, const i64 *start, const u32 *len,
                                                     const u32 *cnt) {
   __shared__ u32 s[CAP];
+  __shared__ u32 s_long[BLOCK];
+  __shared__ u32 s_nlong;
   const u32 n = *cnt;
-  for (u32 r = blockIdx.x; r < n; r += gridDim.x) {
-    i64 st = start[r];
-    u32 m = len[r];
-    u32 p = next_pow2(m);
-    for (u32 i = threadIdx.x; i < p; i += BLOCK) s[i] = i < m ? data[st + i] : NONE32;
+  for (u32 base = blockIdx.x * BLOCK; base < n; base += gridDim.x * BLOCK) {
+    if (threadIdx.x == 0) s_nlong = 0;
     __syncthreads();
-    lds_bitonic<BLOCK>(s, p);
-    for (u32 i = threadIdx.x; i < m; i += BLOCK) data[st + i] = s[i];
+    const u32 w = base + threadIdx.x;
+    if (w < n && len[w] > RUN_W) s_long[atomicAdd(&s_nlong, 1u)] = w;
     __syncthreads();
+    const u32 nl = s_nlong;
+    for (u32 j = 0; j < nl; ++j) {
+      const u32 r = s_long[j];
+      const i64 st = start[r];
+      const u32 m = len[r];
+      const u32 p = next_pow2(m);
+      for (u32 i = threadIdx.x; i < p; i += BLOCK) s[i] = i < m ? data[st + i] : NONE32;
+      __syncthreads();
+      lds_bitonic<BLOCK>(s, p);
+      for (u32 i = threadIdx.x; i < m; i += BLOCK) data[st + i] = s[i];
+      __syncthreads();
+    }
   }
 }
 
@@ -495,8 +538,14 @@ void launch_sort_runs(chp_ctx *c, u32 *data, RunLists rl, const u32 *host_cnt, u
   if (host_cnt[0])
     CHP_LAUNCH(c, "runs_wave", k_runs_wave, waves_grid(host_cnt[0]), 256, 0, data, rl.start[0],
                rl.len[0], rl.cnt + 0);
-  if (host_cnt[1])
-    CHP_LAUNCH(c, "runs_lds", (k_runs_lds<256, LDS_CAP_U32>), host_cnt[1] > 8192 ? 8192 : host_cnt[1], 256, 0, data, rl.start[1], rl.len[1], rl.cnt + 1);
+  if (host_cnt[1]) {
+    const u32 gw = (host_cnt[1] + 3) / 4;
+    CHP_LAUNCH(c, "runs_wreg", k_runs_wreg, gw < 32 * c->n_cu ? gw : 32 * c->n_cu, 256, 0, data,
+               rl.start[1], rl.len[1], rl.cnt + 1);
+    const u32 gl = (host_cnt[1] + 255) / 256;
+    CHP_LAUNCH(c, "runs_lds", (k_runs_lds<256, LDS_CAP_U32>), gl < 8192 ? gl : 8192, 256, 0,
+               data, rl.start[1], rl.len[1], rl.cnt + 1);
+  }
   if (host_cnt[2])
     CHP_LAUNCH(c, "runs_global", (k_runs_global<256, LDS_CAP_U32>), grid_big, 256, 0, data,
                rl.start[2], rl.len[2], rl.cnt + 2, scratch, scratch_per_wg);

@@ -25,8 +25,9 @@ namespace {
 // the compaction pass; a pair gets the bound |I(a)| + |I(b)| in the oversize
 // buffer and is merged by one sort of 64-bit keys (edge << 1 | is_out): in
 // each group of equal edge the first key tells whether it is inbound.
-// Classes by that bound: one wave (<= 64), a workgroup with an LDS table of
-// CINC_SMALL keys (8 KB, many per CU), one of LDS_CAP_U64 keys, global.
+// Classes by that bound: one wave (<= 64 keys in one register a lane,
+// <= CINC_SMALL in up to 16), a workgroup with an LDS table of LDS_CAP_U64
+// keys, global.
 constexpr u32 CINC_SMALL = 1024;
 __global__ __launch_bounds__(256) void k_cinc_classify(u32 Nc, const u32 *rep_of,
                                                        const u32 *match, const i64 *n_off,
@@ -86,6 +87,45 @@ __global__ __launch_bounds__(256) void k_cinc_wave(const i64 *n_off, const u32 *
     u32 nin, ntot;
     wave_group_split_emit<0>(key, m, obuf + ooff[c], nin, ntot);
     if (l == 0) {
+      cnt_in[c] = nin;
+      cnt_tot[c] = ntot;
+    }
+  }
+}
+
+// Pairs with a bound of 65 .. CINC_SMALL: a wave each, the keys sorted in
+// registers (4, 8 or 16 a lane, by the bound), inbound hyperedges first.
+template <int PER>
+__device__ __forceinline__ void cinc_regs(const i64 *n_off, const u32 *n_nin, const u32 *n_inc,
+                                          u32 a, u32 b, u32 m, u32 *out, u32 &nin, u32 &ntot) {
+  const u32 l = lane_id();
+  u64 v[PER];
+#pragma unroll
+  for (u32 q = 0; q < (u32)PER; ++q) {
+    const u32 i = q * WAVE + l;
+    v[q] = i < m ? inc_key(n_off, n_nin, n_inc, a, b, i) : ~0ull;
+  }
+  wave_sort_regs<u64, PER>(v);
+  wave_group_split_emit_regs<0, PER>(v, m, out, nin, ntot);
+}
+
+__global__ __launch_bounds__(256) void k_cinc_wreg(const i64 *n_off, const u32 *n_nin,
+                                                   const u32 *n_inc, const u32 *rep_of,
+                                                   const u32 *match, const i64 *ooff, u32 *obuf,
+                                                   u32 *cnt_in, u32 *cnt_tot, const u32 *list,
+                                                   const u32 *cnt) {
+  const u32 total = *cnt;
+  const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
+  for (u32 w = blockIdx.x * (blockDim.x / WAVE) + wave_id(); w < total; w += nwaves) {
+    const u32 c = list[w];
+    const u32 a = rep_of[c], b = match[a];
+    const u32 m = (u32)(n_off[a + 1] - n_off[a] + n_off[b + 1] - n_off[b]);
+    u32 nin, ntot;
+    u32 *out = obuf + ooff[c];
+    if (m <= 4 * WAVE) cinc_regs<4>(n_off, n_nin, n_inc, a, b, m, out, nin, ntot);
+    else if (m <= 8 * WAVE) cinc_regs<8>(n_off, n_nin, n_inc, a, b, m, out, nin, ntot);
+    else cinc_regs<16>(n_off, n_nin, n_inc, a, b, m, out, nin, ntot);
+    if (lane_id() == 0) {
       cnt_in[c] = nin;
       cnt_tot[c] = ntot;
     }
@@ -368,11 +408,12 @@ void launch_cinc_build(chp_ctx *c, const i64 *n_off, const u32 *n_nin, const u32
     CHP_LAUNCH(c, "cinc_wave", k_cinc_wave, waves_grid(host_cnt[0]), 256, 0, n_off, n_nin, n_inc,
                rep_of, match, ooff, obuf, cnt_in, cnt_tot, (const u32 *)el.list[0],
                (const u32 *)el.cnt + 0);
-  if (host_cnt[1])
-    CHP_LAUNCH(c, "cinc_lds", (k_cinc_lds<256, CINC_SMALL>),
-               host_cnt[1] > 8192 ? 8192 : host_cnt[1], 256, 0, n_off, n_nin, n_inc, rep_of,
-               match, ooff, obuf, cnt_in, cnt_tot, (const u32 *)el.list[1],
-               (const u32 *)el.cnt + 1);
+  if (host_cnt[1]) {
+    const u32 gw = (host_cnt[1] + 3) / 4;
+    CHP_LAUNCH(c, "cinc_wreg", k_cinc_wreg, gw < 32 * c->n_cu ? gw : 32 * c->n_cu, 256, 0, n_off,
+               n_nin, n_inc, rep_of, match, ooff, obuf, cnt_in, cnt_tot,
+               (const u32 *)el.list[1], (const u32 *)el.cnt + 1);
+  }
   if (host_cnt[3])
     CHP_LAUNCH(c, "cinc_lds", (k_cinc_lds<256, LDS_CAP_U64>),
                host_cnt[3] > 8192 ? 8192 : host_cnt[3], 256, 0, n_off, n_nin, n_inc, rep_of,

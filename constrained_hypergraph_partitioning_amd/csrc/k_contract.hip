@@ -116,9 +116,9 @@ __global__ __launch_bounds__(256) void k_econ_tiny(const i64 *e_off, const u32 *
 }
 
 // The LDS class (65 .. LDS_CAP_U64 pins) split by size: those of at most
-// ECON_SMALL pins go to small[0, small_cnt[0]) for a workgroup with an 8 KB
-// table (many per CU), the others to big[0, small_cnt[1]) for the 64 KB one
-// (two per CU).  small_cnt[0..1] zeroed before; one thread per list entry.
+// ECON_SMALL pins go to small[0, small_cnt[0]) for a wave each (keys in
+// registers), the others to big[0, small_cnt[1]) for a workgroup with a
+// 64 KB LDS table (two per CU).  small_cnt[0..1] zeroed before; one thread per list entry.
 constexpr u32 ECON_SMALL = 1024;
 __global__ __launch_bounds__(256) void k_econ_split(const i64 *e_off, const u32 *list,
                                                     const u32 *cnt, u32 *small, u32 *big,
@@ -206,6 +206,43 @@ __global__ __launch_bounds__(256) void k_econ_wave(const i64 *e_off, const u32 *
     u32 nsp, ntot;
     wave_group_split_emit<1>(key, len, opins + a, nsp, ntot);
     if (l == 0) {
+      olen[e] = ntot;
+      onsrc[e] = nsp;
+    }
+  }
+}
+
+// Hyperedges of 65 .. ECON_SMALL pins: a wave each, the keys sorted in
+// registers (4, 8 or 16 a lane, by |e|), distinct sources first.
+template <int PER>
+__device__ __forceinline__ void econ_regs(const u32 *pins, i64 a, u32 len, u32 ns,
+                                          const u32 *gamma, u32 *out, u32 &nsp, u32 &ntot) {
+  const u32 l = lane_id();
+  u64 v[PER];
+#pragma unroll
+  for (u32 q = 0; q < (u32)PER; ++q) {
+    const u32 i = q * WAVE + l;
+    v[q] = i < len ? ((u64)gamma[pins[a + i]] << 1) | (i < ns ? 1u : 0u) : ~0ull;
+  }
+  wave_sort_regs<u64, PER>(v);
+  wave_group_split_emit_regs<1, PER>(v, len, out, nsp, ntot);
+}
+
+__global__ __launch_bounds__(256) void k_econ_wreg(const i64 *e_off, const u32 *e_nsrc,
+                                                   const u32 *pins, const u32 *gamma, u32 *opins,
+                                                   u32 *olen, u32 *onsrc, const u32 *list,
+                                                   const u32 *cnt) {
+  const u32 total = *cnt;
+  const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
+  for (u32 w = blockIdx.x * (blockDim.x / WAVE) + wave_id(); w < total; w += nwaves) {
+    const u32 e = list[w];
+    const i64 a = e_off[e];
+    const u32 len = (u32)(e_off[e + 1] - a), ns = e_nsrc[e];
+    u32 nsp, ntot;
+    if (len <= 4 * WAVE) econ_regs<4>(pins, a, len, ns, gamma, opins + a, nsp, ntot);
+    else if (len <= 8 * WAVE) econ_regs<8>(pins, a, len, ns, gamma, opins + a, nsp, ntot);
+    else econ_regs<16>(pins, a, len, ns, gamma, opins + a, nsp, ntot);
+    if (lane_id() == 0) {
       olen[e] = ntot;
       onsrc[e] = nsp;
     }
@@ -325,9 +362,10 @@ void launch_edge_contract(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const
     u32 *small = rest + 2ull * host_cnt[0], *big = small + host_cnt[1];
     CHP_LAUNCH(c, "econ_split", k_econ_split, grid_for(host_cnt[1], 256), 256, 0, e_off,
                (const u32 *)el.list[1], (const u32 *)el.cnt + 1, small, big, el.cnt + 6);
-    CHP_LAUNCH(c, "econ_lds", (k_econ_lds<256, ECON_SMALL>),
-               host_cnt[1] > 8192 ? 8192 : host_cnt[1], 256, 0, e_off, e_nsrc, pins, gamma, opins,
-               olen, onsrc, (const u32 *)small, (const u32 *)el.cnt + 6);
+    const u32 gw = (host_cnt[1] + 3) / 4;
+    CHP_LAUNCH(c, "econ_wreg", k_econ_wreg, gw < 32 * c->n_cu ? gw : 32 * c->n_cu, 256, 0, e_off,
+               e_nsrc, pins, gamma, opins, olen, onsrc, (const u32 *)small,
+               (const u32 *)el.cnt + 6);
     CHP_LAUNCH(c, "econ_lds", (k_econ_lds<256, LDS_CAP_U64>),
                host_cnt[1] > 8192 ? 8192 : host_cnt[1], 256, 0, e_off, e_nsrc, pins, gamma, opins,
                olen, onsrc, (const u32 *)big, (const u32 *)el.cnt + 7);
