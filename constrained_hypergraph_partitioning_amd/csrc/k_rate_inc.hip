@@ -599,11 +599,14 @@ __global__ __launch_bounds__(FB) void k_rate_inc(RateArgs A, const NodeRec *recs
 }
 
 // Nodes of [0, N) with 1..FRUNS/2 incident hyperedges and min_visits to
-// 2^27 - 1 pins over them (the estimates in sixteenths stay below 2^31) go to the list (record: n, nin, size, deg, i0 and the pin
-// count in nb0) and get skip[n] = 1; gmax = {max size, max |in|} over all.
+// 2^27 - 1 pins over them (the estimates in sixteenths stay below 2^31) go to
+// the list (record: n, nin, size, deg, i0 and the pin count in nb0) and get
+// skip[n] = 1; gmax = {max size, max |in|} over all.  Thread n holds node n;
+// the pin counts are summed by the whole wave, node after node.
 __global__ void k_inc_classify(RateArgs A, u64 min_visits, uint8_t *skip, NodeRec *recs,
                                u32 *cnt, u32 *gmax) {
   const u32 n = blockIdx.x * blockDim.x + threadIdx.x;
+  const u32 l = lane_id();
   bool take_it = false;
   u32 sz = 0, ni = 0, deg = 0;
   u64 w = 0;
@@ -613,13 +616,26 @@ __global__ void k_inc_classify(RateArgs A, u64 min_visits, uint8_t *skip, NodeRe
     deg = (u32)(A.n_off[n + 1] - a);
     sz = A.n_size[n];
     ni = A.n_nin[n];
-    if (deg >= 1 && deg <= FRUNS / 2) {
-      for (u32 j = 0; j < deg; ++j) {
-        const u32 e = A.n_inc[a + j];
-        w += (u64)(A.e_off[e + 1] - A.e_off[e]);
-      }
-      take_it = w >= min_visits && w < (1ull << 27);
+  }
+  const bool counted = n < A.N && deg >= 1 && deg <= FRUNS / 2;
+  u64 todo = __ballot(counted);
+  while (todo) {
+    const u32 i = (u32)__builtin_ctzll(todo);
+    todo &= todo - 1;
+    const u32 di = (u32)__builtin_amdgcn_readlane((int)deg, (int)i);
+    const i64 ai = (i64)((u64)(u32)__builtin_amdgcn_readlane((int)(u32)((u64)a >> 32), (int)i)
+                             << 32 |
+                         (u32)__builtin_amdgcn_readlane((int)(u32)(u64)a, (int)i));
+    u64 part = 0;
+    for (u32 j = l; j < di; j += WAVE) {
+      const u32 e = A.n_inc[ai + j];
+      part += (u64)(A.e_off[e + 1] - A.e_off[e]);
     }
+    part = wave_sum(part);
+    if (l == i) w = part;
+  }
+  if (n < A.N) {
+    take_it = counted && w >= min_visits && w < (1ull << 27);
     skip[n] = take_it ? 1 : 0;
   }
   u32 msz = sz, mni = ni;
