@@ -856,7 +856,20 @@ void rate_batched(chp_ctx *c, Scratch &s, const chp_hgraph *g, const RateArgs &a
     NodeRec *spill = s.get<NodeRec>(nf);
     u32 *sc = s.get<u32>(2);  // spill count, work counter of the second launch
     launch_fill_u32(c, sc, 2, 0);
-    launch_rate_incq(c, a, frecs, fc, fc + 1, fc + 3, nf, c->inc_hash_keys, spill, sc);
+    // every 16th pin of each run, for the nodes' samples (their offsets are
+    // held in 32 bits)
+    const u32 E = g->n_edges;
+    i64 *soff = nullptr;
+    u32 *samp = nullptr;
+    if (samples_bound(E, g->n_pins) < (1ull << 31)) {
+      u32 *scnt = s.get<u32>(E);
+      soff = s.get<i64>((u64)E + 1);
+      i64 *stmp = s.get<i64>(scan_tmp_words(E));
+      samp = s.get<u32>(samples_bound(E, g->n_pins));
+      launch_samples(c, E, g->e_off, g->e_nsrc, g->e_pins, scnt, soff, stmp, samp);
+    }
+    launch_rate_incq(c, a, frecs, fc, fc + 1, fc + 3, nf, c->inc_hash_keys, spill, sc, soff,
+                     samp);
     launch_rate_inc(c, a, spill, sc, fc + 1, sc + 1, c->n_cu, c->inc_hash_keys);
   } else {
     launch_rate_inc(c, a, frecs, fc, fc + 1, fc + 3, nf, c->inc_hash_keys);

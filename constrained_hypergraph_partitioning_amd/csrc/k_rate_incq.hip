@@ -30,6 +30,11 @@
 // reach the best lower bound, no id of the window can win and the window is
 // done; otherwise the same window is visited again with a hash table.
 //
+// The samples of a run are the first pins of its blocks of 2^sh pins.  Where
+// sh >= QSG they come from a per-level array holding every 2^QSG-th pin of
+// each run (k_samples_fill), so that a run's samples lie within a line or two
+// instead of one line each.
+//
 // Run stretches are exact at their start: every run carries its cursor, the
 // first pin at or above the window's low end, found during the visits of the
 // window before (the first pin at or above that window's end).  Only the end
@@ -54,6 +59,7 @@ constexpr u32 QCAP = QHS * 3 / 4;     // keys a hash window claims before it rep
 constexpr u32 QE = 384;               // incident hyperedges
 constexpr u32 QRUNS = 2 * QE;         // a source and a destination run per hyperedge
 constexpr u32 QSMAX = 4096;           // sampled blocks
+constexpr u32 QSG = 4;                // log2 of the per-level sample array's step
 constexpr u32 QNHB = 1024;            // estimate buckets
 constexpr u32 QBS_MIN = 12;           // log2 of the narrowest bucket
 constexpr u32 QHTGT = QCAP * 3 / 4;   // estimated visits a hash window aims at
@@ -98,6 +104,7 @@ struct QSmem {
   i64 eoff[QE];
   u64 tx[QE];    // exact t(e)
   u32 eid[QE];
+  u32 soff[QE];  // its first entry in the per-level sample array
   u32 ens[QE];   // source pins
   u32 elen[QE];  // pins
   u32 q[QE];     // t(e) >> s
@@ -368,7 +375,8 @@ __device__ __forceinline__ void q_judge(const RateArgs &A, QSmem &S, u32 n, u32 
 // Rates node h; false (and nothing written, the bins left empty) when the
 // node must go to k_rate_inc instead.
 __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 max_size,
-                            u32 max_nin, u32 hcap, u64 cap, u64 dmod, u64 magic) {
+                            u32 max_nin, u32 hcap, u64 cap, u64 dmod, u64 magic,
+                            const i64 *samp_off, const u32 *samp) {
   // the thread index is re-read per node through an empty asm, so that the
   // compiler recomputes the slot addresses derived from it inside each node
   // instead of holding dozens of them in registers across the node loop
@@ -397,6 +405,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     S.eoff[tid] = a;
     S.tx[tid] = te;
     S.eid[tid] = e;
+    if (samp) S.soff[tid] = (u32)samp_off[e];
     S.ens[tid] = ns;
     S.elen[tid] = (u32)(b - a);
   }
@@ -446,6 +455,7 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
   // run's thread into rlast, which is cnext until the windows)
   u32 *const rlast = S.cnext;
   constexpr u32 SPT = QSMAX / QB;
+  const bool from_samp = samp && sh >= QSG;
   u32 sf[SPT], sw[SPT], sr[SPT];
   u32 mn = 0xFFFFFFFFu, mx = 0;
   if (tid < deg) {
@@ -470,7 +480,9 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       const i64 base = S.eoff[ke] + ((r & 1) ? S.ens[ke] : 0);
       const u32 p0 = (g - S.rsp[r]) << sh;
       const u32 p1 = (p0 + (1u << sh) < len ? p0 + (1u << sh) : len) - 1;
-      sf[k] = A.e_pins[base + p0];
+      sf[k] = from_samp ? samp[S.soff[ke] + ((r & 1) ? (S.ens[ke] + (1u << QSG) - 1) >> QSG : 0u) +
+                               (p0 >> QSG)]
+                        : A.e_pins[base + p0];
       sw[k] = p1 + 1 - p0;
       sr[k] = r;
     }
@@ -986,7 +998,8 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
 // appended to `spill` for k_rate_inc.
 __global__ __launch_bounds__(QB) void k_rate_incq(RateArgs A, const NodeRec *recs, const u32 *cnt,
                                                   const u32 *gmax, u32 *work, u32 hcap,
-                                                  NodeRec *spill, u32 *spill_cnt) {
+                                                  NodeRec *spill, u32 *spill_cnt,
+                                                  const i64 *samp_off, const u32 *samp) {
   __shared__ QSmem S;
   const u32 tid = threadIdx.x;
   const u64 cap = A.capinfo[0], dmod = A.capinfo[1], magic = A.capinfo[2];
@@ -1005,20 +1018,57 @@ __global__ __launch_bounds__(QB) void k_rate_incq(RateArgs A, const NodeRec *rec
     h.deg = rfl(h.deg);
     h.nin = rfl(h.nin);
     h.size = rfl(h.size);
-    const bool done = rate_node_q(A, S, h, max_size, max_nin, hcap, cap, dmod, magic);
+    const bool done =
+        rate_node_q(A, S, h, max_size, max_nin, hcap, cap, dmod, magic, samp_off, samp);
     if (!done && tid == 0) spill[atomicAdd(spill_cnt, 1u)] = recs[w];
     __syncthreads();
   }
 }
 
+// Entries of hyperedge e in the sample array: every 2^QSG-th pin of its
+// source run, then of its destination run.
+__global__ void k_samples_count(u32 E, const i64 *e_off, const u32 *e_nsrc, u32 *cnt) {
+  const u32 e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  const u32 len = (u32)(e_off[e + 1] - e_off[e]), ns = e_nsrc[e];
+  cnt[e] = ((ns + (1u << QSG) - 1) >> QSG) + ((len - ns + (1u << QSG) - 1) >> QSG);
+}
+
+// A wave per hyperedge, a lane per entry.
+__global__ __launch_bounds__(256) void k_samples_fill(u32 E, const i64 *e_off, const u32 *e_nsrc,
+                                                      const u32 *pins, const i64 *samp_off,
+                                                      u32 *samp) {
+  const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
+  const u32 l = lane_id();
+  for (u32 e = blockIdx.x * (blockDim.x / WAVE) + wave_id(); e < E; e += nwaves) {
+    const i64 a = e_off[e], o = samp_off[e];
+    const u32 ns = e_nsrc[e];
+    const u32 c0 = (ns + (1u << QSG) - 1) >> QSG, c = (u32)(samp_off[e + 1] - o);
+    for (u32 j = l; j < c; j += WAVE)
+      samp[o + j] = pins[a + (j < c0 ? (i64)j << QSG : (i64)ns + ((i64)(j - c0) << QSG))];
+  }
+}
+
 }  // namespace
+
+void launch_samples(chp_ctx *c, u32 E, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
+                    u32 *cnt, i64 *samp_off, i64 *tmp, u32 *samp) {
+  if (E == 0) return;
+  CHP_LAUNCH(c, "samples_count", k_samples_count, grid_for(E, 256), 256, 0, E, e_off, e_nsrc,
+             cnt);
+  scan_u32_to_i64(c, cnt, samp_off, E, tmp);
+  CHP_LAUNCH(c, "samples_fill", k_samples_fill, waves_grid(E), 256, 0, E, e_off, e_nsrc, pins,
+             samp_off, samp);
+}
+
+u64 samples_bound(u32 E, u64 P) { return (P >> QSG) + 2ull * E; }
 
 void launch_rate_incq(chp_ctx *c, const RateArgs &a, const NodeRec *recs, const u32 *cnt,
                       const u32 *gmax, u32 *work, u32 host_count, u32 hash_keys, NodeRec *spill,
-                      u32 *spill_cnt) {
+                      u32 *spill_cnt, const i64 *samp_off, const u32 *samp) {
   if (!host_count) return;
   const u32 g = host_count < c->n_cu ? host_count : c->n_cu;
   const u32 hcap = hash_keys && hash_keys < QCAP ? hash_keys : QCAP;
   CHP_LAUNCH(c, "rate_incq", k_rate_incq, g, QB, 0, a, recs, cnt, gmax, work, hcap, spill,
-             spill_cnt);
+             spill_cnt, samp_off, samp);
 }

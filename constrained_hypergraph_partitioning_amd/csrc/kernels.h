@@ -210,9 +210,17 @@ void launch_rate_inc(chp_ctx *c, const RateArgs &a, const NodeRec *recs, const u
 // The same nodes with 32-bit bins (k_rate_incq.hip) where Delta cannot bind
 // for the node; the nodes it cannot rate are appended to spill / *spill_cnt
 // (zeroed before) for launch_rate_inc.
+// samp_off / samp: the per-level sample array of launch_samples, or null
+// (the samples are then read from the pins).
 void launch_rate_incq(chp_ctx *c, const RateArgs &a, const NodeRec *recs, const u32 *cnt,
                       const u32 *gmax, u32 *work, u32 host_count, u32 hash_keys, NodeRec *spill,
-                      u32 *spill_cnt);
+                      u32 *spill_cnt, const i64 *samp_off, const u32 *samp);
+// Every 16th pin of each run of each hyperedge (source run, then destination
+// run) into samp[samp_off[e] ..]; samp_off [E + 1] by a scan of cnt [E] (tmp:
+// scan_tmp_words(E)); samp holds samples_bound(E, P) entries.
+void launch_samples(chp_ctx *c, u32 E, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
+                    u32 *cnt, i64 *samp_off, i64 *tmp, u32 *samp);
+u64 samples_bound(u32 E, u64 P);
 
 struct MatchScratch {
   u64 *bscore;  // [N] zeroed
