@@ -212,17 +212,18 @@ __global__ __launch_bounds__(BLOCK) void k_runs_global(u32 *data, const i64 *sta
 
 // ---------------------------------------------------------------------------
 // incidence: degrees, feasibility, scatter, per-node runs
-// Degrees and the scatter take the hyperedges in chunks of DW_EDGES
-// consecutive ones, a workgroup of DW_BLOCK threads each (a wave per
-// hyperedge, the lanes over its pins).  A destination whose id falls in the
-// chunk's window of DW_IDS ids counts in LDS (16-bit counts, two a word);
-// where hyperedges are local to their sources (nodes of a ring, a block, a
-// grid) most do, and a chunk then costs one global atomic per id of the
-// window it touched instead of one per pin.  The window is centred on the
-// median of 64 pins sampled evenly from the chunk.  A chunk adds at most
-// DW_EDGES to an id's count (an id is a destination of a valid hyperedge at
-// most once).  Sources, and destinations outside the window, count in global
-// memory directly.
+// Degrees and the scatter take the hyperedges in chunks of epc consecutive
+// ones (at most DW_EDGES, fewer where the graph would not fill the GPU), a
+// workgroup of DW_BLOCK threads each (a wave per hyperedge, the lanes over
+// its pins).  A destination whose id falls in the chunk's window of DW_IDS
+// ids counts in LDS (16-bit counts, two a word); where hyperedges are local
+// to their sources (nodes of a ring, a block, a grid) most do, and a chunk
+// then costs one global atomic per id of the window it touched instead of
+// one per pin.  The window is centred on the median of 64 pins sampled
+// evenly from the chunk.  A chunk adds at most epc <= DW_EDGES to an id's
+// count (an id is a destination of a valid hyperedge at most once).
+// Sources, and destinations outside the window, count in global memory
+// directly.
 constexpr u32 DW_EDGES = 2048, DW_IDS = 65536, DW_BLOCK = 1024;
 
 // The low end of the chunk's window into *s_wb (wave 0; the caller waits).
@@ -237,15 +238,15 @@ __device__ __forceinline__ void chunk_window(const u32 *pins, i64 a0, i64 a1, u3
   if (l == 0) *s_wb = span == 0 ? 0u : (med > DW_IDS / 2 ? med - DW_IDS / 2 : 0u);
 }
 
-__global__ __launch_bounds__(DW_BLOCK) void k_degrees(u32 E, const i64 *e_off,
+__global__ __launch_bounds__(DW_BLOCK) void k_degrees(u32 E, u32 epc, const i64 *e_off,
                                                       const u32 *e_nsrc, const u32 *pins,
                                                       u32 *indeg, u32 *outdeg) {
   __shared__ u32 h[DW_IDS / 2];
   __shared__ u32 s_wb;
-  const u32 nch = (E + DW_EDGES - 1) / DW_EDGES;
+  const u32 nch = (E + epc - 1) / epc;
   const u32 l = lane_id();
   for (u32 ch = blockIdx.x; ch < nch; ch += gridDim.x) {
-    const u32 e0 = ch * DW_EDGES, e1 = E - e0 < DW_EDGES ? E : e0 + DW_EDGES;
+    const u32 e0 = ch * epc, e1 = E - e0 < epc ? E : e0 + epc;
     for (u32 i = threadIdx.x; i < DW_IDS / 2; i += DW_BLOCK) h[i] = 0;
     chunk_window(pins, e_off[e0], e_off[e1], &s_wb);
     __syncthreads();
@@ -287,16 +288,16 @@ __global__ void k_node_feas(u32 N, const u32 *indeg, const u32 *outdeg, const u3
 // which the second pass hands out (an LDS atomic per pin).  An id whose
 // in-degree may not fit 16 bits (n_nin >= 0xFFFF) is marked 0xFFFF and its
 // pins take the global cursor one by one, as outside the window.
-__global__ __launch_bounds__(DW_BLOCK) void k_scatter(u32 E, const i64 *e_off,
+__global__ __launch_bounds__(DW_BLOCK) void k_scatter(u32 E, u32 epc, const i64 *e_off,
                                                       const u32 *e_nsrc, const u32 *pins,
                                                       const i64 *n_off, const u32 *n_nin,
                                                       u32 *cur_in, u32 *cur_out, u32 *n_inc) {
   __shared__ u32 h[DW_IDS / 2];
   __shared__ u32 s_wb;
-  const u32 nch = (E + DW_EDGES - 1) / DW_EDGES;
+  const u32 nch = (E + epc - 1) / epc;
   const u32 l = lane_id();
   for (u32 ch = blockIdx.x; ch < nch; ch += gridDim.x) {
-    const u32 e0 = ch * DW_EDGES, e1 = E - e0 < DW_EDGES ? E : e0 + DW_EDGES;
+    const u32 e0 = ch * epc, e1 = E - e0 < epc ? E : e0 + epc;
     for (u32 i = threadIdx.x; i < DW_IDS / 2; i += DW_BLOCK) h[i] = 0;
     chunk_window(pins, e_off[e0], e_off[e1], &s_wb);
     __syncthreads();
@@ -558,11 +559,19 @@ void launch_edges_check(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const u
              list, count, c->flags);
 }
 
+// Hyperedges per chunk of the degree and scatter kernels: four chunks per CU,
+// from 64 to DW_EDGES.
+static u32 chunk_edges(const chp_ctx *c, u32 E) {
+  const u32 per = E / (4 * c->n_cu);
+  return per < 64 ? 64 : per > DW_EDGES ? DW_EDGES : per;
+}
+
 void launch_degrees(chp_ctx *c, u32 E, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
                     u32 *indeg, u32 *outdeg) {
   if (E == 0) return;
-  const u32 nch = (E + DW_EDGES - 1) / DW_EDGES;
-  CHP_LAUNCH(c, "degrees", k_degrees, nch, DW_BLOCK, 0, E, e_off, e_nsrc, pins, indeg, outdeg);
+  const u32 epc = chunk_edges(c, E);
+  CHP_LAUNCH(c, "degrees", k_degrees, (E + epc - 1) / epc, DW_BLOCK, 0, E, epc, e_off, e_nsrc,
+             pins, indeg, outdeg);
 }
 
 void launch_node_feas(chp_ctx *c, u32 N, const u32 *indeg, const u32 *outdeg, const u32 *n_size,
@@ -575,9 +584,9 @@ void launch_node_feas(chp_ctx *c, u32 N, const u32 *indeg, const u32 *outdeg, co
 void launch_scatter(chp_ctx *c, u32 E, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
                     const i64 *n_off, const u32 *n_nin, u32 *cur_in, u32 *cur_out, u32 *n_inc) {
   if (E == 0) return;
-  const u32 nch = (E + DW_EDGES - 1) / DW_EDGES;
-  CHP_LAUNCH(c, "scatter", k_scatter, nch, DW_BLOCK, 0, E, e_off, e_nsrc, pins, n_off, n_nin,
-             cur_in, cur_out, n_inc);
+  const u32 epc = chunk_edges(c, E);
+  CHP_LAUNCH(c, "scatter", k_scatter, (E + epc - 1) / epc, DW_BLOCK, 0, E, epc, e_off, e_nsrc,
+             pins, n_off, n_nin, cur_in, cur_out, n_inc);
 }
 
 void launch_node_runs(chp_ctx *c, u32 N, const i64 *n_off, const u32 *n_nin, RunLists rl) {
