@@ -349,6 +349,13 @@ __device__ __forceinline__ K wave_sort64(K v) {
   return v;
 }
 
+// Compare-exchange: x takes the smaller key, y the larger.
+__device__ __forceinline__ void cswap(u64 &x, u64 &y) {
+  const u64 lo = x < y ? x : y, hi = x < y ? y : x;
+  x = lo;
+  y = hi;
+}
+
 // Bitonic sort of 64 PER keys across a wave, PER a lane (afterwards lane l
 // holds sorted positions PER l .. PER l + PER - 1, ascending; where each key
 // starts does not matter): the compare-exchanges at distances below PER stay

@@ -56,11 +56,6 @@ __global__ __launch_bounds__(256) void k_edge_classify(u32 E, const i64 *e_off, 
 // to k_econ_wave, with T = *cnt; rest holds 2 T entries and rest_cnt[0..1]
 // are zeroed before.  One thread per entry of list[0, *cnt).
 constexpr u32 TINY = 8;
-__device__ __forceinline__ void cswap(u64 &x, u64 &y) {
-  const u64 lo = x < y ? x : y, hi = x < y ? y : x;
-  x = lo;
-  y = hi;
-}
 __global__ __launch_bounds__(256) void k_econ_tiny(const i64 *e_off, const u32 *e_nsrc,
                                                    const u32 *pins, const u32 *gamma, u32 *opins,
                                                    u32 *olen, u32 *onsrc, const u32 *list,

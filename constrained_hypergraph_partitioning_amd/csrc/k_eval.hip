@@ -6,8 +6,9 @@
 // number, and each one holding a destination pin is a partition that e
 // enters (e counts once towards that partition's inbound set).  Hyperedges of
 // at most 64 pins and those above 512 sort 64-bit keys (rho << 1 | is_source:
-// a group of equal rho whose first key is a destination is entered); the
-// others insert rho into a hash table per wave, destinations first.
+// a group of equal rho whose first key is a destination is entered), those
+// of at most 8 in one lane's registers; the others insert rho into a hash
+// table per wave, destinations first.
 #include "dev.h"
 #include "kernels.h"
 
@@ -42,9 +43,13 @@ __device__ __forceinline__ void flush_sums(u64 conn, u64 cut, u64 lam, u64 *summ
   if (lam) atomicAdd((unsigned long long *)&summary[7], (unsigned long long)lam);
 }
 
-// A wave per hyperedge of at most 64 pins.  The sums are gathered per
-// workgroup and flushed by one thread (three atomics per workgroup: the grid
-// is a few workgroups per CU, so the shared summary words see few atomics).
+// Hyperedges of at most 64 pins.  A wave takes 64 consecutive entries of the
+// list, a lane each: a hyperedge of at most 8 pins (most nets of a netlist)
+// is done by its own lane, its keys sorted in registers by a 19-comparator
+// network; the others one after the other by the whole wave (a key per lane,
+// a wave bitonic sort).  The sums are gathered per workgroup and flushed by
+// one thread (three atomics per workgroup: the grid is a few workgroups per
+// CU, so the shared summary words see few atomics).
 __global__ __launch_bounds__(256) void k_eval_wave(const i64 *e_off, const u32 *e_nsrc,
                                                    const u32 *pins, const u32 *e_w,
                                                    const u32 *rho, u32 k, u32 *part_inb,
@@ -55,24 +60,70 @@ __global__ __launch_bounds__(256) void k_eval_wave(const i64 *e_off, const u32 *
   const u32 nwaves = gridDim.x * (blockDim.x / WAVE);
   const u32 l = lane_id();
   u64 conn = 0, cut = 0, lams = 0;
-  for (u32 w = blockIdx.x * (blockDim.x / WAVE) + wave_id(); w < total; w += nwaves) {
-    const u32 e = list[w];
-    const i64 a = e_off[e];
-    const u32 len = (u32)(e_off[e + 1] - a), ns = e_nsrc[e];
-    u64 key = ~0ull;
-    if (l < len) key = eval_key(rho, k, pins[a + l], l < ns, flags);
-    key = wave_sort64(key);
-    const u64 prev = __shfl_up(key, 1, WAVE);
-    const bool first = l < len && (l == 0 || (prev >> 1) != (key >> 1));
-    if (first && !(key & 1)) atomicAdd(&part_inb[key >> 1], 1u);
-    const u64 lam = (u64)__popcll(__ballot(first));
-    if (l == 0) {
+  for (u32 w0 = (blockIdx.x * (blockDim.x / WAVE) + wave_id()) * WAVE; w0 < total;
+       w0 += nwaves * WAVE) {
+    const u32 w = w0 + l;
+    u32 e = 0, len = 0, ns = 0;
+    i64 a = 0;
+    if (w < total) {
+      e = list[w];
+      a = e_off[e];
+      len = (u32)(e_off[e + 1] - a);
+      ns = e_nsrc[e];
+    }
+    const bool tiny = w < total && len <= 8;
+    if (tiny) {
+      u64 key[8];
+#pragma unroll
+      for (u32 j = 0; j < 8; ++j)
+        key[j] = j < len ? eval_key(rho, k, pins[a + j], j < ns, flags) : ~0ull;
+      cswap(key[0], key[2]), cswap(key[1], key[3]), cswap(key[4], key[6]), cswap(key[5], key[7]);
+      cswap(key[0], key[4]), cswap(key[1], key[5]), cswap(key[2], key[6]), cswap(key[3], key[7]);
+      cswap(key[0], key[1]), cswap(key[2], key[3]), cswap(key[4], key[5]), cswap(key[6], key[7]);
+      cswap(key[2], key[4]), cswap(key[3], key[5]);
+      cswap(key[1], key[4]), cswap(key[3], key[6]);
+      cswap(key[1], key[2]), cswap(key[3], key[4]), cswap(key[5], key[6]);
+      u64 lam = 0;
+#pragma unroll
+      for (u32 j = 0; j < 8; ++j) {
+        if (j < len && (j == 0 || (key[j - 1] >> 1) != (key[j] >> 1))) {
+          ++lam;
+          if (!(key[j] & 1)) atomicAdd(&part_inb[key[j] >> 1], 1u);
+        }
+      }
       const u64 we = e_w[e];
       conn += we * (lam - 1);
       cut += lam > 1 ? we : 0;
       lams += lam;
     }
+    u64 rest = __ballot(w < total && !tiny);
+    while (rest) {
+      const u32 i = (u32)__builtin_ctzll(rest);
+      rest &= rest - 1;
+      const u32 ei = (u32)__builtin_amdgcn_readlane((int)e, (int)i);
+      const u32 li = (u32)__builtin_amdgcn_readlane((int)len, (int)i);
+      const u32 nsi = (u32)__builtin_amdgcn_readlane((int)ns, (int)i);
+      const i64 ai = (i64)((u64)(u32)__builtin_amdgcn_readlane((int)(u32)((u64)a >> 32), (int)i)
+                               << 32 |
+                           (u32)__builtin_amdgcn_readlane((int)(u32)(u64)a, (int)i));
+      u64 key = ~0ull;
+      if (l < li) key = eval_key(rho, k, pins[ai + l], l < nsi, flags);
+      key = wave_sort64(key);
+      const u64 prev = __shfl_up(key, 1, WAVE);
+      const bool first = l < li && (l == 0 || (prev >> 1) != (key >> 1));
+      if (first && !(key & 1)) atomicAdd(&part_inb[key >> 1], 1u);
+      const u64 lam = (u64)__popcll(__ballot(first));
+      if (l == 0) {
+        const u64 we = e_w[ei];
+        conn += we * (lam - 1);
+        cut += lam > 1 ? we : 0;
+        lams += lam;
+      }
+    }
   }
+  conn = wave_sum(conn);
+  cut = wave_sum(cut);
+  lams = wave_sum(lams);
   if (l == 0) {
     s_sum[0][wave_id()] = conn;
     s_sum[1][wave_id()] = cut;
@@ -323,12 +374,12 @@ void launch_eval_edges(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const u3
                        const u32 *e_w, const u32 *rho, u32 k, u32 *part_inb, u64 *summary,
                        EdgeLists el, const u32 *host_cnt, u64 *scratch, u64 per_wg,
                        u32 grid_big) {
-  if (host_cnt[0])
-    CHP_LAUNCH(c, "eval_wave", k_eval_wave,
-               waves_grid(host_cnt[0]) < 8 * c->n_cu ? waves_grid(host_cnt[0]) : 8 * c->n_cu, 256,
-               0, e_off, e_nsrc, pins,
-               e_w, rho, k, part_inb, summary, (const u32 *)el.list[0], (const u32 *)el.cnt + 0,
-               c->flags);
+  if (host_cnt[0]) {
+    const u32 gw = (host_cnt[0] + 4 * WAVE - 1) / (4 * WAVE);  // 64 entries a wave
+    CHP_LAUNCH(c, "eval_wave", k_eval_wave, gw < 8 * c->n_cu ? gw : 8 * c->n_cu, 256, 0, e_off,
+               e_nsrc, pins, e_w, rho, k, part_inb, summary, (const u32 *)el.list[0],
+               (const u32 *)el.cnt + 0, c->flags);
+  }
   if (host_cnt[1]) {
     const u32 gh = (host_cnt[1] + 3) / 4;
     CHP_LAUNCH(c, "eval_hash", k_eval_hash<256>, gh < 32 * c->n_cu ? gh : 32 * c->n_cu, 256, 0,
