@@ -864,6 +864,47 @@ def test_wide_neighbourhoods_and_big_edges(chp, ctx):
     eval_pair(chp, ctx, dg, og, rho, 37, 1 << 30, 1 << 30, "big eval")
 
 
+def test_size_classes(chp, ctx):
+    """Every size class of the build, contraction and evaluation kernels on
+    one graph, against the oracle: hyperedges of 2..8 pins (evaluated by one
+    lane), 9..64 (a wave sort), 65..512 (a wave's hash table), and at the
+    bounds of the register sorts (4, 8 or 16 keys a lane up to 1,024), the
+    LDS sorts (up to 8,192) and the global sort beyond, given unsorted so that
+    their runs are sorted on the device, some with more than 64 sources; nodes
+    with in-degrees in every run-sort class, and a hub that is a destination of
+    66,000 hyperedges (its in-degree does not fit the scatter's 16-bit LDS
+    cursors).  Then two levels and an evaluation under a random partition."""
+    rng = np.random.Generator(np.random.PCG64(41))
+    n = 80000
+    hub = 40000
+    el = []
+    sizes = (3, 8, 9, 33, 64, 65, 200, 256, 257, 400, 512, 513, 700, 1024, 1025, 3000, 8194)
+    for k in sizes:
+        for rep in range(2 if k < 3000 else 1):
+            p = rng.choice(n, k, replace=False)
+            p = p[p != hub]
+            ns = 1 if rep == 0 else min(k // 3, 100)
+            el.append(([int(x) for x in p[:ns]], [int(x) for x in p[ns:]]))
+    # nodes of in-degree 80, 300, 700, 1500 and 9000 (run-sort classes)
+    for node, indeg in ((1000, 80), (2000, 300), (3000, 700), (4000, 1500), (5000, 9000)):
+        for _ in range(indeg):
+            p = rng.choice(np.arange(6000, 20000), 3, replace=False)
+            el.append(([int(p[0])], [node, int(p[1]), int(p[2])]))
+    # the hub: a destination of 66,000 small hyperedges of nearby nodes
+    for _ in range(66000):
+        p = hub - 2000 + rng.choice(4000, 3, replace=False)
+        p = p[p != hub][:2]
+        el.append(([int(p[0])], [hub] + [int(x) for x in p[1:]]))
+    order = rng.permutation(len(el))
+    el = [el[i] for i in order]
+    h = synth.from_lists(n, el, rng.integers(1, 9, len(el)).tolist())
+    say("size classes", len(el), "hyperedges", int(h.n_pins), "pins")
+    multilevel(chp, ctx, h, 1 << 30, 1 << 20, True, 41, 2, tag="classes")
+    dg, og = both(chp, ctx, h, 1 << 30, 1 << 20)
+    rho = synth.uniform_u32(41, 2, n, 500)
+    eval_pair(chp, ctx, dg, og, rho, 500, 1 << 30, 1 << 20, "classes eval")
+
+
 def test_sparse_span_neighbourhoods(chp, ctx):
     """Level-0 neighbourhoods of nodes whose pins spread over a wide id span
     (the workgroup-sort class: 64 < W_n <= 1024 and more bitmap words than
