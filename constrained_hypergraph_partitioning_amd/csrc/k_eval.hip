@@ -164,79 +164,141 @@ __device__ u32 eval_groups(const u64 *s, u32 m, u32 *part_inb, u32 *s_red) {
 // lane counts e towards that partition's inbound set), then the sources;
 // lambda(e) is the number of claims.  Each lane gathers all its pins' rho
 // before its first insert.
-constexpr u32 EH_MAX = 512;          // pins of the largest hyperedge hashed per wave
+//
+// A workgroup takes a chunk of consecutive hyperedges (by id, not from the
+// class list, whose order is that of the workgroups that filled it; at most
+// EV_CHUNK, fewer where the graph would not fill the GPU), its waves the
+// ones of this class among them.  Its inbound counts for the
+// partitions in a window of EV_IDS ids (centred on the median of the
+// partitions of 64 destinations sampled from the chunk) gather in LDS
+// (16-bit counts, two a word: a chunk adds at most EV_CHUNK to a partition)
+// and are flushed with one atomic per touched partition; where hyperedges
+// are local and the partition ids follow the node ids (as after a
+// contraction, whose coarse ids rise with the members' ids) most of them fall
+// in it.  The others count in global memory directly.
+constexpr u32 EH_MAX = 512;           // pins of the largest hyperedge hashed per wave
 constexpr u32 EH_SLOTS = 2 * EH_MAX;  // table slots per wave
 constexpr u32 EH_PER = EH_MAX / WAVE;
+constexpr u32 EV_BLOCK = 1024;  // threads per workgroup
+constexpr u32 EV_CHUNK = 2048;  // most hyperedges in a chunk
+constexpr u32 EV_IDS = 45056;   // partition ids of the LDS window
 
-template <int BLOCK>
-__global__ __launch_bounds__(BLOCK) void k_eval_hash(const i64 *e_off, const u32 *e_nsrc,
-                                                     const u32 *pins, const u32 *e_w,
-                                                     const u32 *rho, u32 k, u32 *part_inb,
-                                                     u64 *summary, const u32 *list,
-                                                     const u32 *cnt, u32 *flags) {
-  __shared__ u32 tab[BLOCK / WAVE][EH_SLOTS];
-  __shared__ u64 s_sum[3][BLOCK / WAVE];
-  const u32 total = *cnt;
-  const u32 nwaves = gridDim.x * (BLOCK / WAVE);
+__global__ __launch_bounds__(EV_BLOCK) void k_eval_hash(u32 E, u32 epc, const i64 *e_off,
+                                                        const u32 *e_nsrc, const u32 *pins,
+                                                        const u32 *e_w, const u32 *rho, u32 k,
+                                                        u32 *part_inb, u64 *summary,
+                                                        u32 *flags) {
+  __shared__ u32 tab[EV_BLOCK / WAVE][EH_SLOTS];
+  __shared__ u32 h[EV_IDS / 2];
+  __shared__ u64 s_sum[3][EV_BLOCK / WAVE];
+  __shared__ u32 s_wb;
+  const u32 nch = (E + epc - 1) / epc;
   const u32 l = lane_id();
   u32 *t = tab[wave_id()];
   for (u32 i = l; i < EH_SLOTS; i += WAVE) t[i] = 0;
   u64 conn = 0, cut = 0, lams = 0;
-  for (u32 w = blockIdx.x * (BLOCK / WAVE) + wave_id(); w < total; w += nwaves) {
-    const u32 e = list[w];
-    const i64 a = e_off[e];
-    const u32 len = (u32)(e_off[e + 1] - a), ns = e_nsrc[e];
-    if (len > EH_MAX) continue;  // (the workgroup sort's)
-    const u32 hs = next_pow2(2 * len);
-    const u32 sh = 32 - (31 - __builtin_clz(hs));
-    u32 p[EH_PER];
-#pragma unroll
-    for (u32 j = 0; j < EH_PER; ++j) {
-      const u32 i = l + j * WAVE;
-      p[j] = i < len ? pins[a + i] : 0;
+  for (u32 ch = blockIdx.x; ch < nch; ch += gridDim.x) {
+    const u32 w0 = ch * epc, w1 = E - w0 < epc ? E : w0 + epc;
+    for (u32 i = threadIdx.x; i < EV_IDS / 2; i += EV_BLOCK) h[i] = 0;
+    if (wave_id() == 0) {
+      // the window: the partition of the middle destination (of a sorted
+      // run: the smallest ones are the far ones where the others are local;
+      // the first pin where all are sources) of 64 hyperedges spread over
+      // the chunk
+      const u32 e = w0 + (u32)((u64)(w1 - w0) * l / WAVE);
+      const i64 ea = e_off[e];
+      const u32 elen = (u32)(e_off[e + 1] - ea), ens = e_nsrc[e];
+      u32 p = elen ? rho[pins[ea + (ens < elen ? ens + (elen - ens) / 2 : 0)]] : 0u;
+      p = p < k ? p : 0;
+      const u64 key = wave_sort64((u64)p);
+      const u32 med = (u32)__shfl(key, WAVE / 2, WAVE);
+      if (l == 0) s_wb = med > EV_IDS / 2 ? med - EV_IDS / 2 : 0u;
     }
-#pragma unroll
-    for (u32 j = 0; j < EH_PER; ++j) {
-      const u32 i = l + j * WAVE;
-      if (i < len) {
-        p[j] = rho[p[j]];
-        if (p[j] >= k) {
-          atomicOr(flags, FLAG_EINVAL);
-          p[j] = 0;
-        }
+    __syncthreads();
+    const u32 wb = s_wb;
+    // a wave screens 64 consecutive hyperedges at a time, a lane each, and
+    // takes those of this class one after the other
+    for (u32 eb = w0 + wave_id() * WAVE; eb < w1; eb += EV_BLOCK) {
+      i64 al = 0;
+      u32 lenl = 0, nsl = 0;
+      if (eb + l < w1) {
+        al = e_off[eb + l];
+        lenl = (u32)(e_off[eb + l + 1] - al);
+        nsl = e_nsrc[eb + l];
       }
-    }
-    u32 claims = 0;
+      u64 todo = __ballot(eb + l < w1 && lenl > WAVE && lenl <= EH_MAX);
+      while (todo) {
+        const u32 li = (u32)__builtin_ctzll(todo);
+        todo &= todo - 1;
+        const u32 e = eb + li;
+        const u32 ahi = (u32)__builtin_amdgcn_readlane((int)(u32)((u64)al >> 32), (int)li);
+        const u32 alo = (u32)__builtin_amdgcn_readlane((int)(u32)(u64)al, (int)li);
+        const i64 a = (i64)((u64)ahi << 32 | alo);
+        const u32 len = (u32)__builtin_amdgcn_readlane((int)lenl, (int)li);
+        const u32 ns = (u32)__builtin_amdgcn_readlane((int)nsl, (int)li);
+        const u32 hs = next_pow2(2 * len);
+        const u32 sh = 32 - (31 - __builtin_clz(hs));
+        u32 p[EH_PER];
 #pragma unroll
-    for (u32 pass = 0; pass < 2; ++pass) {
-      // pass 0: destinations (pins ns .. len - 1); pass 1: sources
+        for (u32 j = 0; j < EH_PER; ++j) {
+          const u32 i = l + j * WAVE;
+          p[j] = i < len ? pins[a + i] : 0;
+        }
 #pragma unroll
-      for (u32 j = 0; j < EH_PER; ++j) {
-        const u32 i = l + j * WAVE;
-        if (i < len && (pass ? i < ns : i >= ns)) {
-          const u32 key = p[j] + 1;
-          u32 s = (p[j] * 0x9E3779B1u) >> sh;
-          for (;;) {
-            const u32 o = atomicCAS(&t[s], 0u, key);
-            if (o == 0) {
-              ++claims;
-              if (!pass) atomicAdd(&part_inb[p[j]], 1u);
-              break;
+        for (u32 j = 0; j < EH_PER; ++j) {
+          const u32 i = l + j * WAVE;
+          if (i < len) {
+            p[j] = rho[p[j]];
+            if (p[j] >= k) {
+              atomicOr(flags, FLAG_EINVAL);
+              p[j] = 0;
             }
-            if (o == key) break;
-            s = (s + 1) & (hs - 1);
           }
         }
+        u32 claims = 0;
+#pragma unroll
+        for (u32 pass = 0; pass < 2; ++pass) {
+          // pass 0: destinations (pins ns .. len - 1); pass 1: sources
+#pragma unroll
+          for (u32 j = 0; j < EH_PER; ++j) {
+            const u32 i = l + j * WAVE;
+            if (i < len && (pass ? i < ns : i >= ns)) {
+              const u32 key = p[j] + 1;
+              u32 s = (p[j] * 0x9E3779B1u) >> sh;
+              for (;;) {
+                const u32 o = atomicCAS(&t[s], 0u, key);
+                if (o == 0) {
+                  ++claims;
+                  if (!pass) {
+                    const u32 r = p[j] - wb;
+                    if (r < EV_IDS) atomicAdd(&h[r >> 1], 1u << ((r & 1) << 4));
+                    else atomicAdd(&part_inb[p[j]], 1u);
+                  }
+                  break;
+                }
+                if (o == key) break;
+                s = (s + 1) & (hs - 1);
+              }
+            }
+          }
+        }
+        const u64 lam = wave_sum(claims);
+        for (u32 i = l; i < hs; i += WAVE) t[i] = 0;
+        if (l == 0) {
+          const u64 we = e_w[e];
+          conn += we * (lam - 1);
+          cut += lam > 1 ? we : 0;
+          lams += lam;
+        }
       }
     }
-    const u64 lam = wave_sum(claims);
-    for (u32 i = l; i < hs; i += WAVE) t[i] = 0;
-    if (l == 0) {
-      const u64 we = e_w[e];
-      conn += we * (lam - 1);
-      cut += lam > 1 ? we : 0;
-      lams += lam;
+    __syncthreads();
+    for (u32 i = threadIdx.x; i < EV_IDS / 2; i += EV_BLOCK) {
+      const u32 x = h[i];
+      if (x & 0xFFFFu) atomicAdd(&part_inb[wb + 2 * i], x & 0xFFFFu);
+      if (x >> 16) atomicAdd(&part_inb[wb + 2 * i + 1], x >> 16);
     }
+    __syncthreads();
   }
   if (l == 0) {
     s_sum[0][wave_id()] = conn;
@@ -245,7 +307,7 @@ __global__ __launch_bounds__(BLOCK) void k_eval_hash(const i64 *e_off, const u32
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < BLOCK / WAVE; ++w) {
+    for (int w = 1; w < EV_BLOCK / WAVE; ++w) {
       conn += s_sum[0][w];
       cut += s_sum[1][w];
       lams += s_sum[2][w];
@@ -381,10 +443,12 @@ void launch_eval_edges(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const u3
                (const u32 *)el.cnt + 0, c->flags);
   }
   if (host_cnt[1]) {
-    const u32 gh = (host_cnt[1] + 3) / 4;
-    CHP_LAUNCH(c, "eval_hash", k_eval_hash<256>, gh < 32 * c->n_cu ? gh : 32 * c->n_cu, 256, 0,
-               e_off, e_nsrc, pins, e_w, rho, k, part_inb, summary, (const u32 *)el.list[1],
-               (const u32 *)el.cnt + 1, c->flags);
+    // chunks of consecutive hyperedges, four per CU (from 64 to EV_CHUNK)
+    const u32 E = host_cnt[0] + host_cnt[1] + host_cnt[2];
+    const u32 per = E / (4 * c->n_cu);
+    const u32 epc = per < 64 ? 64 : per > EV_CHUNK ? EV_CHUNK : per;
+    CHP_LAUNCH(c, "eval_hash", k_eval_hash, (E + epc - 1) / epc, EV_BLOCK, 0, E, epc, e_off,
+               e_nsrc, pins, e_w, rho, k, part_inb, summary, c->flags);
     const u32 gl = (host_cnt[1] + 255) / 256;
     CHP_LAUNCH(c, "eval_lds", (k_eval_lds<256, LDS_CAP_U64>), gl < 8192 ? gl : 8192, 256, 0,
                e_off, e_nsrc, pins, e_w, rho, k, part_inb, summary, (const u32 *)el.list[1],
