@@ -137,10 +137,6 @@ struct QSmem {
 };
 static_assert(sizeof(QSmem) <= 160 * 1024, "LDS");
 
-template <u32 N>
-struct QConst {
-  static constexpr u32 value = N;
-};
 __device__ __forceinline__ u32 rfl(u32 v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ u64 rfl64(u64 v) {
   return ((u64)rfl((u32)(v >> 32)) << 32) | rfl((u32)v);
@@ -726,80 +722,72 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
       // (a lane outside the chunk gets some stretch of the chunk, read but
       // unused; its load is redirected and its pin reads as hi: in no
       // window, and past the end of every stretch of the chunk)
-      // the chunk's visits with its first NU blocks per wave: all QU of them,
-      // or 4 for a last chunk of at most 4 QW blocks (a sketch window's, most
-      // of the time), whose other blocks are empty
-      auto visit = [&](auto nuc) {
-        constexpr u32 NU = decltype(nuc)::value;
-        u32 kk[NU], v[NU];
+      u32 kk[QU], v[QU];
 #pragma unroll
-        for (u32 u = 0; u < NU; ++u) {
-          const u32 k0 = __builtin_amdgcn_readlane(bf_l, u);
-          // starts at block positions 1 .. lane: the set bits of bits >> 1 below
-          // this lane (the lane-mask count)
-          const u64 sb = ((u64)(u32)__builtin_amdgcn_readlane((u32)(sb_l >> 32), u) << 32 |
-                          (u32)__builtin_amdgcn_readlane((u32)sb_l, u)) >> 1;
-          const u32 k = k0 + __builtin_amdgcn_mbcnt_hi((u32)(sb >> 32),
-                                                       __builtin_amdgcn_mbcnt_lo((u32)sb, 0u));
-          kk[u] = k;
+      for (u32 u = 0; u < QU; ++u) {
+        const u32 k0 = __builtin_amdgcn_readlane(bf_l, u);
+        // starts at block positions 1 .. lane: the set bits of bits >> 1 below
+        // this lane (the lane-mask count)
+        const u64 sb = ((u64)(u32)__builtin_amdgcn_readlane((u32)(sb_l >> 32), u) << 32 |
+                        (u32)__builtin_amdgcn_readlane((u32)sb_l, u)) >> 1;
+        const u32 k = k0 + __builtin_amdgcn_mbcnt_hi((u32)(sb >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((u32)sb, 0u));
+        kk[u] = k;
+      }
+      i32 ca[QU];
+#pragma unroll
+      for (u32 u = 0; u < QU; ++u) ca[u] = S.caddr[kk[u]];
+#pragma unroll
+      for (u32 u = 0; u < QU; ++u)
+        v[u] = A.e_pins[(int)lane < lim(u) ? (u32)(ca[u] + (i32)(pbase(u) + lane)) : 0u];
+#pragma unroll
+      for (u32 u = 0; u < QU; ++u) v[u] = (int)lane < lim(u) ? v[u] : hi32;
+      // the first pin >= hi of each stretch: a lane whose pin is >= hi while
+      // the lane before holds a pin < hi of the same stretch does not qualify
+      // (one lane per stretch and wave block; the block's first position
+      // counts as a stretch start)
+#pragma unroll
+      for (u32 u = 0; u < QU; ++u) {
+        const u64 B = __builtin_amdgcn_ballot_w64(v[u] >= hi32);
+        const u64 st = ((u64)(u32)__builtin_amdgcn_readlane((u32)(sb_l >> 32), u) << 32 |
+                        (u32)__builtin_amdgcn_readlane((u32)sb_l, u)) | 1ull;
+        const u64 first = B & ~((B << 1) & ~st);
+        if (__builtin_amdgcn_inverse_ballot_w64(first))
+          atomicMin(&S.cnext[kk[u]], pbase(u) + lane);
+      }
+      u32 qv[QU];
+#pragma unroll
+      for (u32 u = 0; u < QU; ++u) qv[u] = S.cq[kk[u]];
+      const u32 span = hi32 - lo32;
+      if (direct) {
+        // (the largest bin is found by the candidate pass)
+#pragma unroll
+        for (u32 u = 0; u < QU; ++u) {
+          const u32 r = v[u] - lo32;
+          if (r < span && v[u] != n) atomicAdd(&S.t.bin[r >> 1], qv[u] << ((r & 1u) << 4));
         }
-        i32 ca[NU];
+      } else if (sk) {
 #pragma unroll
-        for (u32 u = 0; u < NU; ++u) ca[u] = S.caddr[kk[u]];
-#pragma unroll
-        for (u32 u = 0; u < NU; ++u)
-          v[u] = A.e_pins[(int)lane < lim(u) ? (u32)(ca[u] + (i32)(pbase(u) + lane)) : 0u];
-#pragma unroll
-        for (u32 u = 0; u < NU; ++u) v[u] = (int)lane < lim(u) ? v[u] : hi32;
-        // the first pin >= hi of each stretch: a lane whose pin is >= hi while
-        // the lane before holds a pin < hi of the same stretch does not qualify
-        // (one lane per stretch and wave block; the block's first position
-        // counts as a stretch start)
-#pragma unroll
-        for (u32 u = 0; u < NU; ++u) {
-          const u64 B = __builtin_amdgcn_ballot_w64(v[u] >= hi32);
-          const u64 st = ((u64)(u32)__builtin_amdgcn_readlane((u32)(sb_l >> 32), u) << 32 |
-                          (u32)__builtin_amdgcn_readlane((u32)sb_l, u)) | 1ull;
-          const u64 first = B & ~((B << 1) & ~st);
-          if (__builtin_amdgcn_inverse_ballot_w64(first))
-            atomicMin(&S.cnext[kk[u]], pbase(u) + lane);
+        for (u32 u = 0; u < QU; ++u) {
+          const u32 x = v[u];
+          if (x - lo32 < span && x != n) atomicAdd(&S.t.bin[qsketch(x)], qv[u]);
         }
-        u32 qv[NU];
+      } else {
 #pragma unroll
-        for (u32 u = 0; u < NU; ++u) qv[u] = S.cq[kk[u]];
-        const u32 span = hi32 - lo32;
-        if (direct) {
-          // (the largest bin is found by the candidate pass)
-#pragma unroll
-          for (u32 u = 0; u < NU; ++u) {
-            const u32 r = v[u] - lo32;
-            if (r < span && v[u] != n) atomicAdd(&S.t.bin[r >> 1], qv[u] << ((r & 1u) << 4));
-          }
-        } else if (sk) {
-#pragma unroll
-          for (u32 u = 0; u < NU; ++u) {
-            const u32 x = v[u];
-            if (x - lo32 < span && x != n) atomicAdd(&S.t.bin[qsketch(x)], qv[u]);
-          }
-        } else {
-#pragma unroll
-          for (u32 u = 0; u < NU; ++u) {
-            const u32 x = v[u];
-            if (x >= lo32 && x < hi32 && x != n) {
-              const u32 sl2 = q_insert(S, x, hcap);
-              if (sl2 == QFAIL) {
-                atomicMin(&S.fail_min, x);
-                continue;
-              }
-              const u32 q = qv[u];
-              const u32 o = atomicAdd(&S.t.h.bin[sl2], q) + q;
-              vmax = o > vmax ? o : vmax;
+        for (u32 u = 0; u < QU; ++u) {
+          const u32 x = v[u];
+          if (x >= lo32 && x < hi32 && x != n) {
+            const u32 sl2 = q_insert(S, x, hcap);
+            if (sl2 == QFAIL) {
+              atomicMin(&S.fail_min, x);
+              continue;
             }
+            const u32 q = qv[u];
+            const u32 o = atomicAdd(&S.t.h.bin[sl2], q) + q;
+            vmax = o > vmax ? o : vmax;
           }
         }
-      };
-      if (T - c <= 4 * QW * WAVE) visit(QConst<4>{});
-      else visit(QConst<QU>{});
+      }
       if (!om && !sk && !direct) {
         u32 wv = vmax;
 #pragma unroll
