@@ -1386,7 +1386,7 @@ int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
     // split by size (twice its count)
     u32 *erest = s.get<u32>(2ull * he[0] + 2ull * he[1] + 1);
     launch_edge_contract(c, g->e_off, g->e_nsrc, g->e_pins, gamma, opins, olen, cg.e_nsrc, el, he,
-                         escr, eper, egb, erest);
+                         escr, eper, egb, erest, Nc < (1u << 31) - 1);
     scan_u32_to_i64(c, olen, cg.e_off, E, tmp);
     // -- coarse incidence classes: in'(c) = in(a) u in(b), out' = (out(a) u out(b)) \ in'
     u32 *ibound = s.get<u32>(Nc), *icnt = s.get<u32>(Nc);
@@ -1438,7 +1438,7 @@ int chp_contract(chp_ctx *c, const chp_hgraph *g, const u32 *match, u32 *gamma,
       iscr = s.get<u64>(iper * igb);
     }
     launch_cinc_build(c, g->n_off, g->n_nin, g->n_inc, rep_of, match, iooff, iobuf, cg.n_nin,
-                      icnt, il, hi, iscr, iper, igb);
+                      icnt, il, hi, iscr, iper, igb, E < (1u << 31) - 1);
     scan_u32_to_i64(c, icnt, cg.n_off, Nc, tmp2);
     cg.n_inc = own.get<u32>(cg.n_pins);  // |I'| summed over clusters = pins of G'
     launch_cinc_compact(c, Nc, rep_of, match, g->n_off, g->n_inc, iooff, iobuf, cg.n_off,

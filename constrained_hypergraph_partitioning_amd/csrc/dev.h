@@ -391,19 +391,20 @@ __device__ __forceinline__ void wave_sort_regs(K (&v)[PER]) {
 }
 
 // wave_group_split_emit for m sorted keys held PER a lane as wave_sort_regs
-// leaves them (value << 1 | tag; a group of equal value is represented by its
-// first key): the values of the groups whose first tag is FIRST_TAG go to
-// out[0, n_first), the others to out[n_first, n_total), each in order.
-template <u32 FIRST_TAG, int PER>
-__device__ __forceinline__ void wave_group_split_emit_regs(const u64 (&v)[PER], u32 m, u32 *out,
+// leaves them (value << 1 | tag, 32 or 64 bits; a group of equal value is
+// represented by its first key): the values of the groups whose first tag is
+// FIRST_TAG go to out[0, n_first), the others to out[n_first, n_total), each
+// in order.
+template <u32 FIRST_TAG, int PER, typename K>
+__device__ __forceinline__ void wave_group_split_emit_regs(const K (&v)[PER], u32 m, u32 *out,
                                                            u32 &n_first, u32 &n_total) {
   const u32 l = lane_id();
-  const u64 prev_last = __shfl_up(v[PER - 1], 1, WAVE);
+  const K prev_last = __shfl_up(v[PER - 1], 1, WAVE);
   u32 fmask = 0, omask = 0;
 #pragma unroll
   for (u32 r = 0; r < (u32)PER; ++r) {
     const u32 i = PER * l + r;
-    const u64 pk = r ? v[r - 1] : prev_last;
+    const K pk = r ? v[r - 1] : prev_last;
     const bool f = i < m && (i == 0 || (pk >> 1) != (v[r] >> 1));
     const bool ff = f && (u32)(v[r] & 1) == FIRST_TAG;
     fmask |= (ff ? 1u : 0u) << r;

@@ -95,20 +95,23 @@ __global__ __launch_bounds__(256) void k_cinc_wave(const i64 *n_off, const u32 *
 
 // Pairs with a bound of 65 .. CINC_SMALL: a wave each, the keys sorted in
 // registers (4, 8 or 16 a lane, by the bound), inbound hyperedges first.
-template <int PER>
+// K = u32 when every hyperedge id is below 2^31 - 1 (the key e << 1 | is_out
+// then fits 32 bits, below the padding ~0), u64 otherwise.
+template <typename K, int PER>
 __device__ __forceinline__ void cinc_regs(const i64 *n_off, const u32 *n_nin, const u32 *n_inc,
                                           u32 a, u32 b, u32 m, u32 *out, u32 &nin, u32 &ntot) {
   const u32 l = lane_id();
-  u64 v[PER];
+  K v[PER];
 #pragma unroll
   for (u32 q = 0; q < (u32)PER; ++q) {
     const u32 i = q * WAVE + l;
-    v[q] = i < m ? inc_key(n_off, n_nin, n_inc, a, b, i) : ~0ull;
+    v[q] = i < m ? (K)inc_key(n_off, n_nin, n_inc, a, b, i) : ~(K)0;
   }
-  wave_sort_regs<u64, PER>(v);
+  wave_sort_regs<K, PER>(v);
   wave_group_split_emit_regs<0, PER>(v, m, out, nin, ntot);
 }
 
+template <typename K>
 __global__ __launch_bounds__(256) void k_cinc_wreg(const i64 *n_off, const u32 *n_nin,
                                                    const u32 *n_inc, const u32 *rep_of,
                                                    const u32 *match, const i64 *ooff, u32 *obuf,
@@ -122,9 +125,9 @@ __global__ __launch_bounds__(256) void k_cinc_wreg(const i64 *n_off, const u32 *
     const u32 m = (u32)(n_off[a + 1] - n_off[a] + n_off[b + 1] - n_off[b]);
     u32 nin, ntot;
     u32 *out = obuf + ooff[c];
-    if (m <= 4 * WAVE) cinc_regs<4>(n_off, n_nin, n_inc, a, b, m, out, nin, ntot);
-    else if (m <= 8 * WAVE) cinc_regs<8>(n_off, n_nin, n_inc, a, b, m, out, nin, ntot);
-    else cinc_regs<16>(n_off, n_nin, n_inc, a, b, m, out, nin, ntot);
+    if (m <= 4 * WAVE) cinc_regs<K, 4>(n_off, n_nin, n_inc, a, b, m, out, nin, ntot);
+    else if (m <= 8 * WAVE) cinc_regs<K, 8>(n_off, n_nin, n_inc, a, b, m, out, nin, ntot);
+    else cinc_regs<K, 16>(n_off, n_nin, n_inc, a, b, m, out, nin, ntot);
     if (lane_id() == 0) {
       cnt_in[c] = nin;
       cnt_tot[c] = ntot;
@@ -403,16 +406,19 @@ void launch_cinc_classify(chp_ctx *c, u32 Nc, const u32 *rep_of, const u32 *matc
 void launch_cinc_build(chp_ctx *c, const i64 *n_off, const u32 *n_nin, const u32 *n_inc,
                        const u32 *rep_of, const u32 *match, const i64 *ooff, u32 *obuf,
                        u32 *cnt_in, u32 *cnt_tot, EdgeLists el, const u32 *host_cnt,
-                       u64 *scratch, u64 per_wg, u32 grid_big) {
+                       u64 *scratch, u64 per_wg, u32 grid_big, bool narrow) {
   if (host_cnt[0])
     CHP_LAUNCH(c, "cinc_wave", k_cinc_wave, waves_grid(host_cnt[0]), 256, 0, n_off, n_nin, n_inc,
                rep_of, match, ooff, obuf, cnt_in, cnt_tot, (const u32 *)el.list[0],
                (const u32 *)el.cnt + 0);
   if (host_cnt[1]) {
-    const u32 gw = (host_cnt[1] + 3) / 4;
-    CHP_LAUNCH(c, "cinc_wreg", k_cinc_wreg, gw < 32 * c->n_cu ? gw : 32 * c->n_cu, 256, 0, n_off,
-               n_nin, n_inc, rep_of, match, ooff, obuf, cnt_in, cnt_tot,
-               (const u32 *)el.list[1], (const u32 *)el.cnt + 1);
+    const u32 gw = (host_cnt[1] + 3) / 4, gc = gw < 32 * c->n_cu ? gw : 32 * c->n_cu;
+    if (narrow)
+      CHP_LAUNCH(c, "cinc_wreg", k_cinc_wreg<u32>, gc, 256, 0, n_off, n_nin, n_inc, rep_of, match,
+                 ooff, obuf, cnt_in, cnt_tot, (const u32 *)el.list[1], (const u32 *)el.cnt + 1);
+    else
+      CHP_LAUNCH(c, "cinc_wreg", k_cinc_wreg<u64>, gc, 256, 0, n_off, n_nin, n_inc, rep_of, match,
+                 ooff, obuf, cnt_in, cnt_tot, (const u32 *)el.list[1], (const u32 *)el.cnt + 1);
   }
   if (host_cnt[3])
     CHP_LAUNCH(c, "cinc_lds", (k_cinc_lds<256, LDS_CAP_U64>),

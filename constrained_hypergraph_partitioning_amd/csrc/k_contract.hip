@@ -208,21 +208,24 @@ __global__ __launch_bounds__(256) void k_econ_wave(const i64 *e_off, const u32 *
 }
 
 // Hyperedges of 65 .. ECON_SMALL pins: a wave each, the keys sorted in
-// registers (4, 8 or 16 a lane, by |e|), distinct sources first.
-template <int PER>
+// registers (4, 8 or 16 a lane, by |e|), distinct sources first.  K = u32
+// when every coarse id is below 2^31 - 1 (the key gamma << 1 | tag then
+// fits 32 bits, below the padding ~0), u64 otherwise.
+template <typename K, int PER>
 __device__ __forceinline__ void econ_regs(const u32 *pins, i64 a, u32 len, u32 ns,
                                           const u32 *gamma, u32 *out, u32 &nsp, u32 &ntot) {
   const u32 l = lane_id();
-  u64 v[PER];
+  K v[PER];
 #pragma unroll
   for (u32 q = 0; q < (u32)PER; ++q) {
     const u32 i = q * WAVE + l;
-    v[q] = i < len ? ((u64)gamma[pins[a + i]] << 1) | (i < ns ? 1u : 0u) : ~0ull;
+    v[q] = i < len ? ((K)gamma[pins[a + i]] << 1) | (i < ns ? 1u : 0u) : ~(K)0;
   }
-  wave_sort_regs<u64, PER>(v);
+  wave_sort_regs<K, PER>(v);
   wave_group_split_emit_regs<1, PER>(v, len, out, nsp, ntot);
 }
 
+template <typename K>
 __global__ __launch_bounds__(256) void k_econ_wreg(const i64 *e_off, const u32 *e_nsrc,
                                                    const u32 *pins, const u32 *gamma, u32 *opins,
                                                    u32 *olen, u32 *onsrc, const u32 *list,
@@ -234,9 +237,9 @@ __global__ __launch_bounds__(256) void k_econ_wreg(const i64 *e_off, const u32 *
     const i64 a = e_off[e];
     const u32 len = (u32)(e_off[e + 1] - a), ns = e_nsrc[e];
     u32 nsp, ntot;
-    if (len <= 4 * WAVE) econ_regs<4>(pins, a, len, ns, gamma, opins + a, nsp, ntot);
-    else if (len <= 8 * WAVE) econ_regs<8>(pins, a, len, ns, gamma, opins + a, nsp, ntot);
-    else econ_regs<16>(pins, a, len, ns, gamma, opins + a, nsp, ntot);
+    if (len <= 4 * WAVE) econ_regs<K, 4>(pins, a, len, ns, gamma, opins + a, nsp, ntot);
+    else if (len <= 8 * WAVE) econ_regs<K, 8>(pins, a, len, ns, gamma, opins + a, nsp, ntot);
+    else econ_regs<K, 16>(pins, a, len, ns, gamma, opins + a, nsp, ntot);
     if (lane_id() == 0) {
       olen[e] = ntot;
       onsrc[e] = nsp;
@@ -337,7 +340,7 @@ void launch_edge_classify(chp_ctx *c, u32 E, const i64 *e_off, EdgeLists el) {
 void launch_edge_contract(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
                           const u32 *gamma, u32 *opins, u32 *olen, u32 *onsrc, EdgeLists el,
                           const u32 *host_cnt, u64 *scratch, u64 per_wg, u32 grid_big,
-                          u32 *rest) {
+                          u32 *rest, bool narrow) {
   if (host_cnt[0]) {
     // el.cnt[4] and el.cnt[5] count the wave-class hyperedges of 9..32 and
     // 33..64 pins (zeroed by the classification's fill)
@@ -357,10 +360,13 @@ void launch_edge_contract(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const
     u32 *small = rest + 2ull * host_cnt[0], *big = small + host_cnt[1];
     CHP_LAUNCH(c, "econ_split", k_econ_split, grid_for(host_cnt[1], 256), 256, 0, e_off,
                (const u32 *)el.list[1], (const u32 *)el.cnt + 1, small, big, el.cnt + 6);
-    const u32 gw = (host_cnt[1] + 3) / 4;
-    CHP_LAUNCH(c, "econ_wreg", k_econ_wreg, gw < 32 * c->n_cu ? gw : 32 * c->n_cu, 256, 0, e_off,
-               e_nsrc, pins, gamma, opins, olen, onsrc, (const u32 *)small,
-               (const u32 *)el.cnt + 6);
+    const u32 gw = (host_cnt[1] + 3) / 4, ge = gw < 32 * c->n_cu ? gw : 32 * c->n_cu;
+    if (narrow)
+      CHP_LAUNCH(c, "econ_wreg", k_econ_wreg<u32>, ge, 256, 0, e_off, e_nsrc, pins, gamma, opins,
+                 olen, onsrc, (const u32 *)small, (const u32 *)el.cnt + 6);
+    else
+      CHP_LAUNCH(c, "econ_wreg", k_econ_wreg<u64>, ge, 256, 0, e_off, e_nsrc, pins, gamma, opins,
+                 olen, onsrc, (const u32 *)small, (const u32 *)el.cnt + 6);
     CHP_LAUNCH(c, "econ_lds", (k_econ_lds<256, LDS_CAP_U64>),
                host_cnt[1] > 8192 ? 8192 : host_cnt[1], 256, 0, e_off, e_nsrc, pins, gamma, opins,
                olen, onsrc, (const u32 *)big, (const u32 *)el.cnt + 7);

@@ -243,7 +243,7 @@ void launch_edge_classify(chp_ctx *c, u32 E, const i64 *e_off, EdgeLists el);
 void launch_edge_contract(chp_ctx *c, const i64 *e_off, const u32 *e_nsrc, const u32 *pins,
                           const u32 *gamma, u32 *opins, u32 *olen, u32 *onsrc, EdgeLists el,
                           const u32 *host_cnt, u64 *scratch, u64 per_wg, u32 grid_big,
-                          u32 *rest);
+                          u32 *rest, bool narrow);  // narrow: every gamma < 2^31 - 1
 void launch_pins_compact(chp_ctx *c, u32 E, const i64 *src_off, const u32 *src,
                          const i64 *dst_off, u32 *dst);
 
@@ -254,7 +254,8 @@ void launch_cinc_classify(chp_ctx *c, u32 Nc, const u32 *rep_of, const u32 *matc
 void launch_cinc_build(chp_ctx *c, const i64 *n_off, const u32 *n_nin, const u32 *n_inc,
                        const u32 *rep_of, const u32 *match, const i64 *ooff, u32 *obuf,
                        u32 *cnt_in, u32 *cnt_tot, EdgeLists el, const u32 *host_cnt,
-                       u64 *scratch, u64 per_wg, u32 grid_big);
+                       u64 *scratch, u64 per_wg, u32 grid_big,
+                       bool narrow);  // narrow: every hyperedge id < 2^31 - 1
 void launch_cinc_compact(chp_ctx *c, u32 Nc, const u32 *rep_of, const u32 *match,
                          const i64 *n_off, const u32 *n_inc, const i64 *ooff, const u32 *obuf,
                          const i64 *c_off, u32 *c_inc);
