@@ -219,7 +219,9 @@ void read_many(chp_ctx *c, std::initializer_list<HostRead> items) {
   for (const HostRead &it : items) memcpy(it.host, (const char *)c->pinned + 4 * d.off[k++], it.n);
 }
 
-void read_back(chp_ctx *c, void *host, const void *dev, size_t n) { read_many(c, {{host, dev, n}}); }
+void read_back(chp_ctx *c, void *host, const void *dev, size_t n) {
+  read_many(c, {{host, dev, n}});
+}
 
 void d2d(chp_ctx *c, void *dst, const void *src, size_t n) {
   if (n) hip_check(c, hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, c->stream), "copy");
