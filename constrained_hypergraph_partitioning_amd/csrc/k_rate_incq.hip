@@ -64,7 +64,10 @@ constexpr u32 QNHB = 1024;            // estimate buckets
 constexpr u32 QBS_MIN = 12;           // log2 of the narrowest bucket
 constexpr u32 QHTGT = QCAP * 3 / 4;   // estimated visits a hash window aims at
 constexpr u32 QEST = 16;              // estimates count sixteenths of a visit
-constexpr u32 QSK = 12288;            // estimated visits a sketch window aims at
+constexpr u32 QSK = 16384;            // estimated visits a sketch window aims at
+// (on the 4M-node block level, with direct windows from 2 visits per 16 ids,
+// 8,192, 12,288 and 16,384 took 1,072, 988 and 972 ms per pass; from 4 per
+// 16 ids, 12,288, 16,384 and 24,576 took 955, 938 and 939 ms)
 constexpr u32 QU = 16384 / QB;        // pins per thread per chunk
 constexpr u32 QCH = QB * QU;          // pins per chunk
 constexpr u32 QNBLK = QCH / WAVE;     // wave blocks per chunk
@@ -534,7 +537,11 @@ __device__ bool rate_node_q(const RateArgs &A, QSmem &S, const NodeRec &h, u32 m
     if (tid == 0) S.cum[QNHB] = tot;
   }
   __syncthreads();
-  const u32 dense = QDD / 8 * QEST;  // estimated visits that make a window direct
+  // estimated visits that make a window direct: 6 per 16 ids.  On the
+  // 4M-node block level, with sketches of 16,384 estimated visits, 3, 4, 5
+  // and 6 per 16 ids took 946, 938, 926 and 917 ms per pass and 8 per 16
+  // ids 1,480 ms; 2 per 16 with sketches of 12,288 took 988 ms
+  const u32 dense = QDD * 3 / 8 * QEST;
   {
     const u32 wb = (QDD >> bs) > 0 ? (QDD >> bs) : 1;  // buckets of a direct window
 #pragma unroll
